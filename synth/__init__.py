@@ -1,0 +1,246 @@
+"""Seeded synthetic inputs for the routed-expert MoE workloads.
+
+This module is shared by the oracle side (tests, CPU baseline) and the HIP
+side (tests, bench).  It only draws random inputs -- logits, activations,
+fp32 expert weights, VQ codes/codebooks/scales, tier maps -- and rounds them
+to their storage types.  It holds none of the method's arithmetic: no format
+encoding, no routing, no FFN.
+
+Seeds: numpy PCG64 seeded by SeedSequence([20260711, cfg, kind, expert, proj,
+rep]).  The tuple mirrors the (layer, expert, projection, rank) seed scheme
+and seed base of GLM-5.3-EXL3-TR3-3.42bpw ("What is quantized": deterministic,
+data-free encode).
+
+Workloads (names used throughout tests/ and bench.py):
+  tiny    E=8,   k=2, H=256,  I=128,  T=4     NVFP4 from N(0, 0.02) fp32,
+                                              logits N(0,1)
+  decode  E=256, k=8, H=6144, I=2048, T in {1, 8, 32}, NVFP4 layer,
+                                              logits U[0,1)
+  prefill same layer as decode, T=4096, Zipf(1.1) expert popularity
+  vq      E=256, k=8, H=6144, I=2048, T=8, 2-bit AQLM-style VQ,
+                                              logits U[0,1)
+  mixed   108 NVFP4 + 148 VQ experts (seeded tier map), T in {8, 32},
+          20 hot experts receive 60% of assignments in expectation
+Activations are bf16 ~ N(0, 1) in all of them.
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+SEED_BASE = 20260711
+
+# kinds of random stream
+KIND_W = 0
+KIND_LOGITS = 1
+KIND_X = 2
+KIND_VQ_CODES = 3
+KIND_VQ_CODEBOOK = 4
+KIND_VQ_SCALES = 5
+KIND_TIER = 6
+KIND_HOT = 7
+KIND_ZIPF_RANK = 8
+
+PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
+
+FMT_NVFP4 = 1
+FMT_VQ = 2
+
+
+def rng(cfg, kind, expert=0, proj=0, rep=0):
+    ss = np.random.SeedSequence([SEED_BASE, int(cfg), int(kind), int(expert),
+                                 int(proj), int(rep)])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+# --------------------------------------------------------------------------
+# storage-type rounding of drawn values
+# --------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x):
+    """Round fp32 to bf16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def f32_to_f16_bits(x):
+    """Round to IEEE binary16 (numpy's cast: nearest, ties to even)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# workload shapes
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg: int            # seed slot of the routing/activation streams
+    E: int
+    k: int
+    H: int
+    I: int
+    T: tuple
+    fmt: str            # "nvfp4", "vq" or "mixed"
+    logits: str         # "normal", "uniform", "zipf" or "hot"
+    weight_cfg: int = 1     # seed slot of the NVFP4 weights
+    vq_cfg: int = 3         # seed slot of the VQ codes/codebooks/scales
+    n_nvfp4: int = 0        # mixed only
+    n_hot: int = 0
+    hot_share: float = 0.0
+    zipf_s: float = 0.0
+    extra: dict = field(default_factory=dict, compare=False, hash=False)
+
+
+TINY = Workload("tiny", 0, 8, 2, 256, 128, (4,), "nvfp4", "normal", weight_cfg=0)
+DECODE = Workload("decode", 1, 256, 8, 6144, 2048, (1, 8, 32), "nvfp4", "uniform")
+PREFILL = Workload("prefill", 2, 256, 8, 6144, 2048, (4096,), "nvfp4", "zipf",
+                   zipf_s=1.1)
+VQ = Workload("vq", 3, 256, 8, 6144, 2048, (8,), "vq", "uniform")
+MIXED = Workload("mixed", 4, 256, 8, 6144, 2048, (8, 32), "mixed", "hot",
+                 n_nvfp4=108, n_hot=20, hot_share=0.6)
+
+WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED)}
+
+
+def small_workload(name, E, k, H, I, T, fmt="nvfp4", logits="normal", cfg=100,
+                   n_nvfp4=0, n_hot=0, hot_share=0.0):
+    """A property-test workload with its own seed slot."""
+    return Workload(name, cfg, E, k, H, I, (T,), fmt, logits, weight_cfg=cfg,
+                    vq_cfg=cfg, n_nvfp4=n_nvfp4, n_hot=n_hot, hot_share=hot_share)
+
+
+# --------------------------------------------------------------------------
+# activations and logits
+# --------------------------------------------------------------------------
+
+def activations(wl, T, rep=0):
+    """bf16 ~ N(0, 1) activations [T, H] as uint16 bits."""
+    x = rng(wl.cfg, KIND_X, 0, T, rep).standard_normal((T, wl.H), dtype=np.float32)
+    return f32_to_bf16_bits(x)
+
+
+def logits(wl, T, rep=0):
+    """fp32 router logits [T, E] following the workload's recipe."""
+    g = rng(wl.cfg, KIND_LOGITS, 0, T, rep)
+    if wl.logits == "normal":
+        return g.standard_normal((T, wl.E), dtype=np.float32)
+    if wl.logits == "uniform":
+        return g.random((T, wl.E), dtype=np.float32)
+    if wl.logits == "zipf":
+        return zipf_logits(wl, g, T)
+    if wl.logits == "hot":
+        hot = hot_experts(wl)
+        beta = np.float32(hot_bias(wl.E, wl.k, wl.n_hot, wl.hot_share))
+        lg = g.random((T, wl.E), dtype=np.float32)
+        lg[:, hot] += beta
+        return lg
+    raise ValueError(wl.logits)
+
+
+def zipf_popularity(wl):
+    """p_e proportional to r_e^-s over a seeded permutation r of ranks 1..E."""
+    ranks = rng(wl.cfg, KIND_ZIPF_RANK).permutation(wl.E) + 1
+    p = ranks.astype(np.float64) ** (-wl.zipf_s)
+    return p / p.sum()
+
+
+def zipf_logits(wl, g, T):
+    """ln p_e + Gumbel(0, 1) noise, fp32: the top-k of these samples k experts
+    without replacement with probability proportional to p (Gumbel-top-k)."""
+    p = zipf_popularity(wl)
+    u = g.random((T, wl.E))
+    u = np.clip(u, 1e-300, None)
+    gumbel = -np.log(-np.log(u))
+    return (np.log(p)[None, :] + gumbel).astype(np.float32)
+
+
+def hot_experts(wl):
+    return np.sort(rng(wl.cfg, KIND_HOT).choice(wl.E, size=wl.n_hot, replace=False))
+
+
+def hot_bias(E, k, n_hot, share, n_quad=4000):
+    """Bias b added to the U[0,1) logits of n_hot experts so that, in
+    expectation, a fraction `share` of the top-k picks are hot.
+
+    A hot expert with value y (uniform on [b, 1+b)) is picked iff at most k-1
+    of the other experts exceed y: Binomial(n_hot-1, 1+b-y) hot ones plus
+    Binomial(E-n_hot, max(0, 1-y)) cold ones.  The expected hot share is
+    n_hot/k * P(picked); b is found by bisection (the share grows with b).
+    """
+    from scipy.stats import binom
+
+    def expected_share(b):
+        y = b + (np.arange(n_quad) + 0.5) / n_quad
+        qh = np.clip(1.0 + b - y, 0.0, 1.0)
+        qc = np.clip(1.0 - y, 0.0, 1.0)
+        j = np.arange(k)
+        ph = binom.pmf(j[None, :], n_hot - 1, qh[:, None])       # [n, k]
+        pc = binom.pmf(j[None, :], E - n_hot, qc[:, None])
+        # P(Nh + Nc <= k-1) = sum_{a+c<=k-1} ph[a] pc[c]
+        cpc = np.cumsum(pc, axis=1)
+        prob = np.zeros(n_quad)
+        for a in range(k):
+            prob += ph[:, a] * cpc[:, k - 1 - a]
+        return n_hot / k * prob.mean()
+
+    lo, hi = 0.0, 1.0
+    for _ in range(60):
+        mid = 0.5 * (lo + hi)
+        if expected_share(mid) < share:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+# --------------------------------------------------------------------------
+# expert weights
+# --------------------------------------------------------------------------
+
+def proj_shape(wl, proj):
+    return (wl.I, wl.H) if proj in (PROJ_GATE, PROJ_UP) else (wl.H, wl.I)
+
+
+def nvfp4_source_weights(wl, expert, proj):
+    """fp32 ~ N(0, 0.02) weights [n, kin] of one projection of one expert,
+    before NVFP4 quantization (W_gate, W_up: [I, H]; W_down: [H, I])."""
+    n, kin = proj_shape(wl, proj)
+    z = rng(wl.weight_cfg, KIND_W, expert, proj).standard_normal((n, kin),
+                                                                 dtype=np.float32)
+    return z * np.float32(0.02)
+
+
+def vq_codes(wl, expert, proj):
+    """Uniform uint16 codes [n, kin/8] of one projection of one expert."""
+    n, kin = proj_shape(wl, proj)
+    return rng(wl.vq_cfg, KIND_VQ_CODES, expert, proj).integers(
+        0, 65536, size=(n, kin // 8), dtype=np.uint16)
+
+
+def vq_scales(wl, expert, proj):
+    """fp16 per-output-channel scales ~ U(0.5, 1.5), as uint16 bits [n]."""
+    n, _ = proj_shape(wl, proj)
+    s = rng(wl.vq_cfg, KIND_VQ_SCALES, expert, proj).uniform(0.5, 1.5, size=n)
+    return f32_to_f16_bits(s.astype(np.float32))
+
+
+def vq_codebook(wl, proj, ncode=65536):
+    """One fp16 codebook [ncode, 8] per projection type, shared by all the
+    layer's experts; entries ~ N(0, 0.02); uint16 bits."""
+    c = rng(wl.vq_cfg, KIND_VQ_CODEBOOK, 0, proj).standard_normal(
+        (ncode, 8), dtype=np.float32) * np.float32(0.02)
+    return f32_to_f16_bits(c)
+
+
+def tier_map(wl):
+    """Per-expert format tag (FMT_NVFP4 / FMT_VQ), uint8 [E]."""
+    if wl.fmt == "nvfp4":
+        return np.full(wl.E, FMT_NVFP4, dtype=np.uint8)
+    if wl.fmt == "vq":
+        return np.full(wl.E, FMT_VQ, dtype=np.uint8)
+    tm = np.full(wl.E, FMT_VQ, dtype=np.uint8)
+    nv = rng(wl.cfg, KIND_TIER).choice(wl.E, size=wl.n_nvfp4, replace=False)
+    tm[nv] = FMT_NVFP4
+    return tm

@@ -1,0 +1,287 @@
+"""Pins of the oracle's format code (E2M1, E4M3, NVFP4 encoder, VQ decode)
+against facts fixed outside the oracle: published value tables, a library
+cast, hand-worked blocks, brute force and closed forms.  CPU only."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.formats import nvfp4_unpack_codes
+
+
+def _read_table(path):
+    rows = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- E2M1
+
+def test_e2m1_value_set_matches_published_table(golden_dir):
+    rows = _read_table(os.path.join(golden_dir, "e2m1_values.txt"))
+    assert len(rows) == 16
+    for code, val in rows:
+        got = oracle.e2m1_decode(int(code))
+        want = float(val)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (code, got, want)
+
+
+def test_e2m1_sign_symmetry_and_monotone():
+    v = oracle.e2m1_decode(np.arange(16))
+    assert np.array_equal(v[8:], -v[:8])
+    assert np.all(np.diff(v[:8]) > 0)
+    assert np.array_equal(oracle.E2M1_MAGNITUDES, v[:8])
+
+
+# ---------------------------------------------------------------- E4M3
+
+def test_e4m3_named_values(golden_dir):
+    for hx, val in _read_table(os.path.join(golden_dir, "e4m3_facts.txt")):
+        got = float(oracle.e4m3_decode(int(hx, 16)))
+        if val == "nan":
+            assert math.isnan(got), hx
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), hx
+
+
+def test_e4m3_decode_exhaustive_vs_torch_cast():
+    b = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = b.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_decode(np.arange(256))
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+
+
+def test_e4m3_encode_roundtrip_all_finite_nonneg():
+    b = np.arange(127)
+    assert np.array_equal(oracle.e4m3_encode(oracle.e4m3_decode(b)), b)
+
+
+def test_e4m3_encode_midpoints_go_to_even():
+    t = oracle.e4m3_finite_table()
+    mids = (t[:-1] + t[1:]) / 2
+    enc = oracle.e4m3_encode(mids)
+    lo = np.arange(126)
+    want = np.where(lo % 2 == 0, lo, lo + 1)
+    assert np.array_equal(enc, want)
+    # just above / below a midpoint goes to the nearer neighbour
+    assert np.array_equal(oracle.e4m3_encode(np.nextafter(mids, np.inf)), lo + 1)
+    assert np.array_equal(oracle.e4m3_encode(np.nextafter(mids, -np.inf)), lo)
+
+
+def test_e4m3_encode_edges():
+    assert oracle.e4m3_encode(2.0 ** -10) == 0            # tie 0 | 2^-9 -> even (0)
+    assert oracle.e4m3_encode(np.nextafter(2.0 ** -10, 1)) == 1
+    assert oracle.e4m3_encode(448.0) == 0x7E
+    assert oracle.e4m3_encode(463.9) == 0x7E
+    assert oracle.e4m3_encode(1e6) == 0x7E                 # saturate
+    assert oracle.e4m3_encode(0.0) == 0
+
+
+def test_e4m3_encode_vs_torch_cast_random():
+    rs = np.random.default_rng(1)
+    v = np.concatenate([
+        rs.uniform(0, 448, 20000),
+        np.exp(rs.uniform(np.log(2.0 ** -12), np.log(448.0), 20000)),
+    ]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode(v.astype(np.float64))
+    assert np.array_equal(ref, got)
+
+
+# ---------------------------------------------------------------- NVFP4
+
+def _handworked(golden_dir):
+    out = []
+    with open(os.path.join(golden_dir, "nvfp4_handworked.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, vals, sb, cb = [p.strip() for p in line.split("|")]
+            v = [float.fromhex(t) if "0x" in t else float(t) for t in vals.split()]
+            out.append((name, np.array(v, dtype=np.float32), int(sb, 16),
+                        [int(c, 16) for c in cb.split()]))
+    return out
+
+
+def test_nvfp4_handworked_blocks(golden_dir):
+    blocks = _handworked(golden_dir)
+    assert len(blocks) == 7
+    for name, v, sb, cb in blocks:
+        assert np.all(v.astype(np.float64) == v)  # fixture values are fp32-exact or fp32-rounded
+        codes, scales = oracle.nvfp4_quantize(v[None, :])
+        assert scales[0, 0] == sb, (name, hex(scales[0, 0]))
+        assert list(codes[0]) == cb, (name, [hex(c) for c in codes[0]])
+    # the same blocks side by side in one row, and stacked in rows
+    V = np.concatenate([b[1] for b in blocks])[None, :]
+    codes, scales = oracle.nvfp4_quantize(V)
+    assert list(scales[0]) == [b[2] for b in blocks]
+    assert list(codes[0]) == sum((b[3] for b in blocks), [])
+    codes2, scales2 = oracle.nvfp4_quantize(np.stack([b[1] for b in blocks]))
+    assert list(scales2[:, 0]) == [b[2] for b in blocks]
+
+
+def _brute_force_check(w, codes, scales):
+    """Every element's code is a nearest E2M1 value times S (among all 16
+    codes), ties to an even mantissa, no negative zero; the scale is a nearest
+    E4M3 value to amax/6 (among all 127), ties to even."""
+    n, kin = w.shape
+    table = oracle.e4m3_finite_table()
+    vals16 = oracle.e2m1_decode(np.arange(16))
+    c = nvfp4_unpack_codes(codes)
+    for o in range(n):
+        for b in range(kin // 16):
+            blk = w[o, 16 * b:16 * b + 16].astype(np.float64)
+            t = np.abs(blk).max() / 6.0
+            d = np.abs(table - t)
+            best = np.nonzero(d == d.min())[0]
+            sb = int(scales[o, b])
+            assert sb in best
+            if len(best) == 2:
+                assert sb % 2 == 0
+            S = table[sb]
+            for i in range(16):
+                code = int(c[o, 16 * b + i])
+                if S == 0:
+                    assert code == 0
+                    continue
+                err = np.abs(blk[i] - vals16 * S)
+                cands = np.nonzero(err == err.min())[0]
+                assert code in cands, (o, b, i, blk[i], S, code, cands)
+                mags = set(int(x) & 7 for x in cands)
+                if len(mags) == 2:
+                    assert (code & 7) % 2 == 0
+                if code & 7 == 0:
+                    assert code == 0      # no negative zero
+
+
+def test_nvfp4_brute_force_random_blocks():
+    rs = np.random.default_rng(7)
+    w = (rs.standard_normal((24, 256)) * 0.02).astype(np.float32)
+    # crafted rows: exact midpoints times S, a lone nonzero, tiny blocks
+    w[0, :16] = np.float32(2.0 ** -7) * np.array([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5,
+                                                   -6, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5],
+                                                  dtype=np.float32)
+    w[1, :16] = 0
+    w[1, 16:32] = 0
+    w[1, 20] = np.float32(-0.013)
+    w[2, :16] = np.float32(1e-4) * rs.standard_normal(16).astype(np.float32)
+    w[3, :] = np.float32(100.0) * rs.standard_normal(256).astype(np.float32)
+    codes, scales = oracle.nvfp4_quantize(w)
+    _brute_force_check(w, codes, scales)
+
+
+def test_nvfp4_error_bound_invariant():
+    rs = np.random.default_rng(11)
+    w = (rs.standard_normal((64, 512)) * 0.02).astype(np.float32)
+    codes, scales = oracle.nvfp4_quantize(w)
+    deq = oracle.nvfp4_dequant(codes, scales)
+    S = np.repeat(oracle.e4m3_decode(scales), 16, axis=1)
+    mags = oracle.E2M1_MAGNITUDES
+    halfgap = np.max(np.diff(mags)) / 2         # 1.0 (between 4 and 6)
+    a = np.abs(w.astype(np.float64))
+    sat = a > 6 * S
+    err = np.abs(w - deq)
+    assert np.all(err[~sat] <= halfgap * S[~sat] + 0)
+    # saturated elements decode to +-6 S
+    assert np.all(np.abs(deq[sat]) == 6 * S[sat])
+    # sign agreement wherever the decoded value is nonzero
+    nz = deq != 0
+    assert np.all(np.sign(deq[nz]) == np.sign(w[nz]))
+
+
+def test_nvfp4_zero_blocks_and_zero_scale():
+    w = np.zeros((2, 32), dtype=np.float32)
+    w[1, 16:] = np.float32(3 * 2.0 ** -11)   # amax/6 = 2^-12 -> scale 0 -> all codes 0
+    codes, scales = oracle.nvfp4_quantize(w)
+    assert np.all(codes == 0) and np.all(scales == 0)
+    assert np.all(oracle.nvfp4_dequant(codes, scales) == 0)
+
+
+def test_nvfp4_products_exact_in_bf16_and_f16():
+    vals = oracle.e2m1_decode(np.arange(16))
+    sc = oracle.e4m3_finite_table()
+    prod = (vals[:, None] * sc[None, :]).reshape(-1)
+    as32 = prod.astype(np.float32)
+    assert np.array_equal(as32.astype(np.float64), prod)
+    bf = torch.from_numpy(as32).to(torch.bfloat16).to(torch.float64).numpy()
+    f16 = torch.from_numpy(as32).to(torch.float16).to(torch.float64).numpy()
+    assert np.array_equal(bf, prod)
+    assert np.array_equal(f16, prod)
+
+
+def test_nvfp4_rejects_bad_input():
+    with pytest.raises(ValueError):
+        oracle.nvfp4_quantize(np.zeros((2, 24), np.float32))
+    w = np.zeros((1, 16), np.float32)
+    w[0, 3] = np.nan
+    with pytest.raises(ValueError):
+        oracle.nvfp4_quantize(w)
+
+
+# ---------------------------------------------------------------- VQ
+
+def _f16(x):
+    return np.asarray(x, dtype=np.float16).view(np.uint16)
+
+
+def test_vq_codebook_identity_recovers_codes():
+    ncode = 65536
+    c = np.arange(ncode)
+    cb = np.zeros((ncode, 8), dtype=np.float64)
+    cb[:, 0] = c >> 8
+    cb[:, 1] = c & 255
+    cb[:, 2:] = np.arange(2, 8)[None, :]
+    rs = np.random.default_rng(3)
+    codes = rs.integers(0, ncode, size=(5, 12), dtype=np.uint16)
+    W = oracle.vq_dequant(codes, _f16(np.ones(5)), _f16(cb))
+    Wg = W.reshape(5, 12, 8)
+    rec = (Wg[:, :, 0] * 256 + Wg[:, :, 1]).astype(np.int64)
+    assert np.array_equal(rec, codes.astype(np.int64))
+    assert np.all(Wg[:, :, 2:] == np.arange(2, 8)[None, None, :])
+
+
+def test_vq_power_of_two_scales_shift_rows():
+    rs = np.random.default_rng(5)
+    cb = _f16(rs.standard_normal((256, 8)) * 0.02)
+    codes = rs.integers(0, 256, size=(6, 4), dtype=np.uint16)
+    p = np.array([-3, -1, 0, 1, 2, 5])
+    W = oracle.vq_dequant(codes, _f16(2.0 ** p), cb)
+    C = cb.view(np.float16).astype(np.float64)
+    for o in range(6):
+        for g in range(4):
+            assert np.array_equal(W[o, 8 * g:8 * g + 8], np.ldexp(C[codes[o, g]], p[o]))
+
+
+def test_vq_one_hot_codebook_rows():
+    cb = np.zeros((16, 8))
+    for r in range(16):
+        cb[r, r % 8] = r + 1
+    codes = np.array([[3, 11, 0]], dtype=np.uint16)
+    W = oracle.vq_dequant(codes, _f16([0.5]), _f16(cb))
+    want = np.zeros(24)
+    want[0 + 3] = 2.0
+    want[8 + 3] = 6.0
+    want[16 + 0] = 0.5
+    assert np.array_equal(W[0], want)
+
+
+def test_vq_product_exact_in_fp32():
+    rs = np.random.default_rng(9)
+    cb = _f16(rs.standard_normal((4096, 8)) * 0.02)
+    sc = _f16(rs.uniform(0.5, 1.5, 64))
+    codes = rs.integers(0, 4096, size=(64, 32), dtype=np.uint16)
+    W = oracle.vq_dequant(codes, sc, cb)
+    assert np.array_equal(W.astype(np.float32).astype(np.float64), W)
