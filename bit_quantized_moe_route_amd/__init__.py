@@ -1,0 +1,362 @@
+"""Python binding of libmoeq (the routed-expert MoE forward over NVFP4 / VQ
+expert weights for MI355X).
+
+Argument marshalling only: every step of the forward runs in the library's
+HIP kernels.  PyTorch is used for device memory and the current stream.  If
+libmoeq.so has not been built, every call raises -- there is no fallback.
+
+Calls (same names as the C ABI in include/moeq.h):
+    route_topk(logits, k)                       -> topk_ids, topk_w
+    permute(topk_ids, E)                        -> counts, offsets, perm_src, inv_perm
+    expert_ffn_q(layer, x, perm_src, offsets, k) -> y_perm
+    combine(y_perm, inv_perm, topk_w)           -> out
+    forward(layer, x, logits, k)                -> all of the above
+Host packers: quantize_nvfp4, pack_nvfp4_expert, pack_vq_expert,
+record_bytes, record_table.  Test hook: dequant_q.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoeq.so")
+
+MOE_OK = 0
+MOE_EINVAL = -1
+MOE_EUNSUPPORTED = -2
+MOE_EWORKSPACE = -3
+MOE_EHIP = -4
+
+FMT_NVFP4 = 1
+FMT_VQ = 2
+PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
+VQ_NCODE = 65536
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, fn, detail):
+        self.status = status
+        super().__init__(f"{fn}: status {status}: {detail}")
+
+
+class _QLayerC(ctypes.Structure):
+    _fields_ = [
+        ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("fmt_host", ctypes.c_void_p),
+        ("rec_dev", ctypes.c_void_p),
+        ("nvfp4_w13", ctypes.c_void_p), ("nvfp4_w13_stride", ctypes.c_int64),
+        ("nvfp4_w2", ctypes.c_void_p), ("nvfp4_w2_stride", ctypes.c_int64),
+        ("vq_w13", ctypes.c_void_p), ("vq_w13_stride", ctypes.c_int64),
+        ("vq_w2", ctypes.c_void_p), ("vq_w2_stride", ctypes.c_int64),
+        ("vq_codebook", ctypes.c_void_p * 3),
+        ("vq_codebook_stride", ctypes.c_int64),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_PROTOS = {
+    "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_route_topk": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
+    "moe_permute_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_ffn_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64, _I32]),
+    "moe_expert_ffn_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _P, _I64, _I32, _P,
+                                        _P, _SZ, _P]),
+    "moe_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_quantize_nvfp4": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
+    "moe_record_bytes": (_SZ, [ctypes.c_int, ctypes.c_int, _I32, _I32]),
+    "moe_pack_nvfp4_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
+    "moe_pack_vq_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
+    "moe_record_table": (ctypes.c_int, [_P, _I32, _P, _P, _P]),
+    "moe_dequant_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _I32, _I32, _P, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoeq (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m bit_quantized_moe_route_amd.build` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status, fn):
+    if status != MOE_OK:
+        L = lib()
+        detail = L.moe_last_error().decode() or L.moe_strerror(status).decode()
+        raise MoeError(status, fn, detail)
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------
+# host packers (numpy in, numpy out)
+# --------------------------------------------------------------------------
+
+def quantize_nvfp4(w):
+    """fp32 [n, kin] -> (codes uint8 [n, kin/2], scales uint8 [n, kin/16])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, kin = w.shape
+    codes = np.empty((n, kin // 2), np.uint8)
+    scales = np.empty((n, max(kin // 16, 0)), np.uint8)
+    _check(lib().moe_quantize_nvfp4(_np_ptr(w), n, kin, _np_ptr(codes), _np_ptr(scales)),
+           "moe_quantize_nvfp4")
+    return codes, scales
+
+
+def record_bytes(fmt, which, H, I):
+    return int(lib().moe_record_bytes(fmt, which, H, I))
+
+
+def pack_nvfp4_expert(gate, up, down, H, I, w13=None, w2=None):
+    """gate/up/down = (codes, scales) canonical NVFP4 -> (w13 record, w2 record)."""
+    if w13 is None:
+        w13 = np.empty(record_bytes(FMT_NVFP4, 0, H, I), np.uint8)
+    if w2 is None:
+        w2 = np.empty(record_bytes(FMT_NVFP4, 1, H, I), np.uint8)
+    arrs = [np.ascontiguousarray(a, dtype=np.uint8) for pair in (gate, up, down) for a in pair]
+    _check(lib().moe_pack_nvfp4_expert(*[_np_ptr(a) for a in arrs], H, I, _np_ptr(w13),
+                                       _np_ptr(w2)), "moe_pack_nvfp4_expert")
+    return w13, w2
+
+
+def pack_vq_expert(gate, up, down, H, I, w13=None, w2=None):
+    """gate/up/down = (codes uint16 [n, kin/8], scales fp16 bits uint16 [n])."""
+    if w13 is None:
+        w13 = np.empty(record_bytes(FMT_VQ, 0, H, I), np.uint8)
+    if w2 is None:
+        w2 = np.empty(record_bytes(FMT_VQ, 1, H, I), np.uint8)
+    arrs = [np.ascontiguousarray(a, dtype=np.uint16) for pair in (gate, up, down) for a in pair]
+    _check(lib().moe_pack_vq_expert(*[_np_ptr(a) for a in arrs], H, I, _np_ptr(w13), _np_ptr(w2)),
+           "moe_pack_vq_expert")
+    return w13, w2
+
+
+def record_table(fmt_host):
+    fmt_host = np.ascontiguousarray(fmt_host, dtype=np.uint8)
+    E = fmt_host.shape[0]
+    rec = np.empty(E, np.int32)
+    nn, nv = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().moe_record_table(_np_ptr(fmt_host), E, _np_ptr(rec), ctypes.byref(nn),
+                                  ctypes.byref(nv)), "moe_record_table")
+    return rec, nn.value, nv.value
+
+
+# --------------------------------------------------------------------------
+# device calls (torch tensors for memory and the current stream)
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(dev=None):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("device tensors required")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("contiguous tensors required")
+
+
+class QLayer:
+    """A packed expert layer resident on one GPU.
+
+    Holds the device pools, the record table and the codebooks, and the C
+    descriptor that points at them.  Build it with `QLayer.build(...)`.
+    """
+
+    def __init__(self, E, H, I, fmt_host, device="cuda"):
+        torch = _torch()
+        self.E, self.H, self.I = int(E), int(H), int(I)
+        self.fmt_host = np.ascontiguousarray(fmt_host, dtype=np.uint8)
+        rec, self.n_nvfp4, self.n_vq = record_table(self.fmt_host)
+        self.rec_host = rec
+        self.device = torch.device(device)
+        self.rec_dev = torch.from_numpy(rec).to(self.device)
+        self.stride = {}
+        self.pools = {}
+        for fmt, n in ((FMT_NVFP4, self.n_nvfp4), (FMT_VQ, self.n_vq)):
+            for which in (0, 1):
+                b = record_bytes(fmt, which, H, I)
+                s = (b + 255) // 256 * 256
+                self.stride[(fmt, which)] = s
+                self.pools[(fmt, which)] = (torch.empty(n * s, dtype=torch.uint8, device=self.device)
+                                            if n else None)
+        self.codebooks = [None, None, None]
+        self.codebook_stride = 0
+        self._c = None
+
+    def record_index(self, e):
+        return int(self.rec_host[e] & 0xFFFFFF)
+
+    def set_record(self, e, w13, w2, stream=None):
+        """Copy one expert's two host records (numpy uint8) into its pool slots."""
+        torch = _torch()
+        fmt = int(self.fmt_host[e])
+        idx = self.record_index(e)
+        for which, rec in ((0, w13), (1, w2)):
+            s = self.stride[(fmt, which)]
+            dst = self.pools[(fmt, which)][idx * s: idx * s + rec.shape[0]]
+            dst.copy_(torch.from_numpy(np.ascontiguousarray(rec)), non_blocking=False)
+        self._c = None
+
+    def set_codebooks(self, cbs, stride=0):
+        """cbs: three uint16 arrays [n_vq_books * 65536, 8] (fp16 bits) for gate,
+        up, down; stride = bytes between per-record codebooks (0 = shared)."""
+        torch = _torch()
+        self.codebooks = [torch.from_numpy(np.ascontiguousarray(c, dtype=np.uint16).view(np.int16))
+                          .to(self.device) for c in cbs]
+        self.codebook_stride = int(stride)
+        self._c = None
+
+    def c(self):
+        if self._c is None:
+            d = _QLayerC()
+            d.E, d.H, d.I = self.E, self.H, self.I
+            d.fmt_host = self.fmt_host.ctypes.data
+            d.rec_dev = self.rec_dev.data_ptr()
+            for fmt, n13, n2 in ((FMT_NVFP4, "nvfp4_w13", "nvfp4_w2"), (FMT_VQ, "vq_w13", "vq_w2")):
+                p13, p2 = self.pools[(fmt, 0)], self.pools[(fmt, 1)]
+                setattr(d, n13, p13.data_ptr() if p13 is not None else None)
+                setattr(d, n2, p2.data_ptr() if p2 is not None else None)
+                setattr(d, n13 + "_stride", self.stride[(fmt, 0)])
+                setattr(d, n2 + "_stride", self.stride[(fmt, 1)])
+            for p in range(3):
+                cb = self.codebooks[p]
+                d.vq_codebook[p] = cb.data_ptr() if cb is not None else None
+            d.vq_codebook_stride = self.codebook_stride
+            self._c = d
+        return self._c
+
+    def packed_bytes(self, experts):
+        """Codes + scales bytes of the given experts (each counted once), plus
+        each codebook once if a VQ expert is among them: the bytes a forward
+        over those experts must read."""
+        tot = 0
+        vq = False
+        for e in set(int(x) for x in experts):
+            if self.fmt_host[e] == FMT_NVFP4:
+                tot += 3 * (self.H * self.I // 2 + self.H * self.I // 16)
+            else:
+                vq = True
+                tot += 3 * (self.H * self.I // 8) * 2 + (2 * self.I + self.H) * 2
+        if vq and self.codebook_stride == 0:
+            tot += 3 * VQ_NCODE * 8 * 2
+        return tot
+
+
+def route_topk(logits, k, topk_ids=None, topk_w=None):
+    torch = _torch()
+    _need_cuda(logits)
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route_topk(_dptr(logits), T, E, k, _dptr(topk_ids), _dptr(topk_w),
+                                _stream(logits.device)), "moe_route_topk")
+    return topk_ids, topk_w
+
+
+def permute(topk_ids, E, out=None):
+    torch = _torch()
+    _need_cuda(topk_ids)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    if out is None:
+        out = (torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev))
+    counts, offsets, perm_src, inv_perm = out
+    L = lib()
+    nws = L.moe_permute_workspace_bytes(T, k, E)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
+    _check(L.moe_permute(_dptr(topk_ids), T, k, E, _dptr(counts), _dptr(offsets),
+                         _dptr(perm_src), _dptr(inv_perm), _dptr(ws), nws, _stream(dev)),
+           "moe_permute")
+    return counts, offsets, perm_src, inv_perm
+
+
+def ffn_workspace(layer, T, k):
+    torch = _torch()
+    n = lib().moe_ffn_workspace_bytes(ctypes.byref(layer.c()), T, k)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=layer.device)
+
+
+def expert_ffn_q(layer, x, perm_src, offsets, k, y_perm=None, ws=None):
+    """x: bf16 [T, H] tensor (or int16/uint16 holding bf16 bits)."""
+    torch = _torch()
+    _need_cuda(x, perm_src, offsets)
+    T, H = x.shape
+    if y_perm is None:
+        y_perm = torch.empty((T * k, layer.H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = ffn_workspace(layer, T, k)
+    _check(lib().moe_expert_ffn_q(ctypes.byref(layer.c()), _dptr(x), _dptr(perm_src),
+                                  _dptr(offsets), T, k, _dptr(y_perm), _dptr(ws), ws.numel(),
+                                  _stream(x.device)), "moe_expert_ffn_q")
+    return y_perm
+
+
+def combine(y_perm, inv_perm, topk_w, out=None):
+    torch = _torch()
+    _need_cuda(y_perm, inv_perm, topk_w)
+    T, k = topk_w.shape
+    H = y_perm.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=y_perm.device)
+    _check(lib().moe_combine(_dptr(y_perm), _dptr(inv_perm), _dptr(topk_w), T, k, H, _dptr(out),
+                             _stream(y_perm.device)), "moe_combine")
+    return out
+
+
+def dequant_q(layer, expert, proj):
+    torch = _torch()
+    n, kin = (layer.H, layer.I) if proj == PROJ_DOWN else (layer.I, layer.H)
+    out = torch.empty((n, kin), dtype=torch.float32, device=layer.device)
+    _check(lib().moe_dequant_q(ctypes.byref(layer.c()), expert, proj, _dptr(out),
+                               _stream(layer.device)), "moe_dequant_q")
+    return out
+
+
+def forward(layer, x, logits, k):
+    """route -> permute -> expert FFN -> combine.  Returns a dict of every
+    intermediate (device tensors)."""
+    ids, w = route_topk(logits, k)
+    counts, offsets, perm_src, inv_perm = permute(ids, layer.E)
+    y_perm = expert_ffn_q(layer, x, perm_src, offsets, k)
+    out = combine(y_perm, inv_perm, w)
+    return dict(topk_ids=ids, topk_w=w, counts=counts, offsets=offsets, perm_src=perm_src,
+                inv_perm=inv_perm, y_perm=y_perm, out=out)

@@ -1,0 +1,218 @@
+// C ABI: argument checks, workspace layout and dispatch to the HIP launchers.
+#include <cstdint>
+#include <string>
+
+#include "internal.h"
+
+namespace moeq {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int status, const std::string& msg) {
+    g_last_error = msg;
+    return status;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int check_route_sizes(const char* fn, int64_t T, int32_t E, int32_t k) {
+    if (T < 0) return fail(MOE_EINVAL, std::string(fn) + ": T < 0");
+    if (E < 1 || E > MOE_MAX_E)
+        return fail(MOE_EINVAL, std::string(fn) + ": E must be in [1, " + std::to_string(MOE_MAX_E) + "]");
+    if (k < 1 || k > E || k > MOE_MAX_K)
+        return fail(MOE_EINVAL, std::string(fn) + ": k must be in [1, min(E, " +
+                                    std::to_string(MOE_MAX_K) + ")]");
+    if (T * (int64_t)k >= (int64_t)1 << 31) return fail(MOE_EINVAL, std::string(fn) + ": T*k too large");
+    return MOE_OK;
+}
+
+struct LayerInfo {
+    LayerView view;
+    int32_t count[3];
+};
+
+// Validate a layer descriptor; fill the device view and per-format counts.
+int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
+    const std::string f(fn);
+    if (!L) return fail(MOE_EINVAL, f + ": layer is NULL");
+    if (L->E < 1 || L->E > MOE_MAX_E) return fail(MOE_EINVAL, f + ": bad E");
+    if (L->H <= 0 || L->I <= 0) return fail(MOE_EINVAL, f + ": bad H or I");
+    if (!L->fmt_host || !L->rec_dev) return fail(MOE_EINVAL, f + ": fmt_host / rec_dev is NULL");
+    out.count[0] = out.count[1] = out.count[2] = 0;
+    for (int e = 0; e < L->E; ++e) {
+        const int t = L->fmt_host[e];
+        if (t != MOE_FMT_NVFP4 && t != MOE_FMT_VQ)
+            return fail(MOE_EUNSUPPORTED, f + ": expert " + std::to_string(e) +
+                                              " has format tag " + std::to_string(t) +
+                                              ", which this library does not decode");
+        out.count[t]++;
+    }
+    if (L->H % 16 || L->I % 16)
+        return fail(MOE_EUNSUPPORTED, f + ": H and I must be multiples of 16");
+    LayerView& v = out.view;
+    v.E = L->E;
+    v.H = L->H;
+    v.I = L->I;
+    v.rec = L->rec_dev;
+    v.pool13[0] = v.pool2[0] = nullptr;
+    v.stride13[0] = v.stride2[0] = 0;
+    v.pool13[MOE_FMT_NVFP4] = static_cast<const uint8_t*>(L->nvfp4_w13);
+    v.pool2[MOE_FMT_NVFP4] = static_cast<const uint8_t*>(L->nvfp4_w2);
+    v.stride13[MOE_FMT_NVFP4] = L->nvfp4_w13_stride;
+    v.stride2[MOE_FMT_NVFP4] = L->nvfp4_w2_stride;
+    v.pool13[MOE_FMT_VQ] = static_cast<const uint8_t*>(L->vq_w13);
+    v.pool2[MOE_FMT_VQ] = static_cast<const uint8_t*>(L->vq_w2);
+    v.stride13[MOE_FMT_VQ] = L->vq_w13_stride;
+    v.stride2[MOE_FMT_VQ] = L->vq_w2_stride;
+    for (int p = 0; p < 3; ++p) v.cb[p] = static_cast<const uint8_t*>(L->vq_codebook[p]);
+    v.cb_stride = L->vq_codebook_stride;
+    for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
+        if (!out.count[fmt]) continue;
+        const char* name = fmt == MOE_FMT_NVFP4 ? "NVFP4" : "VQ";
+        if (!v.pool13[fmt] || !v.pool2[fmt])
+            return fail(MOE_EINVAL, f + ": " + name + " experts present but their pool is NULL");
+        const int64_t b13 = (int64_t)moe_record_bytes(fmt, 0, L->H, L->I);
+        const int64_t b2 = (int64_t)moe_record_bytes(fmt, 1, L->H, L->I);
+        if (v.stride13[fmt] < b13 || v.stride2[fmt] < b2 || v.stride13[fmt] % 256 ||
+            v.stride2[fmt] % 256)
+            return fail(MOE_EINVAL, f + ": " + name +
+                                        " record stride smaller than moe_record_bytes() or not a "
+                                        "multiple of 256");
+    }
+    if (out.count[MOE_FMT_VQ]) {
+        for (int p = 0; p < 3; ++p)
+            if (!v.cb[p]) return fail(MOE_EINVAL, f + ": VQ experts present but a codebook is NULL");
+        if (v.cb_stride < 0 || (v.cb_stride && v.cb_stride < (int64_t)MOE_VQ_NCODE * 16))
+            return fail(MOE_EINVAL, f + ": bad vq_codebook_stride");
+    }
+    return MOE_OK;
+}
+
+size_t ffn_ws(const moe_qlayer* L, int64_t T, int32_t k) {
+    return align_up((size_t)T * L->H * 2) + align_up((size_t)T * k * L->I * 2);
+}
+
+}  // namespace
+
+}  // namespace moeq
+
+using namespace moeq;
+
+extern "C" {
+
+const char* moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "success";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_EUNSUPPORTED: return "unsupported format or shape (failed closed)";
+        case MOE_EWORKSPACE: return "workspace too small";
+        case MOE_EHIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                   float* topk_w, void* stream) {
+    g_last_error.clear();
+    int st = check_route_sizes("moe_route_topk", T, E, k);
+    if (st) return st;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w) return fail(MOE_EINVAL, "moe_route_topk: null pointer");
+    return launch_route_topk(logits, T, E, k, topk_ids, topk_w, stream);
+}
+
+size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E) {
+    if (T < 0 || k < 1 || E < 1) return 0;
+    return permute_ws_bytes(T, k, E);
+}
+
+int moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
+                int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, void* ws,
+                size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    int st = check_route_sizes("moe_permute", T, E, k);
+    if (st) return st;
+    if (!counts || !offsets) return fail(MOE_EINVAL, "moe_permute: null pointer");
+    const size_t need = permute_ws_bytes(T, k, E);
+    if (need && (!ws || ws_bytes < need))
+        return fail(MOE_EWORKSPACE, "moe_permute: workspace needs " + std::to_string(need) + " bytes");
+    if (T > 0 && (!topk_ids || !perm_src || !inv_perm))
+        return fail(MOE_EINVAL, "moe_permute: null pointer");
+    // T == 0 still writes counts = 0 and offsets = 0 (one tiny launch)
+    return launch_permute(topk_ids, T, k, E, counts, offsets, perm_src, inv_perm, ws, stream);
+}
+
+size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k) {
+    if (!layer || T < 0 || k < 1 || layer->H <= 0 || layer->I <= 0) return 0;
+    return ffn_ws(layer, T, k);
+}
+
+int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16, const int32_t* perm_src,
+                     const int32_t* offsets, int64_t T, int32_t k, float* y_perm, void* ws,
+                     size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    LayerInfo li;
+    int st = check_layer("moe_expert_ffn_q", layer, li);
+    if (st) return st;
+    st = check_route_sizes("moe_expert_ffn_q", T, layer->E, k);
+    if (st) return st;
+    if (T == 0) return MOE_OK;
+    if (!x_bf16 || !perm_src || !offsets || !y_perm)
+        return fail(MOE_EINVAL, "moe_expert_ffn_q: null pointer");
+    const size_t need = ffn_ws(layer, T, k);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_EWORKSPACE,
+                    "moe_expert_ffn_q: workspace needs " + std::to_string(need) + " bytes");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+        return fail(MOE_EINVAL, "moe_expert_ffn_q: workspace must be 256-byte aligned");
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    uint16_t* x16 = reinterpret_cast<uint16_t*>(w);
+    uint16_t* h16 = reinterpret_cast<uint16_t*>(w + align_up((size_t)T * layer->H * 2));
+    st = launch_x_to_f16(x_bf16, T * layer->H, x16, stream);
+    if (st) return st;
+    for (int phase = 0; phase < 2; ++phase) {
+        for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
+            if (!li.count[fmt]) continue;
+            st = launch_ffn_decode(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T, k, h16,
+                                   y_perm, phase, stream);
+            if (st) return st;
+        }
+    }
+    return MOE_OK;
+}
+
+int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T,
+                int32_t k, int32_t H, float* out, void* stream) {
+    g_last_error.clear();
+    if (T < 0 || k < 1 || k > MOE_MAX_K || H <= 0 || H % 4)
+        return fail(MOE_EINVAL, "moe_combine: need T >= 0, 1 <= k <= 16, H > 0, H % 4 == 0");
+    if (T == 0) return MOE_OK;
+    if (!y_perm || !inv_perm || !topk_w || !out) return fail(MOE_EINVAL, "moe_combine: null pointer");
+    return launch_combine(y_perm, inv_perm, topk_w, T, k, H, out, stream);
+}
+
+int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj, float* out,
+                  void* stream) {
+    g_last_error.clear();
+    LayerInfo li;
+    int st = check_layer("moe_dequant_q", layer, li);
+    if (st) return st;
+    if (expert < 0 || expert >= layer->E) return fail(MOE_EINVAL, "moe_dequant_q: bad expert");
+    if (proj < MOE_PROJ_GATE || proj > MOE_PROJ_DOWN) return fail(MOE_EINVAL, "moe_dequant_q: bad proj");
+    if (!out) return fail(MOE_EINVAL, "moe_dequant_q: out is NULL");
+    // the record index of this expert within its format's pool (host-side)
+    const int fmt = layer->fmt_host[expert];
+    int32_t ridx = 0;
+    for (int e = 0; e < expert; ++e) ridx += layer->fmt_host[e] == fmt;
+    return launch_dequant(li.view, fmt, ridx, proj, out, stream);
+}
+
+}  // extern "C"

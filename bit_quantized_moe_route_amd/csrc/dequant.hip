@@ -1,0 +1,90 @@
+// Test hook: decode one projection of one expert from its device record to
+// fp32 with the same decode routines as the FFN kernels.  Every decoded value
+// is exact (NVFP4: an E2M1 value times an E4M3 scale, exact in fp16; VQ: an
+// fp16 codebook entry times an fp16 scale, exact in fp32), so the output can
+// be compared bit for bit with a plain decode of the canonical bytes.
+#include "dev_common.h"
+
+namespace moeq {
+
+namespace {
+
+// one wave per tile; grid.x = row groups of the projection, grid.y = tiles
+// along the input dimension
+__global__ __launch_bounds__(64) void k_dequant_nv(const uint8_t* __restrict__ rec, int rg_step,
+                                                   int rg_off, int n, int kin,
+                                                   float* __restrict__ out) {
+    const int lane = threadIdx.x;
+    const int g = blockIdx.x;
+    const int kb = blockIdx.y;
+    const int nkb = gridDim.y;
+    const uint8_t* tile = rec + ((int64_t)(g * rg_step + rg_off) * nkb + kb) * kNvTileBytes;
+    NvFrag f = nv_load(tile, lane);
+    f16x8 a[4];
+    nv_decode(f, a);
+    const int row = 16 * g + (lane & 15);
+    const int k0 = kb * kNvTileK + (lane >> 4) * 32;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = k0 + 8 * s + i;
+            if (row < n && k < kin) out[(int64_t)row * kin + k] = (float)a[s][i];
+        }
+}
+
+__global__ __launch_bounds__(64) void k_dequant_vq(const uint8_t* __restrict__ rec, int rg_step,
+                                                   int rg_off, int n, int kin,
+                                                   const uint8_t* __restrict__ cb,
+                                                   const _Float16* __restrict__ scales,
+                                                   float* __restrict__ out) {
+    const int lane = threadIdx.x;
+    const int g = blockIdx.x;
+    const int kb = blockIdx.y;
+    const int nkb = gridDim.y;
+    const uint8_t* tile = rec + ((int64_t)(g * rg_step + rg_off) * nkb + kb) * kVqTileBytes;
+    u32x4 codes = *reinterpret_cast<const u32x4*>(tile + lane * 16);
+    const int row = 16 * g + (lane & 15);
+    const int k0 = kb * kVqTileK + (lane >> 4) * 64;
+    const float sc = row < n ? (float)scales[row] : 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        uint32_t c = (codes[s >> 1] >> (16 * (s & 1))) & 0xffffu;
+        f16x8 a = vq_row(cb, c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = k0 + 8 * s + i;
+            if (row < n && k < kin) out[(int64_t)row * kin + k] = sc * (float)a[i];
+        }
+    }
+}
+
+}  // namespace
+
+int launch_dequant(const LayerView& L, int fmt, int32_t ridx, int32_t proj, float* out,
+                   void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool down = proj == MOE_PROJ_DOWN;
+    const int n = down ? L.H : L.I;
+    const int kin = down ? L.I : L.H;
+    const int rg_step = down ? 1 : 2;
+    const int rg_off = proj == MOE_PROJ_UP ? 1 : 0;
+    const uint8_t* rec = down ? L.pool2[fmt] + (int64_t)ridx * L.stride2[fmt]
+                              : L.pool13[fmt] + (int64_t)ridx * L.stride13[fmt];
+    if (fmt == MOE_FMT_NVFP4) {
+        dim3 grid((unsigned)(n / 16), (unsigned)nv_tiles_k(kin));
+        k_dequant_nv<<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, out);
+    } else {
+        const int64_t nkb = vq_tiles_k(kin);
+        const int groups = down ? L.H / 16 : 2 * (L.I / 16);
+        const _Float16* sc = reinterpret_cast<const _Float16*>(rec + (int64_t)groups * nkb * kVqTileBytes);
+        if (proj == MOE_PROJ_UP) sc += L.I;
+        const uint8_t* cb = L.cb[proj] + (int64_t)ridx * L.cb_stride;
+        dim3 grid((unsigned)(n / 16), (unsigned)nkb);
+        k_dequant_vq<<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, cb, sc, out);
+    }
+    MOEQ_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+}  // namespace moeq

@@ -1,0 +1,118 @@
+// Device-side helpers shared by the HIP kernels: vector types, the NVFP4 and
+// VQ decode routines and the 16x16x32 fp16 MFMA wrapper.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace moeq {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define MOEQ_CHECK_LAUNCH()                                                   \
+    do {                                                                      \
+        hipError_t _e = hipGetLastError();                                    \
+        if (_e != hipSuccess)                                                 \
+            return ::moeq::fail(MOE_EHIP, std::string("HIP launch: ") +       \
+                                              hipGetErrorString(_e));         \
+    } while (0)
+
+// D += A * B over one 16x16x32 fp16 tile (fp32 accumulate).
+// Lane L holds A[row L&15][k (L>>4)*8 + 0..7], B[k (L>>4)*8 + 0..7][col L&15],
+// D[row (L>>4)*4 + i][col L&15], i = 0..3.
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- NVFP4
+// The two E4M3 scale bytes of a lane (low byte = first 16 inputs), decoded to
+// fp16 and broadcast to pairs.  E4M3 -> fp16 is exact (every E4M3 value is a
+// normal fp16).
+__device__ __forceinline__ void nv_scales(uint32_t two_bytes, f16x2& s0, f16x2& s1) {
+    f16x2 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two_bytes, 1.0f, false);
+    s0 = f16x2{s[0], s[0]};
+    s1 = f16x2{s[1], s[1]};
+}
+
+// Eight weights from four code bytes (element 2i in the low nibble of byte i)
+// times their block scale.  The E2M1 -> fp16 conversion is exact, and so is
+// the fp16 product: an E2M1 value (2 significant bits) times an E4M3 scale
+// (4 bits) has at most 6 significant bits and lies in [2^-10, 2688].  (The
+// scale operand of the conversion instruction only takes a power of two, so
+// the scale is applied with a packed fp16 multiply.)
+__device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, f16x2 s) {
+    f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+    f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+    f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+    f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// One lane's 32 decoded weights of an NVFP4 tile: a[s] covers inputs
+// (L>>4)*32 + 8s + 0..7 of the tile, s = 0..3.
+struct NvFrag {
+    u32x4 codes;
+    uint32_t scales;
+};
+
+__device__ __forceinline__ NvFrag nv_load(const uint8_t* tile, int lane) {
+    NvFrag f;
+    f.codes = *reinterpret_cast<const u32x4*>(tile + lane * 16);
+    f.scales = *reinterpret_cast<const uint16_t*>(tile + kNvScaleOff + lane * 2);
+    return f;
+}
+
+__device__ __forceinline__ void nv_decode(const NvFrag& f, f16x8 a[4]) {
+    f16x2 s0, s1;
+    nv_scales(f.scales, s0, s1);
+    a[0] = nv_dequant8(f.codes[0], s0);
+    a[1] = nv_dequant8(f.codes[1], s0);
+    a[2] = nv_dequant8(f.codes[2], s1);
+    a[3] = nv_dequant8(f.codes[3], s1);
+}
+
+// ---------------------------------------------------------------- VQ
+// Codebook row of a uint16 code: 8 fp16 values (16 bytes).
+__device__ __forceinline__ f16x8 vq_row(const uint8_t* cb, uint32_t code) {
+    return *reinterpret_cast<const f16x8*>(cb + (size_t)code * 16);
+}
+
+// Non-temporal 16-byte load for streamed weight bytes (read once per call),
+// so they do not push the shared VQ codebooks out of the caches.
+__device__ __forceinline__ u32x4 load_stream16(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// ---------------------------------------------------------------- experts
+// The s-th expert (ascending id) with at least one assignment and format
+// `fmt`, or -1.  Every lane of the wave gets the same answer.
+__device__ __forceinline__ int find_active_expert(const int32_t* __restrict__ offsets,
+                                                  const int32_t* __restrict__ rec,
+                                                  int E, int fmt, int s, int lane) {
+    int seen = 0;
+    for (int base = 0; base < E; base += 64) {
+        int e = base + lane;
+        bool act = false;
+        if (e < E) {
+            int c = offsets[e + 1] - offsets[e];
+            act = c > 0 && (rec[e] >> 24) == fmt;
+        }
+        uint64_t m = __ballot(act);
+        int n = __popcll(m);
+        if (s < seen + n) {
+            int want = s - seen;   // index of the wanted set bit
+            for (int i = 0; i < want; ++i) m &= m - 1;
+            return base + __ffsll((unsigned long long)m) - 1;
+        }
+        seen += n;
+    }
+    return -1;
+}
+
+}  // namespace moeq

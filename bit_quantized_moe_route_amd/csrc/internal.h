@@ -1,0 +1,77 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "moeq.h"
+
+namespace moeq {
+
+// Per-thread detail of the last rejected call (read by moe_last_error).
+void set_error(const std::string& msg);
+int fail(int status, const std::string& msg);
+
+// Record geometry ------------------------------------------------------------
+//
+// NVFP4 tile: 16 rows x 128 inputs = 1024 code bytes + 128 scale bytes.
+//   code bytes: lane L (0..63) owns bytes [16L, 16L+16): row (L & 15),
+//     inputs kb*128 + (L >> 4)*32 + [0, 32), canonical nibble order.
+//   scale bytes: lane L owns bytes 1024 + [2L, 2L+2): the two E4M3 scales of
+//     those 32 inputs.
+// VQ tile: 16 rows x 256 inputs = 1024 code bytes.
+//   lane L owns bytes [16L, 16L+16) = 8 uint16 codes: row (L & 15), groups
+//     covering inputs kb*256 + (L >> 4)*64 + 8s + [0, 8), s = 0..7.
+// A record is a sequence of row groups of 16 rows, each a sequence of tiles
+// along the input dimension (padded with zero codes/scales).  Gate/up
+// records interleave row groups: group 2j = gate rows 16j.., 2j+1 = up rows.
+// VQ records end with the fp16 per-row scales (gate, up / down), padded to
+// 256 bytes.
+constexpr int kNvTileK = 128;
+constexpr int kNvTileBytes = 1152;
+constexpr int kNvScaleOff = 1024;
+constexpr int kVqTileK = 256;
+constexpr int kVqTileBytes = 1024;
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+inline int64_t nv_tiles_k(int32_t kin) { return round_up(kin, kNvTileK) / kNvTileK; }
+inline int64_t vq_tiles_k(int32_t kin) { return round_up(kin, kVqTileK) / kVqTileK; }
+
+inline int64_t nv_matrix_bytes(int32_t n, int32_t kin) {
+    return (int64_t)(n / 16) * nv_tiles_k(kin) * kNvTileBytes;
+}
+inline int64_t vq_codes_bytes(int32_t n, int32_t kin) {
+    return (int64_t)(n / 16) * vq_tiles_k(kin) * kVqTileBytes;
+}
+
+// Launchers (device code lives in the .hip files) ----------------------------
+struct LayerView {
+    int32_t E, H, I;
+    const int32_t* rec;
+    const uint8_t* pool13[3];   // indexed by format tag (1, 2)
+    const uint8_t* pool2[3];
+    int64_t stride13[3];
+    int64_t stride2[3];
+    const uint8_t* cb[3];       // VQ codebooks gate, up, down
+    int64_t cb_stride;
+};
+
+int launch_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                      int32_t* ids, float* w, void* stream);
+int launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
+                   int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                   int32_t* inv_perm, void* ws, void* stream);
+size_t permute_ws_bytes(int64_t T, int32_t k, int32_t E);
+int launch_combine(const float* y_perm, const int32_t* inv_perm, const float* w,
+                   int64_t T, int32_t k, int32_t H, float* out, void* stream);
+int launch_x_to_f16(const uint16_t* x, int64_t n, uint16_t* x16, void* stream);
+int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,
+                      const int32_t* perm_src, const int32_t* offsets, int64_t T,
+                      int32_t k, uint16_t* h16, float* y_perm, int phase,
+                      void* stream);
+int launch_dequant(const LayerView& L, int fmt, int32_t rec_index, int32_t proj,
+                   float* out, void* stream);
+
+}  // namespace moeq

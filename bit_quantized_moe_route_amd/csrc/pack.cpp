@@ -1,0 +1,219 @@
+// Host-side packers: the NVFP4 encoder (fp32 -> canonical codes + E4M3
+// scales) and the device record layouts of NVFP4 and VQ experts.
+// Plain C++17, no device access.
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+namespace moeq {
+
+namespace {
+
+// Nearest E4M3 (OCP E4M3FN) byte for a finite v >= 0, ties to the even
+// byte, saturating at 448.  Subnormals are m * 2^-9 (byte m); normals are
+// (1 + m/8) * 2^(e-7) (byte e << 3 | m).
+uint8_t e4m3_rne(double v) {
+    if (v >= 448.0) return 0x7e;
+    if (v < 0.015625) {                       // below the smallest normal 2^-6
+        double m = std::nearbyint(v * 512.0);  // exact scaling, ties to even
+        return (uint8_t)m;                     // m == 8 is the normal 2^-6 = byte 8
+    }
+    int e2;
+    double fr = std::frexp(v, &e2);            // v = fr * 2^e2, fr in [0.5, 1)
+    int e = e2 - 1;                            // v = (2 fr) * 2^e, 2 fr in [1, 2)
+    double q = std::nearbyint((2.0 * fr - 1.0) * 8.0);
+    int m = (int)q;
+    if (m == 8) {
+        m = 0;
+        ++e;
+    }
+    int byte = ((e + 7) << 3) | m;
+    return (uint8_t)(byte > 0x7e ? 0x7e : byte);
+}
+
+double e4m3_value(uint8_t b) {
+    int e = (b >> 3) & 15, m = b & 7;
+    double v = e == 0 ? std::ldexp((double)m, -9) : std::ldexp(1.0 + m / 8.0, e - 7);
+    return (b & 0x80) ? -v : v;
+}
+
+// E2M1 magnitude index of a = |w| relative to scale S: nearest of
+// {0, .5, 1, 1.5, 2, 3, 4, 6} * S, ties to the even index, saturating at 6.
+// The comparisons use midpoint * S, which is exact in double.
+inline int e2m1_index(double a, double S) {
+    if (a <= 0.25 * S) return 0;
+    if (a < 0.75 * S) return 1;
+    if (a <= 1.25 * S) return 2;
+    if (a < 1.75 * S) return 3;
+    if (a <= 2.5 * S) return 4;
+    if (a < 3.5 * S) return 5;
+    if (a <= 5.0 * S) return 6;
+    return 7;
+}
+
+}  // namespace
+
+// NVFP4 record tile writer: rows [0, n) x inputs [0, kin) of canonical bytes
+// into row groups rg_step*g + rg_off of a record with nkb tiles per group.
+static void nv_tiles(const uint8_t* codes, const uint8_t* scales, int32_t n, int32_t kin,
+                     int rg_step, int rg_off, uint8_t* rec) {
+    const int64_t nkb = nv_tiles_k(kin);
+    const int kc = kin / 2, ks = kin / 16;
+    for (int g = 0; g < n / 16; ++g) {
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            uint8_t* tile = rec + ((int64_t)(g * rg_step + rg_off) * nkb + kb) * kNvTileBytes;
+            std::memset(tile, 0, kNvTileBytes);
+            for (int L = 0; L < 64; ++L) {
+                const int row = 16 * g + (L & 15);
+                const int k0 = (int)kb * kNvTileK + (L >> 4) * 32;
+                for (int b = 0; b < 16; ++b) {
+                    const int kbyte = k0 / 2 + b;
+                    if (2 * kbyte < kin) tile[L * 16 + b] = codes[(int64_t)row * kc + kbyte];
+                }
+                for (int q = 0; q < 2; ++q) {
+                    const int sb = k0 / 16 + q;
+                    if (sb < ks) tile[kNvScaleOff + L * 2 + q] = scales[(int64_t)row * ks + sb];
+                }
+            }
+        }
+    }
+}
+
+static void vq_tiles(const uint16_t* codes, int32_t n, int32_t kin, int rg_step, int rg_off,
+                     uint8_t* rec) {
+    const int64_t nkb = vq_tiles_k(kin);
+    const int ng = kin / 8;
+    for (int g = 0; g < n / 16; ++g) {
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            uint8_t* tile = rec + ((int64_t)(g * rg_step + rg_off) * nkb + kb) * kVqTileBytes;
+            std::memset(tile, 0, kVqTileBytes);
+            for (int L = 0; L < 64; ++L) {
+                const int row = 16 * g + (L & 15);
+                const int g0 = ((int)kb * kVqTileK + (L >> 4) * 64) / 8;
+                uint16_t* dst = reinterpret_cast<uint16_t*>(tile + L * 16);
+                for (int s = 0; s < 8; ++s)
+                    if (g0 + s < ng) dst[s] = codes[(int64_t)row * ng + g0 + s];
+            }
+        }
+    }
+}
+
+static int64_t vq_rec_bytes(int which, int32_t H, int32_t I) {
+    if (which == 0) return round_up(vq_codes_bytes(2 * I, H) + 2LL * I * 2, 256);
+    return round_up(vq_codes_bytes(H, I) + 2LL * H, 256);
+}
+
+static int64_t nv_rec_bytes(int which, int32_t H, int32_t I) {
+    if (which == 0) return round_up(nv_matrix_bytes(2 * I, H), 256);
+    return round_up(nv_matrix_bytes(H, I), 256);
+}
+
+}  // namespace moeq
+
+using namespace moeq;
+
+extern "C" {
+
+int moe_quantize_nvfp4(const float* w, int32_t n, int32_t kin, uint8_t* codes,
+                       uint8_t* scales) {
+    if (!w || !codes || !scales) return fail(MOE_EINVAL, "moe_quantize_nvfp4: null pointer");
+    if (n < 0 || kin <= 0 || kin % 16 != 0)
+        return fail(MOE_EINVAL, "moe_quantize_nvfp4: need n >= 0, kin > 0, kin % 16 == 0");
+    for (int64_t o = 0; o < n; ++o) {
+        const float* row = w + o * kin;
+        uint8_t* crow = codes + o * (kin / 2);
+        uint8_t* srow = scales + o * (kin / 16);
+        for (int b = 0; b < kin / 16; ++b) {
+            const float* blk = row + 16 * b;
+            double amax = 0.0;
+            for (int i = 0; i < 16; ++i) {
+                if (!std::isfinite(blk[i]))
+                    return fail(MOE_EINVAL, "moe_quantize_nvfp4: non-finite weight");
+                double a = std::fabs((double)blk[i]);
+                if (a > amax) amax = a;
+            }
+            const uint8_t sb = e4m3_rne(amax / 6.0);
+            srow[b] = sb;
+            const double S = e4m3_value(sb);
+            for (int i = 0; i < 16; i += 2) {
+                int c[2];
+                for (int q = 0; q < 2; ++q) {
+                    const double v = (double)blk[i + q];
+                    int m = S > 0.0 ? e2m1_index(std::fabs(v), S) : 0;
+                    c[q] = m | ((v < 0.0 && m != 0) ? 8 : 0);
+                }
+                crow[8 * b + i / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    }
+    return MOE_OK;
+}
+
+size_t moe_record_bytes(int fmt, int which, int32_t H, int32_t I) {
+    if (H <= 0 || I <= 0 || (which != 0 && which != 1)) return 0;
+    if (fmt == MOE_FMT_NVFP4) {
+        if (H % 16 || I % 16) return 0;
+        return (size_t)nv_rec_bytes(which, H, I);
+    }
+    if (fmt == MOE_FMT_VQ) {
+        if (H % 16 || I % 16) return 0;   // row groups of 16 outputs; inputs in groups of 8
+        return (size_t)vq_rec_bytes(which, H, I);
+    }
+    return 0;
+}
+
+int moe_pack_nvfp4_expert(const uint8_t* gc, const uint8_t* gs, const uint8_t* uc,
+                          const uint8_t* us, const uint8_t* dc, const uint8_t* ds, int32_t H,
+                          int32_t I, uint8_t* w13, uint8_t* w2) {
+    if (!gc || !gs || !uc || !us || !dc || !ds || !w13 || !w2)
+        return fail(MOE_EINVAL, "moe_pack_nvfp4_expert: null pointer");
+    if (H <= 0 || I <= 0 || H % 16 || I % 16)
+        return fail(MOE_EUNSUPPORTED, "moe_pack_nvfp4_expert: H and I must be positive multiples of 16");
+    std::memset(w13, 0, (size_t)nv_rec_bytes(0, H, I));
+    std::memset(w2, 0, (size_t)nv_rec_bytes(1, H, I));
+    nv_tiles(gc, gs, I, H, 2, 0, w13);
+    nv_tiles(uc, us, I, H, 2, 1, w13);
+    nv_tiles(dc, ds, H, I, 1, 0, w2);
+    return MOE_OK;
+}
+
+int moe_pack_vq_expert(const uint16_t* gc, const uint16_t* gs, const uint16_t* uc,
+                       const uint16_t* us, const uint16_t* dc, const uint16_t* ds, int32_t H,
+                       int32_t I, uint8_t* w13, uint8_t* w2) {
+    if (!gc || !gs || !uc || !us || !dc || !ds || !w13 || !w2)
+        return fail(MOE_EINVAL, "moe_pack_vq_expert: null pointer");
+    if (H <= 0 || I <= 0 || H % 16 || I % 16)
+        return fail(MOE_EUNSUPPORTED, "moe_pack_vq_expert: H and I must be positive multiples of 16");
+    std::memset(w13, 0, (size_t)vq_rec_bytes(0, H, I));
+    std::memset(w2, 0, (size_t)vq_rec_bytes(1, H, I));
+    vq_tiles(gc, I, H, 2, 0, w13);
+    vq_tiles(uc, I, H, 2, 1, w13);
+    vq_tiles(dc, H, I, 1, 0, w2);
+    const int64_t c13 = vq_codes_bytes(2 * I, H);
+    std::memcpy(w13 + c13, gs, (size_t)I * 2);
+    std::memcpy(w13 + c13 + (size_t)I * 2, us, (size_t)I * 2);
+    std::memcpy(w2 + vq_codes_bytes(H, I), ds, (size_t)H * 2);
+    return MOE_OK;
+}
+
+int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* n_nvfp4,
+                     int32_t* n_vq) {
+    if (!fmt_host || !rec) return fail(MOE_EINVAL, "moe_record_table: null pointer");
+    if (E < 1 || E > MOE_MAX_E) return fail(MOE_EINVAL, "moe_record_table: bad E");
+    int32_t cnt[3] = {0, 0, 0};
+    for (int e = 0; e < E; ++e) {
+        const int f = fmt_host[e];
+        if (f != MOE_FMT_NVFP4 && f != MOE_FMT_VQ)
+            return fail(MOE_EUNSUPPORTED,
+                        "moe_record_table: expert " + std::to_string(e) + " has unknown format tag " +
+                            std::to_string(f));
+        rec[e] = (f << 24) | cnt[f]++;
+    }
+    if (n_nvfp4) *n_nvfp4 = cnt[MOE_FMT_NVFP4];
+    if (n_vq) *n_vq = cnt[MOE_FMT_VQ];
+    return MOE_OK;
+}
+
+}  // extern "C"

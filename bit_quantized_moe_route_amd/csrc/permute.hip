@@ -1,0 +1,113 @@
+// Token permutation: a stable counting sort of the T*k assignments by expert.
+//
+// One workgroup of 1024 threads:
+//   1. histogram of expert ids in LDS;
+//   2. exclusive prefix scan over the E counts (wave scans + a scan of the
+//      wave totals) -> counts, offsets;
+//   3. the assignments in chunks of 1024, in order: within a wave, lanes
+//      with the same expert find each other with 11 ballots (one per bit
+//      of the id); a lane's rank is its position among its peers, plus the
+//      peers in earlier waves of the chunk (per-wave counts in LDS), plus
+//      the running count of that expert from earlier chunks.
+// The result is unique, so it does not depend on timing.
+#include "dev_common.h"
+
+namespace moeq {
+
+namespace {
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / 64;
+
+__global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restrict__ ids,
+                                                          int n, int E,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ perm_src,
+                                                          int32_t* __restrict__ inv_perm) {
+    extern __shared__ int smem[];
+    int* hist = smem;                 // [E]
+    int* run = smem + E;              // [E]
+    int* wtot = smem + 2 * E;         // [kPermWaves]
+    uint8_t* wcnt = reinterpret_cast<uint8_t*>(smem + 2 * E + kPermWaves);  // [kPermWaves][E]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    for (int e = tid; e < E; e += kPermThreads) hist[e] = 0;
+    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
+    __syncthreads();
+    for (int a = tid; a < n; a += kPermThreads) atomicAdd(&hist[ids[a]], 1);
+    __syncthreads();
+
+    // exclusive scan of hist[0..E) (E <= kPermThreads)
+    int c = tid < E ? hist[tid] : 0;
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += wtot[w];
+    int excl = wbase + incl - c;
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = excl;
+        run[tid] = excl;
+    }
+    if (tid == 0) offsets[E] = n;
+    __syncthreads();
+
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < n; base += kPermThreads) {
+        const int a = base + tid;
+        const bool valid = a < n;
+        const int e = valid ? ids[a] : 0x7ff;   // sentinel never equals an id
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 11; ++b) {
+            uint64_t bal = __ballot((e >> b) & 1);
+            peers &= ((e >> b) & 1) ? bal : ~bal;
+        }
+        const int rank_w = __popcll(peers & lt_mask);
+        if (valid && rank_w == 0) wcnt[wave * E + e] = (uint8_t)__popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int r = run[e] + rank_w;
+            for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
+            perm_src[r] = a;
+            inv_perm[a] = r;
+        }
+        __syncthreads();
+        for (int x = tid; x < E; x += kPermThreads) {
+            int s = 0;
+            for (int w = 0; w < kPermWaves; ++w) {
+                s += wcnt[w * E + x];
+                wcnt[w * E + x] = 0;
+            }
+            run[x] += s;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int64_t, int32_t, int32_t) { return 0; }
+
+int launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
+                   int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, void*,
+                   void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int n = (int)(T * k);
+    size_t lds = (size_t)(2 * E + kPermWaves) * sizeof(int) + (size_t)kPermWaves * E;
+    k_permute<<<1, kPermThreads, lds, s>>>(ids, n, E, counts, offsets, perm_src, inv_perm);
+    MOEQ_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+}  // namespace moeq

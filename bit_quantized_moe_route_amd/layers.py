@@ -1,0 +1,59 @@
+"""Loading a packed expert layer onto the GPU.
+
+Weights come from caller-supplied providers (one projection of one expert at
+a time), are encoded and laid out by the library's host packers
+(moe_quantize_nvfp4, moe_pack_*_expert) on a thread pool, and are copied
+into the layer's device pools.  One expert is resident in host memory per
+worker at a time.
+"""
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from . import (FMT_NVFP4, FMT_VQ, PROJ_DOWN, PROJ_GATE, PROJ_UP, QLayer, pack_nvfp4_expert,
+               pack_vq_expert, quantize_nvfp4)
+
+
+def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=None,
+                codebook_stride=0, device="cuda", workers=8):
+    """Build a QLayer.
+
+    nvfp4_weights(e, proj) -> fp32 [n, kin] source weights of an NVFP4 expert
+        (proj 0 = gate [I, H], 1 = up [I, H], 2 = down [H, I]).
+    vq_codes(e, proj) -> (codes uint16 [n, kin/8], scales fp16 bits uint16 [n])
+        of a VQ expert.
+    codebooks: three uint16 arrays (fp16 bits) [65536 * n_books, 8] for gate,
+        up, down.
+    """
+    import torch
+
+    layer = QLayer(E, H, I, fmt_host, device=device)
+    host = {}
+    for key, pool in layer.pools.items():
+        if pool is not None:
+            host[key] = np.zeros(pool.numel(), np.uint8)
+
+    def one(e):
+        fmt = int(layer.fmt_host[e])
+        idx = layer.record_index(e)
+        s13, s2 = layer.stride[(fmt, 0)], layer.stride[(fmt, 1)]
+        dst13 = host[(fmt, 0)][idx * s13: idx * s13 + s13]
+        dst2 = host[(fmt, 1)][idx * s2: idx * s2 + s2]
+        if fmt == FMT_NVFP4:
+            parts = [quantize_nvfp4(nvfp4_weights(e, p)) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
+            w13, w2 = pack_nvfp4_expert(parts[0], parts[1], parts[2], H, I)
+        else:
+            parts = [vq_codes(e, p) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
+            w13, w2 = pack_vq_expert(parts[0], parts[1], parts[2], H, I)
+        dst13[:w13.shape[0]] = w13
+        dst2[:w2.shape[0]] = w2
+
+    with ThreadPoolExecutor(max(1, workers)) as ex:
+        list(ex.map(one, range(E)))
+    for key, arr in host.items():
+        layer.pools[key].copy_(torch.from_numpy(arr))
+    if layer.n_vq:
+        layer.set_codebooks(codebooks, codebook_stride)
+    torch.cuda.synchronize(layer.device)
+    return layer

@@ -1,0 +1,290 @@
+/*
+ * moeq.h -- C ABI of the routed-expert MoE forward over low-bit expert
+ * weights, for AMD Instinct MI355X (gfx950).
+ *
+ * The forward, for T tokens with hidden size H, E experts of intermediate
+ * size I and k experts per token:
+ *
+ *   moe_route_topk    logits [T, E]            -> topk_ids [T, k], topk_w [T, k]
+ *   moe_permute       topk_ids                 -> counts, offsets, perm_src, inv_perm
+ *   moe_expert_ffn_q  x [T, H], perm_src, ...  -> y_perm [T*k, H]
+ *   moe_combine       y_perm, inv_perm, topk_w -> out [T, H]
+ *
+ * Passages these calls follow (titles and sections of the source pages):
+ *   - 256 routed experts per MoE layer, 8 active per token:
+ *     "GLM-5-NVFP4-MTP", Model Description.
+ *   - only the expert MLP (gate, up, down projections) is low-bit:
+ *     "GLM-5-NVFP4-MTP", What's quantized.
+ *   - NVFP4 = 4-bit E2M1 codes with an FP8 (E4M3) scale per 16 elements:
+ *     "GLM-5-NVFP4-MTP", Model Description.
+ *   - AQLM-style vector quantization, per-group codes into a shared codebook:
+ *     "GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw", What it is.
+ *   - a per-expert tier map that the runtime must honour, failing closed
+ *     rather than decoding with the wrong format:
+ *     "GLM-5.3-EXL3-TR3-3.42bpw", What is quantized / Serving;
+ *     "GLM-5.3-Flash-TR3-8bpw (K8)", Why K8 uses the native eager path.
+ *   - records addressed by expert id at a fixed stride:
+ *     "GLM-5.3 Vision NestQuant 1.75-4 bit", Contents.
+ *   - a fixed expert-combine order (the order changes the bits):
+ *     "GLM-5.3-Flash-TR3-8bpw (K8)", Fidelity / Excess over control.
+ *
+ * Conventions
+ *   - Pointers marked [device] are device memory on the current HIP device;
+ *     [host] pointers are host memory.  The caller allocates and owns every
+ *     buffer.  The library never allocates, frees or synchronises, keeps no
+ *     state between calls and is safe to call from several threads.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls are
+ *     stream-ordered and asynchronous: they return after the launch.
+ *   - Arguments are checked on the host before any launch.  A rejected call
+ *     launches nothing and returns a negative status; moe_last_error() then
+ *     describes it (per thread).  There is no fallback path: an unsupported
+ *     format or shape is an error (MOE_EUNSUPPORTED), never a silent decode
+ *     with another format.
+ *   - T == 0 is valid for every device call; moe_permute then writes
+ *     counts = 0 and offsets = 0, the other calls launch nothing.
+ *   - Device-side preconditions that cannot be checked without reading device
+ *     memory (logits not NaN; topk_ids in [0, E); perm_src/offsets produced by
+ *     moe_permute for the same topk_ids; the per-expert record table agreeing
+ *     with the host tier map) are the caller's; violating them gives
+ *     unspecified results but no out-of-bounds access beyond the buffers'
+ *     stated sizes for ids in range.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define MOE_OK            0
+#define MOE_EINVAL       -1   /* bad argument: null pointer, size, shape */
+#define MOE_EUNSUPPORTED -2   /* format / shape this library does not decode */
+#define MOE_EWORKSPACE   -3   /* workspace smaller than *_workspace_bytes() */
+#define MOE_EHIP         -4   /* a HIP launch failed */
+
+/* ---------------------------------------------------------------- formats */
+#define MOE_FMT_NVFP4 1       /* E2M1 codes + E4M3 scale per 16 inputs */
+#define MOE_FMT_VQ    2       /* 8-wide groups, uint16 codes, fp16 codebook,
+                                 fp16 scale per output channel */
+
+#define MOE_PROJ_GATE 0
+#define MOE_PROJ_UP   1
+#define MOE_PROJ_DOWN 2
+
+/* Limits of this build. */
+#define MOE_MAX_E     1024    /* experts per layer */
+#define MOE_MAX_K     16      /* experts per token */
+#define MOE_VQ_NCODE  65536   /* codebook entries (uint16 codes) */
+
+/*
+ * A packed expert layer.  Host struct; the pointers inside are [device]
+ * unless noted.
+ *
+ * Every expert has a format tag.  Experts of one format are stored as
+ * fixed-size records in that format's pool: the record of expert e is at
+ * pool + index(e) * stride, where index(e) is e's rank among the experts of
+ * its format (so a single-format layer has index(e) = e).  Record sizes are
+ * given by moe_record_bytes() and their bytes by the moe_pack_* calls.
+ *
+ *   fmt_host   [host]   uint8 [E]: MOE_FMT_NVFP4 or MOE_FMT_VQ per expert.
+ *   rec_dev    [device] int32 [E]: (fmt << 24) | index(e), as written by
+ *                       moe_record_table() from the same fmt_host.
+ *   nvfp4_w13 / nvfp4_w2   pool bases of NVFP4 gate/up and down records;
+ *   vq_w13 / vq_w2         pool bases of VQ gate/up and down records;
+ *   *_stride               bytes between consecutive records of a pool
+ *                          (>= moe_record_bytes(), multiple of 256).
+ *   vq_codebook[p]  fp16 [65536, 8] codebook of projection p (gate, up,
+ *                   down).  vq_codebook_stride = bytes between the codebooks
+ *                   of consecutive VQ records (index(e)); 0 means one
+ *                   codebook per projection shared by every expert.
+ *
+ * Unused pools (no expert of that format) may be NULL.
+ */
+typedef struct moe_qlayer {
+    int32_t E, H, I;
+    int32_t reserved;
+    const uint8_t* fmt_host;
+    const int32_t* rec_dev;
+    const void* nvfp4_w13;  int64_t nvfp4_w13_stride;
+    const void* nvfp4_w2;   int64_t nvfp4_w2_stride;
+    const void* vq_w13;     int64_t vq_w13_stride;
+    const void* vq_w2;      int64_t vq_w2_stride;
+    const void* vq_codebook[3];
+    int64_t vq_codebook_stride;
+} moe_qlayer;
+
+/* ------------------------------------------------------------- messages */
+
+/* Static text for a status code. */
+const char* moe_strerror(int status);
+/* Detail of the last rejected call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* -------------------------------------------------------------- routing */
+
+/*
+ * moe_route_topk -- per token, the k experts with the largest router logits
+ * and their softmax weights renormalised over the chosen k.
+ *   ("GLM-5-NVFP4-MTP", Model Description: 8 of 256 experts per token.)
+ *
+ *   logits    [device] fp32 [T, E], row-major.
+ *   topk_ids  [device] int32 [T, k] out: ids[t, j] = expert of rank j.
+ *             Ranking: larger logit first; equal logits -> lower expert id
+ *             first; -0.0 and +0.0 are equal.
+ *   topk_w    [device] fp32 [T, k] out: w[t, j] = exp(l_j - l_0) /
+ *             sum_{i<k} exp(l_i - l_0) (fp32 arithmetic).
+ *   Limits: 1 <= E <= MOE_MAX_E, 1 <= k <= min(E, MOE_MAX_K), T >= 0.
+ *   Precondition: no NaN logits, and each token's largest logit is finite
+ *   (other logits may be -inf; they then get weight 0).
+ */
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                   int32_t* topk_ids, float* topk_w, void* stream);
+
+/* -------------------------------------------------------------- permute */
+
+/* Workspace bytes moe_permute needs for these sizes (may be 0). */
+size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E);
+
+/*
+ * moe_permute -- group the T*k assignments by expert (a stable counting sort).
+ *   Assignment a = t*k + j goes to expert e_a = topk_ids[a].
+ *   counts   [device] int32 [E] out: number of assignments per expert.
+ *   offsets  [device] int32 [E+1] out: exclusive prefix sum of counts,
+ *            offsets[E] = T*k.
+ *   perm_src [device] int32 [T*k] out: for each expert in ascending id, its
+ *            assignments in ascending a.  Row i of y_perm belongs to token
+ *            perm_src[i] / k.
+ *   inv_perm [device] int32 [T*k] out: inv_perm[perm_src[i]] = i.
+ *   ws       [device] workspace of >= moe_permute_workspace_bytes() bytes
+ *            (NULL allowed when that is 0).
+ *   Limits: as moe_route_topk; T*k < 2^31.
+ *   The result is unique, so it is bit-identical run to run.
+ */
+int moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
+                int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ expert FFN */
+
+/* Workspace bytes moe_expert_ffn_q needs (the SwiGLU activations h). */
+size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k);
+
+/*
+ * moe_expert_ffn_q -- the expert MLP for every assignment, with the weights
+ * decoded in registers from each expert's own format.
+ *   ("GLM-5-NVFP4-MTP", What's quantized: gate, up and down projections.)
+ *
+ *   For row i of the permuted order, with e the expert whose offsets range
+ *   holds i and t = perm_src[i] / k:
+ *     g = W_gate[e] x_t,  u = W_up[e] x_t      (I outputs each, K = H)
+ *     h = silu(g) * u = g * u / (1 + exp(-g))
+ *     y_perm[i] = W_down[e] h                  (H outputs, K = I)
+ *
+ *   x        [device] bf16 [T, H] as uint16 bits, token order.
+ *   perm_src [device] int32 [T*k], offsets [device] int32 [E+1]: from
+ *            moe_permute.
+ *   y_perm   [device] fp32 [T*k, H] out.
+ *   ws       [device] >= moe_ffn_workspace_bytes() bytes, 256-byte aligned.
+ *
+ *   Arithmetic: decoded weights are exact (every NVFP4 product of an E2M1
+ *   value and an E4M3 scale is exact in bf16 and fp16; VQ codebook entries
+ *   are fp16, the per-channel scale is applied in fp32 after the dot
+ *   product).  Products accumulate in fp32 on the matrix cores; x enters the
+ *   gate/up product as bf16 (NVFP4) or fp16 (VQ), h enters the down product
+ *   as fp16.
+ *   Requirements: H and I multiples of 16 (both formats); every format
+ *   tag in layer->fmt_host must be MOE_FMT_NVFP4 or MOE_FMT_VQ, else
+ *   MOE_EUNSUPPORTED; every pool that a tag refers to must be non-NULL.
+ */
+int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16,
+                     const int32_t* perm_src, const int32_t* offsets,
+                     int64_t T, int32_t k, float* y_perm,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* -------------------------------------------------------------- combine */
+
+/*
+ * moe_combine -- out[t] = sum_{j=0}^{k-1} topk_w[t, j] * y_perm[inv_perm[t*k+j]],
+ * summed in ascending j in fp32, one writer per output element (no atomics),
+ * so the result is bit-identical run to run.
+ *   ("GLM-5.3-Flash-TR3-8bpw (K8)", Fidelity: the combine order changes the
+ *   bits, so it is fixed.)
+ *   y_perm [device] fp32 [T*k, H]; inv_perm [device] int32 [T*k];
+ *   topk_w [device] fp32 [T, k]; out [device] fp32 [T, H] out.
+ */
+int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                int64_t T, int32_t k, int32_t H, float* out, void* stream);
+
+/* ------------------------------------------------------- host-side packers */
+
+/*
+ * moe_quantize_nvfp4 -- [host] encode fp32 weights w [n, kin] (row-major,
+ * kin % 16 == 0) to canonical NVFP4 bytes:
+ *   codes  [n, kin/2]  element 2i in the low nibble of byte i;
+ *   scales [n, kin/16] E4M3 (OCP E4M3FN) byte per 16 contiguous inputs.
+ * Per block: S = E4M3(amax/6), nearest, ties to even, saturating at 448;
+ * S == 0 -> all codes 0; else each element -> nearest E2M1 magnitude of
+ * |w|/S, ties to even mantissa, saturating at 6, sign bit only on nonzero
+ * magnitudes.  ("GLM-5-NVFP4-MTP", Model Description.)
+ * Returns MOE_EINVAL on a null pointer, bad size or a non-finite weight
+ * (then the outputs are unspecified).
+ */
+int moe_quantize_nvfp4(const float* w, int32_t n, int32_t kin,
+                       uint8_t* codes, uint8_t* scales);
+
+/*
+ * Bytes of one expert record in the device tile layout.
+ *   fmt = MOE_FMT_NVFP4 / MOE_FMT_VQ; which = 0 for the gate/up record
+ *   (both projections, rows interleaved by 16), 1 for the down record.
+ * Returns 0 for an unsupported format or shape.
+ */
+size_t moe_record_bytes(int fmt, int which, int32_t H, int32_t I);
+
+/*
+ * moe_pack_nvfp4_expert -- [host] lay the canonical NVFP4 bytes of one
+ * expert out as its two device records (gate/up and down).
+ *   gate/up codes [I, H/2], scales [I, H/16]; down codes [H, I/2],
+ *   scales [H, I/16]; w13_rec / w2_rec [host] out, moe_record_bytes() each.
+ */
+int moe_pack_nvfp4_expert(const uint8_t* gate_codes, const uint8_t* gate_scales,
+                          const uint8_t* up_codes, const uint8_t* up_scales,
+                          const uint8_t* down_codes, const uint8_t* down_scales,
+                          int32_t H, int32_t I, uint8_t* w13_rec, uint8_t* w2_rec);
+
+/*
+ * moe_pack_vq_expert -- [host] lay one VQ expert out as its two records.
+ *   codes uint16 [n, kin/8] (group g covers inputs 8g..8g+7), scales fp16
+ *   bits [n], for gate/up (n = I, kin = H) and down (n = H, kin = I).
+ *   ("GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw", What it is.)
+ */
+int moe_pack_vq_expert(const uint16_t* gate_codes, const uint16_t* gate_scales,
+                       const uint16_t* up_codes, const uint16_t* up_scales,
+                       const uint16_t* down_codes, const uint16_t* down_scales,
+                       int32_t H, int32_t I, uint8_t* w13_rec, uint8_t* w2_rec);
+
+/*
+ * moe_record_table -- [host] fill rec [E] = (fmt << 24) | index(e) from the
+ * tier map, and report how many experts each format has (either count
+ * pointer may be NULL).  MOE_EUNSUPPORTED on an unknown tag.
+ */
+int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec,
+                     int32_t* n_nvfp4, int32_t* n_vq);
+
+/* ------------------------------------------------------------ test hook */
+
+/*
+ * moe_dequant_q -- decode projection `proj` (MOE_PROJ_*) of expert `expert`
+ * to fp32 out [n, kin] ([device]; gate/up: [I, H], down: [H, I]) with the
+ * same device decode routines the FFN kernels use.  Every value is exact.
+ */
+int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj,
+                  float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEQ_H */

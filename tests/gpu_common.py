@@ -1,0 +1,49 @@
+"""Shared helpers of the GPU parity tests."""
+
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+
+ROW_TOL = 1e-2       # max |gpu - oracle| per row <= ROW_TOL * RMS(oracle row)
+W_TOL = 1e-6         # router weights, absolute
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def assert_rows_close(gpu, ref, what, tol=ROW_TOL):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), what
+    rms = np.sqrt(np.mean(ref * ref, axis=1))
+    err = np.max(np.abs(gpu - ref), axis=1)
+    zero = rms == 0
+    assert np.all(gpu[zero] == 0), (what, "rows with zero oracle RMS must be exactly 0")
+    rel = err[~zero] / rms[~zero]
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= tol, (what, "worst row rel err", worst)
+    return worst
+
+
+def build_small_layer(wl, device="cuda"):
+    """A QLayer for workload wl built by the library's packers from the
+    seeded inputs."""
+    from bit_quantized_moe_route_amd.layers import build_layer
+
+    fmt_host = synth.tier_map(wl)
+    cbs = [synth.vq_codebook(wl, p) for p in range(3)] if (fmt_host == synth.FMT_VQ).any() else None
+    return build_layer(
+        wl.E, wl.H, wl.I, fmt_host,
+        nvfp4_weights=lambda e, p: synth.nvfp4_source_weights(wl, e, p),
+        vq_codes=lambda e, p: (synth.vq_codes(wl, e, p), synth.vq_scales(wl, e, p)),
+        codebooks=cbs, device=device, workers=16)
+
+
+def oracle_perm(ids, E):
+    return oracle.permute(ids, E)

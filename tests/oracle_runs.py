@@ -1,0 +1,50 @@
+"""Oracle-side helpers for the parity tests and the CPU baseline: decode one
+expert's weights from the seeded workload with the oracle's own encoder and
+decoders, and evaluate the oracle FFN for given token rows.  Imports only
+numpy, the oracle and the input generators (safe to run in spawned worker
+processes that never touch the GPU)."""
+
+import os
+
+import numpy as np
+
+import oracle
+import synth
+
+
+def expert_weights(wl, e, fmt=None):
+    """(W_gate, W_up, W_down) float64 of expert e of workload wl, decoded by
+    the oracle from the same seeded inputs the GPU layer was built from."""
+    if fmt is None:
+        fmt = int(synth.tier_map(wl)[e])
+    mats = []
+    for p in (synth.PROJ_GATE, synth.PROJ_UP, synth.PROJ_DOWN):
+        if fmt == synth.FMT_NVFP4:
+            c, s = oracle.nvfp4_quantize(synth.nvfp4_source_weights(wl, e, p))
+            mats.append(oracle.nvfp4_dequant(c, s))
+        else:
+            mats.append(oracle.vq_dequant(synth.vq_codes(wl, e, p), synth.vq_scales(wl, e, p),
+                                          synth.vq_codebook(wl, p)))
+    return tuple(mats)
+
+
+def expert_rows(args):
+    """Oracle FFN outputs of expert e for the given bf16 token rows."""
+    wl_name, e, x_bits, fmt = args
+    wl = synth.WORKLOADS[wl_name] if isinstance(wl_name, str) else wl_name
+    W = expert_weights(wl, e, fmt)
+    return oracle.expert_ffn(x_bits, *W)
+
+
+def pool_map(jobs, workers=None):
+    """Run expert_rows over jobs in spawned processes (numpy only)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    if workers is None:
+        workers = max(1, min(len(jobs), 8, len(os.sched_getaffinity(0))))
+    if workers == 1 or len(jobs) == 1:
+        return [expert_rows(j) for j in jobs]
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(workers, mp_context=ctx) as ex:
+        return list(ex.map(expert_rows, jobs))

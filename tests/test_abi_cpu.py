@@ -1,0 +1,261 @@
+"""CPU tests of the C ABI library: it loads, exports every declared symbol,
+its host packers match the oracle byte for byte, and its host-side argument
+checks reject bad calls before any launch (no GPU is touched here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import bit_quantized_moe_route_amd as moeq
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    txt = open(os.path.join(ROOT, "include", "moeq.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 14
+    L = moeq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", moeq.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    # the binding declares a prototype for every one of them
+    assert set(names) == set(moeq._PROTOS)
+
+
+def test_strerror():
+    L = moeq.lib()
+    for st in (0, -1, -2, -3, -4):
+        assert L.moe_strerror(st)
+    assert b"fail" in L.moe_strerror(-2) or b"unsupported" in L.moe_strerror(-2)
+
+
+# ---------------------------------------------------------------- packers
+
+@pytest.mark.parametrize("shape,seed", [((16, 256), 0), ((48, 6144), 1), ((96, 2048), 2),
+                                        ((17, 32), 3)])
+def test_quantize_nvfp4_matches_oracle(shape, seed):
+    rs = np.random.default_rng(seed)
+    w = (rs.standard_normal(shape) * 0.02).astype(np.float32)
+    c, s = moeq.quantize_nvfp4(w)
+    oc, os_ = oracle.nvfp4_quantize(w)
+    assert np.array_equal(c, oc)
+    assert np.array_equal(s, os_)
+
+
+def test_quantize_nvfp4_crafted_matches_oracle(golden_dir):
+    rs = np.random.default_rng(5)
+    rows = []
+    for S in [2.0 ** -9, 3 * 2.0 ** -9, 2.0 ** -7, 0.171875, 1.0, 448.0]:
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, 6, 7, 0.1, 0.9, 4.4, -5, -0.25, 0, 6],
+                        dtype=np.float64) * S
+        rows.append(mids.astype(np.float32))
+    rows.append(np.zeros(16, np.float32))
+    rows.append((rs.standard_normal(16) * 1e-5).astype(np.float32))
+    rows.append((rs.standard_normal(16) * 1e3).astype(np.float32))
+    rows.append(np.array([np.float32(3 * 2.0 ** -11)] + [0] * 15, np.float32))
+    w = np.stack(rows)
+    c, s = moeq.quantize_nvfp4(w)
+    oc, os_ = oracle.nvfp4_quantize(w)
+    assert np.array_equal(c, oc) and np.array_equal(s, os_)
+    # the hand-worked fixture blocks
+    from tests.test_oracle_formats import _handworked
+    for name, v, sb, cb in _handworked(golden_dir):
+        c, s = moeq.quantize_nvfp4(v[None, :])
+        assert s[0, 0] == sb and list(c[0]) == cb, name
+
+
+def test_quantize_nvfp4_rejects_nonfinite():
+    w = np.zeros((2, 16), np.float32)
+    w[1, 5] = np.inf
+    with pytest.raises(moeq.MoeError) as ei:
+        moeq.quantize_nvfp4(w)
+    assert ei.value.status == moeq.MOE_EINVAL
+    with pytest.raises(moeq.MoeError):
+        moeq.quantize_nvfp4(np.zeros((2, 24), np.float32))
+
+
+def _nv_record_offsets(n, kin, rg_step, rg_off):
+    """(row, k) -> (byte offset of the code byte, nibble) and (row, block) ->
+    scale byte offset, following the tile layout documented in moeq's
+    internal header: 16 rows x 128 inputs per 1152-byte tile; lane L holds
+    row L&15, inputs (L>>4)*32 .. +32 as 16 code bytes at 16L, and their two
+    scales at 1024 + 2L."""
+    nkb = (kin + 127) // 128
+    code_off = np.empty((n, kin // 2), np.int64)
+    scale_off = np.empty((n, kin // 16), np.int64)
+    for row in range(n):
+        g, r = divmod(row, 16)
+        for kbyte in range(kin // 2):
+            k = 2 * kbyte
+            kb, kk = divmod(k, 128)
+            L = r + 16 * (kk // 32)
+            tile = (g * rg_step + rg_off) * nkb + kb
+            code_off[row, kbyte] = tile * 1152 + L * 16 + (kk % 32) // 2
+        for b in range(kin // 16):
+            k = 16 * b
+            kb, kk = divmod(k, 128)
+            L = r + 16 * (kk // 32)
+            tile = (g * rg_step + rg_off) * nkb + kb
+            scale_off[row, b] = tile * 1152 + 1024 + 2 * L + (kk % 32) // 16
+    return code_off, scale_off
+
+
+@pytest.mark.parametrize("H,I", [(256, 128), (144, 48)])
+def test_nvfp4_record_layout(H, I):
+    rs = np.random.default_rng(H)
+    mats = []
+    for shape in [(I, H), (I, H), (H, I)]:
+        w = (rs.standard_normal(shape) * 0.02).astype(np.float32)
+        mats.append(moeq.quantize_nvfp4(w))
+    w13, w2 = moeq.pack_nvfp4_expert(mats[0], mats[1], mats[2], H, I)
+    assert w13.size == moeq.record_bytes(moeq.FMT_NVFP4, 0, H, I)
+    for (codes, scales), rec, rg_step, rg_off in [(mats[0], w13, 2, 0), (mats[1], w13, 2, 1),
+                                                   (mats[2], w2, 1, 0)]:
+        n, kin = codes.shape[0], codes.shape[1] * 2
+        co, so = _nv_record_offsets(n, kin, rg_step, rg_off)
+        assert np.array_equal(rec[co], codes)
+        assert np.array_equal(rec[so], scales)
+    # everything else in the records is zero padding
+    used = np.zeros(w13.size, bool)
+    for (codes, scales), rg_off in [(mats[0], 0), (mats[1], 1)]:
+        co, so = _nv_record_offsets(I, H, 2, rg_off)
+        used[co.ravel()] = True
+        used[so.ravel()] = True
+    assert np.all(w13[~used] == 0)
+
+
+def test_vq_record_layout():
+    H, I = 272, 48
+    rs = np.random.default_rng(0)
+    parts = []
+    for n, kin in [(I, H), (I, H), (H, I)]:
+        parts.append((rs.integers(0, 65536, (n, kin // 8), dtype=np.uint16),
+                      rs.integers(0, 65536, n, dtype=np.uint16)))
+    w13, w2 = moeq.pack_vq_expert(parts[0], parts[1], parts[2], H, I)
+    for (codes, scales), rec, rg_step, rg_off, nrg in [(parts[0], w13, 2, 0, 2 * I // 16),
+                                                       (parts[1], w13, 2, 1, 2 * I // 16),
+                                                       (parts[2], w2, 1, 0, H // 16)]:
+        n, ng = codes.shape
+        kin = ng * 8
+        nkb = (kin + 255) // 256
+        r16 = rec[: nrg * nkb * 1024].view(np.uint16)
+        for row in range(n):
+            g, r = divmod(row, 16)
+            for grp in range(ng):
+                kb, kk = divmod(8 * grp, 256)
+                L = r + 16 * (kk // 64)
+                s = (kk % 64) // 8
+                off = ((g * rg_step + rg_off) * nkb + kb) * 1024 + 16 * L + 2 * s
+                assert r16[off // 2] == codes[row, grp]
+    c13 = (2 * I // 16) * ((H + 255) // 256) * 1024
+    assert np.array_equal(w13[c13:c13 + 2 * I].view(np.uint16), parts[0][1])
+    assert np.array_equal(w13[c13 + 2 * I:c13 + 4 * I].view(np.uint16), parts[1][1])
+    c2 = (H // 16) * ((I + 255) // 256) * 1024
+    assert np.array_equal(w2[c2:c2 + 2 * H].view(np.uint16), parts[2][1])
+
+
+def test_record_table():
+    tm = synth.tier_map(synth.MIXED)
+    rec, nn, nv = moeq.record_table(tm)
+    assert nn == 108 and nv == 148
+    for fmt in (1, 2):
+        sel = np.nonzero(tm == fmt)[0]
+        assert np.all(rec[sel] >> 24 == fmt)
+        assert np.array_equal(rec[sel] & 0xFFFFFF, np.arange(sel.size))
+    bad = tm.copy()
+    bad[7] = 3
+    with pytest.raises(moeq.MoeError) as ei:
+        moeq.record_table(bad)
+    assert ei.value.status == moeq.MOE_EUNSUPPORTED
+
+
+# ---------------------------------------------------------------- host-side checks (no launch)
+
+def test_route_rejects_bad_sizes_before_launch():
+    L = moeq.lib()
+    N = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    assert L.moe_route_topk(fake, 4, 0, 1, fake, fake, N) == moeq.MOE_EINVAL
+    assert L.moe_route_topk(fake, 4, 8, 9, fake, fake, N) == moeq.MOE_EINVAL
+    assert L.moe_route_topk(fake, 4, 2048, 8, fake, fake, N) == moeq.MOE_EINVAL
+    assert L.moe_route_topk(fake, 4, 64, 17, fake, fake, N) == moeq.MOE_EINVAL
+    assert L.moe_route_topk(N, 4, 8, 2, fake, fake, N) == moeq.MOE_EINVAL
+    assert b"k must be" in L.moe_last_error() or L.moe_last_error()
+    # T == 0 is a no-op that touches nothing
+    assert L.moe_route_topk(N, 0, 8, 2, N, N, N) == moeq.MOE_OK
+    assert L.moe_combine(N, N, N, 0, 2, 64, N, N) == moeq.MOE_OK
+    assert L.moe_combine(fake, fake, fake, 3, 2, 66, fake, N) == moeq.MOE_EINVAL
+
+
+def _fake_layer(fmt_host, H=256, I=128):
+    d = moeq._QLayerC()
+    d.E = len(fmt_host)
+    d.H, d.I = H, I
+    d.fmt_host = fmt_host.ctypes.data
+    d.rec_dev = 0x1000
+    for name in ("nvfp4_w13", "nvfp4_w2", "vq_w13", "vq_w2"):
+        setattr(d, name, 0x100000)
+    d.nvfp4_w13_stride = 1 << 20
+    d.nvfp4_w2_stride = 1 << 20
+    d.vq_w13_stride = 1 << 20
+    d.vq_w2_stride = 1 << 20
+    for p in range(3):
+        d.vq_codebook[p] = 0x100000
+    return d
+
+
+def test_ffn_fails_closed_on_unknown_format():
+    L = moeq.lib()
+    fake = ctypes.c_void_p(0x1000)
+    tm = np.full(8, moeq.FMT_NVFP4, np.uint8)
+    tm[3] = 7
+    d = _fake_layer(tm)
+    st = L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, 1 << 20,
+                            ctypes.c_void_p(0))
+    assert st == moeq.MOE_EUNSUPPORTED
+    assert b"expert 3" in L.moe_last_error()
+    st = L.moe_dequant_q(ctypes.byref(d), 0, 0, fake, ctypes.c_void_p(0))
+    assert st == moeq.MOE_EUNSUPPORTED
+
+
+def test_ffn_rejects_bad_shapes_and_workspace():
+    L = moeq.lib()
+    fake = ctypes.c_void_p(0x1000)
+    N = ctypes.c_void_p(0)
+    tm = np.full(8, moeq.FMT_NVFP4, np.uint8)
+    d = _fake_layer(tm, H=264, I=128)        # H % 16 != 0
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, 1 << 20,
+                              N) == moeq.MOE_EUNSUPPORTED
+    d = _fake_layer(tm)
+    need = L.moe_ffn_workspace_bytes(ctypes.byref(d), 4, 2)
+    assert need > 0
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, ctypes.c_void_p(0x1000),
+                              need - 1, N) == moeq.MOE_EWORKSPACE
+    d.nvfp4_w13_stride = 1000                # not a multiple of 256 / too small
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, ctypes.c_void_p(0x1000),
+                              need, N) == moeq.MOE_EINVAL
+    d = _fake_layer(tm)
+    d.nvfp4_w2 = None                        # pool missing
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, ctypes.c_void_p(0x1000),
+                              need, N) == moeq.MOE_EINVAL
+    d = _fake_layer(tm)
+    assert L.moe_expert_ffn_q(ctypes.byref(d), N, N, N, 0, 2, N, N, 0, N) == moeq.MOE_OK  # T == 0
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 9, fake, fake, need,
+                              N) == moeq.MOE_EINVAL  # k > E
+    assert L.moe_dequant_q(ctypes.byref(d), 8, 0, fake, N) == moeq.MOE_EINVAL
+    assert L.moe_dequant_q(ctypes.byref(d), 0, 3, fake, N) == moeq.MOE_EINVAL

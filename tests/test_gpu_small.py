@@ -1,0 +1,212 @@
+"""GPU parity at sizes the oracle finishes in seconds: every step of the path
+through the C ABI against the oracle, element by element.  Shapes span
+several tiles and ragged tails (inputs not a multiple of the 128/256-input
+tile, odd token counts, token counts past 16, 32 and 64)."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_moe_route_amd as moeq
+import oracle
+import synth
+from tests.gpu_common import W_TOL, assert_rows_close, build_small_layer, say
+from tests.oracle_runs import expert_weights
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+SMALL = {
+    "tiny": synth.TINY,
+    "nv_ragged": synth.small_workload("nv_ragged", E=16, k=4, H=272, I=80, T=37, cfg=101),
+    "vq_small": synth.small_workload("vq_small", E=12, k=3, H=512, I=144, T=21, fmt="vq", cfg=102),
+    "vq_ragged": synth.small_workload("vq_ragged", E=8, k=2, H=208, I=48, T=9, fmt="vq", cfg=103),
+    "mixed_small": synth.small_workload("mixed_small", E=24, k=6, H=384, I=96, T=70, fmt="mixed",
+                                        logits="hot", cfg=104, n_nvfp4=9, n_hot=4, hot_share=0.6),
+    "nv_k1": synth.small_workload("nv_k1", E=4, k=1, H=128, I=32, T=5, cfg=105),
+    "nv_kE": synth.small_workload("nv_kE", E=6, k=6, H=160, I=64, T=3, cfg=106),
+}
+
+_layers = {}
+
+
+def layer_for(name):
+    if name not in _layers:
+        _layers[name] = build_small_layer(SMALL[name], DEV)
+    return _layers[name]
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("name", ["tiny", "nv_ragged", "vq_small", "vq_ragged", "mixed_small"])
+def test_dequant_bit_exact(name):
+    wl = SMALL[name]
+    say("dequant", name)
+    layer = layer_for(name)
+    for e in range(wl.E):
+        W = expert_weights(wl, e)
+        for p in range(3):
+            got = to_np(moeq.dequant_q(layer, e, p)).astype(np.float64)
+            assert np.array_equal(got, W[p]), (name, e, p)
+
+
+# ------------------------------------------------------------------ route
+
+def _route_check(lg, k):
+    ids, w = moeq.route_topk(torch.from_numpy(lg).to(DEV), k)
+    oids, ow = oracle.route_topk(lg, k)
+    assert np.array_equal(to_np(ids), oids)
+    assert np.max(np.abs(to_np(w).astype(np.float64) - ow)) <= W_TOL
+    return to_np(ids)
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(4, 8, 2, "normal"), (1, 256, 8, "uniform"),
+                                        (33, 256, 8, "uniform"), (300, 64, 5, "normal"),
+                                        (7, 1024, 16, "normal"), (5, 600, 3, "uniform"),
+                                        (9, 3, 3, "normal"), (4096, 256, 8, "zipf")])
+def test_route_topk(T, E, k, kind):
+    say("route", T, E, k, kind)
+    if kind == "zipf":
+        lg = synth.logits(synth.PREFILL, T)
+    else:
+        g = np.random.default_rng(T * 1000 + E)
+        lg = (g.standard_normal((T, E)) if kind == "normal" else g.random((T, E))).astype(np.float32)
+    _route_check(lg, k)
+
+
+def test_route_ties():
+    say("route ties")
+    lg = np.zeros((3, 256), np.float32)
+    lg[1, ::2] = 1.0                 # 128 tied maxima: ids 0, 2, 4, ...
+    lg[2] = np.where(np.arange(256) % 3 == 0, -0.0, 0.0).astype(np.float32)
+    lg[2, 200] = -1.0
+    ids = _route_check(lg, 8)
+    assert list(ids[0]) == list(range(8))
+    assert list(ids[1]) == list(range(0, 16, 2))
+    # coarse logits: many exact ties across the k-th place
+    g = np.random.default_rng(3)
+    lg = (np.round(g.standard_normal((64, 256)) * 2) / 2).astype(np.float32)
+    _route_check(lg, 8)
+    # -inf logits are allowed as long as each token's top logit is finite
+    lg = np.full((2, 40), -np.inf, np.float32)
+    lg[0, 39] = 1.0
+    lg[1, 5] = -3.0
+    lg[1, 17] = -3.0
+    ids = _route_check(lg, 4)
+    assert list(ids[0]) == [39, 0, 1, 2] and list(ids[1]) == [5, 17, 0, 1]
+
+
+# ------------------------------------------------------------------ permute
+
+@pytest.mark.parametrize("T,E,k", [(4, 8, 2), (1, 256, 8), (32, 256, 8), (200, 16, 4),
+                                   (4096, 256, 8), (1500, 1024, 16), (3, 1, 1), (0, 8, 2)])
+def test_permute(T, E, k):
+    say("permute", T, E, k)
+    g = np.random.default_rng(T + E)
+    if T == 4096:
+        ids, _ = oracle.route_topk(synth.logits(synth.PREFILL, T), k)
+    else:
+        ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32) \
+            if T else np.zeros((0, k), np.int32)
+    got = moeq.permute(torch.from_numpy(ids).to(DEV), E)
+    want = oracle.permute(ids, E)
+    for a, b, nm in zip(got, want, ["counts", "offsets", "perm_src", "inv_perm"]):
+        assert np.array_equal(to_np(a), b), nm
+
+
+# ------------------------------------------------------------------ combine
+
+@pytest.mark.parametrize("T,k,H", [(4, 2, 256), (37, 8, 6144), (5, 16, 64)])
+def test_combine(T, k, H):
+    say("combine", T, k, H)
+    g = np.random.default_rng(T)
+    E = max(2 * k, 8)
+    ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)])
+    _, w = oracle.route_topk(g.standard_normal((T, E)).astype(np.float32), k)
+    _, _, perm_src, inv_perm = oracle.permute(ids, E)
+    y_perm = g.standard_normal((T * k, H)).astype(np.float32)
+    out = moeq.combine(torch.from_numpy(y_perm).to(DEV), torch.from_numpy(inv_perm).to(DEV),
+                       torch.from_numpy(w.astype(np.float32)).to(DEV))
+    y = y_perm.astype(np.float64)[inv_perm].reshape(T, k, H)
+    ref = oracle.combine(y, w.astype(np.float32).astype(np.float64))
+    assert_rows_close(to_np(out), ref, "combine", tol=1e-5)
+
+
+# ------------------------------------------------------------------ end to end
+
+def _oracle_forward(wl, x_bits, lg):
+    Wc = {}
+
+    def weights(e):
+        if e not in Wc:
+            Wc[e] = expert_weights(wl, e)
+        return Wc[e]
+    return oracle.forward(x_bits, lg, wl.k, weights)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_parity(name):
+    wl = SMALL[name]
+    T = wl.T[0]
+    say("forward", name, T)
+    layer = layer_for(name)
+    x_bits = synth.activations(wl, T)
+    lg = synth.logits(wl, T)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(DEV)
+    r = moeq.forward(layer, x, torch.from_numpy(lg).to(DEV), wl.k)
+    out, ids, w, y = _oracle_forward(wl, x_bits, lg)
+    assert np.array_equal(to_np(r["topk_ids"]), ids)
+    counts, offsets, perm_src, inv_perm = oracle.permute(ids, wl.E)
+    assert np.array_equal(to_np(r["perm_src"]), perm_src)
+    assert np.array_equal(to_np(r["offsets"]), offsets)
+    y_ref = y.reshape(T * wl.k, wl.H)[perm_src]
+    assert_rows_close(to_np(r["y_perm"]), y_ref, name + " y_perm")
+    assert_rows_close(to_np(r["out"]), out, name + " out")
+
+
+def test_forward_deterministic():
+    wl = SMALL["mixed_small"]
+    T = wl.T[0]
+    say("determinism", wl.name)
+    layer = layer_for("mixed_small")
+    x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(DEV)
+    lg = torch.from_numpy(synth.logits(wl, T)).to(DEV)
+    a = moeq.forward(layer, x, lg, wl.k)
+    b = moeq.forward(layer, x, lg, wl.k)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_zero_scale_expert_gives_exact_zero():
+    """An NVFP4 expert whose scales are all zero outputs exactly 0."""
+    say("zero-scale expert")
+    wl = synth.small_workload("zero", E=4, k=2, H=256, I=64, T=6, cfg=107)
+    from bit_quantized_moe_route_amd.layers import build_layer
+    layer = build_layer(wl.E, wl.H, wl.I, synth.tier_map(wl),
+                        nvfp4_weights=lambda e, p: (np.zeros(synth.proj_shape(wl, p), np.float32)
+                                                    if e == 1 else
+                                                    synth.nvfp4_source_weights(wl, e, p)),
+                        device=DEV)
+    lg = np.zeros((wl.T[0], wl.E), np.float32)
+    lg[:, 1] = 5.0                                   # every token picks expert 1 first
+    x = torch.from_numpy(synth.activations(wl, wl.T[0]).view(np.int16)).to(DEV)
+    r = moeq.forward(layer, x, torch.from_numpy(lg).to(DEV), wl.k)
+    offs = to_np(r["offsets"])
+    y = to_np(r["y_perm"])
+    assert offs[2] - offs[1] == wl.T[0]
+    assert np.all(y[offs[1]:offs[2]] == 0)
+
+
+def test_t_zero_is_noop():
+    say("T = 0")
+    layer = layer_for("tiny")
+    x = torch.empty((0, 256), dtype=torch.int16, device=DEV)
+    lg = torch.empty((0, 8), dtype=torch.float32, device=DEV)
+    r = moeq.forward(layer, x, lg, 2)
+    assert r["out"].shape == (0, 256)
+    assert torch.all(r["counts"] == 0) and torch.all(r["offsets"] == 0)
