@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE forward (route -> permute -> expert
+FFN over low-bit weights -> combine) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload: the GLM-5-class decode layer -- 256 experts, top-8,
+hidden 6144, expert intermediate 2048, NVFP4 weights quantized from
+N(0, 0.02) fp32 -- at a batch of 32 bf16 tokens with uniform-random router
+logits.  A step is one whole forward over one batch; the batches rotate over
+a pool of seeded inputs resident in HBM (so consecutive steps route to
+different experts and the weights stream from HBM, not from the caches).
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value          tokens/s of the whole path
+  roofline       the NVFP4 gate/up kernel: packed gate/up bytes of the
+                 experts it touches per launch / its mean launch time
+                 (HIP events on the launch stream), against 8 TB/s HBM
+  cpu_baseline   the fp64 oracle on a bounded sample (one token), one core
+  extra          the same path on the other workloads (decode T = 1 and 8,
+                 prefill T = 4096 with Zipf(1.1) routing, 2-bit VQ T = 8,
+                 mixed NVFP4/VQ T = 8 and 32)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_quantized_moe_route_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+
+class Runner:
+    """Pre-allocated buffers and a pool of input batches for one workload."""
+
+    def __init__(self, layer, wl, T, reps, dev):
+        import numpy as np
+        import torch
+        import bit_quantized_moe_route_amd as moeq
+        import synth
+
+        self.moeq, self.torch = moeq, torch
+        self.layer, self.wl, self.T, self.k = layer, wl, T, wl.k
+        self.batches = []
+        self.touched = []
+        for r in range(reps):
+            lg = synth.logits(wl, T, rep=r)
+            x = synth.activations(wl, T, rep=r)
+            self.batches.append((torch.from_numpy(lg).to(dev),
+                                 torch.from_numpy(x.view(np.int16)).to(dev)))
+            # experts touched (for byte accounting only)
+            top = np.argsort(-lg, axis=1, kind="stable")[:, :wl.k]
+            self.touched.append(np.unique(top))
+        k, E, H, I = wl.k, wl.E, wl.H, wl.I
+        i32, f32 = torch.int32, torch.float32
+        self.ids = torch.empty((T, k), dtype=i32, device=dev)
+        self.w = torch.empty((T, k), dtype=f32, device=dev)
+        self.perm = (torch.empty(E, dtype=i32, device=dev), torch.empty(E + 1, dtype=i32, device=dev),
+                     torch.empty(T * k, dtype=i32, device=dev), torch.empty(T * k, dtype=i32, device=dev))
+        self.h = torch.empty((T * k, I), dtype=torch.float16, device=dev)
+        self.y = torch.empty((T * k, H), dtype=f32, device=dev)
+        self.out = torch.empty((T, H), dtype=f32, device=dev)
+        self.ws = moeq.gateup_workspace(layer, T)
+        self.ev = []
+
+    def step(self, r, timed):
+        moeq = self.moeq
+        lg, x = self.batches[r % len(self.batches)]
+        moeq.route_topk(lg, self.k, self.ids, self.w)
+        moeq.permute(self.ids, self.wl.E, self.perm)
+        counts, offsets, perm_src, inv_perm = self.perm
+        if timed:
+            e0 = self.torch.cuda.Event(enable_timing=True)
+            e1 = self.torch.cuda.Event(enable_timing=True)
+            e0.record()
+        moeq.expert_gateup_q(self.layer, x, perm_src, offsets, self.k, self.h, self.ws)
+        if timed:
+            e1.record()
+            self.ev.append((r, e0, e1))
+        moeq.expert_down_q(self.layer, self.h, offsets, self.k, self.y)
+        moeq.combine(self.y, inv_perm, self.w, self.out)
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i, False)
+        torch.cuda.synchronize()
+        self.ev = []
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i, True)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        gu_ms = [e0.elapsed_time(e1) for _, e0, e1 in self.ev]
+        return dt, gu_ms
+
+    def bytes_of(self, r, which):
+        """Algorithmic packed-weight bytes of batch r: 'all' (codes + scales
+        of every touched expert, VQ codebooks once) or 'gateup'."""
+        experts = self.touched[r % len(self.touched)]
+        if which == "all":
+            return self.layer.packed_bytes(experts)
+        H, I = self.wl.H, self.wl.I
+        tot = 0
+        for e in experts:
+            if self.layer.fmt_host[e] == self.moeq.FMT_NVFP4:
+                tot += 2 * (H * I // 2 + H * I // 16)
+            else:
+                tot += 2 * (H * I // 8) * 2 + 2 * I * 2
+        return tot
+
+
+def measure(layer, wl, T, steps, warmup, dev, reps=16):
+    rn = Runner(layer, wl, T, reps, dev)
+    dt, gu_ms = rn.run(steps, warmup)
+    idx = [warmup + i for i in range(steps)]
+    all_bytes = sum(rn.bytes_of(r, "all") for r in idx)
+    gu_bytes = sum(rn.bytes_of(r, "gateup") for r in idx)
+    gu_s = sum(gu_ms) / 1e3
+    res = {
+        "T": T,
+        "tokens_per_s": T * steps / dt,
+        "ms_per_step": dt / steps * 1e3,
+        "packed_GBps": all_bytes / dt / 1e9,
+        "packed_frac_hbm": all_bytes / dt / 1e9 / HBM_PEAK_GBS,
+        "experts_touched_mean": sum(len(rn.touched[r % reps]) for r in idx) / steps,
+        "gateup_ms_mean": sum(gu_ms) / len(gu_ms),
+        "gateup_GBps": gu_bytes / gu_s / 1e9,
+        "gateup_bytes_per_launch": gu_bytes / steps,
+    }
+    if T >= 1024:
+        flops = 6.0 * wl.H * wl.I * T * wl.k
+        res["TFLOPs"] = flops / (dt / steps) / 1e12
+        res["frac_mfma"] = res["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+    return res
+
+
+# --------------------------------------------------------------------------
+
+def cpu_baseline(wl, T):
+    """The fp64 oracle on one token of the batch, on one core (BLAS threads
+    pinned to 1).  The oracle's own encoder prepares the canonical NVFP4
+    bytes of the token's experts in a process pool outside the timed region;
+    the timed region is oracle.forward: route, decode of the 8 experts from
+    canonical bytes, FFN and combine."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+
+    lg = synth.logits(wl, T, rep=0)[:1]
+    x = synth.activations(wl, T, rep=0)[:1]
+    ids, _ = oracle.route_topk(lg, wl.k)
+    experts = sorted(int(e) for e in np.unique(ids))
+    jobs = [(e, p) for e in experts for p in range(3)]
+    ncpu = len(os.sched_getaffinity(0))
+    with ProcessPoolExecutor(max(1, min(16, ncpu)), mp_context=mp.get_context("spawn")) as ex:
+        enc = list(ex.map(_oracle_encode, [(wl.name, e, p) for e, p in jobs]))
+    canon = {}
+    for (e, p), cs in zip(jobs, enc):
+        canon.setdefault(e, [None, None, None])[p] = cs
+
+    def weights(e):
+        return tuple(oracle.nvfp4_dequant(*canon[e][p]) for p in range(3))
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.forward(x, lg, wl.k, weights)
+        dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": 1.0 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"1 token of the decode T={T} batch (its {len(experts)} experts): "
+                       f"oracle.forward (fp64 route, NVFP4 decode from canonical bytes, FFN, "
+                       f"combine) on one core of '{cpu_model}' ({ncpu} host cores visible); "
+                       f"{dt:.1f} s"),
+            "seconds": dt}
+
+
+def _oracle_encode(args):
+    import oracle
+    import synth
+    name, e, p = args
+    wl = synth.WORKLOADS[name]
+    return oracle.nvfp4_quantize(synth.nvfp4_source_weights(wl, e, p))
+
+
+# --------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--T", type=int, default=32, help="decode batch of the headline")
+    ap.add_argument("--extra", default="decode1,decode8,prefill,vq,mixed8,mixed32",
+                    help="comma list of other workloads to measure ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_moe_route_amd as moeq
+    import synth
+    from bit_quantized_moe_route_amd.layers import build_layer
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moeq.lib()
+    wl = synth.DECODE
+    t0 = time.perf_counter()
+    log("building the NVFP4 decode layer (256 experts, H 6144, I 2048) ...")
+    nv_layer = build_layer(wl.E, wl.H, wl.I, synth.tier_map(wl),
+                           nvfp4_weights=lambda e, p: synth.nvfp4_source_weights(wl, e, p),
+                           device=dev, workers=16)
+    log(f"  built in {time.perf_counter() - t0:.1f} s")
+
+    log(f"headline: decode T={args.T}, {args.steps} steps after {args.warmup} warm-up")
+    head = measure(nv_layer, wl, args.T, args.steps, args.warmup, dev)
+    log("  ", json.dumps(head))
+
+    extra = {}
+    wanted = [s for s in args.extra.split(",") if s]
+    layers = {}
+    for name in wanted:
+        try:
+            if name.startswith("decode"):
+                T = int(name[len("decode"):])
+                extra[name] = measure(nv_layer, wl, T, 30, 5, dev)
+            elif name == "prefill":
+                extra[name] = measure(nv_layer, synth.PREFILL, 4096, 5, 2, dev, reps=4)
+            elif name == "vq":
+                wq = synth.VQ
+                log("building the VQ layer ...")
+                layers["vq"] = build_layer(
+                    wq.E, wq.H, wq.I, synth.tier_map(wq),
+                    vq_codes=lambda e, p: (synth.vq_codes(wq, e, p), synth.vq_scales(wq, e, p)),
+                    codebooks=[synth.vq_codebook(wq, p) for p in range(3)], device=dev, workers=16)
+                extra[name] = measure(layers["vq"], wq, 8, 30, 5, dev)
+            elif name.startswith("mixed"):
+                wm = synth.MIXED
+                T = int(name[len("mixed"):])
+                if "mixed" not in layers:
+                    log("building the mixed layer ...")
+                    layers["mixed"] = build_layer(
+                        wm.E, wm.H, wm.I, synth.tier_map(wm),
+                        nvfp4_weights=lambda e, p: synth.nvfp4_source_weights(wm, e, p),
+                        vq_codes=lambda e, p: (synth.vq_codes(wm, e, p), synth.vq_scales(wm, e, p)),
+                        codebooks=[synth.vq_codebook(wm, p) for p in range(3)], device=dev,
+                        workers=16)
+                extra[name] = measure(layers["mixed"], wm, T, 30, 5, dev)
+            log(f"  {name}:", json.dumps(extra[name]))
+        except Exception as exc:  # report, keep the headline
+            extra[name] = {"error": repr(exc)}
+            log(f"  {name} failed: {exc!r}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a one-token sample ...")
+        cpu = cpu_baseline(wl, args.T)
+        cpu.pop("seconds", None)
+        log("  ", json.dumps(cpu))
+
+    achieved = head["gateup_GBps"]
+    traffic = read_traffic(f"traffic_gateup_nvfp4_decode_T{args.T}.json")
+    line = {
+        "metric": "routed-expert tokens/s + packed-weight HBM GB/s (decode M=1..32, prefill 4K)",
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 weights (e2m1+e4m3), fp16 MFMA operands, fp32 accumulate/outputs",
+        "data": "synthetic (seeded), resident in HBM",
+        "config": {"workload": f"decode layer: 256 experts, top-8, H 6144, I 2048, NVFP4, "
+                               f"T={args.T} bf16 tokens, uniform router logits",
+                   "experts_touched_mean": head["experts_touched_mean"],
+                   "parallelism": "1 GPU"},
+        "packed_GBps": head["packed_GBps"],
+        "roofline": {"bound": "hbm", "kernel": "k_gateup<NvFmt> (+ x to fp16)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "bytes_per_launch": head["gateup_bytes_per_launch"],
+                     "launch_ms_mean": head["gateup_ms_mean"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,6 +70,10 @@ _PROTOS = {
     "moe_ffn_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64, _I32]),
     "moe_expert_ffn_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _P, _I64, _I32, _P,
                                         _P, _SZ, _P]),
+    "moe_gateup_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64]),
+    "moe_expert_gateup_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _P, _I64, _I32, _P,
+                                           _P, _SZ, _P]),
+    "moe_expert_down_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _I64, _I32, _P, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
     "moe_quantize_nvfp4": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "moe_record_bytes": (_SZ, [ctypes.c_int, ctypes.c_int, _I32, _I32]),
@@ -327,6 +331,39 @@ def expert_ffn_q(layer, x, perm_src, offsets, k, y_perm=None, ws=None):
     _check(lib().moe_expert_ffn_q(ctypes.byref(layer.c()), _dptr(x), _dptr(perm_src),
                                   _dptr(offsets), T, k, _dptr(y_perm), _dptr(ws), ws.numel(),
                                   _stream(x.device)), "moe_expert_ffn_q")
+    return y_perm
+
+
+def gateup_workspace(layer, T):
+    torch = _torch()
+    n = lib().moe_gateup_workspace_bytes(ctypes.byref(layer.c()), T)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=layer.device)
+
+
+def expert_gateup_q(layer, x, perm_src, offsets, k, h=None, ws=None):
+    """First half of the expert FFN: h = silu(W_gate x) * (W_up x), fp16 [T*k, I]."""
+    torch = _torch()
+    _need_cuda(x, perm_src, offsets)
+    T = x.shape[0]
+    if h is None:
+        h = torch.empty((T * k, layer.I), dtype=torch.float16, device=x.device)
+    if ws is None:
+        ws = gateup_workspace(layer, T)
+    _check(lib().moe_expert_gateup_q(ctypes.byref(layer.c()), _dptr(x), _dptr(perm_src),
+                                     _dptr(offsets), T, k, _dptr(h), _dptr(ws), ws.numel(),
+                                     _stream(x.device)), "moe_expert_gateup_q")
+    return h
+
+
+def expert_down_q(layer, h, offsets, k, y_perm=None):
+    """Second half: y_perm = W_down h, fp32 [T*k, H]."""
+    torch = _torch()
+    _need_cuda(h, offsets)
+    T = h.shape[0] // k
+    if y_perm is None:
+        y_perm = torch.empty((T * k, layer.H), dtype=torch.float32, device=h.device)
+    _check(lib().moe_expert_down_q(ctypes.byref(layer.c()), _dptr(h), _dptr(offsets), T, k,
+                                   _dptr(y_perm), _stream(h.device)), "moe_expert_down_q")
     return y_perm
 
 

@@ -155,6 +155,60 @@ size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k) {
     return ffn_ws(layer, T, k);
 }
 
+size_t moe_gateup_workspace_bytes(const moe_qlayer* layer, int64_t T) {
+    if (!layer || T < 0 || layer->H <= 0) return 0;
+    return align_up((size_t)T * layer->H * 2);
+}
+
+int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16, const int32_t* perm_src,
+                        const int32_t* offsets, int64_t T, int32_t k, uint16_t* h_f16, void* ws,
+                        size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    LayerInfo li;
+    int st = check_layer("moe_expert_gateup_q", layer, li);
+    if (st) return st;
+    st = check_route_sizes("moe_expert_gateup_q", T, layer->E, k);
+    if (st) return st;
+    if (T == 0) return MOE_OK;
+    if (!x_bf16 || !perm_src || !offsets || !h_f16)
+        return fail(MOE_EINVAL, "moe_expert_gateup_q: null pointer");
+    const size_t need = align_up((size_t)T * layer->H * 2);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_EWORKSPACE,
+                    "moe_expert_gateup_q: workspace needs " + std::to_string(need) + " bytes");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+        return fail(MOE_EINVAL, "moe_expert_gateup_q: workspace must be 256-byte aligned");
+    uint16_t* x16 = static_cast<uint16_t*>(ws);
+    st = launch_x_to_f16(x_bf16, T * layer->H, x16, stream);
+    if (st) return st;
+    for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
+        if (!li.count[fmt]) continue;
+        st = launch_ffn_decode(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T, k, h_f16,
+                               nullptr, 0, stream);
+        if (st) return st;
+    }
+    return MOE_OK;
+}
+
+int moe_expert_down_q(const moe_qlayer* layer, const uint16_t* h_f16, const int32_t* offsets,
+                      int64_t T, int32_t k, float* y_perm, void* stream) {
+    g_last_error.clear();
+    LayerInfo li;
+    int st = check_layer("moe_expert_down_q", layer, li);
+    if (st) return st;
+    st = check_route_sizes("moe_expert_down_q", T, layer->E, k);
+    if (st) return st;
+    if (T == 0) return MOE_OK;
+    if (!h_f16 || !offsets || !y_perm) return fail(MOE_EINVAL, "moe_expert_down_q: null pointer");
+    for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
+        if (!li.count[fmt]) continue;
+        st = launch_ffn_decode(li.view, fmt, li.count[fmt], nullptr, nullptr, offsets, T, k,
+                               const_cast<uint16_t*>(h_f16), y_perm, 1, stream);
+        if (st) return st;
+    }
+    return MOE_OK;
+}
+
 int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16, const int32_t* perm_src,
                      const int32_t* offsets, int64_t T, int32_t k, float* y_perm, void* ws,
                      size_t ws_bytes, void* stream) {
@@ -174,19 +228,11 @@ int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16, const int3
     if (reinterpret_cast<uintptr_t>(ws) % kAlign)
         return fail(MOE_EINVAL, "moe_expert_ffn_q: workspace must be 256-byte aligned");
     uint8_t* w = static_cast<uint8_t*>(ws);
-    uint16_t* x16 = reinterpret_cast<uint16_t*>(w);
-    uint16_t* h16 = reinterpret_cast<uint16_t*>(w + align_up((size_t)T * layer->H * 2));
-    st = launch_x_to_f16(x_bf16, T * layer->H, x16, stream);
+    const size_t xbytes = align_up((size_t)T * layer->H * 2);
+    uint16_t* h16 = reinterpret_cast<uint16_t*>(w + xbytes);
+    st = moe_expert_gateup_q(layer, x_bf16, perm_src, offsets, T, k, h16, ws, xbytes, stream);
     if (st) return st;
-    for (int phase = 0; phase < 2; ++phase) {
-        for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
-            if (!li.count[fmt]) continue;
-            st = launch_ffn_decode(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T, k, h16,
-                                   y_perm, phase, stream);
-            if (st) return st;
-        }
-    }
-    return MOE_OK;
+    return moe_expert_down_q(layer, h16, offsets, T, k, y_perm, stream);
 }
 
 int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T,

@@ -90,29 +90,52 @@ __device__ __forceinline__ u32x4 load_stream16(const uint8_t* p) {
 }
 
 // ---------------------------------------------------------------- experts
+struct ActiveExpert {
+    int e;      // expert id, -1 if there is no s-th active expert
+    int r0;     // first permuted row of the expert (offsets[e])
+    int me;     // number of rows (assignments) of the expert
+    int ridx;   // record index within its format's pool
+};
+
 // The s-th expert (ascending id) with at least one assignment and format
-// `fmt`, or -1.  Every lane of the wave gets the same answer.
-__device__ __forceinline__ int find_active_expert(const int32_t* __restrict__ offsets,
-                                                  const int32_t* __restrict__ rec,
-                                                  int E, int fmt, int s, int lane) {
+// `fmt`.  All loads are issued up front (one memory round trip); the answer
+// is broadcast from the owning lane, so every lane gets the same result.
+// E <= 64 * 16.
+__device__ __forceinline__ ActiveExpert find_active_expert(const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ rec,
+                                                           int E, int fmt, int s, int lane) {
+    // groups of 4 chunks of 64 experts: one memory round trip per group
+    constexpr int kG = 4;
+    ActiveExpert r{-1, 0, 0, 0};
     int seen = 0;
-    for (int base = 0; base < E; base += 64) {
-        int e = base + lane;
-        bool act = false;
-        if (e < E) {
-            int c = offsets[e + 1] - offsets[e];
-            act = c > 0 && (rec[e] >> 24) == fmt;
+    for (int g0 = 0; g0 < E; g0 += 64 * kG) {
+        int o0[kG], o1[kG], rc[kG];
+#pragma unroll
+        for (int c = 0; c < kG; ++c) {
+            const int e = g0 + 64 * c + lane;
+            const bool in = e < E;
+            o0[c] = in ? offsets[e] : 0;
+            o1[c] = in ? offsets[e + 1] : 0;
+            rc[c] = in ? rec[e] : 0;
         }
-        uint64_t m = __ballot(act);
-        int n = __popcll(m);
-        if (s < seen + n) {
-            int want = s - seen;   // index of the wanted set bit
-            for (int i = 0; i < want; ++i) m &= m - 1;
-            return base + __ffsll((unsigned long long)m) - 1;
+#pragma unroll
+        for (int c = 0; c < kG; ++c) {
+            const bool act = o1[c] > o0[c] && (rc[c] >> 24) == fmt;
+            uint64_t m = __ballot(act);
+            const int n = __popcll(m);
+            if (r.e < 0 && s < seen + n) {
+                for (int i = 0; i < s - seen; ++i) m &= m - 1;   // drop lower set bits
+                const int owner = __ffsll((unsigned long long)m) - 1;
+                r.e = g0 + 64 * c + owner;
+                r.r0 = __builtin_amdgcn_readlane(o0[c], owner);
+                r.me = __builtin_amdgcn_readlane(o1[c], owner) - r.r0;
+                r.ridx = __builtin_amdgcn_readlane(rc[c], owner) & 0xffffff;
+            }
+            seen += n;
         }
-        seen += n;
+        if (r.e >= 0) break;
     }
-    return -1;
+    return r;
 }
 
 }  // namespace moeq

@@ -7,18 +7,18 @@
 // ("GLM-5-NVFP4-MTP", What's quantized: gate, up and down projections of the
 // routed experts are the low-bit part.)
 //
-// Work decomposition (gfx950, wave64):
-//   * one workgroup = 4 waves = one 16-row group of output channels (gate/up:
-//     16 gate rows + the 16 matching up rows) of one active expert;
-//   * the 4 waves split the input dimension (tile kb goes to wave kb % 4) and
-//     reduce their 16x16 fp32 partial tiles through LDS in a fixed order;
-//   * each wave streams its weight tiles straight from HBM into registers
-//     (16-byte loads per lane, one tile = 1 KB of codes per wave-load),
-//     decodes them in registers to fp16 (exact) and feeds
-//     v_mfma_f32_16x16x32_f16 with the weights as the A operand and up to
-//     16 tokens per B operand (tokens of the expert beyond 16 use further
-//     B tiles; lanes of absent tokens carry zeros).
-// The tokens' activations are fp16 copies of x made once per call.
+// Work decomposition (gfx950, wave64, 4 waves per workgroup):
+//   * a wave owns one 16-row group of output channels (gate/up: 16 gate rows
+//     and the 16 matching up rows) and a share of the input dimension: with
+//     KS waves per row group, tile kb goes to wave kb % KS of the group; the
+//     KS partial 16x16 fp32 tiles are summed through LDS in a fixed order;
+//   * the wave streams its weight tiles from HBM straight into registers with
+//     16-byte loads (one tile = 1 KB of codes per wave-wide load), keeping the
+//     next tile's loads in flight while it decodes the current one to fp16
+//     (exact) and feeds v_mfma_f32_16x16x32_f16: weights are the A operand,
+//     up to 16 tokens of the expert the B operand (further tokens use further
+//     B tiles; only the tiles the expert needs are computed);
+//   * the tokens' activations are fp16 copies of x made once per call.
 #include "dev_common.h"
 
 namespace moeq {
@@ -35,14 +35,16 @@ struct NvFmt {
     static constexpr int STEPS = 4;           // MFMA K-steps per tile
     static constexpr int KSPAN = 32;          // inputs per lane per tile
     struct Frag {
-        NvFrag f;
+        u32x4 codes;
+        uint32_t scales;
     };
     __device__ __forceinline__ static void load(Frag& fr, const uint8_t* tile, int lane) {
-        fr.f.codes = load_stream16(tile + lane * 16);
-        fr.f.scales = *reinterpret_cast<const uint16_t*>(tile + kNvScaleOff + lane * 2);
+        fr.codes = load_stream16(tile + lane * 16);
+        fr.scales = *reinterpret_cast<const uint16_t*>(tile + kNvScaleOff + lane * 2);
     }
     __device__ __forceinline__ static void decode(const Frag& fr, const uint8_t*, f16x8 a[STEPS]) {
-        nv_decode(fr.f, a);
+        NvFrag f{fr.codes, fr.scales};
+        nv_decode(f, a);
     }
 };
 
@@ -69,17 +71,19 @@ struct VqFmt {
 };
 
 template <class F>
-__device__ __forceinline__ int64_t tiles_k(int kin) {
+__device__ __forceinline__ int tiles_k(int kin) {
     return (kin + F::TK - 1) / F::TK;
 }
 
-// B operand fragments of one tile for NTT token tiles: lane L holds token
-// (L & 15) + 16 tt, inputs k0 + 8 s .. +7 with k0 = kb*TK + (L>>4)*KSPAN.
+// B operand fragments of one tile for the first `ntt` of NTT token tiles:
+// lane L holds token (L & 15) + 16 tt, inputs k0 + 8 s .. +7 with
+// k0 = kb*TK + (L>>4)*KSPAN.
 template <class F, int NTT>
-__device__ __forceinline__ void load_b(const _Float16* const xrow[NTT], int k0, int K,
+__device__ __forceinline__ void load_b(const _Float16* const xrow[NTT], int ntt, int k0, int K,
                                        f16x8 b[NTT][F::STEPS]) {
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
+        if (tt >= ntt) break;
 #pragma unroll
         for (int s = 0; s < F::STEPS; ++s) {
             const int kk = k0 + 8 * s;
@@ -113,181 +117,224 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * u / (1.0f + expf(-g));
 }
 
-// gate/up + SwiGLU.  grid: x = row-pair group j (I/16), y = active-expert slot,
-// z = chunk of 16*NTT rows of the expert.
-template <class F, int NTT>
-__global__ __launch_bounds__(256) void k_gateup(DecodeArgs A) {
+// Streams NM matrices' tiles (gate/up: NM = 2, down: NM = 1) of one 16-row
+// group over tiles kb = kpart, kpart + KS, ... and accumulates
+// acc[m][tt] += W_m[rows, tile] * B[tile, tokens of tile tt].
+// The loads of the next D tiles stay in flight (a register ring of D + 1
+// stages) while a tile is decoded and multiplied.
+template <class F, int NTT, int NM, int D>
+__device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
+                                             const uint8_t* const cb[NM],
+                                             const _Float16* const xrow[NTT], int ntt, int K,
+                                             int kpart, int KS, int lane,
+                                             f32x4 acc[NM][NTT]) {
+    const int nkb = tiles_k<F>(K);
+    const int ksub = (lane >> 4) * F::KSPAN;
+    const int niter = kpart < nkb ? (nkb - kpart + KS - 1) / KS : 0;   // tiles of this wave
+    typename F::Frag wr[D + 1][NM];
+    f16x8 br[D + 1][NTT][F::STEPS];
+    auto issue = [&](int i, typename F::Frag (&w)[NM], f16x8 (&b)[NTT][F::STEPS]) {
+        const int kb = kpart + i * KS;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) F::load(w[m], tbase[m] + (int64_t)kb * F::TB, lane);
+        load_b<F, NTT>(xrow, ntt, kb * F::TK + ksub, K, b);
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        if (u < niter) issue(u, wr[u], br[u]);
+    for (int it = 0; it < niter; it += D + 1) {
+#pragma unroll
+        for (int u = 0; u <= D; ++u) {
+            const int i = it + u;
+            if (i >= niter) break;
+            if (i + D < niter) issue(i + D, wr[(u + D) % (D + 1)], br[(u + D) % (D + 1)]);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                f16x8 a[F::STEPS];
+                F::decode(wr[u][m], cb[m], a);
+#pragma unroll
+                for (int s = 0; s < F::STEPS; ++s)
+#pragma unroll
+                    for (int tt = 0; tt < NTT; ++tt)
+                        if (tt < ntt) acc[m][tt] = mfma16(a[s], br[u][tt][s], acc[m][tt]);
+            }
+        }
+    }
+}
+
+// Row groups per wave: gate/up 2 row-pair groups (4 weight tiles per input
+// tile), down 4 row groups.
+constexpr int kRpwGateup = 2;
+constexpr int kRpwDown = 4;
+// Tiles kept in flight ahead of the one being used.
+#ifndef MOEQ_PREFETCH
+#define MOEQ_PREFETCH 1
+#endif
+constexpr int kPrefetch = MOEQ_PREFETCH;
+// Waves per SIMD the register budget is sized for (latency hiding).
+#ifndef MOEQ_MIN_WAVES
+#define MOEQ_MIN_WAVES 2
+#endif
+constexpr int kMinWaves = MOEQ_MIN_WAVES;
+
+// One kernel for both halves.  PHASE 0 (gate/up + SwiGLU): a wave owns RPW
+// row-pair groups (RPW gate tiles and RPW up tiles per input tile); PHASE 1
+// (down): a wave owns RPW row groups of W_down.  KS waves split the input
+// dimension of the same rows.  The B fragments (activations) are loaded once
+// per input tile and used for all 2*RPW (or RPW) weight tiles of the wave.
+// grid: x = sets of (4/KS) waves' rows, y = active-expert slot, z = chunk of
+// 16*NTT rows of the expert.
+template <class F, int NTT, int KS, int RPW, int PHASE>
+__global__ __launch_bounds__(256, kMinWaves) void k_ffn(DecodeArgs A) {
+    constexpr int NM = PHASE == 0 ? 2 * RPW : RPW;   // weight tiles per input tile
+    constexpr int SETS = kWaves / KS;                // row sets per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int j = blockIdx.x;
-    const int e = find_active_expert(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
-    if (e < 0) return;
-    const int r0 = A.offsets[e];
-    const int me = A.offsets[e + 1] - r0;
+    const ActiveExpert ae = find_active_expert(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
+    if (ae.e < 0) return;
     const int c0 = blockIdx.z * 16 * NTT;
-    if (c0 >= me) return;
-    const int ridx = A.rec[e] & 0xffffff;
-    const uint8_t* base = A.pool13 + (int64_t)ridx * A.stride13;
-    const int64_t nkb = tiles_k<F>(A.H);
-    const uint8_t* tg = base + (int64_t)(2 * j) * nkb * F::TB;
-    const uint8_t* tu = tg + nkb * F::TB;
-    const uint8_t* cbg = A.cb_gate + (int64_t)ridx * A.cb_stride;
-    const uint8_t* cbu = A.cb_up + (int64_t)ridx * A.cb_stride;
+    if (c0 >= ae.me) return;
+    const int ntt = min(NTT, (ae.me - c0 + 15) / 16);
+    const int set = blockIdx.x * SETS + wave / KS;   // row set of this wave
+    const int kpart = wave % KS;
+    const int K = PHASE == 0 ? A.H : A.I;
+    const int nrg = (PHASE == 0 ? A.I : A.H) / 16;   // row (pair) groups
+    const int g0 = set * RPW;                        // first row (pair) group
+    const int nlive = min(RPW, nrg - g0);            // groups of this wave in range
+    const int nkb = tiles_k<F>(K);
+    const uint8_t* base = PHASE == 0 ? A.pool13 + (int64_t)ae.ridx * A.stride13
+                                     : A.pool2 + (int64_t)ae.ridx * A.stride2;
+    const uint8_t* tb[NM];
+    const uint8_t* cb[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        // gate/up records interleave row groups: 2j = gate, 2j+1 = up
+        const int g = PHASE == 0 ? 2 * min(g0 + m / 2, nrg - 1) + (m & 1) : min(g0 + m, nrg - 1);
+        tb[m] = base + (int64_t)g * nkb * F::TB;
+        cb[m] = PHASE == 0 ? ((m & 1) ? A.cb_up : A.cb_gate) + (int64_t)ae.ridx * A.cb_stride
+                           : A.cb_down + (int64_t)ae.ridx * A.cb_stride;
+    }
 
     const _Float16* xrow[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
         const int c = c0 + (lane & 15) + 16 * tt;
-        xrow[tt] = c < me ? A.x16 + (int64_t)(A.perm_src[r0 + c] / A.k) * A.H : nullptr;
+        if (c >= ae.me)
+            xrow[tt] = nullptr;
+        else if (PHASE == 0)
+            xrow[tt] = A.x16 + (int64_t)(A.perm_src[ae.r0 + c] / A.k) * A.H;
+        else
+            xrow[tt] = A.h16 + (int64_t)(ae.r0 + c) * A.I;
     }
+    f32x4 acc[NM][NTT];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) acc[m][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nlive > 0) stream_tiles<F, NTT, NM, kPrefetch>(tb, cb, xrow, ntt, K, kpart, KS, lane, acc);
 
-    f32x4 accg[NTT], accu[NTT];
+    if constexpr (KS > 1) {
+        // sum the KS partial tiles of a row set in a fixed order (wave order)
+        __shared__ f32x4 red[kWaves][NM][64];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-        accg[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accu[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    for (int64_t kb = wave; kb < nkb; kb += kWaves) {
-        typename F::Frag fg, fu;
-        F::load(fg, tg + kb * F::TB, lane);
-        F::load(fu, tu + kb * F::TB, lane);
-        f16x8 b[NTT][F::STEPS];
-        load_b<F, NTT>(xrow, (int)(kb * F::TK) + (lane >> 4) * F::KSPAN, A.H, b);
-        f16x8 a[F::STEPS];
-        F::decode(fg, cbg, a);
+        for (int tt = 0; tt < NTT; ++tt) {
+            if (tt >= ntt) break;
+            __syncthreads();
 #pragma unroll
-        for (int s = 0; s < F::STEPS; ++s)
+            for (int m = 0; m < NM; ++m) red[wave][m][lane] = acc[m][tt];
+            __syncthreads();
+            if (kpart == 0) {
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) accg[tt] = mfma16(a[s], b[tt][s], accg[tt]);
-        F::decode(fu, cbu, a);
+                for (int w = 1; w < KS; ++w)
 #pragma unroll
-        for (int s = 0; s < F::STEPS; ++s)
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) accu[tt] = mfma16(a[s], b[tt][s], accu[tt]);
-    }
-
-    __shared__ f32x4 red[kWaves][2][NTT][64];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-        red[wave][0][tt][lane] = accg[tt];
-        red[wave][1][tt][lane] = accu[tt];
-    }
-    __syncthreads();
-    if (wave < NTT) {
-        const int tt = wave;
-        f32x4 g = red[0][0][tt][lane], u = red[0][1][tt][lane];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-            g = g + red[w][0][tt][lane];
-            u = u + red[w][1][tt][lane];
+                    for (int m = 0; m < NM; ++m) acc[m][tt] = acc[m][tt] + red[wave + w][m][lane];
+            }
         }
-        const int c = c0 + (lane & 15) + 16 * tt;
-        if (c < me) {
-            const int n0 = 16 * j + (lane >> 4) * 4;
+        if (kpart != 0) return;
+    }
+    const int r4 = (lane >> 4) * 4;
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        if (q >= nlive) break;
+        const int n0 = 16 * (g0 + q) + r4;            // first output channel of this lane
+        if constexpr (PHASE == 0) {
+            float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
             if constexpr (F::kVq) {
-                // VQ: per-output-channel fp16 scales after the dot product
-                const uint8_t* sc = base + (int64_t)(2 * (A.I / 16)) * nkb * F::TB;
-                const _Float16* sg = reinterpret_cast<const _Float16*>(sc);
-                const _Float16* su = sg + A.I;
+                // VQ: per-output-channel fp16 scales, applied after the dot product
+                const _Float16* sp =
+                    reinterpret_cast<const _Float16*>(base + (int64_t)(2 * nrg) * nkb * F::TB);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    g[i] *= (float)sg[n0 + i];
-                    u[i] *= (float)su[n0 + i];
+                    sg[i] = (float)sp[n0 + i];
+                    su[i] = (float)sp[A.I + n0 + i];
                 }
             }
-            f16x4 h;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) h[i] = (_Float16)silu_mul(g[i], u[i]);
-            *reinterpret_cast<f16x4*>(A.h16 + (int64_t)(r0 + c) * A.I + n0) = h;
-        }
-    }
-}
-
-// down.  grid: x = row group j (H/16), y = active-expert slot, z = row chunk.
-template <class F, int NTT>
-__global__ __launch_bounds__(256) void k_down(DecodeArgs A) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int j = blockIdx.x;
-    const int e = find_active_expert(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
-    if (e < 0) return;
-    const int r0 = A.offsets[e];
-    const int me = A.offsets[e + 1] - r0;
-    const int c0 = blockIdx.z * 16 * NTT;
-    if (c0 >= me) return;
-    const int ridx = A.rec[e] & 0xffffff;
-    const uint8_t* base = A.pool2 + (int64_t)ridx * A.stride2;
-    const int64_t nkb = tiles_k<F>(A.I);
-    const uint8_t* tw = base + (int64_t)j * nkb * F::TB;
-    const uint8_t* cbd = A.cb_down + (int64_t)ridx * A.cb_stride;
-
-    const _Float16* xrow[NTT];
+            for (int tt = 0; tt < NTT; ++tt) {
+                const int c = c0 + (lane & 15) + 16 * tt;
+                if (tt < ntt && c < ae.me) {
+                    f16x4 h;
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-        const int c = c0 + (lane & 15) + 16 * tt;
-        xrow[tt] = c < me ? A.h16 + (int64_t)(r0 + c) * A.I : nullptr;
-    }
-    f32x4 acc[NTT];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int64_t kb = wave; kb < nkb; kb += kWaves) {
-        typename F::Frag fw;
-        F::load(fw, tw + kb * F::TB, lane);
-        f16x8 b[NTT][F::STEPS];
-        load_b<F, NTT>(xrow, (int)(kb * F::TK) + (lane >> 4) * F::KSPAN, A.I, b);
-        f16x8 a[F::STEPS];
-        F::decode(fw, cbd, a);
-#pragma unroll
-        for (int s = 0; s < F::STEPS; ++s)
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) acc[tt] = mfma16(a[s], b[tt][s], acc[tt]);
-    }
-
-    __shared__ f32x4 red[kWaves][NTT][64];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) red[wave][tt][lane] = acc[tt];
-    __syncthreads();
-    if (wave < NTT) {
-        const int tt = wave;
-        f32x4 y = red[0][tt][lane];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) y = y + red[w][tt][lane];
-        const int c = c0 + (lane & 15) + 16 * tt;
-        if (c < me) {
-            const int n0 = 16 * j + (lane >> 4) * 4;
-            if constexpr (F::kVq) {
-                const _Float16* sd = reinterpret_cast<const _Float16*>(
-                    base + (int64_t)(A.H / 16) * nkb * F::TB);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] *= (float)sd[n0 + i];
+                    for (int i = 0; i < 4; ++i)
+                        h[i] = (_Float16)silu_mul(acc[2 * q][tt][i] * sg[i],
+                                                  acc[2 * q + 1][tt][i] * su[i]);
+                    *reinterpret_cast<f16x4*>(A.h16 + (int64_t)(ae.r0 + c) * A.I + n0) = h;
+                }
             }
-            *reinterpret_cast<f32x4*>(A.y_perm + (int64_t)(r0 + c) * A.H + n0) = y;
+        } else {
+            float sd[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (F::kVq) {
+                const _Float16* sp =
+                    reinterpret_cast<const _Float16*>(base + (int64_t)nrg * nkb * F::TB);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sd[i] = (float)sp[n0 + i];
+            }
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+                const int c = c0 + (lane & 15) + 16 * tt;
+                if (tt < ntt && c < ae.me) {
+                    f32x4 y = acc[q][tt];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[i] *= sd[i];
+                    *reinterpret_cast<f32x4*>(A.y_perm + (int64_t)(ae.r0 + c) * A.H + n0) = y;
+                }
+            }
         }
     }
 }
 
-template <class F, int NTT>
-int launch_fmt(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
+
+template <class F, int NTT, int KS>
+int launch_ks(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
+    constexpr int SETS = kWaves / KS;
     if (phase == 0) {
-        dim3 grid((unsigned)(a.I / 16), (unsigned)slots, (unsigned)chunks);
-        k_gateup<F, NTT><<<grid, 256, 0, s>>>(a);
+        const int nsets = (a.I / 16 + kRpwGateup - 1) / kRpwGateup;
+        dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
+        k_ffn<F, NTT, KS, kRpwGateup, 0><<<grid, 256, 0, s>>>(a);
     } else {
-        dim3 grid((unsigned)(a.H / 16), (unsigned)slots, (unsigned)chunks);
-        k_down<F, NTT><<<grid, 256, 0, s>>>(a);
+        const int nsets = (a.H / 16 + kRpwDown - 1) / kRpwDown;
+        dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
+        k_ffn<F, NTT, KS, kRpwDown, 1><<<grid, 256, 0, s>>>(a);
     }
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
 }
 
+// Few active experts -> split the input dimension over more waves so the
+// whole chip streams; many -> one wave per row set.
+template <class F, int NTT>
+int launch_fmt(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
+    if (slots <= 16) return launch_ks<F, NTT, 4>(a, slots, chunks, phase, s);
+    if (slots <= 64) return launch_ks<F, NTT, 2>(a, slots, chunks, phase, s);
+    return launch_ks<F, NTT, 1>(a, slots, chunks, phase, s);
+}
+
 template <class F>
 int launch_ntt(const DecodeArgs& a, int64_t T, int slots, int phase, hipStream_t s) {
     // an expert has at most T rows (the k experts of a token are distinct)
-    if (T <= 16) return launch_fmt<F, 1>(a, slots, 1, phase, s);
-    if (T <= 32) return launch_fmt<F, 2>(a, slots, 1, phase, s);
-    const int chunks = (int)((T + 63) / 64);
-    return launch_fmt<F, 4>(a, slots, chunks, phase, s);
+    // tokens of an expert go 16 at a time to the z dimension of the grid
+    const int chunks = (int)((T + 15) / 16);
+    return launch_fmt<F, 1>(a, slots, chunks, phase, s);
 }
 
 }  // namespace

@@ -205,6 +205,28 @@ int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16,
                      int64_t T, int32_t k, float* y_perm,
                      void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * The two halves of moe_expert_ffn_q, for callers that keep h themselves
+ * (or time the halves apart).  moe_expert_ffn_q(...) is exactly
+ * moe_expert_gateup_q into a workspace h followed by moe_expert_down_q.
+ *
+ * moe_expert_gateup_q -- h[i] = silu(W_gate[e] x_t) * (W_up[e] x_t) for every
+ *   permuted row i (e, t as above), written as fp16 to
+ *   h_f16 [device] [T*k, I].  ws [device] >= moe_gateup_workspace_bytes(),
+ *   256-byte aligned (holds the fp16 copy of x).
+ * moe_expert_down_q -- y_perm[i] = W_down[e] h[i] (fp32 [T*k, H]) from
+ *   h_f16 [device] [T*k, I] and offsets [device] [E+1].
+ * Same requirements and errors as moe_expert_ffn_q.
+ */
+size_t moe_gateup_workspace_bytes(const moe_qlayer* layer, int64_t T);
+int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16,
+                        const int32_t* perm_src, const int32_t* offsets,
+                        int64_t T, int32_t k, uint16_t* h_f16,
+                        void* ws, size_t ws_bytes, void* stream);
+int moe_expert_down_q(const moe_qlayer* layer, const uint16_t* h_f16,
+                      const int32_t* offsets, int64_t T, int32_t k,
+                      float* y_perm, void* stream);
+
 /* -------------------------------------------------------------- combine */
 
 /*
