@@ -183,8 +183,12 @@ int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16, const i
     if (st) return st;
     for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
         if (!li.count[fmt]) continue;
-        st = launch_ffn_decode(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T, k, h_f16,
-                               nullptr, 0, stream);
+        if (fmt == MOE_FMT_NVFP4 && T >= kPrefillMinTokens)
+            st = launch_ffn_prefill(li.view, li.count[fmt], x16, perm_src, offsets, T, k, h_f16,
+                                    nullptr, 0, stream);
+        else
+            st = launch_ffn_decode(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T, k,
+                                   h_f16, nullptr, 0, stream);
         if (st) return st;
     }
     return MOE_OK;
@@ -202,8 +206,12 @@ int moe_expert_down_q(const moe_qlayer* layer, const uint16_t* h_f16, const int3
     if (!h_f16 || !offsets || !y_perm) return fail(MOE_EINVAL, "moe_expert_down_q: null pointer");
     for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
         if (!li.count[fmt]) continue;
-        st = launch_ffn_decode(li.view, fmt, li.count[fmt], nullptr, nullptr, offsets, T, k,
-                               const_cast<uint16_t*>(h_f16), y_perm, 1, stream);
+        if (fmt == MOE_FMT_NVFP4 && T >= kPrefillMinTokens)
+            st = launch_ffn_prefill(li.view, li.count[fmt], nullptr, nullptr, offsets, T, k,
+                                    const_cast<uint16_t*>(h_f16), y_perm, 1, stream);
+        else
+            st = launch_ffn_decode(li.view, fmt, li.count[fmt], nullptr, nullptr, offsets, T, k,
+                                   const_cast<uint16_t*>(h_f16), y_perm, 1, stream);
         if (st) return st;
     }
     return MOE_OK;

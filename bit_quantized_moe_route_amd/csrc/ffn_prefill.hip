@@ -1,0 +1,300 @@
+// Expert FFN for large token batches (prefill): a grouped GEMM over the
+// active experts with NVFP4 weights decoded in registers.
+//
+// Per active expert e with M_e rows (permuted order r0 .. r0+M_e):
+//   gate/up:  [g | u] = W13[e] X_e^T,  h = silu(g) * u      -> h (fp16)
+//   down:     Y_e = W_down[e] H_e^T                         -> y_perm (fp32)
+// ("GLM-5-NVFP4-MTP", What's quantized: gate, up and down projections.)
+//
+// Work item = (expert, 128-row tile of its tokens) x (256 weight rows).  A
+// workgroup of 4 waves owns one item; wave w owns 64 weight rows (two 32-row
+// A tiles of v_mfma_f32_32x32x16_f16) and all 128 tokens (four 32-token B
+// tiles), i.e. a 64 x 128 fp32 accumulator block.
+//   * weights: each wave loads its rows' packed NVFP4 tiles from HBM straight
+//     into registers (the next 128-input tile is in flight while the current
+//     one is used), decodes 8 weights at a time to fp16 (exact) right before
+//     the MFMA that uses them;
+//   * tokens: the 128 rows x 128 inputs fp16 tile is gathered (through
+//     perm_src for gate/up) into LDS, double-buffered; rows past the
+//     expert's end and inputs past K are zeros;
+//   * gate/up: a 32-row A tile is 16 gate rows + the 16 matching up rows, so
+//     each lane holds g and u of the same (channel, token) and SwiGLU is fused
+//     in registers before the fp16 store of h.
+// A work item finds its (expert, row tile) from the offsets with a wave
+// prefix scan; the grid's y size is an upper bound on the number of items.
+#include "dev_common.h"
+
+namespace moeq {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128;           // tokens per work item
+constexpr int kBN = 256;           // weight rows per work item
+constexpr int kXS = kNvTileK + 8;  // LDS row stride (halves): 128 inputs + 16 B pad
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+
+struct PrefillArgs {
+    const uint8_t* pool;
+    int64_t stride;
+    const int32_t* rec;
+    const int32_t* offsets;
+    const int32_t* perm_src;
+    const _Float16* x16;
+    _Float16* h16;
+    float* y_perm;
+    int E, H, I, k, fmt;
+};
+
+struct WorkItem {
+    int e, r0, me, ridx, m0;
+};
+
+// The s-th (expert, 128-row tile) over the active experts of format `fmt` in
+// ascending expert id; e = -1 past the end.
+__device__ __forceinline__ WorkItem find_item(const int32_t* __restrict__ offsets,
+                                              const int32_t* __restrict__ rec, int E, int fmt,
+                                              int s, int lane) {
+    WorkItem r{-1, 0, 0, 0, 0};
+    int before = 0;
+    for (int g0 = 0; g0 < E; g0 += 64) {
+        const int e = g0 + lane;
+        int o0 = 0, o1 = 0, rc = 0;
+        if (e < E) {
+            o0 = offsets[e];
+            o1 = offsets[e + 1];
+            rc = rec[e];
+        }
+        const int cnt = (o1 > o0 && (rc >> 24) == fmt) ? (o1 - o0 + kBM - 1) / kBM : 0;
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        const int total = __shfl(incl, 63);
+        const int want = s - before;
+        if (want < total) {
+            const bool mine = cnt > 0 && want >= incl - cnt && want < incl;
+            const uint64_t m = __ballot(mine);
+            const int owner = __ffsll((unsigned long long)m) - 1;
+            r.e = g0 + owner;
+            r.r0 = __shfl(o0, owner);
+            r.me = __shfl(o1, owner) - r.r0;
+            r.ridx = __shfl(rc, owner) & 0xffffff;
+            r.m0 = (want - (__shfl(incl, owner) - __shfl(cnt, owner))) * kBM;
+            break;
+        }
+        before += total;
+    }
+    return r;
+}
+
+// One lane's share of a 32-row A tile for one 128-input tile: rows
+// (L & 31) of record groups ga (L < 16 of the 32) / ga + 1, inputs
+// (L >> 5) * 64 .. +64 = two 16-byte code chunks and their 4 scales.
+struct AFrag {
+    u32x4 c0, c1;
+    uint32_t s0, s1;
+};
+
+__device__ __forceinline__ void load_a(AFrag& f, const uint8_t* grp_base, int64_t gstride,
+                                       int lane, bool valid) {
+    if (!valid) {
+        f.c0 = f.c1 = u32x4{0u, 0u, 0u, 0u};
+        f.s0 = f.s1 = 0u;
+        return;
+    }
+    const int row = lane & 31;
+    const uint8_t* tile = grp_base + (row >> 4) * gstride;   // group ga or ga + 1
+    const int l0 = (row & 15) + 32 * (lane >> 5);            // record lane of inputs 64h..
+    const int l1 = l0 + 16;                                  // ... and 64h + 32..
+    f.c0 = load_stream16(tile + l0 * 16);
+    f.c1 = load_stream16(tile + l1 * 16);
+    f.s0 = *reinterpret_cast<const uint16_t*>(tile + kNvScaleOff + l0 * 2);
+    f.s1 = *reinterpret_cast<const uint16_t*>(tile + kNvScaleOff + l1 * 2);
+}
+
+// 8 decoded weights of K-step s (inputs 64h + 8s .. +7 of the tile).
+__device__ __forceinline__ f16x8 a_step(const AFrag& f, int s) {
+    const uint32_t sc = s < 4 ? f.s0 : f.s1;
+    const u32x4 c = s < 4 ? f.c0 : f.c1;
+    f16x2 s0, s1;
+    nv_scales(sc, s0, s1);
+    const f16x2 sv = ((s & 3) < 2) ? s0 : s1;
+    return nv_dequant8(c[s & 3], sv);
+}
+
+template <int PHASE>
+__global__ __launch_bounds__(256, 2) void k_prefill_nv(PrefillArgs A) {
+    __shared__ _Float16 xs[2][kBM * kXS];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const WorkItem it = find_item(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
+    if (it.e < 0) return;
+    const int K = PHASE == 0 ? A.H : A.I;
+    const int nrg = (PHASE == 0 ? 2 * A.I : A.H) / 16;       // record row groups
+    const int nkb = (K + kNvTileK - 1) / kNvTileK;
+    const int64_t gstride = (int64_t)nkb * kNvTileBytes;     // bytes per row group
+    const int g0 = blockIdx.x * (kBN / 16) + wave * 4;       // first row group of the wave
+    const int mcount = min(kBM, it.me - it.m0);
+    const int nbt = (mcount + 31) / 32;                      // 32-token B tiles in use
+    const uint8_t* base = A.pool + (int64_t)it.ridx * A.stride;
+
+    // X staging: thread tid copies 16 bytes (inputs 8 kc .. +7) of rows
+    // (tid >> 4) + 16 j, j = 0..7.
+    const int kc = tid & 15;
+    const _Float16* src[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int row = (tid >> 4) + 16 * j;
+        if (row >= mcount)
+            src[j] = nullptr;
+        else if (PHASE == 0)
+            src[j] = A.x16 + (int64_t)(A.perm_src[it.r0 + it.m0 + row] / A.k) * A.H;
+        else
+            src[j] = A.h16 + (int64_t)(it.r0 + it.m0 + row) * A.I;
+    }
+    auto load_x = [&](int kb, u32x4 (&v)[8]) {
+        const int kk = kb * kNvTileK + 8 * kc;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = (src[j] != nullptr && kk < K) ? *reinterpret_cast<const u32x4*>(src[j] + kk)
+                                                 : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto store_x = [&](int buf, const u32x4 (&v)[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<u32x4*>(&xs[buf][((tid >> 4) + 16 * j) * kXS + 8 * kc]) = v[j];
+    };
+
+    // weights: A tile a of this wave = record groups g0 + 2a, g0 + 2a + 1
+    const bool va0 = g0 < nrg, va1 = g0 + 2 < nrg;
+    const bool vh0 = g0 + 1 < nrg, vh1 = g0 + 3 < nrg;
+    auto load_w = [&](int kb, AFrag& a0, AFrag& a1) {
+        const int row = lane & 31;
+        load_a(a0, base + (int64_t)g0 * gstride + (int64_t)kb * kNvTileBytes, gstride, lane,
+               row < 16 ? va0 : vh0);
+        load_a(a1, base + (int64_t)(g0 + 2) * gstride + (int64_t)kb * kNvTileBytes, gstride, lane,
+               row < 16 ? va1 : vh1);
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[a][q] = f32x16{};
+
+    u32x4 xv[8];
+    AFrag wc0, wc1, wn0, wn1;
+    load_x(0, xv);
+    load_w(0, wc0, wc1);
+    store_x(0, xv);
+    __syncthreads();
+    const int h = lane >> 5;
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int buf = kb & 1;
+        if (kb + 1 < nkb) {
+            load_x(kb + 1, xv);
+            load_w(kb + 1, wn0, wn1);
+        }
+        const _Float16* xb = &xs[buf][(lane & 31) * kXS + 64 * h];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const f16x8 a0 = a_step(wc0, s);
+            const f16x8 a1 = a_step(wc1, s);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q < nbt) {
+                    const f16x8 b = *reinterpret_cast<const f16x8*>(xb + 32 * q * kXS + 8 * s);
+                    acc[0][q] = mfma32(a0, b, acc[0][q]);
+                    acc[1][q] = mfma32(a1, b, acc[1][q]);
+                }
+            }
+        }
+        if (kb + 1 < nkb) {
+            store_x(buf ^ 1, xv);
+            wc0 = wn0;
+            wc1 = wn1;
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane holds D[row 8(i/4) + 4h + i%4][token 32q + (lane & 31)]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int tok = 32 * q + (lane & 31);
+        if (q >= nbt || tok >= mcount) continue;
+        const int64_t prow = it.r0 + it.m0 + tok;            // permuted row
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int ga = g0 + 2 * a;
+            if (PHASE == 0) {
+                if (ga >= nrg) continue;
+                const int ch = 16 * (ga >> 1) + 4 * h;       // channel of rows 4h..4h+3
+                f16x4 h0, h1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    h0[i] = (_Float16)(acc[a][q][i] * acc[a][q][i + 8] /
+                                       (1.0f + expf(-acc[a][q][i])));
+                    h1[i] = (_Float16)(acc[a][q][i + 4] * acc[a][q][i + 12] /
+                                       (1.0f + expf(-acc[a][q][i + 4])));
+                }
+                _Float16* hp = A.h16 + prow * A.I + ch;
+                *reinterpret_cast<f16x4*>(hp) = h0;
+                *reinterpret_cast<f16x4*>(hp + 8) = h1;
+            } else {
+#pragma unroll
+                for (int r8 = 0; r8 < 4; ++r8) {
+                    const int r = 8 * r8 + 4 * h;            // row within the 32-row tile
+                    if (ga + (r >> 4) >= nrg) continue;
+                    f32x4 y = {acc[a][q][4 * r8], acc[a][q][4 * r8 + 1], acc[a][q][4 * r8 + 2],
+                               acc[a][q][4 * r8 + 3]};
+                    *reinterpret_cast<f32x4*>(A.y_perm + prow * A.H + 16 * ga + r) = y;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+int launch_ffn_prefill(const LayerView& L, int n_fmt, const uint16_t* x16,
+                       const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
+                       uint16_t* h16, float* y_perm, int phase, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    PrefillArgs a;
+    a.pool = phase == 0 ? L.pool13[MOE_FMT_NVFP4] : L.pool2[MOE_FMT_NVFP4];
+    a.stride = phase == 0 ? L.stride13[MOE_FMT_NVFP4] : L.stride2[MOE_FMT_NVFP4];
+    a.rec = L.rec;
+    a.offsets = offsets;
+    a.perm_src = perm_src;
+    a.x16 = reinterpret_cast<const _Float16*>(x16);
+    a.h16 = reinterpret_cast<_Float16*>(h16);
+    a.y_perm = y_perm;
+    a.E = L.E;
+    a.H = L.H;
+    a.I = L.I;
+    a.k = k;
+    a.fmt = MOE_FMT_NVFP4;
+    const int64_t tk = T * k;
+    const int64_t active = tk < n_fmt ? tk : n_fmt;
+    // sum over experts of ceil(M_e / 128) <= T*k / 128 + (number of active experts)
+    const int64_t items = tk / kBM + active;
+    if (items == 0) return MOE_OK;
+    const int nrg = (phase == 0 ? 2 * L.I : L.H) / 16;
+    dim3 grid((unsigned)((nrg + kBN / 16 - 1) / (kBN / 16)), (unsigned)items);
+    if (phase == 0)
+        k_prefill_nv<0><<<grid, 256, 0, s>>>(a);
+    else
+        k_prefill_nv<1><<<grid, 256, 0, s>>>(a);
+    MOEQ_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+}  // namespace moeq

@@ -71,6 +71,11 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x1
                       const int32_t* perm_src, const int32_t* offsets, int64_t T,
                       int32_t k, uint16_t* h16, float* y_perm, int phase,
                       void* stream);
+// NVFP4 experts at T >= kPrefillMinTokens use the grouped-GEMM kernels.
+constexpr int64_t kPrefillMinTokens = 128;
+int launch_ffn_prefill(const LayerView& L, int n_fmt, const uint16_t* x16,
+                       const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
+                       uint16_t* h16, float* y_perm, int phase, void* stream);
 int launch_dequant(const LayerView& L, int fmt, int32_t rec_index, int32_t proj,
                    float* out, void* stream);
 

@@ -105,10 +105,11 @@ WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED)}
 
 
 def small_workload(name, E, k, H, I, T, fmt="nvfp4", logits="normal", cfg=100,
-                   n_nvfp4=0, n_hot=0, hot_share=0.0):
+                   n_nvfp4=0, n_hot=0, hot_share=0.0, zipf_s=0.0):
     """A property-test workload with its own seed slot."""
     return Workload(name, cfg, E, k, H, I, (T,), fmt, logits, weight_cfg=cfg,
-                    vq_cfg=cfg, n_nvfp4=n_nvfp4, n_hot=n_hot, hot_share=hot_share)
+                    vq_cfg=cfg, n_nvfp4=n_nvfp4, n_hot=n_hot, hot_share=hot_share,
+                    zipf_s=zipf_s)
 
 
 # --------------------------------------------------------------------------

@@ -26,6 +26,14 @@ SMALL = {
                                         logits="hot", cfg=104, n_nvfp4=9, n_hot=4, hot_share=0.6),
     "nv_k1": synth.small_workload("nv_k1", E=4, k=1, H=128, I=32, T=5, cfg=105),
     "nv_kE": synth.small_workload("nv_kE", E=6, k=6, H=160, I=64, T=3, cfg=106),
+    # token counts that take the grouped-GEMM path: several 128-row tiles
+    # per expert, skewed counts, ragged H (odd number of 16-row groups) and I
+    "nv_prefill": synth.small_workload("nv_prefill", E=8, k=2, H=512, I=256, T=700, cfg=108),
+    "nv_prefill_ragged": synth.small_workload("nv_prefill_ragged", E=16, k=4, H=272, I=80,
+                                              T=300, logits="zipf", zipf_s=1.1, cfg=109),
+    "mixed_prefill": synth.small_workload("mixed_prefill", E=12, k=3, H=256, I=128, T=260,
+                                          fmt="mixed", logits="hot", cfg=110, n_nvfp4=5,
+                                          n_hot=3, hot_share=0.6),
 }
 
 _layers = {}
