@@ -15,13 +15,15 @@
 //     one is used), decodes 8 weights at a time to fp16 (exact) right before
 //     the MFMA that uses them;
 //   * tokens: the 128 rows x 128 inputs fp16 tile is gathered (through
-//     perm_src for gate/up) into LDS, double-buffered; rows past the
-//     expert's end and inputs past K are zeros;
+//     perm_src for gate/up) into LDS with direct-to-LDS loads (no register
+//     round trip), double-buffered, XOR-swizzled against bank conflicts;
 //   * gate/up: a 32-row A tile is 16 gate rows + the 16 matching up rows, so
 //     each lane holds g and u of the same (channel, token) and SwiGLU is fused
 //     in registers before the fp16 store of h.
 // A work item finds its (expert, row tile) from the offsets with a wave
 // prefix scan; the grid's y size is an upper bound on the number of items.
+#include <type_traits>
+
 #include "dev_common.h"
 
 namespace moeq {
@@ -32,7 +34,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128;           // tokens per work item
 constexpr int kBN = 256;           // weight rows per work item
-constexpr int kXS = kNvTileK + 8;  // LDS row stride (halves): 128 inputs + 16 B pad
+// s_waitcnt immediate for "vmcnt(0)", other counters unconstrained (gfx9 encoding:
+// vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
+constexpr int kVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 acc) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
@@ -113,8 +117,8 @@ __device__ __forceinline__ void load_a(AFrag& f, const uint8_t* grp_base, int64_
     const uint8_t* tile = grp_base + (row >> 4) * gstride;   // group ga or ga + 1
     const int l0 = (row & 15) + 32 * (lane >> 5);            // record lane of inputs 64h..
     const int l1 = l0 + 16;                                  // ... and 64h + 32..
-    f.c0 = load_stream16(tile + l0 * 16);
-    f.c1 = load_stream16(tile + l1 * 16);
+    f.c0 = *reinterpret_cast<const u32x4*>(tile + l0 * 16);
+    f.c1 = *reinterpret_cast<const u32x4*>(tile + l1 * 16);
     f.s0 = *reinterpret_cast<const uint16_t*>(tile + kNvScaleOff + l0 * 2);
     f.s1 = *reinterpret_cast<const uint16_t*>(tile + kNvScaleOff + l1 * 2);
 }
@@ -131,7 +135,7 @@ __device__ __forceinline__ f16x8 a_step(const AFrag& f, int s) {
 
 template <int PHASE>
 __global__ __launch_bounds__(256, 2) void k_prefill_nv(PrefillArgs A) {
-    __shared__ _Float16 xs[2][kBM * kXS];
+    __shared__ _Float16 xs[2][kBM * kNvTileK];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -146,31 +150,29 @@ __global__ __launch_bounds__(256, 2) void k_prefill_nv(PrefillArgs A) {
     const int nbt = (mcount + 31) / 32;                      // 32-token B tiles in use
     const uint8_t* base = A.pool + (int64_t)it.ridx * A.stride;
 
-    // X staging: thread tid copies 16 bytes (inputs 8 kc .. +7) of rows
-    // (tid >> 4) + 16 j, j = 0..7.
-    const int kc = tid & 15;
-    const _Float16* src[8];
+    // X staging with direct-to-LDS loads: wave-instruction j of wave w fills
+    // rows 4 (8 w + j) .. +3 (1 KB); lane L writes row + (L >> 4), physical
+    // 16-byte chunk L & 15, which holds logical chunk (L & 15) ^ (row & 15)
+    // (an XOR swizzle that keeps the B-operand reads free of bank conflicts).
+    // Rows past the expert's end re-read its last row: they only feed output
+    // columns that are never stored.  Inputs past K re-read input 0 of the
+    // row: the matching weights are zero codes with zero scales.
+    const _Float16* xsrc = PHASE == 0 ? A.x16 : A.h16;
+    int trow[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int row = (tid >> 4) + 16 * j;
-        if (row >= mcount)
-            src[j] = nullptr;
-        else if (PHASE == 0)
-            src[j] = A.x16 + (int64_t)(A.perm_src[it.r0 + it.m0 + row] / A.k) * A.H;
-        else
-            src[j] = A.h16 + (int64_t)(it.r0 + it.m0 + row) * A.I;
+        const int row = min(4 * (8 * wave + j) + (lane >> 4), mcount - 1);
+        trow[j] = PHASE == 0 ? A.perm_src[it.r0 + it.m0 + row] / A.k : it.r0 + it.m0 + row;
     }
-    auto load_x = [&](int kb, u32x4 (&v)[8]) {
-        const int kk = kb * kNvTileK + 8 * kc;
+    auto issue_x = [&](int kb, int buf) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[j] = (src[j] != nullptr && kk < K) ? *reinterpret_cast<const u32x4*>(src[j] + kk)
-                                                 : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto store_x = [&](int buf, const u32x4 (&v)[8]) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u32x4*>(&xs[buf][((tid >> 4) + 16 * j) * kXS + 8 * kc]) = v[j];
+        for (int j = 0; j < 8; ++j) {
+            const int row = 4 * (8 * wave + j) + (lane >> 4);
+            int kk = kb * kNvTileK + 8 * ((lane & 15) ^ (row & 15));
+            if (kk >= K) kk = 0;
+            __builtin_amdgcn_global_load_lds(xsrc + (int64_t)trow[j] * K + kk,
+                                             &xs[buf][4 * (8 * wave + j) * kNvTileK], 16, 0, 0);
+        }
     };
 
     // weights: A tile a of this wave = record groups g0 + 2a, g0 + 2a + 1
@@ -190,39 +192,53 @@ __global__ __launch_bounds__(256, 2) void k_prefill_nv(PrefillArgs A) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[a][q] = f32x16{};
 
-    u32x4 xv[8];
-    AFrag wc0, wc1, wn0, wn1;
-    load_x(0, xv);
-    load_w(0, wc0, wc1);
-    store_x(0, xv);
-    __syncthreads();
     const int h = lane >> 5;
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nkb) {
-            load_x(kb + 1, xv);
-            load_w(kb + 1, wn0, wn1);
-        }
-        const _Float16* xb = &xs[buf][(lane & 31) * kXS + 64 * h];
+    // The main loop, specialised for the number of live 32-token B tiles so
+    // that no branch sits between the decode and the MFMAs; register buffers
+    // and LDS buffers alternate with a compile-time parity.
+    auto run = [&](auto nb_c) {
+        constexpr int NB = decltype(nb_c)::value;
+        AFrag w[2][2];
+        issue_x(0, 0);
+        load_w(0, w[0][0], w[0][1]);
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+        // B reads: row (lane & 31) of each 32-token tile, logical chunk 8h + s
+        const _Float16* xrow0 = &xs[0][(lane & 31) * kNvTileK];
+        auto step = [&](int kb, auto p_c) {
+            constexpr int P = decltype(p_c)::value;
+            const bool more = kb + 1 < nkb;
+            if (more) {
+                issue_x(kb + 1, P ^ 1);
+                load_w(kb + 1, w[P ^ 1][0], w[P ^ 1][1]);
+            }
+            const _Float16* xb = xrow0 + P * (kBM * kNvTileK);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const f16x8 a0 = a_step(wc0, s);
-            const f16x8 a1 = a_step(wc1, s);
+            for (int s = 0; s < 8; ++s) {
+                const f16x8 a0 = a_step(w[P][0], s);
+                const f16x8 a1 = a_step(w[P][1], s);
+                const int cofs = 8 * ((8 * h + s) ^ (lane & 15));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (q < nbt) {
-                    const f16x8 b = *reinterpret_cast<const f16x8*>(xb + 32 * q * kXS + 8 * s);
+                for (int q = 0; q < NB; ++q) {
+                    const f16x8 b =
+                        *reinterpret_cast<const f16x8*>(xb + 32 * q * kNvTileK + cofs);
                     acc[0][q] = mfma32(a0, b, acc[0][q]);
                     acc[1][q] = mfma32(a1, b, acc[1][q]);
                 }
             }
+            __builtin_amdgcn_s_waitcnt(kVmcnt0);   // next stage's LDS writes landed
+            __syncthreads();
+        };
+        for (int kb = 0; kb < nkb; kb += 2) {
+            step(kb, std::integral_constant<int, 0>{});
+            if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{});
         }
-        if (kb + 1 < nkb) {
-            store_x(buf ^ 1, xv);
-            wc0 = wn0;
-            wc1 = wn1;
-        }
-        __syncthreads();
+    };
+    switch (nbt) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        default: run(std::integral_constant<int, 4>{}); break;
     }
 
     // epilogue: lane holds D[row 8(i/4) + 4h + i%4][token 32q + (lane & 31)]
