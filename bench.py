@@ -241,6 +241,9 @@ def main():
     ap.add_argument("--extra", default="decode1,decode8,prefill,vq,mixed8,mixed32",
                     help="comma list of other workloads to measure ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (the reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -258,6 +261,20 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moeq.lib()
+    copy_gbs = None
+    if args.probe_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        copy_gbs = 3 * 2 * n / (time.perf_counter() - t0) / 1e9
+        log(f"plain 1 GiB copy: {copy_gbs:.0f} GB/s (read + write)")
+        del src, dst
     wl = synth.DECODE
     t0 = time.perf_counter()
     log("building the NVFP4 decode layer (256 experts, H 6144, I 2048) ...")
