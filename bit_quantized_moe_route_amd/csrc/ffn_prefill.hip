@@ -20,8 +20,9 @@
 //   * gate/up: a 32-row A tile is 16 gate rows + the 16 matching up rows, so
 //     each lane holds g and u of the same (channel, token) and SwiGLU is fused
 //     in registers before the fp16 store of h.
-// A work item finds its (expert, row tile) from the offsets with a wave
-// prefix scan; the grid's y size is an upper bound on the number of items.
+// A workgroup finds its (expert, row tile, weight tile) from the offsets with
+// a wave prefix scan; the grid is an upper bound on the work list (slots past
+// its end exit at once), ordered so that each XCD takes a contiguous slice.
 #include <type_traits>
 
 #include "dev_common.h"
@@ -58,42 +59,68 @@ struct WorkItem {
     int e, r0, me, ridx, m0;
 };
 
-// The s-th (expert, 128-row tile) over the active experts of format `fmt` in
-// ascending expert id; e = -1 past the end.
-__device__ __forceinline__ WorkItem find_item(const int32_t* __restrict__ offsets,
-                                              const int32_t* __restrict__ rec, int E, int fmt,
-                                              int s, int lane) {
+// Locates work item w of the list (item-major, nnt weight tiles per item,
+// items = (expert, 128-row tile) over the active experts of `fmt` in
+// ascending expert id).  All offsets/record loads are issued up front (one
+// memory round trip); the item count comes from the same registers.
+// Returns e = -1 if w is past the end of the list.
+__device__ __forceinline__ WorkItem locate_item(const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ rec, int E, int fmt,
+                                                int nnt, int blk, int lane, int& ntile) {
+    constexpr int kMaxChunks = MOE_MAX_E / 64;
+    int o0[kMaxChunks], o1[kMaxChunks], rc[kMaxChunks], cnt[kMaxChunks];
+    const int nch = (E + 63) / 64;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        const int e = 64 * c + lane;
+        const bool in = c < nch && e < E;
+        o0[c] = in ? offsets[e] : 0;
+        o1[c] = in ? offsets[e + 1] : 0;
+        rc[c] = in ? rec[e] : 0;
+    }
+    int total = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        cnt[c] = (o1[c] > o0[c] && (rc[c] >> 24) == fmt) ? (o1[c] - o0[c] + kBM - 1) / kBM : 0;
+        int t = cnt[c];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+        total += t;
+    }
+    // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
+    // so XCD blk % 8 takes a contiguous slice of the work list.  The weight
+    // tiles of one token tile, and the next few token tiles of the same
+    // expert, then share that XCD's L2.
     WorkItem r{-1, 0, 0, 0, 0};
+    const int nwork = total * nnt;
+    const int quota = (nwork + 7) / 8;
+    const int slot = blk >> 3;
+    const int w = (blk & 7) * quota + slot;
+    if (slot >= quota || w >= nwork) return r;
+    ntile = w % nnt;
+    const int want_item = w / nnt;
     int before = 0;
-    for (int g0 = 0; g0 < E; g0 += 64) {
-        const int e = g0 + lane;
-        int o0 = 0, o1 = 0, rc = 0;
-        if (e < E) {
-            o0 = offsets[e];
-            o1 = offsets[e + 1];
-            rc = rec[e];
-        }
-        const int cnt = (o1 > o0 && (rc >> 24) == fmt) ? (o1 - o0 + kBM - 1) / kBM : 0;
-        int incl = cnt;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        int incl = cnt[c];
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int v = __shfl_up(incl, off);
             if (lane >= off) incl += v;
         }
-        const int total = __shfl(incl, 63);
-        const int want = s - before;
-        if (want < total) {
-            const bool mine = cnt > 0 && want >= incl - cnt && want < incl;
+        const int tot = __shfl(incl, 63);
+        const int want = want_item - before;
+        if (r.e < 0 && want >= 0 && want < tot) {
+            const bool mine = cnt[c] > 0 && want >= incl - cnt[c] && want < incl;
             const uint64_t m = __ballot(mine);
             const int owner = __ffsll((unsigned long long)m) - 1;
-            r.e = g0 + owner;
-            r.r0 = __shfl(o0, owner);
-            r.me = __shfl(o1, owner) - r.r0;
-            r.ridx = __shfl(rc, owner) & 0xffffff;
-            r.m0 = (want - (__shfl(incl, owner) - __shfl(cnt, owner))) * kBM;
-            break;
+            r.e = 64 * c + owner;
+            r.r0 = __shfl(o0[c], owner);
+            r.me = __shfl(o1[c], owner) - r.r0;
+            r.ridx = __shfl(rc[c], owner) & 0xffffff;
+            r.m0 = (want - (__shfl(incl, owner) - __shfl(cnt[c], owner))) * kBM;
         }
-        before += total;
+        before += tot;
     }
     return r;
 }
@@ -139,13 +166,15 @@ __global__ __launch_bounds__(256, 2) void k_prefill_nv(PrefillArgs A) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const WorkItem it = find_item(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
-    if (it.e < 0) return;
     const int K = PHASE == 0 ? A.H : A.I;
     const int nrg = (PHASE == 0 ? 2 * A.I : A.H) / 16;       // record row groups
+    const int nnt = (nrg + kBN / 16 - 1) / (kBN / 16);        // 256-row weight tiles
+    int ntile = 0;
+    const WorkItem it = locate_item(A.offsets, A.rec, A.E, A.fmt, nnt, blockIdx.x, lane, ntile);
+    if (it.e < 0) return;
     const int nkb = (K + kNvTileK - 1) / kNvTileK;
     const int64_t gstride = (int64_t)nkb * kNvTileBytes;     // bytes per row group
-    const int g0 = blockIdx.x * (kBN / 16) + wave * 4;       // first row group of the wave
+    const int g0 = ntile * (kBN / 16) + wave * 4;             // first row group of the wave
     const int mcount = min(kBM, it.me - it.m0);
     const int nbt = (mcount + 31) / 32;                      // 32-token B tiles in use
     const uint8_t* base = A.pool + (int64_t)it.ridx * A.stride;
@@ -304,7 +333,11 @@ int launch_ffn_prefill(const LayerView& L, int n_fmt, const uint16_t* x16,
     const int64_t items = tk / kBM + active;
     if (items == 0) return MOE_OK;
     const int nrg = (phase == 0 ? 2 * L.I : L.H) / 16;
-    dim3 grid((unsigned)((nrg + kBN / 16 - 1) / (kBN / 16)), (unsigned)items);
+    const int64_t nnt = (nrg + kBN / 16 - 1) / (kBN / 16);
+    // 8 slices of ceil(items * nnt / 8) workgroups cover every item; slots past
+    // the actual item count exit at once
+    const int64_t nblocks = 8 * ((items * nnt + 7) / 8);
+    dim3 grid((unsigned)nblocks);
     if (phase == 0)
         k_prefill_nv<0><<<grid, 256, 0, s>>>(a);
     else
