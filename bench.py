@@ -100,8 +100,7 @@ class Runner:
     def step(self, r, timed):
         moeq = self.moeq
         lg, x = self.batches[r % len(self.batches)]
-        moeq.route_topk(lg, self.k, self.ids, self.w)
-        moeq.permute(self.ids, self.wl.E, self.perm)
+        moeq.route_permute(lg, self.k, self.wl.E, (self.ids, self.w) + self.perm)
         counts, offsets, perm_src, inv_perm = self.perm
         if timed:
             e0 = self.torch.cuda.Event(enable_timing=True)
@@ -128,6 +127,25 @@ class Runner:
         gu_ms = [e0.elapsed_time(e1) for _, e0, e1 in self.ev]
         return dt, gu_ms
 
+    def run_graph(self, steps, warmup):
+        """The same steps replayed from HIP graphs, one captured per input
+        batch of the pool (the kernels and buffers are those of `step`)."""
+        torch = self.torch
+        graphs = []
+        for r in range(len(self.batches)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(r, False)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[(warmup + i) % len(graphs)].replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
     def bytes_of(self, r, which):
         """Algorithmic packed-weight bytes of batch r: 'all' (codes + scales
         of every touched expert, VQ codebooks once) or 'gateup'."""
@@ -145,8 +163,12 @@ class Runner:
 
 
 def measure(layer, wl, T, steps, warmup, dev, reps=16):
+    """Eager launches (per-launch HIP events around the gate/up call), then
+    the same steps replayed from HIP graphs; the headline figures are the
+    graph replay's, the kernel-level ones the eager run's."""
     rn = Runner(layer, wl, T, reps, dev)
-    dt, gu_ms = rn.run(steps, warmup)
+    dte, gu_ms = rn.run(steps, warmup)
+    dt = rn.run_graph(steps, warmup)
     idx = [warmup + i for i in range(steps)]
     all_bytes = sum(rn.bytes_of(r, "all") for r in idx)
     gu_bytes = sum(rn.bytes_of(r, "gateup") for r in idx)
@@ -155,6 +177,8 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16):
         "T": T,
         "tokens_per_s": T * steps / dt,
         "ms_per_step": dt / steps * 1e3,
+        "tokens_per_s_eager": T * steps / dte,
+        "ms_per_step_eager": dte / steps * 1e3,
         "packed_GBps": all_bytes / dt / 1e9,
         "packed_frac_hbm": all_bytes / dt / 1e9 / HBM_PEAK_GBS,
         "experts_touched_mean": sum(len(rn.touched[r % reps]) for r in idx) / steps,

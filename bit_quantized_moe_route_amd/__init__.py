@@ -67,6 +67,7 @@ _PROTOS = {
     "moe_route_topk": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
     "moe_ffn_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64, _I32]),
     "moe_expert_ffn_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _P, _I64, _I32, _P,
                                         _P, _SZ, _P]),
@@ -311,6 +312,26 @@ def permute(topk_ids, E, out=None):
                          _dptr(perm_src), _dptr(inv_perm), _dptr(ws), nws, _stream(dev)),
            "moe_permute")
     return counts, offsets, perm_src, inv_perm
+
+
+def route_permute(logits, k, E=None, out=None):
+    """route_topk + permute in one call (one launch for T*k <= 4096).
+    Returns topk_ids, topk_w, counts, offsets, perm_src, inv_perm."""
+    torch = _torch()
+    _need_cuda(logits)
+    T, E_ = logits.shape
+    E = E_ if E is None else E
+    dev = logits.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev))
+    _check(lib().moe_route_permute(_dptr(logits), T, E, k, *[_dptr(t) for t in out],
+                                   _stream(dev)), "moe_route_permute")
+    return out
 
 
 def ffn_workspace(layer, T, k):

@@ -64,6 +64,10 @@ int launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
                    int32_t* counts, int32_t* offsets, int32_t* perm_src,
                    int32_t* inv_perm, void* ws, void* stream);
 size_t permute_ws_bytes(int64_t T, int32_t k, int32_t E);
+bool route_permute_fused_ok(int64_t T, int32_t k);
+int launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
+                         float* w, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                         int32_t* inv_perm, void* stream);
 int launch_combine(const float* y_perm, const int32_t* inv_perm, const float* w,
                    int64_t T, int32_t k, int32_t H, float* out, void* stream);
 int launch_x_to_f16(const uint16_t* x, int64_t n, uint16_t* x16, void* stream);

@@ -1,4 +1,5 @@
-// Token permutation: a stable counting sort of the T*k assignments by expert.
+// Token permutation: a stable counting sort of the T*k assignments by expert,
+// and the fused route + permute kernel for small batches.
 //
 // One workgroup of 1024 threads:
 //   1. histogram of expert ids in LDS;
@@ -10,7 +11,7 @@
 //      peers in earlier waves of the chunk (per-wave counts in LDS), plus
 //      the running count of that expert from earlier chunks.
 // The result is unique, so it does not depend on timing.
-#include "dev_common.h"
+#include "topk_dev.h"
 
 namespace moeq {
 
@@ -18,14 +19,19 @@ namespace {
 
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
+// fused route + permute: the ids stay in LDS; T*k up to this many
+constexpr int kFusedMaxAssign = 4096;
 
-__global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restrict__ ids,
-                                                          int n, int E,
-                                                          int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ perm_src,
-                                                          int32_t* __restrict__ inv_perm) {
-    extern __shared__ int smem[];
+__host__ __device__ constexpr size_t permute_lds_bytes(int E) {
+    return (size_t)(2 * E + kPermWaves) * sizeof(int) + (size_t)kPermWaves * E;
+}
+
+// ids may point to global memory or to LDS.
+__device__ __forceinline__ void permute_body(const int32_t* ids, int n, int E,
+                                             int32_t* __restrict__ counts,
+                                             int32_t* __restrict__ offsets,
+                                             int32_t* __restrict__ perm_src,
+                                             int32_t* __restrict__ inv_perm, int* smem) {
     int* hist = smem;                 // [E]
     int* run = smem + E;              // [E]
     int* wtot = smem + 2 * E;         // [kPermWaves]
@@ -95,6 +101,40 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
     }
 }
 
+__global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restrict__ ids,
+                                                          int n, int E,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ perm_src,
+                                                          int32_t* __restrict__ inv_perm) {
+    extern __shared__ int smem[];
+    permute_body(ids, n, E, counts, offsets, perm_src, inv_perm, smem);
+}
+
+// Route + permute in one workgroup: wave w routes tokens w, w + 16, ...,
+// writing ids/weights to global memory and the ids to LDS, then the
+// workgroup permutes from LDS.
+template <int VPL>
+__global__ __launch_bounds__(kPermThreads) void k_route_permute(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm) {
+    extern __shared__ int smem[];
+    int32_t* lds_ids = smem;                       // [T*k]
+    int* psmem = smem + kFusedMaxAssign;           // permute scratch
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    for (int t = wave; t < T; t += kPermWaves) {
+        route_token<VPL>(logits + (int64_t)t * E, E, k, lane, ids + (int64_t)t * k,
+                         w + (int64_t)t * k);
+        // lane 0 wrote the ids to global; it also puts them in LDS
+        if (lane == 0)
+            for (int j = 0; j < k; ++j) lds_ids[t * k + j] = ids[t * k + j];
+    }
+    __syncthreads();
+    permute_body(lds_ids, T * k, E, counts, offsets, perm_src, inv_perm, psmem);
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int64_t, int32_t, int32_t) { return 0; }
@@ -104,8 +144,25 @@ int launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t*
                    void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int n = (int)(T * k);
-    size_t lds = (size_t)(2 * E + kPermWaves) * sizeof(int) + (size_t)kPermWaves * E;
-    k_permute<<<1, kPermThreads, lds, s>>>(ids, n, E, counts, offsets, perm_src, inv_perm);
+    k_permute<<<1, kPermThreads, permute_lds_bytes(E), s>>>(ids, n, E, counts, offsets, perm_src,
+                                                            inv_perm);
+    MOEQ_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+bool route_permute_fused_ok(int64_t T, int32_t k) { return T * k <= kFusedMaxAssign; }
+
+int launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
+                         float* w, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                         int32_t* inv_perm, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const size_t lds = (size_t)kFusedMaxAssign * sizeof(int32_t) + permute_lds_bytes(E);
+    if (E <= 256)
+        k_route_permute<4><<<1, kPermThreads, lds, s>>>(logits, (int)T, E, k, ids, w, counts,
+                                                        offsets, perm_src, inv_perm);
+    else
+        k_route_permute<16><<<1, kPermThreads, lds, s>>>(logits, (int)T, E, k, ids, w, counts,
+                                                         offsets, perm_src, inv_perm);
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
 }

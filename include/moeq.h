@@ -168,6 +168,18 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
                 int32_t* counts, int32_t* offsets, int32_t* perm_src,
                 int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_route_permute -- moe_route_topk followed by moe_permute, with the
+ * same outputs bit for bit; for T*k <= 4096 both run in one workgroup (one
+ * launch, the ids never leave the chip between the two steps), which is
+ * what a decode step wants.  Same arguments, limits and errors as the two
+ * calls; no workspace.
+ */
+int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
+                      int32_t* topk_ids, float* topk_w, int32_t* counts,
+                      int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
+                      void* stream);
+
 /* ------------------------------------------------------------ expert FFN */
 
 /* Workspace bytes moe_expert_ffn_q needs (the SwiGLU activations h). */

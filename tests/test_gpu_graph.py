@@ -1,0 +1,76 @@
+"""The forward captured in a HIP graph: every replay, with eager work and
+synchronisations in between, equals the eager result bit for bit; and the
+fused route + permute call equals the two separate calls bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_moe_route_amd as moeq
+import synth
+from tests.gpu_common import build_small_layer, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (32, 256, 8), (512, 256, 8), (700, 64, 8),
+                                   (5, 1024, 16), (3, 4, 1)])
+def test_route_permute_equals_separate_calls(T, E, k):
+    say("route_permute", T, E, k)
+    g = np.random.default_rng(T + E)
+    lg = torch.from_numpy(g.random((T, E)).astype(np.float32)).to(DEV)
+    fused = moeq.route_permute(lg, k)
+    ids, w = moeq.route_topk(lg, k)
+    perm = moeq.permute(ids, E)
+    for a, b, nm in zip(fused, (ids, w) + tuple(perm),
+                        ("ids", "w", "counts", "offsets", "perm_src", "inv_perm")):
+        assert torch.equal(a, b), nm
+
+
+def test_graph_replays_equal_eager():
+    wl = synth.small_workload("graph_mixed", E=24, k=6, H=384, I=96, T=20, fmt="mixed",
+                              logits="hot", cfg=111, n_nvfp4=9, n_hot=4, hot_share=0.6)
+    say("graph replays", wl.name)
+    layer = build_small_layer(wl, DEV)
+    T, k = wl.T[0], wl.k
+    lg = torch.from_numpy(synth.logits(wl, T)).to(DEV)
+    x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(DEV)
+    bufs = dict(
+        rp=(torch.empty((T, k), dtype=torch.int32, device=DEV),
+            torch.empty((T, k), dtype=torch.float32, device=DEV),
+            torch.empty(wl.E, dtype=torch.int32, device=DEV),
+            torch.empty(wl.E + 1, dtype=torch.int32, device=DEV),
+            torch.empty(T * k, dtype=torch.int32, device=DEV),
+            torch.empty(T * k, dtype=torch.int32, device=DEV)),
+        h=torch.empty((T * k, wl.I), dtype=torch.float16, device=DEV),
+        y=torch.empty((T * k, wl.H), dtype=torch.float32, device=DEV),
+        out=torch.empty((T, wl.H), dtype=torch.float32, device=DEV),
+        ws=moeq.gateup_workspace(layer, T))
+
+    def step():
+        ids, w, counts, offsets, perm_src, inv_perm = moeq.route_permute(lg, k, wl.E, bufs["rp"])
+        moeq.expert_gateup_q(layer, x, perm_src, offsets, k, bufs["h"], bufs["ws"])
+        moeq.expert_down_q(layer, bufs["h"], offsets, k, bufs["y"])
+        moeq.combine(bufs["y"], inv_perm, w, bufs["out"])
+
+    step()
+    torch.cuda.synchronize()
+    eager = bufs["out"].clone()
+    eager_y = bufs["y"].clone()
+    ref = moeq.forward(layer, x, lg, k)["out"]
+    assert torch.equal(eager, ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = torch.from_numpy(synth.logits(wl, T, rep=5)).to(DEV)
+    for i in range(4):
+        bufs["out"].zero_()
+        bufs["y"].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["out"], eager), f"replay {i}"
+        assert torch.equal(bufs["y"], eager_y), f"replay {i}"
+        # eager work of the program between replays
+        moeq.forward(layer, x, other, k)
+        torch.cuda.synchronize()
