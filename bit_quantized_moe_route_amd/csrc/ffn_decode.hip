@@ -25,7 +25,7 @@ namespace moeq {
 
 namespace {
 
-constexpr int kWaves = 4;
+
 
 // Per-format tile traits ----------------------------------------------------
 struct NvFmt {
@@ -184,10 +184,10 @@ constexpr int kMinWaves = MOEQ_MIN_WAVES;
 // per input tile and used for all 2*RPW (or RPW) weight tiles of the wave.
 // grid: x = sets of (4/KS) waves' rows, y = active-expert slot, z = chunk of
 // 16*NTT rows of the expert.
-template <class F, int NTT, int KS, int RPW, int PHASE>
-__global__ __launch_bounds__(256, kMinWaves) void k_ffn(DecodeArgs A) {
+template <class F, int NTT, int KS, int RPW, int PHASE, int WV>
+__global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
     constexpr int NM = PHASE == 0 ? 2 * RPW : RPW;   // weight tiles per input tile
-    constexpr int SETS = kWaves / KS;                // row sets per workgroup
+    constexpr int SETS = WV / KS;                    // row sets per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const ActiveExpert ae = find_active_expert(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256, kMinWaves) void k_ffn(DecodeArgs A) {
 
     if constexpr (KS > 1) {
         // sum the KS partial tiles of a row set in a fixed order (wave order)
-        __shared__ f32x4 red[kWaves][NM][64];
+        __shared__ f32x4 red[WV][NM][64];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
             if (tt >= ntt) break;
@@ -304,29 +304,30 @@ __global__ __launch_bounds__(256, kMinWaves) void k_ffn(DecodeArgs A) {
 }
 
 
-template <class F, int NTT, int KS>
+template <class F, int NTT, int KS, int WV>
 int launch_ks(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
-    constexpr int SETS = kWaves / KS;
+    constexpr int SETS = WV / KS;
     if (phase == 0) {
         const int nsets = (a.I / 16 + kRpwGateup - 1) / kRpwGateup;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
-        k_ffn<F, NTT, KS, kRpwGateup, 0><<<grid, 256, 0, s>>>(a);
+        k_ffn<F, NTT, KS, kRpwGateup, 0, WV><<<grid, 64 * WV, 0, s>>>(a);
     } else {
         const int nsets = (a.H / 16 + kRpwDown - 1) / kRpwDown;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
-        k_ffn<F, NTT, KS, kRpwDown, 1><<<grid, 256, 0, s>>>(a);
+        k_ffn<F, NTT, KS, kRpwDown, 1, WV><<<grid, 64 * WV, 0, s>>>(a);
     }
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
 }
 
 // Few active experts -> split the input dimension over more waves so the
-// whole chip streams; many -> one wave per row set.
+// whole chip streams; many -> one wave per row set.  (An 8-way split in
+// 8-wave workgroups measured slower at one token than this 4-way split.)
 template <class F, int NTT>
 int launch_fmt(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
-    if (slots <= 16) return launch_ks<F, NTT, 4>(a, slots, chunks, phase, s);
-    if (slots <= 64) return launch_ks<F, NTT, 2>(a, slots, chunks, phase, s);
-    return launch_ks<F, NTT, 1>(a, slots, chunks, phase, s);
+    if (slots <= 16) return launch_ks<F, NTT, 4, 4>(a, slots, chunks, phase, s);
+    if (slots <= 64) return launch_ks<F, NTT, 2, 4>(a, slots, chunks, phase, s);
+    return launch_ks<F, NTT, 1, 4>(a, slots, chunks, phase, s);
 }
 
 template <class F>
