@@ -34,7 +34,17 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128;           // tokens per work item
-constexpr int kBN = 256;           // weight rows per work item
+// Workgroup shape: waves of 64 weight rows each, and token-tile buffers.
+// (Measured: 4 waves x 2 buffers beats 8 waves x 3 buffers and 8 x 2.)
+#ifndef MOEQ_PF_WAVES
+#define MOEQ_PF_WAVES 4
+#endif
+#ifndef MOEQ_PF_STAGES
+#define MOEQ_PF_STAGES 2
+#endif
+constexpr int kPrefillWaves = MOEQ_PF_WAVES;
+constexpr int kPrefillStages = MOEQ_PF_STAGES;
+constexpr int kBN = 64 * kPrefillWaves;   // weight rows per work item
 // s_waitcnt immediate for "vmcnt(0)", other counters unconstrained (gfx9 encoding:
 // vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
 constexpr int kVmcnt0 = 0x0F70;
@@ -160,47 +170,55 @@ __device__ __forceinline__ f16x8 a_step(const AFrag& f, int s) {
     return nv_dequant8(c[s & 3], sv);
 }
 
+// WV waves per workgroup (64 weight rows each), NS token-tile buffers in LDS
+// (NS - 1 tiles in flight ahead of the one in use).  (They are file-level
+// constants, not template parameters: a __shared__ array sized by a template
+// parameter loses its host-side launch stub with this compiler.)
 template <int PHASE>
-__global__ __launch_bounds__(256, 2) void k_prefill_nv(PrefillArgs A) {
-    __shared__ _Float16 xs[2][kBM * kNvTileK];
+__global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArgs A) {
+    constexpr int WV = kPrefillWaves;
+    constexpr int NS = kPrefillStages;
+    constexpr int BN = 64 * WV;        // weight rows per work item
+    constexpr int JX = 32 / WV;        // 1 KB staging loads per wave per token tile
+    __shared__ _Float16 xs[kPrefillStages][kBM * kNvTileK];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int K = PHASE == 0 ? A.H : A.I;
     const int nrg = (PHASE == 0 ? 2 * A.I : A.H) / 16;       // record row groups
-    const int nnt = (nrg + kBN / 16 - 1) / (kBN / 16);        // 256-row weight tiles
+    const int nnt = (nrg + BN / 16 - 1) / (BN / 16);          // weight tiles of BN rows
     int ntile = 0;
     const WorkItem it = locate_item(A.offsets, A.rec, A.E, A.fmt, nnt, blockIdx.x, lane, ntile);
     if (it.e < 0) return;
     const int nkb = (K + kNvTileK - 1) / kNvTileK;
     const int64_t gstride = (int64_t)nkb * kNvTileBytes;     // bytes per row group
-    const int g0 = ntile * (kBN / 16) + wave * 4;             // first row group of the wave
+    const int g0 = ntile * (BN / 16) + wave * 4;              // first row group of the wave
     const int mcount = min(kBM, it.me - it.m0);
     const int nbt = (mcount + 31) / 32;                      // 32-token B tiles in use
     const uint8_t* base = A.pool + (int64_t)it.ridx * A.stride;
 
     // X staging with direct-to-LDS loads: wave-instruction j of wave w fills
-    // rows 4 (8 w + j) .. +3 (1 KB); lane L writes row + (L >> 4), physical
+    // rows 4 (JX w + j) .. +3 (1 KB); lane L writes row + (L >> 4), physical
     // 16-byte chunk L & 15, which holds logical chunk (L & 15) ^ (row & 15)
     // (an XOR swizzle that keeps the B-operand reads free of bank conflicts).
     // Rows past the expert's end re-read its last row: they only feed output
     // columns that are never stored.  Inputs past K re-read input 0 of the
     // row: the matching weights are zero codes with zero scales.
     const _Float16* xsrc = PHASE == 0 ? A.x16 : A.h16;
-    int trow[8];
+    int trow[JX];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int row = min(4 * (8 * wave + j) + (lane >> 4), mcount - 1);
+    for (int j = 0; j < JX; ++j) {
+        const int row = min(4 * (JX * wave + j) + (lane >> 4), mcount - 1);
         trow[j] = PHASE == 0 ? A.perm_src[it.r0 + it.m0 + row] / A.k : it.r0 + it.m0 + row;
     }
     auto issue_x = [&](int kb, int buf) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = 4 * (8 * wave + j) + (lane >> 4);
+        for (int j = 0; j < JX; ++j) {
+            const int row = 4 * (JX * wave + j) + (lane >> 4);
             int kk = kb * kNvTileK + 8 * ((lane & 15) ^ (row & 15));
             if (kk >= K) kk = 0;
             __builtin_amdgcn_global_load_lds(xsrc + (int64_t)trow[j] * K + kk,
-                                             &xs[buf][4 * (8 * wave + j) * kNvTileK], 16, 0, 0);
+                                             &xs[buf][4 * (JX * wave + j) * kNvTileK], 16, 0, 0);
         }
     };
 
@@ -228,20 +246,27 @@ __global__ __launch_bounds__(256, 2) void k_prefill_nv(PrefillArgs A) {
     auto run = [&](auto nb_c) {
         constexpr int NB = decltype(nb_c)::value;
         AFrag w[2][2];
-        issue_x(0, 0);
         load_w(0, w[0][0], w[0][1]);
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+#pragma unroll
+        for (int b = 0; b < NS - 1; ++b)
+            if (b < nkb) issue_x(b, b);
+        // wait for W(0) and X(0); X(1 .. NS-2) may stay in flight
+        if (NS == 3 && nkb > 1)
+            __builtin_amdgcn_s_waitcnt(kVmcnt0 | JX);
+        else
+            __builtin_amdgcn_s_waitcnt(kVmcnt0);
         __syncthreads();
         // B reads: row (lane & 31) of each 32-token tile, logical chunk 8h + s
         const _Float16* xrow0 = &xs[0][(lane & 31) * kNvTileK];
         auto step = [&](int kb, auto p_c) {
             constexpr int P = decltype(p_c)::value;
             const bool more = kb + 1 < nkb;
-            if (more) {
-                issue_x(kb + 1, P ^ 1);
-                load_w(kb + 1, w[P ^ 1][0], w[P ^ 1][1]);
-            }
-            const _Float16* xb = xrow0 + P * (kBM * kNvTileK);
+            // W(kb + 1) first, then X(kb + NS - 1): the wait below then leaves
+            // only the newest token tile in flight
+            if (more) load_w(kb + 1, w[P ^ 1][0], w[P ^ 1][1]);
+            const bool ahead = kb + NS - 1 < nkb;
+            if (ahead) issue_x(kb + NS - 1, (kb + NS - 1) % NS);
+            const _Float16* xb = xrow0 + (kb % NS) * (kBM * kNvTileK);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const f16x8 a0 = a_step(w[P][0], s);
@@ -255,7 +280,12 @@ __global__ __launch_bounds__(256, 2) void k_prefill_nv(PrefillArgs A) {
                     acc[1][q] = mfma32(a1, b, acc[1][q]);
                 }
             }
-            __builtin_amdgcn_s_waitcnt(kVmcnt0);   // next stage's LDS writes landed
+            // W(kb + 1) and X(kb + 1) must have landed; with three buffers
+            // X(kb + 2) may still be in flight
+            if (NS == 3 && ahead)
+                __builtin_amdgcn_s_waitcnt(kVmcnt0 | JX);
+            else
+                __builtin_amdgcn_s_waitcnt(kVmcnt0);
             __syncthreads();
         };
         for (int kb = 0; kb < nkb; kb += 2) {
@@ -339,9 +369,9 @@ int launch_ffn_prefill(const LayerView& L, int n_fmt, const uint16_t* x16,
     const int64_t nblocks = 8 * ((items * nnt + 7) / 8);
     dim3 grid((unsigned)nblocks);
     if (phase == 0)
-        k_prefill_nv<0><<<grid, 256, 0, s>>>(a);
+        k_prefill_nv<0><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
     else
-        k_prefill_nv<1><<<grid, 256, 0, s>>>(a);
+        k_prefill_nv<1><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
 }
