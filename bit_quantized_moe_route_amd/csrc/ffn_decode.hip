@@ -162,6 +162,97 @@ __device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
     }
 }
 
+// VQ tiles.  Every 16-byte codebook row a tile needs is a gather whose
+// address comes from the tile's codes, and each gathered row is one MFMA A
+// fragment.  All NM x 8 gathers of a tile (and its activation fragments) are
+// issued before the tile's first MFMA, and the next tile's codes are loaded
+// behind them, so a wave keeps NM * 8 gathers in flight.  The scheduling
+// barrier stops the compiler from moving each gather next to its MFMA, which
+// leaves one gather in flight per wave and a full wait per MFMA.
+// Lanes of tokens past the expert's rows read the row `xsafe` (their output
+// columns are never stored); inputs past K are zero.
+#ifndef MOEQ_VQ_CODES_AHEAD
+#define MOEQ_VQ_CODES_AHEAD 1
+#endif
+constexpr int kVqCodesAhead = MOEQ_VQ_CODES_AHEAD;
+
+template <int NTT, int NM>
+__device__ __forceinline__ void stream_tiles_vq(const uint8_t* const tbase[NM],
+                                                const uint8_t* const cb[NM],
+                                                const _Float16* const xrow[NTT],
+                                                const _Float16* xsafe, int ntt, int K, int kpart,
+                                                int KS, int lane, f32x4 acc[NM][NTT]) {
+    using F = VqFmt;
+    const int nkb = tiles_k<F>(K);
+    const int ksub = (lane >> 4) * F::KSPAN;
+    const int niter = kpart < nkb ? (nkb - kpart + KS - 1) / KS : 0;
+    if (niter == 0) return;
+    const _Float16* xr[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) xr[tt] = xrow[tt] != nullptr ? xrow[tt] : xsafe;
+    // codes of tiles i .. i + kVqCodesAhead (HBM latency is longer than a
+    // tile's gather round trip)
+    u32x4 codes[NM], ahead[kVqCodesAhead][NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+        codes[m] = load_stream16(tbase[m] + (int64_t)kpart * F::TB + lane * 16);
+#pragma unroll
+    for (int d = 0; d < kVqCodesAhead; ++d)
+        if (d + 1 < niter) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                ahead[d][m] =
+                    load_stream16(tbase[m] + (int64_t)(kpart + (d + 1) * KS) * F::TB + lane * 16);
+        }
+    for (int i = 0; i < niter; ++i) {
+        const int kb = kpart + i * KS;
+        const int k0 = kb * F::TK + ksub;
+        f16x8 a[NM][F::STEPS];
+        f16x8 b[NTT][F::STEPS];
+#pragma unroll
+        for (int s = 0; s < F::STEPS; ++s) {
+            const int kk = k0 + 8 * s;
+            const int kc = kk < K ? kk : K - 8;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+                if (tt < ntt) b[tt][s] = *reinterpret_cast<const f16x8*>(xr[tt] + kc);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const uint32_t c = (codes[m][s >> 1] >> (16 * (s & 1))) & 0xffffu;
+                a[m][s] = vq_row(cb[m], c);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            codes[m] = ahead[0][m];
+#pragma unroll
+            for (int d = 0; d + 1 < kVqCodesAhead; ++d) ahead[d][m] = ahead[d + 1][m];
+        }
+        if (i + 1 + kVqCodesAhead < niter) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                ahead[kVqCodesAhead - 1][m] = load_stream16(
+                    tbase[m] + (int64_t)(kb + (1 + kVqCodesAhead) * KS) * F::TB + lane * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < F::STEPS; ++s) {
+            const bool kin = k0 + 8 * s < K;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+                if (tt >= ntt) break;
+                const f16x8 bb = kin ? b[tt][s] : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                for (int m = 0; m < NM; ++m) acc[m][tt] = mfma16(a[m][s], bb, acc[m][tt]);
+            }
+        }
+    }
+}
+
+#ifndef MOEQ_VQ_GATHER_AHEAD
+#define MOEQ_VQ_GATHER_AHEAD 1
+#endif
+
 // Row groups per wave: gate/up 2 row-pair groups (4 weight tiles per input
 // tile), down 4 row groups.
 constexpr int kRpwGateup = 2;
@@ -231,7 +322,17 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
     for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) acc[m][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (nlive > 0) stream_tiles<F, NTT, NM, kPrefetch>(tb, cb, xrow, ntt, K, kpart, KS, lane, acc);
+    if (nlive > 0) {
+        if constexpr (F::kVq && MOEQ_VQ_GATHER_AHEAD) {
+            // row c0 of the expert exists: a safe row for lanes past its rows
+            const _Float16* xsafe =
+                PHASE == 0 ? A.x16 + (int64_t)(A.perm_src[ae.r0 + c0] / A.k) * A.H
+                           : A.h16 + (int64_t)(ae.r0 + c0) * A.I;
+            stream_tiles_vq<NTT, NM>(tb, cb, xrow, xsafe, ntt, K, kpart, KS, lane, acc);
+        } else {
+            stream_tiles<F, NTT, NM, kPrefetch>(tb, cb, xrow, ntt, K, kpart, KS, lane, acc);
+        }
+    }
 
     if constexpr (KS > 1) {
         // sum the KS partial tiles of a row set in a fixed order (wave order)
