@@ -95,12 +95,13 @@ class Runner:
         self.y = torch.empty((T * k, H), dtype=f32, device=dev)
         self.out = torch.empty((T, H), dtype=f32, device=dev)
         self.ws = moeq.gateup_workspace(layer, T)
+        self.pws = moeq.permute_workspace(T, k, E, dev)
         self.ev = []
 
     def step(self, r, timed):
         moeq = self.moeq
         lg, x = self.batches[r % len(self.batches)]
-        moeq.route_permute(lg, self.k, self.wl.E, (self.ids, self.w) + self.perm)
+        moeq.route_permute(lg, self.k, self.wl.E, (self.ids, self.w) + self.perm, self.pws)
         counts, offsets, perm_src, inv_perm = self.perm
         if timed:
             e0 = self.torch.cuda.Event(enable_timing=True)

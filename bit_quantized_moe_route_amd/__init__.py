@@ -67,7 +67,8 @@ _PROTOS = {
     "moe_route_topk": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
-    "moe_route_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                         _P]),
     "moe_ffn_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64, _I32]),
     "moe_expert_ffn_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _P, _I64, _I32, _P,
                                         _P, _SZ, _P]),
@@ -294,7 +295,10 @@ def route_topk(logits, k, topk_ids=None, topk_w=None):
     return topk_ids, topk_w
 
 
-def permute(topk_ids, E, out=None):
+def permute(topk_ids, E, out=None, ws=None):
+    """Stable counting sort of the assignments by expert.  Returns counts,
+    offsets, perm_src, inv_perm.  `ws`: from permute_workspace (allocated here
+    if needed and not given)."""
     torch = _torch()
     _need_cuda(topk_ids)
     T, k = topk_ids.shape
@@ -307,16 +311,27 @@ def permute(topk_ids, E, out=None):
     counts, offsets, perm_src, inv_perm = out
     L = lib()
     nws = L.moe_permute_workspace_bytes(T, k, E)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
+    if ws is None and nws:
+        ws = permute_workspace(T, k, E, dev)
     _check(L.moe_permute(_dptr(topk_ids), T, k, E, _dptr(counts), _dptr(offsets),
-                         _dptr(perm_src), _dptr(inv_perm), _dptr(ws), nws, _stream(dev)),
+                         _dptr(perm_src), _dptr(inv_perm), _dptr(ws),
+                         ws.numel() if ws is not None else 0, _stream(dev)),
            "moe_permute")
     return counts, offsets, perm_src, inv_perm
 
 
-def route_permute(logits, k, E=None, out=None):
+def permute_workspace(T, k, E, device="cuda"):
+    """Workspace tensor for permute / route_permute at these sizes (None if
+    none is needed)."""
+    torch = _torch()
+    nws = lib().moe_permute_workspace_bytes(T, k, E)
+    return torch.empty(nws, dtype=torch.uint8, device=device) if nws else None
+
+
+def route_permute(logits, k, E=None, out=None, ws=None):
     """route_topk + permute in one call (one launch for T*k <= 4096).
-    Returns topk_ids, topk_w, counts, offsets, perm_src, inv_perm."""
+    Returns topk_ids, topk_w, counts, offsets, perm_src, inv_perm.  `ws`:
+    from permute_workspace (allocated here if needed and not given)."""
     torch = _torch()
     _need_cuda(logits)
     T, E_ = logits.shape
@@ -329,8 +344,13 @@ def route_permute(logits, k, E=None, out=None):
                torch.empty(E + 1, dtype=torch.int32, device=dev),
                torch.empty(T * k, dtype=torch.int32, device=dev),
                torch.empty(T * k, dtype=torch.int32, device=dev))
-    _check(lib().moe_route_permute(_dptr(logits), T, E, k, *[_dptr(t) for t in out],
-                                   _stream(dev)), "moe_route_permute")
+    L = lib()
+    nws = L.moe_permute_workspace_bytes(T, k, E)
+    if ws is None and nws:
+        ws = permute_workspace(T, k, E, dev)
+    _check(L.moe_route_permute(_dptr(logits), T, E, k, *[_dptr(t) for t in out], _dptr(ws),
+                               ws.numel() if ws is not None else 0, _stream(dev)),
+           "moe_route_permute")
     return out
 
 

@@ -152,19 +152,23 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_
 
 int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
                       float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                      int32_t* inv_perm, void* stream) {
+                      int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
     g_last_error.clear();
     int st = check_route_sizes("moe_route_permute", T, E, k);
     if (st) return st;
     if (!counts || !offsets) return fail(MOE_EINVAL, "moe_route_permute: null pointer");
     if (T > 0 && (!logits || !topk_ids || !topk_w || !perm_src || !inv_perm))
         return fail(MOE_EINVAL, "moe_route_permute: null pointer");
+    const size_t need = permute_ws_bytes(T, k, E);
+    if (need && (!ws || ws_bytes < need))
+        return fail(MOE_EWORKSPACE,
+                    "moe_route_permute: workspace needs " + std::to_string(need) + " bytes");
     if (route_permute_fused_ok(T, k))
         return launch_route_permute(logits, T, E, k, topk_ids, topk_w, counts, offsets, perm_src,
                                     inv_perm, stream);
     st = launch_route_topk(logits, T, E, k, topk_ids, topk_w, stream);
     if (st) return st;
-    return launch_permute(topk_ids, T, k, E, counts, offsets, perm_src, inv_perm, nullptr, stream);
+    return launch_permute(topk_ids, T, k, E, counts, offsets, perm_src, inv_perm, ws, stream);
 }
 
 size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k) {

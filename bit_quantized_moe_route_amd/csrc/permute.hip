@@ -1,7 +1,7 @@
 // Token permutation: a stable counting sort of the T*k assignments by expert,
 // and the fused route + permute kernel for small batches.
 //
-// One workgroup of 1024 threads:
+// Small batches (T*k <= 4096), one workgroup of 1024 threads:
 //   1. histogram of expert ids in LDS;
 //   2. exclusive prefix scan over the E counts (wave scans + a scan of the
 //      wave totals) -> counts, offsets;
@@ -10,7 +10,13 @@
 //      of the id); a lane's rank is its position among its peers, plus the
 //      peers in earlier waves of the chunk (per-wave counts in LDS), plus
 //      the running count of that expert from earlier chunks.
-// The result is unique, so it does not depend on timing.
+// Large batches split the assignments into B <= 64 contiguous slices, one
+// workgroup each, in two launches:
+//   1. each workgroup writes its slice's histogram to the workspace [B][E];
+//   2. each workgroup sums the histograms (all of them for the offsets,
+//      those of earlier slices for its own starting slot per expert) and
+//      ranks and scatters its slice as in step 3 above.
+// Either way the result is unique, so it does not depend on timing.
 #include "topk_dev.h"
 
 namespace moeq {
@@ -26,29 +32,13 @@ __host__ __device__ constexpr size_t permute_lds_bytes(int E) {
     return (size_t)(2 * E + kPermWaves) * sizeof(int) + (size_t)kPermWaves * E;
 }
 
-// ids may point to global memory or to LDS.
-__device__ __forceinline__ void permute_body(const int32_t* ids, int n, int E,
-                                             int32_t* __restrict__ counts,
-                                             int32_t* __restrict__ offsets,
-                                             int32_t* __restrict__ perm_src,
-                                             int32_t* __restrict__ inv_perm, int* smem) {
-    int* hist = smem;                 // [E]
-    int* run = smem + E;              // [E]
-    int* wtot = smem + 2 * E;         // [kPermWaves]
-    uint8_t* wcnt = reinterpret_cast<uint8_t*>(smem + 2 * E + kPermWaves);  // [kPermWaves][E]
-
+// Exclusive scan over the workgroup of c (threads tid < E hold the values,
+// E <= kPermThreads); returns the thread's exclusive prefix.  wtot: LDS
+// [kPermWaves].  Ends with a barrier.
+__device__ __forceinline__ int block_exclusive_scan(int c, int* wtot) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-
-    for (int e = tid; e < E; e += kPermThreads) hist[e] = 0;
-    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
-    __syncthreads();
-    for (int a = tid; a < n; a += kPermThreads) atomicAdd(&hist[ids[a]], 1);
-    __syncthreads();
-
-    // exclusive scan of hist[0..E) (E <= kPermThreads)
-    int c = tid < E ? hist[tid] : 0;
     int incl = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -59,19 +49,23 @@ __device__ __forceinline__ void permute_body(const int32_t* ids, int n, int E,
     __syncthreads();
     int wbase = 0;
     for (int w = 0; w < wave; ++w) wbase += wtot[w];
-    int excl = wbase + incl - c;
-    if (tid < E) {
-        counts[tid] = c;
-        offsets[tid] = excl;
-        run[tid] = excl;
-    }
-    if (tid == 0) offsets[E] = n;
     __syncthreads();
+    return wbase + incl - c;
+}
 
+// Ranks the assignments a0 .. a1-1 in order and scatters them: run[e] is the
+// next free slot of expert e (LDS, advanced here); wcnt: LDS
+// [kPermWaves][E] bytes, zero on entry and on exit.
+__device__ __forceinline__ void rank_scatter(const int32_t* ids, int a0, int a1, int E, int* run,
+                                             uint8_t* wcnt, int32_t* __restrict__ perm_src,
+                                             int32_t* __restrict__ inv_perm) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < n; base += kPermThreads) {
+    for (int base = a0; base < a1; base += kPermThreads) {
         const int a = base + tid;
-        const bool valid = a < n;
+        const bool valid = a < a1;
         const int e = valid ? ids[a] : 0x7ff;   // sentinel never equals an id
         uint64_t peers = ~0ull;
 #pragma unroll
@@ -99,6 +93,88 @@ __device__ __forceinline__ void permute_body(const int32_t* ids, int n, int E,
         }
         __syncthreads();
     }
+}
+
+// The whole sort in one workgroup.  ids may point to global memory or to LDS.
+__device__ __forceinline__ void permute_body(const int32_t* ids, int n, int E,
+                                             int32_t* __restrict__ counts,
+                                             int32_t* __restrict__ offsets,
+                                             int32_t* __restrict__ perm_src,
+                                             int32_t* __restrict__ inv_perm, int* smem) {
+    int* hist = smem;                 // [E]
+    int* run = smem + E;              // [E]
+    int* wtot = smem + 2 * E;         // [kPermWaves]
+    uint8_t* wcnt = reinterpret_cast<uint8_t*>(smem + 2 * E + kPermWaves);  // [kPermWaves][E]
+    const int tid = threadIdx.x;
+
+    for (int e = tid; e < E; e += kPermThreads) hist[e] = 0;
+    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
+    __syncthreads();
+    for (int a = tid; a < n; a += kPermThreads) atomicAdd(&hist[ids[a]], 1);
+    __syncthreads();
+
+    const int c = tid < E ? hist[tid] : 0;
+    const int excl = block_exclusive_scan(c, wtot);
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = excl;
+        run[tid] = excl;
+    }
+    if (tid == 0) offsets[E] = n;
+    __syncthreads();
+    rank_scatter(ids, 0, n, E, run, wcnt, perm_src, inv_perm);
+}
+
+// Large batches, launch 1: the histogram of slice blockIdx.x
+// (assignments slice*C .. min(n, slice*C + C)) -> hist_ws[slice][E].
+__global__ __launch_bounds__(kPermThreads) void k_perm_hist(const int32_t* __restrict__ ids, int n,
+                                                            int E, int C,
+                                                            int32_t* __restrict__ hist_ws) {
+    extern __shared__ int smem[];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kPermThreads) smem[e] = 0;
+    __syncthreads();
+    const int a0 = blockIdx.x * C;
+    const int a1 = min(n, a0 + C);
+    for (int a = a0 + tid; a < a1; a += kPermThreads) atomicAdd(&smem[ids[a]], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += kPermThreads) hist_ws[(int64_t)blockIdx.x * E + e] = smem[e];
+}
+
+// Large batches, launch 2: offsets from the nb slice histograms, then slice
+// blockIdx.x ranked and scattered from its own starting slots.
+__global__ __launch_bounds__(kPermThreads) void k_perm_scatter(
+    const int32_t* __restrict__ ids, int n, int E, int C, int nb,
+    const int32_t* __restrict__ hist_ws, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ inv_perm) {
+    extern __shared__ int smem[];
+    int* run = smem;                  // [E]
+    int* wtot = smem + E;             // [kPermWaves]
+    uint8_t* wcnt = reinterpret_cast<uint8_t*>(smem + E + kPermWaves);  // [kPermWaves][E]
+    const int tid = threadIdx.x;
+    const int slice = blockIdx.x;
+    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
+    int total = 0, before = 0;
+    if (tid < E) {
+        for (int b = 0; b < nb; ++b) {
+            const int v = hist_ws[(int64_t)b * E + tid];
+            total += v;
+            before += b < slice ? v : 0;
+        }
+    }
+    const int excl = block_exclusive_scan(total, wtot);
+    if (tid < E) {
+        run[tid] = excl + before;
+        if (slice == 0) {
+            counts[tid] = total;
+            offsets[tid] = excl;
+        }
+    }
+    if (slice == 0 && tid == 0) offsets[E] = n;
+    __syncthreads();
+    const int a0 = slice * C;
+    rank_scatter(ids, a0, min(n, a0 + C), E, run, wcnt, perm_src, inv_perm);
 }
 
 __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restrict__ ids,
@@ -137,15 +213,45 @@ __global__ __launch_bounds__(kPermThreads) void k_route_permute(
 
 }  // namespace
 
-size_t permute_ws_bytes(int64_t, int32_t, int32_t) { return 0; }
+// Slices of the large-batch path: at least kPermSlice assignments each, at
+// most kPermMaxSlices of them.
+constexpr int kPermSlice = 2048;
+constexpr int kPermMaxSlices = 64;
+
+bool permute_single(int64_t n) { return n <= kFusedMaxAssign; }
+
+int permute_slice(int64_t n) {
+    int64_t c = (n + kPermMaxSlices - 1) / kPermMaxSlices;
+    c = (c + kPermThreads - 1) / kPermThreads * kPermThreads;
+    return (int)(c < kPermSlice ? kPermSlice : c);
+}
+
+size_t permute_ws_bytes(int64_t T, int32_t k, int32_t E) {
+    const int64_t n = T * k;
+    if (permute_single(n)) return 0;
+    const int64_t nb = (n + permute_slice(n) - 1) / permute_slice(n);
+    return (size_t)(nb * E) * sizeof(int32_t);
+}
 
 int launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
-                   int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, void*,
+                   int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, void* ws,
                    void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int n = (int)(T * k);
-    k_permute<<<1, kPermThreads, permute_lds_bytes(E), s>>>(ids, n, E, counts, offsets, perm_src,
-                                                            inv_perm);
+    if (permute_single(n)) {
+        k_permute<<<1, kPermThreads, permute_lds_bytes(E), s>>>(ids, n, E, counts, offsets,
+                                                                perm_src, inv_perm);
+        MOEQ_CHECK_LAUNCH();
+        return MOE_OK;
+    }
+    const int C = permute_slice(n);
+    const int nb = (n + C - 1) / C;
+    int32_t* hist = static_cast<int32_t*>(ws);
+    k_perm_hist<<<nb, kPermThreads, (size_t)E * sizeof(int), s>>>(ids, n, E, C, hist);
+    MOEQ_CHECK_LAUNCH();
+    const size_t lds = (size_t)(E + kPermWaves) * sizeof(int) + (size_t)kPermWaves * E;
+    k_perm_scatter<<<nb, kPermThreads, lds, s>>>(ids, n, E, C, nb, hist, counts, offsets,
+                                                 perm_src, inv_perm);
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
 }

@@ -173,12 +173,13 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
  * same outputs bit for bit; for T*k <= 4096 both run in one workgroup (one
  * launch, the ids never leave the chip between the two steps), which is
  * what a decode step wants.  Same arguments, limits and errors as the two
- * calls; no workspace.
+ * calls; ws/ws_bytes as for moe_permute (moe_permute_workspace_bytes gives
+ * the size; it is 0, and ws may be NULL, for T*k <= 4096).
  */
 int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
                       int32_t* topk_ids, float* topk_w, int32_t* counts,
                       int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
-                      void* stream);
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------ expert FFN */
 

@@ -15,7 +15,7 @@ DEV = "cuda"
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 256, 8), (32, 256, 8), (512, 256, 8), (700, 64, 8),
-                                   (5, 1024, 16), (3, 4, 1)])
+                                   (5, 1024, 16), (3, 4, 1), (4096, 256, 8), (300, 1024, 16)])
 def test_route_permute_equals_separate_calls(T, E, k):
     say("route_permute", T, E, k)
     g = np.random.default_rng(T + E)

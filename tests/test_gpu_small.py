@@ -111,12 +111,16 @@ def test_route_ties():
 
 # ------------------------------------------------------------------ permute
 
+# T*k <= 4096 runs in one workgroup; larger batches in up to 64 slices of
+# >= 2048 assignments (513*8: two full slices and a ragged one; 20000*8: 53
+# slices of 3072)
 @pytest.mark.parametrize("T,E,k", [(4, 8, 2), (1, 256, 8), (32, 256, 8), (200, 16, 4),
-                                   (4096, 256, 8), (1500, 1024, 16), (3, 1, 1), (0, 8, 2)])
+                                   (4096, 256, 8), (1500, 1024, 16), (3, 1, 1), (0, 8, 2),
+                                   (512, 64, 8), (513, 64, 8), (20000, 256, 8)])
 def test_permute(T, E, k):
     say("permute", T, E, k)
     g = np.random.default_rng(T + E)
-    if T == 4096:
+    if T in (4096, 20000):
         ids, _ = oracle.route_topk(synth.logits(synth.PREFILL, T), k)
     else:
         ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32) \
