@@ -22,7 +22,7 @@
 //     in registers before the fp16 store of h.
 // A workgroup finds its (expert, row tile, weight tile) from the offsets with
 // a wave prefix scan; the grid is an upper bound on the work list (slots past
-// its end exit at once), ordered so that each XCD takes a contiguous slice.
+// its end exit at once), items dealt round-robin over the 8 XCDs.
 #include <type_traits>
 
 #include "dev_common.h"
@@ -41,6 +41,15 @@ constexpr int kBM = 128;           // tokens per work item
 #endif
 #ifndef MOEQ_PF_STAGES
 #define MOEQ_PF_STAGES 2
+#endif
+#ifndef MOEQ_PF_BPIPE
+#define MOEQ_PF_BPIPE 0
+#endif
+#ifndef MOEQ_PF_ORDER
+#define MOEQ_PF_ORDER 1
+#endif
+#ifndef MOEQ_PF_PRIO
+#define MOEQ_PF_PRIO 0
 #endif
 constexpr int kPrefillWaves = MOEQ_PF_WAVES;
 constexpr int kPrefillStages = MOEQ_PF_STAGES;
@@ -97,11 +106,12 @@ __device__ __forceinline__ WorkItem locate_item(const int32_t* __restrict__ offs
         for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
         total += t;
     }
+    WorkItem r{-1, 0, 0, 0, 0};
+#if MOEQ_PF_ORDER == 0
     // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
     // so XCD blk % 8 takes a contiguous slice of the work list.  The weight
     // tiles of one token tile, and the next few token tiles of the same
     // expert, then share that XCD's L2.
-    WorkItem r{-1, 0, 0, 0, 0};
     const int nwork = total * nnt;
     const int quota = (nwork + 7) / 8;
     const int slot = blk >> 3;
@@ -109,6 +119,18 @@ __device__ __forceinline__ WorkItem locate_item(const int32_t* __restrict__ offs
     if (slot >= quota || w >= nwork) return r;
     ntile = w % nnt;
     const int want_item = w / nnt;
+#else
+    // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
+    // (XCD blk % 8); items are dealt to the XCDs round-robin too, and all
+    // nnt weight tiles of an item run on its XCD, one after the other, so
+    // they share the item's token tiles in that XCD's L2.  Dealing items
+    // (rather than cutting the list into 8 slices) evens out the work per
+    // XCD when expert sizes are skewed.
+    const int slot = blk >> 3;
+    const int want_item = (slot / nnt) * 8 + (blk & 7);
+    ntile = slot % nnt;
+    if (want_item >= total) return r;
+#endif
     int before = 0;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
@@ -267,19 +289,61 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
             const bool ahead = kb + NS - 1 < nkb;
             if (ahead) issue_x(kb + NS - 1, (kb + NS - 1) % NS);
             const _Float16* xb = xrow0 + (kb % NS) * (kBM * kNvTileK);
+            auto rd = [&](int s, int q) {
+                const int cofs = 8 * ((8 * h + s) ^ (lane & 15));
+                return *reinterpret_cast<const f16x8*>(xb + 32 * q * kNvTileK + cofs);
+            };
+#if MOEQ_PF_BPIPE
+            // B fragments are read half a K-step ahead of their MFMAs: the
+            // reads of tiles 2, 3 of step s go out before the MFMAs of tiles
+            // 0, 1, and those of tiles 0, 1 of step s + 1 before the MFMAs of
+            // tiles 2, 3 (the scheduling barriers keep that order).
+            f16x8 bq[NB];
+            bq[0] = rd(0, 0);
+            if constexpr (NB > 1) bq[1] = rd(0, 1);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const f16x8 a0 = a_step(w[P][0], s);
                 const f16x8 a1 = a_step(w[P][1], s);
-                const int cofs = 8 * ((8 * h + s) ^ (lane & 15));
+                if constexpr (NB > 2) bq[2] = rd(s, 2);
+                if constexpr (NB > 3) bq[3] = rd(s, 3);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q < (NB < 2 ? NB : 2); ++q) {
+                    acc[0][q] = mfma32(a0, bq[q], acc[0][q]);
+                    acc[1][q] = mfma32(a1, bq[q], acc[1][q]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (s < 7) {
+                    bq[0] = rd(s + 1, 0);
+                    if constexpr (NB > 1) bq[1] = rd(s + 1, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 2; q < NB; ++q) {
+                    acc[0][q] = mfma32(a0, bq[q], acc[0][q]);
+                    acc[1][q] = mfma32(a1, bq[q], acc[1][q]);
+                }
+            }
+#else
+#if MOEQ_PF_PRIO
+            __builtin_amdgcn_s_setprio(1);
+#endif
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const f16x8 a0 = a_step(w[P][0], s);
+                const f16x8 a1 = a_step(w[P][1], s);
 #pragma unroll
                 for (int q = 0; q < NB; ++q) {
-                    const f16x8 b =
-                        *reinterpret_cast<const f16x8*>(xb + 32 * q * kNvTileK + cofs);
+                    const f16x8 b = rd(s, q);
                     acc[0][q] = mfma32(a0, b, acc[0][q]);
                     acc[1][q] = mfma32(a1, b, acc[1][q]);
                 }
             }
+#if MOEQ_PF_PRIO
+            __builtin_amdgcn_s_setprio(0);
+#endif
+#endif
             // W(kb + 1) and X(kb + 1) must have landed; with three buffers
             // X(kb + 2) may still be in flight
             if (NS == 3 && ahead)
@@ -364,9 +428,15 @@ int launch_ffn_prefill(const LayerView& L, int n_fmt, const uint16_t* x16,
     if (items == 0) return MOE_OK;
     const int nrg = (phase == 0 ? 2 * L.I : L.H) / 16;
     const int64_t nnt = (nrg + kBN / 16 - 1) / (kBN / 16);
+#if MOEQ_PF_ORDER == 0
     // 8 slices of ceil(items * nnt / 8) workgroups cover every item; slots past
     // the actual item count exit at once
     const int64_t nblocks = 8 * ((items * nnt + 7) / 8);
+#else
+    // each XCD takes every 8th item, nnt workgroups per item; slots past the
+    // actual item count exit at once
+    const int64_t nblocks = 8 * ((items + 7) / 8) * nnt;
+#endif
     dim3 grid((unsigned)nblocks);
     if (phase == 0)
         k_prefill_nv<0><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
