@@ -129,23 +129,31 @@ class Runner:
         return dt, gu_ms
 
     def run_graph(self, steps, warmup):
-        """The same steps replayed from HIP graphs, one captured per input
-        batch of the pool (the kernels and buffers are those of `step`)."""
+        """The same steps replayed from HIP graphs, as a decode loop would run
+        them: each graph holds `group` consecutive steps (each on its own input
+        batch; group = the largest divisor of `steps` up to 16), so the host's
+        per-graph launch cost is paid once per group.  The graphs together
+        cover the batch pool a whole number of times.  Returns (seconds, group)."""
+        import math
         torch = self.torch
+        nb = len(self.batches)
+        group = max(d for d in range(1, min(16, steps) + 1) if steps % d == 0)
+        ng = nb // math.gcd(group, nb)
         graphs = []
-        for r in range(len(self.batches)):
+        for gi in range(ng):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                self.step(r, False)
+                for u in range(group):
+                    self.step(gi * group + u, False)
             graphs.append(g)
-        for i in range(warmup):
-            graphs[i % len(graphs)].replay()
+        for i in range(max(1, (warmup + group - 1) // group)):
+            graphs[i % ng].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            graphs[(warmup + i) % len(graphs)].replay()
+        for i in range(steps // group):
+            graphs[i % ng].replay()
         torch.cuda.synchronize()
-        return time.perf_counter() - t0
+        return time.perf_counter() - t0, group
 
     def bytes_of(self, r, which):
         """Algorithmic packed-weight bytes of batch r: 'all' (codes + scales
@@ -169,10 +177,11 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16):
     graph replay's, the kernel-level ones the eager run's."""
     rn = Runner(layer, wl, T, reps, dev)
     dte, gu_ms = rn.run(steps, warmup)
-    dt = rn.run_graph(steps, warmup)
-    idx = [warmup + i for i in range(steps)]
+    dt, group = rn.run_graph(steps, warmup)
+    idx = list(range(steps))                    # batches of the timed graph replays
+    idx_e = [warmup + i for i in range(steps)]  # batches of the timed eager steps
     all_bytes = sum(rn.bytes_of(r, "all") for r in idx)
-    gu_bytes = sum(rn.bytes_of(r, "gateup") for r in idx)
+    gu_bytes = sum(rn.bytes_of(r, "gateup") for r in idx_e)
     gu_s = sum(gu_ms) / 1e3
     res = {
         "T": T,
@@ -180,6 +189,7 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16):
         "ms_per_step": dt / steps * 1e3,
         "tokens_per_s_eager": T * steps / dte,
         "ms_per_step_eager": dte / steps * 1e3,
+        "steps_per_graph": group,
         "packed_GBps": all_bytes / dt / 1e9,
         "packed_frac_hbm": all_bytes / dt / 1e9 / HBM_PEAK_GBS,
         "experts_touched_mean": sum(len(rn.touched[r % reps]) for r in idx) / steps,

@@ -432,8 +432,7 @@ def dequant_q(layer, expert, proj):
 def forward(layer, x, logits, k):
     """route -> permute -> expert FFN -> combine.  Returns a dict of every
     intermediate (device tensors)."""
-    ids, w = route_topk(logits, k)
-    counts, offsets, perm_src, inv_perm = permute(ids, layer.E)
+    ids, w, counts, offsets, perm_src, inv_perm = route_permute(logits, k, layer.E)
     y_perm = expert_ffn_q(layer, x, perm_src, offsets, k)
     out = combine(y_perm, inv_perm, w)
     return dict(topk_ids=ids, topk_w=w, counts=counts, offsets=offsets, perm_src=perm_src,

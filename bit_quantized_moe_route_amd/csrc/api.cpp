@@ -199,16 +199,21 @@ int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16, const i
                     "moe_expert_gateup_q: workspace needs " + std::to_string(need) + " bytes");
     if (reinterpret_cast<uintptr_t>(ws) % kAlign)
         return fail(MOE_EINVAL, "moe_expert_gateup_q: workspace must be 256-byte aligned");
+    // the grouped-GEMM kernels stage fp16 tokens through LDS: convert x once;
+    // the decode kernels convert each fragment they read
     uint16_t* x16 = static_cast<uint16_t*>(ws);
-    st = launch_x_to_f16(x_bf16, T * layer->H, x16, stream);
-    if (st) return st;
+    const bool prefill = li.count[MOE_FMT_NVFP4] && T >= kPrefillMinTokens;
+    if (prefill) {
+        st = launch_x_to_f16(x_bf16, T * layer->H, x16, stream);
+        if (st) return st;
+    }
     for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
         if (!li.count[fmt]) continue;
-        if (fmt == MOE_FMT_NVFP4 && T >= kPrefillMinTokens)
+        if (fmt == MOE_FMT_NVFP4 && prefill)
             st = launch_ffn_prefill(li.view, li.count[fmt], x16, perm_src, offsets, T, k, h_f16,
                                     nullptr, 0, stream);
         else
-            st = launch_ffn_decode(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T, k,
+            st = launch_ffn_decode(li.view, fmt, li.count[fmt], x_bf16, perm_src, offsets, T, k,
                                    h_f16, nullptr, 0, stream);
         if (st) return st;
     }

@@ -33,15 +33,7 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
                                                   uint16_t* __restrict__ x16) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n8) return;
-    u32x4 v = *reinterpret_cast<const u32x4*>(x + i * 8);
-    f16x8 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        float lo = __uint_as_float(v[q] << 16);
-        float hi = __uint_as_float(v[q] & 0xffff0000u);
-        o[2 * q] = (_Float16)lo;
-        o[2 * q + 1] = (_Float16)hi;
-    }
+    const f16x8 o = bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(x + i * 8));
     *reinterpret_cast<f16x8*>(x16 + i * 8) = o;
 }
 

@@ -83,6 +83,19 @@ __device__ __forceinline__ f16x8 vq_row(const uint8_t* cb, uint32_t code) {
     return *reinterpret_cast<const f16x8*>(cb + (size_t)code * 16);
 }
 
+// 8 bf16 values (bits, two per dword, low half first) to fp16: bf16 -> fp32
+// is exact, fp32 -> fp16 rounds to nearest even (exact for
+// 2^-14 <= |x| <= 65504).
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(u32x4 v) {
+    f16x8 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        o[2 * q] = (_Float16)__uint_as_float(v[q] << 16);
+        o[2 * q + 1] = (_Float16)__uint_as_float(v[q] & 0xffff0000u);
+    }
+    return o;
+}
+
 // Non-temporal 16-byte load for streamed weight bytes (read once per call),
 // so they do not push the shared VQ codebooks out of the caches.
 __device__ __forceinline__ u32x4 load_stream16(const uint8_t* p) {

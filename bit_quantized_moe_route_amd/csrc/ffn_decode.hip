@@ -18,7 +18,9 @@
 //     (exact) and feeds v_mfma_f32_16x16x32_f16: weights are the A operand,
 //     up to 16 tokens of the expert the B operand (further tokens use further
 //     B tiles; only the tiles the expert needs are computed);
-//   * the tokens' activations are fp16 copies of x made once per call.
+//   * the B operand is read straight from the bf16 tokens x (gate/up; each
+//     8-element fragment converted to fp16 in registers, exact for
+//     2^-14 <= |x| <= 65504) or from the fp16 activations h (down).
 #include "dev_common.h"
 
 namespace moeq {
@@ -75,12 +77,23 @@ __device__ __forceinline__ int tiles_k(int kin) {
     return (kin + F::TK - 1) / F::TK;
 }
 
+// 8 activations (raw 16-bit words) as fp16: bf16 bits converted (BF) or
+// fp16 bits as they are.  Fragments are loaded raw and converted right
+// before their MFMA, so a load in flight is never waited for early.
+template <bool BF>
+__device__ __forceinline__ f16x8 act_f16(u32x4 v) {
+    if constexpr (BF)
+        return bf16x8_to_f16x8(v);
+    else
+        return __builtin_bit_cast(f16x8, v);
+}
+
 // B operand fragments of one tile for the first `ntt` of NTT token tiles:
 // lane L holds token (L & 15) + 16 tt, inputs k0 + 8 s .. +7 with
 // k0 = kb*TK + (L>>4)*KSPAN.
 template <class F, int NTT>
-__device__ __forceinline__ void load_b(const _Float16* const xrow[NTT], int ntt, int k0, int K,
-                                       f16x8 b[NTT][F::STEPS]) {
+__device__ __forceinline__ void load_b(const uint16_t* const xrow[NTT], int ntt, int k0, int K,
+                                       u32x4 b[NTT][F::STEPS]) {
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
         if (tt >= ntt) break;
@@ -88,9 +101,9 @@ __device__ __forceinline__ void load_b(const _Float16* const xrow[NTT], int ntt,
         for (int s = 0; s < F::STEPS; ++s) {
             const int kk = k0 + 8 * s;
             if (xrow[tt] != nullptr && kk < K)
-                b[tt][s] = *reinterpret_cast<const f16x8*>(xrow[tt] + kk);
+                b[tt][s] = *reinterpret_cast<const u32x4*>(xrow[tt] + kk);
             else
-                b[tt][s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                b[tt][s] = u32x4{0u, 0u, 0u, 0u};
         }
     }
 }
@@ -107,7 +120,7 @@ struct DecodeArgs {
     const int32_t* rec;
     const int32_t* offsets;
     const int32_t* perm_src;
-    const _Float16* x16;
+    const uint16_t* xbf;   // tokens, bf16 bits [T, H]
     _Float16* h16;
     float* y_perm;
     int E, H, I, k, fmt;
@@ -122,18 +135,18 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // acc[m][tt] += W_m[rows, tile] * B[tile, tokens of tile tt].
 // The loads of the next D tiles stay in flight (a register ring of D + 1
 // stages) while a tile is decoded and multiplied.
-template <class F, int NTT, int NM, int D>
+template <class F, int NTT, int NM, int D, bool BF>
 __device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
                                              const uint8_t* const cb[NM],
-                                             const _Float16* const xrow[NTT], int ntt, int K,
+                                             const uint16_t* const xrow[NTT], int ntt, int K,
                                              int kpart, int KS, int lane,
                                              f32x4 acc[NM][NTT]) {
     const int nkb = tiles_k<F>(K);
     const int ksub = (lane >> 4) * F::KSPAN;
     const int niter = kpart < nkb ? (nkb - kpart + KS - 1) / KS : 0;   // tiles of this wave
     typename F::Frag wr[D + 1][NM];
-    f16x8 br[D + 1][NTT][F::STEPS];
-    auto issue = [&](int i, typename F::Frag (&w)[NM], f16x8 (&b)[NTT][F::STEPS]) {
+    u32x4 br[D + 1][NTT][F::STEPS];
+    auto issue = [&](int i, typename F::Frag (&w)[NM], u32x4 (&b)[NTT][F::STEPS]) {
         const int kb = kpart + i * KS;
 #pragma unroll
         for (int m = 0; m < NM; ++m) F::load(w[m], tbase[m] + (int64_t)kb * F::TB, lane);
@@ -156,7 +169,8 @@ __device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
                 for (int s = 0; s < F::STEPS; ++s)
 #pragma unroll
                     for (int tt = 0; tt < NTT; ++tt)
-                        if (tt < ntt) acc[m][tt] = mfma16(a[s], br[u][tt][s], acc[m][tt]);
+                        if (tt < ntt)
+                            acc[m][tt] = mfma16(a[s], act_f16<BF>(br[u][tt][s]), acc[m][tt]);
             }
         }
     }
@@ -176,18 +190,18 @@ __device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
 #endif
 constexpr int kVqCodesAhead = MOEQ_VQ_CODES_AHEAD;
 
-template <int NTT, int NM>
+template <int NTT, int NM, bool BF>
 __device__ __forceinline__ void stream_tiles_vq(const uint8_t* const tbase[NM],
                                                 const uint8_t* const cb[NM],
-                                                const _Float16* const xrow[NTT],
-                                                const _Float16* xsafe, int ntt, int K, int kpart,
+                                                const uint16_t* const xrow[NTT],
+                                                const uint16_t* xsafe, int ntt, int K, int kpart,
                                                 int KS, int lane, f32x4 acc[NM][NTT]) {
     using F = VqFmt;
     const int nkb = tiles_k<F>(K);
     const int ksub = (lane >> 4) * F::KSPAN;
     const int niter = kpart < nkb ? (nkb - kpart + KS - 1) / KS : 0;
     if (niter == 0) return;
-    const _Float16* xr[NTT];
+    const uint16_t* xr[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) xr[tt] = xrow[tt] != nullptr ? xrow[tt] : xsafe;
     // codes of tiles i .. i + kVqCodesAhead (HBM latency is longer than a
@@ -208,14 +222,14 @@ __device__ __forceinline__ void stream_tiles_vq(const uint8_t* const tbase[NM],
         const int kb = kpart + i * KS;
         const int k0 = kb * F::TK + ksub;
         f16x8 a[NM][F::STEPS];
-        f16x8 b[NTT][F::STEPS];
+        u32x4 b[NTT][F::STEPS];
 #pragma unroll
         for (int s = 0; s < F::STEPS; ++s) {
             const int kk = k0 + 8 * s;
             const int kc = kk < K ? kk : K - 8;
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
-                if (tt < ntt) b[tt][s] = *reinterpret_cast<const f16x8*>(xr[tt] + kc);
+                if (tt < ntt) b[tt][s] = *reinterpret_cast<const u32x4*>(xr[tt] + kc);
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 const uint32_t c = (codes[m][s >> 1] >> (16 * (s & 1))) & 0xffffu;
@@ -241,7 +255,7 @@ __device__ __forceinline__ void stream_tiles_vq(const uint8_t* const tbase[NM],
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
                 if (tt >= ntt) break;
-                const f16x8 bb = kin ? b[tt][s] : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                const f16x8 bb = kin ? act_f16<BF>(b[tt][s]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
                 for (int m = 0; m < NM; ++m) acc[m][tt] = mfma16(a[m][s], bb, acc[m][tt]);
             }
@@ -306,16 +320,16 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
                            : A.cb_down + (int64_t)ae.ridx * A.cb_stride;
     }
 
-    const _Float16* xrow[NTT];
+    const uint16_t* xrow[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
         const int c = c0 + (lane & 15) + 16 * tt;
         if (c >= ae.me)
             xrow[tt] = nullptr;
         else if (PHASE == 0)
-            xrow[tt] = A.x16 + (int64_t)(A.perm_src[ae.r0 + c] / A.k) * A.H;
+            xrow[tt] = A.xbf + (int64_t)(A.perm_src[ae.r0 + c] / A.k) * A.H;
         else
-            xrow[tt] = A.h16 + (int64_t)(ae.r0 + c) * A.I;
+            xrow[tt] = reinterpret_cast<const uint16_t*>(A.h16) + (int64_t)(ae.r0 + c) * A.I;
     }
     f32x4 acc[NM][NTT];
 #pragma unroll
@@ -325,12 +339,15 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
     if (nlive > 0) {
         if constexpr (F::kVq && MOEQ_VQ_GATHER_AHEAD) {
             // row c0 of the expert exists: a safe row for lanes past its rows
-            const _Float16* xsafe =
-                PHASE == 0 ? A.x16 + (int64_t)(A.perm_src[ae.r0 + c0] / A.k) * A.H
-                           : A.h16 + (int64_t)(ae.r0 + c0) * A.I;
-            stream_tiles_vq<NTT, NM>(tb, cb, xrow, xsafe, ntt, K, kpart, KS, lane, acc);
+            const uint16_t* xsafe =
+                PHASE == 0
+                    ? A.xbf + (int64_t)(A.perm_src[ae.r0 + c0] / A.k) * A.H
+                    : reinterpret_cast<const uint16_t*>(A.h16) + (int64_t)(ae.r0 + c0) * A.I;
+            stream_tiles_vq<NTT, NM, PHASE == 0>(tb, cb, xrow, xsafe, ntt, K, kpart, KS, lane,
+                                                 acc);
         } else {
-            stream_tiles<F, NTT, NM, kPrefetch>(tb, cb, xrow, ntt, K, kpart, KS, lane, acc);
+            stream_tiles<F, NTT, NM, kPrefetch, PHASE == 0>(tb, cb, xrow, ntt, K, kpart, KS, lane,
+                                                            acc);
         }
     }
 
@@ -441,7 +458,7 @@ int launch_ntt(const DecodeArgs& a, int64_t T, int slots, int phase, hipStream_t
 
 }  // namespace
 
-int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,
+int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,
                       const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
                       uint16_t* h16, float* y_perm, int phase, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -457,7 +474,7 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x1
     a.rec = L.rec;
     a.offsets = offsets;
     a.perm_src = perm_src;
-    a.x16 = reinterpret_cast<const _Float16*>(x16);
+    a.xbf = x_bf16;
     a.h16 = reinterpret_cast<_Float16*>(h16);
     a.y_perm = y_perm;
     a.E = L.E;

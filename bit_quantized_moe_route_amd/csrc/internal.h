@@ -71,7 +71,7 @@ int launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, i
 int launch_combine(const float* y_perm, const int32_t* inv_perm, const float* w,
                    int64_t T, int32_t k, int32_t H, float* out, void* stream);
 int launch_x_to_f16(const uint16_t* x, int64_t n, uint16_t* x16, void* stream);
-int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,
+int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,
                       const int32_t* perm_src, const int32_t* offsets, int64_t T,
                       int32_t k, uint16_t* h16, float* y_perm, int phase,
                       void* stream);

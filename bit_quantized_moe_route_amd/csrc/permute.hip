@@ -16,7 +16,9 @@
 //   2. each workgroup sums the histograms (all of them for the offsets,
 //      those of earlier slices for its own starting slot per expert) and
 //      ranks and scatters its slice as in step 3 above.
-// Either way the result is unique, so it does not depend on timing.
+// Decode batches (T*k <= 64) route and sort in one launch of one workgroup
+// (see k_route_permute_small).  Either way the result is unique, so it does
+// not depend on timing.
 #include "topk_dev.h"
 
 namespace moeq {
@@ -200,15 +202,82 @@ __global__ __launch_bounds__(kPermThreads) void k_route_permute(
     int* psmem = smem + kFusedMaxAssign;           // permute scratch
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    for (int t = wave; t < T; t += kPermWaves) {
+    for (int t = wave; t < T; t += kPermWaves)
         route_token<VPL>(logits + (int64_t)t * E, E, k, lane, ids + (int64_t)t * k,
-                         w + (int64_t)t * k);
-        // lane 0 wrote the ids to global; it also puts them in LDS
-        if (lane == 0)
-            for (int j = 0; j < k; ++j) lds_ids[t * k + j] = ids[t * k + j];
-    }
+                         w + (int64_t)t * k, lds_ids + t * k);
     __syncthreads();
     permute_body(lds_ids, T * k, E, counts, offsets, perm_src, inv_perm, psmem);
+}
+
+// Route + permute for T*k <= 64 (decode): one workgroup of min(T, 16)
+// waves routes the tokens (ids also to LDS); wave 0 then sorts the n = T*k
+// assignments, lane a holding assignment a: an LDS histogram, a wave scan of
+// the E counts (lane L sums experts L*per .. L*per + per - 1), and the rank
+// of a among the lanes with the same expert (11 ballots) added to that
+// expert's offset.
+constexpr int kSmallAssign = 64;
+constexpr int kSmallMaxWaves = 16;
+
+template <int VPL>
+__global__ __launch_bounds__(64 * kSmallMaxWaves) void k_route_permute_small(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm) {
+    __shared__ int sids[kSmallAssign];
+    __shared__ int hist[MOE_MAX_E];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    for (int x = threadIdx.x; x < E; x += blockDim.x) hist[x] = 0;
+    for (int t = wave; t < T; t += nw)
+        route_token<VPL>(logits + (int64_t)t * E, E, k, lane, ids + (int64_t)t * k,
+                         w + (int64_t)t * k, sids + t * k);
+    __syncthreads();
+    const int n = T * k;
+    const bool valid = lane < n;
+    const int e = valid ? sids[lane] : 0x7ff;   // sentinel never equals an id
+    if (wave == 0 && valid) atomicAdd(&hist[e], 1);
+    __syncthreads();
+    if (wave != 0) return;
+    // exclusive scan of hist over the experts: lane L owns a run of `per`
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    int sum = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) sum += hist[e0 + i];
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    int run = incl - sum;
+    for (int i = 0; i < per; ++i) {
+        const int x = e0 + i;
+        if (x < E) {
+            const int c = hist[x];
+            counts[x] = c;
+            offsets[x] = run;
+            hist[x] = run;   // this expert's first slot, for the ranks below
+            run += c;
+        }
+    }
+    if (lane == 0) offsets[E] = n;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+        const uint64_t bal = __ballot((e >> b) & 1);
+        peers &= ((e >> b) & 1) ? bal : ~bal;
+    }
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (valid) {
+        const int r = hist[e] + __popcll(peers & lt_mask);
+        perm_src[r] = lane;
+        inv_perm[lane] = r;
+    }
 }
 
 }  // namespace
@@ -262,6 +331,18 @@ int launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, i
                          float* w, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                          int32_t* inv_perm, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (T * k <= kSmallAssign) {
+        const int waves = T < kSmallMaxWaves ? (int)T : kSmallMaxWaves;
+        const int nt = 64 * (waves > 0 ? waves : 1);
+        if (E <= 256)
+            k_route_permute_small<4><<<1, nt, 0, s>>>(logits, (int)T, E, k, ids, w, counts,
+                                                     offsets, perm_src, inv_perm);
+        else
+            k_route_permute_small<16><<<1, nt, 0, s>>>(logits, (int)T, E, k, ids, w, counts,
+                                                      offsets, perm_src, inv_perm);
+        MOEQ_CHECK_LAUNCH();
+        return MOE_OK;
+    }
     const size_t lds = (size_t)kFusedMaxAssign * sizeof(int32_t) + permute_lds_bytes(E);
     if (E <= 256)
         k_route_permute<4><<<1, kPermThreads, lds, s>>>(logits, (int)T, E, k, ids, w, counts,

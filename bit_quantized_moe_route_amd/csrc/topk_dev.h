@@ -57,10 +57,12 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
     return best;
 }
 
-// Top-k of one token's logits row; lane 0 writes ids[0..k) and w[0..k).
+// Top-k of one token's logits row; lane 0 writes ids[0..k) and w[0..k), and
+// the ids also to lds_ids[0..k) if that is not null.
 template <int VPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
-                                            int32_t* __restrict__ ids, float* __restrict__ wout) {
+                                            int32_t* __restrict__ ids, float* __restrict__ wout,
+                                            int* lds_ids = nullptr) {
     uint64_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -101,6 +103,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
             if (j < k) {
                 ids[j] = top_i[j];
                 wout[j] = ex[j] / sum;
+                if (lds_ids) lds_ids[j] = top_i[j];
             }
         }
     }

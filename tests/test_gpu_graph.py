@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import bit_quantized_moe_route_amd as moeq
+import oracle
 import synth
 from tests.gpu_common import build_small_layer, say
 
@@ -15,17 +16,28 @@ DEV = "cuda"
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 256, 8), (32, 256, 8), (512, 256, 8), (700, 64, 8),
-                                   (5, 1024, 16), (3, 4, 1), (4096, 256, 8), (300, 1024, 16)])
+                                   (5, 1024, 16), (3, 4, 1), (4096, 256, 8), (300, 1024, 16),
+                                   (8, 256, 8), (4, 1024, 16), (64, 16, 1), (9, 64, 7),
+                                   (0, 8, 2)])
 def test_route_permute_equals_separate_calls(T, E, k):
     say("route_permute", T, E, k)
     g = np.random.default_rng(T + E)
     lg = torch.from_numpy(g.random((T, E)).astype(np.float32)).to(DEV)
+    if T >= 4:
+        lg[3] = 0.5   # a token of tied logits: the tie rule picks ids 0 .. k-1
     fused = moeq.route_permute(lg, k)
     ids, w = moeq.route_topk(lg, k)
     perm = moeq.permute(ids, E)
     for a, b, nm in zip(fused, (ids, w) + tuple(perm),
                         ("ids", "w", "counts", "offsets", "perm_src", "inv_perm")):
         assert torch.equal(a, b), nm
+    # and against the oracle
+    lg_np = lg.cpu().numpy()
+    oids, _ = oracle.route_topk(lg_np, k) if T else (np.zeros((0, k), np.int32), None)
+    assert np.array_equal(fused[0].cpu().numpy(), oids)
+    for a, b, nm in zip(fused[2:], oracle.permute(oids, E),
+                        ("counts", "offsets", "perm_src", "inv_perm")):
+        assert np.array_equal(a.cpu().numpy(), b), nm
 
 
 def test_graph_replays_equal_eager():
