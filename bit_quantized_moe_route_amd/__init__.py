@@ -329,7 +329,7 @@ def permute_workspace(T, k, E, device="cuda"):
 
 
 def route_permute(logits, k, E=None, out=None, ws=None):
-    """route_topk + permute in one call (one launch for T*k <= 4096).
+    """route_topk + permute in one call (one launch for T*k <= 64).
     Returns topk_ids, topk_w, counts, offsets, perm_src, inv_perm.  `ws`:
     from permute_workspace (allocated here if needed and not given)."""
     torch = _torch()

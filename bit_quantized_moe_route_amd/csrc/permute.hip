@@ -1,7 +1,7 @@
 // Token permutation: a stable counting sort of the T*k assignments by expert,
-// and the fused route + permute kernel for small batches.
+// and the fused route + permute kernel for decode batches.
 //
-// Small batches (T*k <= 4096), one workgroup of 1024 threads:
+// Batches up to T*k = 4096, one workgroup of 1024 threads:
 //   1. histogram of expert ids in LDS;
 //   2. exclusive prefix scan over the E counts (wave scans + a scan of the
 //      wave totals) -> counts, offsets;
@@ -27,9 +27,6 @@ namespace {
 
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
-// fused route + permute: the ids stay in LDS; T*k up to this many
-constexpr int kFusedMaxAssign = 4096;
-
 __host__ __device__ constexpr size_t permute_lds_bytes(int E) {
     return (size_t)(2 * E + kPermWaves) * sizeof(int) + (size_t)kPermWaves * E;
 }
@@ -189,26 +186,6 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
     permute_body(ids, n, E, counts, offsets, perm_src, inv_perm, smem);
 }
 
-// Route + permute in one workgroup: wave w routes tokens w, w + 16, ...,
-// writing ids/weights to global memory and the ids to LDS, then the
-// workgroup permutes from LDS.
-template <int VPL>
-__global__ __launch_bounds__(kPermThreads) void k_route_permute(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm) {
-    extern __shared__ int smem[];
-    int32_t* lds_ids = smem;                       // [T*k]
-    int* psmem = smem + kFusedMaxAssign;           // permute scratch
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    for (int t = wave; t < T; t += kPermWaves)
-        route_token<VPL>(logits + (int64_t)t * E, E, k, lane, ids + (int64_t)t * k,
-                         w + (int64_t)t * k, lds_ids + t * k);
-    __syncthreads();
-    permute_body(lds_ids, T * k, E, counts, offsets, perm_src, inv_perm, psmem);
-}
-
 // Route + permute for T*k <= 64 (decode): one workgroup of min(T, 16)
 // waves routes the tokens (ids also to LDS); wave 0 then sorts the n = T*k
 // assignments, lane a holding assignment a: an LDS histogram, a wave scan of
@@ -287,7 +264,10 @@ __global__ __launch_bounds__(64 * kSmallMaxWaves) void k_route_permute_small(
 constexpr int kPermSlice = 2048;
 constexpr int kPermMaxSlices = 64;
 
-bool permute_single(int64_t n) { return n <= kFusedMaxAssign; }
+// one-workgroup permute up to this many assignments
+constexpr int kSingleMaxAssign = 4096;
+
+bool permute_single(int64_t n) { return n <= kSingleMaxAssign; }
 
 int permute_slice(int64_t n) {
     int64_t c = (n + kPermMaxSlices - 1) / kPermMaxSlices;
@@ -325,31 +305,20 @@ int launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t*
     return MOE_OK;
 }
 
-bool route_permute_fused_ok(int64_t T, int32_t k) { return T * k <= kFusedMaxAssign; }
+bool route_permute_fused_ok(int64_t T, int32_t k) { return T * k <= kSmallAssign; }
 
 int launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
                          float* w, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                          int32_t* inv_perm, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (T * k <= kSmallAssign) {
-        const int waves = T < kSmallMaxWaves ? (int)T : kSmallMaxWaves;
-        const int nt = 64 * (waves > 0 ? waves : 1);
-        if (E <= 256)
-            k_route_permute_small<4><<<1, nt, 0, s>>>(logits, (int)T, E, k, ids, w, counts,
-                                                     offsets, perm_src, inv_perm);
-        else
-            k_route_permute_small<16><<<1, nt, 0, s>>>(logits, (int)T, E, k, ids, w, counts,
-                                                      offsets, perm_src, inv_perm);
-        MOEQ_CHECK_LAUNCH();
-        return MOE_OK;
-    }
-    const size_t lds = (size_t)kFusedMaxAssign * sizeof(int32_t) + permute_lds_bytes(E);
+    const int waves = T < kSmallMaxWaves ? (int)T : kSmallMaxWaves;
+    const int nt = 64 * (waves > 0 ? waves : 1);
     if (E <= 256)
-        k_route_permute<4><<<1, kPermThreads, lds, s>>>(logits, (int)T, E, k, ids, w, counts,
-                                                        offsets, perm_src, inv_perm);
+        k_route_permute_small<4><<<1, nt, 0, s>>>(logits, (int)T, E, k, ids, w, counts, offsets,
+                                                 perm_src, inv_perm);
     else
-        k_route_permute<16><<<1, kPermThreads, lds, s>>>(logits, (int)T, E, k, ids, w, counts,
-                                                         offsets, perm_src, inv_perm);
+        k_route_permute_small<16><<<1, nt, 0, s>>>(logits, (int)T, E, k, ids, w, counts, offsets,
+                                                  perm_src, inv_perm);
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
 }

@@ -10,8 +10,8 @@
 // The order is carried by one 64-bit key per candidate:
 //   key = (monotone bits of (logit + 0.0)) << 32 | (0xffffffff - id)
 // so the best candidate is the largest key (key 0 = empty or taken; a real
-// key is never 0, even for -inf).  The wave maximum uses DPP row permutes
-// inside each row of 16 lanes and four readlanes across the rows.
+// key is never 0, even for -inf).  Wave maxima use DPP row permutes inside
+// each row of 16 lanes and four readlanes across the rows, on 32-bit halves.
 #pragma once
 
 #include "dev_common.h"
@@ -32,33 +32,28 @@ __device__ __forceinline__ uint64_t make_key(float v, int id) {
     return ((uint64_t)mono_bits(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)id);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)k, CTRL, 0xf, 0xf, false);
-    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(k >> 32), CTRL, 0xf, 0xf, false);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    return o > k ? o : k;
-}
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-// Largest key over the wave (the same value in every lane).
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-    k = dpp_max<0xB1>(k);    // quad_perm [1,0,3,2]
-    k = dpp_max<0x4E>(k);    // quad_perm [2,3,0,1]
-    k = dpp_max<0x141>(k);   // row_half_mirror
-    k = dpp_max<0x140>(k);   // row_mirror: every lane holds its row's maximum
-    uint64_t best = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 16 * r);
-        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 16 * r);
-        const uint64_t v = ((uint64_t)hi << 32) | lo;
-        best = v > best ? v : best;
-    }
-    return best;
+// Largest 32-bit value (unsigned) over the wave, the same in every lane: DPP
+// row permutes inside each row of 16 lanes, then the four rows' maxima.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false));
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false));
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xf, 0xf, false));
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xf, 0xf, false));
+    const uint32_t a = umax32((uint32_t)__builtin_amdgcn_readlane(v, 0),
+                              (uint32_t)__builtin_amdgcn_readlane(v, 16));
+    const uint32_t b = umax32((uint32_t)__builtin_amdgcn_readlane(v, 32),
+                              (uint32_t)__builtin_amdgcn_readlane(v, 48));
+    return umax32(a, b);
 }
 
 // Top-k of one token's logits row; lane 0 writes ids[0..k) and w[0..k), and
 // the ids also to lds_ids[0..k) if that is not null.
+// Each round takes the wave's largest remaining key: first the largest
+// high half (the logit's monotone bits) over the lanes' best keys, then,
+// only if several lanes hold that logit, the largest low half (the lowest
+// id) among them.  The lane that owns the winner clears that key.
 template <int VPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
                                             int32_t* __restrict__ ids, float* __restrict__ wout,
@@ -79,15 +74,32 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
 #pragma unroll
     for (int j = 0; j < MOE_MAX_K; ++j) {
         if (j < k) {
-            uint64_t mine = 0;
+            // the lane's best remaining key and its slot
+            uint64_t mine = key[0];
+            int slot = 0;
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) mine = key[i] > mine ? key[i] : mine;
-            const uint64_t best = wave_max_key(mine);
-            top_i[j] = (int)(0xffffffffu - (uint32_t)best);
-            top_v[j] = mono_float((uint32_t)(best >> 32));
+            for (int i = 1; i < VPL; ++i)
+                if (key[i] > mine) {
+                    mine = key[i];
+                    slot = i;
+                }
+            const uint32_t hi = (uint32_t)(mine >> 32);
+            const uint32_t lo = (uint32_t)mine;
+            const uint32_t best_hi = wave_max_u32(hi);
+            const uint64_t tied = __ballot(hi == best_hi);
+            uint32_t best_lo;
+            if (__popcll(tied) == 1)
+                best_lo = (uint32_t)__builtin_amdgcn_readlane(lo, __ffsll((unsigned long long)tied) - 1);
+            else
+                best_lo = wave_max_u32(hi == best_hi ? lo : 0u);
+            top_i[j] = (int)(0xffffffffu - best_lo);
+            top_v[j] = mono_float(best_hi);
+            // keys are unique (ids differ): exactly one lane holds the winner
+            if (hi == best_hi && lo == best_lo) {
 #pragma unroll
-            for (int i = 0; i < VPL; ++i)
-                if (key[i] == best) key[i] = 0ull;   // taken (keys are unique: ids differ)
+                for (int i = 0; i < VPL; ++i)
+                    if (i == slot) key[i] = 0ull;
+            }
         }
     }
     if (lane == 0) {

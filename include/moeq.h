@@ -170,11 +170,12 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
 
 /*
  * moe_route_permute -- moe_route_topk followed by moe_permute, with the
- * same outputs bit for bit; for T*k <= 4096 both run in one workgroup (one
- * launch, the ids never leave the chip between the two steps), which is
- * what a decode step wants.  Same arguments, limits and errors as the two
- * calls; ws/ws_bytes as for moe_permute (moe_permute_workspace_bytes gives
- * the size; it is 0, and ws may be NULL, for T*k <= 4096).
+ * same outputs bit for bit.  For T*k <= 64 (a decode step) both run in one
+ * launch of one workgroup (the ids never leave the chip between the two
+ * steps); larger batches run the two steps' own kernels.  Same arguments,
+ * limits and errors as the two calls; ws/ws_bytes as for moe_permute
+ * (moe_permute_workspace_bytes gives the size; it is 0, and ws may be NULL,
+ * for T*k <= 4096).
  */
 int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
                       int32_t* topk_ids, float* topk_w, int32_t* counts,
