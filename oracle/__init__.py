@@ -19,12 +19,15 @@ it follows:
 * GLM-5.3-Flash-TR3-8bpw (K8), "Fidelity" / "Excess over control" -- the
   expert-combine order changes the bits, so the combine order is fixed.
 
-Where the pages are silent the oracle takes the plainest reading; every such
-reading is listed in the design doc (readings R1..).
+Where the pages are silent the oracle takes the plainest reading, stated in
+the docstring of the function that makes it.
 
 Parity status per function (what pins each one is in tests/test_oracle_*.py):
   e2m1_decode, e4m3_decode, e4m3_encode, nvfp4_quantize, nvfp4_dequant,
-  vq_dequant, route_topk, permute, expert_ffn, combine, forward -- all pinned.
+  vq_dequant, vq8_dequant, route_topk, permute, expert_ffn, combine, forward
+  -- all pinned.  vq8_dequant's arithmetic is pinned; its code shape (M
+  8-bit codes per 8-weight group into M 256-entry codebooks whose rows are
+  summed) is a reading the pages do not fix: parity unpinned for the shape.
 """
 
 from .formats import (  # noqa: F401
@@ -36,6 +39,7 @@ from .formats import (  # noqa: F401
     nvfp4_quantize,
     nvfp4_dequant,
     vq_dequant,
+    vq8_dequant,
     bf16_bits_to_f64,
     f16_bits_to_f64,
 )

@@ -18,6 +18,14 @@ AQLM-style VQ (GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw, "What it is":
 per-group codes into a shared codebook) is read as: groups of 8 consecutive
 input weights, one uint16 code per group indexing a 65536 x 8 fp16 codebook,
 and one fp16 scale per output channel: W[o, 8g+j] = S[o] * C[code[o, g], j].
+
+The small-codebook VQ modules (the same page: 1-, 2- and 3-bit modules,
+"per-group codes + shared codebook") are read as groups of 8 input weights
+with M = 1 or 2 uint8 codes each, code m indexing a 256 x 8 fp16 codebook
+C_m shared by the layer's experts, the rows summed (additive codebooks, as
+in AQLM): W[o, 8g+j] = S[o] * sum_m C_m[code[o, g, m], j].  M = 1 is 1 bit
+per weight, M = 2 is 2 bits per weight.  The pages do not give these code
+shapes; they are this reading's.
 """
 
 import numpy as np
@@ -215,3 +223,31 @@ def vq_dequant(codes, scales_f16, codebook_f16):
         raise ValueError("scale shape mismatch")
     rows = C[codes.astype(np.int64)]          # [n, g, 8]
     return (S[:, None, None] * rows).reshape(n, g * 8)
+
+
+def vq8_dequant(codes, scales_f16, codebooks_f16):
+    """W[o, 8g + j] = S[o] * sum_m C_m[code[o, g, m], j] in float64.
+
+    codes uint8 [n, kin/8, M]; scales_f16 uint16 bits [n]; codebooks_f16: M
+    arrays of uint16 bits [256, 8] (C_0, C_1, ...).  The sum of the M fp16
+    rows is exact in float64; the product with S rounds once (float64).
+    (GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw, "What it is": 1/2/3-bit modules
+    with per-group codes and shared codebooks; the M x 8-bit code shape is a
+    reading, see the module docstring.)
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    S = f16_bits_to_f64(np.asarray(scales_f16, dtype=np.uint16))
+    if codes.ndim != 3:
+        raise ValueError("codes must be [n, kin/8, M]")
+    n, g, M = codes.shape
+    if len(codebooks_f16) != M:
+        raise ValueError("one codebook per code of a group")
+    if S.shape != (n,):
+        raise ValueError("scale shape mismatch")
+    acc = np.zeros((n, g, 8), dtype=np.float64)
+    for m in range(M):
+        C = f16_bits_to_f64(np.asarray(codebooks_f16[m], dtype=np.uint16))
+        if C.shape != (256, 8):
+            raise ValueError("codebook must be [256, 8]")
+        acc += C[codes[:, :, m].astype(np.int64)]
+    return (S[:, None, None] * acc).reshape(n, g * 8)

@@ -40,11 +40,14 @@ KIND_VQ_SCALES = 5
 KIND_TIER = 6
 KIND_HOT = 7
 KIND_ZIPF_RANK = 8
+KIND_VQ8_CODES = 9
+KIND_VQ8_CODEBOOK = 10
 
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 
 FMT_NVFP4 = 1
 FMT_VQ = 2
+FMT_VQ8 = 3
 
 
 def rng(cfg, kind, expert=0, proj=0, rep=0):
@@ -82,7 +85,7 @@ class Workload:
     H: int
     I: int
     T: tuple
-    fmt: str            # "nvfp4", "vq" or "mixed"
+    fmt: str            # "nvfp4", "vq", "vq8", "mixed" or "mixed3" (all three)
     logits: str         # "normal", "uniform", "zipf" or "hot"
     weight_cfg: int = 1     # seed slot of the NVFP4 weights
     vq_cfg: int = 3         # seed slot of the VQ codes/codebooks/scales
@@ -90,6 +93,7 @@ class Workload:
     n_hot: int = 0
     hot_share: float = 0.0
     zipf_s: float = 0.0
+    vq8_m: int = 0          # codes per 8-weight group of the small-codebook VQ
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
 
@@ -101,15 +105,19 @@ VQ = Workload("vq", 3, 256, 8, 6144, 2048, (8,), "vq", "uniform")
 MIXED = Workload("mixed", 4, 256, 8, 6144, 2048, (8, 32), "mixed", "hot",
                  n_nvfp4=108, n_hot=20, hot_share=0.6)
 
-WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED)}
+# small-codebook VQ decode layers (1 and 2 bits per weight), T = 8
+VQ1 = Workload("vq1", 5, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=5, vq8_m=1)
+VQ2X8 = Workload("vq2x8", 6, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=6, vq8_m=2)
+
+WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED, VQ1, VQ2X8)}
 
 
 def small_workload(name, E, k, H, I, T, fmt="nvfp4", logits="normal", cfg=100,
-                   n_nvfp4=0, n_hot=0, hot_share=0.0, zipf_s=0.0):
+                   n_nvfp4=0, n_hot=0, hot_share=0.0, zipf_s=0.0, vq8_m=0):
     """A property-test workload with its own seed slot."""
     return Workload(name, cfg, E, k, H, I, (T,), fmt, logits, weight_cfg=cfg,
                     vq_cfg=cfg, n_nvfp4=n_nvfp4, n_hot=n_hot, hot_share=hot_share,
-                    zipf_s=zipf_s)
+                    zipf_s=zipf_s, vq8_m=vq8_m)
 
 
 # --------------------------------------------------------------------------
@@ -235,13 +243,41 @@ def vq_codebook(wl, proj, ncode=65536):
     return f32_to_f16_bits(c)
 
 
+def vq8_codes(wl, expert, proj):
+    """Uniform uint8 codes [n, kin/8, M] of one projection of one expert
+    (small-codebook VQ, M = wl.vq8_m codes per 8-weight group)."""
+    n, kin = proj_shape(wl, proj)
+    return rng(wl.vq_cfg, KIND_VQ8_CODES, expert, proj).integers(
+        0, 256, size=(n, kin // 8, wl.vq8_m), dtype=np.uint8)
+
+
+def vq8_codebooks(wl, proj):
+    """The M fp16 codebooks [256, 8] of one projection type, shared by all the
+    layer's experts; entries ~ N(0, 0.02 / sqrt(M)) so that a summed row has
+    the spread of the 2-bit codebook's; uint16 bits."""
+    M = wl.vq8_m
+    out = []
+    for m in range(M):
+        c = rng(wl.vq_cfg, KIND_VQ8_CODEBOOK, m, proj).standard_normal(
+            (256, 8), dtype=np.float32) * np.float32(0.02 / np.sqrt(M))
+        out.append(f32_to_f16_bits(c))
+    return out
+
+
 def tier_map(wl):
-    """Per-expert format tag (FMT_NVFP4 / FMT_VQ), uint8 [E]."""
+    """Per-expert format tag (FMT_NVFP4 / FMT_VQ / FMT_VQ8), uint8 [E]."""
     if wl.fmt == "nvfp4":
         return np.full(wl.E, FMT_NVFP4, dtype=np.uint8)
     if wl.fmt == "vq":
         return np.full(wl.E, FMT_VQ, dtype=np.uint8)
+    if wl.fmt == "vq8":
+        return np.full(wl.E, FMT_VQ8, dtype=np.uint8)
+    g = rng(wl.cfg, KIND_TIER)
     tm = np.full(wl.E, FMT_VQ, dtype=np.uint8)
-    nv = rng(wl.cfg, KIND_TIER).choice(wl.E, size=wl.n_nvfp4, replace=False)
+    nv = g.choice(wl.E, size=wl.n_nvfp4, replace=False)
     tm[nv] = FMT_NVFP4
+    if wl.fmt == "mixed3":
+        # half of the remaining experts take the small-codebook VQ
+        rest = np.flatnonzero(tm == FMT_VQ)
+        tm[g.choice(rest, size=len(rest) // 2, replace=False)] = FMT_VQ8
     return tm

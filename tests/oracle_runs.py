@@ -22,6 +22,9 @@ def expert_weights(wl, e, fmt=None):
         if fmt == synth.FMT_NVFP4:
             c, s = oracle.nvfp4_quantize(synth.nvfp4_source_weights(wl, e, p))
             mats.append(oracle.nvfp4_dequant(c, s))
+        elif fmt == synth.FMT_VQ8:
+            mats.append(oracle.vq8_dequant(synth.vq8_codes(wl, e, p), synth.vq_scales(wl, e, p),
+                                           synth.vq8_codebooks(wl, p)))
         else:
             mats.append(oracle.vq_dequant(synth.vq_codes(wl, e, p), synth.vq_scales(wl, e, p),
                                           synth.vq_codebook(wl, p)))

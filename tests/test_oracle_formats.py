@@ -285,3 +285,64 @@ def test_vq_product_exact_in_fp32():
     codes = rs.integers(0, 4096, size=(64, 32), dtype=np.uint16)
     W = oracle.vq_dequant(codes, sc, cb)
     assert np.array_equal(W.astype(np.float32).astype(np.float64), W)
+
+
+# ------------------------------------------------------ small-codebook VQ
+
+def test_vq8_identity_codebooks_recover_both_codes():
+    # C_0[c] = 256 c and C_1[c] = c in every column (both exact in fp16):
+    # the summed row is 256 c0 + c1, which gives back both codes
+    c = np.arange(256, dtype=np.float64)
+    cb0 = _f16(np.repeat((256 * c)[:, None], 8, axis=1))
+    cb1 = _f16(np.repeat(c[:, None], 8, axis=1))
+    rs = np.random.default_rng(11)
+    codes = rs.integers(0, 256, size=(7, 9, 2), dtype=np.uint8)
+    W = oracle.vq8_dequant(codes, _f16(np.ones(7)), [cb0, cb1]).reshape(7, 9, 8)
+    v = W[:, :, 0].astype(np.int64)
+    assert np.array_equal(v >> 8, codes[:, :, 0]) and np.array_equal(v & 255, codes[:, :, 1])
+    assert np.all(W == W[:, :, :1])
+
+
+def test_vq8_single_codebook_is_the_plain_lookup():
+    # M = 1 is the 2-bit VQ decode restricted to a 256-entry codebook
+    rs = np.random.default_rng(12)
+    cb = _f16(rs.standard_normal((256, 8)) * 0.02)
+    sc = _f16(rs.uniform(0.5, 1.5, 5))
+    codes = rs.integers(0, 256, size=(5, 6, 1), dtype=np.uint8)
+    W = oracle.vq8_dequant(codes, sc, [cb])
+    assert np.array_equal(W, oracle.vq_dequant(codes[:, :, 0].astype(np.uint16), sc, cb))
+
+
+def test_vq8_is_additive_over_codebooks():
+    rs = np.random.default_rng(13)
+    cbs = [_f16(rs.standard_normal((256, 8)) * 0.01) for _ in range(2)]
+    codes = rs.integers(0, 256, size=(4, 5, 2), dtype=np.uint8)
+    one = _f16(np.ones(4))
+    W = oracle.vq8_dequant(codes, one, cbs)
+    W0 = oracle.vq8_dequant(codes[:, :, :1], one, cbs[:1])
+    W1 = oracle.vq8_dequant(codes[:, :, 1:], one, cbs[1:])
+    assert np.array_equal(W, W0 + W1)   # fp16 rows of this range sum exactly
+
+
+def test_vq8_one_hot_rows_and_power_of_two_scales():
+    cb0 = np.zeros((256, 8))
+    cb1 = np.zeros((256, 8))
+    cb0[5, 2] = 3.0
+    cb1[7, 6] = -1.5
+    codes = np.array([[[5, 0], [0, 7], [5, 7]]], dtype=np.uint8)
+    W = oracle.vq8_dequant(codes, _f16([4.0]), [_f16(cb0), _f16(cb1)])
+    want = np.zeros(24)
+    want[2] = 12.0
+    want[8 + 6] = -6.0
+    want[16 + 2], want[16 + 6] = 12.0, -6.0
+    assert np.array_equal(W[0], want)
+
+
+def test_vq8_rejects_bad_shapes():
+    cb = _f16(np.zeros((256, 8)))
+    with pytest.raises(ValueError):
+        oracle.vq8_dequant(np.zeros((2, 3), np.uint8), _f16(np.ones(2)), [cb])
+    with pytest.raises(ValueError):
+        oracle.vq8_dequant(np.zeros((2, 3, 2), np.uint8), _f16(np.ones(2)), [cb])
+    with pytest.raises(ValueError):
+        oracle.vq8_dequant(np.zeros((2, 3, 1), np.uint8), _f16(np.ones(2)), [_f16(np.zeros((16, 8)))])
