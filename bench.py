@@ -19,6 +19,7 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   cpu_baseline   the fp64 oracle on a bounded sample (one token), one core
   extra          the same path on the other workloads (decode T = 1 and 8,
                  prefill T = 4096 with Zipf(1.1) routing, 2-bit VQ T = 8,
+                 small-codebook VQ at 1 and 2 bits per weight T = 8,
                  mixed NVFP4/VQ T = 8 and 32)
 """
 
@@ -179,6 +180,8 @@ class Runner:
         for e in experts:
             if self.layer.fmt_host[e] == self.moeq.FMT_NVFP4:
                 tot += 2 * (H * I // 2 + H * I // 16)
+            elif self.layer.fmt_host[e] == self.moeq.FMT_VQ8:
+                tot += 2 * (H * I // 8) * self.layer.vq8_m + 2 * I * 2
             else:
                 tot += 2 * (H * I // 8) * 2 + 2 * I * 2
         return tot
@@ -286,7 +289,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--T", type=int, default=32, help="decode batch of the headline")
-    ap.add_argument("--extra", default="decode1,decode8,prefill,vq,mixed8,mixed32",
+    ap.add_argument("--extra", default="decode1,decode8,prefill,vq,vq1,vq2x8,mixed8,mixed32",
                     help="comma list of other workloads to measure ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy", action="store_true",
@@ -353,6 +356,16 @@ def main():
                     vq_codes=lambda e, p: (synth.vq_codes(wq, e, p), synth.vq_scales(wq, e, p)),
                     codebooks=[synth.vq_codebook(wq, p) for p in range(3)], device=dev, workers=16)
                 extra[name] = measure(layers["vq"], wq, 8, 30, 5, dev)
+            elif name in ("vq1", "vq2x8"):
+                w8 = synth.WORKLOADS[name]
+                log(f"building the small-codebook VQ layer {name} ...")
+                lay8 = build_layer(
+                    w8.E, w8.H, w8.I, synth.tier_map(w8),
+                    vq8_codes=lambda e, p: (synth.vq8_codes(w8, e, p), synth.vq_scales(w8, e, p)),
+                    codebooks8=[synth.vq8_codebooks(w8, p) for p in range(3)], vq8_m=w8.vq8_m,
+                    device=dev, workers=16)
+                extra[name] = measure(lay8, w8, 8, 30, 5, dev)
+                del lay8
             elif name.startswith("mixed"):
                 wm = synth.MIXED
                 T = int(name[len("mixed"):])

@@ -31,8 +31,10 @@ MOE_EHIP = -4
 
 FMT_NVFP4 = 1
 FMT_VQ = 2
+FMT_VQ8 = 3
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 VQ_NCODE = 65536
+VQ8_NCODE = 256
 
 
 class MoeError(RuntimeError):
@@ -44,7 +46,7 @@ class MoeError(RuntimeError):
 class _QLayerC(ctypes.Structure):
     _fields_ = [
         ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("vq8_m", ctypes.c_int32),
         ("fmt_host", ctypes.c_void_p),
         ("rec_dev", ctypes.c_void_p),
         ("nvfp4_w13", ctypes.c_void_p), ("nvfp4_w13_stride", ctypes.c_int64),
@@ -53,6 +55,9 @@ class _QLayerC(ctypes.Structure):
         ("vq_w2", ctypes.c_void_p), ("vq_w2_stride", ctypes.c_int64),
         ("vq_codebook", ctypes.c_void_p * 3),
         ("vq_codebook_stride", ctypes.c_int64),
+        ("vq8_w13", ctypes.c_void_p), ("vq8_w13_stride", ctypes.c_int64),
+        ("vq8_w2", ctypes.c_void_p), ("vq8_w2_stride", ctypes.c_int64),
+        ("vq8_codebook", ctypes.c_void_p * 3),
     ]
 
 
@@ -79,9 +84,11 @@ _PROTOS = {
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
     "moe_quantize_nvfp4": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "moe_record_bytes": (_SZ, [ctypes.c_int, ctypes.c_int, _I32, _I32]),
+    "moe_record_bytes_vq8": (_SZ, [ctypes.c_int, _I32, _I32, _I32]),
+    "moe_pack_vq8_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _I32, _P, _P]),
     "moe_pack_nvfp4_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
     "moe_pack_vq_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
-    "moe_record_table": (ctypes.c_int, [_P, _I32, _P, _P, _P]),
+    "moe_record_table": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P]),
     "moe_dequant_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _I32, _I32, _P, _P]),
 }
 
@@ -131,7 +138,9 @@ def quantize_nvfp4(w):
     return codes, scales
 
 
-def record_bytes(fmt, which, H, I):
+def record_bytes(fmt, which, H, I, vq8_m=0):
+    if fmt == FMT_VQ8:
+        return int(lib().moe_record_bytes_vq8(which, H, I, vq8_m))
     return int(lib().moe_record_bytes(fmt, which, H, I))
 
 
@@ -159,14 +168,30 @@ def pack_vq_expert(gate, up, down, H, I, w13=None, w2=None):
     return w13, w2
 
 
+def pack_vq8_expert(gate, up, down, H, I, m, w13=None, w2=None):
+    """gate/up/down = (codes uint8 [n, kin/8, m], scales fp16 bits uint16 [n])."""
+    if w13 is None:
+        w13 = np.empty(record_bytes(FMT_VQ8, 0, H, I, m), np.uint8)
+    if w2 is None:
+        w2 = np.empty(record_bytes(FMT_VQ8, 1, H, I, m), np.uint8)
+    arrs = []
+    for codes, scales in (gate, up, down):
+        arrs.append(np.ascontiguousarray(codes, dtype=np.uint8))
+        arrs.append(np.ascontiguousarray(scales, dtype=np.uint16))
+    _check(lib().moe_pack_vq8_expert(*[_np_ptr(a) for a in arrs], H, I, m, _np_ptr(w13),
+                                     _np_ptr(w2)), "moe_pack_vq8_expert")
+    return w13, w2
+
+
 def record_table(fmt_host):
+    """(rec [E] int32, experts per format {FMT_NVFP4: n, FMT_VQ: n, FMT_VQ8: n})."""
     fmt_host = np.ascontiguousarray(fmt_host, dtype=np.uint8)
     E = fmt_host.shape[0]
     rec = np.empty(E, np.int32)
-    nn, nv = ctypes.c_int32(), ctypes.c_int32()
+    nn, nv, n8 = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(lib().moe_record_table(_np_ptr(fmt_host), E, _np_ptr(rec), ctypes.byref(nn),
-                                  ctypes.byref(nv)), "moe_record_table")
-    return rec, nn.value, nv.value
+                                  ctypes.byref(nv), ctypes.byref(n8)), "moe_record_table")
+    return rec, {FMT_NVFP4: nn.value, FMT_VQ: nv.value, FMT_VQ8: n8.value}
 
 
 # --------------------------------------------------------------------------
@@ -202,25 +227,30 @@ class QLayer:
     descriptor that points at them.  Build it with `QLayer.build(...)`.
     """
 
-    def __init__(self, E, H, I, fmt_host, device="cuda"):
+    def __init__(self, E, H, I, fmt_host, device="cuda", vq8_m=0):
         torch = _torch()
         self.E, self.H, self.I = int(E), int(H), int(I)
         self.fmt_host = np.ascontiguousarray(fmt_host, dtype=np.uint8)
-        rec, self.n_nvfp4, self.n_vq = record_table(self.fmt_host)
+        rec, counts = record_table(self.fmt_host)
+        self.n_nvfp4, self.n_vq, self.n_vq8 = counts[FMT_NVFP4], counts[FMT_VQ], counts[FMT_VQ8]
+        if self.n_vq8 and vq8_m not in (1, 2):
+            raise ValueError("a layer with small-codebook VQ experts needs vq8_m = 1 or 2")
+        self.vq8_m = int(vq8_m)
         self.rec_host = rec
         self.device = torch.device(device)
         self.rec_dev = torch.from_numpy(rec).to(self.device)
         self.stride = {}
         self.pools = {}
-        for fmt, n in ((FMT_NVFP4, self.n_nvfp4), (FMT_VQ, self.n_vq)):
+        for fmt, n in ((FMT_NVFP4, self.n_nvfp4), (FMT_VQ, self.n_vq), (FMT_VQ8, self.n_vq8)):
             for which in (0, 1):
-                b = record_bytes(fmt, which, H, I)
+                b = record_bytes(fmt, which, H, I, self.vq8_m) if n else 0
                 s = (b + 255) // 256 * 256
                 self.stride[(fmt, which)] = s
                 self.pools[(fmt, which)] = (torch.empty(n * s, dtype=torch.uint8, device=self.device)
                                             if n else None)
         self.codebooks = [None, None, None]
         self.codebook_stride = 0
+        self.codebooks8 = [None, None, None]
         self._c = None
 
     def record_index(self, e):
@@ -246,13 +276,30 @@ class QLayer:
         self.codebook_stride = int(stride)
         self._c = None
 
+    def set_codebooks8(self, cbs):
+        """Small-codebook VQ: for gate, up and down, a list of vq8_m uint16
+        arrays [256, 8] (fp16 bits), codebook 0 first."""
+        torch = _torch()
+        out = []
+        for books in cbs:
+            if len(books) != self.vq8_m:
+                raise ValueError("vq8_m codebooks per projection")
+            a = np.ascontiguousarray(np.concatenate([np.asarray(b, dtype=np.uint16) for b in books]))
+            if a.shape != (self.vq8_m * VQ8_NCODE, 8):
+                raise ValueError("codebooks must be [256, 8] each")
+            out.append(torch.from_numpy(a.view(np.int16)).to(self.device))
+        self.codebooks8 = out
+        self._c = None
+
     def c(self):
         if self._c is None:
             d = _QLayerC()
             d.E, d.H, d.I = self.E, self.H, self.I
             d.fmt_host = self.fmt_host.ctypes.data
             d.rec_dev = self.rec_dev.data_ptr()
-            for fmt, n13, n2 in ((FMT_NVFP4, "nvfp4_w13", "nvfp4_w2"), (FMT_VQ, "vq_w13", "vq_w2")):
+            d.vq8_m = self.vq8_m
+            for fmt, n13, n2 in ((FMT_NVFP4, "nvfp4_w13", "nvfp4_w2"), (FMT_VQ, "vq_w13", "vq_w2"),
+                                 (FMT_VQ8, "vq8_w13", "vq8_w2")):
                 p13, p2 = self.pools[(fmt, 0)], self.pools[(fmt, 1)]
                 setattr(d, n13, p13.data_ptr() if p13 is not None else None)
                 setattr(d, n2, p2.data_ptr() if p2 is not None else None)
@@ -262,6 +309,9 @@ class QLayer:
                 cb = self.codebooks[p]
                 d.vq_codebook[p] = cb.data_ptr() if cb is not None else None
             d.vq_codebook_stride = self.codebook_stride
+            for p in range(3):
+                cb = self.codebooks8[p]
+                d.vq8_codebook[p] = cb.data_ptr() if cb is not None else None
             self._c = d
         return self._c
 
@@ -270,15 +320,20 @@ class QLayer:
         each codebook once if a VQ expert is among them: the bytes a forward
         over those experts must read."""
         tot = 0
-        vq = False
+        vq = vq8 = False
         for e in set(int(x) for x in experts):
             if self.fmt_host[e] == FMT_NVFP4:
                 tot += 3 * (self.H * self.I // 2 + self.H * self.I // 16)
+            elif self.fmt_host[e] == FMT_VQ8:
+                vq8 = True
+                tot += 3 * (self.H * self.I // 8) * self.vq8_m + (2 * self.I + self.H) * 2
             else:
                 vq = True
                 tot += 3 * (self.H * self.I // 8) * 2 + (2 * self.I + self.H) * 2
         if vq and self.codebook_stride == 0:
             tot += 3 * VQ_NCODE * 8 * 2
+        if vq8:
+            tot += 3 * self.vq8_m * VQ8_NCODE * 8 * 2
         return tot
 
 

@@ -34,7 +34,7 @@ int check_route_sizes(const char* fn, int64_t T, int32_t E, int32_t k) {
 
 struct LayerInfo {
     LayerView view;
-    int32_t count[3];
+    int32_t count[kNumFmt];
 };
 
 // Validate a layer descriptor; fill the device view and per-format counts.
@@ -44,10 +44,10 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     if (L->E < 1 || L->E > MOE_MAX_E) return fail(MOE_EINVAL, f + ": bad E");
     if (L->H <= 0 || L->I <= 0) return fail(MOE_EINVAL, f + ": bad H or I");
     if (!L->fmt_host || !L->rec_dev) return fail(MOE_EINVAL, f + ": fmt_host / rec_dev is NULL");
-    out.count[0] = out.count[1] = out.count[2] = 0;
+    for (int t = 0; t < kNumFmt; ++t) out.count[t] = 0;
     for (int e = 0; e < L->E; ++e) {
         const int t = L->fmt_host[e];
-        if (t != MOE_FMT_NVFP4 && t != MOE_FMT_VQ)
+        if (t != MOE_FMT_NVFP4 && t != MOE_FMT_VQ && t != MOE_FMT_VQ8)
             return fail(MOE_EUNSUPPORTED, f + ": expert " + std::to_string(e) +
                                               " has format tag " + std::to_string(t) +
                                               ", which this library does not decode");
@@ -70,15 +70,27 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     v.pool2[MOE_FMT_VQ] = static_cast<const uint8_t*>(L->vq_w2);
     v.stride13[MOE_FMT_VQ] = L->vq_w13_stride;
     v.stride2[MOE_FMT_VQ] = L->vq_w2_stride;
+    v.pool13[MOE_FMT_VQ8] = static_cast<const uint8_t*>(L->vq8_w13);
+    v.pool2[MOE_FMT_VQ8] = static_cast<const uint8_t*>(L->vq8_w2);
+    v.stride13[MOE_FMT_VQ8] = L->vq8_w13_stride;
+    v.stride2[MOE_FMT_VQ8] = L->vq8_w2_stride;
     for (int p = 0; p < 3; ++p) v.cb[p] = static_cast<const uint8_t*>(L->vq_codebook[p]);
     v.cb_stride = L->vq_codebook_stride;
-    for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
+    for (int p = 0; p < 3; ++p) v.cb8[p] = static_cast<const uint8_t*>(L->vq8_codebook[p]);
+    v.vq8_m = L->vq8_m;
+    if (out.count[MOE_FMT_VQ8] && (L->vq8_m < 1 || L->vq8_m > MOE_VQ8_MAX_M))
+        return fail(MOE_EUNSUPPORTED, f + ": vq8_m must be 1 or 2");
+    for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!out.count[fmt]) continue;
-        const char* name = fmt == MOE_FMT_NVFP4 ? "NVFP4" : "VQ";
+        const char* name = fmt == MOE_FMT_NVFP4 ? "NVFP4" : fmt == MOE_FMT_VQ ? "VQ" : "VQ8";
         if (!v.pool13[fmt] || !v.pool2[fmt])
             return fail(MOE_EINVAL, f + ": " + name + " experts present but their pool is NULL");
-        const int64_t b13 = (int64_t)moe_record_bytes(fmt, 0, L->H, L->I);
-        const int64_t b2 = (int64_t)moe_record_bytes(fmt, 1, L->H, L->I);
+        const int64_t b13 = fmt == MOE_FMT_VQ8
+                                ? (int64_t)moe_record_bytes_vq8(0, L->H, L->I, L->vq8_m)
+                                : (int64_t)moe_record_bytes(fmt, 0, L->H, L->I);
+        const int64_t b2 = fmt == MOE_FMT_VQ8
+                               ? (int64_t)moe_record_bytes_vq8(1, L->H, L->I, L->vq8_m)
+                               : (int64_t)moe_record_bytes(fmt, 1, L->H, L->I);
         if (v.stride13[fmt] < b13 || v.stride2[fmt] < b2 || v.stride13[fmt] % 256 ||
             v.stride2[fmt] % 256)
             return fail(MOE_EINVAL, f + ": " + name +
@@ -91,6 +103,9 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
         if (v.cb_stride < 0 || (v.cb_stride && v.cb_stride < (int64_t)MOE_VQ_NCODE * 16))
             return fail(MOE_EINVAL, f + ": bad vq_codebook_stride");
     }
+    if (out.count[MOE_FMT_VQ8])
+        for (int p = 0; p < 3; ++p)
+            if (!v.cb8[p]) return fail(MOE_EINVAL, f + ": VQ8 experts present but a codebook is NULL");
     return MOE_OK;
 }
 
@@ -207,7 +222,7 @@ int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16, const i
         st = launch_x_to_f16(x_bf16, T * layer->H, x16, stream);
         if (st) return st;
     }
-    for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
+    for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!li.count[fmt]) continue;
         if (fmt == MOE_FMT_NVFP4 && prefill)
             st = launch_ffn_prefill(li.view, li.count[fmt], x16, perm_src, offsets, T, k, h_f16,
@@ -230,7 +245,7 @@ int moe_expert_down_q(const moe_qlayer* layer, const uint16_t* h_f16, const int3
     if (st) return st;
     if (T == 0) return MOE_OK;
     if (!h_f16 || !offsets || !y_perm) return fail(MOE_EINVAL, "moe_expert_down_q: null pointer");
-    for (int fmt = MOE_FMT_NVFP4; fmt <= MOE_FMT_VQ; ++fmt) {
+    for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!li.count[fmt]) continue;
         if (fmt == MOE_FMT_NVFP4 && T >= kPrefillMinTokens)
             st = launch_ffn_prefill(li.view, li.count[fmt], nullptr, nullptr, offsets, T, k,

@@ -1,8 +1,10 @@
 // Test hook: decode one projection of one expert from its device record to
-// fp32 with the same decode routines as the FFN kernels.  Every decoded value
-// is exact (NVFP4: an E2M1 value times an E4M3 scale, exact in fp16; VQ: an
+// fp32 with the same decode routines as the FFN kernels.  NVFP4 and VQ values
+// are exact (NVFP4: an E2M1 value times an E4M3 scale, exact in fp16; VQ: an
 // fp16 codebook entry times an fp16 scale, exact in fp32), so the output can
-// be compared bit for bit with a plain decode of the canonical bytes.
+// be compared bit for bit with a plain decode of the canonical bytes.  VQ8
+// with one code per group is exact too; with two it is
+// fp32(fp32(C_0 + C_1) * S).
 #include "dev_common.h"
 
 namespace moeq {
@@ -59,6 +61,40 @@ __global__ __launch_bounds__(64) void k_dequant_vq(const uint8_t* __restrict__ r
     }
 }
 
+// VQ8: the M small codebooks of the projection, [M][256][8] fp16
+template <int M>
+__global__ __launch_bounds__(64) void k_dequant_vq8(const uint8_t* __restrict__ rec, int rg_step,
+                                                    int rg_off, int n, int kin,
+                                                    const uint8_t* __restrict__ cb,
+                                                    const _Float16* __restrict__ scales,
+                                                    float* __restrict__ out) {
+    const int lane = threadIdx.x;
+    const int g = blockIdx.x;
+    const int kb = blockIdx.y;
+    const int nkb = gridDim.y;
+    const uint8_t* tile =
+        rec + ((int64_t)(g * rg_step + rg_off) * nkb + kb) * (kVq8TileBytesPerCode * M);
+    const uint8_t* lc = tile + lane * 8 * M;
+    const int row = 16 * g + (lane & 15);
+    const int k0 = kb * kVq8TileK + (lane >> 4) * 64;
+    const float sc = row < n ? (float)scales[row] : 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const f16x8 a = vq_row(cb + m * (MOE_VQ8_NCODE * 16), lc[M * s + m]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] += (float)a[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = k0 + 8 * s + i;
+            if (row < n && k < kin) out[(int64_t)row * kin + k] = sc * v[i];
+        }
+    }
+}
+
 }  // namespace
 
 int launch_dequant(const LayerView& L, int fmt, int32_t ridx, int32_t proj, float* out,
@@ -74,6 +110,17 @@ int launch_dequant(const LayerView& L, int fmt, int32_t ridx, int32_t proj, floa
     if (fmt == MOE_FMT_NVFP4) {
         dim3 grid((unsigned)(n / 16), (unsigned)nv_tiles_k(kin));
         k_dequant_nv<<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, out);
+    } else if (fmt == MOE_FMT_VQ8) {
+        const int64_t nkb = vq_tiles_k(kin);
+        const int groups = down ? L.H / 16 : 2 * (L.I / 16);
+        const int64_t tb = (int64_t)kVq8TileBytesPerCode * L.vq8_m;
+        const _Float16* sc = reinterpret_cast<const _Float16*>(rec + (int64_t)groups * nkb * tb);
+        if (proj == MOE_PROJ_UP) sc += L.I;
+        dim3 grid((unsigned)(n / 16), (unsigned)nkb);
+        if (L.vq8_m == 1)
+            k_dequant_vq8<1><<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, L.cb8[proj], sc, out);
+        else
+            k_dequant_vq8<2><<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, L.cb8[proj], sc, out);
     } else {
         const int64_t nkb = vq_tiles_k(kin);
         const int groups = down ? L.H / 16 : 2 * (L.I / 16);

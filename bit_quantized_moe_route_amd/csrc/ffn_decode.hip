@@ -32,6 +32,7 @@ namespace {
 // Per-format tile traits ----------------------------------------------------
 struct NvFmt {
     static constexpr bool kVq = false;
+    static constexpr bool kVq8 = false;
     static constexpr int TK = kNvTileK;       // inputs per tile
     static constexpr int TB = kNvTileBytes;   // bytes per tile
     static constexpr int STEPS = 4;           // MFMA K-steps per tile
@@ -52,6 +53,7 @@ struct NvFmt {
 
 struct VqFmt {
     static constexpr bool kVq = true;
+    static constexpr bool kVq8 = false;
     static constexpr int TK = kVqTileK;
     static constexpr int TB = kVqTileBytes;
     static constexpr int STEPS = 8;
@@ -70,6 +72,23 @@ struct VqFmt {
             a[s] = vq_row(cb, c);
         }
     }
+};
+
+// Small-codebook VQ: M uint8 codes per 8-weight group into M 256-entry fp16
+// codebooks shared by the layer (rows summed).  The kernel's codebooks sit
+// in LDS (M x 4 KB per projection), so a lookup is an LDS read, not an L2
+// gather; each codebook's row is its own MFMA A fragment (the sum of the M
+// exact products is taken in the fp32 accumulator; adding the fp16 rows
+// first would round).  Per-row scales as for VQ.
+template <int M>
+struct Vq8Fmt {
+    static constexpr bool kVq = true;
+    static constexpr bool kVq8 = true;
+    static constexpr int CODES = M;
+    static constexpr int TK = kVq8TileK;
+    static constexpr int TB = kVq8TileBytesPerCode * M;
+    static constexpr int STEPS = 8;
+    static constexpr int KSPAN = 64;
 };
 
 template <class F>
@@ -117,6 +136,7 @@ struct DecodeArgs {
     const uint8_t* cb_up;
     const uint8_t* cb_down;
     int64_t cb_stride;
+    const uint8_t* cb8[3];   // VQ8 codebooks per projection, [M][256][8] fp16
     const int32_t* rec;
     const int32_t* offsets;
     const int32_t* perm_src;
@@ -263,6 +283,66 @@ __device__ __forceinline__ void stream_tiles_vq(const uint8_t* const tbase[NM],
     }
 }
 
+// VQ8 tiles: codes (8M bytes per lane per tile) stream from HBM with the
+// next tile's codes and activations in flight (as stream_tiles); lcb[m] is
+// the LDS copy of matrix m's codebooks ([M][256][8] fp16).
+template <int NTT, int NM, int M, bool BF>
+__device__ __forceinline__ void stream_tiles_vq8(const uint8_t* const tbase[NM],
+                                                 const _Float16* const lcb[NM],
+                                                 const uint16_t* const xrow[NTT], int ntt,
+                                                 int K, int kpart, int KS, int lane,
+                                                 f32x4 acc[NM][NTT]) {
+    using F = Vq8Fmt<M>;
+    constexpr int CW = 2 * M;   // code dwords per lane per tile
+    const int nkb = tiles_k<F>(K);
+    const int ksub = (lane >> 4) * F::KSPAN;
+    const int niter = kpart < nkb ? (nkb - kpart + KS - 1) / KS : 0;
+    uint32_t cw[2][NM][CW];
+    u32x4 br[2][NTT][F::STEPS];
+    auto issue = [&](int i, uint32_t (&c)[NM][CW], u32x4 (&b)[NTT][F::STEPS]) {
+        const int kb = kpart + i * KS;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const uint8_t* p = tbase[m] + (int64_t)kb * F::TB + lane * 8 * M;
+            if constexpr (M == 1) {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+                c[m][0] = v[0];
+                c[m][1] = v[1];
+            } else {
+                const u32x4 v = load_stream16(p);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) c[m][q] = v[q];
+            }
+        }
+        load_b<F, NTT>(xrow, ntt, kb * F::TK + ksub, K, b);
+    };
+    if (niter > 0) issue(0, cw[0], br[0]);
+    for (int it = 0; it < niter; it += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = it + u;
+            if (i >= niter) break;
+            if (i + 1 < niter) issue(i + 1, cw[u ^ 1], br[u ^ 1]);
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int s = 0; s < F::STEPS; ++s)
+#pragma unroll
+                    for (int j = 0; j < M; ++j) {
+                        const int byte = M * s + j;
+                        const uint32_t code = (cw[u][m][byte >> 2] >> (8 * (byte & 3))) & 0xffu;
+                        const f16x8 a = *reinterpret_cast<const f16x8*>(
+                            lcb[m] + (j * MOE_VQ8_NCODE + code) * 8);
+#pragma unroll
+                        for (int tt = 0; tt < NTT; ++tt)
+                            if (tt < ntt)
+                                acc[m][tt] = mfma16(a, act_f16<BF>(br[u][tt][s]), acc[m][tt]);
+                    }
+        }
+    }
+}
+
 #ifndef MOEQ_VQ_GATHER_AHEAD
 #define MOEQ_VQ_GATHER_AHEAD 1
 #endif
@@ -300,6 +380,20 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
     const int c0 = blockIdx.z * 16 * NTT;
     if (c0 >= ae.me) return;
     const int ntt = min(NTT, (ae.me - c0 + 15) / 16);
+    // VQ8: the codebooks of this kernel's projections into LDS (dynamic LDS:
+    // gate and up for PHASE 0, down for PHASE 1)
+    extern __shared__ _Float16 lds_cb[];
+    if constexpr (F::kVq8) {
+        constexpr int NP = PHASE == 0 ? 2 : 1;
+        constexpr int CHUNKS = F::CODES * MOE_VQ8_NCODE;   // 16-byte rows per projection
+        for (int i = threadIdx.x; i < NP * CHUNKS; i += 64 * WV) {
+            const int pj = i / CHUNKS;
+            const uint8_t* src = A.cb8[PHASE == 0 ? pj : 2] + (int64_t)(i % CHUNKS) * 16;
+            *reinterpret_cast<u32x4*>(lds_cb + (int64_t)i * 8) =
+                *reinterpret_cast<const u32x4*>(src);
+        }
+        __syncthreads();
+    }
     const int set = blockIdx.x * SETS + wave / KS;   // row set of this wave
     const int kpart = wave % KS;
     const int K = PHASE == 0 ? A.H : A.I;
@@ -337,7 +431,14 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) acc[m][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (nlive > 0) {
-        if constexpr (F::kVq && MOEQ_VQ_GATHER_AHEAD) {
+        if constexpr (F::kVq8) {
+            const _Float16* lcb[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                lcb[m] = lds_cb + (PHASE == 0 ? (m & 1) : 0) * (F::CODES * MOE_VQ8_NCODE * 8);
+            stream_tiles_vq8<NTT, NM, F::CODES, PHASE == 0>(tb, lcb, xrow, ntt, K, kpart, KS,
+                                                            lane, acc);
+        } else if constexpr (F::kVq && MOEQ_VQ_GATHER_AHEAD) {
             // row c0 of the expert exists: a safe row for lanes past its rows
             const uint16_t* xsafe =
                 PHASE == 0
@@ -422,17 +523,25 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
 }
 
 
+template <class F>
+constexpr size_t codebook_lds_bytes(int phase) {
+    if constexpr (F::kVq8)
+        return (size_t)(phase == 0 ? 2 : 1) * F::CODES * MOE_VQ8_NCODE * 16;
+    else
+        return 0;
+}
+
 template <class F, int NTT, int KS, int WV>
 int launch_ks(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
     constexpr int SETS = WV / KS;
     if (phase == 0) {
         const int nsets = (a.I / 16 + kRpwGateup - 1) / kRpwGateup;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
-        k_ffn<F, NTT, KS, kRpwGateup, 0, WV><<<grid, 64 * WV, 0, s>>>(a);
+        k_ffn<F, NTT, KS, kRpwGateup, 0, WV><<<grid, 64 * WV, codebook_lds_bytes<F>(0), s>>>(a);
     } else {
         const int nsets = (a.H / 16 + kRpwDown - 1) / kRpwDown;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
-        k_ffn<F, NTT, KS, kRpwDown, 1, WV><<<grid, 64 * WV, 0, s>>>(a);
+        k_ffn<F, NTT, KS, kRpwDown, 1, WV><<<grid, 64 * WV, codebook_lds_bytes<F>(1), s>>>(a);
     }
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
@@ -471,6 +580,7 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
     a.cb_up = L.cb[1];
     a.cb_down = L.cb[2];
     a.cb_stride = L.cb_stride;
+    for (int p = 0; p < 3; ++p) a.cb8[p] = L.cb8[p];
     a.rec = L.rec;
     a.offsets = offsets;
     a.perm_src = perm_src;
@@ -486,6 +596,10 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
     const int slots = (int)(tk < n_fmt ? tk : n_fmt);
     if (slots == 0) return MOE_OK;
     if (fmt == MOE_FMT_NVFP4) return launch_ntt<NvFmt>(a, T, slots, phase, s);
+    if (fmt == MOE_FMT_VQ8) {
+        if (L.vq8_m == 1) return launch_ntt<Vq8Fmt<1>>(a, T, slots, phase, s);
+        return launch_ntt<Vq8Fmt<2>>(a, T, slots, phase, s);
+    }
     return launch_ntt<VqFmt>(a, T, slots, phase, s);
 }
 

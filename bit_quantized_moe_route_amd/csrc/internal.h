@@ -23,16 +23,22 @@ int fail(int status, const std::string& msg);
 // VQ tile: 16 rows x 256 inputs = 1024 code bytes.
 //   lane L owns bytes [16L, 16L+16) = 8 uint16 codes: row (L & 15), groups
 //     covering inputs kb*256 + (L >> 4)*64 + 8s + [0, 8), s = 0..7.
+// VQ8 tile (m = 1 or 2 uint8 codes per group): 16 rows x 256 inputs =
+//   512 m code bytes; lane L owns bytes [8mL, 8mL + 8m): row (L & 15), the
+//   groups of inputs kb*256 + (L >> 4)*64 + 8s + [0, 8), s = 0..7, each group's
+//   m codes consecutive (code j of group s at byte m*s + j).
 // A record is a sequence of row groups of 16 rows, each a sequence of tiles
 // along the input dimension (padded with zero codes/scales).  Gate/up
 // records interleave row groups: group 2j = gate rows 16j.., 2j+1 = up rows.
-// VQ records end with the fp16 per-row scales (gate, up / down), padded to
-// 256 bytes.
+// VQ and VQ8 records end with the fp16 per-row scales (gate, up / down),
+// padded to 256 bytes.
 constexpr int kNvTileK = 128;
 constexpr int kNvTileBytes = 1152;
 constexpr int kNvScaleOff = 1024;
 constexpr int kVqTileK = 256;
 constexpr int kVqTileBytes = 1024;
+constexpr int kVq8TileK = 256;
+constexpr int kVq8TileBytesPerCode = 512;   // times m
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
@@ -45,17 +51,23 @@ inline int64_t nv_matrix_bytes(int32_t n, int32_t kin) {
 inline int64_t vq_codes_bytes(int32_t n, int32_t kin) {
     return (int64_t)(n / 16) * vq_tiles_k(kin) * kVqTileBytes;
 }
+inline int64_t vq8_codes_bytes(int32_t n, int32_t kin, int32_t m) {
+    return (int64_t)(n / 16) * vq_tiles_k(kin) * kVq8TileBytesPerCode * m;
+}
 
 // Launchers (device code lives in the .hip files) ----------------------------
+constexpr int kNumFmt = 4;      // format tags 1 .. 3
 struct LayerView {
     int32_t E, H, I;
+    int32_t vq8_m;
     const int32_t* rec;
-    const uint8_t* pool13[3];   // indexed by format tag (1, 2)
-    const uint8_t* pool2[3];
-    int64_t stride13[3];
-    int64_t stride2[3];
+    const uint8_t* pool13[kNumFmt];   // indexed by format tag
+    const uint8_t* pool2[kNumFmt];
+    int64_t stride13[kNumFmt];
+    int64_t stride2[kNumFmt];
     const uint8_t* cb[3];       // VQ codebooks gate, up, down
     int64_t cb_stride;
+    const uint8_t* cb8[3];      // VQ8 codebooks gate, up, down: [m][256][8] fp16
 };
 
 int launch_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,

@@ -100,6 +100,33 @@ static void vq_tiles(const uint16_t* codes, int32_t n, int32_t kin, int rg_step,
     }
 }
 
+static void vq8_tiles(const uint8_t* codes, int32_t n, int32_t kin, int32_t m, int rg_step,
+                      int rg_off, uint8_t* rec) {
+    const int64_t nkb = vq_tiles_k(kin);
+    const int ng = kin / 8;
+    const int64_t tb = (int64_t)kVq8TileBytesPerCode * m;
+    for (int g = 0; g < n / 16; ++g) {
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            uint8_t* tile = rec + ((int64_t)(g * rg_step + rg_off) * nkb + kb) * tb;
+            std::memset(tile, 0, (size_t)tb);
+            for (int L = 0; L < 64; ++L) {
+                const int row = 16 * g + (L & 15);
+                const int g0 = ((int)kb * kVq8TileK + (L >> 4) * 64) / 8;
+                uint8_t* dst = tile + (int64_t)L * 8 * m;
+                for (int s = 0; s < 8; ++s)
+                    if (g0 + s < ng)
+                        for (int j = 0; j < m; ++j)
+                            dst[m * s + j] = codes[((int64_t)row * ng + g0 + s) * m + j];
+            }
+        }
+    }
+}
+
+static int64_t vq8_rec_bytes(int which, int32_t H, int32_t I, int32_t m) {
+    if (which == 0) return round_up(vq8_codes_bytes(2 * I, H, m) + 2LL * I * 2, 256);
+    return round_up(vq8_codes_bytes(H, I, m) + 2LL * H, 256);
+}
+
 static int64_t vq_rec_bytes(int which, int32_t H, int32_t I) {
     if (which == 0) return round_up(vq_codes_bytes(2 * I, H) + 2LL * I * 2, 256);
     return round_up(vq_codes_bytes(H, I) + 2LL * H, 256);
@@ -164,6 +191,12 @@ size_t moe_record_bytes(int fmt, int which, int32_t H, int32_t I) {
     return 0;
 }
 
+size_t moe_record_bytes_vq8(int which, int32_t H, int32_t I, int32_t m) {
+    if (H <= 0 || I <= 0 || (which != 0 && which != 1) || m < 1 || m > MOE_VQ8_MAX_M) return 0;
+    if (H % 16 || I % 16) return 0;
+    return (size_t)vq8_rec_bytes(which, H, I, m);
+}
+
 int moe_pack_nvfp4_expert(const uint8_t* gc, const uint8_t* gs, const uint8_t* uc,
                           const uint8_t* us, const uint8_t* dc, const uint8_t* ds, int32_t H,
                           int32_t I, uint8_t* w13, uint8_t* w2) {
@@ -198,14 +231,35 @@ int moe_pack_vq_expert(const uint16_t* gc, const uint16_t* gs, const uint16_t* u
     return MOE_OK;
 }
 
+int moe_pack_vq8_expert(const uint8_t* gc, const uint16_t* gs, const uint8_t* uc,
+                        const uint16_t* us, const uint8_t* dc, const uint16_t* ds, int32_t H,
+                        int32_t I, int32_t m, uint8_t* w13, uint8_t* w2) {
+    if (!gc || !gs || !uc || !us || !dc || !ds || !w13 || !w2)
+        return fail(MOE_EINVAL, "moe_pack_vq8_expert: null pointer");
+    if (H <= 0 || I <= 0 || H % 16 || I % 16)
+        return fail(MOE_EUNSUPPORTED, "moe_pack_vq8_expert: H and I must be positive multiples of 16");
+    if (m < 1 || m > MOE_VQ8_MAX_M)
+        return fail(MOE_EUNSUPPORTED, "moe_pack_vq8_expert: m must be 1 or 2");
+    std::memset(w13, 0, (size_t)vq8_rec_bytes(0, H, I, m));
+    std::memset(w2, 0, (size_t)vq8_rec_bytes(1, H, I, m));
+    vq8_tiles(gc, I, H, m, 2, 0, w13);
+    vq8_tiles(uc, I, H, m, 2, 1, w13);
+    vq8_tiles(dc, H, I, m, 1, 0, w2);
+    const int64_t c13 = vq8_codes_bytes(2 * I, H, m);
+    std::memcpy(w13 + c13, gs, (size_t)I * 2);
+    std::memcpy(w13 + c13 + (size_t)I * 2, us, (size_t)I * 2);
+    std::memcpy(w2 + vq8_codes_bytes(H, I, m), ds, (size_t)H * 2);
+    return MOE_OK;
+}
+
 int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* n_nvfp4,
-                     int32_t* n_vq) {
+                     int32_t* n_vq, int32_t* n_vq8) {
     if (!fmt_host || !rec) return fail(MOE_EINVAL, "moe_record_table: null pointer");
     if (E < 1 || E > MOE_MAX_E) return fail(MOE_EINVAL, "moe_record_table: bad E");
-    int32_t cnt[3] = {0, 0, 0};
+    int32_t cnt[kNumFmt] = {0, 0, 0, 0};
     for (int e = 0; e < E; ++e) {
         const int f = fmt_host[e];
-        if (f != MOE_FMT_NVFP4 && f != MOE_FMT_VQ)
+        if (f != MOE_FMT_NVFP4 && f != MOE_FMT_VQ && f != MOE_FMT_VQ8)
             return fail(MOE_EUNSUPPORTED,
                         "moe_record_table: expert " + std::to_string(e) + " has unknown format tag " +
                             std::to_string(f));
@@ -213,6 +267,7 @@ int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* 
     }
     if (n_nvfp4) *n_nvfp4 = cnt[MOE_FMT_NVFP4];
     if (n_vq) *n_vq = cnt[MOE_FMT_VQ];
+    if (n_vq8) *n_vq8 = cnt[MOE_FMT_VQ8];
     return MOE_OK;
 }
 

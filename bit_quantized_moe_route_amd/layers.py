@@ -11,12 +11,13 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from . import (FMT_NVFP4, FMT_VQ, PROJ_DOWN, PROJ_GATE, PROJ_UP, QLayer, pack_nvfp4_expert,
-               pack_vq_expert, quantize_nvfp4)
+from . import (FMT_NVFP4, FMT_VQ, FMT_VQ8, PROJ_DOWN, PROJ_GATE, PROJ_UP, QLayer,
+               pack_nvfp4_expert, pack_vq8_expert, pack_vq_expert, quantize_nvfp4)
 
 
 def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=None,
-                codebook_stride=0, device="cuda", workers=8):
+                codebook_stride=0, vq8_codes=None, codebooks8=None, vq8_m=0, device="cuda",
+                workers=8):
     """Build a QLayer.
 
     nvfp4_weights(e, proj) -> fp32 [n, kin] source weights of an NVFP4 expert
@@ -25,10 +26,13 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         of a VQ expert.
     codebooks: three uint16 arrays (fp16 bits) [65536 * n_books, 8] for gate,
         up, down.
+    vq8_codes(e, proj) -> (codes uint8 [n, kin/8, vq8_m], scales fp16 bits [n])
+        of a small-codebook VQ expert; codebooks8: for gate, up, down a list of
+        vq8_m uint16 arrays [256, 8].
     """
     import torch
 
-    layer = QLayer(E, H, I, fmt_host, device=device)
+    layer = QLayer(E, H, I, fmt_host, device=device, vq8_m=vq8_m)
     host = {}
     for key, pool in layer.pools.items():
         if pool is not None:
@@ -43,6 +47,9 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         if fmt == FMT_NVFP4:
             parts = [quantize_nvfp4(nvfp4_weights(e, p)) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
             w13, w2 = pack_nvfp4_expert(parts[0], parts[1], parts[2], H, I)
+        elif fmt == FMT_VQ8:
+            parts = [vq8_codes(e, p) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
+            w13, w2 = pack_vq8_expert(parts[0], parts[1], parts[2], H, I, vq8_m)
         else:
             parts = [vq_codes(e, p) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
             w13, w2 = pack_vq_expert(parts[0], parts[1], parts[2], H, I)
@@ -55,5 +62,7 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         layer.pools[key].copy_(torch.from_numpy(arr))
     if layer.n_vq:
         layer.set_codebooks(codebooks, codebook_stride)
+    if layer.n_vq8:
+        layer.set_codebooks8(codebooks8)
     torch.cuda.synchronize(layer.device)
     return layer

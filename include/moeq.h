@@ -70,6 +70,10 @@ extern "C" {
 #define MOE_FMT_NVFP4 1       /* E2M1 codes + E4M3 scale per 16 inputs */
 #define MOE_FMT_VQ    2       /* 8-wide groups, uint16 codes, fp16 codebook,
                                  fp16 scale per output channel */
+#define MOE_FMT_VQ8   3       /* 8-wide groups, M = 1 or 2 uint8 codes into M
+                                 256-entry fp16 codebooks whose rows are
+                                 summed, fp16 scale per output channel
+                                 (M bits per weight) */
 
 #define MOE_PROJ_GATE 0
 #define MOE_PROJ_UP   1
@@ -79,6 +83,8 @@ extern "C" {
 #define MOE_MAX_E     1024    /* experts per layer */
 #define MOE_MAX_K     16      /* experts per token */
 #define MOE_VQ_NCODE  65536   /* codebook entries (uint16 codes) */
+#define MOE_VQ8_NCODE 256     /* entries of each small codebook (uint8 codes) */
+#define MOE_VQ8_MAX_M 2       /* small codebooks per group */
 
 /*
  * A packed expert layer.  Host struct; the pointers inside are [device]
@@ -90,7 +96,8 @@ extern "C" {
  * its format (so a single-format layer has index(e) = e).  Record sizes are
  * given by moe_record_bytes() and their bytes by the moe_pack_* calls.
  *
- *   fmt_host   [host]   uint8 [E]: MOE_FMT_NVFP4 or MOE_FMT_VQ per expert.
+ *   fmt_host   [host]   uint8 [E]: MOE_FMT_NVFP4, MOE_FMT_VQ or MOE_FMT_VQ8
+ *                       per expert.
  *   rec_dev    [device] int32 [E]: (fmt << 24) | index(e), as written by
  *                       moe_record_table() from the same fmt_host.
  *   nvfp4_w13 / nvfp4_w2   pool bases of NVFP4 gate/up and down records;
@@ -101,12 +108,17 @@ extern "C" {
  *                   down).  vq_codebook_stride = bytes between the codebooks
  *                   of consecutive VQ records (index(e)); 0 means one
  *                   codebook per projection shared by every expert.
+ *   vq8_m           codes per group of the MOE_FMT_VQ8 experts (1 or 2);
+ *                   any value if the layer has none.
+ *   vq8_w13 / vq8_w2   pool bases of the MOE_FMT_VQ8 records;
+ *   vq8_codebook[p] fp16 [vq8_m][256][8]: the small codebooks of projection
+ *                   p, shared by every MOE_FMT_VQ8 expert of the layer.
  *
  * Unused pools (no expert of that format) may be NULL.
  */
 typedef struct moe_qlayer {
     int32_t E, H, I;
-    int32_t reserved;
+    int32_t vq8_m;
     const uint8_t* fmt_host;
     const int32_t* rec_dev;
     const void* nvfp4_w13;  int64_t nvfp4_w13_stride;
@@ -115,6 +127,9 @@ typedef struct moe_qlayer {
     const void* vq_w2;      int64_t vq_w2_stride;
     const void* vq_codebook[3];
     int64_t vq_codebook_stride;
+    const void* vq8_w13;    int64_t vq8_w13_stride;
+    const void* vq8_w2;     int64_t vq8_w2_stride;
+    const void* vq8_codebook[3];
 } moe_qlayer;
 
 /* ------------------------------------------------------------- messages */
@@ -280,6 +295,9 @@ int moe_quantize_nvfp4(const float* w, int32_t n, int32_t kin,
  */
 size_t moe_record_bytes(int fmt, int which, int32_t H, int32_t I);
 
+/* Bytes of one MOE_FMT_VQ8 record with m codes per group (0 on bad sizes). */
+size_t moe_record_bytes_vq8(int which, int32_t H, int32_t I, int32_t m);
+
 /*
  * moe_pack_nvfp4_expert -- [host] lay the canonical NVFP4 bytes of one
  * expert out as its two device records (gate/up and down).
@@ -303,19 +321,34 @@ int moe_pack_vq_expert(const uint16_t* gate_codes, const uint16_t* gate_scales,
                        int32_t H, int32_t I, uint8_t* w13_rec, uint8_t* w2_rec);
 
 /*
+ * moe_pack_vq8_expert -- [host] lay one MOE_FMT_VQ8 expert out as its two
+ * records.  codes uint8 [n, kin/8, m] (code j of group g indexes codebook
+ * j; group g covers inputs 8g..8g+7), scales fp16 bits [n], for gate/up
+ * (n = I, kin = H) and down (n = H, kin = I); m = 1 or 2.
+ *   ("GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw", What it is: 1/2/3-bit
+ *   modules with per-group codes and shared codebooks.)
+ */
+int moe_pack_vq8_expert(const uint8_t* gate_codes, const uint16_t* gate_scales,
+                        const uint8_t* up_codes, const uint16_t* up_scales,
+                        const uint8_t* down_codes, const uint16_t* down_scales,
+                        int32_t H, int32_t I, int32_t m, uint8_t* w13_rec, uint8_t* w2_rec);
+
+/*
  * moe_record_table -- [host] fill rec [E] = (fmt << 24) | index(e) from the
- * tier map, and report how many experts each format has (either count
- * pointer may be NULL).  MOE_EUNSUPPORTED on an unknown tag.
+ * tier map, and report how many experts each format has (any count pointer
+ * may be NULL).  MOE_EUNSUPPORTED on an unknown tag.
  */
 int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec,
-                     int32_t* n_nvfp4, int32_t* n_vq);
+                     int32_t* n_nvfp4, int32_t* n_vq, int32_t* n_vq8);
 
 /* ------------------------------------------------------------ test hook */
 
 /*
  * moe_dequant_q -- decode projection `proj` (MOE_PROJ_*) of expert `expert`
  * to fp32 out [n, kin] ([device]; gate/up: [I, H], down: [H, I]) with the
- * same device decode routines the FFN kernels use.  Every value is exact.
+ * same device decode routines the FFN kernels use.  NVFP4 and VQ values are
+ * exact; a MOE_FMT_VQ8 value with m = 2 is fp32(fp32(C_0 + C_1) * S) (two
+ * roundings; the FFN kernels multiply each codebook row exactly instead).
  */
 int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj,
                   float* out, void* stream);

@@ -38,11 +38,15 @@ def build_small_layer(wl, device="cuda"):
 
     fmt_host = synth.tier_map(wl)
     cbs = [synth.vq_codebook(wl, p) for p in range(3)] if (fmt_host == synth.FMT_VQ).any() else None
+    cbs8 = ([synth.vq8_codebooks(wl, p) for p in range(3)]
+            if (fmt_host == synth.FMT_VQ8).any() else None)
     return build_layer(
         wl.E, wl.H, wl.I, fmt_host,
         nvfp4_weights=lambda e, p: synth.nvfp4_source_weights(wl, e, p),
         vq_codes=lambda e, p: (synth.vq_codes(wl, e, p), synth.vq_scales(wl, e, p)),
-        codebooks=cbs, device=device, workers=16)
+        codebooks=cbs,
+        vq8_codes=lambda e, p: (synth.vq8_codes(wl, e, p), synth.vq_scales(wl, e, p)),
+        codebooks8=cbs8, vq8_m=wl.vq8_m, device=device, workers=16)
 
 
 def oracle_perm(ids, E):

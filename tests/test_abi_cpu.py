@@ -169,16 +169,59 @@ def test_vq_record_layout():
     assert np.array_equal(w2[c2:c2 + 2 * H].view(np.uint16), parts[2][1])
 
 
+@pytest.mark.parametrize("m", [1, 2])
+def test_vq8_record_layout(m):
+    H, I = 272, 48
+    rs = np.random.default_rng(m)
+    parts = []
+    for n, kin in [(I, H), (I, H), (H, I)]:
+        parts.append((rs.integers(0, 256, (n, kin // 8, m), dtype=np.uint8),
+                      rs.integers(0, 65536, n, dtype=np.uint16)))
+    w13, w2 = moeq.pack_vq8_expert(parts[0], parts[1], parts[2], H, I, m)
+    assert w13.size == moeq.record_bytes(moeq.FMT_VQ8, 0, H, I, m) and w13.size % 256 == 0
+    tb = 512 * m
+    for (codes, scales), rec, rg_step, rg_off, nrg in [(parts[0], w13, 2, 0, 2 * I // 16),
+                                                       (parts[1], w13, 2, 1, 2 * I // 16),
+                                                       (parts[2], w2, 1, 0, H // 16)]:
+        n, ng, _ = codes.shape
+        kin = ng * 8
+        nkb = (kin + 255) // 256
+        for row in range(n):
+            g, r = divmod(row, 16)
+            for grp in range(ng):
+                kb, kk = divmod(8 * grp, 256)
+                L = r + 16 * (kk // 64)
+                s = (kk % 64) // 8
+                off = ((g * rg_step + rg_off) * nkb + kb) * tb + 8 * m * L + m * s
+                assert np.array_equal(rec[off:off + m], codes[row, grp])
+    c13 = (2 * I // 16) * ((H + 255) // 256) * tb
+    assert np.array_equal(w13[c13:c13 + 2 * I].view(np.uint16), parts[0][1])
+    assert np.array_equal(w13[c13 + 2 * I:c13 + 4 * I].view(np.uint16), parts[1][1])
+    c2 = (H // 16) * ((I + 255) // 256) * tb
+    assert np.array_equal(w2[c2:c2 + 2 * H].view(np.uint16), parts[2][1])
+    with pytest.raises(moeq.MoeError):
+        moeq.pack_vq8_expert(parts[0], parts[1], parts[2], H, I, 3)
+    assert moeq.record_bytes(moeq.FMT_VQ8, 0, H, I, 3) == 0
+
+
 def test_record_table():
     tm = synth.tier_map(synth.MIXED)
-    rec, nn, nv = moeq.record_table(tm)
-    assert nn == 108 and nv == 148
+    rec, counts = moeq.record_table(tm)
+    assert counts == {1: 108, 2: 148, 3: 0}
     for fmt in (1, 2):
         sel = np.nonzero(tm == fmt)[0]
         assert np.all(rec[sel] >> 24 == fmt)
         assert np.array_equal(rec[sel] & 0xFFFFFF, np.arange(sel.size))
+    tm3 = synth.tier_map(synth.small_workload("m3", E=40, k=4, H=64, I=32, T=4, fmt="mixed3",
+                                              n_nvfp4=10, vq8_m=2))
+    rec, counts = moeq.record_table(tm3)
+    assert counts[1] == 10 and counts[3] == 15 and counts[2] == 15
+    for fmt in (1, 2, 3):
+        sel = np.nonzero(tm3 == fmt)[0]
+        assert np.all(rec[sel] >> 24 == fmt)
+        assert np.array_equal(rec[sel] & 0xFFFFFF, np.arange(sel.size))
     bad = tm.copy()
-    bad[7] = 3
+    bad[7] = 4
     with pytest.raises(moeq.MoeError) as ei:
         moeq.record_table(bad)
     assert ei.value.status == moeq.MOE_EUNSUPPORTED

@@ -1,7 +1,8 @@
 """GPU parity at the full GLM-5-class sizes (256 experts, top-8, H 6144,
 I 2048) in the launch configurations the benchmark times: decode T = 1, 8,
-32 (NVFP4), prefill T = 4096 with Zipf(1.1) routing (NVFP4), 2-bit VQ T = 8
-and the mixed NVFP4/VQ layer at T = 8 and 32.
+32 (NVFP4), prefill T = 4096 with Zipf(1.1) routing (NVFP4), 2-bit VQ T = 8,
+the small-codebook VQ layers (1 and 2 bits per weight) at T = 8 and the mixed
+NVFP4/VQ layer at T = 8 and 32.
 
 Routing and permutation are compared in full (bit-exact).  Expert outputs
 are compared row by row against the oracle on sampled experts (the oracle
@@ -189,6 +190,27 @@ def test_vq_full_sampled():
         W = expert_weights(wl, e)
         for p in range(3):
             assert np.array_equal(to_np(moeq.dequant_q(lay, e, p)).astype(np.float64), W[p]), (e, p)
+
+
+@pytest.mark.parametrize("name", ["vq1", "vq2x8"])
+def test_vq8_full_sampled(name):
+    """Small-codebook VQ (1 and 2 bits per weight) at the full layer size, T = 8."""
+    wl = synth.WORKLOADS[name]
+    say("vq8 full T=8", name)
+    lay = layer(name)
+    x_bits, lg, r = run_forward(wl, lay, 8)
+    ids, w, offsets, perm_src = check_routing(wl, lg, r)
+    experts = pick(offsets, n=4, seed=3)
+    check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
+    check_combine_property(wl, r)
+    for e in experts[:2]:
+        W = expert_weights(wl, e)
+        for p in range(3):
+            got = to_np(moeq.dequant_q(lay, e, p)).astype(np.float64)
+            if wl.vq8_m == 1:
+                assert np.array_equal(got, W[p]), (e, p)
+            else:
+                assert np.all(np.abs(got - W[p]) <= 2.0 ** -22 * np.abs(W[p])), (e, p)
 
 
 @pytest.mark.timeout(900)

@@ -34,6 +34,18 @@ SMALL = {
     "mixed_prefill": synth.small_workload("mixed_prefill", E=12, k=3, H=256, I=128, T=260,
                                           fmt="mixed", logits="hot", cfg=110, n_nvfp4=5,
                                           n_hot=3, hot_share=0.6),
+    # small-codebook VQ: one and two 8-bit codes per group, ragged shapes, and a
+    # layer of all three formats (token counts past 64 and 128 included)
+    "vq8_1": synth.small_workload("vq8_1", E=12, k=3, H=512, I=144, T=21, fmt="vq8", cfg=120,
+                                  vq8_m=1),
+    "vq8_2_ragged": synth.small_workload("vq8_2_ragged", E=8, k=2, H=208, I=48, T=9, fmt="vq8",
+                                         cfg=121, vq8_m=2),
+    "mixed3": synth.small_workload("mixed3", E=24, k=6, H=384, I=96, T=70, fmt="mixed3",
+                                   logits="hot", cfg=122, n_nvfp4=8, n_hot=4, hot_share=0.6,
+                                   vq8_m=2),
+    "mixed3_prefill": synth.small_workload("mixed3_prefill", E=12, k=3, H=256, I=128, T=260,
+                                           fmt="mixed3", logits="hot", cfg=123, n_nvfp4=4,
+                                           n_hot=3, hot_share=0.6, vq8_m=1),
 }
 
 _layers = {}
@@ -61,6 +73,24 @@ def test_dequant_bit_exact(name):
         for p in range(3):
             got = to_np(moeq.dequant_q(layer, e, p)).astype(np.float64)
             assert np.array_equal(got, W[p]), (name, e, p)
+
+
+@pytest.mark.parametrize("name", ["vq8_1", "vq8_2_ragged", "mixed3"])
+def test_dequant_vq8(name):
+    """Small-codebook VQ decode: exact with one code per group; with two, the
+    hook's fp32(fp32(C_0 + C_1) * S) is within 2 roundings of the exact value."""
+    wl = SMALL[name]
+    say("dequant vq8", name)
+    layer = layer_for(name)
+    tm = synth.tier_map(wl)
+    for e in np.flatnonzero(tm == synth.FMT_VQ8):
+        W = expert_weights(wl, int(e))
+        for p in range(3):
+            got = to_np(moeq.dequant_q(layer, int(e), p)).astype(np.float64)
+            if wl.vq8_m == 1:
+                assert np.array_equal(got, W[p]), (name, e, p)
+            else:
+                assert np.all(np.abs(got - W[p]) <= 2.0 ** -22 * np.abs(W[p])), (name, e, p)
 
 
 # ------------------------------------------------------------------ route
