@@ -16,7 +16,7 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   roofline       the NVFP4 gate/up kernel: packed gate/up bytes of the
                  experts it touches per launch / its mean launch time
                  (HIP events on the launch stream), against 8 TB/s HBM
-  cpu_baseline   the fp64 oracle on a bounded sample (one token), one core
+  cpu_baseline   the fp64 oracle on a bounded sample (three tokens), one core
   extra          the same path on the other workloads (decode T = 1 and 8,
                  prefill T = 4096 with Zipf(1.1) routing, 2-bit VQ T = 8,
                  small-codebook VQ at 1 and 2 bits per weight T = 8,
@@ -222,12 +222,15 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16):
 
 # --------------------------------------------------------------------------
 
+CPU_SAMPLE_TOKENS = 3
+
+
 def cpu_baseline(wl, T):
-    """The fp64 oracle on one token of the batch, on one core (BLAS threads
-    pinned to 1).  The oracle's own encoder prepares the canonical NVFP4
-    bytes of the token's experts in a process pool outside the timed region;
-    the timed region is oracle.forward: route, decode of the 8 experts from
-    canonical bytes, FFN and combine."""
+    """The fp64 oracle on the first CPU_SAMPLE_TOKENS tokens of the batch, on
+    one core (BLAS threads pinned to 1).  The oracle's own encoder prepares
+    the canonical NVFP4 bytes of those tokens' experts in a process pool
+    outside the timed region; the timed region is oracle.forward: route,
+    decode of the touched experts from canonical bytes, FFN and combine."""
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
 
@@ -237,8 +240,9 @@ def cpu_baseline(wl, T):
     import oracle
     import synth
 
-    lg = synth.logits(wl, T, rep=0)[:1]
-    x = synth.activations(wl, T, rep=0)[:1]
+    nt = CPU_SAMPLE_TOKENS
+    lg = synth.logits(wl, T, rep=0)[:nt]
+    x = synth.activations(wl, T, rep=0)[:nt]
     ids, _ = oracle.route_topk(lg, wl.k)
     experts = sorted(int(e) for e in np.unique(ids))
     jobs = [(e, p) for e in experts for p in range(3)]
@@ -265,8 +269,8 @@ def cpu_baseline(wl, T):
                     break
     except OSError:
         pass
-    return {"value": 1.0 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"1 token of the decode T={T} batch (its {len(experts)} experts): "
+    return {"value": nt / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{nt} tokens of the decode T={T} batch ({len(experts)} experts): "
                        f"oracle.forward (fp64 route, NVFP4 decode from canonical bytes, FFN, "
                        f"combine) on one core of '{cpu_model}' ({ncpu} host cores visible); "
                        f"{dt:.1f} s"),
@@ -385,7 +389,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the oracle on a one-token sample ...")
+        log(f"timing the oracle on a {CPU_SAMPLE_TOKENS}-token sample ...")
         cpu = cpu_baseline(wl, args.T)
         cpu.pop("seconds", None)
         log("  ", json.dumps(cpu))
@@ -410,7 +414,7 @@ def main():
                    "experts_touched_mean": head["experts_touched_mean"],
                    "parallelism": "1 GPU"},
         "packed_GBps": head["packed_GBps"],
-        "roofline": {"bound": "hbm", "kernel": "k_gateup<NvFmt> (+ x to fp16)",
+        "roofline": {"bound": "hbm", "kernel": "k_ffn<NvFmt, 1, 1, 2, 0, 4> (NVFP4 gate/up + SwiGLU)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": head["gateup_bytes_per_launch"],
