@@ -20,7 +20,8 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   extra          the same path on the other workloads (decode T = 1 and 8,
                  prefill T = 4096 with Zipf(1.1) routing, 2-bit VQ T = 8,
                  small-codebook VQ at 1 and 2 bits per weight T = 8,
-                 mixed NVFP4/VQ T = 8 and 32)
+                 mixed NVFP4/VQ T = 8 and 32, and the same mixed layer with
+                 its hot experts switched to the NVFP4 tier at run time)
 """
 
 import argparse
@@ -293,7 +294,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--T", type=int, default=32, help="decode batch of the headline")
-    ap.add_argument("--extra", default="decode1,decode8,prefill,vq,vq1,vq2x8,mixed8,mixed32",
+    ap.add_argument("--extra",
+                    default="decode1,decode8,prefill,vq,vq1,vq2x8,mixed8,mixed32,mixedhot8,mixedhot32",
                     help="comma list of other workloads to measure ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy", action="store_true",
@@ -370,6 +372,22 @@ def main():
                     device=dev, workers=16)
                 extra[name] = measure(lay8, w8, 8, 30, 5, dev)
                 del lay8
+            elif name.startswith("mixedhot"):
+                # the mixed layer packed in both formats (resident), its tier map
+                # switched at run time so that the hot experts take the 4-bit tier
+                wm = synth.MIXED
+                T = int(name[len("mixedhot"):])
+                if "mixed_resident" not in layers:
+                    layers.pop("mixed", None)
+                    log("building the mixed layer with both formats resident ...")
+                    layers["mixed_resident"] = build_layer(
+                        wm.E, wm.H, wm.I, synth.tier_map(wm),
+                        nvfp4_weights=lambda e, p: synth.nvfp4_source_weights(wm, e, p),
+                        vq_codes=lambda e, p: (synth.vq_codes(wm, e, p), synth.vq_scales(wm, e, p)),
+                        codebooks=[synth.vq_codebook(wm, p) for p in range(3)], device=dev,
+                        workers=16, resident_formats={moeq.FMT_NVFP4, moeq.FMT_VQ})
+                    layers["mixed_resident"].set_tiers(synth.tier_map_hot(wm))
+                extra[name] = measure(layers["mixed_resident"], wm, T, 30, 5, dev)
             elif name.startswith("mixed"):
                 wm = synth.MIXED
                 T = int(name[len("mixed"):])

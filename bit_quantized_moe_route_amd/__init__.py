@@ -32,6 +32,7 @@ MOE_EHIP = -4
 FMT_NVFP4 = 1
 FMT_VQ = 2
 FMT_VQ8 = 3
+REC_COMPACT, REC_RESIDENT = 0, 1
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 VQ_NCODE = 65536
 VQ8_NCODE = 256
@@ -58,6 +59,7 @@ class _QLayerC(ctypes.Structure):
         ("vq8_w13", ctypes.c_void_p), ("vq8_w13_stride", ctypes.c_int64),
         ("vq8_w2", ctypes.c_void_p), ("vq8_w2_stride", ctypes.c_int64),
         ("vq8_codebook", ctypes.c_void_p * 3),
+        ("record_mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -89,6 +91,7 @@ _PROTOS = {
     "moe_pack_nvfp4_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
     "moe_pack_vq_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
     "moe_record_table": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P]),
+    "moe_record_table_resident": (ctypes.c_int, [_P, _I32, _P]),
     "moe_dequant_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _I32, _I32, _P, _P]),
 }
 
@@ -194,6 +197,15 @@ def record_table(fmt_host):
     return rec, {FMT_NVFP4: nn.value, FMT_VQ: nv.value, FMT_VQ8: n8.value}
 
 
+def record_table_resident(fmt_host):
+    """rec [E] = fmt << 24 | e (every used pool holds every expert at slot e)."""
+    fmt_host = np.ascontiguousarray(fmt_host, dtype=np.uint8)
+    rec = np.empty(fmt_host.shape[0], np.int32)
+    _check(lib().moe_record_table_resident(_np_ptr(fmt_host), fmt_host.shape[0], _np_ptr(rec)),
+           "moe_record_table_resident")
+    return rec
+
+
 # --------------------------------------------------------------------------
 # device calls (torch tensors for memory and the current stream)
 # --------------------------------------------------------------------------
@@ -227,13 +239,26 @@ class QLayer:
     descriptor that points at them.  Build it with `QLayer.build(...)`.
     """
 
-    def __init__(self, E, H, I, fmt_host, device="cuda", vq8_m=0):
+    def __init__(self, E, H, I, fmt_host, device="cuda", vq8_m=0, resident_formats=None):
+        """resident_formats: None (compact pools: each expert stored in its own
+        format only) or a set of format tags whose pools hold every expert at
+        slot e, so that set_tiers() can move experts between those formats
+        between calls."""
         torch = _torch()
         self.E, self.H, self.I = int(E), int(H), int(I)
         self.fmt_host = np.ascontiguousarray(fmt_host, dtype=np.uint8)
-        rec, counts = record_table(self.fmt_host)
+        self.resident = frozenset(resident_formats) if resident_formats else None
+        _, counts = record_table(self.fmt_host)
+        if self.resident is not None:
+            if not set(np.unique(self.fmt_host).tolist()) <= self.resident:
+                raise ValueError("every expert's format must be one of the resident formats")
+            rec = record_table_resident(self.fmt_host)
+            sizes = {f: (self.E if f in self.resident else 0) for f in (FMT_NVFP4, FMT_VQ, FMT_VQ8)}
+        else:
+            rec = record_table(self.fmt_host)[0]
+            sizes = dict(counts)
         self.n_nvfp4, self.n_vq, self.n_vq8 = counts[FMT_NVFP4], counts[FMT_VQ], counts[FMT_VQ8]
-        if self.n_vq8 and vq8_m not in (1, 2):
+        if sizes[FMT_VQ8] and vq8_m not in (1, 2):
             raise ValueError("a layer with small-codebook VQ experts needs vq8_m = 1 or 2")
         self.vq8_m = int(vq8_m)
         self.rec_host = rec
@@ -241,7 +266,8 @@ class QLayer:
         self.rec_dev = torch.from_numpy(rec).to(self.device)
         self.stride = {}
         self.pools = {}
-        for fmt, n in ((FMT_NVFP4, self.n_nvfp4), (FMT_VQ, self.n_vq), (FMT_VQ8, self.n_vq8)):
+        for fmt in (FMT_NVFP4, FMT_VQ, FMT_VQ8):
+            n = sizes[fmt]
             for which in (0, 1):
                 b = record_bytes(fmt, which, H, I, self.vq8_m) if n else 0
                 s = (b + 255) // 256 * 256
@@ -256,11 +282,31 @@ class QLayer:
     def record_index(self, e):
         return int(self.rec_host[e] & 0xFFFFFF)
 
-    def set_record(self, e, w13, w2, stream=None):
-        """Copy one expert's two host records (numpy uint8) into its pool slots."""
+    def set_tiers(self, fmt_host):
+        """Resident layers: move experts between the resident formats.  The
+        host tier map is updated in place and the device record table by a
+        copy on the current stream, so calls issued afterwards on that stream
+        use the new tiers."""
         torch = _torch()
-        fmt = int(self.fmt_host[e])
-        idx = self.record_index(e)
+        if self.resident is None:
+            raise ValueError("set_tiers needs a layer built with resident_formats")
+        new = np.ascontiguousarray(fmt_host, dtype=np.uint8)
+        if new.shape != self.fmt_host.shape or not set(np.unique(new).tolist()) <= self.resident:
+            raise ValueError("tier map must give every expert one of the resident formats")
+        rec = record_table_resident(new)
+        self.fmt_host[:] = new          # in place: the C descriptor points at this array
+        self.rec_host = rec
+        self.rec_dev.copy_(torch.from_numpy(rec))
+        _, counts = record_table(self.fmt_host)
+        self.n_nvfp4, self.n_vq, self.n_vq8 = counts[FMT_NVFP4], counts[FMT_VQ], counts[FMT_VQ8]
+
+    def set_record(self, e, w13, w2, fmt=None, stream=None):
+        """Copy one expert's two host records (numpy uint8) into its pool slots
+        (fmt: the format of the records; a resident layer holds one per
+        resident format)."""
+        torch = _torch()
+        fmt = int(self.fmt_host[e]) if fmt is None else int(fmt)
+        idx = e if self.resident is not None else self.record_index(e)
         for which, rec in ((0, w13), (1, w2)):
             s = self.stride[(fmt, which)]
             dst = self.pools[(fmt, which)][idx * s: idx * s + rec.shape[0]]
@@ -298,6 +344,7 @@ class QLayer:
             d.fmt_host = self.fmt_host.ctypes.data
             d.rec_dev = self.rec_dev.data_ptr()
             d.vq8_m = self.vq8_m
+            d.record_mode = REC_RESIDENT if self.resident is not None else REC_COMPACT
             for fmt, n13, n2 in ((FMT_NVFP4, "nvfp4_w13", "nvfp4_w2"), (FMT_VQ, "vq_w13", "vq_w2"),
                                  (FMT_VQ8, "vq8_w13", "vq8_w2")):
                 p13, p2 = self.pools[(fmt, 0)], self.pools[(fmt, 1)]

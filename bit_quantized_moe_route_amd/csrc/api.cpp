@@ -44,6 +44,8 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     if (L->E < 1 || L->E > MOE_MAX_E) return fail(MOE_EINVAL, f + ": bad E");
     if (L->H <= 0 || L->I <= 0) return fail(MOE_EINVAL, f + ": bad H or I");
     if (!L->fmt_host || !L->rec_dev) return fail(MOE_EINVAL, f + ": fmt_host / rec_dev is NULL");
+    if (L->record_mode != MOE_REC_COMPACT && L->record_mode != MOE_REC_RESIDENT)
+        return fail(MOE_EINVAL, f + ": unknown record_mode");
     for (int t = 0; t < kNumFmt; ++t) out.count[t] = 0;
     for (int e = 0; e < L->E; ++e) {
         const int t = L->fmt_host[e];
@@ -306,7 +308,10 @@ int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj, float* 
     // the record index of this expert within its format's pool (host-side)
     const int fmt = layer->fmt_host[expert];
     int32_t ridx = 0;
-    for (int e = 0; e < expert; ++e) ridx += layer->fmt_host[e] == fmt;
+    if (layer->record_mode == MOE_REC_RESIDENT)
+        ridx = expert;
+    else
+        for (int e = 0; e < expert; ++e) ridx += layer->fmt_host[e] == fmt;
     return launch_dequant(li.view, fmt, ridx, proj, out, stream);
 }
 

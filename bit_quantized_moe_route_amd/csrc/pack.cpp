@@ -271,4 +271,17 @@ int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* 
     return MOE_OK;
 }
 
+int moe_record_table_resident(const uint8_t* fmt_host, int32_t E, int32_t* rec) {
+    if (!fmt_host || !rec) return fail(MOE_EINVAL, "moe_record_table_resident: null pointer");
+    if (E < 1 || E > MOE_MAX_E) return fail(MOE_EINVAL, "moe_record_table_resident: bad E");
+    for (int e = 0; e < E; ++e) {
+        const int f = fmt_host[e];
+        if (f != MOE_FMT_NVFP4 && f != MOE_FMT_VQ && f != MOE_FMT_VQ8)
+            return fail(MOE_EUNSUPPORTED, "moe_record_table_resident: expert " + std::to_string(e) +
+                                              " has unknown format tag " + std::to_string(f));
+        rec[e] = (f << 24) | e;
+    }
+    return MOE_OK;
+}
+
 }  // extern "C"

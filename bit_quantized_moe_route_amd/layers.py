@@ -17,7 +17,7 @@ from . import (FMT_NVFP4, FMT_VQ, FMT_VQ8, PROJ_DOWN, PROJ_GATE, PROJ_UP, QLayer
 
 def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=None,
                 codebook_stride=0, vq8_codes=None, codebooks8=None, vq8_m=0, device="cuda",
-                workers=8):
+                workers=8, resident_formats=None):
     """Build a QLayer.
 
     nvfp4_weights(e, proj) -> fp32 [n, kin] source weights of an NVFP4 expert
@@ -29,18 +29,27 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
     vq8_codes(e, proj) -> (codes uint8 [n, kin/8, vq8_m], scales fp16 bits [n])
         of a small-codebook VQ expert; codebooks8: for gate, up, down a list of
         vq8_m uint16 arrays [256, 8].
+    resident_formats: None, or the formats every expert is packed in (slot e of
+        each of those pools), for a layer whose tiers change at run time
+        (QLayer.set_tiers).
     """
     import torch
 
-    layer = QLayer(E, H, I, fmt_host, device=device, vq8_m=vq8_m)
+    layer = QLayer(E, H, I, fmt_host, device=device, vq8_m=vq8_m,
+                   resident_formats=resident_formats)
     host = {}
     for key, pool in layer.pools.items():
         if pool is not None:
             host[key] = np.zeros(pool.numel(), np.uint8)
 
     def one(e):
-        fmt = int(layer.fmt_host[e])
-        idx = layer.record_index(e)
+        if layer.resident is not None:
+            for fmt in sorted(layer.resident):
+                pack_one(e, fmt, e)
+        else:
+            pack_one(e, int(layer.fmt_host[e]), layer.record_index(e))
+
+    def pack_one(e, fmt, idx):
         s13, s2 = layer.stride[(fmt, 0)], layer.stride[(fmt, 1)]
         dst13 = host[(fmt, 0)][idx * s13: idx * s13 + s13]
         dst2 = host[(fmt, 1)][idx * s2: idx * s2 + s2]
@@ -60,9 +69,9 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         list(ex.map(one, range(E)))
     for key, arr in host.items():
         layer.pools[key].copy_(torch.from_numpy(arr))
-    if layer.n_vq:
+    if layer.pools[(FMT_VQ, 0)] is not None:
         layer.set_codebooks(codebooks, codebook_stride)
-    if layer.n_vq8:
+    if layer.pools[(FMT_VQ8, 0)] is not None:
         layer.set_codebooks8(codebooks8)
     torch.cuda.synchronize(layer.device)
     return layer

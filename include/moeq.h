@@ -113,6 +113,19 @@ extern "C" {
  *   vq8_w13 / vq8_w2   pool bases of the MOE_FMT_VQ8 records;
  *   vq8_codebook[p] fp16 [vq8_m][256][8]: the small codebooks of projection
  *                   p, shared by every MOE_FMT_VQ8 expert of the layer.
+ *   record_mode     MOE_REC_COMPACT: index(e) = e's rank among the experts of
+ *                   its format (rec from moe_record_table);
+ *                   MOE_REC_RESIDENT: every pool that is used holds a record for
+ *                   every expert at slot e, index(e) = e (rec from
+ *                   moe_record_table_resident).  A resident layer switches an
+ *                   expert's tier between calls by rewriting fmt_host[e] and
+ *                   rec_dev[e] only ("GLM-5.3 Vision NestQuant 1.75-4 bit",
+ *                   introduction and Serving: experts move between bit tiers
+ *                   at serve time; "GLM-5.3-EXL3-TR3-3.42bpw", What is
+ *                   quantized: the per-expert tier map).  Launch sizes follow
+ *                   the number of experts per format, so a HIP graph captured
+ *                   before a switch stays valid only if those counts are
+ *                   unchanged (a swap of tiers).
  *
  * Unused pools (no expert of that format) may be NULL.
  */
@@ -130,7 +143,12 @@ typedef struct moe_qlayer {
     const void* vq8_w13;    int64_t vq8_w13_stride;
     const void* vq8_w2;     int64_t vq8_w2_stride;
     const void* vq8_codebook[3];
+    int32_t record_mode;
+    int32_t reserved;
 } moe_qlayer;
+
+#define MOE_REC_COMPACT   0
+#define MOE_REC_RESIDENT  1
 
 /* ------------------------------------------------------------- messages */
 
@@ -340,6 +358,13 @@ int moe_pack_vq8_expert(const uint8_t* gate_codes, const uint16_t* gate_scales,
  */
 int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec,
                      int32_t* n_nvfp4, int32_t* n_vq, int32_t* n_vq8);
+
+/*
+ * moe_record_table_resident -- [host] rec [E] = (fmt << 24) | e for a layer
+ * in MOE_REC_RESIDENT mode (every used pool holds every expert at slot e).
+ * MOE_EUNSUPPORTED on an unknown tag.
+ */
+int moe_record_table_resident(const uint8_t* fmt_host, int32_t E, int32_t* rec);
 
 /* ------------------------------------------------------------ test hook */
 

@@ -264,6 +264,19 @@ def vq8_codebooks(wl, proj):
     return out
 
 
+def tier_map_hot(wl):
+    """The mixed layer's tier map with its hot experts at the high tier: the
+    n_hot hot experts and a seeded choice of n_nvfp4 - n_hot others are NVFP4,
+    the rest VQ (the 4-bit tier goes to the experts that take most tokens)."""
+    hot = hot_experts(wl)
+    rest = np.setdiff1d(np.arange(wl.E), hot)
+    others = rng(wl.cfg, KIND_TIER, 1).choice(rest, size=wl.n_nvfp4 - len(hot), replace=False)
+    tm = np.full(wl.E, FMT_VQ, dtype=np.uint8)
+    tm[hot] = FMT_NVFP4
+    tm[others] = FMT_NVFP4
+    return tm
+
+
 def tier_map(wl):
     """Per-expert format tag (FMT_NVFP4 / FMT_VQ / FMT_VQ8), uint8 [E]."""
     if wl.fmt == "nvfp4":

@@ -31,22 +31,24 @@ def assert_rows_close(gpu, ref, what, tol=ROW_TOL):
     return worst
 
 
-def build_small_layer(wl, device="cuda"):
+def build_small_layer(wl, device="cuda", resident_formats=None):
     """A QLayer for workload wl built by the library's packers from the
-    seeded inputs."""
+    seeded inputs (resident_formats: pack every expert in each of these
+    formats, for tier switches)."""
     from bit_quantized_moe_route_amd.layers import build_layer
 
     fmt_host = synth.tier_map(wl)
-    cbs = [synth.vq_codebook(wl, p) for p in range(3)] if (fmt_host == synth.FMT_VQ).any() else None
-    cbs8 = ([synth.vq8_codebooks(wl, p) for p in range(3)]
-            if (fmt_host == synth.FMT_VQ8).any() else None)
+    used = set(np.unique(fmt_host).tolist()) | set(resident_formats or ())
+    cbs = [synth.vq_codebook(wl, p) for p in range(3)] if synth.FMT_VQ in used else None
+    cbs8 = [synth.vq8_codebooks(wl, p) for p in range(3)] if synth.FMT_VQ8 in used else None
     return build_layer(
         wl.E, wl.H, wl.I, fmt_host,
         nvfp4_weights=lambda e, p: synth.nvfp4_source_weights(wl, e, p),
         vq_codes=lambda e, p: (synth.vq_codes(wl, e, p), synth.vq_scales(wl, e, p)),
         codebooks=cbs,
         vq8_codes=lambda e, p: (synth.vq8_codes(wl, e, p), synth.vq_scales(wl, e, p)),
-        codebooks8=cbs8, vq8_m=wl.vq8_m, device=device, workers=16)
+        codebooks8=cbs8, vq8_m=wl.vq8_m, device=device, workers=16,
+        resident_formats=resident_formats)
 
 
 def oracle_perm(ids, E):

@@ -204,6 +204,15 @@ def test_vq8_record_layout(m):
     assert moeq.record_bytes(moeq.FMT_VQ8, 0, H, I, 3) == 0
 
 
+def test_record_table_resident():
+    tm = np.array([1, 2, 2, 3, 1, 3], np.uint8)
+    rec = moeq.record_table_resident(tm)
+    assert np.array_equal(rec >> 24, tm) and np.array_equal(rec & 0xFFFFFF, np.arange(6))
+    with pytest.raises(moeq.MoeError) as ei:
+        moeq.record_table_resident(np.array([1, 5], np.uint8))
+    assert ei.value.status == moeq.MOE_EUNSUPPORTED
+
+
 def test_record_table():
     tm = synth.tier_map(synth.MIXED)
     rec, counts = moeq.record_table(tm)

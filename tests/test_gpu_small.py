@@ -252,3 +252,51 @@ def test_t_zero_is_noop():
     r = moeq.forward(layer, x, lg, 2)
     assert r["out"].shape == (0, 256)
     assert torch.all(r["counts"] == 0) and torch.all(r["offsets"] == 0)
+
+
+# ------------------------------------------------------------------ tier switch
+
+def _forward_check(wl, layer, tiers, rep, label):
+    T = wl.T[0]
+    x_bits = synth.activations(wl, T, rep=rep)
+    lg = synth.logits(wl, T, rep=rep)
+    r = moeq.forward(layer, torch.from_numpy(x_bits.view(np.int16)).to(DEV),
+                     torch.from_numpy(lg).to(DEV), wl.k)
+    Wc = {}
+
+    def weights(e):
+        if e not in Wc:
+            Wc[e] = expert_weights(wl, e, int(tiers[e]))
+        return Wc[e]
+    out, ids, w, y = oracle.forward(x_bits, lg, wl.k, weights)
+    assert np.array_equal(to_np(r["topk_ids"]), ids)
+    counts, offsets, perm_src, inv_perm = oracle.permute(ids, wl.E)
+    y_ref = y.reshape(T * wl.k, wl.H)[perm_src]
+    assert_rows_close(to_np(r["y_perm"]), y_ref, label + " y_perm")
+    assert_rows_close(to_np(r["out"]), out, label + " out")
+
+
+def test_tier_switch_between_calls():
+    """A resident layer (every expert packed in NVFP4, VQ and VQ8) moves experts
+    between tiers between calls; each call matches the oracle under the tier
+    map in force, including the hot experts moved to the 4-bit tier and
+    all-one-format maps."""
+    wl = synth.small_workload("tiers", E=24, k=6, H=256, I=96, T=40, fmt="mixed", logits="hot",
+                              cfg=130, n_nvfp4=9, n_hot=4, hot_share=0.6, vq8_m=2)
+    say("tier switch")
+    fmts = {synth.FMT_NVFP4, synth.FMT_VQ, synth.FMT_VQ8}
+    layer = build_small_layer(wl, DEV, resident_formats=fmts)
+    maps = [synth.tier_map(wl), synth.tier_map_hot(wl),
+            np.full(wl.E, synth.FMT_VQ8, np.uint8), np.full(wl.E, synth.FMT_NVFP4, np.uint8),
+            np.random.default_rng(5).choice([1, 2, 3], size=wl.E).astype(np.uint8)]
+    for i, tm in enumerate(maps):
+        if i:
+            layer.set_tiers(tm)
+        _forward_check(wl, layer, tm, i, f"tiers {i}")
+        e = int(np.flatnonzero(tm == tm[0])[0])
+        W = expert_weights(wl, e, int(tm[e]))
+        got = to_np(moeq.dequant_q(layer, e, 0)).astype(np.float64)
+        if tm[e] == synth.FMT_VQ8:
+            assert np.all(np.abs(got - W[0]) <= 2.0 ** -22 * np.abs(W[0]))
+        else:
+            assert np.array_equal(got, W[0])
