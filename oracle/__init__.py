@@ -24,7 +24,8 @@ the docstring of the function that makes it.
 
 Parity status per function (what pins each one is in tests/test_oracle_*.py):
   e2m1_decode, e4m3_decode, e4m3_encode, nvfp4_quantize, nvfp4_dequant,
-  vq_dequant, vq8_dequant, route_topk, permute, expert_ffn, combine, forward
+  vq_dequant, vq8_dequant, route_topk, permute, expert_ffn, combine,
+  combine_shared, forward
   -- all pinned.  vq8_dequant's arithmetic is pinned; its code shape (M
   8-bit codes per 8-weight group into M 256-entry codebooks whose rows are
   summed) is a reading the pages do not fix: parity unpinned for the shape.
@@ -48,5 +49,6 @@ from .moe import (  # noqa: F401
     permute,
     expert_ffn,
     combine,
+    combine_shared,
     forward,
 )

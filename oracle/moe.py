@@ -112,13 +112,25 @@ def combine(y, w):
     return out
 
 
-def forward(x_bits, logits, k, expert_weights):
+def combine_shared(y, w, y_shared):
+    """The routed combine followed by the shared expert's output:
+    out[t] = (sum_{j=0}^{k-1} w[t, j] * y[t, j]) + y_shared[t], the routed sum
+    in ascending j first.  (GLM-5.3-EXL3-TR3-3.42bpw, What is quantized: the
+    layers carry BF16 shared experts next to the routed ones; every token
+    passes through the shared expert with weight 1.  Adding it after the
+    routed sum is a reading.)"""
+    return combine(y, w) + np.asarray(y_shared, dtype=np.float64)
+
+
+def forward(x_bits, logits, k, expert_weights, shared_weights=None):
     """The whole routed-expert forward for T tokens.
 
     x_bits uint16 bf16 bits [T, H]; logits fp32 [T, E]; expert_weights(e) ->
     (W_gate [I, H], W_up [I, H], W_down [H, I]) float64, called once per
-    touched expert.  Returns (out [T, H], ids [T, k], w [T, k],
-    y [T, k, H]) where y[t, j] = FFN_{ids[t, j]}(x_t).
+    touched expert; shared_weights: None or the shared expert's (W_gate, W_up,
+    W_down) float64.  Returns (out [T, H], ids [T, k], w [T, k],
+    y [T, k, H]) where y[t, j] = FFN_{ids[t, j]}(x_t); with a shared expert,
+    out adds FFN_shared(x_t) after the routed sum.
     """
     x = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16))
     ids, w = route_topk(logits, k)
@@ -129,4 +141,6 @@ def forward(x_bits, logits, k, expert_weights):
         wg, wu, wd = expert_weights(int(e))
         tt, jj = np.nonzero(ids == e)
         y[tt, jj] = expert_ffn(x[tt], wg, wu, wd)
-    return combine(y, w), ids, w, y
+    if shared_weights is None:
+        return combine(y, w), ids, w, y
+    return combine_shared(y, w, expert_ffn(x, *shared_weights)), ids, w, y

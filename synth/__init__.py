@@ -42,12 +42,14 @@ KIND_HOT = 7
 KIND_ZIPF_RANK = 8
 KIND_VQ8_CODES = 9
 KIND_VQ8_CODEBOOK = 10
+KIND_SHARED = 11
 
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 
 FMT_NVFP4 = 1
 FMT_VQ = 2
 FMT_VQ8 = 3
+FMT_BF16 = 4
 
 
 def rng(cfg, kind, expert=0, proj=0, rep=0):
@@ -241,6 +243,14 @@ def vq_codebook(wl, proj, ncode=65536):
     c = rng(wl.vq_cfg, KIND_VQ_CODEBOOK, 0, proj).standard_normal(
         (ncode, 8), dtype=np.float32) * np.float32(0.02)
     return f32_to_f16_bits(c)
+
+
+def shared_weights_bf16(wl, proj):
+    """The layer's BF16 shared expert: fp32 N(0, 0.02) rounded to bf16 (nearest
+    even), as uint16 bits (W_gate, W_up: [I, H]; W_down: [H, I])."""
+    n, kin = proj_shape(wl, proj)
+    z = rng(wl.cfg, KIND_SHARED, 0, proj).standard_normal((n, kin), dtype=np.float32)
+    return f32_to_bf16_bits(z * np.float32(0.02))
 
 
 def vq8_codes(wl, expert, proj):

@@ -260,3 +260,41 @@ def test_synth_is_deterministic():
     assert x.dtype == np.uint16 and x.shape == (4, 256)
     tm = synth.tier_map(synth.MIXED)
     assert (tm == synth.FMT_NVFP4).sum() == 108 and (tm == synth.FMT_VQ).sum() == 148
+
+
+# ------------------------------------------------------------ shared expert
+
+def test_shared_expert_alone_when_routed_outputs_vanish():
+    # routed experts with all-zero weights: the forward is the shared FFN
+    rs = np.random.default_rng(21)
+    T, E, k, H, I = 5, 6, 2, 32, 16
+    x = synth.f32_to_bf16_bits(rs.standard_normal((T, H)).astype(np.float32))
+    lg = rs.standard_normal((T, E)).astype(np.float32)
+    zero = (np.zeros((I, H)), np.zeros((I, H)), np.zeros((H, I)))
+    sh = (rs.standard_normal((I, H)) * 0.1, rs.standard_normal((I, H)) * 0.1,
+          rs.standard_normal((H, I)) * 0.1)
+    out, ids, w, y = oracle.forward(x, lg, k, lambda e: zero, shared_weights=sh)
+    assert np.all(y == 0)
+    assert np.array_equal(out, oracle.expert_ffn(x, *sh))
+
+
+def test_shared_expert_dense_form():
+    # out = sum_e [e routed] w_te FFN_e(x_t) + FFN_s(x_t), computed densely
+    rs = np.random.default_rng(22)
+    T, E, k, H, I = 7, 5, 3, 24, 8
+    x = synth.f32_to_bf16_bits(rs.standard_normal((T, H)).astype(np.float32))
+    lg = rs.standard_normal((T, E)).astype(np.float32)
+    Ws = {e: (rs.standard_normal((I, H)) * 0.2, rs.standard_normal((I, H)) * 0.2,
+              rs.standard_normal((H, I)) * 0.2) for e in range(E)}
+    sh = (rs.standard_normal((I, H)) * 0.2, rs.standard_normal((I, H)) * 0.2,
+          rs.standard_normal((H, I)) * 0.2)
+    out, ids, w, y = oracle.forward(x, lg, k, lambda e: Ws[e], shared_weights=sh)
+    dense = oracle.expert_ffn(x, *sh)
+    for e in range(E):
+        m = (ids == e)
+        wt = (w * m).sum(axis=1)
+        dense = dense + wt[:, None] * oracle.expert_ffn(x, *Ws[e])
+    assert np.allclose(out, dense, rtol=1e-12, atol=1e-12)
+    # and without the shared expert the routed part alone
+    out0, *_ = oracle.forward(x, lg, k, lambda e: Ws[e])
+    assert np.allclose(out - out0, oracle.expert_ffn(x, *sh), rtol=1e-12, atol=1e-12)
