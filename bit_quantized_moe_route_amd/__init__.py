@@ -1,5 +1,5 @@
 """Python binding of libmoeq (the routed-expert MoE forward over NVFP4 / VQ
-expert weights for MI355X).
+expert weights, with an optional BF16 shared expert, for MI355X).
 
 Argument marshalling only: every step of the forward runs in the library's
 HIP kernels.  PyTorch is used for device memory and the current stream.  If
@@ -10,9 +10,12 @@ Calls (same names as the C ABI in include/moeq.h):
     permute(topk_ids, E)                        -> counts, offsets, perm_src, inv_perm
     expert_ffn_q(layer, x, perm_src, offsets, k) -> y_perm
     combine(y_perm, inv_perm, topk_w)           -> out
-    forward(layer, x, logits, k)                -> all of the above
+    shared_ffn(shared, x)                       -> y_shared
+    combine_shared(y_perm, inv_perm, topk_w, y_shared) -> out
+    forward(layer, x, logits, k, shared=None)   -> all of the above
 Host packers: quantize_nvfp4, pack_nvfp4_expert, pack_vq_expert,
-record_bytes, record_table.  Test hook: dequant_q.
+pack_vq8_expert, pack_bf16_expert, record_bytes, record_table.  Test hook:
+dequant_q.
 """
 
 import ctypes
@@ -32,6 +35,8 @@ MOE_EHIP = -4
 FMT_NVFP4 = 1
 FMT_VQ = 2
 FMT_VQ8 = 3
+FMT_BF16 = 4
+FORMATS = (FMT_NVFP4, FMT_VQ, FMT_VQ8, FMT_BF16)
 REC_COMPACT, REC_RESIDENT = 0, 1
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 VQ_NCODE = 65536
@@ -59,6 +64,8 @@ class _QLayerC(ctypes.Structure):
         ("vq8_w13", ctypes.c_void_p), ("vq8_w13_stride", ctypes.c_int64),
         ("vq8_w2", ctypes.c_void_p), ("vq8_w2_stride", ctypes.c_int64),
         ("vq8_codebook", ctypes.c_void_p * 3),
+        ("bf16_w13", ctypes.c_void_p), ("bf16_w13_stride", ctypes.c_int64),
+        ("bf16_w2", ctypes.c_void_p), ("bf16_w2_stride", ctypes.c_int64),
         ("record_mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
@@ -84,13 +91,17 @@ _PROTOS = {
                                            _P, _SZ, _P]),
     "moe_expert_down_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _I64, _I32, _P, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_shared_ffn_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64]),
+    "moe_shared_ffn": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _I64, _P, _P, _SZ, _P]),
+    "moe_combine_shared": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _P, _P]),
     "moe_quantize_nvfp4": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "moe_record_bytes": (_SZ, [ctypes.c_int, ctypes.c_int, _I32, _I32]),
     "moe_record_bytes_vq8": (_SZ, [ctypes.c_int, _I32, _I32, _I32]),
     "moe_pack_vq8_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _I32, _P, _P]),
     "moe_pack_nvfp4_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
     "moe_pack_vq_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
-    "moe_record_table": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P]),
+    "moe_pack_bf16_expert": (ctypes.c_int, [_P] * 3 + [_I32, _I32, _P, _P]),
+    "moe_record_table": (ctypes.c_int, [_P, _I32, _P, _P]),
     "moe_record_table_resident": (ctypes.c_int, [_P, _I32, _P]),
     "moe_dequant_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _I32, _I32, _P, _P]),
 }
@@ -186,15 +197,32 @@ def pack_vq8_expert(gate, up, down, H, I, m, w13=None, w2=None):
     return w13, w2
 
 
+def pack_bf16_expert(gate, up, down, H, I, w13=None, w2=None):
+    """gate, up [I, H], down [H, I]: bf16 bits (uint16 / int16) or torch
+    bfloat16 CPU tensors -> (w13 record, w2 record)."""
+    if w13 is None:
+        w13 = np.empty(record_bytes(FMT_BF16, 0, H, I), np.uint8)
+    if w2 is None:
+        w2 = np.empty(record_bytes(FMT_BF16, 1, H, I), np.uint8)
+    arrs = []
+    for a in (gate, up, down):
+        if hasattr(a, "view") and not isinstance(a, np.ndarray):   # torch bfloat16
+            a = a.contiguous().view(_torch().int16).numpy()
+        arrs.append(np.ascontiguousarray(a).view(np.uint16))
+    _check(lib().moe_pack_bf16_expert(*[_np_ptr(a) for a in arrs], H, I, _np_ptr(w13),
+                                      _np_ptr(w2)), "moe_pack_bf16_expert")
+    return w13, w2
+
+
 def record_table(fmt_host):
-    """(rec [E] int32, experts per format {FMT_NVFP4: n, FMT_VQ: n, FMT_VQ8: n})."""
+    """(rec [E] int32, experts per format {tag: n for every tag in FORMATS})."""
     fmt_host = np.ascontiguousarray(fmt_host, dtype=np.uint8)
     E = fmt_host.shape[0]
     rec = np.empty(E, np.int32)
-    nn, nv, n8 = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().moe_record_table(_np_ptr(fmt_host), E, _np_ptr(rec), ctypes.byref(nn),
-                                  ctypes.byref(nv), ctypes.byref(n8)), "moe_record_table")
-    return rec, {FMT_NVFP4: nn.value, FMT_VQ: nv.value, FMT_VQ8: n8.value}
+    n = np.zeros(max(FORMATS) + 1, np.int32)
+    _check(lib().moe_record_table(_np_ptr(fmt_host), E, _np_ptr(rec), _np_ptr(n)),
+           "moe_record_table")
+    return rec, {f: int(n[f]) for f in FORMATS}
 
 
 def record_table_resident(fmt_host):
@@ -253,11 +281,11 @@ class QLayer:
             if not set(np.unique(self.fmt_host).tolist()) <= self.resident:
                 raise ValueError("every expert's format must be one of the resident formats")
             rec = record_table_resident(self.fmt_host)
-            sizes = {f: (self.E if f in self.resident else 0) for f in (FMT_NVFP4, FMT_VQ, FMT_VQ8)}
+            sizes = {f: (self.E if f in self.resident else 0) for f in FORMATS}
         else:
             rec = record_table(self.fmt_host)[0]
             sizes = dict(counts)
-        self.n_nvfp4, self.n_vq, self.n_vq8 = counts[FMT_NVFP4], counts[FMT_VQ], counts[FMT_VQ8]
+        self.counts = counts
         if sizes[FMT_VQ8] and vq8_m not in (1, 2):
             raise ValueError("a layer with small-codebook VQ experts needs vq8_m = 1 or 2")
         self.vq8_m = int(vq8_m)
@@ -266,7 +294,7 @@ class QLayer:
         self.rec_dev = torch.from_numpy(rec).to(self.device)
         self.stride = {}
         self.pools = {}
-        for fmt in (FMT_NVFP4, FMT_VQ, FMT_VQ8):
+        for fmt in FORMATS:
             n = sizes[fmt]
             for which in (0, 1):
                 b = record_bytes(fmt, which, H, I, self.vq8_m) if n else 0
@@ -297,8 +325,7 @@ class QLayer:
         self.fmt_host[:] = new          # in place: the C descriptor points at this array
         self.rec_host = rec
         self.rec_dev.copy_(torch.from_numpy(rec))
-        _, counts = record_table(self.fmt_host)
-        self.n_nvfp4, self.n_vq, self.n_vq8 = counts[FMT_NVFP4], counts[FMT_VQ], counts[FMT_VQ8]
+        self.counts = record_table(self.fmt_host)[1]
 
     def set_record(self, e, w13, w2, fmt=None, stream=None):
         """Copy one expert's two host records (numpy uint8) into its pool slots
@@ -346,7 +373,8 @@ class QLayer:
             d.vq8_m = self.vq8_m
             d.record_mode = REC_RESIDENT if self.resident is not None else REC_COMPACT
             for fmt, n13, n2 in ((FMT_NVFP4, "nvfp4_w13", "nvfp4_w2"), (FMT_VQ, "vq_w13", "vq_w2"),
-                                 (FMT_VQ8, "vq8_w13", "vq8_w2")):
+                                 (FMT_VQ8, "vq8_w13", "vq8_w2"),
+                                 (FMT_BF16, "bf16_w13", "bf16_w2")):
                 p13, p2 = self.pools[(fmt, 0)], self.pools[(fmt, 1)]
                 setattr(d, n13, p13.data_ptr() if p13 is not None else None)
                 setattr(d, n2, p2.data_ptr() if p2 is not None else None)
@@ -371,6 +399,8 @@ class QLayer:
         for e in set(int(x) for x in experts):
             if self.fmt_host[e] == FMT_NVFP4:
                 tot += 3 * (self.H * self.I // 2 + self.H * self.I // 16)
+            elif self.fmt_host[e] == FMT_BF16:
+                tot += 3 * self.H * self.I * 2
             elif self.fmt_host[e] == FMT_VQ8:
                 vq8 = True
                 tot += 3 * (self.H * self.I // 8) * self.vq8_m + (2 * self.I + self.H) * 2
@@ -522,6 +552,42 @@ def combine(y_perm, inv_perm, topk_w, out=None):
     return out
 
 
+def shared_workspace(shared, T):
+    torch = _torch()
+    n = lib().moe_shared_ffn_workspace_bytes(ctypes.byref(shared.c()), T)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=shared.device)
+
+
+def shared_ffn(shared, x, y=None, ws=None):
+    """The shared expert (a one-expert QLayer) on every token: fp32 [T, H]."""
+    torch = _torch()
+    _need_cuda(x)
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, shared.H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = shared_workspace(shared, T)
+    _check(lib().moe_shared_ffn(ctypes.byref(shared.c()), _dptr(x), T, _dptr(y), _dptr(ws),
+                                ws.numel(), _stream(x.device)), "moe_shared_ffn")
+    return y
+
+
+def combine_shared(y_perm, inv_perm, topk_w, y_shared, out=None):
+    """combine, then + y_shared (the shared expert's output) per token."""
+    torch = _torch()
+    _need_cuda(y_perm, inv_perm, topk_w, y_shared)
+    T, k = topk_w.shape
+    H = y_perm.shape[1]
+    if tuple(y_shared.shape) != (T, H) or y_shared.dtype != torch.float32:
+        raise ValueError("y_shared must be fp32 [T, H]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=y_perm.device)
+    _check(lib().moe_combine_shared(_dptr(y_perm), _dptr(inv_perm), _dptr(topk_w),
+                                    _dptr(y_shared), T, k, H, _dptr(out), _stream(y_perm.device)),
+           "moe_combine_shared")
+    return out
+
+
 def dequant_q(layer, expert, proj):
     torch = _torch()
     n, kin = (layer.H, layer.I) if proj == PROJ_DOWN else (layer.I, layer.H)
@@ -531,11 +597,17 @@ def dequant_q(layer, expert, proj):
     return out
 
 
-def forward(layer, x, logits, k):
-    """route -> permute -> expert FFN -> combine.  Returns a dict of every
+def forward(layer, x, logits, k, shared=None):
+    """route -> permute -> expert FFN -> combine (+ the shared expert's output
+    when `shared`, a one-expert QLayer, is given).  Returns a dict of every
     intermediate (device tensors)."""
     ids, w, counts, offsets, perm_src, inv_perm = route_permute(logits, k, layer.E)
     y_perm = expert_ffn_q(layer, x, perm_src, offsets, k)
-    out = combine(y_perm, inv_perm, w)
-    return dict(topk_ids=ids, topk_w=w, counts=counts, offsets=offsets, perm_src=perm_src,
-                inv_perm=inv_perm, y_perm=y_perm, out=out)
+    r = dict(topk_ids=ids, topk_w=w, counts=counts, offsets=offsets, perm_src=perm_src,
+             inv_perm=inv_perm, y_perm=y_perm)
+    if shared is None:
+        r["out"] = combine(y_perm, inv_perm, w)
+    else:
+        r["y_shared"] = shared_ffn(shared, x)
+        r["out"] = combine_shared(y_perm, inv_perm, w, r["y_shared"])
+    return r

@@ -49,7 +49,7 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     for (int t = 0; t < kNumFmt; ++t) out.count[t] = 0;
     for (int e = 0; e < L->E; ++e) {
         const int t = L->fmt_host[e];
-        if (t != MOE_FMT_NVFP4 && t != MOE_FMT_VQ && t != MOE_FMT_VQ8)
+        if (t < MOE_FMT_NVFP4 || t > MOE_FMT_MAX)
             return fail(MOE_EUNSUPPORTED, f + ": expert " + std::to_string(e) +
                                               " has format tag " + std::to_string(t) +
                                               ", which this library does not decode");
@@ -76,6 +76,10 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     v.pool2[MOE_FMT_VQ8] = static_cast<const uint8_t*>(L->vq8_w2);
     v.stride13[MOE_FMT_VQ8] = L->vq8_w13_stride;
     v.stride2[MOE_FMT_VQ8] = L->vq8_w2_stride;
+    v.pool13[MOE_FMT_BF16] = static_cast<const uint8_t*>(L->bf16_w13);
+    v.pool2[MOE_FMT_BF16] = static_cast<const uint8_t*>(L->bf16_w2);
+    v.stride13[MOE_FMT_BF16] = L->bf16_w13_stride;
+    v.stride2[MOE_FMT_BF16] = L->bf16_w2_stride;
     for (int p = 0; p < 3; ++p) v.cb[p] = static_cast<const uint8_t*>(L->vq_codebook[p]);
     v.cb_stride = L->vq_codebook_stride;
     for (int p = 0; p < 3; ++p) v.cb8[p] = static_cast<const uint8_t*>(L->vq8_codebook[p]);
@@ -84,7 +88,10 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
         return fail(MOE_EUNSUPPORTED, f + ": vq8_m must be 1 or 2");
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!out.count[fmt]) continue;
-        const char* name = fmt == MOE_FMT_NVFP4 ? "NVFP4" : fmt == MOE_FMT_VQ ? "VQ" : "VQ8";
+        const char* name = fmt == MOE_FMT_NVFP4 ? "NVFP4"
+                           : fmt == MOE_FMT_VQ  ? "VQ"
+                           : fmt == MOE_FMT_VQ8 ? "VQ8"
+                                                : "BF16";
         if (!v.pool13[fmt] || !v.pool2[fmt])
             return fail(MOE_EINVAL, f + ": " + name + " experts present but their pool is NULL");
         const int64_t b13 = fmt == MOE_FMT_VQ8
@@ -113,6 +120,50 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
 
 size_t ffn_ws(const moe_qlayer* L, int64_t T, int32_t k) {
     return align_up((size_t)T * L->H * 2) + align_up((size_t)T * k * L->I * 2);
+}
+
+// Gate/up + SwiGLU of every format present.  perm_src == offsets == NULL is
+// the identity map of a one-expert layer (k = 1).  x16 [T, H] is workspace
+// for the fp16 copy of x that the grouped-GEMM kernels stage through LDS.
+int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_src,
+               const int32_t* offsets, int64_t T, int32_t k, uint16_t* h_f16, uint16_t* x16,
+               void* stream) {
+    const bool prefill = T >= kPrefillMinTokens;
+    bool need_x16 = false;
+    for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt)
+        need_x16 |= prefill && li.count[fmt] && prefill_fmt(fmt);
+    if (need_x16) {
+        const int st = launch_x_to_f16(x_bf16, T * li.view.H, x16, stream);
+        if (st) return st;
+    }
+    for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
+        if (!li.count[fmt]) continue;
+        const int st =
+            prefill && prefill_fmt(fmt)
+                ? launch_ffn_prefill(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T, k,
+                                     h_f16, nullptr, 0, stream)
+                : launch_ffn_decode(li.view, fmt, li.count[fmt], x_bf16, perm_src, offsets, T, k,
+                                    h_f16, nullptr, 0, stream);
+        if (st) return st;
+    }
+    return MOE_OK;
+}
+
+// Down projection of every format present (offsets == NULL: identity map).
+int run_down(const LayerInfo& li, const uint16_t* h_f16, const int32_t* offsets, int64_t T,
+             int32_t k, float* y_perm, void* stream) {
+    const bool prefill = T >= kPrefillMinTokens;
+    for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
+        if (!li.count[fmt]) continue;
+        uint16_t* h = const_cast<uint16_t*>(h_f16);
+        const int st = prefill && prefill_fmt(fmt)
+                           ? launch_ffn_prefill(li.view, fmt, li.count[fmt], nullptr, nullptr,
+                                                offsets, T, k, h, y_perm, 1, stream)
+                           : launch_ffn_decode(li.view, fmt, li.count[fmt], nullptr, nullptr,
+                                               offsets, T, k, h, y_perm, 1, stream);
+        if (st) return st;
+    }
+    return MOE_OK;
 }
 
 }  // namespace
@@ -218,23 +269,8 @@ int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16, const i
         return fail(MOE_EINVAL, "moe_expert_gateup_q: workspace must be 256-byte aligned");
     // the grouped-GEMM kernels stage fp16 tokens through LDS: convert x once;
     // the decode kernels convert each fragment they read
-    uint16_t* x16 = static_cast<uint16_t*>(ws);
-    const bool prefill = li.count[MOE_FMT_NVFP4] && T >= kPrefillMinTokens;
-    if (prefill) {
-        st = launch_x_to_f16(x_bf16, T * layer->H, x16, stream);
-        if (st) return st;
-    }
-    for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
-        if (!li.count[fmt]) continue;
-        if (fmt == MOE_FMT_NVFP4 && prefill)
-            st = launch_ffn_prefill(li.view, li.count[fmt], x16, perm_src, offsets, T, k, h_f16,
-                                    nullptr, 0, stream);
-        else
-            st = launch_ffn_decode(li.view, fmt, li.count[fmt], x_bf16, perm_src, offsets, T, k,
-                                   h_f16, nullptr, 0, stream);
-        if (st) return st;
-    }
-    return MOE_OK;
+    return run_gateup(li, x_bf16, perm_src, offsets, T, k, h_f16, static_cast<uint16_t*>(ws),
+                      stream);
 }
 
 int moe_expert_down_q(const moe_qlayer* layer, const uint16_t* h_f16, const int32_t* offsets,
@@ -247,17 +283,7 @@ int moe_expert_down_q(const moe_qlayer* layer, const uint16_t* h_f16, const int3
     if (st) return st;
     if (T == 0) return MOE_OK;
     if (!h_f16 || !offsets || !y_perm) return fail(MOE_EINVAL, "moe_expert_down_q: null pointer");
-    for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
-        if (!li.count[fmt]) continue;
-        if (fmt == MOE_FMT_NVFP4 && T >= kPrefillMinTokens)
-            st = launch_ffn_prefill(li.view, li.count[fmt], nullptr, nullptr, offsets, T, k,
-                                    const_cast<uint16_t*>(h_f16), y_perm, 1, stream);
-        else
-            st = launch_ffn_decode(li.view, fmt, li.count[fmt], nullptr, nullptr, offsets, T, k,
-                                   const_cast<uint16_t*>(h_f16), y_perm, 1, stream);
-        if (st) return st;
-    }
-    return MOE_OK;
+    return run_down(li, h_f16, offsets, T, k, y_perm, stream);
 }
 
 int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16, const int32_t* perm_src,
@@ -286,6 +312,36 @@ int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16, const int3
     return moe_expert_down_q(layer, h16, offsets, T, k, y_perm, stream);
 }
 
+size_t moe_shared_ffn_workspace_bytes(const moe_qlayer* shared, int64_t T) {
+    if (!shared || T < 0 || shared->H <= 0 || shared->I <= 0) return 0;
+    return ffn_ws(shared, T, 1);
+}
+
+int moe_shared_ffn(const moe_qlayer* shared, const uint16_t* x_bf16, int64_t T,
+                   float* y_shared, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    LayerInfo li;
+    int st = check_layer("moe_shared_ffn", shared, li);
+    if (st) return st;
+    if (shared->E != 1) return fail(MOE_EINVAL, "moe_shared_ffn: the shared layer must have E == 1");
+    st = check_route_sizes("moe_shared_ffn", T, 1, 1);
+    if (st) return st;
+    if (T == 0) return MOE_OK;
+    if (!x_bf16 || !y_shared) return fail(MOE_EINVAL, "moe_shared_ffn: null pointer");
+    const size_t need = ffn_ws(shared, T, 1);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_EWORKSPACE,
+                    "moe_shared_ffn: workspace needs " + std::to_string(need) + " bytes");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+        return fail(MOE_EINVAL, "moe_shared_ffn: workspace must be 256-byte aligned");
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    uint16_t* x16 = reinterpret_cast<uint16_t*>(w);
+    uint16_t* h16 = reinterpret_cast<uint16_t*>(w + align_up((size_t)T * shared->H * 2));
+    st = run_gateup(li, x_bf16, nullptr, nullptr, T, 1, h16, x16, stream);
+    if (st) return st;
+    return run_down(li, h16, nullptr, T, 1, y_shared, stream);
+}
+
 int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T,
                 int32_t k, int32_t H, float* out, void* stream) {
     g_last_error.clear();
@@ -293,7 +349,20 @@ int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_
         return fail(MOE_EINVAL, "moe_combine: need T >= 0, 1 <= k <= 16, H > 0, H % 4 == 0");
     if (T == 0) return MOE_OK;
     if (!y_perm || !inv_perm || !topk_w || !out) return fail(MOE_EINVAL, "moe_combine: null pointer");
-    return launch_combine(y_perm, inv_perm, topk_w, T, k, H, out, stream);
+    return launch_combine(y_perm, inv_perm, topk_w, nullptr, T, k, H, out, stream);
+}
+
+int moe_combine_shared(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                       const float* y_shared, int64_t T, int32_t k, int32_t H, float* out,
+                       void* stream) {
+    g_last_error.clear();
+    if (T < 0 || k < 1 || k > MOE_MAX_K || H <= 0 || H % 4)
+        return fail(MOE_EINVAL,
+                    "moe_combine_shared: need T >= 0, 1 <= k <= 16, H > 0, H % 4 == 0");
+    if (T == 0) return MOE_OK;
+    if (!y_perm || !inv_perm || !topk_w || !y_shared || !out)
+        return fail(MOE_EINVAL, "moe_combine_shared: null pointer");
+    return launch_combine(y_perm, inv_perm, topk_w, y_shared, T, k, H, out, stream);
 }
 
 int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj, float* out,

@@ -1,7 +1,8 @@
 // Gated combine and the activation conversion.
 //
 // out[t] = sum_{j=0}^{k-1} w[t, j] * y_perm[inv_perm[t*k + j]], summed in
-// ascending j in fp32.  Every output element has exactly one writer, so no
+// ascending j in fp32, plus the shared expert's y_shared[t] after the sum when
+// there is one.  Every output element has exactly one writer, so no
 // atomics are needed and the bits do not depend on scheduling.
 // (The combine order changes the bits: "GLM-5.3-Flash-TR3-8bpw (K8)",
 // Fidelity / Excess over control.)
@@ -11,9 +12,11 @@ namespace moeq {
 
 namespace {
 
+template <bool SHARED>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_perm,
                                                  const int32_t* __restrict__ inv_perm,
-                                                 const float* __restrict__ w, int k, int H,
+                                                 const float* __restrict__ w,
+                                                 const float* __restrict__ y_shared, int k, int H,
                                                  int nbh, float* __restrict__ out) {
     const int64_t t = blockIdx.x / nbh;
     const int h = ((blockIdx.x % nbh) * 256 + threadIdx.x) * 4;
@@ -25,6 +28,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_per
         f32x4 y = *reinterpret_cast<const f32x4*>(y_perm + row * H + h);
         acc = acc + wj * y;
     }
+    if constexpr (SHARED) acc = acc + *reinterpret_cast<const f32x4*>(y_shared + t * H + h);
     *reinterpret_cast<f32x4*>(out + t * H + h) = acc;
 }
 
@@ -39,11 +43,17 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
 
 }  // namespace
 
-int launch_combine(const float* y_perm, const int32_t* inv_perm, const float* w, int64_t T,
-                   int32_t k, int32_t H, float* out, void* stream) {
+int launch_combine(const float* y_perm, const int32_t* inv_perm, const float* w,
+                   const float* y_shared, int64_t T, int32_t k, int32_t H, float* out,
+                   void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int nbh = (H / 4 + 255) / 256;
-    k_combine<<<(unsigned)(T * nbh), 256, 0, s>>>(y_perm, inv_perm, w, k, H, nbh, out);
+    if (y_shared)
+        k_combine<true><<<(unsigned)(T * nbh), 256, 0, s>>>(y_perm, inv_perm, w, y_shared, k, H,
+                                                            nbh, out);
+    else
+        k_combine<false><<<(unsigned)(T * nbh), 256, 0, s>>>(y_perm, inv_perm, w, nullptr, k, H,
+                                                             nbh, out);
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
 }

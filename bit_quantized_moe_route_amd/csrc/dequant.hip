@@ -4,7 +4,8 @@
 // fp16 codebook entry times an fp16 scale, exact in fp32), so the output can
 // be compared bit for bit with a plain decode of the canonical bytes.  VQ8
 // with one code per group is exact too; with two it is
-// fp32(fp32(C_0 + C_1) * S).
+// fp32(fp32(C_0 + C_1) * S).  BF16 gives the kernels' fp16 operand: the
+// stored weight rounded to fp16 (equal to it for |w| >= 2^-17).
 #include "dev_common.h"
 
 namespace moeq {
@@ -61,6 +62,28 @@ __global__ __launch_bounds__(64) void k_dequant_vq(const uint8_t* __restrict__ r
     }
 }
 
+__global__ __launch_bounds__(64) void k_dequant_bf16(const uint8_t* __restrict__ rec,
+                                                     int rg_step, int rg_off, int n, int kin,
+                                                     float* __restrict__ out) {
+    const int lane = threadIdx.x;
+    const int g = blockIdx.x;
+    const int kb = blockIdx.y;
+    const int nkb = gridDim.y;
+    const uint8_t* tile = rec + ((int64_t)(g * rg_step + rg_off) * nkb + kb) * kBf16TileBytes;
+    const int row = 16 * g + (lane & 15);
+    const int k0 = kb * kBf16TileK + (lane >> 4) * 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f16x8 a =
+            bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(tile + 1024 * j + lane * 16));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = k0 + 8 * j + i;
+            if (row < n && k < kin) out[(int64_t)row * kin + k] = (float)a[i];
+        }
+    }
+}
+
 // VQ8: the M small codebooks of the projection, [M][256][8] fp16
 template <int M>
 __global__ __launch_bounds__(64) void k_dequant_vq8(const uint8_t* __restrict__ rec, int rg_step,
@@ -110,6 +133,9 @@ int launch_dequant(const LayerView& L, int fmt, int32_t ridx, int32_t proj, floa
     if (fmt == MOE_FMT_NVFP4) {
         dim3 grid((unsigned)(n / 16), (unsigned)nv_tiles_k(kin));
         k_dequant_nv<<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, out);
+    } else if (fmt == MOE_FMT_BF16) {
+        dim3 grid((unsigned)(n / 16), (unsigned)bf16_tiles_k(kin));
+        k_dequant_bf16<<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, out);
     } else if (fmt == MOE_FMT_VQ8) {
         const int64_t nkb = vq_tiles_k(kin);
         const int groups = down ? L.H / 16 : 2 * (L.I / 16);

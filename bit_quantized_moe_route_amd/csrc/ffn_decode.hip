@@ -91,6 +91,30 @@ struct Vq8Fmt {
     static constexpr int KSPAN = 64;
 };
 
+// BF16 weights as stored: a lane's 32 weights of a tile are four contiguous
+// 1 KB slices' 16-byte chunks; each chunk converts to one fp16 A fragment
+// (bf16 -> fp32 exact, fp32 -> fp16 nearest even: exact for
+// 2^-17 <= |w| <= 65504, since a bf16 value has 8 significant bits).
+struct Bf16Fmt {
+    static constexpr bool kVq = false;
+    static constexpr bool kVq8 = false;
+    static constexpr int TK = kBf16TileK;
+    static constexpr int TB = kBf16TileBytes;
+    static constexpr int STEPS = 4;
+    static constexpr int KSPAN = 32;
+    struct Frag {
+        u32x4 c[4];
+    };
+    __device__ __forceinline__ static void load(Frag& fr, const uint8_t* tile, int lane) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fr.c[j] = load_stream16(tile + 1024 * j + lane * 16);
+    }
+    __device__ __forceinline__ static void decode(const Frag& fr, const uint8_t*, f16x8 a[STEPS]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = bf16x8_to_f16x8(fr.c[j]);
+    }
+};
+
 template <class F>
 __device__ __forceinline__ int tiles_k(int kin) {
     return (kin + F::TK - 1) / F::TK;
@@ -144,6 +168,7 @@ struct DecodeArgs {
     _Float16* h16;
     float* y_perm;
     int E, H, I, k, fmt;
+    int rows;              // offsets == NULL: rows of the identity map
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -369,13 +394,17 @@ constexpr int kMinWaves = MOEQ_MIN_WAVES;
 // per input tile and used for all 2*RPW (or RPW) weight tiles of the wave.
 // grid: x = sets of (4/KS) waves' rows, y = active-expert slot, z = chunk of
 // 16*NTT rows of the expert.
-template <class F, int NTT, int KS, int RPW, int PHASE, int WV>
+// ID: offsets / perm_src are the identity map of a one-expert layer (a
+// shared expert: its rows are the tokens).
+template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID>
 __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
     constexpr int NM = PHASE == 0 ? 2 * RPW : RPW;   // weight tiles per input tile
     constexpr int SETS = WV / KS;                    // row sets per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const ActiveExpert ae = find_active_expert(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
+    const ActiveExpert ae =
+        ID ? ActiveExpert{blockIdx.y == 0 ? 0 : -1, 0, A.rows, 0}
+           : find_active_expert(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
     if (ae.e < 0) return;
     const int c0 = blockIdx.z * 16 * NTT;
     if (c0 >= ae.me) return;
@@ -421,7 +450,7 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
         if (c >= ae.me)
             xrow[tt] = nullptr;
         else if (PHASE == 0)
-            xrow[tt] = A.xbf + (int64_t)(A.perm_src[ae.r0 + c] / A.k) * A.H;
+            xrow[tt] = A.xbf + (int64_t)(ID ? c : A.perm_src[ae.r0 + c] / A.k) * A.H;
         else
             xrow[tt] = reinterpret_cast<const uint16_t*>(A.h16) + (int64_t)(ae.r0 + c) * A.I;
     }
@@ -442,7 +471,7 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
             // row c0 of the expert exists: a safe row for lanes past its rows
             const uint16_t* xsafe =
                 PHASE == 0
-                    ? A.xbf + (int64_t)(A.perm_src[ae.r0 + c0] / A.k) * A.H
+                    ? A.xbf + (int64_t)(ID ? c0 : A.perm_src[ae.r0 + c0] / A.k) * A.H
                     : reinterpret_cast<const uint16_t*>(A.h16) + (int64_t)(ae.r0 + c0) * A.I;
             stream_tiles_vq<NTT, NM, PHASE == 0>(tb, cb, xrow, xsafe, ntt, K, kpart, KS, lane,
                                                  acc);
@@ -531,17 +560,18 @@ constexpr size_t codebook_lds_bytes(int phase) {
         return 0;
 }
 
-template <class F, int NTT, int KS, int WV>
+template <class F, int NTT, int KS, int WV, bool ID>
 int launch_ks(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
     constexpr int SETS = WV / KS;
     if (phase == 0) {
         const int nsets = (a.I / 16 + kRpwGateup - 1) / kRpwGateup;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
-        k_ffn<F, NTT, KS, kRpwGateup, 0, WV><<<grid, 64 * WV, codebook_lds_bytes<F>(0), s>>>(a);
+        k_ffn<F, NTT, KS, kRpwGateup, 0, WV, ID>
+            <<<grid, 64 * WV, codebook_lds_bytes<F>(0), s>>>(a);
     } else {
         const int nsets = (a.H / 16 + kRpwDown - 1) / kRpwDown;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
-        k_ffn<F, NTT, KS, kRpwDown, 1, WV><<<grid, 64 * WV, codebook_lds_bytes<F>(1), s>>>(a);
+        k_ffn<F, NTT, KS, kRpwDown, 1, WV, ID><<<grid, 64 * WV, codebook_lds_bytes<F>(1), s>>>(a);
     }
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
@@ -550,11 +580,13 @@ int launch_ks(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t
 // Few active experts -> split the input dimension over more waves so the
 // whole chip streams; many -> one wave per row set.  (An 8-way split in
 // 8-wave workgroups measured slower at one token than this 4-way split.)
+// (The identity map of a one-expert layer has one slot.)
 template <class F, int NTT>
 int launch_fmt(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
-    if (slots <= 16) return launch_ks<F, NTT, 4, 4>(a, slots, chunks, phase, s);
-    if (slots <= 64) return launch_ks<F, NTT, 2, 4>(a, slots, chunks, phase, s);
-    return launch_ks<F, NTT, 1, 4>(a, slots, chunks, phase, s);
+    if (a.offsets == nullptr) return launch_ks<F, NTT, 4, 4, true>(a, 1, chunks, phase, s);
+    if (slots <= 16) return launch_ks<F, NTT, 4, 4, false>(a, slots, chunks, phase, s);
+    if (slots <= 64) return launch_ks<F, NTT, 2, 4, false>(a, slots, chunks, phase, s);
+    return launch_ks<F, NTT, 1, 4, false>(a, slots, chunks, phase, s);
 }
 
 template <class F>
@@ -592,10 +624,12 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
     a.I = L.I;
     a.k = k;
     a.fmt = fmt;
+    a.rows = (int)T;
     const int64_t tk = T * k;
     const int slots = (int)(tk < n_fmt ? tk : n_fmt);
     if (slots == 0) return MOE_OK;
     if (fmt == MOE_FMT_NVFP4) return launch_ntt<NvFmt>(a, T, slots, phase, s);
+    if (fmt == MOE_FMT_BF16) return launch_ntt<Bf16Fmt>(a, T, slots, phase, s);
     if (fmt == MOE_FMT_VQ8) {
         if (L.vq8_m == 1) return launch_ntt<Vq8Fmt<1>>(a, T, slots, phase, s);
         return launch_ntt<Vq8Fmt<2>>(a, T, slots, phase, s);

@@ -1,5 +1,5 @@
 // Expert FFN for large token batches (prefill): a grouped GEMM over the
-// active experts with NVFP4 weights decoded in registers.
+// active experts with NVFP4 (or BF16) weights decoded in registers.
 //
 // Per active expert e with M_e rows (permuted order r0 .. r0+M_e):
 //   gate/up:  [g | u] = W13[e] X_e^T,  h = silu(g) * u      -> h (fp16)
@@ -9,7 +9,9 @@
 // Work item = (expert, 128-row tile of its tokens) x (256 weight rows).  A
 // workgroup of 4 waves owns one item; wave w owns 64 weight rows (two 32-row
 // A tiles of v_mfma_f32_32x32x16_f16) and all 128 tokens (four 32-token B
-// tiles), i.e. a 64 x 128 fp32 accumulator block.
+// tiles), i.e. a 64 x 128 fp32 accumulator block.  (BF16 experts: 32
+// weight rows per wave, since a raw bf16 A fragment takes four times the
+// registers of an NVFP4 one.)
 //   * weights: each wave loads its rows' packed NVFP4 tiles from HBM straight
 //     into registers (the next 128-input tile is in flight while the current
 //     one is used), decodes 8 weights at a time to fp16 (exact) right before
@@ -53,7 +55,6 @@ constexpr int kBM = 128;           // tokens per work item
 #endif
 constexpr int kPrefillWaves = MOEQ_PF_WAVES;
 constexpr int kPrefillStages = MOEQ_PF_STAGES;
-constexpr int kBN = 64 * kPrefillWaves;   // weight rows per work item
 // s_waitcnt immediate for "vmcnt(0)", other counters unconstrained (gfx9 encoding:
 // vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
 constexpr int kVmcnt0 = 0x0F70;
@@ -66,12 +67,13 @@ struct PrefillArgs {
     const uint8_t* pool;
     int64_t stride;
     const int32_t* rec;
-    const int32_t* offsets;
-    const int32_t* perm_src;
+    const int32_t* offsets;    // NULL: one expert whose rows are the tokens
+    const int32_t* perm_src;   // NULL: identity
     const _Float16* x16;
     _Float16* h16;
     float* y_perm;
     int E, H, I, k, fmt;
+    int rows;                  // offsets == NULL: rows of the identity map
 };
 
 struct WorkItem {
@@ -83,9 +85,29 @@ struct WorkItem {
 // ascending expert id).  All offsets/record loads are issued up front (one
 // memory round trip); the item count comes from the same registers.
 // Returns e = -1 if w is past the end of the list.
+// ID: the identity map of a one-expert layer (rows 0 .. rows-1 of expert 0).
+template <bool ID>
 __device__ __forceinline__ WorkItem locate_item(const int32_t* __restrict__ offsets,
                                                 const int32_t* __restrict__ rec, int E, int fmt,
-                                                int nnt, int blk, int lane, int& ntile) {
+                                                int rows, int nnt, int blk, int lane,
+                                                int& ntile) {
+    if constexpr (ID) {
+#if MOEQ_PF_ORDER == 0
+        const int total = (rows + kBM - 1) / kBM;
+        const int nwork = total * nnt;
+        const int quota = (nwork + 7) / 8;
+        const int slot = blk >> 3;
+        const int w = (blk & 7) * quota + slot;
+        ntile = w % nnt;
+        const int want_item = (slot >= quota || w >= nwork) ? total : w / nnt;
+#else
+        const int slot = blk >> 3;
+        const int want_item = (slot / nnt) * 8 + (blk & 7);
+        ntile = slot % nnt;
+#endif
+        if (want_item * kBM >= rows) return WorkItem{-1, 0, 0, 0, 0};
+        return WorkItem{0, 0, rows, 0, want_item * kBM};
+    }
     constexpr int kMaxChunks = MOE_MAX_E / 64;
     int o0[kMaxChunks], o1[kMaxChunks], rc[kMaxChunks], cnt[kMaxChunks];
     const int nch = (E + 63) / 64;
@@ -192,15 +214,66 @@ __device__ __forceinline__ f16x8 a_step(const AFrag& f, int s) {
     return nv_dequant8(c[s & 3], sv);
 }
 
-// WV waves per workgroup (64 weight rows each), NS token-tile buffers in LDS
-// (NS - 1 tiles in flight ahead of the one in use).  (They are file-level
-// constants, not template parameters: a __shared__ array sized by a template
-// parameter loses its host-side launch stub with this compiler.)
-template <int PHASE>
-__global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArgs A) {
+// Weight formats of the grouped GEMM: NA 32-row A tiles per wave, TB bytes
+// per 16-row x 128-input record tile, the per-lane fragment of one A tile
+// and one 128-input tile, and its fp16 A operand of K-step s.
+struct PfNv {
+    static constexpr int NA = 2;
+    static constexpr int TB = kNvTileBytes;
+    using Frag = AFrag;
+    __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
+                                                int lane, bool valid) {
+        load_a(f, grp_base, gstride, lane, valid);
+    }
+    __device__ __forceinline__ static f16x8 step(const Frag& f, int s) { return a_step(f, s); }
+};
+
+// BF16: lane L (row L & 31, half h = L >> 5) needs inputs 64h + 8s .. +7,
+// s = 0..7: record lane (row & 15) + 32h holds 64h + 8j (s = j < 4), record
+// lane + 16 holds 64h + 32 + 8j (s = 4 + j), slice j of the tile.
+struct PfBf16 {
+    static constexpr int NA = 1;
+    static constexpr int TB = kBf16TileBytes;
+    struct Frag {
+        u32x4 c[8];
+    };
+    __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
+                                                int lane, bool valid) {
+        if (!valid) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) f.c[s] = u32x4{0u, 0u, 0u, 0u};
+            return;
+        }
+        const int row = lane & 31;
+        const uint8_t* tile = grp_base + (row >> 4) * gstride;
+        const int l0 = (row & 15) + 32 * (lane >> 5);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f.c[j] = *reinterpret_cast<const u32x4*>(tile + 1024 * j + l0 * 16);
+            f.c[4 + j] = *reinterpret_cast<const u32x4*>(tile + 1024 * j + (l0 + 16) * 16);
+        }
+    }
+    __device__ __forceinline__ static f16x8 step(const Frag& f, int s) {
+        return bf16x8_to_f16x8(f.c[s]);
+    }
+};
+
+template <class PF>
+constexpr int pf_bn() {
+    return 32 * PF::NA * kPrefillWaves;   // weight rows per work item
+}
+
+// WV waves per workgroup (32 NA weight rows each), NS token-tile buffers in
+// LDS (NS - 1 tiles in flight ahead of the one in use).  (They are
+// file-level constants, not template parameters: a __shared__ array sized by
+// a template parameter loses its host-side launch stub with this compiler.)
+// ID: offsets / perm_src are the identity map of a one-expert layer.
+template <class PF, int PHASE, bool ID>
+__global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A) {
     constexpr int WV = kPrefillWaves;
     constexpr int NS = kPrefillStages;
-    constexpr int BN = 64 * WV;        // weight rows per work item
+    constexpr int NA = PF::NA;
+    constexpr int BN = pf_bn<PF>();    // weight rows per work item
     constexpr int JX = 32 / WV;        // 1 KB staging loads per wave per token tile
     __shared__ _Float16 xs[kPrefillStages][kBM * kNvTileK];
     const int tid = threadIdx.x;
@@ -210,11 +283,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
     const int nrg = (PHASE == 0 ? 2 * A.I : A.H) / 16;       // record row groups
     const int nnt = (nrg + BN / 16 - 1) / (BN / 16);          // weight tiles of BN rows
     int ntile = 0;
-    const WorkItem it = locate_item(A.offsets, A.rec, A.E, A.fmt, nnt, blockIdx.x, lane, ntile);
+    const WorkItem it =
+        locate_item<ID>(A.offsets, A.rec, A.E, A.fmt, A.rows, nnt, blockIdx.x, lane, ntile);
     if (it.e < 0) return;
     const int nkb = (K + kNvTileK - 1) / kNvTileK;
-    const int64_t gstride = (int64_t)nkb * kNvTileBytes;     // bytes per row group
-    const int g0 = ntile * (BN / 16) + wave * 4;              // first row group of the wave
+    const int64_t gstride = (int64_t)nkb * PF::TB;            // bytes per row group
+    const int g0 = ntile * (BN / 16) + wave * 2 * NA;         // first row group of the wave
     const int mcount = min(kBM, it.me - it.m0);
     const int nbt = (mcount + 31) / 32;                      // 32-token B tiles in use
     const uint8_t* base = A.pool + (int64_t)it.ridx * A.stride;
@@ -231,7 +305,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
 #pragma unroll
     for (int j = 0; j < JX; ++j) {
         const int row = min(4 * (JX * wave + j) + (lane >> 4), mcount - 1);
-        trow[j] = PHASE == 0 ? A.perm_src[it.r0 + it.m0 + row] / A.k : it.r0 + it.m0 + row;
+        const int prow = it.r0 + it.m0 + row;
+        trow[j] = PHASE == 0 && !ID ? A.perm_src[prow] / A.k : prow;
     }
     auto issue_x = [&](int kb, int buf) {
 #pragma unroll
@@ -245,19 +320,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
     };
 
     // weights: A tile a of this wave = record groups g0 + 2a, g0 + 2a + 1
-    const bool va0 = g0 < nrg, va1 = g0 + 2 < nrg;
-    const bool vh0 = g0 + 1 < nrg, vh1 = g0 + 3 < nrg;
-    auto load_w = [&](int kb, AFrag& a0, AFrag& a1) {
-        const int row = lane & 31;
-        load_a(a0, base + (int64_t)g0 * gstride + (int64_t)kb * kNvTileBytes, gstride, lane,
-               row < 16 ? va0 : vh0);
-        load_a(a1, base + (int64_t)(g0 + 2) * gstride + (int64_t)kb * kNvTileBytes, gstride, lane,
-               row < 16 ? va1 : vh1);
+    bool valid[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) valid[a] = g0 + 2 * a + ((lane & 31) < 16 ? 0 : 1) < nrg;
+    auto load_w = [&](int kb, typename PF::Frag (&wa)[NA]) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+            PF::load(wa[a], base + (int64_t)(g0 + 2 * a) * gstride + (int64_t)kb * PF::TB,
+                     gstride, lane, valid[a]);
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[NA][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[a][q] = f32x16{};
 
@@ -267,8 +342,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
     // and LDS buffers alternate with a compile-time parity.
     auto run = [&](auto nb_c) {
         constexpr int NB = decltype(nb_c)::value;
-        AFrag w[2][2];
-        load_w(0, w[0][0], w[0][1]);
+        typename PF::Frag w[2][NA];
+        load_w(0, w[0]);
 #pragma unroll
         for (int b = 0; b < NS - 1; ++b)
             if (b < nkb) issue_x(b, b);
@@ -285,7 +360,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
             const bool more = kb + 1 < nkb;
             // W(kb + 1) first, then X(kb + NS - 1): the wait below then leaves
             // only the newest token tile in flight
-            if (more) load_w(kb + 1, w[P ^ 1][0], w[P ^ 1][1]);
+            if (more) load_w(kb + 1, w[P ^ 1]);
             const bool ahead = kb + NS - 1 < nkb;
             if (ahead) issue_x(kb + NS - 1, (kb + NS - 1) % NS);
             const _Float16* xb = xrow0 + (kb % NS) * (kBM * kNvTileK);
@@ -303,16 +378,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
             if constexpr (NB > 1) bq[1] = rd(0, 1);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const f16x8 a0 = a_step(w[P][0], s);
-                const f16x8 a1 = a_step(w[P][1], s);
+                f16x8 av[NA];
+#pragma unroll
+                for (int a = 0; a < NA; ++a) av[a] = PF::step(w[P][a], s);
                 if constexpr (NB > 2) bq[2] = rd(s, 2);
                 if constexpr (NB > 3) bq[3] = rd(s, 3);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int q = 0; q < (NB < 2 ? NB : 2); ++q) {
-                    acc[0][q] = mfma32(a0, bq[q], acc[0][q]);
-                    acc[1][q] = mfma32(a1, bq[q], acc[1][q]);
-                }
+                for (int q = 0; q < (NB < 2 ? NB : 2); ++q)
+#pragma unroll
+                    for (int a = 0; a < NA; ++a) acc[a][q] = mfma32(av[a], bq[q], acc[a][q]);
                 __builtin_amdgcn_sched_barrier(0);
                 if (s < 7) {
                     bq[0] = rd(s + 1, 0);
@@ -320,10 +395,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int q = 2; q < NB; ++q) {
-                    acc[0][q] = mfma32(a0, bq[q], acc[0][q]);
-                    acc[1][q] = mfma32(a1, bq[q], acc[1][q]);
-                }
+                for (int q = 2; q < NB; ++q)
+#pragma unroll
+                    for (int a = 0; a < NA; ++a) acc[a][q] = mfma32(av[a], bq[q], acc[a][q]);
             }
 #else
 #if MOEQ_PF_PRIO
@@ -331,13 +405,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
 #endif
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const f16x8 a0 = a_step(w[P][0], s);
-                const f16x8 a1 = a_step(w[P][1], s);
+                f16x8 av[NA];
+#pragma unroll
+                for (int a = 0; a < NA; ++a) av[a] = PF::step(w[P][a], s);
 #pragma unroll
                 for (int q = 0; q < NB; ++q) {
                     const f16x8 b = rd(s, q);
-                    acc[0][q] = mfma32(a0, b, acc[0][q]);
-                    acc[1][q] = mfma32(a1, b, acc[1][q]);
+#pragma unroll
+                    for (int a = 0; a < NA; ++a) acc[a][q] = mfma32(av[a], b, acc[a][q]);
                 }
             }
 #if MOEQ_PF_PRIO
@@ -371,7 +446,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
         if (q >= nbt || tok >= mcount) continue;
         const int64_t prow = it.r0 + it.m0 + tok;            // permuted row
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
+        for (int a = 0; a < NA; ++a) {
             const int ga = g0 + 2 * a;
             if (PHASE == 0) {
                 if (ga >= nrg) continue;
@@ -403,31 +478,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill_nv(PrefillArg
 
 }  // namespace
 
-int launch_ffn_prefill(const LayerView& L, int n_fmt, const uint16_t* x16,
-                       const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
-                       uint16_t* h16, float* y_perm, int phase, void* stream) {
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    PrefillArgs a;
-    a.pool = phase == 0 ? L.pool13[MOE_FMT_NVFP4] : L.pool2[MOE_FMT_NVFP4];
-    a.stride = phase == 0 ? L.stride13[MOE_FMT_NVFP4] : L.stride2[MOE_FMT_NVFP4];
-    a.rec = L.rec;
-    a.offsets = offsets;
-    a.perm_src = perm_src;
-    a.x16 = reinterpret_cast<const _Float16*>(x16);
-    a.h16 = reinterpret_cast<_Float16*>(h16);
-    a.y_perm = y_perm;
-    a.E = L.E;
-    a.H = L.H;
-    a.I = L.I;
-    a.k = k;
-    a.fmt = MOE_FMT_NVFP4;
-    const int64_t tk = T * k;
-    const int64_t active = tk < n_fmt ? tk : n_fmt;
-    // sum over experts of ceil(M_e / 128) <= T*k / 128 + (number of active experts)
-    const int64_t items = tk / kBM + active;
-    if (items == 0) return MOE_OK;
-    const int nrg = (phase == 0 ? 2 * L.I : L.H) / 16;
-    const int64_t nnt = (nrg + kBN / 16 - 1) / (kBN / 16);
+namespace {
+
+template <class PF, bool ID>
+int launch_pf(const PrefillArgs& a, int64_t items, int phase, hipStream_t s) {
+    constexpr int BN = pf_bn<PF>();
+    const int nrg = (phase == 0 ? 2 * a.I : a.H) / 16;
+    const int64_t nnt = (nrg + BN / 16 - 1) / (BN / 16);
 #if MOEQ_PF_ORDER == 0
     // 8 slices of ceil(items * nnt / 8) workgroups cover every item; slots past
     // the actual item count exit at once
@@ -439,11 +496,45 @@ int launch_ffn_prefill(const LayerView& L, int n_fmt, const uint16_t* x16,
 #endif
     dim3 grid((unsigned)nblocks);
     if (phase == 0)
-        k_prefill_nv<0><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
+        k_prefill<PF, 0, ID><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
     else
-        k_prefill_nv<1><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
+        k_prefill<PF, 1, ID><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
+}
+
+}  // namespace
+
+int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,
+                       const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
+                       uint16_t* h16, float* y_perm, int phase, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    PrefillArgs a;
+    a.pool = phase == 0 ? L.pool13[fmt] : L.pool2[fmt];
+    a.stride = phase == 0 ? L.stride13[fmt] : L.stride2[fmt];
+    a.rec = L.rec;
+    a.offsets = offsets;
+    a.perm_src = perm_src;
+    a.x16 = reinterpret_cast<const _Float16*>(x16);
+    a.h16 = reinterpret_cast<_Float16*>(h16);
+    a.y_perm = y_perm;
+    a.E = L.E;
+    a.H = L.H;
+    a.I = L.I;
+    a.k = k;
+    a.fmt = fmt;
+    a.rows = (int)T;
+    const int64_t tk = T * k;
+    const int64_t active = tk < n_fmt ? tk : n_fmt;
+    // sum over experts of ceil(M_e / 128) <= T*k / 128 + (number of active experts)
+    const int64_t items = tk / kBM + active;
+    if (items == 0) return MOE_OK;
+    const bool id = offsets == nullptr;
+    if (fmt == MOE_FMT_BF16)
+        return id ? launch_pf<PfBf16, true>(a, items, phase, s)
+                  : launch_pf<PfBf16, false>(a, items, phase, s);
+    return id ? launch_pf<PfNv, true>(a, items, phase, s)
+              : launch_pf<PfNv, false>(a, items, phase, s);
 }
 
 }  // namespace moeq

@@ -27,6 +27,10 @@ int fail(int status, const std::string& msg);
 //   512 m code bytes; lane L owns bytes [8mL, 8mL + 8m): row (L & 15), the
 //   groups of inputs kb*256 + (L >> 4)*64 + 8s + [0, 8), s = 0..7, each group's
 //   m codes consecutive (code j of group s at byte m*s + j).
+// BF16 tile: 16 rows x 128 inputs = 4096 bytes in 4 slices of 1024: slice j,
+//   lane L owns bytes [1024j + 16L, +16) = 8 bf16 weights of row (L & 15),
+//   inputs kb*128 + (L >> 4)*32 + 8j + [0, 8) (so one 16-byte load per lane
+//   reads a contiguous 1 KB slice).
 // A record is a sequence of row groups of 16 rows, each a sequence of tiles
 // along the input dimension (padded with zero codes/scales).  Gate/up
 // records interleave row groups: group 2j = gate rows 16j.., 2j+1 = up rows.
@@ -39,6 +43,8 @@ constexpr int kVqTileK = 256;
 constexpr int kVqTileBytes = 1024;
 constexpr int kVq8TileK = 256;
 constexpr int kVq8TileBytesPerCode = 512;   // times m
+constexpr int kBf16TileK = 128;
+constexpr int kBf16TileBytes = 4096;
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
@@ -54,9 +60,13 @@ inline int64_t vq_codes_bytes(int32_t n, int32_t kin) {
 inline int64_t vq8_codes_bytes(int32_t n, int32_t kin, int32_t m) {
     return (int64_t)(n / 16) * vq_tiles_k(kin) * kVq8TileBytesPerCode * m;
 }
+inline int64_t bf16_tiles_k(int32_t kin) { return round_up(kin, kBf16TileK) / kBf16TileK; }
+inline int64_t bf16_matrix_bytes(int32_t n, int32_t kin) {
+    return (int64_t)(n / 16) * bf16_tiles_k(kin) * kBf16TileBytes;
+}
 
 // Launchers (device code lives in the .hip files) ----------------------------
-constexpr int kNumFmt = 4;      // format tags 1 .. 3
+constexpr int kNumFmt = MOE_FMT_MAX + 1;   // format tags 1 .. MOE_FMT_MAX
 struct LayerView {
     int32_t E, H, I;
     int32_t vq8_m;
@@ -81,15 +91,20 @@ int launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, i
                          float* w, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                          int32_t* inv_perm, void* stream);
 int launch_combine(const float* y_perm, const int32_t* inv_perm, const float* w,
-                   int64_t T, int32_t k, int32_t H, float* out, void* stream);
+                   const float* y_shared, int64_t T, int32_t k, int32_t H, float* out,
+                   void* stream);
 int launch_x_to_f16(const uint16_t* x, int64_t n, uint16_t* x16, void* stream);
+// perm_src == NULL and offsets == NULL: the identity map of a one-expert
+// layer (rows 0 .. T-1 of expert 0 are tokens 0 .. T-1, k = 1).
 int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,
                       const int32_t* perm_src, const int32_t* offsets, int64_t T,
                       int32_t k, uint16_t* h16, float* y_perm, int phase,
                       void* stream);
-// NVFP4 experts at T >= kPrefillMinTokens use the grouped-GEMM kernels.
+// NVFP4 and BF16 experts at T >= kPrefillMinTokens use the grouped-GEMM
+// kernels.
 constexpr int64_t kPrefillMinTokens = 128;
-int launch_ffn_prefill(const LayerView& L, int n_fmt, const uint16_t* x16,
+inline bool prefill_fmt(int fmt) { return fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16; }
+int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,
                        const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
                        uint16_t* h16, float* y_perm, int phase, void* stream);
 int launch_dequant(const LayerView& L, int fmt, int32_t rec_index, int32_t proj,

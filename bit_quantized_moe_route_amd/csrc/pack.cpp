@@ -1,5 +1,5 @@
 // Host-side packers: the NVFP4 encoder (fp32 -> canonical codes + E4M3
-// scales) and the device record layouts of NVFP4 and VQ experts.
+// scales) and the device record layouts of NVFP4, VQ, VQ8 and BF16 experts.
 // Plain C++17, no device access.
 #include <cmath>
 #include <cstring>
@@ -122,6 +122,35 @@ static void vq8_tiles(const uint8_t* codes, int32_t n, int32_t kin, int32_t m, i
     }
 }
 
+// BF16 record tile writer (bf16 bits [n, kin], row-major).
+static void bf16_tiles(const uint16_t* w, int32_t n, int32_t kin, int rg_step, int rg_off,
+                       uint8_t* rec) {
+    const int64_t nkb = bf16_tiles_k(kin);
+    for (int g = 0; g < n / 16; ++g) {
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            uint8_t* tile = rec + ((int64_t)(g * rg_step + rg_off) * nkb + kb) * kBf16TileBytes;
+            std::memset(tile, 0, kBf16TileBytes);
+            for (int j = 0; j < 4; ++j)
+                for (int L = 0; L < 64; ++L) {
+                    const int row = 16 * g + (L & 15);
+                    const int k0 = (int)kb * kBf16TileK + (L >> 4) * 32 + 8 * j;
+                    uint16_t* dst = reinterpret_cast<uint16_t*>(tile + 1024 * j + 16 * L);
+                    for (int i = 0; i < 8; ++i)
+                        if (k0 + i < kin) dst[i] = w[(int64_t)row * kin + k0 + i];
+                }
+        }
+    }
+}
+
+static int64_t bf16_rec_bytes(int which, int32_t H, int32_t I) {
+    if (which == 0) return round_up(bf16_matrix_bytes(2 * I, H), 256);
+    return round_up(bf16_matrix_bytes(H, I), 256);
+}
+
+// A bf16 weight the kernels can use as fp16: finite and |w| <= 65504 (the
+// largest bf16 below 65520, where fp16 rounding would overflow, is 65280).
+static bool bf16_fits_f16(uint16_t b) { return (b & 0x7fffu) < 0x4780u; }
+
 static int64_t vq8_rec_bytes(int which, int32_t H, int32_t I, int32_t m) {
     if (which == 0) return round_up(vq8_codes_bytes(2 * I, H, m) + 2LL * I * 2, 256);
     return round_up(vq8_codes_bytes(H, I, m) + 2LL * H, 256);
@@ -188,6 +217,10 @@ size_t moe_record_bytes(int fmt, int which, int32_t H, int32_t I) {
         if (H % 16 || I % 16) return 0;   // row groups of 16 outputs; inputs in groups of 8
         return (size_t)vq_rec_bytes(which, H, I);
     }
+    if (fmt == MOE_FMT_BF16) {
+        if (H % 16 || I % 16) return 0;
+        return (size_t)bf16_rec_bytes(which, H, I);
+    }
     return 0;
 }
 
@@ -252,22 +285,42 @@ int moe_pack_vq8_expert(const uint8_t* gc, const uint16_t* gs, const uint8_t* uc
     return MOE_OK;
 }
 
-int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* n_nvfp4,
-                     int32_t* n_vq, int32_t* n_vq8) {
+int moe_pack_bf16_expert(const uint16_t* gate, const uint16_t* up, const uint16_t* down,
+                         int32_t H, int32_t I, uint8_t* w13, uint8_t* w2) {
+    if (!gate || !up || !down || !w13 || !w2)
+        return fail(MOE_EINVAL, "moe_pack_bf16_expert: null pointer");
+    if (H <= 0 || I <= 0 || H % 16 || I % 16)
+        return fail(MOE_EUNSUPPORTED, "moe_pack_bf16_expert: H and I must be positive multiples of 16");
+    const int64_t n = (int64_t)H * I;
+    for (const uint16_t* m : {gate, up, down})
+        for (int64_t i = 0; i < n; ++i)
+            if (!bf16_fits_f16(m[i]))
+                return fail(MOE_EINVAL,
+                            "moe_pack_bf16_expert: a weight is not finite or exceeds 65504");
+    std::memset(w13, 0, (size_t)bf16_rec_bytes(0, H, I));
+    std::memset(w2, 0, (size_t)bf16_rec_bytes(1, H, I));
+    bf16_tiles(gate, I, H, 2, 0, w13);
+    bf16_tiles(up, I, H, 2, 1, w13);
+    bf16_tiles(down, H, I, 1, 0, w2);
+    return MOE_OK;
+}
+
+static bool known_fmt(int f) { return f >= MOE_FMT_NVFP4 && f <= MOE_FMT_MAX; }
+
+int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* n_by_fmt) {
     if (!fmt_host || !rec) return fail(MOE_EINVAL, "moe_record_table: null pointer");
     if (E < 1 || E > MOE_MAX_E) return fail(MOE_EINVAL, "moe_record_table: bad E");
-    int32_t cnt[kNumFmt] = {0, 0, 0, 0};
+    int32_t cnt[kNumFmt] = {};
     for (int e = 0; e < E; ++e) {
         const int f = fmt_host[e];
-        if (f != MOE_FMT_NVFP4 && f != MOE_FMT_VQ && f != MOE_FMT_VQ8)
+        if (!known_fmt(f))
             return fail(MOE_EUNSUPPORTED,
                         "moe_record_table: expert " + std::to_string(e) + " has unknown format tag " +
                             std::to_string(f));
         rec[e] = (f << 24) | cnt[f]++;
     }
-    if (n_nvfp4) *n_nvfp4 = cnt[MOE_FMT_NVFP4];
-    if (n_vq) *n_vq = cnt[MOE_FMT_VQ];
-    if (n_vq8) *n_vq8 = cnt[MOE_FMT_VQ8];
+    if (n_by_fmt)
+        for (int f = 0; f < kNumFmt; ++f) n_by_fmt[f] = cnt[f];
     return MOE_OK;
 }
 
@@ -276,7 +329,7 @@ int moe_record_table_resident(const uint8_t* fmt_host, int32_t E, int32_t* rec) 
     if (E < 1 || E > MOE_MAX_E) return fail(MOE_EINVAL, "moe_record_table_resident: bad E");
     for (int e = 0; e < E; ++e) {
         const int f = fmt_host[e];
-        if (f != MOE_FMT_NVFP4 && f != MOE_FMT_VQ && f != MOE_FMT_VQ8)
+        if (!known_fmt(f))
             return fail(MOE_EUNSUPPORTED, "moe_record_table_resident: expert " + std::to_string(e) +
                                               " has unknown format tag " + std::to_string(f));
         rec[e] = (f << 24) | e;

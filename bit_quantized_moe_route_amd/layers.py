@@ -11,13 +11,14 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from . import (FMT_NVFP4, FMT_VQ, FMT_VQ8, PROJ_DOWN, PROJ_GATE, PROJ_UP, QLayer,
-               pack_nvfp4_expert, pack_vq8_expert, pack_vq_expert, quantize_nvfp4)
+from . import (FMT_BF16, FMT_NVFP4, FMT_VQ, FMT_VQ8, PROJ_DOWN, PROJ_GATE, PROJ_UP, QLayer,
+               pack_bf16_expert, pack_nvfp4_expert, pack_vq8_expert, pack_vq_expert,
+               quantize_nvfp4)
 
 
 def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=None,
-                codebook_stride=0, vq8_codes=None, codebooks8=None, vq8_m=0, device="cuda",
-                workers=8, resident_formats=None):
+                codebook_stride=0, vq8_codes=None, codebooks8=None, vq8_m=0, bf16_weights=None,
+                device="cuda", workers=8, resident_formats=None):
     """Build a QLayer.
 
     nvfp4_weights(e, proj) -> fp32 [n, kin] source weights of an NVFP4 expert
@@ -29,6 +30,8 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
     vq8_codes(e, proj) -> (codes uint8 [n, kin/8, vq8_m], scales fp16 bits [n])
         of a small-codebook VQ expert; codebooks8: for gate, up, down a list of
         vq8_m uint16 arrays [256, 8].
+    bf16_weights(e, proj) -> bf16 bits uint16 [n, kin] of a BF16 expert (a
+        routed BF16-tier expert, or the one expert of a shared-expert layer).
     resident_formats: None, or the formats every expert is packed in (slot e of
         each of those pools), for a layer whose tiers change at run time
         (QLayer.set_tiers).
@@ -56,6 +59,9 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         if fmt == FMT_NVFP4:
             parts = [quantize_nvfp4(nvfp4_weights(e, p)) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
             w13, w2 = pack_nvfp4_expert(parts[0], parts[1], parts[2], H, I)
+        elif fmt == FMT_BF16:
+            parts = [bf16_weights(e, p) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
+            w13, w2 = pack_bf16_expert(parts[0], parts[1], parts[2], H, I)
         elif fmt == FMT_VQ8:
             parts = [vq8_codes(e, p) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
             w13, w2 = pack_vq8_expert(parts[0], parts[1], parts[2], H, I, vq8_m)

@@ -10,6 +10,12 @@
  *   moe_expert_ffn_q  x [T, H], perm_src, ...  -> y_perm [T*k, H]
  *   moe_combine       y_perm, inv_perm, topk_w -> out [T, H]
  *
+ * and, for layers with a shared expert that every token passes through,
+ *
+ *   moe_shared_ffn      x [T, H]                   -> y_shared [T, H]
+ *   moe_combine_shared  y_perm, inv_perm, topk_w,
+ *                       y_shared                   -> out [T, H]
+ *
  * Passages these calls follow (titles and sections of the source pages):
  *   - 256 routed experts per MoE layer, 8 active per token:
  *     "GLM-5-NVFP4-MTP", Model Description.
@@ -27,6 +33,10 @@
  *     "GLM-5.3 Vision NestQuant 1.75-4 bit", Contents.
  *   - a fixed expert-combine order (the order changes the bits):
  *     "GLM-5.3-Flash-TR3-8bpw (K8)", Fidelity / Excess over control.
+ *   - BF16 shared experts beside the low-bit routed ones:
+ *     "GLM-5.3-EXL3-TR3-3.42bpw", What is quantized; "GLM-5-NVFP4-MTP",
+ *     What's quantized (shared experts are among the non-expert weights
+ *     kept in BF16).
  *
  * Conventions
  *   - Pointers marked [device] are device memory on the current HIP device;
@@ -74,6 +84,8 @@ extern "C" {
                                  256-entry fp16 codebooks whose rows are
                                  summed, fp16 scale per output channel
                                  (M bits per weight) */
+#define MOE_FMT_BF16  4       /* bf16 weights as stored, no scales */
+#define MOE_FMT_MAX   4       /* largest format tag */
 
 #define MOE_PROJ_GATE 0
 #define MOE_PROJ_UP   1
@@ -96,8 +108,7 @@ extern "C" {
  * its format (so a single-format layer has index(e) = e).  Record sizes are
  * given by moe_record_bytes() and their bytes by the moe_pack_* calls.
  *
- *   fmt_host   [host]   uint8 [E]: MOE_FMT_NVFP4, MOE_FMT_VQ or MOE_FMT_VQ8
- *                       per expert.
+ *   fmt_host   [host]   uint8 [E]: a format tag (MOE_FMT_*) per expert.
  *   rec_dev    [device] int32 [E]: (fmt << 24) | index(e), as written by
  *                       moe_record_table() from the same fmt_host.
  *   nvfp4_w13 / nvfp4_w2   pool bases of NVFP4 gate/up and down records;
@@ -113,6 +124,7 @@ extern "C" {
  *   vq8_w13 / vq8_w2   pool bases of the MOE_FMT_VQ8 records;
  *   vq8_codebook[p] fp16 [vq8_m][256][8]: the small codebooks of projection
  *                   p, shared by every MOE_FMT_VQ8 expert of the layer.
+ *   bf16_w13 / bf16_w2 pool bases of the MOE_FMT_BF16 records.
  *   record_mode     MOE_REC_COMPACT: index(e) = e's rank among the experts of
  *                   its format (rec from moe_record_table);
  *                   MOE_REC_RESIDENT: every pool that is used holds a record for
@@ -143,6 +155,8 @@ typedef struct moe_qlayer {
     const void* vq8_w13;    int64_t vq8_w13_stride;
     const void* vq8_w2;     int64_t vq8_w2_stride;
     const void* vq8_codebook[3];
+    const void* bf16_w13;   int64_t bf16_w13_stride;
+    const void* bf16_w2;    int64_t bf16_w2_stride;
     int32_t record_mode;
     int32_t reserved;
 } moe_qlayer;
@@ -237,15 +251,16 @@ size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k);
  *   y_perm   [device] fp32 [T*k, H] out.
  *   ws       [device] >= moe_ffn_workspace_bytes() bytes, 256-byte aligned.
  *
- *   Arithmetic: decoded weights are exact (every NVFP4 product of an E2M1
- *   value and an E4M3 scale is exact in bf16 and fp16; VQ codebook entries
- *   are fp16, the per-channel scale is applied in fp32 after the dot
- *   product).  Products accumulate in fp32 on the matrix cores; x enters the
- *   gate/up product as bf16 (NVFP4) or fp16 (VQ), h enters the down product
- *   as fp16.
- *   Requirements: H and I multiples of 16 (both formats); every format
- *   tag in layer->fmt_host must be MOE_FMT_NVFP4 or MOE_FMT_VQ, else
- *   MOE_EUNSUPPORTED; every pool that a tag refers to must be non-NULL.
+ *   Arithmetic: the matrix cores multiply fp16 operands and accumulate in
+ *   fp32.  Decoded NVFP4 and VQ weights are exact in fp16 (an E2M1 value
+ *   times an E4M3 scale; fp16 codebook entries, the per-channel scale applied
+ *   in fp32 after the dot product); bf16 weights and x are converted to fp16
+ *   (exact for 2^-17 <= |v| <= 65504 with 8 significant bits; smaller
+ *   magnitudes round to fp16's subnormal grid, spacing 2^-24); h enters the
+ *   down product as fp16.
+ *   Requirements: H and I multiples of 16; every format tag in
+ *   layer->fmt_host must be one of MOE_FMT_*, else MOE_EUNSUPPORTED; every
+ *   pool that a tag refers to must be non-NULL.
  */
 int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16,
                      const int32_t* perm_src, const int32_t* offsets,
@@ -274,6 +289,29 @@ int moe_expert_down_q(const moe_qlayer* layer, const uint16_t* h_f16,
                       const int32_t* offsets, int64_t T, int32_t k,
                       float* y_perm, void* stream);
 
+/* -------------------------------------------------------- shared expert */
+
+/* Workspace bytes moe_shared_ffn needs (h, and x as fp16 for T >= 128). */
+size_t moe_shared_ffn_workspace_bytes(const moe_qlayer* shared, int64_t T);
+
+/*
+ * moe_shared_ffn -- the shared expert, an expert that every token passes
+ * through with weight 1:  y_shared[t] = W_down (silu(W_gate x_t) * W_up x_t).
+ *   ("GLM-5.3-EXL3-TR3-3.42bpw", What is quantized: the layers keep BF16
+ *   shared experts beside the routed ones.)
+ *
+ *   shared   a one-expert layer (E == 1) in any format, normally
+ *            MOE_FMT_BF16; its I is the shared expert's intermediate size.
+ *   x        [device] bf16 [T, H] bits, token order.
+ *   y_shared [device] fp32 [T, H] out.
+ *   ws       [device] >= moe_shared_ffn_workspace_bytes(), 256-byte aligned.
+ *   The same kernels, arithmetic and errors as moe_expert_ffn_q with
+ *   perm_src = (0, 1, .., T-1), offsets = (0, T) and k = 1, which this call
+ *   implies without reading them from memory.
+ */
+int moe_shared_ffn(const moe_qlayer* shared, const uint16_t* x_bf16, int64_t T,
+                   float* y_shared, void* ws, size_t ws_bytes, void* stream);
+
 /* -------------------------------------------------------------- combine */
 
 /*
@@ -287,6 +325,18 @@ int moe_expert_down_q(const moe_qlayer* layer, const uint16_t* h_f16,
  */
 int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
                 int64_t T, int32_t k, int32_t H, float* out, void* stream);
+
+/*
+ * moe_combine_shared -- moe_combine with the shared expert's output added
+ * after the routed sum:
+ *   out[t] = (sum_{j=0}^{k-1} topk_w[t, j] * y_perm[inv_perm[t*k+j]]) + y_shared[t]
+ * (the routed sum in ascending j in fp32, then one fp32 add; one writer per
+ * element).  y_shared [device] fp32 [T, H] (from moe_shared_ffn); the other
+ * arguments as moe_combine.
+ */
+int moe_combine_shared(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                       const float* y_shared, int64_t T, int32_t k, int32_t H, float* out,
+                       void* stream);
 
 /* ------------------------------------------------------- host-side packers */
 
@@ -307,7 +357,8 @@ int moe_quantize_nvfp4(const float* w, int32_t n, int32_t kin,
 
 /*
  * Bytes of one expert record in the device tile layout.
- *   fmt = MOE_FMT_NVFP4 / MOE_FMT_VQ; which = 0 for the gate/up record
+ *   fmt = MOE_FMT_NVFP4 / MOE_FMT_VQ / MOE_FMT_BF16 (MOE_FMT_VQ8: use
+ *   moe_record_bytes_vq8); which = 0 for the gate/up record
  *   (both projections, rows interleaved by 16), 1 for the down record.
  * Returns 0 for an unsupported format or shape.
  */
@@ -352,12 +403,20 @@ int moe_pack_vq8_expert(const uint8_t* gate_codes, const uint16_t* gate_scales,
                         int32_t H, int32_t I, int32_t m, uint8_t* w13_rec, uint8_t* w2_rec);
 
 /*
- * moe_record_table -- [host] fill rec [E] = (fmt << 24) | index(e) from the
- * tier map, and report how many experts each format has (any count pointer
- * may be NULL).  MOE_EUNSUPPORTED on an unknown tag.
+ * moe_pack_bf16_expert -- [host] lay one MOE_FMT_BF16 expert out as its two
+ * records.  gate, up [I, H] and down [H, I]: bf16 bits, row-major.
+ * MOE_EINVAL if a weight is not finite or |w| > 65504 (the kernels use the
+ * weights as fp16).
  */
-int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec,
-                     int32_t* n_nvfp4, int32_t* n_vq, int32_t* n_vq8);
+int moe_pack_bf16_expert(const uint16_t* gate, const uint16_t* up, const uint16_t* down,
+                         int32_t H, int32_t I, uint8_t* w13_rec, uint8_t* w2_rec);
+
+/*
+ * moe_record_table -- [host] fill rec [E] = (fmt << 24) | index(e) from the
+ * tier map, and n_by_fmt [MOE_FMT_MAX + 1] (may be NULL) with the number of
+ * experts of each tag (entry 0 is 0).  MOE_EUNSUPPORTED on an unknown tag.
+ */
+int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* n_by_fmt);
 
 /*
  * moe_record_table_resident -- [host] rec [E] = (fmt << 24) | e for a layer
@@ -373,7 +432,8 @@ int moe_record_table_resident(const uint8_t* fmt_host, int32_t E, int32_t* rec);
  * to fp32 out [n, kin] ([device]; gate/up: [I, H], down: [H, I]) with the
  * same device decode routines the FFN kernels use.  NVFP4 and VQ values are
  * exact; a MOE_FMT_VQ8 value with m = 2 is fp32(fp32(C_0 + C_1) * S) (two
- * roundings; the FFN kernels multiply each codebook row exactly instead).
+ * roundings; the FFN kernels multiply each codebook row exactly instead); a
+ * MOE_FMT_BF16 value is the stored weight as the kernels' fp16 operand.
  */
 int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj,
                   float* out, void* stream);

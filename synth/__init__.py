@@ -87,7 +87,8 @@ class Workload:
     H: int
     I: int
     T: tuple
-    fmt: str            # "nvfp4", "vq", "vq8", "mixed" or "mixed3" (all three)
+    fmt: str            # "nvfp4", "vq", "vq8", "bf16", "mixed" (NVFP4 + VQ), "mixed3"
+                        # (+ VQ8) or "nv_bf16" (NVFP4 + BF16)
     logits: str         # "normal", "uniform", "zipf" or "hot"
     weight_cfg: int = 1     # seed slot of the NVFP4 weights
     vq_cfg: int = 3         # seed slot of the VQ codes/codebooks/scales
@@ -96,6 +97,7 @@ class Workload:
     hot_share: float = 0.0
     zipf_s: float = 0.0
     vq8_m: int = 0          # codes per 8-weight group of the small-codebook VQ
+    shared: bool = False    # the layer has a BF16 shared expert
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
 
@@ -111,15 +113,24 @@ MIXED = Workload("mixed", 4, 256, 8, 6144, 2048, (8, 32), "mixed", "hot",
 VQ1 = Workload("vq1", 5, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=5, vq8_m=1)
 VQ2X8 = Workload("vq2x8", 6, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=6, vq8_m=2)
 
-WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED, VQ1, VQ2X8)}
+# the NVFP4 decode and prefill layers with a BF16 shared expert of the same
+# intermediate size (the routed experts, routing and tokens are those of
+# DECODE / PREFILL: same seed slots)
+DECODE_SHARED = Workload("decode_shared", 1, 256, 8, 6144, 2048, (1, 8, 32), "nvfp4", "uniform",
+                         shared=True)
+PREFILL_SHARED = Workload("prefill_shared", 2, 256, 8, 6144, 2048, (4096,), "nvfp4", "zipf",
+                          zipf_s=1.1, shared=True)
+
+WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED, VQ1, VQ2X8, DECODE_SHARED,
+                                 PREFILL_SHARED)}
 
 
 def small_workload(name, E, k, H, I, T, fmt="nvfp4", logits="normal", cfg=100,
-                   n_nvfp4=0, n_hot=0, hot_share=0.0, zipf_s=0.0, vq8_m=0):
+                   n_nvfp4=0, n_hot=0, hot_share=0.0, zipf_s=0.0, vq8_m=0, shared=False):
     """A property-test workload with its own seed slot."""
     return Workload(name, cfg, E, k, H, I, (T,), fmt, logits, weight_cfg=cfg,
                     vq_cfg=cfg, n_nvfp4=n_nvfp4, n_hot=n_hot, hot_share=hot_share,
-                    zipf_s=zipf_s, vq8_m=vq8_m)
+                    zipf_s=zipf_s, vq8_m=vq8_m, shared=shared)
 
 
 # --------------------------------------------------------------------------
@@ -223,6 +234,12 @@ def nvfp4_source_weights(wl, expert, proj):
     return z * np.float32(0.02)
 
 
+def bf16_weights(wl, expert, proj):
+    """Routed BF16-tier weights: the same N(0, 0.02) source weights as the
+    NVFP4 tier, rounded to bf16 (nearest even), as uint16 bits."""
+    return f32_to_bf16_bits(nvfp4_source_weights(wl, expert, proj))
+
+
 def vq_codes(wl, expert, proj):
     """Uniform uint16 codes [n, kin/8] of one projection of one expert."""
     n, kin = proj_shape(wl, proj)
@@ -288,9 +305,15 @@ def tier_map_hot(wl):
 
 
 def tier_map(wl):
-    """Per-expert format tag (FMT_NVFP4 / FMT_VQ / FMT_VQ8), uint8 [E]."""
+    """Per-expert format tag (FMT_NVFP4 / FMT_VQ / FMT_VQ8 / FMT_BF16), uint8 [E]."""
     if wl.fmt == "nvfp4":
         return np.full(wl.E, FMT_NVFP4, dtype=np.uint8)
+    if wl.fmt == "bf16":
+        return np.full(wl.E, FMT_BF16, dtype=np.uint8)
+    if wl.fmt == "nv_bf16":
+        tm = np.full(wl.E, FMT_BF16, dtype=np.uint8)
+        tm[rng(wl.cfg, KIND_TIER).choice(wl.E, size=wl.n_nvfp4, replace=False)] = FMT_NVFP4
+        return tm
     if wl.fmt == "vq":
         return np.full(wl.E, FMT_VQ, dtype=np.uint8)
     if wl.fmt == "vq8":

@@ -47,8 +47,18 @@ def build_small_layer(wl, device="cuda", resident_formats=None):
         vq_codes=lambda e, p: (synth.vq_codes(wl, e, p), synth.vq_scales(wl, e, p)),
         codebooks=cbs,
         vq8_codes=lambda e, p: (synth.vq8_codes(wl, e, p), synth.vq_scales(wl, e, p)),
-        codebooks8=cbs8, vq8_m=wl.vq8_m, device=device, workers=16,
-        resident_formats=resident_formats)
+        codebooks8=cbs8, vq8_m=wl.vq8_m,
+        bf16_weights=lambda e, p: synth.bf16_weights(wl, e, p),
+        device=device, workers=16, resident_formats=resident_formats)
+
+
+def build_shared_layer(wl, device="cuda"):
+    """The workload's BF16 shared expert as a one-expert QLayer."""
+    from bit_quantized_moe_route_amd.layers import build_layer
+
+    return build_layer(1, wl.H, wl.I, np.array([synth.FMT_BF16], np.uint8),
+                       bf16_weights=lambda e, p: synth.shared_weights_bf16(wl, p),
+                       device=device, workers=1)
 
 
 def oracle_perm(ids, E):

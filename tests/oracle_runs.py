@@ -22,6 +22,8 @@ def expert_weights(wl, e, fmt=None):
         if fmt == synth.FMT_NVFP4:
             c, s = oracle.nvfp4_quantize(synth.nvfp4_source_weights(wl, e, p))
             mats.append(oracle.nvfp4_dequant(c, s))
+        elif fmt == synth.FMT_BF16:
+            mats.append(oracle.bf16_bits_to_f64(synth.bf16_weights(wl, e, p)))
         elif fmt == synth.FMT_VQ8:
             mats.append(oracle.vq8_dequant(synth.vq8_codes(wl, e, p), synth.vq_scales(wl, e, p),
                                            synth.vq8_codebooks(wl, p)))
@@ -29,6 +31,12 @@ def expert_weights(wl, e, fmt=None):
             mats.append(oracle.vq_dequant(synth.vq_codes(wl, e, p), synth.vq_scales(wl, e, p),
                                           synth.vq_codebook(wl, p)))
     return tuple(mats)
+
+
+def shared_weights(wl):
+    """(W_gate, W_up, W_down) float64 of the layer's BF16 shared expert."""
+    return tuple(oracle.bf16_bits_to_f64(synth.shared_weights_bf16(wl, p))
+                 for p in (synth.PROJ_GATE, synth.PROJ_UP, synth.PROJ_DOWN))
 
 
 def expert_rows(args):

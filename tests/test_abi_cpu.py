@@ -204,6 +204,51 @@ def test_vq8_record_layout(m):
     assert moeq.record_bytes(moeq.FMT_VQ8, 0, H, I, 3) == 0
 
 
+@pytest.mark.parametrize("H,I", [(256, 128), (272, 48)])
+def test_bf16_record_layout(H, I):
+    # byte offset of weight (row, k) from the tile layout: 16-row groups, 128
+    # inputs per 4096-byte tile, slice j = (k % 32) // 8 of 1 KB, lane
+    # L = row % 16 + 16 * ((k % 128) // 32), 16 bytes per lane
+    rs = np.random.default_rng(H + I)
+    mats = [synth.f32_to_bf16_bits((rs.standard_normal(sh) * 0.02).astype(np.float32))
+            for sh in [(I, H), (I, H), (H, I)]]
+    w13, w2 = moeq.pack_bf16_expert(mats[0], mats[1], mats[2], H, I)
+    assert w13.size == moeq.record_bytes(moeq.FMT_BF16, 0, H, I) and w13.size % 256 == 0
+    assert w2.size == moeq.record_bytes(moeq.FMT_BF16, 1, H, I)
+    used13 = np.zeros(w13.size // 2, bool)
+    for w, rec, rg_step, rg_off, used in [(mats[0], w13, 2, 0, used13), (mats[1], w13, 2, 1, used13),
+                                          (mats[2], w2, 1, 0, None)]:
+        n, kin = w.shape
+        nkb = (kin + 127) // 128
+        row = np.arange(n)[:, None]
+        k = np.arange(kin)[None, :]
+        g, r = row // 16, row % 16
+        kb, kk = k // 128, k % 128
+        L = r + 16 * (kk // 32)
+        tile = (g * rg_step + rg_off) * nkb + kb
+        off = tile * 4096 + 1024 * ((kk % 32) // 8) + 16 * L + 2 * (kk % 8)
+        assert np.array_equal(rec.view(np.uint16)[off // 2], w)
+        if used is not None:
+            used[(off // 2).ravel()] = True
+    assert np.all(w13.view(np.uint16)[~used13] == 0)       # padding is zero
+
+
+def test_pack_bf16_range():
+    H, I = 32, 16
+    z = np.zeros((I, H), np.uint16)
+    d = np.zeros((H, I), np.uint16)
+    big = z.copy()
+    big[3, 5] = 0x477F                        # 65280: the largest bf16 <= 65504
+    big[4, 6] = 0xC77F
+    moeq.pack_bf16_expert(big, z, d, H, I)
+    for bits in (0x4780, 0xC780, 0x7F80, 0xFF80, 0x7FC0):   # 65536, -65536, inf, -inf, nan
+        bad = z.copy()
+        bad[1, 2] = bits
+        with pytest.raises(moeq.MoeError) as ei:
+            moeq.pack_bf16_expert(z, bad, d, H, I)
+        assert ei.value.status == moeq.MOE_EINVAL
+
+
 def test_record_table_resident():
     tm = np.array([1, 2, 2, 3, 1, 3], np.uint8)
     rec = moeq.record_table_resident(tm)
@@ -216,7 +261,7 @@ def test_record_table_resident():
 def test_record_table():
     tm = synth.tier_map(synth.MIXED)
     rec, counts = moeq.record_table(tm)
-    assert counts == {1: 108, 2: 148, 3: 0}
+    assert counts == {1: 108, 2: 148, 3: 0, 4: 0}
     for fmt in (1, 2):
         sel = np.nonzero(tm == fmt)[0]
         assert np.all(rec[sel] >> 24 == fmt)
@@ -229,8 +274,11 @@ def test_record_table():
         sel = np.nonzero(tm3 == fmt)[0]
         assert np.all(rec[sel] >> 24 == fmt)
         assert np.array_equal(rec[sel] & 0xFFFFFF, np.arange(sel.size))
+    rec, counts = moeq.record_table(np.array([4, 1, 4], np.uint8))
+    assert counts == {1: 1, 2: 0, 3: 0, 4: 2}
+    assert list(rec) == [4 << 24, 1 << 24, (4 << 24) | 1]
     bad = tm.copy()
-    bad[7] = 4
+    bad[7] = 5
     with pytest.raises(moeq.MoeError) as ei:
         moeq.record_table(bad)
     assert ei.value.status == moeq.MOE_EUNSUPPORTED
@@ -269,6 +317,32 @@ def _fake_layer(fmt_host, H=256, I=128):
     for p in range(3):
         d.vq_codebook[p] = 0x100000
     return d
+
+
+def test_shared_ffn_and_combine_shared_host_checks():
+    L = moeq.lib()
+    fake = ctypes.c_void_p(0x1000)
+    N = ctypes.c_void_p(0)
+    d = _fake_layer(np.full(2, moeq.FMT_NVFP4, np.uint8))
+    need = L.moe_shared_ffn_workspace_bytes(ctypes.byref(d), 4)
+    assert need > 0
+    assert L.moe_shared_ffn(ctypes.byref(d), fake, 4, fake, fake, need, N) == moeq.MOE_EINVAL
+    assert b"E == 1" in L.moe_last_error()
+    d = _fake_layer(np.full(1, moeq.FMT_BF16, np.uint8))
+    d.bf16_w13 = d.bf16_w2 = 0x100000
+    d.bf16_w13_stride = d.bf16_w2_stride = 1 << 20
+    assert L.moe_shared_ffn(ctypes.byref(d), N, 0, N, N, 0, N) == moeq.MOE_OK   # T == 0
+    assert L.moe_shared_ffn(ctypes.byref(d), fake, 4, fake, fake, need - 1,
+                            N) == moeq.MOE_EWORKSPACE
+    assert L.moe_shared_ffn(ctypes.byref(d), N, 4, fake, fake, need, N) == moeq.MOE_EINVAL
+    d.bf16_w2 = None
+    assert L.moe_shared_ffn(ctypes.byref(d), fake, 4, fake, fake, need, N) == moeq.MOE_EINVAL
+    d.bf16_w2 = 0x100000
+    d.bf16_w2_stride = 1000
+    assert L.moe_shared_ffn(ctypes.byref(d), fake, 4, fake, fake, need, N) == moeq.MOE_EINVAL
+    assert L.moe_combine_shared(N, N, N, N, 0, 2, 64, N, N) == moeq.MOE_OK
+    assert L.moe_combine_shared(fake, fake, fake, N, 3, 2, 64, fake, N) == moeq.MOE_EINVAL
+    assert L.moe_combine_shared(fake, fake, fake, fake, 3, 2, 66, fake, N) == moeq.MOE_EINVAL
 
 
 def test_ffn_fails_closed_on_unknown_format():

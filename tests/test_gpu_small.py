@@ -10,8 +10,9 @@ import torch
 import bit_quantized_moe_route_amd as moeq
 import oracle
 import synth
-from tests.gpu_common import W_TOL, assert_rows_close, build_small_layer, say
-from tests.oracle_runs import expert_weights
+from tests.gpu_common import (W_TOL, assert_rows_close, build_shared_layer, build_small_layer,
+                               say)
+from tests.oracle_runs import expert_weights, shared_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +47,15 @@ SMALL = {
     "mixed3_prefill": synth.small_workload("mixed3_prefill", E=12, k=3, H=256, I=128, T=260,
                                            fmt="mixed3", logits="hot", cfg=123, n_nvfp4=4,
                                            n_hot=3, hot_share=0.6, vq8_m=1),
+    # BF16 experts (the weights as stored): alone with ragged shapes, beside
+    # NVFP4 ones, and in the grouped-GEMM path next to NVFP4 experts
+    "bf16_ragged": synth.small_workload("bf16_ragged", E=8, k=2, H=272, I=80, T=37, fmt="bf16",
+                                        cfg=140),
+    "nv_bf16": synth.small_workload("nv_bf16", E=16, k=4, H=384, I=96, T=70, fmt="nv_bf16",
+                                    cfg=141, n_nvfp4=8),
+    "nv_bf16_prefill": synth.small_workload("nv_bf16_prefill", E=12, k=3, H=272, I=144, T=260,
+                                            fmt="nv_bf16", logits="zipf", zipf_s=1.1, cfg=142,
+                                            n_nvfp4=6),
 }
 
 _layers = {}
@@ -91,6 +101,23 @@ def test_dequant_vq8(name):
                 assert np.array_equal(got, W[p]), (name, e, p)
             else:
                 assert np.all(np.abs(got - W[p]) <= 2.0 ** -22 * np.abs(W[p])), (name, e, p)
+
+
+@pytest.mark.parametrize("name", ["bf16_ragged", "nv_bf16"])
+def test_dequant_bf16(name):
+    """BF16 decode: the kernels' fp16 operand, i.e. the stored weight rounded
+    to fp16 (nearest even), which is the weight itself for |w| >= 2^-17."""
+    wl = SMALL[name]
+    say("dequant bf16", name)
+    layer = layer_for(name)
+    tm = synth.tier_map(wl)
+    for e in np.flatnonzero(tm == synth.FMT_BF16):
+        W = expert_weights(wl, int(e))
+        for p in range(3):
+            got = to_np(moeq.dequant_q(layer, int(e), p)).astype(np.float64)
+            assert np.array_equal(got, W[p].astype(np.float16).astype(np.float64)), (name, e, p)
+            big = np.abs(W[p]) >= 2.0 ** -17
+            assert np.array_equal(got[big], W[p][big])
 
 
 # ------------------------------------------------------------------ route
@@ -177,6 +204,27 @@ def test_combine(T, k, H):
     y = y_perm.astype(np.float64)[inv_perm].reshape(T, k, H)
     ref = oracle.combine(y, w.astype(np.float32).astype(np.float64))
     assert_rows_close(to_np(out), ref, "combine", tol=1e-5)
+
+
+@pytest.mark.parametrize("T,k,H", [(4, 2, 256), (37, 8, 6144), (5, 16, 64)])
+def test_combine_shared(T, k, H):
+    """combine + the shared expert's output: against the oracle, and bit for
+    bit the fp32 sum of the routed combine and y_shared."""
+    say("combine_shared", T, k, H)
+    g = np.random.default_rng(T + 50)
+    E = max(2 * k, 8)
+    ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)])
+    _, w = oracle.route_topk(g.standard_normal((T, E)).astype(np.float32), k)
+    _, _, perm_src, inv_perm = oracle.permute(ids, E)
+    y_perm = g.standard_normal((T * k, H)).astype(np.float32)
+    y_sh = g.standard_normal((T, H)).astype(np.float32)
+    args = [torch.from_numpy(a).to(DEV) for a in (y_perm, inv_perm, w.astype(np.float32))]
+    ysh = torch.from_numpy(y_sh).to(DEV)
+    out = moeq.combine_shared(*args, ysh)
+    y = y_perm.astype(np.float64)[inv_perm].reshape(T, k, H)
+    ref = oracle.combine_shared(y, w.astype(np.float32).astype(np.float64), y_sh)
+    assert_rows_close(to_np(out), ref, "combine_shared", tol=1e-5)
+    assert torch.equal(out, moeq.combine(*args) + ysh)
 
 
 # ------------------------------------------------------------------ end to end
@@ -300,3 +348,67 @@ def test_tier_switch_between_calls():
             assert np.all(np.abs(got - W[0]) <= 2.0 ** -22 * np.abs(W[0]))
         else:
             assert np.array_equal(got, W[0])
+
+
+# ------------------------------------------------------------------ shared expert
+
+SHARED = {
+    # one token; 37 tokens (three 16-token chunks, ragged H and I); the
+    # grouped-GEMM path with a ragged last 128-token tile; a larger one; a
+    # mixed NVFP4 / VQ routed layer
+    "sh_t1": synth.small_workload("sh_t1", E=8, k=2, H=256, I=128, T=1, cfg=150, shared=True),
+    "sh_ragged": synth.small_workload("sh_ragged", E=16, k=4, H=272, I=80, T=37, cfg=151,
+                                      shared=True),
+    "sh_prefill": synth.small_workload("sh_prefill", E=8, k=2, H=272, I=80, T=300, cfg=152,
+                                       logits="zipf", zipf_s=1.1, shared=True),
+    "sh_prefill_big": synth.small_workload("sh_prefill_big", E=8, k=2, H=512, I=256, T=700,
+                                           cfg=153, shared=True),
+    "sh_mixed": synth.small_workload("sh_mixed", E=24, k=6, H=384, I=96, T=70, fmt="mixed",
+                                     logits="hot", cfg=154, n_nvfp4=9, n_hot=4, hot_share=0.6,
+                                     shared=True),
+}
+
+
+@pytest.mark.parametrize("name", list(SHARED))
+def test_shared_expert_forward(name):
+    """Routed experts + the BF16 shared expert: the shared FFN on every token
+    and the combined output against the oracle."""
+    wl = SHARED[name]
+    T = wl.T[0]
+    say("shared forward", name, T)
+    layer = build_small_layer(wl, DEV)
+    shared = build_shared_layer(wl, DEV)
+    x_bits = synth.activations(wl, T)
+    lg = synth.logits(wl, T)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(DEV)
+    r = moeq.forward(layer, x, torch.from_numpy(lg).to(DEV), wl.k, shared=shared)
+    Ws = shared_weights(wl)
+    assert_rows_close(to_np(r["y_shared"]), oracle.expert_ffn(x_bits, *Ws), name + " y_shared")
+    Wc = {}
+
+    def weights(e):
+        if e not in Wc:
+            Wc[e] = expert_weights(wl, e)
+        return Wc[e]
+    out, ids, w, y = oracle.forward(x_bits, lg, wl.k, weights, shared_weights=Ws)
+    assert np.array_equal(to_np(r["topk_ids"]), ids)
+    assert_rows_close(to_np(r["out"]), out, name + " out")
+    # the shared layer's dequant hook: the stored bf16 weights as fp16
+    for p in range(3):
+        got = to_np(moeq.dequant_q(shared, 0, p)).astype(np.float64)
+        assert np.array_equal(got, Ws[p].astype(np.float16).astype(np.float64))
+
+
+def test_shared_ffn_matches_routed_call():
+    """moe_shared_ffn is moe_expert_ffn_q with the identity map: the two give
+    the same bits."""
+    wl = SHARED["sh_ragged"]
+    T = wl.T[0]
+    say("shared = identity-routed", T)
+    shared = build_shared_layer(wl, DEV)
+    x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(DEV)
+    perm = torch.arange(T, dtype=torch.int32, device=DEV)
+    offs = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    a = moeq.shared_ffn(shared, x)
+    b = moeq.expert_ffn_q(shared, x, perm, offs, 1)
+    assert torch.equal(a, b)
