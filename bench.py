@@ -20,8 +20,9 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   extra          the same path on the other workloads (decode T = 1 and 8,
                  prefill T = 4096 with Zipf(1.1) routing, 2-bit VQ T = 8,
                  small-codebook VQ at 1 and 2 bits per weight T = 8,
-                 mixed NVFP4/VQ T = 8 and 32, and the same mixed layer with
-                 its hot experts switched to the NVFP4 tier at run time)
+                 mixed NVFP4/VQ T = 8 and 32, the same mixed layer with
+                 its hot experts switched to the NVFP4 tier at run time, and
+                 the decode and prefill layers with a BF16 shared expert)
 """
 
 import argparse
@@ -73,7 +74,7 @@ def read_traffic(name):
 class Runner:
     """Pre-allocated buffers and a pool of input batches for one workload."""
 
-    def __init__(self, layer, wl, T, reps, dev):
+    def __init__(self, layer, wl, T, reps, dev, shared=None):
         import numpy as np
         import torch
         import bit_quantized_moe_route_amd as moeq
@@ -102,7 +103,12 @@ class Runner:
         self.out = torch.empty((T, H), dtype=f32, device=dev)
         self.ws = moeq.gateup_workspace(layer, T)
         self.pws = moeq.permute_workspace(T, k, E, dev)
+        self.shared = shared
+        if shared is not None:
+            self.y_sh = torch.empty((T, H), dtype=f32, device=dev)
+            self.sws = moeq.shared_workspace(shared, T)
         self.ev = []
+        self.ev_sh = []
 
     def step(self, r, timed):
         moeq = self.moeq
@@ -127,7 +133,18 @@ class Runner:
         else:
             moeq.expert_gateup_q(self.layer, x, perm_src, offsets, self.k, self.h, self.ws)
         moeq.expert_down_q(self.layer, self.h, offsets, self.k, self.y)
-        moeq.combine(self.y, inv_perm, self.w, self.out)
+        if self.shared is None:
+            moeq.combine(self.y, inv_perm, self.w, self.out)
+            return
+        if timed:
+            e0 = self.torch.cuda.Event(enable_timing=True)
+            e1 = self.torch.cuda.Event(enable_timing=True)
+            e0.record()
+        moeq.shared_ffn(self.shared, x, self.y_sh, self.sws)
+        if timed:
+            e1.record()
+            self.ev_sh.append((r, e0, e1))
+        moeq.combine_shared(self.y, inv_perm, self.w, self.y_sh, self.out)
 
     def run(self, steps, warmup):
         torch = self.torch
@@ -135,6 +152,7 @@ class Runner:
             self.step(i, False)
         torch.cuda.synchronize()
         self.ev = []
+        self.ev_sh = []
         t0 = time.perf_counter()
         for i in range(steps):
             self.step(warmup + i, True)
@@ -175,7 +193,8 @@ class Runner:
         of every touched expert, VQ codebooks once) or 'gateup'."""
         experts = self.touched[r % len(self.touched)]
         if which == "all":
-            return self.layer.packed_bytes(experts)
+            sh = self.shared.packed_bytes([0]) if self.shared is not None else 0
+            return self.layer.packed_bytes(experts) + sh
         H, I = self.wl.H, self.wl.I
         tot = 0
         for e in experts:
@@ -188,11 +207,13 @@ class Runner:
         return tot
 
 
-def measure(layer, wl, T, steps, warmup, dev, reps=16):
+def measure(layer, wl, T, steps, warmup, dev, reps=16, shared=None):
     """Eager launches (per-launch HIP events around the gate/up call), then
     the same steps replayed from HIP graphs; the headline figures are the
-    graph replay's, the kernel-level ones the eager run's."""
-    rn = Runner(layer, wl, T, reps, dev)
+    graph replay's, the kernel-level ones the eager run's.  A shared expert
+    runs after the routed experts on the same stream (its HIP events bracket
+    its three launches)."""
+    rn = Runner(layer, wl, T, reps, dev, shared)
     dte, gu_ms = rn.run(steps, warmup)
     dt, group = rn.run_graph(steps, warmup)
     idx = list(range(steps))                    # batches of the timed graph replays
@@ -214,10 +235,18 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16):
         "gateup_GBps": gu_bytes / gu_s / 1e9,
         "gateup_bytes_per_launch": gu_bytes / steps,
     }
+    if shared is not None:
+        sh_ms = [e0.elapsed_time(e1) for _, e0, e1 in rn.ev_sh]
+        sh_bytes = shared.packed_bytes([0])
+        res["shared_ms_mean"] = sum(sh_ms) / len(sh_ms)
+        res["shared_GBps"] = sh_bytes / (res["shared_ms_mean"] / 1e3) / 1e9
+        res["shared_bytes"] = sh_bytes
     if T >= 1024:
-        flops = 6.0 * wl.H * wl.I * T * wl.k
+        flops = 6.0 * wl.H * wl.I * T * (wl.k + (1 if shared is not None else 0))
         res["TFLOPs"] = flops / (dt / steps) / 1e12
         res["frac_mfma"] = res["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+        if shared is not None:
+            res["shared_TFLOPs"] = 6.0 * wl.H * wl.I * T / (res["shared_ms_mean"] / 1e3) / 1e12
     return res
 
 
@@ -295,7 +324,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--T", type=int, default=32, help="decode batch of the headline")
     ap.add_argument("--extra",
-                    default="decode1,decode8,prefill,vq,vq1,vq2x8,mixed8,mixed32,mixedhot8,mixedhot32",
+                    default="decode1,decode8,prefill,vq,vq1,vq2x8,mixed8,mixed32,mixedhot8,"
+                            "mixedhot32,shared1,shared8,shared32,prefillshared",
                     help="comma list of other workloads to measure ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy", action="store_true",
@@ -349,7 +379,23 @@ def main():
     layers = {}
     for name in wanted:
         try:
-            if name.startswith("decode"):
+            if name.startswith("shared") or name == "prefillshared":
+                # the NVFP4 layer (same routed experts, routing and tokens) with
+                # a BF16 shared expert of intermediate size I
+                ws_ = synth.PREFILL_SHARED if name == "prefillshared" else synth.DECODE_SHARED
+                if "shared" not in layers:
+                    log("building the BF16 shared expert ...")
+                    layers["shared"] = build_layer(
+                        1, ws_.H, ws_.I, np.array([moeq.FMT_BF16], np.uint8),
+                        bf16_weights=lambda e, p: synth.shared_weights_bf16(synth.DECODE_SHARED, p),
+                        device=dev, workers=1)
+                if name == "prefillshared":
+                    extra[name] = measure(nv_layer, ws_, 4096, 5, 2, dev, reps=4,
+                                          shared=layers["shared"])
+                else:
+                    T = int(name[len("shared"):])
+                    extra[name] = measure(nv_layer, ws_, T, 30, 5, dev, shared=layers["shared"])
+            elif name.startswith("decode"):
                 T = int(name[len("decode"):])
                 extra[name] = measure(nv_layer, wl, T, 30, 5, dev)
             elif name == "prefill":
@@ -432,7 +478,8 @@ def main():
                    "experts_touched_mean": head["experts_touched_mean"],
                    "parallelism": "1 GPU"},
         "packed_GBps": head["packed_GBps"],
-        "roofline": {"bound": "hbm", "kernel": "k_ffn<NvFmt, 1, 1, 2, 0, 4> (NVFP4 gate/up + SwiGLU)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_ffn<NvFmt, 1, 1, 2, 0, 4, false> (NVFP4 gate/up + SwiGLU)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": head["gateup_bytes_per_launch"],

@@ -597,10 +597,38 @@ def dequant_q(layer, expert, proj):
     return out
 
 
-def forward(layer, x, logits, k, shared=None):
+_side_streams = {}
+
+
+def side_stream(device):
+    """A second stream of `device` (default priority), for the shared expert,
+    which depends on x only and so can run beside the routed experts."""
+    torch = _torch()
+    d = torch.device(device)
+    key = d.index if d.index is not None else torch.cuda.current_device()
+    if key not in _side_streams:
+        _side_streams[key] = torch.cuda.Stream(device=d)
+    return _side_streams[key]
+
+
+def forward(layer, x, logits, k, shared=None, overlap=False):
     """route -> permute -> expert FFN -> combine (+ the shared expert's output
-    when `shared`, a one-expert QLayer, is given).  Returns a dict of every
-    intermediate (device tensors)."""
+    when `shared`, a one-expert QLayer, is given).  With overlap, the shared
+    expert runs on side_stream(), forked from and joined back into the current
+    stream (so the call stays stream-ordered and can be graph-captured), while
+    the routed experts run on the current stream.  (Measured on MI355X: no
+    faster in a graph, whose replay ran both branches on one queue, and slower
+    eagerly, so it is off by default.)  Returns a dict of every intermediate
+    (device tensors)."""
+    torch = _torch()
+    if shared is not None:
+        main = torch.cuda.current_stream(x.device)
+        y_sh = torch.empty((x.shape[0], shared.H), dtype=torch.float32, device=x.device)
+        sws = shared_workspace(shared, x.shape[0])
+        side = side_stream(x.device) if overlap else main
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            shared_ffn(shared, x, y_sh, sws)
     ids, w, counts, offsets, perm_src, inv_perm = route_permute(logits, k, layer.E)
     y_perm = expert_ffn_q(layer, x, perm_src, offsets, k)
     r = dict(topk_ids=ids, topk_w=w, counts=counts, offsets=offsets, perm_src=perm_src,
@@ -608,6 +636,7 @@ def forward(layer, x, logits, k, shared=None):
     if shared is None:
         r["out"] = combine(y_perm, inv_perm, w)
     else:
-        r["y_shared"] = shared_ffn(shared, x)
-        r["out"] = combine_shared(y_perm, inv_perm, w, r["y_shared"])
+        main.wait_stream(side)
+        r["y_shared"] = y_sh
+        r["out"] = combine_shared(y_perm, inv_perm, w, y_sh)
     return r

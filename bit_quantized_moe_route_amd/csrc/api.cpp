@@ -122,12 +122,18 @@ size_t ffn_ws(const moe_qlayer* L, int64_t T, int32_t k) {
     return align_up((size_t)T * L->H * 2) + align_up((size_t)T * k * L->I * 2);
 }
 
+// moe_shared_ffn: x16 | h16 | the gate/up partial sums of the decode path.
+size_t shared_ws(const moe_qlayer* L, int64_t T) {
+    return ffn_ws(L, T, 1) + align_up(shared_part_bytes(T, L->I));
+}
+
 // Gate/up + SwiGLU of every format present.  perm_src == offsets == NULL is
-// the identity map of a one-expert layer (k = 1).  x16 [T, H] is workspace
-// for the fp16 copy of x that the grouped-GEMM kernels stage through LDS.
+// the identity map of a one-expert layer (k = 1; part: the decode path's
+// partial sums).  x16 [T, H] is workspace for the fp16 copy of x that the
+// grouped-GEMM kernels stage through LDS.
 int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_src,
                const int32_t* offsets, int64_t T, int32_t k, uint16_t* h_f16, uint16_t* x16,
-               void* stream) {
+               float* part, void* stream) {
     const bool prefill = T >= kPrefillMinTokens;
     bool need_x16 = false;
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt)
@@ -142,8 +148,10 @@ int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_
             prefill && prefill_fmt(fmt)
                 ? launch_ffn_prefill(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T, k,
                                      h_f16, nullptr, 0, stream)
-                : launch_ffn_decode(li.view, fmt, li.count[fmt], x_bf16, perm_src, offsets, T, k,
-                                    h_f16, nullptr, 0, stream);
+            : offsets ? launch_ffn_decode(li.view, fmt, li.count[fmt], x_bf16, perm_src, offsets,
+                                          T, k, h_f16, nullptr, 0, stream)
+                      : launch_shared_decode(li.view, fmt, x_bf16, T, h_f16, part, nullptr, 0,
+                                             stream);
         if (st) return st;
     }
     return MOE_OK;
@@ -156,11 +164,14 @@ int run_down(const LayerInfo& li, const uint16_t* h_f16, const int32_t* offsets,
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!li.count[fmt]) continue;
         uint16_t* h = const_cast<uint16_t*>(h_f16);
-        const int st = prefill && prefill_fmt(fmt)
-                           ? launch_ffn_prefill(li.view, fmt, li.count[fmt], nullptr, nullptr,
-                                                offsets, T, k, h, y_perm, 1, stream)
-                           : launch_ffn_decode(li.view, fmt, li.count[fmt], nullptr, nullptr,
-                                               offsets, T, k, h, y_perm, 1, stream);
+        const int st =
+            prefill && prefill_fmt(fmt)
+                ? launch_ffn_prefill(li.view, fmt, li.count[fmt], nullptr, nullptr, offsets, T, k,
+                                     h, y_perm, 1, stream)
+            : offsets ? launch_ffn_decode(li.view, fmt, li.count[fmt], nullptr, nullptr, offsets,
+                                          T, k, h, y_perm, 1, stream)
+                      : launch_shared_decode(li.view, fmt, nullptr, T, h, nullptr, y_perm, 1,
+                                             stream);
         if (st) return st;
     }
     return MOE_OK;
@@ -270,7 +281,7 @@ int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16, const i
     // the grouped-GEMM kernels stage fp16 tokens through LDS: convert x once;
     // the decode kernels convert each fragment they read
     return run_gateup(li, x_bf16, perm_src, offsets, T, k, h_f16, static_cast<uint16_t*>(ws),
-                      stream);
+                      nullptr, stream);
 }
 
 int moe_expert_down_q(const moe_qlayer* layer, const uint16_t* h_f16, const int32_t* offsets,
@@ -314,7 +325,7 @@ int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16, const int3
 
 size_t moe_shared_ffn_workspace_bytes(const moe_qlayer* shared, int64_t T) {
     if (!shared || T < 0 || shared->H <= 0 || shared->I <= 0) return 0;
-    return ffn_ws(shared, T, 1);
+    return shared_ws(shared, T);
 }
 
 int moe_shared_ffn(const moe_qlayer* shared, const uint16_t* x_bf16, int64_t T,
@@ -328,7 +339,7 @@ int moe_shared_ffn(const moe_qlayer* shared, const uint16_t* x_bf16, int64_t T,
     if (st) return st;
     if (T == 0) return MOE_OK;
     if (!x_bf16 || !y_shared) return fail(MOE_EINVAL, "moe_shared_ffn: null pointer");
-    const size_t need = ffn_ws(shared, T, 1);
+    const size_t need = shared_ws(shared, T);
     if (!ws || ws_bytes < need)
         return fail(MOE_EWORKSPACE,
                     "moe_shared_ffn: workspace needs " + std::to_string(need) + " bytes");
@@ -337,7 +348,8 @@ int moe_shared_ffn(const moe_qlayer* shared, const uint16_t* x_bf16, int64_t T,
     uint8_t* w = static_cast<uint8_t*>(ws);
     uint16_t* x16 = reinterpret_cast<uint16_t*>(w);
     uint16_t* h16 = reinterpret_cast<uint16_t*>(w + align_up((size_t)T * shared->H * 2));
-    st = run_gateup(li, x_bf16, nullptr, nullptr, T, 1, h16, x16, stream);
+    float* part = reinterpret_cast<float*>(w + ffn_ws(shared, T, 1));
+    st = run_gateup(li, x_bf16, nullptr, nullptr, T, 1, h16, x16, part, stream);
     if (st) return st;
     return run_down(li, h16, nullptr, T, 1, y_shared, stream);
 }

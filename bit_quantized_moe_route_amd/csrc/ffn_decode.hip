@@ -169,6 +169,8 @@ struct DecodeArgs {
     float* y_perm;
     int E, H, I, k, fmt;
     int rows;              // offsets == NULL: rows of the identity map
+    int nsplit;            // PART kernels: workgroups splitting the input dimension
+    float* part;           // PART kernels: fp32 [nsplit][rows][2I] partial g | u
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -381,6 +383,13 @@ constexpr int kRpwDown = 4;
 #define MOEQ_PREFETCH 1
 #endif
 constexpr int kPrefetch = MOEQ_PREFETCH;
+// ... for the one expert of a shared-expert layer, whose waves have only a
+// few tiles each (the whole expert is spread over the chip).  (Measured: 2
+// and 3 are no faster at one token and spill at 32.)
+#ifndef MOEQ_SH_PREFETCH
+#define MOEQ_SH_PREFETCH 1
+#endif
+constexpr int kPrefetchShared = MOEQ_SH_PREFETCH;
 // Waves per SIMD the register budget is sized for (latency hiding).
 #ifndef MOEQ_MIN_WAVES
 #define MOEQ_MIN_WAVES 2
@@ -395,8 +404,12 @@ constexpr int kMinWaves = MOEQ_MIN_WAVES;
 // grid: x = sets of (4/KS) waves' rows, y = active-expert slot, z = chunk of
 // 16*NTT rows of the expert.
 // ID: offsets / perm_src are the identity map of a one-expert layer (a
-// shared expert: its rows are the tokens).
-template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID>
+// shared expert: its rows are the tokens).  PART (gate/up only): the input
+// dimension is also split over A.nsplit workgroups (blockIdx.x % nsplit),
+// which write fp32 partial g and u to A.part instead of h; k_swiglu_parts
+// sums them and applies SwiGLU.  (One expert alone has too few row groups to
+// fill the chip.)
+template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID, bool PART = false>
 __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
     constexpr int NM = PHASE == 0 ? 2 * RPW : RPW;   // weight tiles per input tile
     constexpr int SETS = WV / KS;                    // row sets per workgroup
@@ -423,8 +436,11 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
         }
         __syncthreads();
     }
-    const int set = blockIdx.x * SETS + wave / KS;   // row set of this wave
-    const int kpart = wave % KS;
+    const int kloc = wave % KS;                      // part of the workgroup's inputs
+    const int split = PART ? (int)blockIdx.x % A.nsplit : 0;
+    const int set = (PART ? (int)blockIdx.x / A.nsplit : (int)blockIdx.x) * SETS + wave / KS;
+    const int kpart = split * KS + kloc;             // first input tile of this wave
+    const int kstride = PART ? KS * A.nsplit : KS;   // ... and the stride between its tiles
     const int K = PHASE == 0 ? A.H : A.I;
     const int nrg = (PHASE == 0 ? A.I : A.H) / 16;   // row (pair) groups
     const int g0 = set * RPW;                        // first row (pair) group
@@ -465,19 +481,19 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
 #pragma unroll
             for (int m = 0; m < NM; ++m)
                 lcb[m] = lds_cb + (PHASE == 0 ? (m & 1) : 0) * (F::CODES * MOE_VQ8_NCODE * 8);
-            stream_tiles_vq8<NTT, NM, F::CODES, PHASE == 0>(tb, lcb, xrow, ntt, K, kpart, KS,
-                                                            lane, acc);
+            stream_tiles_vq8<NTT, NM, F::CODES, PHASE == 0>(tb, lcb, xrow, ntt, K, kpart,
+                                                            kstride, lane, acc);
         } else if constexpr (F::kVq && MOEQ_VQ_GATHER_AHEAD) {
             // row c0 of the expert exists: a safe row for lanes past its rows
             const uint16_t* xsafe =
                 PHASE == 0
                     ? A.xbf + (int64_t)(ID ? c0 : A.perm_src[ae.r0 + c0] / A.k) * A.H
                     : reinterpret_cast<const uint16_t*>(A.h16) + (int64_t)(ae.r0 + c0) * A.I;
-            stream_tiles_vq<NTT, NM, PHASE == 0>(tb, cb, xrow, xsafe, ntt, K, kpart, KS, lane,
-                                                 acc);
+            stream_tiles_vq<NTT, NM, PHASE == 0>(tb, cb, xrow, xsafe, ntt, K, kpart, kstride,
+                                                 lane, acc);
         } else {
-            stream_tiles<F, NTT, NM, kPrefetch, PHASE == 0>(tb, cb, xrow, ntt, K, kpart, KS, lane,
-                                                            acc);
+            stream_tiles<F, NTT, NM, ID ? kPrefetchShared : kPrefetch, PHASE == 0>(
+                tb, cb, xrow, ntt, K, kpart, kstride, lane, acc);
         }
     }
 
@@ -491,14 +507,14 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
 #pragma unroll
             for (int m = 0; m < NM; ++m) red[wave][m][lane] = acc[m][tt];
             __syncthreads();
-            if (kpart == 0) {
+            if (kloc == 0) {
 #pragma unroll
                 for (int w = 1; w < KS; ++w)
 #pragma unroll
                     for (int m = 0; m < NM; ++m) acc[m][tt] = acc[m][tt] + red[wave + w][m][lane];
             }
         }
-        if (kpart != 0) return;
+        if (kloc != 0) return;
     }
     const int r4 = (lane >> 4) * 4;
 #pragma unroll
@@ -516,6 +532,26 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
                     sg[i] = (float)sp[n0 + i];
                     su[i] = (float)sp[A.I + n0 + i];
                 }
+            }
+            if constexpr (PART) {
+                // fp32 partial sums of this workgroup's inputs: g at [.., n],
+                // u at [.., I + n] of row (split, c)
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) {
+                    const int c = c0 + (lane & 15) + 16 * tt;
+                    if (tt < ntt && c < ae.me) {
+                        f32x4 g, u;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            g[i] = acc[2 * q][tt][i] * sg[i];
+                            u[i] = acc[2 * q + 1][tt][i] * su[i];
+                        }
+                        float* pp = A.part + ((int64_t)split * A.rows + c) * (2 * A.I) + n0;
+                        *reinterpret_cast<f32x4*>(pp) = g;
+                        *reinterpret_cast<f32x4*>(pp + A.I) = u;
+                    }
+                }
+                continue;
             }
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
@@ -552,6 +588,27 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
 }
 
 
+// h[c, n..n+3] = silu(g) * u with g, u the sums over the nsplit partials in
+// ascending split order (one thread per 4 channels of a row).
+__global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ part, int nsplit,
+                                                      int rows, int I, _Float16* __restrict__ h16) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nq = I / 4;
+    if (i >= (int64_t)rows * nq) return;
+    const int c = (int)(i / nq);
+    const int n = (int)(i % nq) * 4;
+    f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < nsplit; ++sp) {
+        const float* pp = part + ((int64_t)sp * rows + c) * (2 * I) + n;
+        g = g + *reinterpret_cast<const f32x4*>(pp);
+        u = u + *reinterpret_cast<const f32x4*>(pp + I);
+    }
+    f16x4 h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) h[q] = (_Float16)silu_mul(g[q], u[q]);
+    *reinterpret_cast<f16x4*>(h16 + (int64_t)c * I + n) = h;
+}
+
 template <class F>
 constexpr size_t codebook_lds_bytes(int phase) {
     if constexpr (F::kVq8)
@@ -560,18 +617,19 @@ constexpr size_t codebook_lds_bytes(int phase) {
         return 0;
 }
 
-template <class F, int NTT, int KS, int WV, bool ID>
+template <class F, int NTT, int KS, int WV>
 int launch_ks(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
     constexpr int SETS = WV / KS;
     if (phase == 0) {
         const int nsets = (a.I / 16 + kRpwGateup - 1) / kRpwGateup;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
-        k_ffn<F, NTT, KS, kRpwGateup, 0, WV, ID>
+        k_ffn<F, NTT, KS, kRpwGateup, 0, WV, false>
             <<<grid, 64 * WV, codebook_lds_bytes<F>(0), s>>>(a);
     } else {
         const int nsets = (a.H / 16 + kRpwDown - 1) / kRpwDown;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
-        k_ffn<F, NTT, KS, kRpwDown, 1, WV, ID><<<grid, 64 * WV, codebook_lds_bytes<F>(1), s>>>(a);
+        k_ffn<F, NTT, KS, kRpwDown, 1, WV, false>
+            <<<grid, 64 * WV, codebook_lds_bytes<F>(1), s>>>(a);
     }
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
@@ -580,13 +638,88 @@ int launch_ks(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t
 // Few active experts -> split the input dimension over more waves so the
 // whole chip streams; many -> one wave per row set.  (An 8-way split in
 // 8-wave workgroups measured slower at one token than this 4-way split.)
-// (The identity map of a one-expert layer has one slot.)
 template <class F, int NTT>
 int launch_fmt(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
-    if (a.offsets == nullptr) return launch_ks<F, NTT, 4, 4, true>(a, 1, chunks, phase, s);
-    if (slots <= 16) return launch_ks<F, NTT, 4, 4, false>(a, slots, chunks, phase, s);
-    if (slots <= 64) return launch_ks<F, NTT, 2, 4, false>(a, slots, chunks, phase, s);
-    return launch_ks<F, NTT, 1, 4, false>(a, slots, chunks, phase, s);
+    if (slots <= 16) return launch_ks<F, NTT, 4, 4>(a, slots, chunks, phase, s);
+    if (slots <= 64) return launch_ks<F, NTT, 2, 4>(a, slots, chunks, phase, s);
+    return launch_ks<F, NTT, 1, 4>(a, slots, chunks, phase, s);
+}
+
+// The identity map of a one-expert layer (a shared expert): one 16-row group
+// (pair) per wave, 4 waves splitting the inputs of a workgroup, and for
+// gate/up a further split of the inputs over nsplit workgroups (partials
+// summed by k_swiglu_parts), so that one expert's rows fill the chip.  Up to
+// 16 NTT tokens per wave pass (NTT = 2 for batches past 16 tokens, 1 for
+// VQ8, whose LDS lookups need the registers; more tokens take further chunks
+// of the grid's z dimension).
+#ifndef MOEQ_SH_KS13
+#define MOEQ_SH_KS13 4      // waves of a workgroup splitting the gate/up inputs
+#endif
+#ifndef MOEQ_SH_RPW13
+#define MOEQ_SH_RPW13 1     // gate/up row-pair groups per wave
+#endif
+#ifndef MOEQ_SH_KS2
+#define MOEQ_SH_KS2 4
+#endif
+#ifndef MOEQ_SH_RPW2
+#define MOEQ_SH_RPW2 2      // down row groups per wave
+#endif
+#ifndef MOEQ_SH_NTT
+#define MOEQ_SH_NTT 2       // largest token tile count per wave pass
+#endif
+#ifndef MOEQ_SH_WV13
+#define MOEQ_SH_WV13 4      // waves per gate/up workgroup
+#endif
+#ifndef MOEQ_SH_WV2
+#define MOEQ_SH_WV2 4
+#endif
+#ifndef MOEQ_SH_PART
+#define MOEQ_SH_PART 1      // split the gate/up inputs over workgroups too
+#endif
+template <class F, int NTT>
+int launch_shared_ntt(DecodeArgs a, int phase, hipStream_t s) {
+    const int chunks = (a.rows + 16 * NTT - 1) / (16 * NTT);
+    if (phase == 0) {
+        constexpr int KS = MOEQ_SH_KS13, RPW = MOEQ_SH_RPW13, WV = MOEQ_SH_WV13, SETS = WV / KS;
+        const int nsets = (a.I / 16 + RPW - 1) / RPW;
+        const int nblk = (nsets + SETS - 1) / SETS;
+        if constexpr (MOEQ_SH_PART) {
+            const int nkb = (a.H + F::TK - 1) / F::TK;
+            int nsplit = (kSharedTargetBlocks + nblk - 1) / nblk;
+            nsplit = nsplit < kSharedMaxSplit ? nsplit : kSharedMaxSplit;
+            nsplit = nsplit <= nkb / KS ? nsplit : (nkb / KS > 1 ? nkb / KS : 1);
+            a.nsplit = nsplit;
+            dim3 grid((unsigned)(nblk * nsplit), 1u, (unsigned)chunks);
+            k_ffn<F, NTT, KS, RPW, 0, WV, true, true>
+                <<<grid, 64 * WV, codebook_lds_bytes<F>(0), s>>>(a);
+            MOEQ_CHECK_LAUNCH();
+            const int64_t n = (int64_t)a.rows * (a.I / 4);
+            k_swiglu_parts<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.part, nsplit, a.rows,
+                                                                       a.I, a.h16);
+        } else {
+            dim3 grid((unsigned)nblk, 1u, (unsigned)chunks);
+            k_ffn<F, NTT, KS, RPW, 0, WV, true, false>
+                <<<grid, 64 * WV, codebook_lds_bytes<F>(0), s>>>(a);
+        }
+    } else {
+        constexpr int KS = MOEQ_SH_KS2, RPW = MOEQ_SH_RPW2, WV = MOEQ_SH_WV2, SETS = WV / KS;
+        const int nsets = (a.H / 16 + RPW - 1) / RPW;
+        dim3 grid((unsigned)((nsets + SETS - 1) / SETS), 1u, (unsigned)chunks);
+        k_ffn<F, NTT, KS, RPW, 1, WV, true, false>
+            <<<grid, 64 * WV, codebook_lds_bytes<F>(1), s>>>(a);
+    }
+    MOEQ_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+template <class F>
+int launch_shared_fmt(const DecodeArgs& a, int phase, hipStream_t s) {
+    if constexpr (F::kVq8) {
+        return launch_shared_ntt<F, 1>(a, phase, s);
+    } else {
+        if (MOEQ_SH_NTT < 2 || a.rows <= 16) return launch_shared_ntt<F, 1>(a, phase, s);
+        return launch_shared_ntt<F, MOEQ_SH_NTT < 2 ? 1 : 2>(a, phase, s);
+    }
 }
 
 template <class F>
@@ -597,12 +730,9 @@ int launch_ntt(const DecodeArgs& a, int64_t T, int slots, int phase, hipStream_t
     return launch_fmt<F, 1>(a, slots, chunks, phase, s);
 }
 
-}  // namespace
-
-int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,
-                      const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
-                      uint16_t* h16, float* y_perm, int phase, void* stream) {
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+DecodeArgs decode_args(const LayerView& L, int fmt, const uint16_t* x_bf16,
+                       const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
+                       uint16_t* h16, float* y_perm) {
     DecodeArgs a;
     a.pool13 = L.pool13[fmt];
     a.pool2 = L.pool2[fmt];
@@ -625,6 +755,18 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
     a.k = k;
     a.fmt = fmt;
     a.rows = (int)T;
+    a.nsplit = 1;
+    a.part = nullptr;
+    return a;
+}
+
+}  // namespace
+
+int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,
+                      const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
+                      uint16_t* h16, float* y_perm, int phase, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const DecodeArgs a = decode_args(L, fmt, x_bf16, perm_src, offsets, T, k, h16, y_perm);
     const int64_t tk = T * k;
     const int slots = (int)(tk < n_fmt ? tk : n_fmt);
     if (slots == 0) return MOE_OK;
@@ -635,6 +777,25 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
         return launch_ntt<Vq8Fmt<2>>(a, T, slots, phase, s);
     }
     return launch_ntt<VqFmt>(a, T, slots, phase, s);
+}
+
+}  // namespace moeq
+
+namespace moeq {
+
+int launch_shared_decode(const LayerView& L, int fmt, const uint16_t* x_bf16, int64_t T,
+                         uint16_t* h16, float* part, float* y, int phase, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    DecodeArgs a = decode_args(L, fmt, x_bf16, nullptr, nullptr, T, 1, h16, y);
+    a.part = part;
+    if (T == 0) return MOE_OK;
+    if (fmt == MOE_FMT_NVFP4) return launch_shared_fmt<NvFmt>(a, phase, s);
+    if (fmt == MOE_FMT_BF16) return launch_shared_fmt<Bf16Fmt>(a, phase, s);
+    if (fmt == MOE_FMT_VQ8) {
+        if (L.vq8_m == 1) return launch_shared_fmt<Vq8Fmt<1>>(a, phase, s);
+        return launch_shared_fmt<Vq8Fmt<2>>(a, phase, s);
+    }
+    return launch_shared_fmt<VqFmt>(a, phase, s);
 }
 
 }  // namespace moeq

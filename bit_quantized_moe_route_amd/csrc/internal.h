@@ -94,14 +94,26 @@ int launch_combine(const float* y_perm, const int32_t* inv_perm, const float* w,
                    const float* y_shared, int64_t T, int32_t k, int32_t H, float* out,
                    void* stream);
 int launch_x_to_f16(const uint16_t* x, int64_t n, uint16_t* x16, void* stream);
-// perm_src == NULL and offsets == NULL: the identity map of a one-expert
-// layer (rows 0 .. T-1 of expert 0 are tokens 0 .. T-1, k = 1).
 int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,
                       const int32_t* perm_src, const int32_t* offsets, int64_t T,
                       int32_t k, uint16_t* h16, float* y_perm, int phase,
                       void* stream);
+// The one expert of a shared-expert layer through the identity map (rows
+// 0 .. T-1 are tokens 0 .. T-1): phase 0 writes fp32 partial g | u to part
+// (shared_part_bytes) and then h, phase 1 writes y [T, H].
+#ifndef MOEQ_SH_TARGET
+#define MOEQ_SH_TARGET 512
+#endif
+constexpr int kSharedMaxSplit = 16;                  // workgroups splitting the gate/up inputs
+constexpr int kSharedTargetBlocks = MOEQ_SH_TARGET;  // gate/up workgroups aimed for
+inline size_t shared_part_bytes(int64_t T, int32_t I) {
+    return (size_t)kSharedMaxSplit * (size_t)T * 2 * (size_t)I * 4;
+}
+int launch_shared_decode(const LayerView& L, int fmt, const uint16_t* x_bf16, int64_t T,
+                         uint16_t* h16, float* part, float* y, int phase, void* stream);
 // NVFP4 and BF16 experts at T >= kPrefillMinTokens use the grouped-GEMM
-// kernels.
+// kernels (perm_src == offsets == NULL: the identity map of a one-expert
+// layer).
 constexpr int64_t kPrefillMinTokens = 128;
 inline bool prefill_fmt(int fmt) { return fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16; }
 int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,

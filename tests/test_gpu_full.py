@@ -232,3 +232,51 @@ def test_mixed_full_sampled(T):
     say(f"mixed T={T}: hot share {share:.3f}, hot NVFP4 experts "
         f"{int((fmt_host[hot] == synth.FMT_NVFP4).sum())}/{len(hot)}")
     assert 0.35 < share < 0.85
+
+
+# ------------------------------------------------------------------ shared expert
+
+_shared = {}
+
+
+def shared_layer(wl):
+    if wl.name not in _shared:
+        from tests.gpu_common import build_shared_layer
+        say("building full shared expert", wl.name)
+        _shared[wl.name] = build_shared_layer(wl, DEV)
+    return _shared[wl.name]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,T", [("decode_shared", 1), ("decode_shared", 32),
+                                    ("prefill_shared", 4096)])
+def test_shared_expert_full(name, T):
+    """The BF16 shared expert (H 6144, I 2048) beside the full NVFP4 layer, in
+    the benchmark's configurations: its output rows against the oracle (all
+    rows in decode, a sample spanning every 128-token tile in prefill), and the
+    combined output through the combine property plus y_shared."""
+    from tests.oracle_runs import shared_weights
+    wl = synth.WORKLOADS[name]
+    say("shared full", name, T)
+    lay = layer("decode")                   # the same routed NVFP4 layer
+    sh = shared_layer(wl)
+    x_bits = synth.activations(wl, T)
+    lg = synth.logits(wl, T)
+    r = moeq.forward(lay, torch.from_numpy(x_bits.view(np.int16)).to(DEV),
+                     torch.from_numpy(lg).to(DEV), wl.k, shared=sh)
+    torch.cuda.synchronize()
+    check_routing(wl, lg, r)
+    # decode: every row; prefill: one row of every 128-token tile, and the last
+    rows = (np.arange(T) if T <= 64 else
+            np.array([128 * i + (37 * i) % 128 for i in range(T // 128)] + [T - 1]))
+    Ws = shared_weights(wl)
+    ref = oracle.expert_ffn(x_bits[rows], *Ws)
+    assert_rows_close(to_np(r["y_shared"])[rows], ref, f"{name} y_shared")
+    # out = the routed combine (fixed order) + y_shared
+    y = to_np(r["y_perm"]).astype(np.float64)
+    inv = to_np(r["inv_perm"]).reshape(T, wl.k)
+    w = to_np(r["topk_w"]).astype(np.float64)
+    want = to_np(r["y_shared"]).astype(np.float64)
+    for j in range(wl.k):
+        want = want + w[:, j, None] * y[inv[:, j]]
+    assert_rows_close(to_np(r["out"]), want, f"{name} out", tol=1e-5)

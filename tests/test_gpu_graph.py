@@ -86,3 +86,36 @@ def test_graph_replays_equal_eager():
         # eager work of the program between replays
         moeq.forward(layer, x, other, k)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [16, 40])
+def test_graph_with_shared_expert_on_side_stream(T):
+    """The forward with a BF16 shared expert on the side stream (fork from and
+    join into the capture stream), captured in a graph: every replay equals
+    the eager single-stream result bit for bit."""
+    wl = synth.small_workload("graph_shared", E=16, k=4, H=272, I=80, T=T, cfg=112, shared=True)
+    say("graph shared", T)
+    from tests.gpu_common import build_shared_layer
+    layer = build_small_layer(wl, DEV)
+    shared = build_shared_layer(wl, DEV)
+    lg = torch.from_numpy(synth.logits(wl, T)).to(DEV)
+    x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(DEV)
+    serial = moeq.forward(layer, x, lg, wl.k, shared=shared, overlap=False)
+    torch.cuda.synchronize()
+    over = moeq.forward(layer, x, lg, wl.k, shared=shared, overlap=True)
+    torch.cuda.synchronize()
+    for key in ("out", "y_shared", "y_perm"):
+        assert torch.equal(serial[key], over[key]), key
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = moeq.forward(layer, x, lg, wl.k, shared=shared, overlap=True)
+    other = torch.from_numpy(synth.logits(wl, T, rep=3)).to(DEV)
+    for i in range(4):
+        cap["out"].zero_()
+        cap["y_shared"].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cap["out"], serial["out"]), f"replay {i}"
+        assert torch.equal(cap["y_shared"], serial["y_shared"]), f"replay {i}"
+        moeq.forward(layer, x, other, wl.k, shared=shared, overlap=True)
+        torch.cuda.synchronize()
