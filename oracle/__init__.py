@@ -18,6 +18,10 @@ it follows:
   codes into a shared codebook.
 * GLM-5.3-Flash-TR3-8bpw (K8), "Fidelity" / "Excess over control" -- the
   expert-combine order changes the bits, so the combine order is fixed.
+* GLM-5.3-EXL3-TR3-3.42bpw, "What is quantized" -- BF16 shared experts beside
+  the routed ones.
+* GLM-5.3 Vision NestQuant 1.75-4 bit, "Method" -- random signs and a
+  Hadamard-128 transform on both sides of each weight matrix.
 
 Where the pages are silent the oracle takes the plainest reading, stated in
 the docstring of the function that makes it.
@@ -25,7 +29,8 @@ the docstring of the function that makes it.
 Parity status per function (what pins each one is in tests/test_oracle_*.py):
   e2m1_decode, e4m3_decode, e4m3_encode, nvfp4_quantize, nvfp4_dequant,
   vq_dequant, vq8_dequant, route_topk, permute, expert_ffn, combine,
-  combine_shared, forward
+  combine_shared, forward, hadamard, rotate, unrotate, rotate_weights,
+  unrotate_weights
   -- all pinned.  vq8_dequant's arithmetic is pinned; its code shape (M
   8-bit codes per 8-weight group into M 256-entry codebooks whose rows are
   summed) is a reading the pages do not fix: parity unpinned for the shape.
@@ -43,6 +48,13 @@ from .formats import (  # noqa: F401
     vq8_dequant,
     bf16_bits_to_f64,
     f16_bits_to_f64,
+)
+from .rotation import (  # noqa: F401
+    hadamard,
+    rotate,
+    unrotate,
+    rotate_weights,
+    unrotate_weights,
 )
 from .moe import (  # noqa: F401
     route_topk,

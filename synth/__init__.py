@@ -43,6 +43,10 @@ KIND_ZIPF_RANK = 8
 KIND_VQ8_CODES = 9
 KIND_VQ8_CODEBOOK = 10
 KIND_SHARED = 11
+KIND_ROT_SIGNS = 12
+
+# sides of a rotated expert that carry their own random signs
+ROT_IN13, ROT_OUT_GATE, ROT_OUT_UP, ROT_IN2, ROT_OUT2 = 0, 1, 2, 3, 4
 
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 
@@ -98,6 +102,7 @@ class Workload:
     zipf_s: float = 0.0
     vq8_m: int = 0          # codes per 8-weight group of the small-codebook VQ
     shared: bool = False    # the layer has a BF16 shared expert
+    rot: bool = False       # expert weights stored rotated (signs + Hadamard-128)
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
 
@@ -116,21 +121,26 @@ VQ2X8 = Workload("vq2x8", 6, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=
 # the NVFP4 decode and prefill layers with a BF16 shared expert of the same
 # intermediate size (the routed experts, routing and tokens are those of
 # DECODE / PREFILL: same seed slots)
+# the decode layer with rotated NVFP4 experts: the stored matrices (the NVFP4
+# source weights) are taken to be in the rotated domain, W_rot ~ N(0, 0.02)
+DECODE_ROT = Workload("decode_rot", 7, 256, 8, 6144, 2048, (1, 8, 32), "nvfp4", "uniform",
+                      weight_cfg=1, rot=True)
 DECODE_SHARED = Workload("decode_shared", 1, 256, 8, 6144, 2048, (1, 8, 32), "nvfp4", "uniform",
                          shared=True)
 PREFILL_SHARED = Workload("prefill_shared", 2, 256, 8, 6144, 2048, (4096,), "nvfp4", "zipf",
                           zipf_s=1.1, shared=True)
 
 WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED, VQ1, VQ2X8, DECODE_SHARED,
-                                 PREFILL_SHARED)}
+                                 PREFILL_SHARED, DECODE_ROT)}
 
 
 def small_workload(name, E, k, H, I, T, fmt="nvfp4", logits="normal", cfg=100,
-                   n_nvfp4=0, n_hot=0, hot_share=0.0, zipf_s=0.0, vq8_m=0, shared=False):
+                   n_nvfp4=0, n_hot=0, hot_share=0.0, zipf_s=0.0, vq8_m=0, shared=False,
+                   rot=False):
     """A property-test workload with its own seed slot."""
     return Workload(name, cfg, E, k, H, I, (T,), fmt, logits, weight_cfg=cfg,
                     vq_cfg=cfg, n_nvfp4=n_nvfp4, n_hot=n_hot, hot_share=hot_share,
-                    zipf_s=zipf_s, vq8_m=vq8_m, shared=shared)
+                    zipf_s=zipf_s, vq8_m=vq8_m, shared=shared, rot=rot)
 
 
 # --------------------------------------------------------------------------
@@ -232,6 +242,18 @@ def nvfp4_source_weights(wl, expert, proj):
     z = rng(wl.weight_cfg, KIND_W, expert, proj).standard_normal((n, kin),
                                                                  dtype=np.float32)
     return z * np.float32(0.02)
+
+
+def rot_sign_len(wl, side):
+    return wl.H if side in (ROT_IN13, ROT_OUT2) else wl.I
+
+
+def rot_signs(wl, expert, side):
+    """The random signs (+1 / -1, int8) of one side of a rotated expert's
+    matrices (ROT_IN13: the gate/up input, shared by both; ROT_OUT_GATE,
+    ROT_OUT_UP; ROT_IN2, ROT_OUT2: the down projection's input and output)."""
+    g = rng(wl.cfg, KIND_ROT_SIGNS, expert, side)
+    return np.where(g.random(rot_sign_len(wl, side)) < 0.5, -1, 1).astype(np.int8)
 
 
 def bf16_weights(wl, expert, proj):

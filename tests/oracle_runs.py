@@ -30,7 +30,19 @@ def expert_weights(wl, e, fmt=None):
         else:
             mats.append(oracle.vq_dequant(synth.vq_codes(wl, e, p), synth.vq_scales(wl, e, p),
                                           synth.vq_codebook(wl, p)))
+    if wl.rot:
+        # rotated storage: the effective weights are R_out^T W_rot R_in
+        s = {side: synth.rot_signs(wl, e, side) for side in range(5)}
+        mats = [oracle.unrotate_weights(mats[0], s[synth.ROT_OUT_GATE], s[synth.ROT_IN13]),
+                oracle.unrotate_weights(mats[1], s[synth.ROT_OUT_UP], s[synth.ROT_IN13]),
+                oracle.unrotate_weights(mats[2], s[synth.ROT_OUT2], s[synth.ROT_IN2])]
     return tuple(mats)
+
+
+def stored_weights(wl, e, fmt=None):
+    """The decoded matrices as stored (rotated for a rotated layer)."""
+    import dataclasses
+    return expert_weights(dataclasses.replace(wl, rot=False), e, fmt)
 
 
 def shared_weights(wl):
