@@ -101,7 +101,7 @@ class Runner:
         self.h = torch.empty((T * k, I), dtype=torch.float16, device=dev)
         self.y = torch.empty((T * k, H), dtype=f32, device=dev)
         self.out = torch.empty((T, H), dtype=f32, device=dev)
-        self.ws = moeq.gateup_workspace(layer, T)
+        self.ws = moeq.gateup_workspace(layer, T, k)
         self.pws = moeq.permute_workspace(T, k, E, dev)
         self.shared = shared
         if shared is not None:

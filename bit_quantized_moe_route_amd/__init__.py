@@ -67,6 +67,7 @@ class _QLayerC(ctypes.Structure):
         ("bf16_w13", ctypes.c_void_p), ("bf16_w13_stride", ctypes.c_int64),
         ("bf16_w2", ctypes.c_void_p), ("bf16_w2_stride", ctypes.c_int64),
         ("record_mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("rot_signs", ctypes.c_void_p),
     ]
 
 
@@ -86,7 +87,7 @@ _PROTOS = {
     "moe_ffn_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64, _I32]),
     "moe_expert_ffn_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _P, _I64, _I32, _P,
                                         _P, _SZ, _P]),
-    "moe_gateup_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64]),
+    "moe_gateup_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64, _I32]),
     "moe_expert_gateup_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _P, _I64, _I32, _P,
                                            _P, _SZ, _P]),
     "moe_expert_down_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _I64, _I32, _P, _P]),
@@ -101,6 +102,9 @@ _PROTOS = {
     "moe_pack_nvfp4_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
     "moe_pack_vq_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _P, _P]),
     "moe_pack_bf16_expert": (ctypes.c_int, [_P] * 3 + [_I32, _I32, _P, _P]),
+    "moe_rot_sign_bytes": (_SZ, [_I32, _I32]),
+    "moe_pack_rot_signs": (ctypes.c_int, [_P] * 5 + [_I32, _I32, _P]),
+    "moe_rotate_matrix": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P]),
     "moe_record_table": (ctypes.c_int, [_P, _I32, _P, _P]),
     "moe_record_table_resident": (ctypes.c_int, [_P, _I32, _P]),
     "moe_dequant_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _I32, _I32, _P, _P]),
@@ -214,6 +218,32 @@ def pack_bf16_expert(gate, up, down, H, I, w13=None, w2=None):
     return w13, w2
 
 
+def rot_sign_bytes(H, I):
+    return int(lib().moe_rot_sign_bytes(H, I))
+
+
+def pack_rot_signs(s_in13, s_out_gate, s_out_up, s_in2, s_out2, H, I):
+    """One expert's rotation signs (int8 +-1 arrays) -> the packed bits."""
+    arrs = [np.ascontiguousarray(a, dtype=np.int8) for a in
+            (s_in13, s_out_gate, s_out_up, s_in2, s_out2)]
+    out = np.empty(rot_sign_bytes(H, I), np.uint8)
+    _check(lib().moe_pack_rot_signs(*[_np_ptr(a) for a in arrs], H, I, _np_ptr(out)),
+           "moe_pack_rot_signs")
+    return out
+
+
+def rotate_matrix(w, s_out, s_in):
+    """W_rot = R_out W R_in^T (fp32 in and out, fp64 inside), R = signs then
+    Hadamard-128 / sqrt(128) per block: the offline step of a rotated format."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    so = np.ascontiguousarray(s_out, dtype=np.int8)
+    si = np.ascontiguousarray(s_in, dtype=np.int8)
+    out = np.empty_like(w)
+    _check(lib().moe_rotate_matrix(_np_ptr(w), w.shape[0], w.shape[1], _np_ptr(so), _np_ptr(si),
+                                   _np_ptr(out)), "moe_rotate_matrix")
+    return out
+
+
 def record_table(fmt_host):
     """(rec [E] int32, experts per format {tag: n for every tag in FORMATS})."""
     fmt_host = np.ascontiguousarray(fmt_host, dtype=np.uint8)
@@ -305,6 +335,7 @@ class QLayer:
         self.codebooks = [None, None, None]
         self.codebook_stride = 0
         self.codebooks8 = [None, None, None]
+        self.rot_signs = None
         self._c = None
 
     def record_index(self, e):
@@ -364,6 +395,19 @@ class QLayer:
         self.codebooks8 = out
         self._c = None
 
+    def set_rot_signs(self, signs):
+        """Rotated storage: signs uint8 [E, rot_sign_bytes(H, I)] (one row per
+        expert from pack_rot_signs); None: the stored matrices are the weights."""
+        torch = _torch()
+        if signs is None:
+            self.rot_signs = None
+        else:
+            a = np.ascontiguousarray(signs, dtype=np.uint8)
+            if a.shape != (self.E, rot_sign_bytes(self.H, self.I)):
+                raise ValueError("rotation signs must be [E, rot_sign_bytes(H, I)]")
+            self.rot_signs = torch.from_numpy(a).to(self.device)
+        self._c = None
+
     def c(self):
         if self._c is None:
             d = _QLayerC()
@@ -387,6 +431,7 @@ class QLayer:
             for p in range(3):
                 cb = self.codebooks8[p]
                 d.vq8_codebook[p] = cb.data_ptr() if cb is not None else None
+            d.rot_signs = self.rot_signs.data_ptr() if self.rot_signs is not None else None
             self._c = d
         return self._c
 
@@ -507,9 +552,9 @@ def expert_ffn_q(layer, x, perm_src, offsets, k, y_perm=None, ws=None):
     return y_perm
 
 
-def gateup_workspace(layer, T):
+def gateup_workspace(layer, T, k):
     torch = _torch()
-    n = lib().moe_gateup_workspace_bytes(ctypes.byref(layer.c()), T)
+    n = lib().moe_gateup_workspace_bytes(ctypes.byref(layer.c()), T, k)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=layer.device)
 
 
@@ -521,7 +566,7 @@ def expert_gateup_q(layer, x, perm_src, offsets, k, h=None, ws=None):
     if h is None:
         h = torch.empty((T * k, layer.I), dtype=torch.float16, device=x.device)
     if ws is None:
-        ws = gateup_workspace(layer, T)
+        ws = gateup_workspace(layer, T, k)
     _check(lib().moe_expert_gateup_q(ctypes.byref(layer.c()), _dptr(x), _dptr(perm_src),
                                      _dptr(offsets), T, k, _dptr(h), _dptr(ws), ws.numel(),
                                      _stream(x.device)), "moe_expert_gateup_q")

@@ -84,6 +84,10 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     v.cb_stride = L->vq_codebook_stride;
     for (int p = 0; p < 3; ++p) v.cb8[p] = static_cast<const uint8_t*>(L->vq8_codebook[p]);
     v.vq8_m = L->vq8_m;
+    v.rot = L->rot_signs;
+    v.rot_stride = (int64_t)(2 * (int64_t)L->H + 3 * (int64_t)L->I) / 8;
+    if (v.rot && (L->H % MOE_ROT_BLOCK || L->I % MOE_ROT_BLOCK))
+        return fail(MOE_EUNSUPPORTED, f + ": a rotated layer needs H and I multiples of 128");
     if (out.count[MOE_FMT_VQ8] && (L->vq8_m < 1 || L->vq8_m > MOE_VQ8_MAX_M))
         return fail(MOE_EUNSUPPORTED, f + ": vq8_m must be 1 or 2");
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
@@ -118,13 +122,23 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     return MOE_OK;
 }
 
+// moe_expert_gateup_q: the fp16 copy of x, or for a rotated layer the rotated
+// rows x' [T*k, H] and the raw gate/up products [T*k, 2I] fp32.
+size_t gateup_ws(const moe_qlayer* L, int64_t T, int32_t k) {
+    if (L->rot_signs)
+        return align_up((size_t)T * k * L->H * 2) + align_up((size_t)T * k * 2 * L->I * 4);
+    return align_up((size_t)T * L->H * 2);
+}
+
+// moe_expert_ffn_q: gate/up's workspace, then h [T*k, I] fp16.
 size_t ffn_ws(const moe_qlayer* L, int64_t T, int32_t k) {
-    return align_up((size_t)T * L->H * 2) + align_up((size_t)T * k * L->I * 2);
+    return gateup_ws(L, T, k) + align_up((size_t)T * k * L->I * 2);
 }
 
 // moe_shared_ffn: x16 | h16 | the gate/up partial sums of the decode path.
 size_t shared_ws(const moe_qlayer* L, int64_t T) {
-    return ffn_ws(L, T, 1) + align_up(shared_part_bytes(T, L->I));
+    return align_up((size_t)T * L->H * 2) + align_up((size_t)T * L->I * 2) +
+           align_up(shared_part_bytes(T, L->I));
 }
 
 // Gate/up + SwiGLU of every format present.  perm_src == offsets == NULL is
@@ -135,6 +149,24 @@ int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_
                const int32_t* offsets, int64_t T, int32_t k, uint16_t* h_f16, uint16_t* x16,
                float* part, void* stream) {
     const bool prefill = T >= kPrefillMinTokens;
+    if (li.view.rot) {
+        // rotated layer: x' rows per assignment (in the place of x16), the raw
+        // products in gu (after them), then h' from both
+        float* gu = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(x16) +
+                                             align_up((size_t)T * k * li.view.H * 2));
+        int st = launch_rot_in(li.view, x_bf16, perm_src, offsets, T, k, x16, stream);
+        if (st) return st;
+        for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
+            if (!li.count[fmt]) continue;
+            st = prefill && prefill_fmt(fmt)
+                     ? launch_ffn_prefill(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T,
+                                          k, h_f16, nullptr, 0, stream, gu)
+                     : launch_ffn_decode(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T,
+                                         k, h_f16, nullptr, 0, stream, gu);
+            if (st) return st;
+        }
+        return launch_rot_mid(li.view, gu, offsets, T * k, h_f16, stream);
+    }
     bool need_x16 = false;
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt)
         need_x16 |= prefill && li.count[fmt] && prefill_fmt(fmt);
@@ -174,6 +206,7 @@ int run_down(const LayerInfo& li, const uint16_t* h_f16, const int32_t* offsets,
                                              stream);
         if (st) return st;
     }
+    if (li.view.rot) return launch_rot_out(li.view, y_perm, offsets, T * k, stream);
     return MOE_OK;
 }
 
@@ -255,9 +288,9 @@ size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k) {
     return ffn_ws(layer, T, k);
 }
 
-size_t moe_gateup_workspace_bytes(const moe_qlayer* layer, int64_t T) {
-    if (!layer || T < 0 || layer->H <= 0) return 0;
-    return align_up((size_t)T * layer->H * 2);
+size_t moe_gateup_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k) {
+    if (!layer || T < 0 || k < 1 || layer->H <= 0 || layer->I <= 0) return 0;
+    return gateup_ws(layer, T, k);
 }
 
 int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16, const int32_t* perm_src,
@@ -272,7 +305,7 @@ int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16, const i
     if (T == 0) return MOE_OK;
     if (!x_bf16 || !perm_src || !offsets || !h_f16)
         return fail(MOE_EINVAL, "moe_expert_gateup_q: null pointer");
-    const size_t need = align_up((size_t)T * layer->H * 2);
+    const size_t need = gateup_ws(layer, T, k);
     if (!ws || ws_bytes < need)
         return fail(MOE_EWORKSPACE,
                     "moe_expert_gateup_q: workspace needs " + std::to_string(need) + " bytes");
@@ -316,7 +349,7 @@ int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16, const int3
     if (reinterpret_cast<uintptr_t>(ws) % kAlign)
         return fail(MOE_EINVAL, "moe_expert_ffn_q: workspace must be 256-byte aligned");
     uint8_t* w = static_cast<uint8_t*>(ws);
-    const size_t xbytes = align_up((size_t)T * layer->H * 2);
+    const size_t xbytes = gateup_ws(layer, T, k);
     uint16_t* h16 = reinterpret_cast<uint16_t*>(w + xbytes);
     st = moe_expert_gateup_q(layer, x_bf16, perm_src, offsets, T, k, h16, ws, xbytes, stream);
     if (st) return st;
@@ -335,6 +368,8 @@ int moe_shared_ffn(const moe_qlayer* shared, const uint16_t* x_bf16, int64_t T,
     int st = check_layer("moe_shared_ffn", shared, li);
     if (st) return st;
     if (shared->E != 1) return fail(MOE_EINVAL, "moe_shared_ffn: the shared layer must have E == 1");
+    if (shared->rot_signs)
+        return fail(MOE_EUNSUPPORTED, "moe_shared_ffn: a rotated shared layer is not supported");
     st = check_route_sizes("moe_shared_ffn", T, 1, 1);
     if (st) return st;
     if (T == 0) return MOE_OK;
@@ -348,7 +383,8 @@ int moe_shared_ffn(const moe_qlayer* shared, const uint16_t* x_bf16, int64_t T,
     uint8_t* w = static_cast<uint8_t*>(ws);
     uint16_t* x16 = reinterpret_cast<uint16_t*>(w);
     uint16_t* h16 = reinterpret_cast<uint16_t*>(w + align_up((size_t)T * shared->H * 2));
-    float* part = reinterpret_cast<float*>(w + ffn_ws(shared, T, 1));
+    float* part = reinterpret_cast<float*>(w + align_up((size_t)T * shared->H * 2) +
+                                           align_up((size_t)T * shared->I * 2));
     st = run_gateup(li, x_bf16, nullptr, nullptr, T, 1, h16, x16, part, stream);
     if (st) return st;
     return run_down(li, h16, nullptr, T, 1, y_shared, stream);

@@ -408,9 +408,14 @@ constexpr int kMinWaves = MOEQ_MIN_WAVES;
 // dimension is also split over A.nsplit workgroups (blockIdx.x % nsplit),
 // which write fp32 partial g and u to A.part instead of h; k_swiglu_parts
 // sums them and applies SwiGLU.  (One expert alone has too few row groups to
-// fill the chip.)
-template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID, bool PART = false>
+// fill the chip.)  ROT (gate/up of a rotated layer, with PART and nsplit = 1):
+// the B operand is the fp16 rotated row of each assignment (A.xbf points to
+// [rows, H] in permuted order) and the raw products go to A.part.
+template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID, bool PART = false,
+          bool ROT = false>
 __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
+    static_assert(!ROT || (PART && PHASE == 0 && !ID), "rotated gate/up writes raw products");
+    constexpr bool XBF = PHASE == 0 && !ROT;        // B operand is bf16
     constexpr int NM = PHASE == 0 ? 2 * RPW : RPW;   // weight tiles per input tile
     constexpr int SETS = WV / KS;                    // row sets per workgroup
     const int lane = threadIdx.x & 63;
@@ -466,7 +471,8 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
         if (c >= ae.me)
             xrow[tt] = nullptr;
         else if (PHASE == 0)
-            xrow[tt] = A.xbf + (int64_t)(ID ? c : A.perm_src[ae.r0 + c] / A.k) * A.H;
+            xrow[tt] = A.xbf + (int64_t)(ROT ? ae.r0 + c
+                                             : ID ? c : A.perm_src[ae.r0 + c] / A.k) * A.H;
         else
             xrow[tt] = reinterpret_cast<const uint16_t*>(A.h16) + (int64_t)(ae.r0 + c) * A.I;
     }
@@ -481,18 +487,18 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
 #pragma unroll
             for (int m = 0; m < NM; ++m)
                 lcb[m] = lds_cb + (PHASE == 0 ? (m & 1) : 0) * (F::CODES * MOE_VQ8_NCODE * 8);
-            stream_tiles_vq8<NTT, NM, F::CODES, PHASE == 0>(tb, lcb, xrow, ntt, K, kpart,
-                                                            kstride, lane, acc);
+            stream_tiles_vq8<NTT, NM, F::CODES, XBF>(tb, lcb, xrow, ntt, K, kpart, kstride, lane,
+                                                     acc);
         } else if constexpr (F::kVq && MOEQ_VQ_GATHER_AHEAD) {
             // row c0 of the expert exists: a safe row for lanes past its rows
             const uint16_t* xsafe =
                 PHASE == 0
-                    ? A.xbf + (int64_t)(ID ? c0 : A.perm_src[ae.r0 + c0] / A.k) * A.H
+                    ? A.xbf + (int64_t)(ROT ? ae.r0 + c0
+                                            : ID ? c0 : A.perm_src[ae.r0 + c0] / A.k) * A.H
                     : reinterpret_cast<const uint16_t*>(A.h16) + (int64_t)(ae.r0 + c0) * A.I;
-            stream_tiles_vq<NTT, NM, PHASE == 0>(tb, cb, xrow, xsafe, ntt, K, kpart, kstride,
-                                                 lane, acc);
+            stream_tiles_vq<NTT, NM, XBF>(tb, cb, xrow, xsafe, ntt, K, kpart, kstride, lane, acc);
         } else {
-            stream_tiles<F, NTT, NM, ID ? kPrefetchShared : kPrefetch, PHASE == 0>(
+            stream_tiles<F, NTT, NM, ID ? kPrefetchShared : kPrefetch, XBF>(
                 tb, cb, xrow, ntt, K, kpart, kstride, lane, acc);
         }
     }
@@ -535,7 +541,7 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
             }
             if constexpr (PART) {
                 // fp32 partial sums of this workgroup's inputs: g at [.., n],
-                // u at [.., I + n] of row (split, c)
+                // u at [.., I + n] of row (split, r0 + c)
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt) {
                     const int c = c0 + (lane & 15) + 16 * tt;
@@ -546,7 +552,8 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
                             g[i] = acc[2 * q][tt][i] * sg[i];
                             u[i] = acc[2 * q + 1][tt][i] * su[i];
                         }
-                        float* pp = A.part + ((int64_t)split * A.rows + c) * (2 * A.I) + n0;
+                        float* pp =
+                            A.part + ((int64_t)split * A.rows + ae.r0 + c) * (2 * A.I) + n0;
                         *reinterpret_cast<f32x4*>(pp) = g;
                         *reinterpret_cast<f32x4*>(pp + A.I) = u;
                     }
@@ -623,8 +630,12 @@ int launch_ks(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t
     if (phase == 0) {
         const int nsets = (a.I / 16 + kRpwGateup - 1) / kRpwGateup;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
-        k_ffn<F, NTT, KS, kRpwGateup, 0, WV, false>
-            <<<grid, 64 * WV, codebook_lds_bytes<F>(0), s>>>(a);
+        if (a.part)   // a rotated layer: raw products
+            k_ffn<F, NTT, KS, kRpwGateup, 0, WV, false, true, true>
+                <<<grid, 64 * WV, codebook_lds_bytes<F>(0), s>>>(a);
+        else
+            k_ffn<F, NTT, KS, kRpwGateup, 0, WV, false>
+                <<<grid, 64 * WV, codebook_lds_bytes<F>(0), s>>>(a);
     } else {
         const int nsets = (a.H / 16 + kRpwDown - 1) / kRpwDown;
         dim3 grid((unsigned)((nsets + SETS - 1) / SETS), (unsigned)slots, (unsigned)chunks);
@@ -764,9 +775,10 @@ DecodeArgs decode_args(const LayerView& L, int fmt, const uint16_t* x_bf16,
 
 int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,
                       const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
-                      uint16_t* h16, float* y_perm, int phase, void* stream) {
+                      uint16_t* h16, float* y_perm, int phase, void* stream, float* gu) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const DecodeArgs a = decode_args(L, fmt, x_bf16, perm_src, offsets, T, k, h16, y_perm);
+    DecodeArgs a = decode_args(L, fmt, x_bf16, perm_src, offsets, T, k, h16, y_perm);
+    a.part = phase == 0 ? gu : nullptr;   // nsplit = 1
     const int64_t tk = T * k;
     const int slots = (int)(tk < n_fmt ? tk : n_fmt);
     if (slots == 0) return MOE_OK;

@@ -74,6 +74,7 @@ struct PrefillArgs {
     float* y_perm;
     int E, H, I, k, fmt;
     int rows;                  // offsets == NULL: rows of the identity map
+    float* gu;                 // rotated layers: raw g | u [rows, 2I] (gate/up)
 };
 
 struct WorkItem {
@@ -267,9 +268,13 @@ constexpr int pf_bn() {
 // LDS (NS - 1 tiles in flight ahead of the one in use).  (They are
 // file-level constants, not template parameters: a __shared__ array sized by
 // a template parameter loses its host-side launch stub with this compiler.)
-// ID: offsets / perm_src are the identity map of a one-expert layer.
-template <class PF, int PHASE, bool ID>
+// ID: offsets / perm_src are the identity map of a one-expert layer.  ROT
+// (gate/up of a rotated layer): the token tile rows are the fp16 rotated rows
+// of the assignments (x16 = [rows, H] in permuted order) and the raw fp32
+// products go to A.gu instead of h.
+template <class PF, int PHASE, bool ID, bool ROT = false>
 __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A) {
+    static_assert(!ROT || (PHASE == 0 && !ID), "rotated: gate/up of a routed layer");
     constexpr int WV = kPrefillWaves;
     constexpr int NS = kPrefillStages;
     constexpr int NA = PF::NA;
@@ -306,7 +311,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
     for (int j = 0; j < JX; ++j) {
         const int row = min(4 * (JX * wave + j) + (lane >> 4), mcount - 1);
         const int prow = it.r0 + it.m0 + row;
-        trow[j] = PHASE == 0 && !ID ? A.perm_src[prow] / A.k : prow;
+        trow[j] = PHASE == 0 && !ID && !ROT ? A.perm_src[prow] / A.k : prow;
     }
     auto issue_x = [&](int kb, int buf) {
 #pragma unroll
@@ -448,7 +453,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
             const int ga = g0 + 2 * a;
-            if (PHASE == 0) {
+            if (PHASE == 0 && ROT) {
+                if (ga >= nrg) continue;
+                const int ch = 16 * (ga >> 1) + 4 * h;
+                // gate rows ch..+3, ch+8..+11: acc i, i + 4; up: i + 8, i + 12
+                float* gp = A.gu + prow * (2 * A.I) + ch;
+                *reinterpret_cast<f32x4*>(gp) =
+                    f32x4{acc[a][q][0], acc[a][q][1], acc[a][q][2], acc[a][q][3]};
+                *reinterpret_cast<f32x4*>(gp + 8) =
+                    f32x4{acc[a][q][4], acc[a][q][5], acc[a][q][6], acc[a][q][7]};
+                *reinterpret_cast<f32x4*>(gp + A.I) =
+                    f32x4{acc[a][q][8], acc[a][q][9], acc[a][q][10], acc[a][q][11]};
+                *reinterpret_cast<f32x4*>(gp + A.I + 8) =
+                    f32x4{acc[a][q][12], acc[a][q][13], acc[a][q][14], acc[a][q][15]};
+            } else if (PHASE == 0) {
                 if (ga >= nrg) continue;
                 const int ch = 16 * (ga >> 1) + 4 * h;       // channel of rows 4h..4h+3
                 f16x4 h0, h1;
@@ -482,6 +500,7 @@ namespace {
 
 template <class PF, bool ID>
 int launch_pf(const PrefillArgs& a, int64_t items, int phase, hipStream_t s) {
+    constexpr bool kId = ID;
     constexpr int BN = pf_bn<PF>();
     const int nrg = (phase == 0 ? 2 * a.I : a.H) / 16;
     const int64_t nnt = (nrg + BN / 16 - 1) / (BN / 16);
@@ -495,10 +514,13 @@ int launch_pf(const PrefillArgs& a, int64_t items, int phase, hipStream_t s) {
     const int64_t nblocks = 8 * ((items + 7) / 8) * nnt;
 #endif
     dim3 grid((unsigned)nblocks);
-    if (phase == 0)
+    if (phase == 0 && a.gu) {
+        if constexpr (!kId) k_prefill<PF, 0, false, true><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
+    } else if (phase == 0) {
         k_prefill<PF, 0, ID><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
-    else
+    } else {
         k_prefill<PF, 1, ID><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
+    }
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
 }
@@ -507,7 +529,7 @@ int launch_pf(const PrefillArgs& a, int64_t items, int phase, hipStream_t s) {
 
 int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,
                        const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
-                       uint16_t* h16, float* y_perm, int phase, void* stream) {
+                       uint16_t* h16, float* y_perm, int phase, void* stream, float* gu) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     PrefillArgs a;
     a.pool = phase == 0 ? L.pool13[fmt] : L.pool2[fmt];
@@ -524,6 +546,7 @@ int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x
     a.k = k;
     a.fmt = fmt;
     a.rows = (int)T;
+    a.gu = phase == 0 ? gu : nullptr;
     const int64_t tk = T * k;
     const int64_t active = tk < n_fmt ? tk : n_fmt;
     // sum over experts of ceil(M_e / 128) <= T*k / 128 + (number of active experts)

@@ -78,6 +78,8 @@ struct LayerView {
     const uint8_t* cb[3];       // VQ codebooks gate, up, down
     int64_t cb_stride;
     const uint8_t* cb8[3];      // VQ8 codebooks gate, up, down: [m][256][8] fp16
+    const uint8_t* rot;         // rotation sign bits per expert (NULL: not rotated)
+    int64_t rot_stride;         // bytes per expert: (2H + 3I) / 8
 };
 
 int launch_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
@@ -94,10 +96,13 @@ int launch_combine(const float* y_perm, const int32_t* inv_perm, const float* w,
                    const float* y_shared, int64_t T, int32_t k, int32_t H, float* out,
                    void* stream);
 int launch_x_to_f16(const uint16_t* x, int64_t n, uint16_t* x16, void* stream);
+// gu != NULL (gate/up of a rotated layer): x is the fp16 rotated rows
+// [T*k, H] in permuted order, and the raw fp32 products g | u go to
+// gu [T*k, 2I] instead of h.
 int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,
                       const int32_t* perm_src, const int32_t* offsets, int64_t T,
                       int32_t k, uint16_t* h16, float* y_perm, int phase,
-                      void* stream);
+                      void* stream, float* gu = nullptr);
 // The one expert of a shared-expert layer through the identity map (rows
 // 0 .. T-1 are tokens 0 .. T-1): phase 0 writes fp32 partial g | u to part
 // (shared_part_bytes) and then h, phase 1 writes y [T, H].
@@ -118,7 +123,17 @@ constexpr int64_t kPrefillMinTokens = 128;
 inline bool prefill_fmt(int fmt) { return fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16; }
 int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,
                        const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
-                       uint16_t* h16, float* y_perm, int phase, void* stream);
+                       uint16_t* h16, float* y_perm, int phase, void* stream,
+                       float* gu = nullptr);
+// Rotated layers: x' = rotated rows of x per assignment (fp16 [T*k, H]);
+// h' from the raw gate/up products gu (fp16 [rows, I]); y rotated back in
+// place (fp32 [rows, H]).
+int launch_rot_in(const LayerView& L, const uint16_t* x_bf16, const int32_t* perm_src,
+                  const int32_t* offsets, int64_t T, int32_t k, uint16_t* xrot, void* stream);
+int launch_rot_mid(const LayerView& L, const float* gu, const int32_t* offsets, int64_t rows,
+                   uint16_t* h16, void* stream);
+int launch_rot_out(const LayerView& L, float* y, const int32_t* offsets, int64_t rows,
+                   void* stream);
 int launch_dequant(const LayerView& L, int fmt, int32_t rec_index, int32_t proj,
                    float* out, void* stream);
 

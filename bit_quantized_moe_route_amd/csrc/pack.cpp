@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -306,6 +307,75 @@ int moe_pack_bf16_expert(const uint16_t* gate, const uint16_t* up, const uint16_
 }
 
 static bool known_fmt(int f) { return f >= MOE_FMT_NVFP4 && f <= MOE_FMT_MAX; }
+
+size_t moe_rot_sign_bytes(int32_t H, int32_t I) {
+    if (H <= 0 || I <= 0 || H % 8 || I % 8) return 0;
+    return (size_t)(2 * (int64_t)H + 3 * (int64_t)I) / 8;
+}
+
+int moe_pack_rot_signs(const int8_t* s_in13, const int8_t* s_og, const int8_t* s_ou,
+                       const int8_t* s_in2, const int8_t* s_o2, int32_t H, int32_t I,
+                       uint8_t* out) {
+    if (!s_in13 || !s_og || !s_ou || !s_in2 || !s_o2 || !out)
+        return fail(MOE_EINVAL, "moe_pack_rot_signs: null pointer");
+    if (!moe_rot_sign_bytes(H, I)) return fail(MOE_EINVAL, "moe_pack_rot_signs: bad H or I");
+    const int8_t* sec[5] = {s_in13, s_og, s_ou, s_in2, s_o2};
+    const int32_t len[5] = {H, I, I, I, H};
+    uint8_t* o = out;
+    for (int q = 0; q < 5; ++q) {
+        for (int32_t b = 0; b < len[q] / 8; ++b) {
+            uint8_t byte = 0;
+            for (int i = 0; i < 8; ++i) {
+                const int8_t v = sec[q][8 * b + i];
+                if (v != 1 && v != -1)
+                    return fail(MOE_EINVAL, "moe_pack_rot_signs: a sign is not +1 or -1");
+                if (v < 0) byte |= (uint8_t)(1u << i);
+            }
+            *o++ = byte;
+        }
+    }
+    return MOE_OK;
+}
+
+// v <- R v for one vector: signs, then per 128-block the Hadamard butterflies
+// and 1/sqrt(128) (fp64).
+static void rotate_vec(double* v, int32_t n, const int8_t* s) {
+    const double norm = 1.0 / std::sqrt((double)MOE_ROT_BLOCK);
+    for (int32_t i = 0; i < n; ++i) v[i] *= s[i];
+    for (int32_t b0 = 0; b0 < n; b0 += MOE_ROT_BLOCK) {
+        double* w = v + b0;
+        for (int len = 1; len < MOE_ROT_BLOCK; len <<= 1)
+            for (int i = 0; i < MOE_ROT_BLOCK; i += 2 * len)
+                for (int j = i; j < i + len; ++j) {
+                    const double a = w[j], c = w[j + len];
+                    w[j] = a + c;
+                    w[j + len] = a - c;
+                }
+        for (int i = 0; i < MOE_ROT_BLOCK; ++i) w[i] *= norm;
+    }
+}
+
+int moe_rotate_matrix(const float* w, int32_t n_out, int32_t n_in, const int8_t* s_out,
+                      const int8_t* s_in, float* out) {
+    if (!w || !s_out || !s_in || !out) return fail(MOE_EINVAL, "moe_rotate_matrix: null pointer");
+    if (n_out <= 0 || n_in <= 0 || n_out % MOE_ROT_BLOCK || n_in % MOE_ROT_BLOCK)
+        return fail(MOE_EINVAL, "moe_rotate_matrix: sizes must be positive multiples of 128");
+    for (int32_t i = 0; i < n_in; ++i)
+        if (s_in[i] != 1 && s_in[i] != -1) return fail(MOE_EINVAL, "moe_rotate_matrix: bad sign");
+    for (int32_t i = 0; i < n_out; ++i)
+        if (s_out[i] != 1 && s_out[i] != -1) return fail(MOE_EINVAL, "moe_rotate_matrix: bad sign");
+    std::vector<double> m((size_t)n_out * n_in);
+    for (size_t i = 0; i < m.size(); ++i) m[i] = w[i];
+    for (int32_t o = 0; o < n_out; ++o) rotate_vec(&m[(size_t)o * n_in], n_in, s_in);  // W R_in^T
+    std::vector<double> col(n_out);
+    for (int32_t c = 0; c < n_in; ++c) {                                               // R_out (.)
+        for (int32_t o = 0; o < n_out; ++o) col[o] = m[(size_t)o * n_in + c];
+        rotate_vec(col.data(), n_out, s_out);
+        for (int32_t o = 0; o < n_out; ++o) m[(size_t)o * n_in + c] = col[o];
+    }
+    for (size_t i = 0; i < m.size(); ++i) out[i] = (float)m[i];
+    return MOE_OK;
+}
 
 int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* n_by_fmt) {
     if (!fmt_host || !rec) return fail(MOE_EINVAL, "moe_record_table: null pointer");

@@ -18,7 +18,7 @@ from . import (FMT_BF16, FMT_NVFP4, FMT_VQ, FMT_VQ8, PROJ_DOWN, PROJ_GATE, PROJ_
 
 def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=None,
                 codebook_stride=0, vq8_codes=None, codebooks8=None, vq8_m=0, bf16_weights=None,
-                device="cuda", workers=8, resident_formats=None):
+                device="cuda", workers=8, resident_formats=None, rot_signs=None):
     """Build a QLayer.
 
     nvfp4_weights(e, proj) -> fp32 [n, kin] source weights of an NVFP4 expert
@@ -35,6 +35,10 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
     resident_formats: None, or the formats every expert is packed in (slot e of
         each of those pools), for a layer whose tiers change at run time
         (QLayer.set_tiers).
+    rot_signs(e) -> (s_in13 [H], s_out_gate [I], s_out_up [I], s_in2 [I],
+        s_out2 [H]) int8 +-1: the layer's matrices are stored rotated (the
+        providers above return the rotated matrices) and these are each
+        expert's signs.
     """
     import torch
 
@@ -75,6 +79,9 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         list(ex.map(one, range(E)))
     for key, arr in host.items():
         layer.pools[key].copy_(torch.from_numpy(arr))
+    if rot_signs is not None:
+        from . import pack_rot_signs
+        layer.set_rot_signs(np.stack([pack_rot_signs(*rot_signs(e), H, I) for e in range(E)]))
     if layer.pools[(FMT_VQ, 0)] is not None:
         layer.set_codebooks(codebooks, codebook_stride)
     if layer.pools[(FMT_VQ8, 0)] is not None:

@@ -33,6 +33,9 @@
  *     "GLM-5.3 Vision NestQuant 1.75-4 bit", Contents.
  *   - a fixed expert-combine order (the order changes the bits):
  *     "GLM-5.3-Flash-TR3-8bpw (K8)", Fidelity / Excess over control.
+ *   - stored matrices rotated by random signs and a Hadamard-128 transform
+ *     on both sides, the activations rotated online:
+ *     "GLM-5.3 Vision NestQuant 1.75-4 bit", Method.
  *   - BF16 shared experts beside the low-bit routed ones:
  *     "GLM-5.3-EXL3-TR3-3.42bpw", What is quantized; "GLM-5-NVFP4-MTP",
  *     What's quantized (shared experts are among the non-expert weights
@@ -97,6 +100,7 @@ extern "C" {
 #define MOE_VQ_NCODE  65536   /* codebook entries (uint16 codes) */
 #define MOE_VQ8_NCODE 256     /* entries of each small codebook (uint8 codes) */
 #define MOE_VQ8_MAX_M 2       /* small codebooks per group */
+#define MOE_ROT_BLOCK 128     /* Hadamard block of rotated layers */
 
 /*
  * A packed expert layer.  Host struct; the pointers inside are [device]
@@ -125,6 +129,17 @@ extern "C" {
  *   vq8_codebook[p] fp16 [vq8_m][256][8]: the small codebooks of projection
  *                   p, shared by every MOE_FMT_VQ8 expert of the layer.
  *   bf16_w13 / bf16_w2 pool bases of the MOE_FMT_BF16 records.
+ *   rot_signs       NULL: the stored matrices are the weights.  Otherwise
+ *                   every expert's matrices are stored rotated,
+ *                   W_rot = R_out W R_in^T with R = blockdiag(H_128/sqrt(128))
+ *                   diag(s) ("GLM-5.3 Vision NestQuant 1.75-4 bit", Method:
+ *                   random signs + Hadamard-128 on both sides of each matrix),
+ *                   and the FFN rotates activations online.  [device] uint8,
+ *                   moe_rot_sign_bytes(H, I) per expert at e * that stride,
+ *                   from moe_pack_rot_signs: the sign bits of the gate/up
+ *                   input (shared by gate and up), the gate output, the up
+ *                   output, the down input and the down output.  Needs H and
+ *                   I multiples of 128.
  *   record_mode     MOE_REC_COMPACT: index(e) = e's rank among the experts of
  *                   its format (rec from moe_record_table);
  *                   MOE_REC_RESIDENT: every pool that is used holds a record for
@@ -159,6 +174,7 @@ typedef struct moe_qlayer {
     const void* bf16_w2;    int64_t bf16_w2_stride;
     int32_t record_mode;
     int32_t reserved;
+    const uint8_t* rot_signs;
 } moe_qlayer;
 
 #define MOE_REC_COMPACT   0
@@ -231,7 +247,9 @@ int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
 
 /* ------------------------------------------------------------ expert FFN */
 
-/* Workspace bytes moe_expert_ffn_q needs (the SwiGLU activations h). */
+/* Workspace bytes moe_expert_ffn_q needs (the SwiGLU activations h, the fp16
+ * copy of x, and for a rotated layer the rotated x rows and the gate/up
+ * products). */
 size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k);
 
 /*
@@ -258,9 +276,15 @@ size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k);
  *   (exact for 2^-17 <= |v| <= 65504 with 8 significant bits; smaller
  *   magnitudes round to fp16's subnormal grid, spacing 2^-24); h enters the
  *   down product as fp16.
- *   Requirements: H and I multiples of 16; every format tag in
- *   layer->fmt_host must be one of MOE_FMT_*, else MOE_EUNSUPPORTED; every
- *   pool that a tag refers to must be non-NULL.
+ *   Rotated layers (rot_signs != NULL): x_t is rotated per assignment with
+ *   its expert's input signs (x' = H_128 (s x) / 16, fp16), the stored
+ *   matrices multiply x', the gate and up products are rotated back
+ *   (g = s H_128 g' / 8) before SwiGLU, h is rotated for the down product
+ *   (h' = H_128 (s h) / 16) and its output rotated back (y = s H_128 y' / 8);
+ *   the powers of two make the rotations' 1/sqrt(128) factors exact.
+ *   Requirements: H and I multiples of 16 (of 128 for a rotated layer);
+ *   every format tag in layer->fmt_host must be one of MOE_FMT_*, else
+ *   MOE_EUNSUPPORTED; every pool that a tag refers to must be non-NULL.
  */
 int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16,
                      const int32_t* perm_src, const int32_t* offsets,
@@ -274,13 +298,14 @@ int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16,
  *
  * moe_expert_gateup_q -- h[i] = silu(W_gate[e] x_t) * (W_up[e] x_t) for every
  *   permuted row i (e, t as above), written as fp16 to
- *   h_f16 [device] [T*k, I].  ws [device] >= moe_gateup_workspace_bytes(),
- *   256-byte aligned (holds the fp16 copy of x).
+ *   h_f16 [device] [T*k, I] (for a rotated layer: h' = H_128 (s h) / 16, the
+ *   down product's input).  ws [device] >= moe_gateup_workspace_bytes(),
+ *   256-byte aligned (holds the fp16 copy of x, or the rotated rows).
  * moe_expert_down_q -- y_perm[i] = W_down[e] h[i] (fp32 [T*k, H]) from
  *   h_f16 [device] [T*k, I] and offsets [device] [E+1].
  * Same requirements and errors as moe_expert_ffn_q.
  */
-size_t moe_gateup_workspace_bytes(const moe_qlayer* layer, int64_t T);
+size_t moe_gateup_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k);
 int moe_expert_gateup_q(const moe_qlayer* layer, const uint16_t* x_bf16,
                         const int32_t* perm_src, const int32_t* offsets,
                         int64_t T, int32_t k, uint16_t* h_f16,
@@ -418,6 +443,29 @@ int moe_pack_bf16_expert(const uint16_t* gate, const uint16_t* up, const uint16_
  */
 int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* n_by_fmt);
 
+/* Bytes of one expert's rotation signs: (2H + 3I) / 8 (0 on bad sizes). */
+size_t moe_rot_sign_bytes(int32_t H, int32_t I);
+
+/*
+ * moe_pack_rot_signs -- [host] one expert's rotation signs (int8 +1 / -1) as
+ * the bits rot_signs holds: s_in13 [H] (gate/up input), s_out_gate [I],
+ * s_out_up [I], s_in2 [I] (down input), s_out2 [H] (down output), in that
+ * order, bit i of byte b = channel 8b + i of the section is -1.
+ * out [host] moe_rot_sign_bytes(H, I).  MOE_EINVAL on a value other than +-1.
+ */
+int moe_pack_rot_signs(const int8_t* s_in13, const int8_t* s_out_gate, const int8_t* s_out_up,
+                       const int8_t* s_in2, const int8_t* s_out2, int32_t H, int32_t I,
+                       uint8_t* out);
+
+/*
+ * moe_rotate_matrix -- [host] W_rot = R_out W R_in^T for fp32 W [n_out, n_in]
+ * (n_out, n_in multiples of 128; s_out [n_out], s_in [n_in] int8 +-1),
+ * computed in fp64 and rounded once to fp32 into out [n_out, n_in] (may
+ * alias w).  The offline step of a rotated format: rotate, then encode.
+ */
+int moe_rotate_matrix(const float* w, int32_t n_out, int32_t n_in, const int8_t* s_out,
+                      const int8_t* s_in, float* out);
+
 /*
  * moe_record_table_resident -- [host] rec [E] = (fmt << 24) | e for a layer
  * in MOE_REC_RESIDENT mode (every used pool holds every expert at slot e).
@@ -433,7 +481,8 @@ int moe_record_table_resident(const uint8_t* fmt_host, int32_t E, int32_t* rec);
  * same device decode routines the FFN kernels use.  NVFP4 and VQ values are
  * exact; a MOE_FMT_VQ8 value with m = 2 is fp32(fp32(C_0 + C_1) * S) (two
  * roundings; the FFN kernels multiply each codebook row exactly instead); a
- * MOE_FMT_BF16 value is the stored weight as the kernels' fp16 operand.
+ * MOE_FMT_BF16 value is the stored weight as the kernels' fp16 operand.  For
+ * a rotated layer this is the stored (rotated) matrix.
  */
 int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj,
                   float* out, void* stream);

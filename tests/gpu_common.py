@@ -49,7 +49,9 @@ def build_small_layer(wl, device="cuda", resident_formats=None):
         vq8_codes=lambda e, p: (synth.vq8_codes(wl, e, p), synth.vq_scales(wl, e, p)),
         codebooks8=cbs8, vq8_m=wl.vq8_m,
         bf16_weights=lambda e, p: synth.bf16_weights(wl, e, p),
-        device=device, workers=16, resident_formats=resident_formats)
+        device=device, workers=16, resident_formats=resident_formats,
+        rot_signs=(lambda e: tuple(synth.rot_signs(wl, e, side) for side in range(5)))
+        if wl.rot else None)
 
 
 def build_shared_layer(wl, device="cuda"):

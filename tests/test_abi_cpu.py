@@ -385,3 +385,66 @@ def test_ffn_rejects_bad_shapes_and_workspace():
                               N) == moeq.MOE_EINVAL  # k > E
     assert L.moe_dequant_q(ctypes.byref(d), 8, 0, fake, N) == moeq.MOE_EINVAL
     assert L.moe_dequant_q(ctypes.byref(d), 0, 3, fake, N) == moeq.MOE_EINVAL
+
+
+# ---------------------------------------------------------------- rotation helpers
+
+def test_rot_sign_bytes_and_packing():
+    H, I = 256, 128
+    assert moeq.rot_sign_bytes(H, I) == (2 * H + 3 * I) // 8
+    assert moeq.rot_sign_bytes(250, 128) == 0
+    rs = np.random.default_rng(3)
+    secs = [np.where(rs.random(n) < 0.5, -1, 1).astype(np.int8) for n in (H, I, I, I, H)]
+    b = moeq.pack_rot_signs(*secs, H, I)
+    # bit i of byte j of a section = channel 8j + i is negative, sections in order
+    bits = np.unpackbits(b, bitorder="little").astype(bool)
+    want = np.concatenate([s < 0 for s in secs])
+    assert np.array_equal(bits, want)
+    bad = [x.copy() for x in secs]
+    bad[3][5] = 0
+    with pytest.raises(moeq.MoeError) as ei:
+        moeq.pack_rot_signs(*bad, H, I)
+    assert ei.value.status == moeq.MOE_EINVAL
+
+
+def test_rotate_matrix_matches_oracle():
+    """The library's offline rotation (fp64 butterflies, one rounding to fp32)
+    against the oracle's (fp64 block products): equal to within one fp32
+    rounding, and the inverse rotation gives the matrix back."""
+    rs = np.random.default_rng(9)
+    n_out, n_in = 256, 384
+    w = (rs.standard_normal((n_out, n_in)) * 0.02).astype(np.float32)
+    so = np.where(rs.random(n_out) < 0.5, -1, 1).astype(np.int8)
+    si = np.where(rs.random(n_in) < 0.5, -1, 1).astype(np.int8)
+    got = moeq.rotate_matrix(w, so, si)
+    want = oracle.rotate_weights(w.astype(np.float64), so, si)
+    assert np.all(np.abs(got - want) <= 2.0 ** -24 * np.abs(want) + 1e-45)
+    back = oracle.unrotate_weights(got.astype(np.float64), so, si)
+    assert np.allclose(back, w, rtol=0, atol=1e-8)
+    with pytest.raises(moeq.MoeError):
+        moeq.rotate_matrix(w[:, :200], so, si[:200])
+
+
+def test_rotated_layer_host_checks():
+    L = moeq.lib()
+    fake = ctypes.c_void_p(0x1000)
+    N = ctypes.c_void_p(0)
+    tm = np.full(8, moeq.FMT_NVFP4, np.uint8)
+    d = _fake_layer(tm, H=272, I=128)
+    d.rot_signs = 0x2000                      # H not a multiple of 128
+    need = L.moe_ffn_workspace_bytes(ctypes.byref(d), 4, 2)
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, need,
+                              N) == moeq.MOE_EUNSUPPORTED
+    d = _fake_layer(tm)
+    plain = L.moe_ffn_workspace_bytes(ctypes.byref(d), 4, 2)
+    d.rot_signs = 0x2000
+    rot = L.moe_ffn_workspace_bytes(ctypes.byref(d), 4, 2)
+    # rotated: x' [T*k, H] fp16 + g | u [T*k, 2I] fp32 + h [T*k, I] fp16, 256-aligned
+    assert rot == 4 * 2 * 256 * 2 + 4 * 2 * 2 * 128 * 4 + 4 * 2 * 128 * 2
+    assert rot > plain
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, rot - 1,
+                              N) == moeq.MOE_EWORKSPACE
+    one = _fake_layer(np.full(1, moeq.FMT_NVFP4, np.uint8))
+    one.rot_signs = 0x2000
+    assert L.moe_shared_ffn(ctypes.byref(one), fake, 4, fake, fake, 1 << 24,
+                            N) == moeq.MOE_EUNSUPPORTED

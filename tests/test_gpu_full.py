@@ -280,3 +280,22 @@ def test_shared_expert_full(name, T):
     for j in range(wl.k):
         want = want + w[:, j, None] * y[inv[:, j]]
     assert_rows_close(to_np(r["out"]), want, f"{name} out", tol=1e-5)
+
+
+# ------------------------------------------------------------------ rotated storage
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [1, 32])
+def test_rotated_full_sampled(T):
+    """The decode layer stored rotated (signs + Hadamard-128 on both sides of
+    every matrix, the NVFP4 codes those of the rotated matrices): sampled
+    experts' rows against the oracle's R_out^T Q(W_rot) R_in, the combine
+    through its property."""
+    wl = synth.DECODE_ROT
+    say("rotated full", T)
+    lay = layer("decode_rot")
+    x_bits, lg, r = run_forward(wl, lay, T)
+    ids, w, offsets, perm_src = check_routing(wl, lg, r)
+    experts = pick(offsets, n=2, seed=T + 40)
+    check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
+    check_combine_property(wl, r)

@@ -58,7 +58,7 @@ def test_graph_replays_equal_eager():
         h=torch.empty((T * k, wl.I), dtype=torch.float16, device=DEV),
         y=torch.empty((T * k, wl.H), dtype=torch.float32, device=DEV),
         out=torch.empty((T, wl.H), dtype=torch.float32, device=DEV),
-        ws=moeq.gateup_workspace(layer, T))
+        ws=moeq.gateup_workspace(layer, T, k))
 
     def step():
         ids, w, counts, offsets, perm_src, inv_perm = moeq.route_permute(lg, k, wl.E, bufs["rp"])
@@ -118,4 +118,28 @@ def test_graph_with_shared_expert_on_side_stream(T):
         assert torch.equal(cap["out"], serial["out"]), f"replay {i}"
         assert torch.equal(cap["y_shared"], serial["y_shared"]), f"replay {i}"
         moeq.forward(layer, x, other, wl.k, shared=shared, overlap=True)
+        torch.cuda.synchronize()
+
+
+def test_graph_rotated_layer():
+    """A rotated layer's forward (three rotation launches around the GEMMs)
+    captured in a graph: replays equal the eager result bit for bit."""
+    wl = synth.small_workload("graph_rot", E=16, k=4, H=256, I=128, T=24, cfg=113, rot=True)
+    say("graph rotated")
+    layer = build_small_layer(wl, DEV)
+    T = wl.T[0]
+    lg = torch.from_numpy(synth.logits(wl, T)).to(DEV)
+    x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(DEV)
+    eager = moeq.forward(layer, x, lg, wl.k)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = moeq.forward(layer, x, lg, wl.k)
+    other = torch.from_numpy(synth.logits(wl, T, rep=2)).to(DEV)
+    for i in range(3):
+        cap["out"].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cap["out"], eager["out"]), f"replay {i}"
+        moeq.forward(layer, x, other, wl.k)
         torch.cuda.synchronize()

@@ -56,6 +56,19 @@ SMALL = {
     "nv_bf16_prefill": synth.small_workload("nv_bf16_prefill", E=12, k=3, H=272, I=144, T=260,
                                             fmt="nv_bf16", logits="zipf", zipf_s=1.1, cfg=142,
                                             n_nvfp4=6),
+    # rotated layers (signs + Hadamard-128 on both sides of every matrix):
+    # decode with ragged T, the grouped-GEMM path, all four formats
+    "rot_nv": synth.small_workload("rot_nv", E=16, k=4, H=384, I=256, T=37, cfg=170, rot=True),
+    "rot_prefill": synth.small_workload("rot_prefill", E=8, k=2, H=512, I=256, T=300,
+                                        logits="zipf", zipf_s=1.1, cfg=171, rot=True),
+    "rot_mixed3": synth.small_workload("rot_mixed3", E=24, k=6, H=384, I=128, T=70,
+                                       fmt="mixed3", logits="hot", cfg=172, n_nvfp4=8, n_hot=4,
+                                       hot_share=0.6, vq8_m=2, rot=True),
+    "rot_nv_bf16": synth.small_workload("rot_nv_bf16", E=12, k=3, H=256, I=128, T=9,
+                                        fmt="nv_bf16", cfg=173, n_nvfp4=5, rot=True),
+    "rot_bf16_prefill": synth.small_workload("rot_bf16_prefill", E=6, k=2, H=256, I=128,
+                                             T=200, fmt="nv_bf16", cfg=174, n_nvfp4=3,
+                                             rot=True),
 }
 
 _layers = {}
@@ -437,3 +450,44 @@ def test_shared_expert_other_formats(fmt, T):
     y = moeq.shared_ffn(lay, torch.from_numpy(x_bits.view(np.int16)).to(DEV))
     ref = oracle.expert_ffn(x_bits, *expert_weights(wl, 0, fmt))
     assert_rows_close(to_np(y), ref, f"shared fmt {fmt}")
+
+
+# ------------------------------------------------------------------ rotation
+
+def test_rotated_dequant_is_the_stored_matrix():
+    """A rotated layer's dequant hook returns the stored (rotated) matrices."""
+    from tests.oracle_runs import stored_weights
+    wl = SMALL["rot_nv"]
+    say("rotated dequant")
+    layer = layer_for("rot_nv")
+    for e in (0, 7, 15):
+        W = stored_weights(wl, e)
+        for p in range(3):
+            assert np.array_equal(to_np(moeq.dequant_q(layer, e, p)).astype(np.float64), W[p])
+
+
+def test_rotation_changes_nothing_for_unrotated_weights():
+    """Storing R_out W R_in^T (the library's offline rotation, in fp32) and
+    running the rotated layer gives the plain layer's output within the
+    tolerance: the online rotations undo the stored ones."""
+    from bit_quantized_moe_route_amd.layers import build_layer
+    wl = synth.small_workload("rot_id", E=8, k=2, H=256, I=128, T=12, fmt="bf16", cfg=175)
+    say("rotation round trip")
+    T = wl.T[0]
+    signs = {e: tuple(synth.rot_signs(wl, e, side) for side in range(5)) for e in range(wl.E)}
+    sides = {0: (1, 0), 1: (2, 0), 2: (4, 3)}            # proj -> (out side, in side)
+
+    def rotated(e, p):
+        w = oracle.bf16_bits_to_f64(synth.bf16_weights(wl, e, p)).astype(np.float32)
+        so, si = sides[p]
+        return synth.f32_to_bf16_bits(moeq.rotate_matrix(w, signs[e][so], signs[e][si]))
+
+    plain = build_small_layer(wl, DEV)
+    rot = build_layer(wl.E, wl.H, wl.I, synth.tier_map(wl), bf16_weights=rotated, device=DEV,
+                      workers=4, rot_signs=lambda e: signs[e])
+    x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(DEV)
+    lg = torch.from_numpy(synth.logits(wl, T)).to(DEV)
+    a = moeq.forward(plain, x, lg, wl.k)["out"]
+    b = moeq.forward(rot, x, lg, wl.k)["out"]
+    # bf16 rounding of the rotated weights: a few 2^-9 relative per weight
+    assert_rows_close(to_np(b), to_np(a).astype(np.float64), "rotated vs plain", tol=2e-2)
