@@ -21,8 +21,10 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                  prefill T = 4096 with Zipf(1.1) routing, 2-bit VQ T = 8,
                  small-codebook VQ at 1 and 2 bits per weight T = 8,
                  mixed NVFP4/VQ T = 8 and 32, the same mixed layer with
-                 its hot experts switched to the NVFP4 tier at run time, and
-                 the decode and prefill layers with a BF16 shared expert)
+                 its hot experts switched to the NVFP4 tier at run time,
+                 the decode and prefill layers with a BF16 shared expert, and
+                 the decode layer stored rotated (online Hadamard-128
+                 rotations around every matrix))
 """
 
 import argparse
@@ -325,7 +327,8 @@ def main():
     ap.add_argument("--T", type=int, default=32, help="decode batch of the headline")
     ap.add_argument("--extra",
                     default="decode1,decode8,prefill,vq,vq1,vq2x8,mixed8,mixed32,mixedhot8,"
-                            "mixedhot32,shared1,shared8,shared32,prefillshared",
+                            "mixedhot32,shared1,shared8,shared32,prefillshared,rot1,rot8,rot32,"
+                            "rotprefill",
                     help="comma list of other workloads to measure ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy", action="store_true",
@@ -395,6 +398,22 @@ def main():
                 else:
                     T = int(name[len("shared"):])
                     extra[name] = measure(nv_layer, ws_, T, 30, 5, dev, shared=layers["shared"])
+            elif name.startswith("rot"):
+                # the same NVFP4 codes read as the rotated matrices of a rotated
+                # layer: the decode layer with each expert's signs attached
+                wr = synth.DECODE_ROT
+                nv_layer.set_rot_signs(np.stack([
+                    moeq.pack_rot_signs(*[synth.rot_signs(wr, e, sd) for sd in range(5)],
+                                        wr.H, wr.I) for e in range(wr.E)]))
+                try:
+                    if name == "rotprefill":
+                        wpr = synth.Workload("prefill_rot", 2, 256, 8, 6144, 2048, (4096,),
+                                             "nvfp4", "zipf", zipf_s=1.1, rot=True)
+                        extra[name] = measure(nv_layer, wpr, 4096, 5, 2, dev, reps=4)
+                    else:
+                        extra[name] = measure(nv_layer, wr, int(name[len("rot"):]), 30, 5, dev)
+                finally:
+                    nv_layer.set_rot_signs(None)
             elif name.startswith("decode"):
                 T = int(name[len("decode"):])
                 extra[name] = measure(nv_layer, wl, T, 30, 5, dev)

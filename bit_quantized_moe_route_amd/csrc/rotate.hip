@@ -13,28 +13,38 @@
 //                              h'[r] = H (s_in2[e] * h) / 16               -> fp16
 //   k_rot<2> (down output):    y[r]  = s_o2[e] * H y'[r] / 8               (in place)
 //
-// for every permuted row r of expert e and token t = perm_src[r] / k, one
-// 128-wide block per wave: lane L holds elements 2L and 2L+1 and the seven
-// butterfly stages are one in-lane stage and six lane exchanges.
+// for every permuted row r of expert e and token t = perm_src[r] / k.  A
+// workgroup of 4 waves owns 4 spw 256-element spans of a row (all of it for
+// many rows, 4 spans for few, so that a decode step still has enough
+// workgroups); wave w takes spans w, w + 4, ...: lane L holds elements
+// 4L .. 4L+3 of a span, i.e.
+// half L >> 5 of the span's two 128-blocks, so each wave access is a
+// contiguous 16-byte-per-lane load or store, and a block's seven butterfly
+// stages are two in-lane stages and five lane exchanges inside a half-wave.
+// The next span's loads are issued before the current span is transformed.
+// A row of an odd number of 128-blocks ends with a half span: its upper
+// half-wave neither loads nor stores (its butterflies never mix with the
+// lower half's).
 #include "dev_common.h"
 
 namespace moeq {
 
 namespace {
 
-// Unnormalised Walsh-Hadamard transform of the wave's 128 values (Sylvester
-// order: out[i] = sum_j (-1)^popcount(i & j) in[j]).
-__device__ __forceinline__ void fwht128(float& a, float& b, int lane) {
-    float t = a + b;
-    b = a - b;
-    a = t;
+// Unnormalised Walsh-Hadamard transform of each half-wave's 128 values
+// (Sylvester order: out[i] = sum_j (-1)^popcount(i & j) in[j]), lane L
+// holding elements 4 (L & 31) + q.
+__device__ __forceinline__ void fwht128(f32x4& v, int lane) {
+    float a = v[0] + v[1], b = v[0] - v[1], c = v[2] + v[3], d = v[2] - v[3];
+    v = f32x4{a + c, b + d, a - c, b - d};
 #pragma unroll
-    for (int s = 0; s < 6; ++s) {
-        const float pa = __shfl_xor(a, 1 << s);
-        const float pb = __shfl_xor(b, 1 << s);
+    for (int s = 0; s < 5; ++s) {
         const bool hi = (lane >> s) & 1;
-        a = hi ? pa - a : a + pa;
-        b = hi ? pb - b : b + pb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float p = __shfl_xor(v[q], 1 << s);
+            v[q] = hi ? p - v[q] : v[q] + p;
+        }
     }
 }
 
@@ -51,16 +61,26 @@ __device__ __forceinline__ int row_expert(const int32_t* __restrict__ offsets, i
     return n;
 }
 
-// Signs of elements 2L, 2L+1 of 128-block b of a section (bit set = -1).
-__device__ __forceinline__ void signs2(const uint8_t* sec, int b, int lane, float& sa, float& sb) {
-    const uint32_t byte = sec[16 * b + (lane >> 2)];
-    const int bit = (2 * lane) & 7;
-    sa = (byte >> bit) & 1 ? -1.f : 1.f;
-    sb = (byte >> (bit + 1)) & 1 ? -1.f : 1.f;
+// Signs of the lane's 4 elements of span s of a section (bit set = -1);
+// +1 for a lane outside the row.
+__device__ __forceinline__ f32x4 signs4(const uint8_t* sec, int s, int lane, bool in) {
+    const uint32_t bits = in ? sec[32 * s + (lane >> 1)] >> (4 * (lane & 1)) : 0u;
+    return f32x4{bits & 1 ? -1.f : 1.f, bits & 2 ? -1.f : 1.f, bits & 4 ? -1.f : 1.f,
+                 bits & 8 ? -1.f : 1.f};
 }
 
 __device__ __forceinline__ float silu_mul_r(float g, float u) {
     return g * u / (1.0f + expf(-g));
+}
+
+__device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 v) {
+    return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
+
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 v, float sc) {
+    return f16x4{(_Float16)(v[0] * sc), (_Float16)(v[1] * sc), (_Float16)(v[2] * sc),
+                 (_Float16)(v[3] * sc)};
 }
 
 struct RotArgs {
@@ -74,70 +94,100 @@ struct RotArgs {
     _Float16* h16;          // MODE 1: out h' [rows, I]
     float* y;               // MODE 2: [rows, H] in place
     int E, H, I, k, rows;
-    int nblk;               // 128-blocks per row (H or I / 128)
-    int nbw;                // workgroups per row (nblk / 4, rounded up)
+    int nspan;              // 256-element spans per row, the last maybe half
+    int half_tail;          // the row ends with a half span
+    int spw;                // spans per wave
+    int nwg;                // workgroups per row
 };
 
 template <int MODE>
 __global__ __launch_bounds__(256) void k_rot(RotArgs A) {
     const int lane = threadIdx.x & 63;
-    const int r = blockIdx.x / A.nbw;
-    const int b = (blockIdx.x % A.nbw) * 4 + (threadIdx.x >> 6);
-    if (r >= A.rows || b >= A.nblk) return;
+    const int wave = threadIdx.x >> 6;
+    const int r = blockIdx.x / A.nwg;
+    const int s0 = (blockIdx.x % A.nwg) * 4 * A.spw + wave;   // first span of the wave
+    const int send = min(A.nspan, s0 - wave + 4 * A.spw);     // end of the workgroup's spans
+    if (s0 >= send) return;
     const int e = row_expert(A.offsets, A.E, r, lane);
     const uint8_t* sg = A.signs + (int64_t)e * A.sign_stride;
-    const int c = 128 * b + 2 * lane;                      // first element of the lane
-    float sa, sb;
+    const int o = 4 * lane;                                   // lane's offset in a span
+    // does the lane's part of span s lie inside the row?
+    auto in = [&](int s) { return !A.half_tail || s + 1 < A.nspan || lane < 32; };
     if constexpr (MODE == 0) {
-        const int t = A.perm_src[r] / A.k;
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(A.x + (int64_t)t * A.H + c);
-        float a = __uint_as_float(v << 16), bb = __uint_as_float(v & 0xffff0000u);
-        signs2(sg, b, lane, sa, sb);
-        a *= sa;
-        bb *= sb;
-        fwht128(a, bb, lane);
-        f16x2 o = {(_Float16)(a * 0.0625f), (_Float16)(bb * 0.0625f)};
-        *reinterpret_cast<f16x2*>(A.xrot + (int64_t)r * A.H + c) = o;
+        const uint16_t* xr = A.x + (int64_t)(A.perm_src[r] / A.k) * A.H + o;
+        _Float16* dst = A.xrot + (int64_t)r * A.H + o;
+        uint2 cur = make_uint2(0u, 0u);
+        if (in(s0)) cur = *reinterpret_cast<const uint2*>(xr + 256 * s0);
+        for (int s = s0; s < send; s += 4) {
+            uint2 nxt = cur;
+            if (s + 4 < send && in(s + 4))
+                nxt = *reinterpret_cast<const uint2*>(xr + 256 * (s + 4));
+            f32x4 v = bf16x4_to_f32(cur) * signs4(sg, s, lane, in(s));
+            fwht128(v, lane);
+            if (in(s)) *reinterpret_cast<f16x4*>(dst + 256 * s) = to_f16x4(v, 0.0625f);
+            cur = nxt;
+        }
     } else if constexpr (MODE == 1) {
-        const float* gp = A.gu + (int64_t)r * (2 * A.I) + c;
-        float2 g = *reinterpret_cast<const float2*>(gp);
-        float2 u = *reinterpret_cast<const float2*>(gp + A.I);
-        fwht128(g.x, g.y, lane);
-        fwht128(u.x, u.y, lane);
+        const float* gp = A.gu + (int64_t)r * (2 * A.I) + o;
+        _Float16* dst = A.h16 + (int64_t)r * A.I + o;
         const uint8_t* s_og = sg + A.H / 8;
         const uint8_t* s_ou = s_og + A.I / 8;
         const uint8_t* s_i2 = s_ou + A.I / 8;
-        signs2(s_og, b, lane, sa, sb);
-        g.x *= sa * 0.125f;
-        g.y *= sb * 0.125f;
-        signs2(s_ou, b, lane, sa, sb);
-        u.x *= sa * 0.125f;
-        u.y *= sb * 0.125f;
-        float h0 = silu_mul_r(g.x, u.x), h1 = silu_mul_r(g.y, u.y);
-        signs2(s_i2, b, lane, sa, sb);
-        h0 *= sa;
-        h1 *= sb;
-        fwht128(h0, h1, lane);
-        f16x2 o = {(_Float16)(h0 * 0.0625f), (_Float16)(h1 * 0.0625f)};
-        *reinterpret_cast<f16x2*>(A.h16 + (int64_t)r * A.I + c) = o;
+        f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+        if (in(s0)) {
+            g = *reinterpret_cast<const f32x4*>(gp + 256 * s0);
+            u = *reinterpret_cast<const f32x4*>(gp + A.I + 256 * s0);
+        }
+        for (int s = s0; s < send; s += 4) {
+            f32x4 gn = g, un = u;
+            if (s + 4 < send && in(s + 4)) {
+                gn = *reinterpret_cast<const f32x4*>(gp + 256 * (s + 4));
+                un = *reinterpret_cast<const f32x4*>(gp + A.I + 256 * (s + 4));
+            }
+            const bool ok = in(s);
+            fwht128(g, lane);
+            fwht128(u, lane);
+            g = g * signs4(s_og, s, lane, ok) * 0.125f;
+            u = u * signs4(s_ou, s, lane, ok) * 0.125f;
+            f32x4 h;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = silu_mul_r(g[q], u[q]);
+            h = h * signs4(s_i2, s, lane, ok);
+            fwht128(h, lane);
+            if (ok) *reinterpret_cast<f16x4*>(dst + 256 * s) = to_f16x4(h, 0.0625f);
+            g = gn;
+            u = un;
+        }
     } else {
-        float2* yp = reinterpret_cast<float2*>(A.y + (int64_t)r * A.H + c);
-        float2 y = *yp;
-        fwht128(y.x, y.y, lane);
+        float* yp = A.y + (int64_t)r * A.H + o;
         const uint8_t* s_o2 = sg + A.H / 8 + 3 * (A.I / 8);
-        signs2(s_o2, b, lane, sa, sb);
-        y.x *= sa * 0.125f;
-        y.y *= sb * 0.125f;
-        *yp = y;
+        f32x4 cur = {0.f, 0.f, 0.f, 0.f};
+        if (in(s0)) cur = *reinterpret_cast<const f32x4*>(yp + 256 * s0);
+        for (int s = s0; s < send; s += 4) {
+            f32x4 nxt = cur;
+            if (s + 4 < send && in(s + 4))
+                nxt = *reinterpret_cast<const f32x4*>(yp + 256 * (s + 4));
+            const bool ok = in(s);
+            fwht128(cur, lane);
+            if (ok)
+                *reinterpret_cast<f32x4*>(yp + 256 * s) =
+                    cur * signs4(s_o2, s, lane, ok) * 0.125f;
+            cur = nxt;
+        }
     }
 }
 
+constexpr int kRotWholeRowMin = 1024;   // rows from which a workgroup takes a whole row
+
 template <int MODE>
 int launch_rot(RotArgs a, int n, hipStream_t s) {
-    a.nblk = n / 128;
-    a.nbw = (a.nblk + 3) / 4;
+    a.nspan = (n + 255) / 256;
+    a.half_tail = n % 256 != 0;
+    // whole rows per workgroup once there are enough rows to fill the chip
+    a.spw = a.rows >= kRotWholeRowMin ? (a.nspan + 3) / 4 : 1;
+    a.nwg = (a.nspan + 4 * a.spw - 1) / (4 * a.spw);
     if (a.rows == 0) return MOE_OK;
-    k_rot<MODE><<<(unsigned)((int64_t)a.rows * a.nbw), 256, 0, s>>>(a);
+    k_rot<MODE><<<(unsigned)((int64_t)a.rows * a.nwg), 256, 0, s>>>(a);
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
 }
