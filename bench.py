@@ -326,7 +326,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--T", type=int, default=32, help="decode batch of the headline")
     ap.add_argument("--extra",
-                    default="decode1,decode8,prefill,vq,vq1,vq2x8,mixed8,mixed32,mixedhot8,"
+                    default="decode1,decode8,prefill,vq,vq1,vq2x8,vq3x8,mixed8,mixed32,mixedhot8,"
                             "mixedhot32,shared1,shared8,shared32,prefillshared,rot1,rot8,rot32,"
                             "rotprefill",
                     help="comma list of other workloads to measure ('' for none)")
@@ -427,7 +427,7 @@ def main():
                     vq_codes=lambda e, p: (synth.vq_codes(wq, e, p), synth.vq_scales(wq, e, p)),
                     codebooks=[synth.vq_codebook(wq, p) for p in range(3)], device=dev, workers=16)
                 extra[name] = measure(layers["vq"], wq, 8, 30, 5, dev)
-            elif name in ("vq1", "vq2x8"):
+            elif name in ("vq1", "vq2x8", "vq3x8"):
                 w8 = synth.WORKLOADS[name]
                 log(f"building the small-codebook VQ layer {name} ...")
                 lay8 = build_layer(

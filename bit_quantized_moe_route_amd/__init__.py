@@ -316,8 +316,8 @@ class QLayer:
             rec = record_table(self.fmt_host)[0]
             sizes = dict(counts)
         self.counts = counts
-        if sizes[FMT_VQ8] and vq8_m not in (1, 2):
-            raise ValueError("a layer with small-codebook VQ experts needs vq8_m = 1 or 2")
+        if sizes[FMT_VQ8] and vq8_m not in (1, 2, 3):
+            raise ValueError("a layer with small-codebook VQ experts needs vq8_m = 1, 2 or 3")
         self.vq8_m = int(vq8_m)
         self.rec_host = rec
         self.device = torch.device(device)

@@ -89,7 +89,7 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     if (v.rot && (L->H % MOE_ROT_BLOCK || L->I % MOE_ROT_BLOCK))
         return fail(MOE_EUNSUPPORTED, f + ": a rotated layer needs H and I multiples of 128");
     if (out.count[MOE_FMT_VQ8] && (L->vq8_m < 1 || L->vq8_m > MOE_VQ8_MAX_M))
-        return fail(MOE_EUNSUPPORTED, f + ": vq8_m must be 1 or 2");
+        return fail(MOE_EUNSUPPORTED, f + ": vq8_m must be 1, 2 or 3");
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!out.count[fmt]) continue;
         const char* name = fmt == MOE_FMT_NVFP4 ? "NVFP4"

@@ -3,8 +3,8 @@
 // are exact (NVFP4: an E2M1 value times an E4M3 scale, exact in fp16; VQ: an
 // fp16 codebook entry times an fp16 scale, exact in fp32), so the output can
 // be compared bit for bit with a plain decode of the canonical bytes.  VQ8
-// with one code per group is exact too; with two it is
-// fp32(fp32(C_0 + C_1) * S).  BF16 gives the kernels' fp16 operand: the
+// with one code per group is exact too; with two or three it is
+// fp32(fp32(C_0 + .. + C_{m-1}) * S).  BF16 gives the kernels' fp16 operand: the
 // stored weight rounded to fp16 (equal to it for |w| >= 2^-17).
 #include "dev_common.h"
 
@@ -145,6 +145,8 @@ int launch_dequant(const LayerView& L, int fmt, int32_t ridx, int32_t proj, floa
         dim3 grid((unsigned)(n / 16), (unsigned)nkb);
         if (L.vq8_m == 1)
             k_dequant_vq8<1><<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, L.cb8[proj], sc, out);
+        else if (L.vq8_m == 3)
+            k_dequant_vq8<3><<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, L.cb8[proj], sc, out);
         else
             k_dequant_vq8<2><<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, L.cb8[proj], sc, out);
     } else {

@@ -331,11 +331,16 @@ __device__ __forceinline__ void stream_tiles_vq8(const uint8_t* const tbase[NM],
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             const uint8_t* p = tbase[m] + (int64_t)kb * F::TB + lane * 8 * M;
-            if constexpr (M == 1) {
+            if constexpr (M == 1 || M == 3) {
+                // 8 bytes per load (3 codes per group: 24 bytes, 8-byte aligned)
                 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-                c[m][0] = v[0];
-                c[m][1] = v[1];
+#pragma unroll
+                for (int q = 0; q < M; ++q) {
+                    const u32x2 v =
+                        __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + 8 * q));
+                    c[m][2 * q] = v[0];
+                    c[m][2 * q + 1] = v[1];
+                }
             } else {
                 const u32x4 v = load_stream16(p);
 #pragma unroll
@@ -786,6 +791,7 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
     if (fmt == MOE_FMT_BF16) return launch_ntt<Bf16Fmt>(a, T, slots, phase, s);
     if (fmt == MOE_FMT_VQ8) {
         if (L.vq8_m == 1) return launch_ntt<Vq8Fmt<1>>(a, T, slots, phase, s);
+        if (L.vq8_m == 3) return launch_ntt<Vq8Fmt<3>>(a, T, slots, phase, s);
         return launch_ntt<Vq8Fmt<2>>(a, T, slots, phase, s);
     }
     return launch_ntt<VqFmt>(a, T, slots, phase, s);
@@ -805,6 +811,7 @@ int launch_shared_decode(const LayerView& L, int fmt, const uint16_t* x_bf16, in
     if (fmt == MOE_FMT_BF16) return launch_shared_fmt<Bf16Fmt>(a, phase, s);
     if (fmt == MOE_FMT_VQ8) {
         if (L.vq8_m == 1) return launch_shared_fmt<Vq8Fmt<1>>(a, phase, s);
+        if (L.vq8_m == 3) return launch_shared_fmt<Vq8Fmt<3>>(a, phase, s);
         return launch_shared_fmt<Vq8Fmt<2>>(a, phase, s);
     }
     return launch_shared_fmt<VqFmt>(a, phase, s);

@@ -23,7 +23,7 @@ int fail(int status, const std::string& msg);
 // VQ tile: 16 rows x 256 inputs = 1024 code bytes.
 //   lane L owns bytes [16L, 16L+16) = 8 uint16 codes: row (L & 15), groups
 //     covering inputs kb*256 + (L >> 4)*64 + 8s + [0, 8), s = 0..7.
-// VQ8 tile (m = 1 or 2 uint8 codes per group): 16 rows x 256 inputs =
+// VQ8 tile (m = 1, 2 or 3 uint8 codes per group): 16 rows x 256 inputs =
 //   512 m code bytes; lane L owns bytes [8mL, 8mL + 8m): row (L & 15), the
 //   groups of inputs kb*256 + (L >> 4)*64 + 8s + [0, 8), s = 0..7, each group's
 //   m codes consecutive (code j of group s at byte m*s + j).

@@ -273,7 +273,7 @@ int moe_pack_vq8_expert(const uint8_t* gc, const uint16_t* gs, const uint8_t* uc
     if (H <= 0 || I <= 0 || H % 16 || I % 16)
         return fail(MOE_EUNSUPPORTED, "moe_pack_vq8_expert: H and I must be positive multiples of 16");
     if (m < 1 || m > MOE_VQ8_MAX_M)
-        return fail(MOE_EUNSUPPORTED, "moe_pack_vq8_expert: m must be 1 or 2");
+        return fail(MOE_EUNSUPPORTED, "moe_pack_vq8_expert: m must be 1, 2 or 3");
     std::memset(w13, 0, (size_t)vq8_rec_bytes(0, H, I, m));
     std::memset(w2, 0, (size_t)vq8_rec_bytes(1, H, I, m));
     vq8_tiles(gc, I, H, m, 2, 0, w13);

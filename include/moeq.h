@@ -83,7 +83,7 @@ extern "C" {
 #define MOE_FMT_NVFP4 1       /* E2M1 codes + E4M3 scale per 16 inputs */
 #define MOE_FMT_VQ    2       /* 8-wide groups, uint16 codes, fp16 codebook,
                                  fp16 scale per output channel */
-#define MOE_FMT_VQ8   3       /* 8-wide groups, M = 1 or 2 uint8 codes into M
+#define MOE_FMT_VQ8   3       /* 8-wide groups, M = 1, 2 or 3 uint8 codes into M
                                  256-entry fp16 codebooks whose rows are
                                  summed, fp16 scale per output channel
                                  (M bits per weight) */
@@ -99,7 +99,7 @@ extern "C" {
 #define MOE_MAX_K     16      /* experts per token */
 #define MOE_VQ_NCODE  65536   /* codebook entries (uint16 codes) */
 #define MOE_VQ8_NCODE 256     /* entries of each small codebook (uint8 codes) */
-#define MOE_VQ8_MAX_M 2       /* small codebooks per group */
+#define MOE_VQ8_MAX_M 3       /* small codebooks per group */
 #define MOE_ROT_BLOCK 128     /* Hadamard block of rotated layers */
 
 /*
@@ -123,7 +123,7 @@ extern "C" {
  *                   down).  vq_codebook_stride = bytes between the codebooks
  *                   of consecutive VQ records (index(e)); 0 means one
  *                   codebook per projection shared by every expert.
- *   vq8_m           codes per group of the MOE_FMT_VQ8 experts (1 or 2);
+ *   vq8_m           codes per group of the MOE_FMT_VQ8 experts (1, 2 or 3);
  *                   any value if the layer has none.
  *   vq8_w13 / vq8_w2   pool bases of the MOE_FMT_VQ8 records;
  *   vq8_codebook[p] fp16 [vq8_m][256][8]: the small codebooks of projection
@@ -418,7 +418,7 @@ int moe_pack_vq_expert(const uint16_t* gate_codes, const uint16_t* gate_scales,
  * moe_pack_vq8_expert -- [host] lay one MOE_FMT_VQ8 expert out as its two
  * records.  codes uint8 [n, kin/8, m] (code j of group g indexes codebook
  * j; group g covers inputs 8g..8g+7), scales fp16 bits [n], for gate/up
- * (n = I, kin = H) and down (n = H, kin = I); m = 1 or 2.
+ * (n = I, kin = H) and down (n = H, kin = I); m = 1, 2 or 3.
  *   ("GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw", What it is: 1/2/3-bit
  *   modules with per-group codes and shared codebooks.)
  */
@@ -479,8 +479,8 @@ int moe_record_table_resident(const uint8_t* fmt_host, int32_t E, int32_t* rec);
  * moe_dequant_q -- decode projection `proj` (MOE_PROJ_*) of expert `expert`
  * to fp32 out [n, kin] ([device]; gate/up: [I, H], down: [H, I]) with the
  * same device decode routines the FFN kernels use.  NVFP4 and VQ values are
- * exact; a MOE_FMT_VQ8 value with m = 2 is fp32(fp32(C_0 + C_1) * S) (two
- * roundings; the FFN kernels multiply each codebook row exactly instead); a
+ * exact; a MOE_FMT_VQ8 value with m >= 2 is fp32(fp32(C_0 + .. + C_{m-1}) * S) (fp32
+ * sums; the FFN kernels multiply each codebook row exactly instead); a
  * MOE_FMT_BF16 value is the stored weight as the kernels' fp16 operand.  For
  * a rotated layer this is the stored (rotated) matrix.
  */

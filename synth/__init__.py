@@ -117,6 +117,8 @@ MIXED = Workload("mixed", 4, 256, 8, 6144, 2048, (8, 32), "mixed", "hot",
 # small-codebook VQ decode layers (1 and 2 bits per weight), T = 8
 VQ1 = Workload("vq1", 5, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=5, vq8_m=1)
 VQ2X8 = Workload("vq2x8", 6, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=6, vq8_m=2)
+# the 3-bit module: three uint8 codes per group into three 256-entry codebooks
+VQ3X8 = Workload("vq3x8", 8, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=8, vq8_m=3)
 
 # the NVFP4 decode and prefill layers with a BF16 shared expert of the same
 # intermediate size (the routed experts, routing and tokens are those of
@@ -130,7 +132,7 @@ DECODE_SHARED = Workload("decode_shared", 1, 256, 8, 6144, 2048, (1, 8, 32), "nv
 PREFILL_SHARED = Workload("prefill_shared", 2, 256, 8, 6144, 2048, (4096,), "nvfp4", "zipf",
                           zipf_s=1.1, shared=True)
 
-WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED, VQ1, VQ2X8, DECODE_SHARED,
+WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED, VQ1, VQ2X8, VQ3X8, DECODE_SHARED,
                                  PREFILL_SHARED, DECODE_ROT)}
 
 

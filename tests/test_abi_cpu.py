@@ -169,7 +169,7 @@ def test_vq_record_layout():
     assert np.array_equal(w2[c2:c2 + 2 * H].view(np.uint16), parts[2][1])
 
 
-@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("m", [1, 2, 3])
 def test_vq8_record_layout(m):
     H, I = 272, 48
     rs = np.random.default_rng(m)
@@ -200,8 +200,8 @@ def test_vq8_record_layout(m):
     c2 = (H // 16) * ((I + 255) // 256) * tb
     assert np.array_equal(w2[c2:c2 + 2 * H].view(np.uint16), parts[2][1])
     with pytest.raises(moeq.MoeError):
-        moeq.pack_vq8_expert(parts[0], parts[1], parts[2], H, I, 3)
-    assert moeq.record_bytes(moeq.FMT_VQ8, 0, H, I, 3) == 0
+        moeq.pack_vq8_expert(parts[0], parts[1], parts[2], H, I, 4)
+    assert moeq.record_bytes(moeq.FMT_VQ8, 0, H, I, 4) == 0
 
 
 @pytest.mark.parametrize("H,I", [(256, 128), (272, 48)])

@@ -192,7 +192,7 @@ def test_vq_full_sampled():
             assert np.array_equal(to_np(moeq.dequant_q(lay, e, p)).astype(np.float64), W[p]), (e, p)
 
 
-@pytest.mark.parametrize("name", ["vq1", "vq2x8"])
+@pytest.mark.parametrize("name", ["vq1", "vq2x8", "vq3x8"])
 def test_vq8_full_sampled(name):
     """Small-codebook VQ (1 and 2 bits per weight) at the full layer size, T = 8."""
     wl = synth.WORKLOADS[name]

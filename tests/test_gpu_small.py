@@ -41,6 +41,11 @@ SMALL = {
                                   vq8_m=1),
     "vq8_2_ragged": synth.small_workload("vq8_2_ragged", E=8, k=2, H=208, I=48, T=9, fmt="vq8",
                                          cfg=121, vq8_m=2),
+    "vq8_3_ragged": synth.small_workload("vq8_3_ragged", E=8, k=2, H=208, I=48, T=21, fmt="vq8",
+                                         cfg=124, vq8_m=3),
+    "mixed3_m3": synth.small_workload("mixed3_m3", E=24, k=6, H=384, I=96, T=70, fmt="mixed3",
+                                      logits="hot", cfg=125, n_nvfp4=8, n_hot=4, hot_share=0.6,
+                                      vq8_m=3),
     "mixed3": synth.small_workload("mixed3", E=24, k=6, H=384, I=96, T=70, fmt="mixed3",
                                    logits="hot", cfg=122, n_nvfp4=8, n_hot=4, hot_share=0.6,
                                    vq8_m=2),
@@ -98,7 +103,7 @@ def test_dequant_bit_exact(name):
             assert np.array_equal(got, W[p]), (name, e, p)
 
 
-@pytest.mark.parametrize("name", ["vq8_1", "vq8_2_ragged", "mixed3"])
+@pytest.mark.parametrize("name", ["vq8_1", "vq8_2_ragged", "mixed3", "vq8_3_ragged"])
 def test_dequant_vq8(name):
     """Small-codebook VQ decode: exact with one code per group; with two, the
     hook's fp32(fp32(C_0 + C_1) * S) is within 2 roundings of the exact value."""

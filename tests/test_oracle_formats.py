@@ -346,3 +346,28 @@ def test_vq8_rejects_bad_shapes():
         oracle.vq8_dequant(np.zeros((2, 3, 2), np.uint8), _f16(np.ones(2)), [cb])
     with pytest.raises(ValueError):
         oracle.vq8_dequant(np.zeros((2, 3, 1), np.uint8), _f16(np.ones(2)), [_f16(np.zeros((16, 8)))])
+
+
+def test_vq8_three_codebooks_recover_all_codes():
+    # the 3-bit module: C_0[c] = 256^2 c would overflow fp16, so use
+    # C_0[c] = 16 c0, C_1[c] = c1 / 16 (c < 16 only: 4-bit codes in each), C_2
+    # one-hot columns; the summed row gives back every code
+    rs = np.random.default_rng(14)
+    c = np.arange(256, dtype=np.float64)
+    cb0 = _f16(np.repeat((16.0 * (c % 16))[:, None], 8, axis=1))
+    cb1 = _f16(np.repeat(((c % 16) / 16.0)[:, None], 8, axis=1))
+    cb2 = np.zeros((256, 8))
+    for code in range(8):
+        cb2[code, code] = 1024.0
+    codes = np.stack([rs.integers(0, 16, size=(5, 6)), rs.integers(0, 16, size=(5, 6)),
+                      rs.integers(0, 8, size=(5, 6))], axis=-1).astype(np.uint8)
+    W = oracle.vq8_dequant(codes, _f16(np.ones(5)), [cb0, cb1, _f16(cb2)]).reshape(5, 6, 8)
+    base = W.min(axis=2)                          # the column without the one-hot 1024
+    assert np.array_equal(np.round(base // 16), codes[:, :, 0])
+    assert np.array_equal(np.round((base % 16) * 16), codes[:, :, 1])
+    assert np.array_equal(np.argmax(W, axis=2), codes[:, :, 2])
+    # and it is the sum of the three single-codebook decodes
+    one = _f16(np.ones(5))
+    parts = [oracle.vq8_dequant(codes[:, :, j:j + 1], one, [cb][:1])
+             for j, cb in enumerate([cb0, cb1, _f16(cb2)])]
+    assert np.array_equal(W.reshape(5, 48), parts[0] + parts[1] + parts[2])
