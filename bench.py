@@ -326,7 +326,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--T", type=int, default=32, help="decode batch of the headline")
     ap.add_argument("--extra",
-                    default="decode1,decode8,prefill,vq,vq1,vq2x8,vq3x8,mixed8,mixed32,mixedhot8,"
+                    default="decode1,decode8,prefill,vq,vqprefill,vq1,vq2x8,vq3x8,vq2x8prefill,"
+                            "mixed8,mixed32,mixedhot8,"
                             "mixedhot32,shared1,shared8,shared32,prefillshared,rot1,rot8,rot32,"
                             "rotprefill",
                     help="comma list of other workloads to measure ('' for none)")
@@ -419,23 +420,37 @@ def main():
                 extra[name] = measure(nv_layer, wl, T, 30, 5, dev)
             elif name == "prefill":
                 extra[name] = measure(nv_layer, synth.PREFILL, 4096, 5, 2, dev, reps=4)
-            elif name == "vq":
+            elif name in ("vq", "vqprefill"):
                 wq = synth.VQ
-                log("building the VQ layer ...")
-                layers["vq"] = build_layer(
-                    wq.E, wq.H, wq.I, synth.tier_map(wq),
-                    vq_codes=lambda e, p: (synth.vq_codes(wq, e, p), synth.vq_scales(wq, e, p)),
-                    codebooks=[synth.vq_codebook(wq, p) for p in range(3)], device=dev, workers=16)
-                extra[name] = measure(layers["vq"], wq, 8, 30, 5, dev)
-            elif name in ("vq1", "vq2x8", "vq3x8"):
-                w8 = synth.WORKLOADS[name]
+                if "vq" not in layers:
+                    log("building the VQ layer ...")
+                    layers["vq"] = build_layer(
+                        wq.E, wq.H, wq.I, synth.tier_map(wq),
+                        vq_codes=lambda e, p: (synth.vq_codes(wq, e, p),
+                                               synth.vq_scales(wq, e, p)),
+                        codebooks=[synth.vq_codebook(wq, p) for p in range(3)], device=dev,
+                        workers=16)
+                if name == "vqprefill":
+                    wp = synth.Workload(name, 2, wq.E, wq.k, wq.H, wq.I, (4096,), "vq", "zipf",
+                                        zipf_s=1.1, vq_cfg=wq.vq_cfg)
+                    extra[name] = measure(layers["vq"], wp, 4096, 3, 1, dev, reps=4)
+                else:
+                    extra[name] = measure(layers["vq"], wq, 8, 30, 5, dev)
+            elif name in ("vq1", "vq2x8", "vq3x8", "vq1prefill", "vq2x8prefill", "vq3x8prefill"):
+                w8 = synth.WORKLOADS[name.replace("prefill", "")]
                 log(f"building the small-codebook VQ layer {name} ...")
                 lay8 = build_layer(
                     w8.E, w8.H, w8.I, synth.tier_map(w8),
                     vq8_codes=lambda e, p: (synth.vq8_codes(w8, e, p), synth.vq_scales(w8, e, p)),
                     codebooks8=[synth.vq8_codebooks(w8, p) for p in range(3)], vq8_m=w8.vq8_m,
                     device=dev, workers=16)
-                extra[name] = measure(lay8, w8, 8, 30, 5, dev)
+                if name.endswith("prefill"):
+                    # the same layer at T = 4096 with the prefill routing
+                    wp = synth.Workload(name, 2, w8.E, w8.k, w8.H, w8.I, (4096,), "vq8", "zipf",
+                                        zipf_s=1.1, vq_cfg=w8.vq_cfg, vq8_m=w8.vq8_m)
+                    extra[name] = measure(lay8, wp, 4096, 3, 1, dev, reps=4)
+                else:
+                    extra[name] = measure(lay8, w8, 8, 30, 5, dev)
                 del lay8
             elif name.startswith("mixedhot"):
                 # the mixed layer packed in both formats (resident), its tier map

@@ -158,7 +158,7 @@ int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_
         if (st) return st;
         for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
             if (!li.count[fmt]) continue;
-            st = prefill && prefill_fmt(fmt)
+            st = prefill && prefill_fmt(fmt, false)
                      ? launch_ffn_prefill(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T,
                                           k, h_f16, nullptr, 0, stream, gu)
                      : launch_ffn_decode(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T,
@@ -169,7 +169,7 @@ int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_
     }
     bool need_x16 = false;
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt)
-        need_x16 |= prefill && li.count[fmt] && prefill_fmt(fmt);
+        need_x16 |= prefill && li.count[fmt] && prefill_fmt(fmt, offsets == nullptr);
     if (need_x16) {
         const int st = launch_x_to_f16(x_bf16, T * li.view.H, x16, stream);
         if (st) return st;
@@ -177,7 +177,7 @@ int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!li.count[fmt]) continue;
         const int st =
-            prefill && prefill_fmt(fmt)
+            prefill && prefill_fmt(fmt, offsets == nullptr)
                 ? launch_ffn_prefill(li.view, fmt, li.count[fmt], x16, perm_src, offsets, T, k,
                                      h_f16, nullptr, 0, stream)
             : offsets ? launch_ffn_decode(li.view, fmt, li.count[fmt], x_bf16, perm_src, offsets,
@@ -197,7 +197,7 @@ int run_down(const LayerInfo& li, const uint16_t* h_f16, const int32_t* offsets,
         if (!li.count[fmt]) continue;
         uint16_t* h = const_cast<uint16_t*>(h_f16);
         const int st =
-            prefill && prefill_fmt(fmt)
+            prefill && prefill_fmt(fmt, offsets == nullptr)
                 ? launch_ffn_prefill(li.view, fmt, li.count[fmt], nullptr, nullptr, offsets, T, k,
                                      h, y_perm, 1, stream)
             : offsets ? launch_ffn_decode(li.view, fmt, li.count[fmt], nullptr, nullptr, offsets,

@@ -1,5 +1,6 @@
 // Expert FFN for large token batches (prefill): a grouped GEMM over the
-// active experts with NVFP4 (or BF16) weights decoded in registers.
+// active experts with their weights decoded in registers (NVFP4, BF16, and
+// VQ codes whose codebook rows come from LDS (small codebooks) or L2).
 //
 // Per active expert e with M_e rows (permuted order r0 .. r0+M_e):
 //   gate/up:  [g | u] = W13[e] X_e^T,  h = silu(g) * u      -> h (fp16)
@@ -44,14 +45,8 @@ constexpr int kBM = 128;           // tokens per work item
 #ifndef MOEQ_PF_STAGES
 #define MOEQ_PF_STAGES 2
 #endif
-#ifndef MOEQ_PF_BPIPE
-#define MOEQ_PF_BPIPE 0
-#endif
 #ifndef MOEQ_PF_ORDER
 #define MOEQ_PF_ORDER 1
-#endif
-#ifndef MOEQ_PF_PRIO
-#define MOEQ_PF_PRIO 0
 #endif
 constexpr int kPrefillWaves = MOEQ_PF_WAVES;
 constexpr int kPrefillStages = MOEQ_PF_STAGES;
@@ -66,6 +61,9 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 acc) {
 struct PrefillArgs {
     const uint8_t* pool;
     int64_t stride;
+    const uint8_t* cb[3];      // VQ codebooks (gate, up, down), per record at cb_stride
+    int64_t cb_stride;
+    const uint8_t* cb8[3];     // VQ8 codebooks (gate, up, down): [M][256][8] fp16
     const int32_t* rec;
     const int32_t* offsets;    // NULL: one expert whose rows are the tokens
     const int32_t* perm_src;   // NULL: identity
@@ -215,18 +213,29 @@ __device__ __forceinline__ f16x8 a_step(const AFrag& f, int s) {
     return nv_dequant8(c[s & 3], sv);
 }
 
-// Weight formats of the grouped GEMM: NA 32-row A tiles per wave, TB bytes
-// per 16-row x 128-input record tile, the per-lane fragment of one A tile
-// and one 128-input tile, and its fp16 A operand of K-step s.
+// Weight formats of the grouped GEMM.  NA 32-row A tiles per wave; NSUB A
+// operands (MFMAs) per K-step; group_bytes(K) bytes per 16-row record group;
+// load() reads the lane's fragment of one A tile for the 128-input step kb
+// (grp_base = the tile's first record group); step(f, s, j, ctx) is the fp16
+// A operand j of K-step s (inputs 64h + 8s .. +7 of the step); kScales: fp16
+// per-row scales follow the record's code tiles; cb_lds(phase): bytes of
+// codebooks the workgroup keeps in LDS; ctx: the lane's codebook base.
 struct PfNv {
     static constexpr int NA = 2;
-    static constexpr int TB = kNvTileBytes;
+    static constexpr int NSUB = 1;
+    static constexpr bool kScales = false;
+    static constexpr int cb_lds(int) { return 0; }
+    __device__ __forceinline__ static int64_t group_bytes(int K) {
+        return (int64_t)((K + kNvTileK - 1) / kNvTileK) * kNvTileBytes;
+    }
     using Frag = AFrag;
     __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
-                                                int lane, bool valid) {
-        load_a(f, grp_base, gstride, lane, valid);
+                                                int kb, int K, int lane, bool valid) {
+        load_a(f, grp_base + (int64_t)kb * kNvTileBytes, gstride, lane, valid);
     }
-    __device__ __forceinline__ static f16x8 step(const Frag& f, int s) { return a_step(f, s); }
+    __device__ __forceinline__ static f16x8 step(const Frag& f, int s, int, const void*) {
+        return a_step(f, s);
+    }
 };
 
 // BF16: lane L (row L & 31, half h = L >> 5) needs inputs 64h + 8s .. +7,
@@ -234,19 +243,24 @@ struct PfNv {
 // lane + 16 holds 64h + 32 + 8j (s = 4 + j), slice j of the tile.
 struct PfBf16 {
     static constexpr int NA = 1;
-    static constexpr int TB = kBf16TileBytes;
+    static constexpr int NSUB = 1;
+    static constexpr bool kScales = false;
+    static constexpr int cb_lds(int) { return 0; }
+    __device__ __forceinline__ static int64_t group_bytes(int K) {
+        return (int64_t)((K + kBf16TileK - 1) / kBf16TileK) * kBf16TileBytes;
+    }
     struct Frag {
         u32x4 c[8];
     };
     __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
-                                                int lane, bool valid) {
+                                                int kb, int K, int lane, bool valid) {
         if (!valid) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) f.c[s] = u32x4{0u, 0u, 0u, 0u};
             return;
         }
         const int row = lane & 31;
-        const uint8_t* tile = grp_base + (row >> 4) * gstride;
+        const uint8_t* tile = grp_base + (int64_t)kb * kBf16TileBytes + (row >> 4) * gstride;
         const int l0 = (row & 15) + 32 * (lane >> 5);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -254,8 +268,114 @@ struct PfBf16 {
             f.c[4 + j] = *reinterpret_cast<const u32x4*>(tile + 1024 * j + (l0 + 16) * 16);
         }
     }
-    __device__ __forceinline__ static f16x8 step(const Frag& f, int s) {
+    __device__ __forceinline__ static f16x8 step(const Frag& f, int s, int, const void*) {
         return bf16x8_to_f16x8(f.c[s]);
+    }
+};
+
+// VQ codes (8 inputs per code) in 256-input record tiles: for the 128-input
+// step kb, lane L (row L & 31, half h = L >> 5) needs the 8 groups of inputs
+// (kb & 1) * 128 + 64h + 8s, s = 0..7, which record lane
+// (row & 15) + 16 (2 (kb & 1) + h) holds.  Groups at or past K (the zero
+// codes of the padding still select a codebook row) give a zero operand.
+// Per-row fp16 scales are applied in the epilogue.
+//
+// M uint8 codes per group into M 256-entry codebooks held in LDS (one MFMA
+// per codebook row: every product exact, as in the decode kernels).
+// MOEQ_PF_VQ8_SUM: sum a group's codebook rows in fp32 and round once to fp16
+// (one MFMA instead of M).  Measured 10-12% faster at M = 2 and 3 (the LDS
+// lookups and occupancy limit these kernels, not the MFMAs); off, so that
+// every product stays exact as in the decode kernels.
+#ifndef MOEQ_PF_VQ8_SUM
+#define MOEQ_PF_VQ8_SUM 0
+#endif
+template <int M>
+struct PfVq8 {
+    static constexpr int NA = 2;
+    static constexpr int NSUB = MOEQ_PF_VQ8_SUM ? 1 : M;
+    static constexpr bool kScales = true;
+    static constexpr int cb_lds(int phase) { return (phase == 0 ? 2 : 1) * M * MOE_VQ8_NCODE * 16; }
+    __device__ __forceinline__ static int64_t group_bytes(int K) {
+        return (int64_t)((K + kVq8TileK - 1) / kVq8TileK) * kVq8TileBytesPerCode * M;
+    }
+    struct Frag {
+        uint32_t c[2 * M];
+        int nvalid;     // K-steps of the lane inside K
+    };
+    __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
+                                                int kb, int K, int lane, bool valid) {
+        const int row = lane & 31;
+        const int h = lane >> 5;
+        const int k0 = kb * 128 + 64 * h;
+        f.nvalid = valid ? max(0, min(8, (K - k0) / 8)) : 0;
+        const uint8_t* p = grp_base + (int64_t)(kb >> 1) * (kVq8TileBytesPerCode * M) +
+                           (row >> 4) * gstride +
+                           ((row & 15) + 16 * (2 * (kb & 1) + h)) * (8 * M);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int q = 0; q < M; ++q) {
+            u32x2 v = {0u, 0u};
+            if (valid) v = *reinterpret_cast<const u32x2*>(p + 8 * q);
+            f.c[2 * q] = v[0];
+            f.c[2 * q + 1] = v[1];
+        }
+    }
+    // ctx: the lane's projection codebooks in LDS ([M][256][8] fp16)
+    __device__ __forceinline__ static f16x8 row(const Frag& f, int s, int j, const void* ctx) {
+        const int byte = M * s + j;
+        const uint32_t code = (f.c[byte >> 2] >> (8 * (byte & 3))) & 0xffu;
+        return *(reinterpret_cast<const f16x8*>(ctx) + j * MOE_VQ8_NCODE + code);
+    }
+    __device__ __forceinline__ static f16x8 step(const Frag& f, int s, int j, const void* ctx) {
+        f16x8 r;
+        if constexpr (MOEQ_PF_VQ8_SUM && M > 1) {
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < M; ++jj) {
+                const f16x8 c = row(f, s, jj, ctx);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] += (float)c[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r[i] = (_Float16)v[i];
+        } else {
+            r = row(f, s, j, ctx);
+        }
+        return s < f.nvalid ? r : f16x8{};
+    }
+};
+
+// 16-bit VQ codes into a 65536 x 8 fp16 codebook read from L2 (a gather per
+// operand).
+struct PfVq {
+    static constexpr int NA = 2;
+    static constexpr int NSUB = 1;
+    static constexpr bool kScales = true;
+    static constexpr int cb_lds(int) { return 0; }
+    __device__ __forceinline__ static int64_t group_bytes(int K) {
+        return (int64_t)((K + kVqTileK - 1) / kVqTileK) * kVqTileBytes;
+    }
+    struct Frag {
+        u32x4 c;
+        int nvalid;
+    };
+    __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
+                                                int kb, int K, int lane, bool valid) {
+        const int row = lane & 31;
+        const int h = lane >> 5;
+        const int k0 = kb * 128 + 64 * h;
+        f.nvalid = valid ? max(0, min(8, (K - k0) / 8)) : 0;
+        f.c = u32x4{0u, 0u, 0u, 0u};
+        if (valid)
+            f.c = *reinterpret_cast<const u32x4*>(grp_base + (int64_t)(kb >> 1) * kVqTileBytes +
+                                                  (row >> 4) * gstride +
+                                                  ((row & 15) + 16 * (2 * (kb & 1) + h)) * 16);
+    }
+    // ctx: the lane's projection codebook in global memory
+    __device__ __forceinline__ static f16x8 step(const Frag& f, int s, int, const void* ctx) {
+        const uint32_t code = (f.c[s >> 1] >> (16 * (s & 1))) & 0xffffu;
+        const f16x8 r = vq_row(reinterpret_cast<const uint8_t*>(ctx), code);
+        return s < f.nvalid ? r : f16x8{};
     }
 };
 
@@ -292,7 +412,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
         locate_item<ID>(A.offsets, A.rec, A.E, A.fmt, A.rows, nnt, blockIdx.x, lane, ntile);
     if (it.e < 0) return;
     const int nkb = (K + kNvTileK - 1) / kNvTileK;
-    const int64_t gstride = (int64_t)nkb * PF::TB;            // bytes per row group
+    const int64_t gstride = PF::group_bytes(K);               // bytes per row group
     const int g0 = ntile * (BN / 16) + wave * 2 * NA;         // first row group of the wave
     const int mcount = min(kBM, it.me - it.m0);
     const int nbt = (mcount + 31) / 32;                      // 32-token B tiles in use
@@ -331,9 +451,27 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
     auto load_w = [&](int kb, typename PF::Frag (&wa)[NA]) {
 #pragma unroll
         for (int a = 0; a < NA; ++a)
-            PF::load(wa[a], base + (int64_t)(g0 + 2 * a) * gstride + (int64_t)kb * PF::TB,
-                     gstride, lane, valid[a]);
+            PF::load(wa[a], base + (int64_t)(g0 + 2 * a) * gstride, gstride, kb, K, lane,
+                     valid[a]);
     };
+    // the lane's codebooks: small ones copied into LDS by the workgroup (gate
+    // then up, or down), large ones read from L2; rows 16..31 of an A tile
+    // are up rows in the gate/up pass
+    const bool up_row = PHASE == 0 && (lane & 31) >= 16;
+    const void* ctx = nullptr;
+    if constexpr (PF::cb_lds(0) > 0) {
+        extern __shared__ _Float16 pf_cb[];
+        constexpr int NCH = PF::cb_lds(PHASE) / 16;        // 16-byte rows
+        constexpr int PER = NCH / (PHASE == 0 ? 2 : 1);
+        for (int i = tid; i < NCH; i += 64 * WV) {
+            const uint8_t* src = A.cb8[PHASE == 0 ? i / PER : 2] + (int64_t)(i % PER) * 16;
+            *reinterpret_cast<u32x4*>(pf_cb + (int64_t)i * 8) =
+                *reinterpret_cast<const u32x4*>(src);
+        }
+        ctx = pf_cb + (up_row ? PER * 8 : 0);
+    } else if constexpr (PF::kScales) {
+        ctx = A.cb[PHASE == 0 ? (up_row ? 1 : 0) : 2] + (int64_t)it.ridx * A.cb_stride;
+    }
 
     f32x16 acc[NA][4];
 #pragma unroll
@@ -373,57 +511,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
                 const int cofs = 8 * ((8 * h + s) ^ (lane & 15));
                 return *reinterpret_cast<const f16x8*>(xb + 32 * q * kNvTileK + cofs);
             };
-#if MOEQ_PF_BPIPE
-            // B fragments are read half a K-step ahead of their MFMAs: the
-            // reads of tiles 2, 3 of step s go out before the MFMAs of tiles
-            // 0, 1, and those of tiles 0, 1 of step s + 1 before the MFMAs of
-            // tiles 2, 3 (the scheduling barriers keep that order).
-            f16x8 bq[NB];
-            bq[0] = rd(0, 0);
-            if constexpr (NB > 1) bq[1] = rd(0, 1);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                f16x8 av[NA];
 #pragma unroll
-                for (int a = 0; a < NA; ++a) av[a] = PF::step(w[P][a], s);
-                if constexpr (NB > 2) bq[2] = rd(s, 2);
-                if constexpr (NB > 3) bq[3] = rd(s, 3);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < PF::NSUB; ++j) {
+                    f16x8 av[NA];
 #pragma unroll
-                for (int q = 0; q < (NB < 2 ? NB : 2); ++q)
+                    for (int a = 0; a < NA; ++a) av[a] = PF::step(w[P][a], s, j, ctx);
 #pragma unroll
-                    for (int a = 0; a < NA; ++a) acc[a][q] = mfma32(av[a], bq[q], acc[a][q]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (s < 7) {
-                    bq[0] = rd(s + 1, 0);
-                    if constexpr (NB > 1) bq[1] = rd(s + 1, 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int q = 0; q < NB; ++q) {
+                        const f16x8 b = rd(s, q);
 #pragma unroll
-                for (int q = 2; q < NB; ++q)
-#pragma unroll
-                    for (int a = 0; a < NA; ++a) acc[a][q] = mfma32(av[a], bq[q], acc[a][q]);
-            }
-#else
-#if MOEQ_PF_PRIO
-            __builtin_amdgcn_s_setprio(1);
-#endif
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                f16x8 av[NA];
-#pragma unroll
-                for (int a = 0; a < NA; ++a) av[a] = PF::step(w[P][a], s);
-#pragma unroll
-                for (int q = 0; q < NB; ++q) {
-                    const f16x8 b = rd(s, q);
-#pragma unroll
-                    for (int a = 0; a < NA; ++a) acc[a][q] = mfma32(av[a], b, acc[a][q]);
+                        for (int a = 0; a < NA; ++a) acc[a][q] = mfma32(av[a], b, acc[a][q]);
+                    }
                 }
             }
-#if MOEQ_PF_PRIO
-            __builtin_amdgcn_s_setprio(0);
-#endif
-#endif
             // W(kb + 1) and X(kb + 1) must have landed; with three buffers
             // X(kb + 2) may still be in flight
             if (NS == 3 && ahead)
@@ -453,6 +555,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
             const int ga = g0 + 2 * a;
+            if constexpr (PF::kScales) {
+                // per-output-row fp16 scales after the code tiles: acc element
+                // e of this lane belongs to row (e / 4) * 8 + 4h + e % 4 of the
+                // 32-row tile (record group ga + (e >= 8), its row (e/4 % 2) * 8
+                // + 4h + e % 4)
+                const _Float16* sp =
+                    reinterpret_cast<const _Float16*>(base + (int64_t)nrg * gstride);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int r = ((e >> 2) & 1) * 8 + 4 * h + (e & 3);   // row in its group
+                    const int g = ga + (e >> 3);
+                    const int o = PHASE == 0 ? (g & 1) * A.I + 16 * (g >> 1) + r : 16 * g + r;
+                    if (g < nrg) acc[a][q][e] *= (float)sp[o];
+                }
+            }
             if (PHASE == 0 && ROT) {
                 if (ga >= nrg) continue;
                 const int ch = 16 * (ga >> 1) + 4 * h;
@@ -514,12 +631,14 @@ int launch_pf(const PrefillArgs& a, int64_t items, int phase, hipStream_t s) {
     const int64_t nblocks = 8 * ((items + 7) / 8) * nnt;
 #endif
     dim3 grid((unsigned)nblocks);
+    const size_t lds = (size_t)PF::cb_lds(phase);   // codebooks kept in LDS
     if (phase == 0 && a.gu) {
-        if constexpr (!kId) k_prefill<PF, 0, false, true><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
+        if constexpr (!kId)
+            k_prefill<PF, 0, false, true><<<grid, 64 * kPrefillWaves, lds, s>>>(a);
     } else if (phase == 0) {
-        k_prefill<PF, 0, ID><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
+        k_prefill<PF, 0, ID><<<grid, 64 * kPrefillWaves, lds, s>>>(a);
     } else {
-        k_prefill<PF, 1, ID><<<grid, 64 * kPrefillWaves, 0, s>>>(a);
+        k_prefill<PF, 1, ID><<<grid, 64 * kPrefillWaves, lds, s>>>(a);
     }
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
@@ -534,6 +653,11 @@ int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x
     PrefillArgs a;
     a.pool = phase == 0 ? L.pool13[fmt] : L.pool2[fmt];
     a.stride = phase == 0 ? L.stride13[fmt] : L.stride2[fmt];
+    for (int p = 0; p < 3; ++p) {
+        a.cb[p] = L.cb[p];
+        a.cb8[p] = L.cb8[p];
+    }
+    a.cb_stride = L.cb_stride;
     a.rec = L.rec;
     a.offsets = offsets;
     a.perm_src = perm_src;
@@ -552,12 +676,21 @@ int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x
     // sum over experts of ceil(M_e / 128) <= T*k / 128 + (number of active experts)
     const int64_t items = tk / kBM + active;
     if (items == 0) return MOE_OK;
-    const bool id = offsets == nullptr;
-    if (fmt == MOE_FMT_BF16)
-        return id ? launch_pf<PfBf16, true>(a, items, phase, s)
-                  : launch_pf<PfBf16, false>(a, items, phase, s);
-    return id ? launch_pf<PfNv, true>(a, items, phase, s)
-              : launch_pf<PfNv, false>(a, items, phase, s);
+    const bool id = offsets == nullptr;   // NVFP4 and BF16 only (prefill_fmt)
+    switch (fmt) {
+        case MOE_FMT_BF16:
+            return id ? launch_pf<PfBf16, true>(a, items, phase, s)
+                      : launch_pf<PfBf16, false>(a, items, phase, s);
+        case MOE_FMT_VQ:
+            return launch_pf<PfVq, false>(a, items, phase, s);
+        case MOE_FMT_VQ8:
+            if (L.vq8_m == 1) return launch_pf<PfVq8<1>, false>(a, items, phase, s);
+            if (L.vq8_m == 3) return launch_pf<PfVq8<3>, false>(a, items, phase, s);
+            return launch_pf<PfVq8<2>, false>(a, items, phase, s);
+        default:
+            return id ? launch_pf<PfNv, true>(a, items, phase, s)
+                      : launch_pf<PfNv, false>(a, items, phase, s);
+    }
 }
 
 }  // namespace moeq

@@ -116,11 +116,13 @@ inline size_t shared_part_bytes(int64_t T, int32_t I) {
 }
 int launch_shared_decode(const LayerView& L, int fmt, const uint16_t* x_bf16, int64_t T,
                          uint16_t* h16, float* part, float* y, int phase, void* stream);
-// NVFP4 and BF16 experts at T >= kPrefillMinTokens use the grouped-GEMM
-// kernels (perm_src == offsets == NULL: the identity map of a one-expert
-// layer).
+// Experts at T >= kPrefillMinTokens use the grouped-GEMM kernels, every
+// format for routed layers; the identity map of a one-expert layer
+// (perm_src == offsets == NULL) only for NVFP4 and BF16.
 constexpr int64_t kPrefillMinTokens = 128;
-inline bool prefill_fmt(int fmt) { return fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16; }
+inline bool prefill_fmt(int fmt, bool identity) {
+    return !identity || fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16;
+}
 int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,
                        const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,
                        uint16_t* h16, float* y_perm, int phase, void* stream,

@@ -299,3 +299,23 @@ def test_rotated_full_sampled(T):
     experts = pick(offsets, n=2, seed=T + 40)
     check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
     check_combine_property(wl, r)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["vq2x8", "vq"])
+def test_vq_prefill_full_sampled(name):
+    """VQ layers (2 x 8-bit codes with LDS codebooks; 16-bit codes from L2) at
+    T = 4096 with the prefill routing: the grouped-GEMM path."""
+    import dataclasses
+    base = synth.WORKLOADS[name]
+    wl = dataclasses.replace(base, cfg=2, T=(4096,), logits="zipf", zipf_s=1.1)
+    say("vq prefill full", name)
+    lay = layer(name)
+    x_bits, lg, r = run_forward(wl, lay, 4096)
+    ids, w, offsets, perm_src = check_routing(wl, lg, r)
+    counts = np.diff(offsets)
+    experts = pick(offsets, n=2, seed=5)
+    act = np.nonzero(counts > 0)[0]
+    experts.append(int(act[np.argmin(counts[act])]))
+    check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
+    check_combine_property(wl, r)

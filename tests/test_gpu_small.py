@@ -74,6 +74,20 @@ SMALL = {
     "rot_bf16_prefill": synth.small_workload("rot_bf16_prefill", E=6, k=2, H=256, I=128,
                                              T=200, fmt="nv_bf16", cfg=174, n_nvfp4=3,
                                              rot=True),
+    # VQ codes in the grouped GEMM: small codebooks in LDS (1-3 codes per
+    # group) and 16-bit codes from L2, inputs not a multiple of the 256-input
+    # tile (zero codes past K still select a row: masked), a rotated layer
+    "vq8_2_prefill": synth.small_workload("vq8_2_prefill", E=8, k=2, H=208, I=80, T=300,
+                                          fmt="vq8", logits="zipf", zipf_s=1.1, cfg=126,
+                                          vq8_m=2),
+    "vq8_3_prefill": synth.small_workload("vq8_3_prefill", E=6, k=2, H=272, I=48, T=200,
+                                          fmt="vq8", cfg=127, vq8_m=3),
+    "vq8_1_prefill": synth.small_workload("vq8_1_prefill", E=6, k=3, H=400, I=144, T=150,
+                                          fmt="vq8", cfg=128, vq8_m=1),
+    "vq_prefill": synth.small_workload("vq_prefill", E=8, k=2, H=336, I=64, T=260, fmt="vq",
+                                       cfg=129),
+    "rot_vq8_prefill": synth.small_workload("rot_vq8_prefill", E=8, k=2, H=256, I=128, T=200,
+                                            fmt="vq8", cfg=176, vq8_m=2, rot=True),
 }
 
 _layers = {}
