@@ -184,11 +184,18 @@ class Runner:
         for i in range(max(1, (warmup + group - 1) // group)):
             graphs[i % ng].replay()
         torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps // group + 1)]
         t0 = time.perf_counter()
+        ev[0].record()
         for i in range(steps // group):
             graphs[i % ng].replay()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return time.perf_counter() - t0, group
+        dt = time.perf_counter() - t0
+        # per-step time of each replay (HIP events between replays)
+        self.replay_step_ms = [ev[i].elapsed_time(ev[i + 1]) / group
+                               for i in range(steps // group)]
+        return dt, group
 
     def bytes_of(self, r, which):
         """Algorithmic packed-weight bytes of batch r: 'all' (codes + scales
@@ -223,10 +230,13 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16, shared=None):
     all_bytes = sum(rn.bytes_of(r, "all") for r in idx)
     gu_bytes = sum(rn.bytes_of(r, "gateup") for r in idx_e)
     gu_s = sum(gu_ms) / 1e3
+    import numpy as np
+    q = np.percentile(rn.replay_step_ms, [10, 50, 90])
     res = {
         "T": T,
         "tokens_per_s": T * steps / dt,
         "ms_per_step": dt / steps * 1e3,
+        "step_ms_p10_p50_p90": [float(v) for v in q],
         "tokens_per_s_eager": T * steps / dte,
         "ms_per_step_eager": dte / steps * 1e3,
         "steps_per_graph": group,
@@ -366,6 +376,21 @@ def main():
         copy_gbs = 3 * 2 * n / (time.perf_counter() - t0) / 1e9
         log(f"plain 1 GiB copy: {copy_gbs:.0f} GB/s (read + write)")
         del src, dst
+    # the HBM read rate the weight-streaming kernels' kind of load reaches on
+    # this box (a 4 GiB buffer, read once per launch)
+    probe = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    sink = moeq.probe_read(probe)
+    for _ in range(2):
+        moeq.probe_read(probe, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        moeq.probe_read(probe, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * probe.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    log(f"HBM read probe (moe_probe_read, 4 GiB): {read_gbs:.0f} GB/s")
+    del probe, sink
     wl = synth.DECODE
     t0 = time.perf_counter()
     log("building the NVFP4 decode layer (256 experts, H 6144, I 2048) ...")
@@ -512,6 +537,7 @@ def main():
                    "experts_touched_mean": head["experts_touched_mean"],
                    "parallelism": "1 GPU"},
         "packed_GBps": head["packed_GBps"],
+        "hbm_read_probe_GBps": read_gbs,
         "roofline": {"bound": "hbm",
                      "kernel": "k_ffn<NvFmt, 1, 1, 2, 0, 4, false, false, false> (NVFP4 gate/up + SwiGLU)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

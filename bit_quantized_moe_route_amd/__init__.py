@@ -108,6 +108,7 @@ _PROTOS = {
     "moe_record_table": (ctypes.c_int, [_P, _I32, _P, _P]),
     "moe_record_table_resident": (ctypes.c_int, [_P, _I32, _P]),
     "moe_dequant_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _I32, _I32, _P, _P]),
+    "moe_probe_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
 }
 
 _lib = None
@@ -631,6 +632,21 @@ def combine_shared(y_perm, inv_perm, topk_w, y_shared, out=None):
                                     _dptr(y_shared), T, k, H, _dptr(out), _stream(y_perm.device)),
            "moe_combine_shared")
     return out
+
+
+PROBE_BLOCKS = 2048
+
+
+def probe_read(buf, sink=None):
+    """Read a device tensor once with the weight kernels' kind of loads (a
+    measurement aid); returns the per-workgroup XOR sink."""
+    torch = _torch()
+    _need_cuda(buf)
+    if sink is None:
+        sink = torch.empty(PROBE_BLOCKS, dtype=torch.int32, device=buf.device)
+    _check(lib().moe_probe_read(_dptr(buf), buf.numel() * buf.element_size(), _dptr(sink),
+                                _stream(buf.device)), "moe_probe_read")
+    return sink
 
 
 def dequant_q(layer, expert, proj):

@@ -413,6 +413,15 @@ int moe_combine_shared(const float* y_perm, const int32_t* inv_perm, const float
     return launch_combine(y_perm, inv_perm, topk_w, y_shared, T, k, H, out, stream);
 }
 
+int moe_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    g_last_error.clear();
+    if (!buf || !sink) return fail(MOE_EINVAL, "moe_probe_read: null pointer");
+    if (bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+        return fail(MOE_EINVAL, "moe_probe_read: bytes and buf must be multiples of 16");
+    if (bytes == 0) return MOE_OK;
+    return launch_probe_read(buf, bytes, sink, MOE_PROBE_BLOCKS, stream);
+}
+
 int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj, float* out,
                   void* stream) {
     g_last_error.clear();

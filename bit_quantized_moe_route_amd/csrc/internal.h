@@ -138,5 +138,6 @@ int launch_rot_out(const LayerView& L, float* y, const int32_t* offsets, int64_t
                    void* stream);
 int launch_dequant(const LayerView& L, int fmt, int32_t rec_index, int32_t proj,
                    float* out, void* stream);
+int launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, void* stream);
 
 }  // namespace moeq

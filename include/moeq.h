@@ -487,6 +487,20 @@ int moe_record_table_resident(const uint8_t* fmt_host, int32_t E, int32_t* rec);
 int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj,
                   float* out, void* stream);
 
+/* ------------------------------------------------------ measurement aid */
+
+/* Workgroups moe_probe_read launches (the size of its sink). */
+#define MOE_PROBE_BLOCKS 2048
+
+/*
+ * moe_probe_read -- read `bytes` of [device] buf once with 16-byte
+ * non-temporal loads (the weight-streaming kernels' kind of load) and write
+ * the XOR of what each workgroup read to sink [device] uint32
+ * [MOE_PROBE_BLOCKS]: timing it gives the HBM read rate those kernels can
+ * reach.  bytes must be a multiple of 16 and buf 16-byte aligned.
+ */
+int moe_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -115,7 +115,7 @@ def _nv_record_offsets(n, kin, rg_step, rg_off):
     return code_off, scale_off
 
 
-@pytest.mark.parametrize("H,I", [(256, 128), (144, 48)])
+@pytest.mark.parametrize("H,I", [(256, 128), (144, 48), (2304, 1152)])
 def test_nvfp4_record_layout(H, I):
     rs = np.random.default_rng(H)
     mats = []

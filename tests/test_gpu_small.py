@@ -510,3 +510,17 @@ def test_rotation_changes_nothing_for_unrotated_weights():
     b = moeq.forward(rot, x, lg, wl.k)["out"]
     # bf16 rounding of the rotated weights: a few 2^-9 relative per weight
     assert_rows_close(to_np(b), to_np(a).astype(np.float64), "rotated vs plain", tol=2e-2)
+
+
+# ------------------------------------------------------------------ measurement aid
+
+@pytest.mark.parametrize("nbytes", [1 << 20, (1 << 20) + 48, 16])
+def test_probe_read_reads_every_word_once(nbytes):
+    """moe_probe_read's per-workgroup XORs combine to the XOR of every 32-bit
+    word of the buffer (a word read twice or never would break it)."""
+    say("probe read", nbytes)
+    g = np.random.default_rng(nbytes)
+    words = g.integers(0, 2**31, size=nbytes // 4, dtype=np.int64).astype(np.int32)
+    sink = moeq.probe_read(torch.from_numpy(words).to(DEV))
+    got = np.bitwise_xor.reduce(to_np(sink).astype(np.uint32))
+    assert got == np.bitwise_xor.reduce(words.astype(np.uint32))
