@@ -105,6 +105,7 @@ class Runner:
         self.out = torch.empty((T, H), dtype=f32, device=dev)
         self.ws = moeq.gateup_workspace(layer, T, k)
         self.pws = moeq.permute_workspace(T, k, E, dev)
+        self.lws = moeq.layer_workspace(layer, T, k)
         self.shared = shared
         if shared is not None:
             self.y_sh = torch.empty((T, H), dtype=f32, device=dev)
@@ -113,39 +114,47 @@ class Runner:
         self.ev_sh = []
 
     def step(self, r, timed):
+        """One layer forward on batch r.  Untimed (warm-up and the graph
+        replays that give the headline figures): the one-call layer,
+        moe_layer_forward (fused for decode batches of <= 16 assignments).
+        Timed eager steps: the step-by-step calls, with HIP events around the
+        gate/up call (the kernel-level figures)."""
         moeq = self.moeq
         lg, x = self.batches[r % len(self.batches)]
+        if not timed:
+            y_sh = None
+            if self.shared is not None:
+                moeq.shared_ffn(self.shared, x, self.y_sh, self.sws)
+                y_sh = self.y_sh
+            moeq.layer_forward(self.layer, x, lg, self.k, y_shared=y_sh, out=self.out,
+                               ids=self.ids, w=self.w, ws=self.lws)
+            return
         moeq.route_permute(lg, self.k, self.wl.E, (self.ids, self.w) + self.perm, self.pws)
         counts, offsets, perm_src, inv_perm = self.perm
-        if timed:
-            # the C call with its arguments marshalled before the first event,
-            # so the events bracket the kernel rather than Python's overhead
-            import ctypes
-            L = moeq.lib()
-            args = (ctypes.byref(self.layer.c()), moeq._dptr(x), moeq._dptr(perm_src),
-                    moeq._dptr(offsets), self.T, self.k, moeq._dptr(self.h), moeq._dptr(self.ws),
-                    self.ws.numel(), moeq._stream(x.device))
-            e0 = self.torch.cuda.Event(enable_timing=True)
-            e1 = self.torch.cuda.Event(enable_timing=True)
-            e0.record()
-            rc = L.moe_expert_gateup_q(*args)
-            e1.record()
-            moeq._check(rc, "moe_expert_gateup_q")
-            self.ev.append((r, e0, e1))
-        else:
-            moeq.expert_gateup_q(self.layer, x, perm_src, offsets, self.k, self.h, self.ws)
+        # the C call with its arguments marshalled before the first event, so
+        # the events bracket the kernel rather than Python's overhead
+        import ctypes
+        L = moeq.lib()
+        args = (ctypes.byref(self.layer.c()), moeq._dptr(x), moeq._dptr(perm_src),
+                moeq._dptr(offsets), self.T, self.k, moeq._dptr(self.h), moeq._dptr(self.ws),
+                self.ws.numel(), moeq._stream(x.device))
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = L.moe_expert_gateup_q(*args)
+        e1.record()
+        moeq._check(rc, "moe_expert_gateup_q")
+        self.ev.append((r, e0, e1))
         moeq.expert_down_q(self.layer, self.h, offsets, self.k, self.y)
         if self.shared is None:
             moeq.combine(self.y, inv_perm, self.w, self.out)
             return
-        if timed:
-            e0 = self.torch.cuda.Event(enable_timing=True)
-            e1 = self.torch.cuda.Event(enable_timing=True)
-            e0.record()
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
         moeq.shared_ffn(self.shared, x, self.y_sh, self.sws)
-        if timed:
-            e1.record()
-            self.ev_sh.append((r, e0, e1))
+        e1.record()
+        self.ev_sh.append((r, e0, e1))
         moeq.combine_shared(self.y, inv_perm, self.w, self.y_sh, self.out)
 
     def run(self, steps, warmup):

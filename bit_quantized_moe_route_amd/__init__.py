@@ -95,6 +95,9 @@ _PROTOS = {
     "moe_shared_ffn_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64]),
     "moe_shared_ffn": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _I64, _P, _P, _SZ, _P]),
     "moe_combine_shared": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_layer_forward_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64, _I32]),
+    "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _I64, _I32, _P, _P,
+                                         _P, _P, _P, _SZ, _P]),
     "moe_quantize_nvfp4": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "moe_record_bytes": (_SZ, [ctypes.c_int, ctypes.c_int, _I32, _I32]),
     "moe_record_bytes_vq8": (_SZ, [ctypes.c_int, _I32, _I32, _I32]),
@@ -670,6 +673,43 @@ def side_stream(device):
     if key not in _side_streams:
         _side_streams[key] = torch.cuda.Stream(device=d)
     return _side_streams[key]
+
+
+def layer_workspace(layer, T, k):
+    torch = _torch()
+    n = lib().moe_layer_forward_workspace_bytes(ctypes.byref(layer.c()), T, k)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=layer.device)
+
+
+def layer_forward(layer, x, logits, k, y_shared=None, out=None, ids=None, w=None, ws=None):
+    """The whole routed layer in one C call (moe_layer_forward): returns
+    (topk_ids [T, k] int32, topk_w [T, k] fp32, out [T, H] fp32), with
+    y_shared (fp32 [T, H], a shared expert's output) added after the routed
+    sum when given.  Decode batches (T*k <= 16, k <= 8) of single-format,
+    unrotated layers run fused in two launches."""
+    torch = _torch()
+    _need_cuda(x, logits)
+    T = x.shape[0]
+    if tuple(logits.shape) != (T, layer.E) or logits.dtype != torch.float32:
+        raise ValueError("logits must be fp32 [T, E]")
+    if y_shared is not None:
+        _need_cuda(y_shared)
+        if tuple(y_shared.shape) != (T, layer.H) or y_shared.dtype != torch.float32:
+            raise ValueError("y_shared must be fp32 [T, H]")
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, layer.H), dtype=torch.float32, device=dev)
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = layer_workspace(layer, T, k)
+    _check(lib().moe_layer_forward(ctypes.byref(layer.c()), _dptr(x), _dptr(logits), T, k,
+                                   _dptr(y_shared), _dptr(ids),
+                                   _dptr(w), _dptr(out), _dptr(ws), ws.numel(), _stream(dev)),
+           "moe_layer_forward")
+    return ids, w, out
 
 
 def forward(layer, x, logits, k, shared=None, overlap=False):

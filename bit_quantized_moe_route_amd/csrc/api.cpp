@@ -141,6 +141,34 @@ size_t shared_ws(const moe_qlayer* L, int64_t T) {
            align_up(shared_part_bytes(T, L->I));
 }
 
+// moe_layer_forward: the small-batch fused path needs only h [T*k, I] fp16;
+// the step-by-step path counts | offsets | perm_src | inv_perm | the permute
+// workspace | the expert-FFN workspace | y_perm [T*k, H] fp32.
+bool layer_small_ok(const LayerInfo& li, int64_t T, int32_t k) {
+    int nfmt = 0;
+    for (int f = MOE_FMT_NVFP4; f < kNumFmt; ++f) nfmt += li.count[f] > 0;
+    return nfmt == 1 && !li.view.rot && li.view.E <= 256 && k <= 8 &&
+           T * k <= kSmallFusedAssign;
+}
+
+struct LayerWs {
+    size_t counts, offsets, perm_src, inv_perm, pws, ffn, y_perm, total;
+};
+
+LayerWs layer_ws(const moe_qlayer* L, int64_t T, int32_t k) {
+    LayerWs w;
+    const size_t tk = (size_t)T * k;
+    w.counts = 0;
+    w.offsets = w.counts + align_up((size_t)L->E * 4);
+    w.perm_src = w.offsets + align_up((size_t)(L->E + 1) * 4);
+    w.inv_perm = w.perm_src + align_up(tk * 4);
+    w.pws = w.inv_perm + align_up(tk * 4);
+    w.ffn = w.pws + align_up(permute_ws_bytes(T, k, L->E));
+    w.y_perm = w.ffn + ffn_ws(L, T, k);
+    w.total = w.y_perm + align_up(tk * L->H * 4);
+    return w;
+}
+
 // Gate/up + SwiGLU of every format present.  perm_src == offsets == NULL is
 // the identity map of a one-expert layer (k = 1; part: the decode path's
 // partial sums).  x16 [T, H] is workspace for the fp16 copy of x that the
@@ -411,6 +439,51 @@ int moe_combine_shared(const float* y_perm, const int32_t* inv_perm, const float
     if (!y_perm || !inv_perm || !topk_w || !y_shared || !out)
         return fail(MOE_EINVAL, "moe_combine_shared: null pointer");
     return launch_combine(y_perm, inv_perm, topk_w, y_shared, T, k, H, out, stream);
+}
+
+size_t moe_layer_forward_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k) {
+    if (!layer || T < 0 || k < 1 || layer->E < 1 || layer->H <= 0 || layer->I <= 0) return 0;
+    return layer_ws(layer, T, k).total;
+}
+
+int moe_layer_forward(const moe_qlayer* layer, const uint16_t* x_bf16, const float* logits,
+                      int64_t T, int32_t k, const float* y_shared, int32_t* topk_ids,
+                      float* topk_w, float* out, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    LayerInfo li;
+    int st = check_layer("moe_layer_forward", layer, li);
+    if (st) return st;
+    st = check_route_sizes("moe_layer_forward", T, layer->E, k);
+    if (st) return st;
+    if (layer->H % 4) return fail(MOE_EINVAL, "moe_layer_forward: H % 4 != 0");
+    if (T == 0) return MOE_OK;
+    if (!x_bf16 || !logits || !topk_ids || !topk_w || !out)
+        return fail(MOE_EINVAL, "moe_layer_forward: null pointer");
+    const LayerWs lw = layer_ws(layer, T, k);
+    if (!ws || ws_bytes < lw.total)
+        return fail(MOE_EWORKSPACE,
+                    "moe_layer_forward: workspace needs " + std::to_string(lw.total) + " bytes");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+        return fail(MOE_EINVAL, "moe_layer_forward: workspace must be 256-byte aligned");
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    if (layer_small_ok(li, T, k)) {
+        int fmt = MOE_FMT_NVFP4;
+        while (!li.count[fmt]) ++fmt;
+        return launch_layer_small(li.view, fmt, x_bf16, logits, T, k, topk_ids, topk_w,
+                                  reinterpret_cast<uint16_t*>(w), y_shared, out, stream);
+    }
+    int32_t* counts = reinterpret_cast<int32_t*>(w + lw.counts);
+    int32_t* offsets = reinterpret_cast<int32_t*>(w + lw.offsets);
+    int32_t* perm_src = reinterpret_cast<int32_t*>(w + lw.perm_src);
+    int32_t* inv_perm = reinterpret_cast<int32_t*>(w + lw.inv_perm);
+    float* y_perm = reinterpret_cast<float*>(w + lw.y_perm);
+    st = moe_route_permute(logits, T, layer->E, k, topk_ids, topk_w, counts, offsets, perm_src,
+                           inv_perm, w + lw.pws, lw.ffn - lw.pws, stream);
+    if (st) return st;
+    st = moe_expert_ffn_q(layer, x_bf16, perm_src, offsets, T, k, y_perm, w + lw.ffn,
+                          lw.y_perm - lw.ffn, stream);
+    if (st) return st;
+    return launch_combine(y_perm, inv_perm, topk_w, y_shared, T, k, layer->H, out, stream);
 }
 
 int moe_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

@@ -21,7 +21,9 @@
 //   * the B operand is read straight from the bf16 tokens x (gate/up; each
 //     8-element fragment converted to fp16 in registers, exact for
 //     2^-14 <= |x| <= 65504) or from the fp16 activations h (down).
-#include "dev_common.h"
+#include <type_traits>
+
+#include "topk_dev.h"
 
 namespace moeq {
 
@@ -171,6 +173,12 @@ struct DecodeArgs {
     int rows;              // offsets == NULL: rows of the identity map
     int nsplit;            // PART kernels: workgroups splitting the input dimension
     float* part;           // PART kernels: fp32 [nsplit][rows][2I] partial g | u
+    // small-batch fused layer (ROUTE gate/up, k_down_combine)
+    const float* logits;   // fp32 [T, E]
+    int32_t* topk_ids;     // [T, k]: written by the gate/up kernel, read by down
+    float* topk_w;
+    const float* y_shared; // NULL or fp32 [T, H], added after the routed sum
+    float* out;            // fp32 [T, H]
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -395,6 +403,11 @@ constexpr int kPrefetch = MOEQ_PREFETCH;
 #define MOEQ_SH_PREFETCH 1
 #endif
 constexpr int kPrefetchShared = MOEQ_SH_PREFETCH;
+// ... for the routed gate/up kernel of the small-batch fused layer.
+#ifndef MOEQ_ROUTE_PREFETCH
+#define MOEQ_ROUTE_PREFETCH 1
+#endif
+constexpr int kPrefetchRoute = MOEQ_ROUTE_PREFETCH;
 // Waves per SIMD the register budget is sized for (latency hiding).
 #ifndef MOEQ_MIN_WAVES
 #define MOEQ_MIN_WAVES 2
@@ -416,18 +429,47 @@ constexpr int kMinWaves = MOEQ_MIN_WAVES;
 // fill the chip.)  ROT (gate/up of a rotated layer, with PART and nsplit = 1):
 // the B operand is the fp16 rotated row of each assignment (A.xbf points to
 // [rows, H] in permuted order) and the raw products go to A.part.
+// ROUTE (gate/up of the small-batch fused layer): blockIdx.y is assignment
+// a = t*k + j; each wave takes token t's top-k from the logits itself, the
+// expert of rank j is its one "row", and h goes to row a (token order, no
+// permutation); one workgroup per token writes the token's ids and weights.
+// Single-format layers only (the record index of expert e is e).
 template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID, bool PART = false,
-          bool ROT = false>
+          bool ROT = false, bool ROUTE = false>
 __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
     static_assert(!ROT || (PART && PHASE == 0 && !ID), "rotated gate/up writes raw products");
+    static_assert(!ROUTE || (PHASE == 0 && !ID && !PART && !ROT), "routed gate/up only");
     constexpr bool XBF = PHASE == 0 && !ROT;        // B operand is bf16
     constexpr int NM = PHASE == 0 ? 2 * RPW : RPW;   // weight tiles per input tile
     constexpr int SETS = WV / KS;                    // row sets per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const ActiveExpert ae =
-        ID ? ActiveExpert{blockIdx.y == 0 ? 0 : -1, 0, A.rows, 0}
-           : find_active_expert(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
+    ActiveExpert ae;
+    if constexpr (ROUTE) {
+        const int a = blockIdx.y;
+        const int t = a / A.k, j = a % A.k;
+        float top_v[MOE_MAX_K];
+        int top_i[MOE_MAX_K];
+        topk_select<4>(A.logits + (int64_t)t * A.E, A.E, A.k, lane, top_v, top_i);
+        int e = top_i[0];
+#pragma unroll
+        for (int jj = 1; jj < MOE_MAX_K; ++jj)
+            if (jj == j) e = top_i[jj];
+        if (j == 0 && blockIdx.x == 0 && wave == 0 && lane == 0) {
+            float w[MOE_MAX_K];
+            topk_weights(top_v, A.k, w);
+#pragma unroll
+            for (int jj = 0; jj < MOE_MAX_K; ++jj)
+                if (jj < A.k) {
+                    A.topk_ids[(int64_t)t * A.k + jj] = top_i[jj];
+                    A.topk_w[(int64_t)t * A.k + jj] = w[jj];
+                }
+        }
+        ae = ActiveExpert{e, a, 1, e};
+    } else {
+        ae = ID ? ActiveExpert{blockIdx.y == 0 ? 0 : -1, 0, A.rows, 0}
+                : find_active_expert(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
+    }
     if (ae.e < 0) return;
     const int c0 = blockIdx.z * 16 * NTT;
     if (c0 >= ae.me) return;
@@ -476,8 +518,10 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
         if (c >= ae.me)
             xrow[tt] = nullptr;
         else if (PHASE == 0)
-            xrow[tt] = A.xbf + (int64_t)(ROT ? ae.r0 + c
-                                             : ID ? c : A.perm_src[ae.r0 + c] / A.k) * A.H;
+            xrow[tt] = A.xbf + (int64_t)(ROT     ? ae.r0 + c
+                                         : ROUTE ? ae.r0 / A.k
+                                         : ID    ? c
+                                                 : A.perm_src[ae.r0 + c] / A.k) * A.H;
         else
             xrow[tt] = reinterpret_cast<const uint16_t*>(A.h16) + (int64_t)(ae.r0 + c) * A.I;
     }
@@ -498,12 +542,14 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
             // row c0 of the expert exists: a safe row for lanes past its rows
             const uint16_t* xsafe =
                 PHASE == 0
-                    ? A.xbf + (int64_t)(ROT ? ae.r0 + c0
-                                            : ID ? c0 : A.perm_src[ae.r0 + c0] / A.k) * A.H
+                    ? A.xbf + (int64_t)(ROT     ? ae.r0 + c0
+                                        : ROUTE ? ae.r0 / A.k
+                                        : ID    ? c0
+                                                : A.perm_src[ae.r0 + c0] / A.k) * A.H
                     : reinterpret_cast<const uint16_t*>(A.h16) + (int64_t)(ae.r0 + c0) * A.I;
             stream_tiles_vq<NTT, NM, XBF>(tb, cb, xrow, xsafe, ntt, K, kpart, kstride, lane, acc);
         } else {
-            stream_tiles<F, NTT, NM, ID ? kPrefetchShared : kPrefetch, XBF>(
+            stream_tiles<F, NTT, NM, ID ? kPrefetchShared : ROUTE ? kPrefetchRoute : kPrefetch, XBF>(
                 tb, cb, xrow, ntt, K, kpart, kstride, lane, acc);
         }
     }
@@ -619,6 +665,124 @@ __global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ 
 #pragma unroll
     for (int q = 0; q < 4; ++q) h[q] = (_Float16)silu_mul(g[q], u[q]);
     *reinterpret_cast<f16x4*>(h16 + (int64_t)c * I + n) = h;
+}
+
+// Down projection and gated combine of the small-batch fused layer, for one
+// token t (blockIdx.y) and one 16-row group g of the output (blockIdx.x):
+//   out[t, rows of g] = sum_{j<k} w[t, j] * (W_down[e_j] h[t*k + j])[rows of g]
+//                       (+ y_shared[t, rows of g])
+// in ascending j in fp32, e_j / w[t, j] as the routed gate/up kernel wrote
+// them.  Wave (sg, kloc) = (slot group, input part): it streams the tiles
+// kloc, kloc + 4, ... of W_down[e_j] for the NSL slots j of group sg, with
+// the h rows of those slots as the B operand's columns (column m = slot
+// NSL sg + m, so one B load serves every slot and column m of the m-th
+// product is the wanted one).  The 4 input parts are summed through LDS in
+// wave order and wave 0 takes the weighted sum over the slots, so each y_j
+// and the sum are the bits of the unfused down kernel and combine for the
+// same batch.  (Fixed combine order: "GLM-5.3-Flash-TR3-8bpw (K8)", Fidelity.)
+// NSL = 8 (NVFP4, VQ8: one group of 4-wave workgroups, two per CU) or 4
+// (BF16 and 16-bit VQ, whose A fragments take more registers: NG groups).
+constexpr int kDcKS = 4;     // waves splitting the input dimension of a slot group
+constexpr int kDcMaxK = 8;   // k of the fused path
+template <class F, int NSL, int NG>
+__global__ __launch_bounds__(64 * kDcKS * NG, kMinWaves) void k_down_combine(DecodeArgs A) {
+    constexpr int KS = kDcKS, NM = NSL, WV = KS * NG;
+    static_assert(NSL * NG <= 16, "slots are B columns");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int kloc = wave % KS;
+    const int sg = wave / KS;
+    const int t = blockIdx.y;
+    const int g = blockIdx.x;
+    extern __shared__ _Float16 lds_cb[];
+    if constexpr (F::kVq8) {
+        constexpr int CHUNKS = F::CODES * MOE_VQ8_NCODE;
+        for (int i = threadIdx.x; i < CHUNKS; i += 64 * WV)
+            *reinterpret_cast<u32x4*>(lds_cb + (int64_t)i * 8) =
+                *reinterpret_cast<const u32x4*>(A.cb8[2] + (int64_t)i * 16);
+        __syncthreads();
+    }
+    const int K = A.I;
+    const int nrg = A.H / 16;
+    const int nkb = tiles_k<F>(K);
+    const int j0 = sg * NM;                        // first slot of the group
+    const int nsl = min(NM, A.k - j0);             // its live slots (>= 1)
+    const int32_t* ids = A.topk_ids + (int64_t)t * A.k;
+    // the gate weights, loaded now for the epilogue (uniform: scalar loads)
+    float wts[kDcMaxK];
+#pragma unroll
+    for (int j = 0; j < kDcMaxK; ++j) wts[j] = j < A.k ? A.topk_w[(int64_t)t * A.k + j] : 0.f;
+    const uint8_t* tb[NM];
+    const uint8_t* cb[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        // slots past k repeat the last live one (same addresses: no new HBM bytes)
+        const int e = ids[j0 + min(m, nsl - 1)];
+        tb[m] = A.pool2 + (int64_t)e * A.stride2 + (int64_t)g * nkb * F::TB;
+        cb[m] = A.cb_down + (int64_t)e * A.cb_stride;
+    }
+    const int col = lane & 15;                     // B column = slot j0 + col
+    const uint16_t* xrow[1];
+    xrow[0] = col < nsl ? reinterpret_cast<const uint16_t*>(A.h16) +
+                              ((int64_t)t * A.k + j0 + col) * A.I
+                        : nullptr;
+    f32x4 acc[NM][1];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (F::kVq8) {
+        const _Float16* lcb[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) lcb[m] = lds_cb;
+        stream_tiles_vq8<1, NM, F::CODES, false>(tb, lcb, xrow, 1, K, kloc, KS, lane, acc);
+    } else if constexpr (F::kVq && MOEQ_VQ_GATHER_AHEAD) {
+        const uint16_t* xsafe =
+            reinterpret_cast<const uint16_t*>(A.h16) + ((int64_t)t * A.k + j0) * A.I;
+        stream_tiles_vq<1, NM, false>(tb, cb, xrow, xsafe, 1, K, kloc, KS, lane, acc);
+    } else {
+        stream_tiles<F, 1, NM, kPrefetch, false>(tb, cb, xrow, 1, K, kloc, KS, lane, acc);
+    }
+    // the KS input parts of each slot group, summed in wave order
+    __shared__ f32x4 red[WV][NM][64];
+    __shared__ f32x4 ys[NG][64];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) red[wave][m][lane] = acc[m][0];
+    __syncthreads();
+    if (kloc == 0) {
+#pragma unroll
+        for (int w = 1; w < KS; ++w)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[m][0] = acc[m][0] + red[wave + w][m][lane];
+        // this lane's slot: column col of product col
+        f32x4 y = acc[0][0];
+#pragma unroll
+        for (int m = 1; m < NM; ++m)
+            if (col == m) y = acc[m][0];
+        if constexpr (F::kVq) {
+            // per-output-channel scales of the slot's expert
+            const int e = ids[j0 + min(col, nsl - 1)];
+            const _Float16* sp = reinterpret_cast<const _Float16*>(
+                A.pool2 + (int64_t)e * A.stride2 + (int64_t)nrg * nkb * F::TB);
+            const int n0 = 16 * g + (lane >> 4) * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] *= (float)sp[n0 + i];
+        }
+        ys[sg][lane] = y;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // lane 16q + c of ys[sg] holds rows 4q .. 4q+3 of the group for slot NSL sg + c
+    const int q16 = lane & 48;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kDcMaxK; ++j) {
+        if (j >= A.k) break;
+        const f32x4 y = ys[j / NM][q16 + j % NM];
+        o = o + wts[j] * y;
+    }
+    if (col != 0) return;
+    const int64_t n = (int64_t)t * A.H + 16 * g + (lane >> 4) * 4;
+    if (A.y_shared) o = o + *reinterpret_cast<const f32x4*>(A.y_shared + n);
+    *reinterpret_cast<f32x4*>(A.out + n) = o;
 }
 
 template <class F>
@@ -773,10 +937,58 @@ DecodeArgs decode_args(const LayerView& L, int fmt, const uint16_t* x_bf16,
     a.rows = (int)T;
     a.nsplit = 1;
     a.part = nullptr;
+    a.logits = nullptr;
+    a.topk_ids = nullptr;
+    a.topk_w = nullptr;
+    a.y_shared = nullptr;
+    a.out = nullptr;
     return a;
 }
 
+template <class F>
+int launch_small_fmt(const DecodeArgs& a, int64_t T, hipStream_t s) {
+    // gate/up: the shape of the unfused decode kernel for <= 16 assignments
+    // (4 waves splitting the inputs of 2 row-pair groups), one grid row per
+    // assignment
+    const int nsets = (a.I / 16 + kRpwGateup - 1) / kRpwGateup;
+    dim3 g1((unsigned)nsets, (unsigned)(T * a.k), 1u);
+    k_ffn<F, 1, 4, kRpwGateup, 0, 4, false, false, false, true>
+        <<<g1, 256, codebook_lds_bytes<F>(0), s>>>(a);
+    MOEQ_CHECK_LAUNCH();
+    dim3 g2((unsigned)(a.H / 16), (unsigned)T, 1u);
+    constexpr bool kWide = std::is_same<F, NvFmt>::value || F::kVq8;   // 8 slots per wave
+    if (a.k <= 4)
+        k_down_combine<F, 4, 1><<<g2, 64 * kDcKS, codebook_lds_bytes<F>(1), s>>>(a);
+    else if constexpr (kWide)
+        k_down_combine<F, 8, 1><<<g2, 64 * kDcKS, codebook_lds_bytes<F>(1), s>>>(a);
+    else
+        k_down_combine<F, 4, 2><<<g2, 128 * kDcKS, codebook_lds_bytes<F>(1), s>>>(a);
+    MOEQ_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
 }  // namespace
+
+int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, const float* logits,
+                       int64_t T, int32_t k, int32_t* topk_ids, float* topk_w, uint16_t* h16,
+                       const float* y_shared, float* out, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    DecodeArgs a = decode_args(L, fmt, x_bf16, nullptr, nullptr, T, k, h16, nullptr);
+    a.logits = logits;
+    a.topk_ids = topk_ids;
+    a.topk_w = topk_w;
+    a.y_shared = y_shared;
+    a.out = out;
+    if (T == 0) return MOE_OK;
+    if (fmt == MOE_FMT_NVFP4) return launch_small_fmt<NvFmt>(a, T, s);
+    if (fmt == MOE_FMT_BF16) return launch_small_fmt<Bf16Fmt>(a, T, s);
+    if (fmt == MOE_FMT_VQ8) {
+        if (L.vq8_m == 1) return launch_small_fmt<Vq8Fmt<1>>(a, T, s);
+        if (L.vq8_m == 3) return launch_small_fmt<Vq8Fmt<3>>(a, T, s);
+        return launch_small_fmt<Vq8Fmt<2>>(a, T, s);
+    }
+    return launch_small_fmt<VqFmt>(a, T, s);
+}
 
 int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,
                       const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,

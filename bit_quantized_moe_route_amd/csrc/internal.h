@@ -136,6 +136,17 @@ int launch_rot_mid(const LayerView& L, const float* gu, const int32_t* offsets, 
                    uint16_t* h16, void* stream);
 int launch_rot_out(const LayerView& L, float* y, const int32_t* offsets, int64_t rows,
                    void* stream);
+// The small-batch fused layer (single-format, unrotated layers, E <= 256,
+// k <= 8, T*k <= kSmallFusedAssign): gate/up with the routing inside
+// (topk_ids / topk_w written, h16 [T*k, I] in token order), then down +
+// gated combine (+ y_shared) into out [T, H].
+#ifndef MOEQ_SMALL_ASSIGN
+#define MOEQ_SMALL_ASSIGN 16
+#endif
+constexpr int64_t kSmallFusedAssign = MOEQ_SMALL_ASSIGN;
+int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, const float* logits,
+                       int64_t T, int32_t k, int32_t* topk_ids, float* topk_w, uint16_t* h16,
+                       const float* y_shared, float* out, void* stream);
 int launch_dequant(const LayerView& L, int fmt, int32_t rec_index, int32_t proj,
                    float* out, void* stream);
 int launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, void* stream);

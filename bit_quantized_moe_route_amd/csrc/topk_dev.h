@@ -1,5 +1,5 @@
-// Device routine of the router top-k (shared by the route kernel and the
-// fused route + permute kernel).
+// Device routine of the router top-k (shared by the route kernel, the fused
+// route + permute kernel and the small-batch fused layer kernels).
 //
 // One wavefront per token.  Each lane holds E/64 (rounded up) logits.  k
 // rounds of a wave-wide argmax pick the experts in rank order: larger logit
@@ -48,24 +48,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return umax32(a, b);
 }
 
-// Top-k of one token's logits row; lane 0 writes ids[0..k) and w[0..k), and
-// the ids also to lds_ids[0..k) if that is not null.
+// Top-k of one token's logits row, the same in every lane: top_i[j] / top_v[j]
+// = id and logit of rank j (j < k).
 // Each round takes the wave's largest remaining key: first the largest
 // high half (the logit's monotone bits) over the lanes' best keys, then,
 // only if several lanes hold that logit, the largest low half (the lowest
 // id) among them.  The lane that owns the winner clears that key.
 template <int VPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
-                                            int32_t* __restrict__ ids, float* __restrict__ wout,
-                                            int* lds_ids = nullptr) {
+__device__ __forceinline__ void topk_select(const float* __restrict__ row, int E, int k, int lane,
+                                            float (&top_v)[MOE_MAX_K], int (&top_i)[MOE_MAX_K]) {
     uint64_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e = lane + 64 * i;
         key[i] = e < E ? make_key(row[e], e) : 0ull;
     }
-    float top_v[MOE_MAX_K];
-    int top_i[MOE_MAX_K];
 #pragma unroll
     for (int j = 0; j < MOE_MAX_K; ++j) {
         top_v[j] = 0.f;
@@ -102,19 +99,40 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
             }
         }
     }
-    if (lane == 0) {
-        float sum = 0.f;
-        float ex[MOE_MAX_K];
+}
+
+// The softmax weights of the chosen logits (fp32): w[j] = exp(v_j - v_0) /
+// sum_{i<k} exp(v_i - v_0).
+__device__ __forceinline__ void topk_weights(const float (&top_v)[MOE_MAX_K], int k,
+                                             float (&w)[MOE_MAX_K]) {
+    float sum = 0.f;
+    float ex[MOE_MAX_K];
 #pragma unroll
-        for (int j = 0; j < MOE_MAX_K; ++j) {
-            ex[j] = j < k ? expf(top_v[j] - top_v[0]) : 0.f;
-            sum += ex[j];
-        }
+    for (int j = 0; j < MOE_MAX_K; ++j) {
+        ex[j] = j < k ? expf(top_v[j] - top_v[0]) : 0.f;
+        sum += ex[j];
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) w[j] = ex[j] / sum;
+}
+
+// Top-k of one token's logits row; lane 0 writes ids[0..k) and w[0..k), and
+// the ids also to lds_ids[0..k) if that is not null.
+template <int VPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
+                                            int32_t* __restrict__ ids, float* __restrict__ wout,
+                                            int* lds_ids = nullptr) {
+    float top_v[MOE_MAX_K];
+    int top_i[MOE_MAX_K];
+    topk_select<VPL>(row, E, k, lane, top_v, top_i);
+    if (lane == 0) {
+        float w[MOE_MAX_K];
+        topk_weights(top_v, k, w);
 #pragma unroll
         for (int j = 0; j < MOE_MAX_K; ++j) {
             if (j < k) {
                 ids[j] = top_i[j];
-                wout[j] = ex[j] / sum;
+                wout[j] = w[j];
                 if (lds_ids) lds_ids[j] = top_i[j];
             }
         }

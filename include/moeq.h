@@ -10,6 +10,7 @@
  *   moe_expert_ffn_q  x [T, H], perm_src, ...  -> y_perm [T*k, H]
  *   moe_combine       y_perm, inv_perm, topk_w -> out [T, H]
  *
+ * (moe_layer_forward runs the four in one call, fused for decode batches),
  * and, for layers with a shared expert that every token passes through,
  *
  *   moe_shared_ffn      x [T, H]                   -> y_shared [T, H]
@@ -362,6 +363,38 @@ int moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_
 int moe_combine_shared(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
                        const float* y_shared, int64_t T, int32_t k, int32_t H, float* out,
                        void* stream);
+
+/* -------------------------------------------------------- whole layer */
+
+/*
+ * moe_layer_forward -- the whole routed layer in one call: moe_route_topk,
+ * moe_permute, moe_expert_ffn_q and moe_combine (moe_combine_shared when
+ * y_shared is not NULL), with every intermediate in the workspace.
+ * (The routed-expert forward: "GLM-5-NVFP4-MTP", Model Description and
+ * What's quantized.)
+ *
+ *   layer      as for moe_expert_ffn_q.
+ *   x_bf16     [device] bf16 [T, H]; logits [device] fp32 [T, E].
+ *   y_shared   [device] fp32 [T, H] or NULL: a shared expert's output
+ *              (moe_shared_ffn), added after the routed sum.
+ *   topk_ids, topk_w  [device] [T, k] out, as moe_route_topk writes them.
+ *   out        [device] fp32 [T, H] out.
+ *   workspace  [device] >= moe_layer_forward_workspace_bytes(layer, T, k)
+ *              bytes, 256-byte aligned; contents on return unspecified.
+ *
+ * Small batches of single-format, unrotated layers (T*k <= 16, k <= 8,
+ * E <= 256: decode) take a fused path of two launches and no permutation:
+ * the gate/up kernel ranks the token's experts from the logits itself, the
+ * down kernel forms the gated sum in ascending j.  Its results are the bits
+ * of the step-by-step calls on the same inputs (each expert's rows, partial
+ * sums and the combine are taken in the same order).  Other batches run the
+ * step-by-step calls.  Errors as for those calls (checked before any launch).
+ */
+size_t moe_layer_forward_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k);
+int moe_layer_forward(const moe_qlayer* layer, const uint16_t* x_bf16, const float* logits,
+                      int64_t T, int32_t k, const float* y_shared, int32_t* topk_ids,
+                      float* topk_w, float* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* ------------------------------------------------------- host-side packers */
 

@@ -387,6 +387,36 @@ def test_ffn_rejects_bad_shapes_and_workspace():
     assert L.moe_dequant_q(ctypes.byref(d), 0, 3, fake, N) == moeq.MOE_EINVAL
 
 
+def test_layer_forward_host_checks():
+    """moe_layer_forward: the step-by-step calls' checks, before any launch."""
+    L = moeq.lib()
+    fake = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x100000)          # 256-byte aligned stand-in
+    N = ctypes.c_void_p(0)
+    tm = np.full(8, moeq.FMT_NVFP4, np.uint8)
+    d = _fake_layer(tm)
+    need = L.moe_layer_forward_workspace_bytes(ctypes.byref(d), 4, 2)
+    # at least the step-by-step path's buffers: expert-FFN workspace + y_perm
+    assert need >= L.moe_ffn_workspace_bytes(ctypes.byref(d), 4, 2) + 4 * 2 * 256 * 4
+    assert need % 256 == 0
+    assert L.moe_layer_forward_workspace_bytes(None, 4, 2) == 0
+    args = lambda T, k, nbytes, w=ws: (ctypes.byref(d), fake, fake, T, k, N, fake, fake, fake, w,
+                                       nbytes, N)
+    assert L.moe_layer_forward(*args(0, 2, 0, N)) == moeq.MOE_OK            # T == 0
+    assert L.moe_layer_forward(*args(4, 2, need - 1)) == moeq.MOE_EWORKSPACE
+    assert L.moe_layer_forward(*args(4, 2, need, ctypes.c_void_p(0x100010))) == moeq.MOE_EINVAL
+    assert L.moe_layer_forward(*args(4, 9, need)) == moeq.MOE_EINVAL        # k > E
+    assert L.moe_layer_forward(ctypes.byref(d), N, fake, 4, 2, N, fake, fake, fake, ws, need,
+                               N) == moeq.MOE_EINVAL                          # x NULL
+    assert L.moe_layer_forward(ctypes.byref(d), fake, fake, 4, 2, N, fake, fake, N, ws, need,
+                               N) == moeq.MOE_EINVAL                          # out NULL
+    bad = tm.copy()
+    bad[5] = 9
+    d = _fake_layer(bad)
+    assert L.moe_layer_forward(*args(4, 2, need)) == moeq.MOE_EUNSUPPORTED
+    assert b"expert 5" in L.moe_last_error()
+
+
 # ---------------------------------------------------------------- rotation helpers
 
 def test_rot_sign_bytes_and_packing():

@@ -117,6 +117,35 @@ def test_decode_T1_full_forward():
         assert_rows_close(y_perm[row:row + 1], ref, f"decode T=1 expert {ids[0, j]}")
     out = oracle.combine(y, w)
     assert_rows_close(to_np(r["out"]), out, "decode T=1 out")
+    # the one-call layer (fused at this size): the same routing, the oracle's
+    # row, and the step-by-step calls' bits
+    x = torch.from_numpy(x_bits.view(np.int16)).to(DEV)
+    f_ids, f_w, f_out = moeq.layer_forward(lay, x, torch.from_numpy(lg).to(DEV), wl.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(f_ids), ids)
+    assert_rows_close(to_np(f_out), out, "decode T=1 layer_forward out")
+    assert torch.equal(f_w, r["topk_w"]) and torch.equal(f_out, r["out"])
+
+
+@pytest.mark.timeout(900)
+def test_decode_T2_layer_forward_full():
+    """Two tokens through the fused one-call layer (16 assignments): routing
+    bit-exact, the step-by-step calls' bits, and token 1's row against the
+    oracle (all 8 of its experts)."""
+    wl = synth.DECODE
+    say("decode T=2 layer_forward full")
+    lay = layer("decode")
+    x_bits, lg, r = run_forward(wl, lay, 2, rep=3)
+    ids, w, offsets, perm_src = check_routing(wl, lg, r)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(DEV)
+    f_ids, f_w, f_out = moeq.layer_forward(lay, x, torch.from_numpy(lg).to(DEV), wl.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(f_ids), ids)
+    assert torch.equal(f_w, r["topk_w"]) and torch.equal(f_out, r["out"])
+    y = np.zeros((1, wl.k, wl.H))
+    for j, ref in enumerate(pool_map([(wl.name, int(e), x_bits[1:2], 1) for e in ids[1]])):
+        y[0, j] = ref[0]
+    assert_rows_close(to_np(f_out)[1:2], oracle.combine(y, w[1:2]), "decode T=2 token 1 out")
 
 
 @pytest.mark.timeout(900)
