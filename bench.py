@@ -548,7 +548,7 @@ def main():
         "packed_GBps": head["packed_GBps"],
         "hbm_read_probe_GBps": read_gbs,
         "roofline": {"bound": "hbm",
-                     "kernel": "k_ffn<NvFmt, 1, 1, 2, 0, 4, false, false, false> (NVFP4 gate/up + SwiGLU)",
+                     "kernel": "k_ffn<NvFmt, 1, 1, 2, 0, 4, false, false, false, false> (NVFP4 gate/up + SwiGLU)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": head["gateup_bytes_per_launch"],
