@@ -7,17 +7,17 @@
 //   down:     Y_e = W_down[e] H_e^T                         -> y_perm (fp32)
 // ("GLM-5-NVFP4-MTP", What's quantized: gate, up and down projections.)
 //
-// Work item = (expert, 128-row tile of its tokens) x (256 weight rows).  A
+// Work item = (expert, 64-row tile of its tokens) x (256 weight rows).  A
 // workgroup of 4 waves owns one item; wave w owns 64 weight rows (two 32-row
-// A tiles of v_mfma_f32_32x32x16_f16) and all 128 tokens (four 32-token B
-// tiles), i.e. a 64 x 128 fp32 accumulator block.  (BF16 experts: 32
+// A tiles of v_mfma_f32_32x32x16_f16) and all 64 tokens (two 32-token B
+// tiles), i.e. a 64 x 64 fp32 accumulator block.  (BF16 experts: 32
 // weight rows per wave, since a raw bf16 A fragment takes four times the
 // registers of an NVFP4 one.)
 //   * weights: each wave loads its rows' packed NVFP4 tiles from HBM straight
 //     into registers (the next 128-input tile is in flight while the current
 //     one is used), decodes 8 weights at a time to fp16 (exact) right before
 //     the MFMA that uses them;
-//   * tokens: the 128 rows x 128 inputs fp16 tile is gathered (through
+//   * tokens: the 64 rows x 128 inputs fp16 tile is gathered (through
 //     perm_src for gate/up) into LDS with direct-to-LDS loads (no register
 //     round trip), double-buffered, XOR-swizzled against bank conflicts;
 //   * gate/up: a 32-row A tile is 16 gate rows + the 16 matching up rows, so
@@ -36,7 +36,14 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;           // tokens per work item
+// Tokens per work item, per weight format (the trait's BM): 64 for NVFP4
+// and small-codebook VQ, 128 for BF16 and 16-bit VQ.  (Measured at T = 4096:
+// 64-token items, three waves per SIMD, ran the NVFP4 passes 2-4% faster and
+// the small-codebook ones 5-15% faster than 128-token items at two waves per
+// SIMD, although each decoded weight then feeds half as many MFMAs; 16-bit
+// VQ, whose codebook rows are L2 gathers per item, ran 30% slower, and BF16
+// 1% slower.)
+constexpr int kBMMax = 128;
 // Workgroup shape: waves of 64 weight rows each, and token-tile buffers.
 // (Measured: 4 waves x 2 buffers beats 8 waves x 3 buffers and 8 x 2.)
 #ifndef MOEQ_PF_WAVES
@@ -47,6 +54,12 @@ constexpr int kBM = 128;           // tokens per work item
 #endif
 #ifndef MOEQ_PF_ORDER
 #define MOEQ_PF_ORDER 1
+#endif
+#ifndef MOEQ_PF_OCC
+#define MOEQ_PF_OCC 2
+#endif
+#ifndef MOEQ_PF_PIPE
+#define MOEQ_PF_PIPE 0
 #endif
 constexpr int kPrefillWaves = MOEQ_PF_WAVES;
 constexpr int kPrefillStages = MOEQ_PF_STAGES;
@@ -80,19 +93,19 @@ struct WorkItem {
 };
 
 // Locates work item w of the list (item-major, nnt weight tiles per item,
-// items = (expert, 128-row tile) over the active experts of `fmt` in
+// items = (expert, BM-row tile) over the active experts of `fmt` in
 // ascending expert id).  All offsets/record loads are issued up front (one
 // memory round trip); the item count comes from the same registers.
 // Returns e = -1 if w is past the end of the list.
 // ID: the identity map of a one-expert layer (rows 0 .. rows-1 of expert 0).
-template <bool ID>
+template <int BM, bool ID>
 __device__ __forceinline__ WorkItem locate_item(const int32_t* __restrict__ offsets,
                                                 const int32_t* __restrict__ rec, int E, int fmt,
                                                 int rows, int nnt, int blk, int lane,
                                                 int& ntile) {
     if constexpr (ID) {
 #if MOEQ_PF_ORDER == 0
-        const int total = (rows + kBM - 1) / kBM;
+        const int total = (rows + BM - 1) / BM;
         const int nwork = total * nnt;
         const int quota = (nwork + 7) / 8;
         const int slot = blk >> 3;
@@ -104,8 +117,8 @@ __device__ __forceinline__ WorkItem locate_item(const int32_t* __restrict__ offs
         const int want_item = (slot / nnt) * 8 + (blk & 7);
         ntile = slot % nnt;
 #endif
-        if (want_item * kBM >= rows) return WorkItem{-1, 0, 0, 0, 0};
-        return WorkItem{0, 0, rows, 0, want_item * kBM};
+        if (want_item * BM >= rows) return WorkItem{-1, 0, 0, 0, 0};
+        return WorkItem{0, 0, rows, 0, want_item * BM};
     }
     constexpr int kMaxChunks = MOE_MAX_E / 64;
     int o0[kMaxChunks], o1[kMaxChunks], rc[kMaxChunks], cnt[kMaxChunks];
@@ -121,7 +134,7 @@ __device__ __forceinline__ WorkItem locate_item(const int32_t* __restrict__ offs
     int total = 0;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
-        cnt[c] = (o1[c] > o0[c] && (rc[c] >> 24) == fmt) ? (o1[c] - o0[c] + kBM - 1) / kBM : 0;
+        cnt[c] = (o1[c] > o0[c] && (rc[c] >> 24) == fmt) ? (o1[c] - o0[c] + BM - 1) / BM : 0;
         int t = cnt[c];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
@@ -171,7 +184,7 @@ __device__ __forceinline__ WorkItem locate_item(const int32_t* __restrict__ offs
             r.r0 = __shfl(o0[c], owner);
             r.me = __shfl(o1[c], owner) - r.r0;
             r.ridx = __shfl(rc[c], owner) & 0xffffff;
-            r.m0 = (want - (__shfl(incl, owner) - __shfl(cnt[c], owner))) * kBM;
+            r.m0 = (want - (__shfl(incl, owner) - __shfl(cnt[c], owner))) * BM;
         }
         before += tot;
     }
@@ -221,6 +234,7 @@ __device__ __forceinline__ f16x8 a_step(const AFrag& f, int s) {
 // per-row scales follow the record's code tiles; cb_lds(phase): bytes of
 // codebooks the workgroup keeps in LDS; ctx: the lane's codebook base.
 struct PfNv {
+    static constexpr int BM = 64;
     static constexpr int NA = 2;
     static constexpr int NSUB = 1;
     static constexpr bool kScales = false;
@@ -242,6 +256,7 @@ struct PfNv {
 // s = 0..7: record lane (row & 15) + 32h holds 64h + 8j (s = j < 4), record
 // lane + 16 holds 64h + 32 + 8j (s = 4 + j), slice j of the tile.
 struct PfBf16 {
+    static constexpr int BM = 128;
     static constexpr int NA = 1;
     static constexpr int NSUB = 1;
     static constexpr bool kScales = false;
@@ -291,6 +306,7 @@ struct PfBf16 {
 #endif
 template <int M>
 struct PfVq8 {
+    static constexpr int BM = 64;
     static constexpr int NA = 2;
     static constexpr int NSUB = MOEQ_PF_VQ8_SUM ? 1 : M;
     static constexpr bool kScales = true;
@@ -348,6 +364,7 @@ struct PfVq8 {
 // 16-bit VQ codes into a 65536 x 8 fp16 codebook read from L2 (a gather per
 // operand).
 struct PfVq {
+    static constexpr int BM = 128;
     static constexpr int NA = 2;
     static constexpr int NSUB = 1;
     static constexpr bool kScales = true;
@@ -384,23 +401,32 @@ constexpr int pf_bn() {
     return 32 * PF::NA * kPrefillWaves;   // weight rows per work item
 }
 
-// WV waves per workgroup (32 NA weight rows each), NS token-tile buffers in
-// LDS (NS - 1 tiles in flight ahead of the one in use).  (They are
-// file-level constants, not template parameters: a __shared__ array sized by
-// a template parameter loses its host-side launch stub with this compiler.)
+// WV waves per workgroup (32 NA weight rows each), NS token-tile buffers of
+// PF::BM tokens in dynamic LDS (NS - 1 tiles in flight ahead of the one in
+// use).  (WV and NS are file-level constants, not template parameters: a
+// static __shared__ array sized by a template parameter lost its host-side
+// launch stub with this compiler; the token tiles now sit in dynamic LDS.)
 // ID: offsets / perm_src are the identity map of a one-expert layer.  ROT
 // (gate/up of a rotated layer): the token tile rows are the fp16 rotated rows
 // of the assignments (x16 = [rows, H] in permuted order) and the raw fp32
 // products go to A.gu instead of h.
 template <class PF, int PHASE, bool ID, bool ROT = false>
-__global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A) {
+#ifdef MOEQ_PF_NUMVGPR
+__attribute__((amdgpu_num_vgpr(MOEQ_PF_NUMVGPR)))
+#endif
+__global__ __launch_bounds__(64 * kPrefillWaves, MOEQ_PF_OCC) void k_prefill(PrefillArgs A) {
     static_assert(!ROT || (PHASE == 0 && !ID), "rotated: gate/up of a routed layer");
     constexpr int WV = kPrefillWaves;
     constexpr int NS = kPrefillStages;
     constexpr int NA = PF::NA;
     constexpr int BN = pf_bn<PF>();    // weight rows per work item
-    constexpr int JX = 32 / WV;        // 1 KB staging loads per wave per token tile
-    __shared__ _Float16 xs[kPrefillStages][kBM * kNvTileK];
+    constexpr int BM = PF::BM;         // tokens per work item
+    constexpr int NBM = BM / 32;       // 32-token B tiles per work item
+    constexpr int JX = BM / 4 / WV;    // 1 KB staging loads per wave per token tile
+    // dynamic LDS: NS token-tile buffers of BM x 128 fp16, then the codebooks
+    // the workgroup keeps in LDS (small-codebook VQ)
+    extern __shared__ _Float16 pf_lds[];
+    _Float16* const xs = pf_lds;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -409,12 +435,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
     const int nnt = (nrg + BN / 16 - 1) / (BN / 16);          // weight tiles of BN rows
     int ntile = 0;
     const WorkItem it =
-        locate_item<ID>(A.offsets, A.rec, A.E, A.fmt, A.rows, nnt, blockIdx.x, lane, ntile);
+        locate_item<BM, ID>(A.offsets, A.rec, A.E, A.fmt, A.rows, nnt, blockIdx.x, lane, ntile);
     if (it.e < 0) return;
     const int nkb = (K + kNvTileK - 1) / kNvTileK;
     const int64_t gstride = PF::group_bytes(K);               // bytes per row group
     const int g0 = ntile * (BN / 16) + wave * 2 * NA;         // first row group of the wave
-    const int mcount = min(kBM, it.me - it.m0);
+    const int mcount = min(BM, it.me - it.m0);
     const int nbt = (mcount + 31) / 32;                      // 32-token B tiles in use
     const uint8_t* base = A.pool + (int64_t)it.ridx * A.stride;
 
@@ -440,7 +466,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
             int kk = kb * kNvTileK + 8 * ((lane & 15) ^ (row & 15));
             if (kk >= K) kk = 0;
             __builtin_amdgcn_global_load_lds(xsrc + (int64_t)trow[j] * K + kk,
-                                             &xs[buf][4 * (JX * wave + j) * kNvTileK], 16, 0, 0);
+                                             xs + buf * (BM * kNvTileK) +
+                                                 4 * (JX * wave + j) * kNvTileK,
+                                             16, 0, 0);
         }
     };
 
@@ -460,7 +488,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
     const bool up_row = PHASE == 0 && (lane & 31) >= 16;
     const void* ctx = nullptr;
     if constexpr (PF::cb_lds(0) > 0) {
-        extern __shared__ _Float16 pf_cb[];
+        _Float16* const pf_cb = pf_lds + NS * BM * kNvTileK;
         constexpr int NCH = PF::cb_lds(PHASE) / 16;        // 16-byte rows
         constexpr int PER = NCH / (PHASE == 0 ? 2 : 1);
         for (int i = tid; i < NCH; i += 64 * WV) {
@@ -473,11 +501,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
         ctx = A.cb[PHASE == 0 ? (up_row ? 1 : 0) : 2] + (int64_t)it.ridx * A.cb_stride;
     }
 
-    f32x16 acc[NA][4];
+    f32x16 acc[NA][NBM];
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[a][q] = f32x16{};
+        for (int q = 0; q < NBM; ++q) acc[a][q] = f32x16{};
 
     const int h = lane >> 5;
     // The main loop, specialised for the number of live 32-token B tiles so
@@ -497,7 +525,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
             __builtin_amdgcn_s_waitcnt(kVmcnt0);
         __syncthreads();
         // B reads: row (lane & 31) of each 32-token tile, logical chunk 8h + s
-        const _Float16* xrow0 = &xs[0][(lane & 31) * kNvTileK];
+        const _Float16* xrow0 = xs + (lane & 31) * kNvTileK;
         auto step = [&](int kb, auto p_c) {
             constexpr int P = decltype(p_c)::value;
             const bool more = kb + 1 < nkb;
@@ -506,11 +534,43 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
             if (more) load_w(kb + 1, w[P ^ 1]);
             const bool ahead = kb + NS - 1 < nkb;
             if (ahead) issue_x(kb + NS - 1, (kb + NS - 1) % NS);
-            const _Float16* xb = xrow0 + (kb % NS) * (kBM * kNvTileK);
+            const _Float16* xb = xrow0 + (kb % NS) * (BM * kNvTileK);
             auto rd = [&](int s, int q) {
                 const int cofs = 8 * ((8 * h + s) ^ (lane & 15));
                 return *reinterpret_cast<const f16x8*>(xb + 32 * q * kNvTileK + cofs);
             };
+#if MOEQ_PF_PIPE
+            // software-pipelined: the A operands and B fragments of sub-step
+            // u + 1 are decoded / read before the MFMAs of sub-step u
+            constexpr int NU = 8 * PF::NSUB;
+            f16x8 av[2][NA], bv[2][NB];
+#pragma unroll
+            for (int a = 0; a < NA; ++a) av[0][a] = PF::step(w[P][a], 0, 0, ctx);
+#pragma unroll
+            for (int q = 0; q < NB; ++q) bv[0][q] = rd(0, q);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int c = u & 1;
+                const int s = u / PF::NSUB;
+                if (u + 1 < NU) {
+                    const int s1 = (u + 1) / PF::NSUB, j1 = (u + 1) % PF::NSUB;
+#pragma unroll
+                    for (int a = 0; a < NA; ++a) av[c ^ 1][a] = PF::step(w[P][a], s1, j1, ctx);
+#pragma unroll
+                    for (int q = 0; q < NB; ++q) bv[c ^ 1][q] = s1 != s ? rd(s1, q) : bv[c][q];
+                }
+#if MOEQ_PF_PIPE >= 2
+                __builtin_amdgcn_sched_barrier(0);
+#endif
+#pragma unroll
+                for (int q = 0; q < NB; ++q)
+#pragma unroll
+                    for (int a = 0; a < NA; ++a) acc[a][q] = mfma32(av[c][a], bv[c][q], acc[a][q]);
+#if MOEQ_PF_PIPE >= 2
+                __builtin_amdgcn_sched_barrier(0);
+#endif
+            }
+#else
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
 #pragma unroll
@@ -526,6 +586,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
                     }
                 }
             }
+#endif
             // W(kb + 1) and X(kb + 1) must have landed; with three buffers
             // X(kb + 2) may still be in flight
             if (NS == 3 && ahead)
@@ -539,16 +600,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
             if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{});
         }
     };
-    switch (nbt) {
-        case 1: run(std::integral_constant<int, 1>{}); break;
-        case 2: run(std::integral_constant<int, 2>{}); break;
-        case 3: run(std::integral_constant<int, 3>{}); break;
-        default: run(std::integral_constant<int, 4>{}); break;
+    if constexpr (NBM == 2) {
+        if (nbt == 1) run(std::integral_constant<int, 1>{});
+        else run(std::integral_constant<int, 2>{});
+    } else {
+        switch (nbt) {
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            default: run(std::integral_constant<int, 4>{}); break;
+        }
     }
 
     // epilogue: lane holds D[row 8(i/4) + 4h + i%4][token 32q + (lane & 31)]
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NBM; ++q) {
         const int tok = 32 * q + (lane & 31);
         if (q >= nbt || tok >= mcount) continue;
         const int64_t prow = it.r0 + it.m0 + tok;            // permuted row
@@ -616,9 +682,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 2) void k_prefill(PrefillArgs A
 namespace {
 
 template <class PF, bool ID>
-int launch_pf(const PrefillArgs& a, int64_t items, int phase, hipStream_t s) {
+int launch_pf(const PrefillArgs& a, int64_t tk, int64_t active, int phase, hipStream_t s) {
     constexpr bool kId = ID;
     constexpr int BN = pf_bn<PF>();
+    static_assert(PF::BM % 32 == 0 && PF::BM <= kBMMax, "token tile");
+    // sum over experts of ceil(M_e / BM) <= T*k / BM + (number of active experts)
+    const int64_t items = tk / PF::BM + active;
+    if (items == 0) return MOE_OK;
     const int nrg = (phase == 0 ? 2 * a.I : a.H) / 16;
     const int64_t nnt = (nrg + BN / 16 - 1) / (BN / 16);
 #if MOEQ_PF_ORDER == 0
@@ -631,7 +701,8 @@ int launch_pf(const PrefillArgs& a, int64_t items, int phase, hipStream_t s) {
     const int64_t nblocks = 8 * ((items + 7) / 8) * nnt;
 #endif
     dim3 grid((unsigned)nblocks);
-    const size_t lds = (size_t)PF::cb_lds(phase);   // codebooks kept in LDS
+    // token-tile buffers, then the codebooks kept in LDS (at most 64 KB)
+    const size_t lds = (size_t)kPrefillStages * PF::BM * kNvTileK * 2 + (size_t)PF::cb_lds(phase);
     if (phase == 0 && a.gu) {
         if constexpr (!kId)
             k_prefill<PF, 0, false, true><<<grid, 64 * kPrefillWaves, lds, s>>>(a);
@@ -672,24 +743,21 @@ int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x
     a.rows = (int)T;
     a.gu = phase == 0 ? gu : nullptr;
     const int64_t tk = T * k;
-    const int64_t active = tk < n_fmt ? tk : n_fmt;
-    // sum over experts of ceil(M_e / 128) <= T*k / 128 + (number of active experts)
-    const int64_t items = tk / kBM + active;
-    if (items == 0) return MOE_OK;
+    const int64_t act = tk < n_fmt ? tk : n_fmt;
     const bool id = offsets == nullptr;   // NVFP4 and BF16 only (prefill_fmt)
     switch (fmt) {
         case MOE_FMT_BF16:
-            return id ? launch_pf<PfBf16, true>(a, items, phase, s)
-                      : launch_pf<PfBf16, false>(a, items, phase, s);
+            return id ? launch_pf<PfBf16, true>(a, tk, act, phase, s)
+                      : launch_pf<PfBf16, false>(a, tk, act, phase, s);
         case MOE_FMT_VQ:
-            return launch_pf<PfVq, false>(a, items, phase, s);
+            return launch_pf<PfVq, false>(a, tk, act, phase, s);
         case MOE_FMT_VQ8:
-            if (L.vq8_m == 1) return launch_pf<PfVq8<1>, false>(a, items, phase, s);
-            if (L.vq8_m == 3) return launch_pf<PfVq8<3>, false>(a, items, phase, s);
-            return launch_pf<PfVq8<2>, false>(a, items, phase, s);
+            if (L.vq8_m == 1) return launch_pf<PfVq8<1>, false>(a, tk, act, phase, s);
+            if (L.vq8_m == 3) return launch_pf<PfVq8<3>, false>(a, tk, act, phase, s);
+            return launch_pf<PfVq8<2>, false>(a, tk, act, phase, s);
         default:
-            return id ? launch_pf<PfNv, true>(a, items, phase, s)
-                      : launch_pf<PfNv, false>(a, items, phase, s);
+            return id ? launch_pf<PfNv, true>(a, tk, act, phase, s)
+                      : launch_pf<PfNv, false>(a, tk, act, phase, s);
     }
 }
 
