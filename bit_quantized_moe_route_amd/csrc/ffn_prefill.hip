@@ -58,9 +58,6 @@ constexpr int kBMMax = 128;
 #ifndef MOEQ_PF_OCC
 #define MOEQ_PF_OCC 2
 #endif
-#ifndef MOEQ_PF_PIPE
-#define MOEQ_PF_PIPE 0
-#endif
 constexpr int kPrefillWaves = MOEQ_PF_WAVES;
 constexpr int kPrefillStages = MOEQ_PF_STAGES;
 // s_waitcnt immediate for "vmcnt(0)", other counters unconstrained (gfx9 encoding:
@@ -411,9 +408,6 @@ constexpr int pf_bn() {
 // of the assignments (x16 = [rows, H] in permuted order) and the raw fp32
 // products go to A.gu instead of h.
 template <class PF, int PHASE, bool ID, bool ROT = false>
-#ifdef MOEQ_PF_NUMVGPR
-__attribute__((amdgpu_num_vgpr(MOEQ_PF_NUMVGPR)))
-#endif
 __global__ __launch_bounds__(64 * kPrefillWaves, MOEQ_PF_OCC) void k_prefill(PrefillArgs A) {
     static_assert(!ROT || (PHASE == 0 && !ID), "rotated: gate/up of a routed layer");
     constexpr int WV = kPrefillWaves;
@@ -539,38 +533,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, MOEQ_PF_OCC) void k_prefill(Pre
                 const int cofs = 8 * ((8 * h + s) ^ (lane & 15));
                 return *reinterpret_cast<const f16x8*>(xb + 32 * q * kNvTileK + cofs);
             };
-#if MOEQ_PF_PIPE
-            // software-pipelined: the A operands and B fragments of sub-step
-            // u + 1 are decoded / read before the MFMAs of sub-step u
-            constexpr int NU = 8 * PF::NSUB;
-            f16x8 av[2][NA], bv[2][NB];
-#pragma unroll
-            for (int a = 0; a < NA; ++a) av[0][a] = PF::step(w[P][a], 0, 0, ctx);
-#pragma unroll
-            for (int q = 0; q < NB; ++q) bv[0][q] = rd(0, q);
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const int c = u & 1;
-                const int s = u / PF::NSUB;
-                if (u + 1 < NU) {
-                    const int s1 = (u + 1) / PF::NSUB, j1 = (u + 1) % PF::NSUB;
-#pragma unroll
-                    for (int a = 0; a < NA; ++a) av[c ^ 1][a] = PF::step(w[P][a], s1, j1, ctx);
-#pragma unroll
-                    for (int q = 0; q < NB; ++q) bv[c ^ 1][q] = s1 != s ? rd(s1, q) : bv[c][q];
-                }
-#if MOEQ_PF_PIPE >= 2
-                __builtin_amdgcn_sched_barrier(0);
-#endif
-#pragma unroll
-                for (int q = 0; q < NB; ++q)
-#pragma unroll
-                    for (int a = 0; a < NA; ++a) acc[a][q] = mfma32(av[c][a], bv[c][q], acc[a][q]);
-#if MOEQ_PF_PIPE >= 2
-                __builtin_amdgcn_sched_barrier(0);
-#endif
-            }
-#else
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
 #pragma unroll
@@ -586,7 +548,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, MOEQ_PF_OCC) void k_prefill(Pre
                     }
                 }
             }
-#endif
             // W(kb + 1) and X(kb + 1) must have landed; with three buffers
             // X(kb + 2) may still be in flight
             if (NS == 3 && ahead)
