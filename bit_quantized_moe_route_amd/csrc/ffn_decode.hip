@@ -818,16 +818,10 @@ int launch_ks(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t
 // Few active experts -> split the input dimension over more waves so the
 // whole chip streams; many -> one wave per row set.  (An 8-way split in
 // 8-wave workgroups measured slower at one token than this 4-way split.)
-#ifndef MOEQ_KS4_SLOTS
-#define MOEQ_KS4_SLOTS 16
-#endif
-#ifndef MOEQ_KS2_SLOTS
-#define MOEQ_KS2_SLOTS 64
-#endif
 template <class F, int NTT>
 int launch_fmt(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_t s) {
-    if (slots <= MOEQ_KS4_SLOTS) return launch_ks<F, NTT, 4, 4>(a, slots, chunks, phase, s);
-    if (slots <= MOEQ_KS2_SLOTS) return launch_ks<F, NTT, 2, 4>(a, slots, chunks, phase, s);
+    if (slots <= 16) return launch_ks<F, NTT, 4, 4>(a, slots, chunks, phase, s);
+    if (slots <= 64) return launch_ks<F, NTT, 2, 4>(a, slots, chunks, phase, s);
     return launch_ks<F, NTT, 1, 4>(a, slots, chunks, phase, s);
 }
 
