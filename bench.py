@@ -216,8 +216,9 @@ class Runner:
         H, I = self.wl.H, self.wl.I
         tot = 0
         for e in experts:
-            if self.layer.fmt_host[e] == self.moeq.FMT_NVFP4:
-                tot += 2 * (H * I // 2 + H * I // 16)
+            if self.layer.fmt_host[e] in (self.moeq.FMT_NVFP4, self.moeq.FMT_NVFP4R):
+                planes = 2 if self.layer.fmt_host[e] == self.moeq.FMT_NVFP4R else 1
+                tot += planes * 2 * (H * I // 2 + H * I // 16)
             elif self.layer.fmt_host[e] == self.moeq.FMT_VQ8:
                 tot += 2 * (H * I // 8) * self.layer.vq8_m + 2 * I * 2
             else:
@@ -347,7 +348,8 @@ def main():
     ap.add_argument("--extra",
                     default="decode1,decode8,prefill,vq,vqprefill,vq1,vq2x8,vq3x8,vq2x8prefill,"
                             "mixed8,mixed32,mixedhot8,"
-                            "mixedhot32,shared1,shared8,shared32,prefillshared,rot1,rot8,rot32,"
+                            "mixedhot32,nested8,nested32,shared1,shared8,shared32,prefillshared,"
+                            "rot1,rot8,rot32,"
                             "rotprefill",
                     help="comma list of other workloads to measure ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -486,6 +488,21 @@ def main():
                 else:
                     extra[name] = measure(lay8, w8, 8, 30, 5, dev)
                 del lay8
+            elif name.startswith("nested"):
+                # the decode layer's experts held nested: two-level records
+                # resident, the hot experts lifted to the two-level tier, the
+                # rest on the records' base planes
+                wn = synth.NESTED
+                T = int(name[len("nested"):])
+                if "nested" not in layers:
+                    log("building the nested two-level NVFP4 layer ...")
+                    layers["nested"] = build_layer(
+                        wn.E, wn.H, wn.I, synth.tier_map(wn),
+                        nvfp4_weights=lambda e, p: synth.nvfp4_source_weights(wn, e, p),
+                        device=dev, workers=16,
+                        resident_formats={moeq.FMT_NVFP4, moeq.FMT_NVFP4R},
+                        nvfp4r_shift=synth.NVFP4R_SHIFT)
+                extra[name] = measure(layers["nested"], wn, T, 30, 5, dev)
             elif name.startswith("mixedhot"):
                 # the mixed layer packed in both formats (resident), its tier map
                 # switched at run time so that the hot experts take the 4-bit tier

@@ -13,9 +13,10 @@ Calls (same names as the C ABI in include/moeq.h):
     shared_ffn(shared, x)                       -> y_shared
     combine_shared(y_perm, inv_perm, topk_w, y_shared) -> out
     forward(layer, x, logits, k, shared=None)   -> all of the above
-Host packers: quantize_nvfp4, pack_nvfp4_expert, pack_vq_expert,
-pack_vq8_expert, pack_bf16_expert, record_bytes, record_table.  Test hook:
-dequant_q.
+    layer_forward(layer, x, logits, k)          -> topk_ids, topk_w, out (one C call)
+Host packers: quantize_nvfp4, quantize_nvfp4_residual, pack_nvfp4_expert,
+pack_nvfp4r_expert, pack_vq_expert, pack_vq8_expert, pack_bf16_expert,
+record_bytes, record_table.  Test hook: dequant_q.
 """
 
 import ctypes
@@ -36,7 +37,8 @@ FMT_NVFP4 = 1
 FMT_VQ = 2
 FMT_VQ8 = 3
 FMT_BF16 = 4
-FORMATS = (FMT_NVFP4, FMT_VQ, FMT_VQ8, FMT_BF16)
+FMT_NVFP4R = 5      # nested two-level NVFP4: base plane + residual plane
+FORMATS = (FMT_NVFP4, FMT_VQ, FMT_VQ8, FMT_BF16, FMT_NVFP4R)
 REC_COMPACT, REC_RESIDENT = 0, 1
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 VQ_NCODE = 65536
@@ -68,6 +70,9 @@ class _QLayerC(ctypes.Structure):
         ("bf16_w2", ctypes.c_void_p), ("bf16_w2_stride", ctypes.c_int64),
         ("record_mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("rot_signs", ctypes.c_void_p),
+        ("nvfp4r_w13", ctypes.c_void_p), ("nvfp4r_w13_stride", ctypes.c_int64),
+        ("nvfp4r_w2", ctypes.c_void_p), ("nvfp4r_w2_stride", ctypes.c_int64),
+        ("nvfp4r_shift", ctypes.c_int32), ("reserved2", ctypes.c_int32),
     ]
 
 
@@ -99,6 +104,8 @@ _PROTOS = {
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _I64, _I32, _P, _P,
                                          _P, _P, _P, _SZ, _P]),
     "moe_quantize_nvfp4": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
+    "moe_quantize_nvfp4_residual": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "moe_pack_nvfp4r_expert": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
     "moe_record_bytes": (_SZ, [ctypes.c_int, ctypes.c_int, _I32, _I32]),
     "moe_record_bytes_vq8": (_SZ, [ctypes.c_int, _I32, _I32, _I32]),
     "moe_pack_vq8_expert": (ctypes.c_int, [_P] * 6 + [_I32, _I32, _I32, _P, _P]),
@@ -160,6 +167,23 @@ def quantize_nvfp4(w):
     return codes, scales
 
 
+NVFP4R_SHIFT = 8    # default residual-plane exponent of a nested layer
+
+
+def quantize_nvfp4_residual(w, shift=NVFP4R_SHIFT):
+    """fp32 [n, kin] -> ((base codes, base scales), (residual codes, residual
+    scales)): the two planes of a nested two-level NVFP4 matrix (the residual
+    plane holds the residual times 2^shift)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, kin = w.shape
+    out = [np.empty((n, kin // 2), np.uint8), np.empty((n, max(kin // 16, 0)), np.uint8),
+           np.empty((n, kin // 2), np.uint8), np.empty((n, max(kin // 16, 0)), np.uint8)]
+    _check(lib().moe_quantize_nvfp4_residual(_np_ptr(w), n, kin, shift,
+                                             *[_np_ptr(a) for a in out]),
+           "moe_quantize_nvfp4_residual")
+    return (out[0], out[1]), (out[2], out[3])
+
+
 def record_bytes(fmt, which, H, I, vq8_m=0):
     if fmt == FMT_VQ8:
         return int(lib().moe_record_bytes_vq8(which, H, I, vq8_m))
@@ -175,6 +199,23 @@ def pack_nvfp4_expert(gate, up, down, H, I, w13=None, w2=None):
     arrs = [np.ascontiguousarray(a, dtype=np.uint8) for pair in (gate, up, down) for a in pair]
     _check(lib().moe_pack_nvfp4_expert(*[_np_ptr(a) for a in arrs], H, I, _np_ptr(w13),
                                        _np_ptr(w2)), "moe_pack_nvfp4_expert")
+    return w13, w2
+
+
+def pack_nvfp4r_expert(base, res, H, I, w13=None, w2=None):
+    """base / res = ((codes, scales) of gate, up, down) of the two planes ->
+    (w13 record, w2 record) of a nested two-level NVFP4 expert."""
+    if w13 is None:
+        w13 = np.empty(record_bytes(FMT_NVFP4R, 0, H, I), np.uint8)
+    if w2 is None:
+        w2 = np.empty(record_bytes(FMT_NVFP4R, 1, H, I), np.uint8)
+    b = [np.ascontiguousarray(a, dtype=np.uint8) for pair in base for a in pair]
+    r = [np.ascontiguousarray(a, dtype=np.uint8) for pair in res for a in pair]
+    bp = (ctypes.c_void_p * 6)(*[a.ctypes.data for a in b])
+    rp = (ctypes.c_void_p * 6)(*[a.ctypes.data for a in r])
+    _check(lib().moe_pack_nvfp4r_expert(ctypes.cast(bp, ctypes.c_void_p),
+                                        ctypes.cast(rp, ctypes.c_void_p), H, I, _np_ptr(w13),
+                                        _np_ptr(w2)), "moe_pack_nvfp4r_expert")
     return w13, w2
 
 
@@ -301,11 +342,15 @@ class QLayer:
     descriptor that points at them.  Build it with `QLayer.build(...)`.
     """
 
-    def __init__(self, E, H, I, fmt_host, device="cuda", vq8_m=0, resident_formats=None):
+    def __init__(self, E, H, I, fmt_host, device="cuda", vq8_m=0, resident_formats=None,
+                 nvfp4r_shift=NVFP4R_SHIFT):
         """resident_formats: None (compact pools: each expert stored in its own
         format only) or a set of format tags whose pools hold every expert at
         slot e, so that set_tiers() can move experts between those formats
-        between calls."""
+        between calls.  With both FMT_NVFP4 and FMT_NVFP4R resident the layer
+        is nested: the NVFP4 pools are the NVFP4R records themselves (their
+        base planes), so moving an expert between the two tiers changes no
+        bytes (set_residual writes a residual plane on its own)."""
         torch = _torch()
         self.E, self.H, self.I = int(E), int(H), int(I)
         self.fmt_host = np.ascontiguousarray(fmt_host, dtype=np.uint8)
@@ -323,12 +368,21 @@ class QLayer:
         if sizes[FMT_VQ8] and vq8_m not in (1, 2, 3):
             raise ValueError("a layer with small-codebook VQ experts needs vq8_m = 1, 2 or 3")
         self.vq8_m = int(vq8_m)
+        self.nvfp4r_shift = int(nvfp4r_shift)
         self.rec_host = rec
         self.device = torch.device(device)
         self.rec_dev = torch.from_numpy(rec).to(self.device)
         self.stride = {}
         self.pools = {}
-        for fmt in FORMATS:
+        nested = (self.resident is not None and FMT_NVFP4 in self.resident
+                  and FMT_NVFP4R in self.resident)
+        self.alias = {FMT_NVFP4: FMT_NVFP4R} if nested else {}
+        for fmt in sorted(FORMATS, key=lambda f: f in self.alias):
+            if fmt in self.alias:
+                for which in (0, 1):
+                    self.stride[(fmt, which)] = self.stride[(self.alias[fmt], which)]
+                    self.pools[(fmt, which)] = self.pools[(self.alias[fmt], which)]
+                continue
             n = sizes[fmt]
             for which in (0, 1):
                 b = record_bytes(fmt, which, H, I, self.vq8_m) if n else 0
@@ -372,6 +426,21 @@ class QLayer:
         for which, rec in ((0, w13), (1, w2)):
             s = self.stride[(fmt, which)]
             dst = self.pools[(fmt, which)][idx * s: idx * s + rec.shape[0]]
+            dst.copy_(torch.from_numpy(np.ascontiguousarray(rec)), non_blocking=False)
+        self._c = None
+
+    def set_residual(self, e, res13, res2):
+        """Nested layers: write the residual planes (NVFP4 records, numpy
+        uint8) of expert e's two-level records, leaving their base planes as
+        they are."""
+        torch = _torch()
+        idx = e if self.resident is not None else self.record_index(e)
+        for which, rec in ((0, res13), (1, res2)):
+            off = record_bytes(FMT_NVFP4, which, self.H, self.I)
+            if rec.shape[0] > off:
+                raise ValueError("a residual plane is one NVFP4 record")
+            s = self.stride[(FMT_NVFP4R, which)]
+            dst = self.pools[(FMT_NVFP4R, which)][idx * s + off: idx * s + off + rec.shape[0]]
             dst.copy_(torch.from_numpy(np.ascontiguousarray(rec)), non_blocking=False)
         self._c = None
 
@@ -419,10 +488,12 @@ class QLayer:
             d.fmt_host = self.fmt_host.ctypes.data
             d.rec_dev = self.rec_dev.data_ptr()
             d.vq8_m = self.vq8_m
+            d.nvfp4r_shift = self.nvfp4r_shift
             d.record_mode = REC_RESIDENT if self.resident is not None else REC_COMPACT
             for fmt, n13, n2 in ((FMT_NVFP4, "nvfp4_w13", "nvfp4_w2"), (FMT_VQ, "vq_w13", "vq_w2"),
                                  (FMT_VQ8, "vq8_w13", "vq8_w2"),
-                                 (FMT_BF16, "bf16_w13", "bf16_w2")):
+                                 (FMT_BF16, "bf16_w13", "bf16_w2"),
+                                 (FMT_NVFP4R, "nvfp4r_w13", "nvfp4r_w2")):
                 p13, p2 = self.pools[(fmt, 0)], self.pools[(fmt, 1)]
                 setattr(d, n13, p13.data_ptr() if p13 is not None else None)
                 setattr(d, n2, p2.data_ptr() if p2 is not None else None)
@@ -446,8 +517,9 @@ class QLayer:
         tot = 0
         vq = vq8 = False
         for e in set(int(x) for x in experts):
-            if self.fmt_host[e] == FMT_NVFP4:
-                tot += 3 * (self.H * self.I // 2 + self.H * self.I // 16)
+            if self.fmt_host[e] in (FMT_NVFP4, FMT_NVFP4R):
+                planes = 2 if self.fmt_host[e] == FMT_NVFP4R else 1
+                tot += planes * 3 * (self.H * self.I // 2 + self.H * self.I // 16)
             elif self.fmt_host[e] == FMT_BF16:
                 tot += 3 * self.H * self.I * 2
             elif self.fmt_host[e] == FMT_VQ8:

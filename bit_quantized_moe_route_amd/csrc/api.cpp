@@ -1,4 +1,5 @@
 // C ABI: argument checks, workspace layout and dispatch to the HIP launchers.
+#include <cmath>
 #include <cstdint>
 #include <string>
 
@@ -80,6 +81,13 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     v.pool2[MOE_FMT_BF16] = static_cast<const uint8_t*>(L->bf16_w2);
     v.stride13[MOE_FMT_BF16] = L->bf16_w13_stride;
     v.stride2[MOE_FMT_BF16] = L->bf16_w2_stride;
+    v.pool13[MOE_FMT_NVFP4R] = static_cast<const uint8_t*>(L->nvfp4r_w13);
+    v.pool2[MOE_FMT_NVFP4R] = static_cast<const uint8_t*>(L->nvfp4r_w2);
+    v.stride13[MOE_FMT_NVFP4R] = L->nvfp4r_w13_stride;
+    v.stride2[MOE_FMT_NVFP4R] = L->nvfp4r_w2_stride;
+    v.res13 = nv_record_bytes(0, L->H, L->I);
+    v.res2 = nv_record_bytes(1, L->H, L->I);
+    v.res_scale = 1.0f;
     for (int p = 0; p < 3; ++p) v.cb[p] = static_cast<const uint8_t*>(L->vq_codebook[p]);
     v.cb_stride = L->vq_codebook_stride;
     for (int p = 0; p < 3; ++p) v.cb8[p] = static_cast<const uint8_t*>(L->vq8_codebook[p]);
@@ -88,14 +96,20 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     v.rot_stride = (int64_t)(2 * (int64_t)L->H + 3 * (int64_t)L->I) / 8;
     if (v.rot && (L->H % MOE_ROT_BLOCK || L->I % MOE_ROT_BLOCK))
         return fail(MOE_EUNSUPPORTED, f + ": a rotated layer needs H and I multiples of 128");
+    if (out.count[MOE_FMT_NVFP4R]) {
+        if (L->nvfp4r_shift < 0 || L->nvfp4r_shift > 14)
+            return fail(MOE_EUNSUPPORTED, f + ": nvfp4r_shift must be in [0, 14]");
+        v.res_scale = std::ldexp(1.0f, -L->nvfp4r_shift);
+    }
     if (out.count[MOE_FMT_VQ8] && (L->vq8_m < 1 || L->vq8_m > MOE_VQ8_MAX_M))
         return fail(MOE_EUNSUPPORTED, f + ": vq8_m must be 1, 2 or 3");
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!out.count[fmt]) continue;
-        const char* name = fmt == MOE_FMT_NVFP4 ? "NVFP4"
-                           : fmt == MOE_FMT_VQ  ? "VQ"
-                           : fmt == MOE_FMT_VQ8 ? "VQ8"
-                                                : "BF16";
+        const char* name = fmt == MOE_FMT_NVFP4  ? "NVFP4"
+                           : fmt == MOE_FMT_VQ   ? "VQ"
+                           : fmt == MOE_FMT_VQ8  ? "VQ8"
+                           : fmt == MOE_FMT_BF16 ? "BF16"
+                                                 : "NVFP4R";
         if (!v.pool13[fmt] || !v.pool2[fmt])
             return fail(MOE_EINVAL, f + ": " + name + " experts present but their pool is NULL");
         const int64_t b13 = fmt == MOE_FMT_VQ8

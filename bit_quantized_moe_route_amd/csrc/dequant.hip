@@ -5,7 +5,8 @@
 // be compared bit for bit with a plain decode of the canonical bytes.  VQ8
 // with one code per group is exact too; with two or three it is
 // fp32(fp32(C_0 + .. + C_{m-1}) * S).  BF16 gives the kernels' fp16 operand: the
-// stored weight rounded to fp16 (equal to it for |w| >= 2^-17).
+// stored weight rounded to fp16 (equal to it for |w| >= 2^-17).  Nested
+// two-level NVFP4 gives fp32(base + residual * 2^-shift).
 #include "dev_common.h"
 
 namespace moeq {
@@ -14,9 +15,11 @@ namespace {
 
 // one wave per tile; grid.x = row groups of the projection, grid.y = tiles
 // along the input dimension
+// res != 0 (MOE_FMT_NVFP4R): plus the residual plane res bytes further on
+// times rscale, summed in fp32.
 __global__ __launch_bounds__(64) void k_dequant_nv(const uint8_t* __restrict__ rec, int rg_step,
-                                                   int rg_off, int n, int kin,
-                                                   float* __restrict__ out) {
+                                                   int rg_off, int n, int kin, int64_t res,
+                                                   float rscale, float* __restrict__ out) {
     const int lane = threadIdx.x;
     const int g = blockIdx.x;
     const int kb = blockIdx.y;
@@ -25,6 +28,19 @@ __global__ __launch_bounds__(64) void k_dequant_nv(const uint8_t* __restrict__ r
     NvFrag f = nv_load(tile, lane);
     f16x8 a[4];
     nv_decode(f, a);
+    float v[4][8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[s][i] = (float)a[s][i];
+    if (res) {
+        NvFrag fr = nv_load(tile + res, lane);
+        nv_decode(fr, a);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[s][i] += (float)a[s][i] * rscale;
+    }
     const int row = 16 * g + (lane & 15);
     const int k0 = kb * kNvTileK + (lane >> 4) * 32;
 #pragma unroll
@@ -32,7 +48,7 @@ __global__ __launch_bounds__(64) void k_dequant_nv(const uint8_t* __restrict__ r
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int k = k0 + 8 * s + i;
-            if (row < n && k < kin) out[(int64_t)row * kin + k] = (float)a[s][i];
+            if (row < n && k < kin) out[(int64_t)row * kin + k] = v[s][i];
         }
 }
 
@@ -130,9 +146,10 @@ int launch_dequant(const LayerView& L, int fmt, int32_t ridx, int32_t proj, floa
     const int rg_off = proj == MOE_PROJ_UP ? 1 : 0;
     const uint8_t* rec = down ? L.pool2[fmt] + (int64_t)ridx * L.stride2[fmt]
                               : L.pool13[fmt] + (int64_t)ridx * L.stride13[fmt];
-    if (fmt == MOE_FMT_NVFP4) {
+    if (fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_NVFP4R) {
         dim3 grid((unsigned)(n / 16), (unsigned)nv_tiles_k(kin));
-        k_dequant_nv<<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, out);
+        const int64_t res = fmt == MOE_FMT_NVFP4 ? 0 : down ? L.res2 : L.res13;
+        k_dequant_nv<<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, res, L.res_scale, out);
     } else if (fmt == MOE_FMT_BF16) {
         dim3 grid((unsigned)(n / 16), (unsigned)bf16_tiles_k(kin));
         k_dequant_bf16<<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, out);

@@ -33,6 +33,7 @@ namespace {
 
 // Per-format tile traits ----------------------------------------------------
 struct NvFmt {
+    static constexpr int PLANES = 1;
     static constexpr bool kVq = false;
     static constexpr bool kVq8 = false;
     static constexpr int TK = kNvTileK;       // inputs per tile
@@ -54,6 +55,7 @@ struct NvFmt {
 };
 
 struct VqFmt {
+    static constexpr int PLANES = 1;
     static constexpr bool kVq = true;
     static constexpr bool kVq8 = false;
     static constexpr int TK = kVqTileK;
@@ -84,6 +86,7 @@ struct VqFmt {
 // first would round).  Per-row scales as for VQ.
 template <int M>
 struct Vq8Fmt {
+    static constexpr int PLANES = 1;
     static constexpr bool kVq = true;
     static constexpr bool kVq8 = true;
     static constexpr int CODES = M;
@@ -98,6 +101,7 @@ struct Vq8Fmt {
 // (bf16 -> fp32 exact, fp32 -> fp16 nearest even: exact for
 // 2^-17 <= |w| <= 65504, since a bf16 value has 8 significant bits).
 struct Bf16Fmt {
+    static constexpr int PLANES = 1;
     static constexpr bool kVq = false;
     static constexpr bool kVq8 = false;
     static constexpr int TK = kBf16TileK;
@@ -114,6 +118,37 @@ struct Bf16Fmt {
     __device__ __forceinline__ static void decode(const Frag& fr, const uint8_t*, f16x8 a[STEPS]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[j] = bf16x8_to_f16x8(fr.c[j]);
+    }
+};
+
+// Nested two-level NVFP4 (MOE_FMT_NVFP4R): a tile of the base plane and the
+// tile at the same place of the residual plane, poff bytes further on, whose
+// scales are multiplied by the layer's power of two pscale; each plane's
+// decoded fragment is its own MFMA A operand (both products exact, summed in
+// the fp32 accumulator).  ("GLM-5.3 Vision NestQuant 1.75-4 bit",
+// introduction: a base plus a residual plane that lifts it.)
+struct Nv2Fmt : NvFmt {
+    static constexpr int PLANES = 2;
+    struct Frag {
+        NvFmt::Frag p[2];
+    };
+    __device__ __forceinline__ static void load(Frag& fr, const uint8_t* tile, int lane,
+                                                int64_t poff) {
+        NvFmt::load(fr.p[0], tile, lane);
+        NvFmt::load(fr.p[1], tile + poff, lane);
+    }
+    __device__ __forceinline__ static void decode2(const Frag& fr, f16x8 a0[STEPS],
+                                                   f16x8 a1[STEPS], _Float16 ps) {
+        NvFmt::decode(fr.p[0], nullptr, a0);
+        f16x2 s0, s1;
+        nv_scales(fr.p[1].scales, s0, s1);
+        const f16x2 p2 = {ps, ps};
+        s0 = s0 * p2;
+        s1 = s1 * p2;
+        a1[0] = nv_dequant8(fr.p[1].codes[0], s0);
+        a1[1] = nv_dequant8(fr.p[1].codes[1], s0);
+        a1[2] = nv_dequant8(fr.p[1].codes[2], s1);
+        a1[3] = nv_dequant8(fr.p[1].codes[3], s1);
     }
 };
 
@@ -171,6 +206,8 @@ struct DecodeArgs {
     float* y_perm;
     int E, H, I, k, fmt;
     int rows;              // offsets == NULL: rows of the identity map
+    int64_t res13, res2;   // MOE_FMT_NVFP4R: residual plane offset in a record
+    float res_scale;       // ... and its decode factor
     int nsplit;            // PART kernels: workgroups splitting the input dimension
     float* part;           // PART kernels: fp32 [nsplit][rows][2I] partial g | u
     // small-batch fused layer (ROUTE gate/up, k_down_combine)
@@ -195,7 +232,8 @@ __device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
                                              const uint8_t* const cb[NM],
                                              const uint16_t* const xrow[NTT], int ntt, int K,
                                              int kpart, int KS, int lane,
-                                             f32x4 acc[NM][NTT]) {
+                                             f32x4 acc[NM][NTT], int64_t poff = 0,
+                                             float pscale = 1.f) {
     const int nkb = tiles_k<F>(K);
     const int ksub = (lane >> 4) * F::KSPAN;
     const int niter = kpart < nkb ? (nkb - kpart + KS - 1) / KS : 0;   // tiles of this wave
@@ -204,7 +242,12 @@ __device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
     auto issue = [&](int i, typename F::Frag (&w)[NM], u32x4 (&b)[NTT][F::STEPS]) {
         const int kb = kpart + i * KS;
 #pragma unroll
-        for (int m = 0; m < NM; ++m) F::load(w[m], tbase[m] + (int64_t)kb * F::TB, lane);
+        for (int m = 0; m < NM; ++m) {
+            if constexpr (F::PLANES == 2)
+                F::load(w[m], tbase[m] + (int64_t)kb * F::TB, lane, poff);
+            else
+                F::load(w[m], tbase[m] + (int64_t)kb * F::TB, lane);
+        }
         load_b<F, NTT>(xrow, ntt, kb * F::TK + ksub, K, b);
     };
 #pragma unroll
@@ -218,14 +261,28 @@ __device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
             if (i + D < niter) issue(i + D, wr[(u + D) % (D + 1)], br[(u + D) % (D + 1)]);
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                f16x8 a[F::STEPS];
-                F::decode(wr[u][m], cb[m], a);
+                if constexpr (F::PLANES == 2) {
+                    f16x8 a0[F::STEPS], a1[F::STEPS];
+                    F::decode2(wr[u][m], a0, a1, (_Float16)pscale);
 #pragma unroll
-                for (int s = 0; s < F::STEPS; ++s)
+                    for (int s = 0; s < F::STEPS; ++s)
 #pragma unroll
-                    for (int tt = 0; tt < NTT; ++tt)
-                        if (tt < ntt)
-                            acc[m][tt] = mfma16(a[s], act_f16<BF>(br[u][tt][s]), acc[m][tt]);
+                        for (int tt = 0; tt < NTT; ++tt)
+                            if (tt < ntt) {
+                                const f16x8 bb = act_f16<BF>(br[u][tt][s]);
+                                acc[m][tt] = mfma16(a0[s], bb, acc[m][tt]);
+                                acc[m][tt] = mfma16(a1[s], bb, acc[m][tt]);
+                            }
+                } else {
+                    f16x8 a[F::STEPS];
+                    F::decode(wr[u][m], cb[m], a);
+#pragma unroll
+                    for (int s = 0; s < F::STEPS; ++s)
+#pragma unroll
+                        for (int tt = 0; tt < NTT; ++tt)
+                            if (tt < ntt)
+                                acc[m][tt] = mfma16(a[s], act_f16<BF>(br[u][tt][s]), acc[m][tt]);
+                }
             }
         }
     }
@@ -550,7 +607,8 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
             stream_tiles_vq<NTT, NM, XBF>(tb, cb, xrow, xsafe, ntt, K, kpart, kstride, lane, acc);
         } else {
             stream_tiles<F, NTT, NM, ID ? kPrefetchShared : ROUTE ? kPrefetchRoute : kPrefetch, XBF>(
-                tb, cb, xrow, ntt, K, kpart, kstride, lane, acc);
+                tb, cb, xrow, ntt, K, kpart, kstride, lane, acc, PHASE == 0 ? A.res13 : A.res2,
+                A.res_scale);
         }
     }
 
@@ -739,7 +797,8 @@ __global__ __launch_bounds__(64 * kDcKS * NG, kMinWaves) void k_down_combine(Dec
             reinterpret_cast<const uint16_t*>(A.h16) + ((int64_t)t * A.k + j0) * A.I;
         stream_tiles_vq<1, NM, false>(tb, cb, xrow, xsafe, 1, K, kloc, KS, lane, acc);
     } else {
-        stream_tiles<F, 1, NM, kPrefetch, false>(tb, cb, xrow, 1, K, kloc, KS, lane, acc);
+        stream_tiles<F, 1, NM, kPrefetch, false>(tb, cb, xrow, 1, K, kloc, KS, lane, acc, A.res2,
+                                                 A.res_scale);
     }
     // the KS input parts of each slot group, summed in wave order
     __shared__ f32x4 red[WV][NM][64];
@@ -935,6 +994,9 @@ DecodeArgs decode_args(const LayerView& L, int fmt, const uint16_t* x_bf16,
     a.k = k;
     a.fmt = fmt;
     a.rows = (int)T;
+    a.res13 = L.res13;
+    a.res2 = L.res2;
+    a.res_scale = L.res_scale;
     a.nsplit = 1;
     a.part = nullptr;
     a.logits = nullptr;
@@ -981,6 +1043,7 @@ int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, cons
     a.out = out;
     if (T == 0) return MOE_OK;
     if (fmt == MOE_FMT_NVFP4) return launch_small_fmt<NvFmt>(a, T, s);
+    if (fmt == MOE_FMT_NVFP4R) return launch_small_fmt<Nv2Fmt>(a, T, s);
     if (fmt == MOE_FMT_BF16) return launch_small_fmt<Bf16Fmt>(a, T, s);
     if (fmt == MOE_FMT_VQ8) {
         if (L.vq8_m == 1) return launch_small_fmt<Vq8Fmt<1>>(a, T, s);
@@ -1000,6 +1063,7 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
     const int slots = (int)(tk < n_fmt ? tk : n_fmt);
     if (slots == 0) return MOE_OK;
     if (fmt == MOE_FMT_NVFP4) return launch_ntt<NvFmt>(a, T, slots, phase, s);
+    if (fmt == MOE_FMT_NVFP4R) return launch_ntt<Nv2Fmt>(a, T, slots, phase, s);
     if (fmt == MOE_FMT_BF16) return launch_ntt<Bf16Fmt>(a, T, slots, phase, s);
     if (fmt == MOE_FMT_VQ8) {
         if (L.vq8_m == 1) return launch_ntt<Vq8Fmt<1>>(a, T, slots, phase, s);
@@ -1020,6 +1084,7 @@ int launch_shared_decode(const LayerView& L, int fmt, const uint16_t* x_bf16, in
     a.part = part;
     if (T == 0) return MOE_OK;
     if (fmt == MOE_FMT_NVFP4) return launch_shared_fmt<NvFmt>(a, phase, s);
+    if (fmt == MOE_FMT_NVFP4R) return launch_shared_fmt<Nv2Fmt>(a, phase, s);
     if (fmt == MOE_FMT_BF16) return launch_shared_fmt<Bf16Fmt>(a, phase, s);
     if (fmt == MOE_FMT_VQ8) {
         if (L.vq8_m == 1) return launch_shared_fmt<Vq8Fmt<1>>(a, phase, s);

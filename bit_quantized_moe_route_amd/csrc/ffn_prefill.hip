@@ -83,6 +83,8 @@ struct PrefillArgs {
     int E, H, I, k, fmt;
     int rows;                  // offsets == NULL: rows of the identity map
     float* gu;                 // rotated layers: raw g | u [rows, 2I] (gate/up)
+    int64_t res;               // MOE_FMT_NVFP4R: residual plane offset in a record
+    float res_scale;           // ... and its decode factor
 };
 
 struct WorkItem {
@@ -241,11 +243,46 @@ struct PfNv {
     }
     using Frag = AFrag;
     __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
-                                                int kb, int K, int lane, bool valid) {
+                                                int kb, int K, int lane, bool valid,
+                                                int64_t, float) {
         load_a(f, grp_base + (int64_t)kb * kNvTileBytes, gstride, lane, valid);
     }
     __device__ __forceinline__ static f16x8 step(const Frag& f, int s, int, const void*) {
         return a_step(f, s);
+    }
+};
+
+// Nested two-level NVFP4 (MOE_FMT_NVFP4R): the base plane's tile and the
+// residual plane's (poff bytes further on in the record, its scales times the
+// layer's power of two pscale); sub-step j of a K-step is plane j, each its
+// own exact MFMA A operand.
+struct PfNv2 {
+    static constexpr int BM = 64;
+    static constexpr int NA = 2;
+    static constexpr int NSUB = 2;
+    static constexpr bool kScales = false;
+    static constexpr int cb_lds(int) { return 0; }
+    __device__ __forceinline__ static int64_t group_bytes(int K) { return PfNv::group_bytes(K); }
+    struct Frag {
+        AFrag p[2];
+        _Float16 ps;
+    };
+    __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
+                                                int kb, int K, int lane, bool valid,
+                                                int64_t poff, float pscale) {
+        const uint8_t* t = grp_base + (int64_t)kb * kNvTileBytes;
+        load_a(f.p[0], t, gstride, lane, valid);
+        load_a(f.p[1], t + poff, gstride, lane, valid);
+        f.ps = (_Float16)pscale;
+    }
+    __device__ __forceinline__ static f16x8 step(const Frag& f, int s, int j, const void*) {
+        if (j == 0) return a_step(f.p[0], s);
+        const uint32_t sc = s < 4 ? f.p[1].s0 : f.p[1].s1;
+        const u32x4 c = s < 4 ? f.p[1].c0 : f.p[1].c1;
+        f16x2 s0, s1;
+        nv_scales(sc, s0, s1);
+        const f16x2 sv = (((s & 3) < 2) ? s0 : s1) * f16x2{f.ps, f.ps};
+        return nv_dequant8(c[s & 3], sv);
     }
 };
 
@@ -265,7 +302,8 @@ struct PfBf16 {
         u32x4 c[8];
     };
     __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
-                                                int kb, int K, int lane, bool valid) {
+                                                int kb, int K, int lane, bool valid,
+                                                int64_t, float) {
         if (!valid) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) f.c[s] = u32x4{0u, 0u, 0u, 0u};
@@ -316,7 +354,8 @@ struct PfVq8 {
         int nvalid;     // K-steps of the lane inside K
     };
     __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
-                                                int kb, int K, int lane, bool valid) {
+                                                int kb, int K, int lane, bool valid,
+                                                int64_t, float) {
         const int row = lane & 31;
         const int h = lane >> 5;
         const int k0 = kb * 128 + 64 * h;
@@ -374,7 +413,8 @@ struct PfVq {
         int nvalid;
     };
     __device__ __forceinline__ static void load(Frag& f, const uint8_t* grp_base, int64_t gstride,
-                                                int kb, int K, int lane, bool valid) {
+                                                int kb, int K, int lane, bool valid,
+                                                int64_t, float) {
         const int row = lane & 31;
         const int h = lane >> 5;
         const int k0 = kb * 128 + 64 * h;
@@ -474,7 +514,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, MOEQ_PF_OCC) void k_prefill(Pre
 #pragma unroll
         for (int a = 0; a < NA; ++a)
             PF::load(wa[a], base + (int64_t)(g0 + 2 * a) * gstride, gstride, kb, K, lane,
-                     valid[a]);
+                     valid[a], A.res, A.res_scale);
     };
     // the lane's codebooks: small ones copied into LDS by the workgroup (gate
     // then up, or down), large ones read from L2; rows 16..31 of an A tile
@@ -703,6 +743,8 @@ int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x
     a.fmt = fmt;
     a.rows = (int)T;
     a.gu = phase == 0 ? gu : nullptr;
+    a.res = phase == 0 ? L.res13 : L.res2;
+    a.res_scale = L.res_scale;
     const int64_t tk = T * k;
     const int64_t act = tk < n_fmt ? tk : n_fmt;
     const bool id = offsets == nullptr;   // NVFP4 and BF16 only (prefill_fmt)
@@ -716,6 +758,9 @@ int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x
             if (L.vq8_m == 1) return launch_pf<PfVq8<1>, false>(a, tk, act, phase, s);
             if (L.vq8_m == 3) return launch_pf<PfVq8<3>, false>(a, tk, act, phase, s);
             return launch_pf<PfVq8<2>, false>(a, tk, act, phase, s);
+        case MOE_FMT_NVFP4R:
+            return id ? launch_pf<PfNv2, true>(a, tk, act, phase, s)
+                      : launch_pf<PfNv2, false>(a, tk, act, phase, s);
         default:
             return id ? launch_pf<PfNv, true>(a, tk, act, phase, s)
                       : launch_pf<PfNv, false>(a, tk, act, phase, s);

@@ -60,6 +60,12 @@ inline int64_t vq_codes_bytes(int32_t n, int32_t kin) {
 inline int64_t vq8_codes_bytes(int32_t n, int32_t kin, int32_t m) {
     return (int64_t)(n / 16) * vq_tiles_k(kin) * kVq8TileBytesPerCode * m;
 }
+// NVFP4 record bytes (which = 0: gate/up, 1: down); also the offset of the
+// residual plane inside a MOE_FMT_NVFP4R record.
+inline int64_t nv_record_bytes(int which, int32_t H, int32_t I) {
+    return which == 0 ? round_up(nv_matrix_bytes(2 * I, H), 256)
+                      : round_up(nv_matrix_bytes(H, I), 256);
+}
 inline int64_t bf16_tiles_k(int32_t kin) { return round_up(kin, kBf16TileK) / kBf16TileK; }
 inline int64_t bf16_matrix_bytes(int32_t n, int32_t kin) {
     return (int64_t)(n / 16) * bf16_tiles_k(kin) * kBf16TileBytes;
@@ -78,6 +84,8 @@ struct LayerView {
     const uint8_t* cb[3];       // VQ codebooks gate, up, down
     int64_t cb_stride;
     const uint8_t* cb8[3];      // VQ8 codebooks gate, up, down: [m][256][8] fp16
+    int64_t res13, res2;        // MOE_FMT_NVFP4R: residual plane offset in a record
+    float res_scale;            // ... and its decode factor 2^-nvfp4r_shift
     const uint8_t* rot;         // rotation sign bits per expert (NULL: not rotated)
     int64_t rot_stride;         // bytes per expert: (2H + 3I) / 8
 };
@@ -118,10 +126,10 @@ int launch_shared_decode(const LayerView& L, int fmt, const uint16_t* x_bf16, in
                          uint16_t* h16, float* part, float* y, int phase, void* stream);
 // Experts at T >= kPrefillMinTokens use the grouped-GEMM kernels, every
 // format for routed layers; the identity map of a one-expert layer
-// (perm_src == offsets == NULL) only for NVFP4 and BF16.
+// (perm_src == offsets == NULL) only for NVFP4 (one or two planes) and BF16.
 constexpr int64_t kPrefillMinTokens = 128;
 inline bool prefill_fmt(int fmt, bool identity) {
-    return !identity || fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16;
+    return !identity || fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16 || fmt == MOE_FMT_NVFP4R;
 }
 int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x16,
                        const int32_t* perm_src, const int32_t* offsets, int64_t T, int32_t k,

@@ -162,10 +162,7 @@ static int64_t vq_rec_bytes(int which, int32_t H, int32_t I) {
     return round_up(vq_codes_bytes(H, I) + 2LL * H, 256);
 }
 
-static int64_t nv_rec_bytes(int which, int32_t H, int32_t I) {
-    if (which == 0) return round_up(nv_matrix_bytes(2 * I, H), 256);
-    return round_up(nv_matrix_bytes(H, I), 256);
-}
+static int64_t nv_rec_bytes(int which, int32_t H, int32_t I) { return nv_record_bytes(which, H, I); }
 
 }  // namespace moeq
 
@@ -208,11 +205,35 @@ int moe_quantize_nvfp4(const float* w, int32_t n, int32_t kin, uint8_t* codes,
     return MOE_OK;
 }
 
+int moe_quantize_nvfp4_residual(const float* w, int32_t n, int32_t kin, int32_t shift,
+                                uint8_t* bc, uint8_t* bs, uint8_t* rc, uint8_t* rs) {
+    if (!w || !bc || !bs || !rc || !rs)
+        return fail(MOE_EINVAL, "moe_quantize_nvfp4_residual: null pointer");
+    if (shift < 0 || shift > 14)
+        return fail(MOE_EINVAL, "moe_quantize_nvfp4_residual: shift must be in [0, 14]");
+    int st = moe_quantize_nvfp4(w, n, kin, bc, bs);
+    if (st) return st;
+    // r = fp32((w - base) * 2^shift), the base value (an E2M1 value times its
+    // E4M3 scale) and the product exact in double
+    static const double kE2m1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    std::vector<float> r((size_t)n * kin);
+    for (int64_t o = 0; o < n; ++o)
+        for (int32_t k = 0; k < kin; ++k) {
+            const uint8_t byte = bc[o * (kin / 2) + k / 2];
+            const int c = (k & 1) ? byte >> 4 : byte & 15;
+            const double S = e4m3_value(bs[o * (kin / 16) + k / 16]);
+            const double q = ((c & 8) ? -1.0 : 1.0) * kE2m1[c & 7] * S;
+            r[(size_t)o * kin + k] =
+                (float)std::ldexp((double)w[(size_t)o * kin + k] - q, shift);
+        }
+    return moe_quantize_nvfp4(r.data(), n, kin, rc, rs);
+}
+
 size_t moe_record_bytes(int fmt, int which, int32_t H, int32_t I) {
     if (H <= 0 || I <= 0 || (which != 0 && which != 1)) return 0;
-    if (fmt == MOE_FMT_NVFP4) {
+    if (fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_NVFP4R) {
         if (H % 16 || I % 16) return 0;
-        return (size_t)nv_rec_bytes(which, H, I);
+        return (size_t)nv_rec_bytes(which, H, I) * (fmt == MOE_FMT_NVFP4R ? 2 : 1);
     }
     if (fmt == MOE_FMT_VQ) {
         if (H % 16 || I % 16) return 0;   // row groups of 16 outputs; inputs in groups of 8
@@ -244,6 +265,18 @@ int moe_pack_nvfp4_expert(const uint8_t* gc, const uint8_t* gs, const uint8_t* u
     nv_tiles(uc, us, I, H, 2, 1, w13);
     nv_tiles(dc, ds, H, I, 1, 0, w2);
     return MOE_OK;
+}
+
+int moe_pack_nvfp4r_expert(const uint8_t* const base[6], const uint8_t* const res[6], int32_t H,
+                           int32_t I, uint8_t* w13, uint8_t* w2) {
+    if (!base || !res || !w13 || !w2) return fail(MOE_EINVAL, "moe_pack_nvfp4r_expert: null pointer");
+    for (int i = 0; i < 6; ++i)
+        if (!base[i] || !res[i]) return fail(MOE_EINVAL, "moe_pack_nvfp4r_expert: null pointer");
+    int st = moe_pack_nvfp4_expert(base[0], base[1], base[2], base[3], base[4], base[5], H, I, w13,
+                                   w2);
+    if (st) return st;
+    return moe_pack_nvfp4_expert(res[0], res[1], res[2], res[3], res[4], res[5], H, I,
+                                 w13 + nv_rec_bytes(0, H, I), w2 + nv_rec_bytes(1, H, I));
 }
 
 int moe_pack_vq_expert(const uint16_t* gc, const uint16_t* gs, const uint16_t* uc,

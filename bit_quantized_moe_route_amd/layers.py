@@ -11,18 +11,21 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from . import (FMT_BF16, FMT_NVFP4, FMT_VQ, FMT_VQ8, PROJ_DOWN, PROJ_GATE, PROJ_UP, QLayer,
-               pack_bf16_expert, pack_nvfp4_expert, pack_vq8_expert, pack_vq_expert,
-               quantize_nvfp4)
+from . import (FMT_BF16, FMT_NVFP4, FMT_NVFP4R, FMT_VQ, FMT_VQ8, PROJ_DOWN, PROJ_GATE, PROJ_UP,
+               QLayer, pack_bf16_expert, pack_nvfp4_expert, pack_nvfp4r_expert, pack_vq8_expert,
+               pack_vq_expert, quantize_nvfp4, quantize_nvfp4_residual)
 
 
 def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=None,
                 codebook_stride=0, vq8_codes=None, codebooks8=None, vq8_m=0, bf16_weights=None,
-                device="cuda", workers=8, resident_formats=None, rot_signs=None):
+                device="cuda", workers=8, resident_formats=None, rot_signs=None,
+                nvfp4r_shift=None):
     """Build a QLayer.
 
     nvfp4_weights(e, proj) -> fp32 [n, kin] source weights of an NVFP4 expert
-        (proj 0 = gate [I, H], 1 = up [I, H], 2 = down [H, I]).
+        (proj 0 = gate [I, H], 1 = up [I, H], 2 = down [H, I]), also of a
+        nested two-level NVFP4 expert (its base and residual planes are
+        quantized from them).
     vq_codes(e, proj) -> (codes uint16 [n, kin/8], scales fp16 bits uint16 [n])
         of a VQ expert.
     codebooks: three uint16 arrays (fp16 bits) [65536 * n_books, 8] for gate,
@@ -34,7 +37,11 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         routed BF16-tier expert, or the one expert of a shared-expert layer).
     resident_formats: None, or the formats every expert is packed in (slot e of
         each of those pools), for a layer whose tiers change at run time
-        (QLayer.set_tiers).
+        (QLayer.set_tiers); {FMT_NVFP4, FMT_NVFP4R} (with others or not) makes
+        the layer nested: NVFP4-tier experts run on the base planes of their
+        two-level records.
+    nvfp4r_shift: the residual-plane exponent of two-level NVFP4 experts
+        (default NVFP4R_SHIFT).
     rot_signs(e) -> (s_in13 [H], s_out_gate [I], s_out_up [I], s_in2 [I],
         s_out2 [H]) int8 +-1: the layer's matrices are stored rotated (the
         providers above return the rotated matrices) and these are each
@@ -42,17 +49,20 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
     """
     import torch
 
+    from . import NVFP4R_SHIFT
     layer = QLayer(E, H, I, fmt_host, device=device, vq8_m=vq8_m,
-                   resident_formats=resident_formats)
+                   resident_formats=resident_formats,
+                   nvfp4r_shift=NVFP4R_SHIFT if nvfp4r_shift is None else nvfp4r_shift)
     host = {}
     for key, pool in layer.pools.items():
-        if pool is not None:
+        if pool is not None and key[0] not in layer.alias:
             host[key] = np.zeros(pool.numel(), np.uint8)
 
     def one(e):
         if layer.resident is not None:
             for fmt in sorted(layer.resident):
-                pack_one(e, fmt, e)
+                if fmt not in layer.alias:   # a nested layer's base planes
+                    pack_one(e, fmt, e)
         else:
             pack_one(e, int(layer.fmt_host[e]), layer.record_index(e))
 
@@ -63,6 +73,10 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         if fmt == FMT_NVFP4:
             parts = [quantize_nvfp4(nvfp4_weights(e, p)) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
             w13, w2 = pack_nvfp4_expert(parts[0], parts[1], parts[2], H, I)
+        elif fmt == FMT_NVFP4R:
+            parts = [quantize_nvfp4_residual(nvfp4_weights(e, p), layer.nvfp4r_shift)
+                     for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
+            w13, w2 = pack_nvfp4r_expert([q[0] for q in parts], [q[1] for q in parts], H, I)
         elif fmt == FMT_BF16:
             parts = [bf16_weights(e, p) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
             w13, w2 = pack_bf16_expert(parts[0], parts[1], parts[2], H, I)

@@ -37,6 +37,9 @@
  *   - stored matrices rotated by random signs and a Hadamard-128 transform
  *     on both sides, the activations rotated online:
  *     "GLM-5.3 Vision NestQuant 1.75-4 bit", Method.
+ *   - a nested two-level format, a base plus a residual plane that lifts an
+ *     expert to the higher tier at serving time with the base bytes
+ *     unchanged: "GLM-5.3 Vision NestQuant 1.75-4 bit", introduction.
  *   - BF16 shared experts beside the low-bit routed ones:
  *     "GLM-5.3-EXL3-TR3-3.42bpw", What is quantized; "GLM-5-NVFP4-MTP",
  *     What's quantized (shared experts are among the non-expert weights
@@ -89,7 +92,10 @@ extern "C" {
                                  summed, fp16 scale per output channel
                                  (M bits per weight) */
 #define MOE_FMT_BF16  4       /* bf16 weights as stored, no scales */
-#define MOE_FMT_MAX   4       /* largest format tag */
+#define MOE_FMT_NVFP4R 5      /* nested two-level NVFP4: an NVFP4 base plane
+                                 plus an NVFP4 residual plane on top of it
+                                 (weights = base + residual) */
+#define MOE_FMT_MAX   5       /* largest format tag */
 
 #define MOE_PROJ_GATE 0
 #define MOE_PROJ_UP   1
@@ -130,6 +136,24 @@ extern "C" {
  *   vq8_codebook[p] fp16 [vq8_m][256][8]: the small codebooks of projection
  *                   p, shared by every MOE_FMT_VQ8 expert of the layer.
  *   bf16_w13 / bf16_w2 pool bases of the MOE_FMT_BF16 records.
+ *   nvfp4r_w13 / nvfp4r_w2  pool bases of the MOE_FMT_NVFP4R records: each
+ *                   record is an NVFP4 record (the base plane) followed by
+ *                   the NVFP4 record of the residual plane, each of
+ *                   moe_record_bytes(MOE_FMT_NVFP4, ...) bytes.  A resident
+ *                   layer may point nvfp4_w13 / nvfp4_w2 at the same pools
+ *                   with the same strides: an expert tagged MOE_FMT_NVFP4
+ *                   then runs on its base plane alone, and retagging it
+ *                   MOE_FMT_NVFP4R adds the residual plane on top, with the
+ *                   base bytes unchanged ("GLM-5.3 Vision NestQuant 1.75-4
+ *                   bit", introduction: a nested two-level format whose
+ *                   residual plane lifts an expert to the higher tier at
+ *                   serving time).
+ *   nvfp4r_shift    0 .. 14: the residual plane holds the residual times
+ *                   2^nvfp4r_shift (a per-layer power of two that brings its
+ *                   small block maxima into the E4M3 scales' normal range)
+ *                   and is decoded times 2^-nvfp4r_shift; every decoded value
+ *                   stays exact in fp16.  Any value if the layer has no
+ *                   MOE_FMT_NVFP4R experts.
  *   rot_signs       NULL: the stored matrices are the weights.  Otherwise
  *                   every expert's matrices are stored rotated,
  *                   W_rot = R_out W R_in^T with R = blockdiag(H_128/sqrt(128))
@@ -176,6 +200,10 @@ typedef struct moe_qlayer {
     int32_t record_mode;
     int32_t reserved;
     const uint8_t* rot_signs;
+    const void* nvfp4r_w13; int64_t nvfp4r_w13_stride;
+    const void* nvfp4r_w2;  int64_t nvfp4r_w2_stride;
+    int32_t nvfp4r_shift;
+    int32_t reserved2;
 } moe_qlayer;
 
 #define MOE_REC_COMPACT   0
@@ -414,8 +442,22 @@ int moe_quantize_nvfp4(const float* w, int32_t n, int32_t kin,
                        uint8_t* codes, uint8_t* scales);
 
 /*
+ * moe_quantize_nvfp4_residual -- [host] the two planes of MOE_FMT_NVFP4R:
+ * base = moe_quantize_nvfp4(w); residual = moe_quantize_nvfp4(r) with
+ * r = fp32((w - base value) * 2^shift) (exact in fp64, rounded once to
+ * fp32), 0 <= shift <= 14.  Same byte layout and errors as
+ * moe_quantize_nvfp4.
+ * ("GLM-5.3 Vision NestQuant 1.75-4 bit", introduction and Method: a base
+ * plus a residual plane coding what the base leaves.)
+ */
+int moe_quantize_nvfp4_residual(const float* w, int32_t n, int32_t kin, int32_t shift,
+                                uint8_t* base_codes, uint8_t* base_scales,
+                                uint8_t* res_codes, uint8_t* res_scales);
+
+/*
  * Bytes of one expert record in the device tile layout.
- *   fmt = MOE_FMT_NVFP4 / MOE_FMT_VQ / MOE_FMT_BF16 (MOE_FMT_VQ8: use
+ *   fmt = MOE_FMT_NVFP4 / MOE_FMT_VQ / MOE_FMT_BF16 / MOE_FMT_NVFP4R (twice
+ *   the NVFP4 record: base plane, then residual plane) (MOE_FMT_VQ8: use
  *   moe_record_bytes_vq8); which = 0 for the gate/up record
  *   (both projections, rows interleaved by 16), 1 for the down record.
  * Returns 0 for an unsupported format or shape.
@@ -435,6 +477,17 @@ int moe_pack_nvfp4_expert(const uint8_t* gate_codes, const uint8_t* gate_scales,
                           const uint8_t* up_codes, const uint8_t* up_scales,
                           const uint8_t* down_codes, const uint8_t* down_scales,
                           int32_t H, int32_t I, uint8_t* w13_rec, uint8_t* w2_rec);
+
+/*
+ * moe_pack_nvfp4r_expert -- [host] lay one MOE_FMT_NVFP4R expert out as its
+ * two records: the base plane's NVFP4 record (from base_parts) followed by
+ * the residual plane's (from res_parts).  base_parts / res_parts: the six
+ * arrays moe_pack_nvfp4_expert takes, in its order (gate codes, gate scales,
+ * up codes, up scales, down codes, down scales).  w13_rec / w2_rec [host]
+ * out, moe_record_bytes(MOE_FMT_NVFP4R, ...) each.
+ */
+int moe_pack_nvfp4r_expert(const uint8_t* const base_parts[6], const uint8_t* const res_parts[6],
+                           int32_t H, int32_t I, uint8_t* w13_rec, uint8_t* w2_rec);
 
 /*
  * moe_pack_vq_expert -- [host] lay one VQ expert out as its two records.
@@ -514,8 +567,10 @@ int moe_record_table_resident(const uint8_t* fmt_host, int32_t E, int32_t* rec);
  * same device decode routines the FFN kernels use.  NVFP4 and VQ values are
  * exact; a MOE_FMT_VQ8 value with m >= 2 is fp32(fp32(C_0 + .. + C_{m-1}) * S) (fp32
  * sums; the FFN kernels multiply each codebook row exactly instead); a
- * MOE_FMT_BF16 value is the stored weight as the kernels' fp16 operand.  For
- * a rotated layer this is the stored (rotated) matrix.
+ * MOE_FMT_BF16 value is the stored weight as the kernels' fp16 operand; a
+ * MOE_FMT_NVFP4R value is fp32(base + residual * 2^-nvfp4r_shift) (the FFN
+ * kernels multiply each plane exactly instead).  For a rotated layer this is the stored (rotated)
+ * matrix.
  */
 int moe_dequant_q(const moe_qlayer* layer, int32_t expert, int32_t proj,
                   float* out, void* stream);

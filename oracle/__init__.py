@@ -21,7 +21,8 @@ it follows:
 * GLM-5.3-EXL3-TR3-3.42bpw, "What is quantized" -- BF16 shared experts beside
   the routed ones.
 * GLM-5.3 Vision NestQuant 1.75-4 bit, "Method" -- random signs and a
-  Hadamard-128 transform on both sides of each weight matrix.
+  Hadamard-128 transform on both sides of each weight matrix; introduction --
+  a nested two-level format: a base plus a residual plane on top of it.
 
 Where the pages are silent the oracle takes the plainest reading, stated in
 the docstring of the function that makes it.
@@ -30,7 +31,7 @@ Parity status per function (what pins each one is in tests/test_oracle_*.py):
   e2m1_decode, e4m3_decode, e4m3_encode, nvfp4_quantize, nvfp4_dequant,
   vq_dequant, vq8_dequant, route_topk, permute, expert_ffn, combine,
   combine_shared, forward, hadamard, rotate, unrotate, rotate_weights,
-  unrotate_weights
+  unrotate_weights, nvfp4_residual_quantize, nvfp4r_dequant
   -- all pinned.  vq8_dequant's arithmetic is pinned; its code shape (M
   8-bit codes per 8-weight group into M 256-entry codebooks whose rows are
   summed) is a reading the pages do not fix: parity unpinned for the shape.
@@ -44,6 +45,8 @@ from .formats import (  # noqa: F401
     e4m3_finite_table,
     nvfp4_quantize,
     nvfp4_dequant,
+    nvfp4_residual_quantize,
+    nvfp4r_dequant,
     vq_dequant,
     vq8_dequant,
     bf16_bits_to_f64,

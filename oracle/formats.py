@@ -204,6 +204,37 @@ def nvfp4_dequant(codes, scales):
 
 
 # --------------------------------------------------------------------------
+# Nested two-level NVFP4 (a base plane plus a residual plane)
+# --------------------------------------------------------------------------
+
+def nvfp4_residual_quantize(w, shift):
+    """The two planes of a nested two-level NVFP4 matrix.
+
+    "GLM-5.3 Vision NestQuant 1.75-4 bit", introduction and Method: each
+    expert has a base plus a residual plane that lifts it to the higher tier;
+    the residual is coded on what the base leaves.  Reading (their base and
+    residual are trellis codes; here both planes are NVFP4): base =
+    nvfp4_quantize(w); residual = nvfp4_quantize(r) with r = (w - base value)
+    * 2^shift, exact in float64 and rounded once to fp32.  The power of two
+    brings the residual's small block maxima into the normal range of the
+    E4M3 scales (without it most of them round to a zero scale).  Returns
+    ((base codes, base scales), (residual codes, residual scales)).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    if not 0 <= shift <= 14:
+        raise ValueError("shift must be in [0, 14]")
+    bc, bs = nvfp4_quantize(w)
+    r = np.ldexp(w.astype(np.float64) - nvfp4_dequant(bc, bs), shift).astype(np.float32)
+    rc, rs = nvfp4_quantize(r)
+    return (bc, bs), (rc, rs)
+
+
+def nvfp4r_dequant(base, res, shift):
+    """W = base value + residual value * 2^-shift (NVFP4 decodes), float64."""
+    return nvfp4_dequant(*base) + np.ldexp(nvfp4_dequant(*res), -shift)
+
+
+# --------------------------------------------------------------------------
 # AQLM-style VQ decode
 # --------------------------------------------------------------------------
 

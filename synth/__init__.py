@@ -54,6 +54,8 @@ FMT_NVFP4 = 1
 FMT_VQ = 2
 FMT_VQ8 = 3
 FMT_BF16 = 4
+FMT_NVFP4R = 5      # nested two-level NVFP4 (base plane + residual plane)
+NVFP4R_SHIFT = 8    # residual-plane exponent of the nested layers
 
 
 def rng(cfg, kind, expert=0, proj=0, rep=0):
@@ -92,7 +94,8 @@ class Workload:
     I: int
     T: tuple
     fmt: str            # "nvfp4", "vq", "vq8", "bf16", "mixed" (NVFP4 + VQ), "mixed3"
-                        # (+ VQ8) or "nv_bf16" (NVFP4 + BF16)
+                        # (+ VQ8), "nv_bf16" (NVFP4 + BF16) or "nested" (NVFP4 base
+                        # tier, some experts lifted to two-level NVFP4)
     logits: str         # "normal", "uniform", "zipf" or "hot"
     weight_cfg: int = 1     # seed slot of the NVFP4 weights
     vq_cfg: int = 3         # seed slot of the VQ codes/codebooks/scales
@@ -129,11 +132,16 @@ DECODE_ROT = Workload("decode_rot", 7, 256, 8, 6144, 2048, (1, 8, 32), "nvfp4", 
                       weight_cfg=1, rot=True)
 DECODE_SHARED = Workload("decode_shared", 1, 256, 8, 6144, 2048, (1, 8, 32), "nvfp4", "uniform",
                          shared=True)
+# the decode layer's NVFP4 experts (same source weights) held nested: every
+# expert's two-level record resident, the 20 hot experts (60% of the
+# assignments) lifted to the two-level tier, the rest on their base planes
+NESTED = Workload("nested", 9, 256, 8, 6144, 2048, (8, 32), "nested", "hot", weight_cfg=1,
+                  n_hot=20, hot_share=0.6)
 PREFILL_SHARED = Workload("prefill_shared", 2, 256, 8, 6144, 2048, (4096,), "nvfp4", "zipf",
                           zipf_s=1.1, shared=True)
 
 WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED, VQ1, VQ2X8, VQ3X8, DECODE_SHARED,
-                                 PREFILL_SHARED, DECODE_ROT)}
+                                 PREFILL_SHARED, DECODE_ROT, NESTED)}
 
 
 def small_workload(name, E, k, H, I, T, fmt="nvfp4", logits="normal", cfg=100,
@@ -329,7 +337,8 @@ def tier_map_hot(wl):
 
 
 def tier_map(wl):
-    """Per-expert format tag (FMT_NVFP4 / FMT_VQ / FMT_VQ8 / FMT_BF16), uint8 [E]."""
+    """Per-expert format tag (FMT_NVFP4 / FMT_VQ / FMT_VQ8 / FMT_BF16 /
+    FMT_NVFP4R), uint8 [E]."""
     if wl.fmt == "nvfp4":
         return np.full(wl.E, FMT_NVFP4, dtype=np.uint8)
     if wl.fmt == "bf16":
@@ -342,6 +351,13 @@ def tier_map(wl):
         return np.full(wl.E, FMT_VQ, dtype=np.uint8)
     if wl.fmt == "vq8":
         return np.full(wl.E, FMT_VQ8, dtype=np.uint8)
+    if wl.fmt == "nested":
+        # the hot experts (or n_nvfp4 seeded ones) on the two-level tier
+        tm = np.full(wl.E, FMT_NVFP4, dtype=np.uint8)
+        up = (hot_experts(wl) if wl.n_hot
+              else rng(wl.cfg, KIND_TIER).choice(wl.E, size=wl.n_nvfp4, replace=False))
+        tm[up] = FMT_NVFP4R
+        return tm
     g = rng(wl.cfg, KIND_TIER)
     tm = np.full(wl.E, FMT_VQ, dtype=np.uint8)
     nv = g.choice(wl.E, size=wl.n_nvfp4, replace=False)

@@ -38,6 +38,10 @@ def build_small_layer(wl, device="cuda", resident_formats=None):
     from bit_quantized_moe_route_amd.layers import build_layer
 
     fmt_host = synth.tier_map(wl)
+    if wl.fmt == "nested" and resident_formats is None:
+        # both tiers resident: the NVFP4 tier runs on the two-level records'
+        # base planes
+        resident_formats = {synth.FMT_NVFP4, synth.FMT_NVFP4R}
     used = set(np.unique(fmt_host).tolist()) | set(resident_formats or ())
     cbs = [synth.vq_codebook(wl, p) for p in range(3)] if synth.FMT_VQ in used else None
     cbs8 = [synth.vq8_codebooks(wl, p) for p in range(3)] if synth.FMT_VQ8 in used else None
@@ -50,6 +54,7 @@ def build_small_layer(wl, device="cuda", resident_formats=None):
         codebooks8=cbs8, vq8_m=wl.vq8_m,
         bf16_weights=lambda e, p: synth.bf16_weights(wl, e, p),
         device=device, workers=16, resident_formats=resident_formats,
+        nvfp4r_shift=synth.NVFP4R_SHIFT,
         rot_signs=(lambda e: tuple(synth.rot_signs(wl, e, side) for side in range(5)))
         if wl.rot else None)
 

@@ -22,6 +22,10 @@ def expert_weights(wl, e, fmt=None):
         if fmt == synth.FMT_NVFP4:
             c, s = oracle.nvfp4_quantize(synth.nvfp4_source_weights(wl, e, p))
             mats.append(oracle.nvfp4_dequant(c, s))
+        elif fmt == synth.FMT_NVFP4R:
+            base, res = oracle.nvfp4_residual_quantize(synth.nvfp4_source_weights(wl, e, p),
+                                                       synth.NVFP4R_SHIFT)
+            mats.append(oracle.nvfp4r_dequant(base, res, synth.NVFP4R_SHIFT))
         elif fmt == synth.FMT_BF16:
             mats.append(oracle.bf16_bits_to_f64(synth.bf16_weights(wl, e, p)))
         elif fmt == synth.FMT_VQ8:

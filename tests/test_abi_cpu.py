@@ -57,6 +57,41 @@ def test_quantize_nvfp4_matches_oracle(shape, seed):
     assert np.array_equal(s, os_)
 
 
+@pytest.mark.parametrize("shape,seed,shift", [((8, 64), 1, 8), ((48, 272), 2, 0), ((16, 128), 3, 14)])
+def test_quantize_nvfp4_residual_matches_oracle(shape, seed, shift):
+    """The library's two-plane quantizer (C) against the oracle's (numpy),
+    byte for byte; its base plane is the plain NVFP4 quantization."""
+    rs = np.random.default_rng(seed)
+    w = (rs.standard_normal(shape) * 0.02).astype(np.float32)
+    (bc, bs), (rc, rs_) = moeq.quantize_nvfp4_residual(w, shift)
+    (obc, obs), (orc, ors) = oracle.nvfp4_residual_quantize(w, shift)
+    for a, b in ((bc, obc), (bs, obs), (rc, orc), (rs_, ors)):
+        assert np.array_equal(a, b)
+    c, s = moeq.quantize_nvfp4(w)
+    assert np.array_equal(bc, c) and np.array_equal(bs, s)
+    with pytest.raises(moeq.MoeError):
+        moeq.quantize_nvfp4_residual(w, 15)
+
+
+def test_nvfp4r_record_layout():
+    """A two-level record is the base plane's NVFP4 record followed by the
+    residual plane's, each at the NVFP4 record size."""
+    H, I = 272, 80
+    rs = np.random.default_rng(4)
+    parts = [moeq.quantize_nvfp4_residual((rs.standard_normal(sh) * 0.02).astype(np.float32))
+             for sh in ((I, H), (I, H), (H, I))]
+    base = [p[0] for p in parts]
+    res = [p[1] for p in parts]
+    w13, w2 = moeq.pack_nvfp4r_expert(base, res, H, I)
+    n13, n2 = moeq.record_bytes(moeq.FMT_NVFP4, 0, H, I), moeq.record_bytes(moeq.FMT_NVFP4, 1, H, I)
+    assert w13.shape[0] == 2 * n13 == moeq.record_bytes(moeq.FMT_NVFP4R, 0, H, I)
+    assert w2.shape[0] == 2 * n2 == moeq.record_bytes(moeq.FMT_NVFP4R, 1, H, I)
+    b13, b2 = moeq.pack_nvfp4_expert(*base, H, I)
+    r13, r2 = moeq.pack_nvfp4_expert(*res, H, I)
+    assert np.array_equal(w13[:n13], b13) and np.array_equal(w13[n13:], r13)
+    assert np.array_equal(w2[:n2], b2) and np.array_equal(w2[n2:], r2)
+
+
 def test_quantize_nvfp4_crafted_matches_oracle(golden_dir):
     rs = np.random.default_rng(5)
     rows = []
@@ -254,14 +289,14 @@ def test_record_table_resident():
     rec = moeq.record_table_resident(tm)
     assert np.array_equal(rec >> 24, tm) and np.array_equal(rec & 0xFFFFFF, np.arange(6))
     with pytest.raises(moeq.MoeError) as ei:
-        moeq.record_table_resident(np.array([1, 5], np.uint8))
+        moeq.record_table_resident(np.array([1, 6], np.uint8))
     assert ei.value.status == moeq.MOE_EUNSUPPORTED
 
 
 def test_record_table():
     tm = synth.tier_map(synth.MIXED)
     rec, counts = moeq.record_table(tm)
-    assert counts == {1: 108, 2: 148, 3: 0, 4: 0}
+    assert counts == {1: 108, 2: 148, 3: 0, 4: 0, 5: 0}
     for fmt in (1, 2):
         sel = np.nonzero(tm == fmt)[0]
         assert np.all(rec[sel] >> 24 == fmt)
@@ -275,10 +310,13 @@ def test_record_table():
         assert np.all(rec[sel] >> 24 == fmt)
         assert np.array_equal(rec[sel] & 0xFFFFFF, np.arange(sel.size))
     rec, counts = moeq.record_table(np.array([4, 1, 4], np.uint8))
-    assert counts == {1: 1, 2: 0, 3: 0, 4: 2}
+    assert counts == {1: 1, 2: 0, 3: 0, 4: 2, 5: 0}
     assert list(rec) == [4 << 24, 1 << 24, (4 << 24) | 1]
+    rec, counts = moeq.record_table(np.array([5, 1, 5, 5], np.uint8))
+    assert counts[5] == 3 and counts[1] == 1
+    assert list(rec) == [5 << 24, 1 << 24, (5 << 24) | 1, (5 << 24) | 2]
     bad = tm.copy()
-    bad[7] = 5
+    bad[7] = 6
     with pytest.raises(moeq.MoeError) as ei:
         moeq.record_table(bad)
     assert ei.value.status == moeq.MOE_EUNSUPPORTED
@@ -385,6 +423,30 @@ def test_ffn_rejects_bad_shapes_and_workspace():
                               N) == moeq.MOE_EINVAL  # k > E
     assert L.moe_dequant_q(ctypes.byref(d), 8, 0, fake, N) == moeq.MOE_EINVAL
     assert L.moe_dequant_q(ctypes.byref(d), 0, 3, fake, N) == moeq.MOE_EINVAL
+
+
+def test_nvfp4r_layer_host_checks():
+    """Two-level NVFP4 experts need their pools and a residual exponent in
+    [0, 14]; checked before any launch."""
+    L = moeq.lib()
+    fake = ctypes.c_void_p(0x1000)
+    N = ctypes.c_void_p(0)
+    tm = np.array([1, 5, 5, 1], np.uint8)
+    d = _fake_layer(tm)
+    need = L.moe_ffn_workspace_bytes(ctypes.byref(d), 4, 2)
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, need,
+                              N) == moeq.MOE_EINVAL            # NVFP4R pools NULL
+    assert b"NVFP4R" in L.moe_last_error()
+    d.nvfp4r_w13 = d.nvfp4r_w2 = 0x100000
+    d.nvfp4r_w13_stride = d.nvfp4r_w2_stride = 1 << 20
+    d.nvfp4r_shift = 15
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, need,
+                              N) == moeq.MOE_EUNSUPPORTED
+    assert b"nvfp4r_shift" in L.moe_last_error()
+    d.nvfp4r_shift = 8
+    d.nvfp4r_w2_stride = moeq.record_bytes(moeq.FMT_NVFP4, 1, 256, 128)   # one plane only
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, need,
+                              N) == moeq.MOE_EINVAL
 
 
 def test_layer_forward_host_checks():

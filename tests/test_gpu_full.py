@@ -2,7 +2,8 @@
 I 2048) in the launch configurations the benchmark times: decode T = 1, 8,
 32 (NVFP4), prefill T = 4096 with Zipf(1.1) routing (NVFP4), 2-bit VQ T = 8,
 the small-codebook VQ layers (1 and 2 bits per weight) at T = 8 and the mixed
-NVFP4/VQ layer at T = 8 and 32.
+NVFP4/VQ layer at T = 8 and 32, and the decode layer held nested (two-level NVFP4
+experts) at T = 8.
 
 Routing and permutation are compared in full (bit-exact).  Expert outputs
 are compared row by row against the oracle on sampled experts (the oracle
@@ -261,6 +262,26 @@ def test_mixed_full_sampled(T):
     say(f"mixed T={T}: hot share {share:.3f}, hot NVFP4 experts "
         f"{int((fmt_host[hot] == synth.FMT_NVFP4).sum())}/{len(hot)}")
     assert 0.35 < share < 0.85
+
+
+@pytest.mark.timeout(900)
+def test_nested_full_sampled():
+    """The decode layer's experts held nested (two-level records resident,
+    the 20 hot experts lifted to the two-level tier) at T = 8: routing, the
+    rows of a two-level and a base-tier expert against the oracle, the
+    combine property."""
+    wl = synth.NESTED
+    T = 8
+    say("nested full", T)
+    lay = layer("nested")
+    fmt_host = synth.tier_map(wl)
+    assert int((fmt_host == synth.FMT_NVFP4R).sum()) == wl.n_hot
+    x_bits, lg, r = run_forward(wl, lay, T)
+    ids, w, offsets, perm_src = check_routing(wl, lg, r)
+    experts = (pick(offsets, fmt_host, synth.FMT_NVFP4R, n=1, seed=T)
+               + pick(offsets, fmt_host, synth.FMT_NVFP4, n=1, seed=T + 1))
+    check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, fmt_host)
+    check_combine_property(wl, r)
 
 
 # ------------------------------------------------------------------ shared expert

@@ -202,6 +202,68 @@ def test_nvfp4_error_bound_invariant():
     assert np.all(np.sign(deq[nz]) == np.sign(w[nz]))
 
 
+# ---------------------------------------------------- nested two-level NVFP4
+
+def test_nvfp4r_representable_matrix_has_zero_residual():
+    """A matrix of NVFP4 values whose every block holds a +-6 code (so its
+    scale is recovered exactly) is its own base: the residual plane is all
+    zero codes and zero scales, and the two-level value is the matrix."""
+    rs = np.random.default_rng(21)
+    n, kin = 8, 64
+    codes = rs.integers(0, 16, size=(n, kin)).astype(np.uint8)
+    codes[:, ::16] = 7                                   # a +6 in every block
+    sb = rs.integers(0x20, 0x60, size=(n, kin // 16)).astype(np.uint8)   # normal E4M3
+    w = oracle.e2m1_decode(codes) * np.repeat(oracle.e4m3_decode(sb), 16, axis=1)
+    assert np.all(w.astype(np.float32) == w)
+    for shift in (0, 8):
+        (bc, bs), (rc, rscale) = oracle.nvfp4_residual_quantize(w.astype(np.float32), shift)
+        assert np.array_equal(oracle.nvfp4_dequant(bc, bs), w)
+        assert np.all(rc == 0) and np.all(rscale == 0)
+        assert np.array_equal(oracle.nvfp4r_dequant((bc, bs), (rc, rscale), shift), w)
+
+
+def test_nvfp4r_error_bound_and_nesting():
+    """The base plane is the plain NVFP4 quantization (the nested tier's
+    bytes), and the two-level error obeys the NVFP4 bound on the residual:
+    with S the residual block's E4M3 scale and a its largest |r|, an element
+    not past 6 S is within S (half the widest E2M1 gap) of r, one past it
+    within |r| - 6 S; scaled back by 2^-shift, plus r's fp32 rounding."""
+    rs = np.random.default_rng(22)
+    w = (rs.standard_normal((32, 512)) * 0.02).astype(np.float32)
+    shift = 8
+    (bc, bs), (rc, rsc) = oracle.nvfp4_residual_quantize(w, shift)
+    c0, s0 = oracle.nvfp4_quantize(w)
+    assert np.array_equal(bc, c0) and np.array_equal(bs, s0)
+    base = oracle.nvfp4_dequant(bc, bs)
+    r64 = np.ldexp(w.astype(np.float64) - base, shift)
+    r = r64.astype(np.float32).astype(np.float64)
+    S = np.repeat(oracle.e4m3_decode(rsc), 16, axis=1)
+    q = oracle.nvfp4_dequant(rc, rsc)
+    sat = np.abs(r) > 6 * S
+    err = np.abs(r - q)
+    assert np.all(err[~sat] <= S[~sat])
+    assert np.all(err[sat] <= np.abs(r[sat]) - 6 * S[sat] + 1e-30)
+    two = oracle.nvfp4r_dequant((bc, bs), (rc, rsc), shift)
+    bound = np.ldexp(np.where(sat, np.abs(r) - 6 * S, S) + np.abs(r64 - r), -shift)
+    assert np.all(np.abs(w - two) <= bound * (1 + 1e-12))
+    # the residual plane cuts the error of N(0, 0.02) weights by an order of
+    # magnitude (its scales are in E4M3's normal range at this shift)
+    assert np.sqrt(np.mean((w - two) ** 2)) < np.sqrt(np.mean((w - base) ** 2)) / 8
+
+
+def test_nvfp4r_shift_zero_loses_small_residuals():
+    """Without the power of two the residual's block maxima fall below the
+    smallest E4M3 scale and most residual blocks get scale 0 (why the layer
+    carries an exponent for the residual plane)."""
+    rs = np.random.default_rng(23)
+    w = (rs.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    (_, _), (_, rsc0) = oracle.nvfp4_residual_quantize(w, 0)
+    (_, _), (_, rsc8) = oracle.nvfp4_residual_quantize(w, 8)
+    assert np.mean(rsc0 == 0) > 0.5 and np.all(rsc8 != 0)
+    with pytest.raises(ValueError):
+        oracle.nvfp4_residual_quantize(w, 15)
+
+
 def test_nvfp4_zero_blocks_and_zero_scale():
     w = np.zeros((2, 32), dtype=np.float32)
     w[1, 16:] = np.float32(3 * 2.0 ** -11)   # amax/6 = 2^-12 -> scale 0 -> all codes 0
