@@ -101,7 +101,7 @@ extern "C" {
 #define MOE_PROJ_UP   1
 #define MOE_PROJ_DOWN 2
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define MOE_MAX_E     1024    /* experts per layer */
 #define MOE_MAX_K     16      /* experts per token */
 #define MOE_VQ_NCODE  65536   /* codebook entries (uint16 codes) */
