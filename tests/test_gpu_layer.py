@@ -50,6 +50,12 @@ CASES = {
     "mixed": (synth.small_workload("lf_mixed", E=24, k=6, H=384, I=96, T=2, fmt="mixed",
                                    logits="hot", cfg=188, n_nvfp4=9, n_hot=4, hot_share=0.6), 2),
     "rot": (synth.small_workload("lf_rot", E=16, k=4, H=384, I=256, T=1, cfg=189, rot=True), 1),
+    # the edges of the fused path: exactly 16 assignments (fused) and 17
+    # (not), k = 9 > 8 at one token (not), 257 experts (not: more than 256)
+    "edge_16": (synth.small_workload("lf_edge16", E=24, k=4, H=256, I=128, T=4, cfg=192), 4),
+    "edge_17": (synth.small_workload("lf_edge17", E=24, k=1, H=256, I=128, T=17, cfg=193), 17),
+    "edge_k9": (synth.small_workload("lf_edgek9", E=24, k=9, H=256, I=128, T=1, cfg=194), 1),
+    "edge_e257": (synth.small_workload("lf_edgee257", E=257, k=8, H=128, I=64, T=2, cfg=195), 2),
 }
 
 _layers = {}
