@@ -451,7 +451,8 @@ def test_shared_ffn_matches_routed_call(T):
 
 
 @pytest.mark.parametrize("fmt,T", [(synth.FMT_NVFP4, 20), (synth.FMT_VQ8, 9), (synth.FMT_VQ, 33),
-                                   (synth.FMT_NVFP4, 150)])
+                                   (synth.FMT_NVFP4, 150), (synth.FMT_NVFP4R, 20),
+                                   (synth.FMT_NVFP4R, 150)])
 def test_shared_expert_other_formats(fmt, T):
     """A shared-expert layer in a low-bit format goes through the same calls."""
     from bit_quantized_moe_route_amd.layers import build_layer
@@ -464,7 +465,7 @@ def test_shared_expert_other_formats(fmt, T):
         codebooks=[synth.vq_codebook(wl, p) for p in range(3)] if fmt == synth.FMT_VQ else None,
         vq8_codes=lambda e, p: (synth.vq8_codes(wl, e, p), synth.vq_scales(wl, e, p)),
         codebooks8=[synth.vq8_codebooks(wl, p) for p in range(3)] if fmt == synth.FMT_VQ8 else None,
-        vq8_m=2, device=DEV, workers=1)
+        vq8_m=2, device=DEV, workers=1, nvfp4r_shift=synth.NVFP4R_SHIFT)
     x_bits = synth.activations(wl, T)
     y = moeq.shared_ffn(lay, torch.from_numpy(x_bits.view(np.int16)).to(DEV))
     ref = oracle.expert_ffn(x_bits, *expert_weights(wl, 0, fmt))
