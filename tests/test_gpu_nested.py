@@ -31,6 +31,12 @@ NESTED = {
     "nest_prefill": synth.small_workload("nest_prefill", E=8, k=2, H=256, I=128, T=260,
                                          fmt="nested", logits="zipf", zipf_s=1.1, cfg=202,
                                          n_nvfp4=3),
+    # stored rotated (signs + Hadamard-128 on both sides): decode and prefill
+    "nest_rot": synth.small_workload("nest_rot", E=12, k=3, H=256, I=128, T=21, fmt="nested",
+                                     cfg=204, n_nvfp4=5, rot=True),
+    "nest_rot_prefill": synth.small_workload("nest_rot_prefill", E=8, k=2, H=256, I=128,
+                                             T=200, fmt="nested", cfg=205, n_nvfp4=4,
+                                             rot=True),
 }
 
 
