@@ -100,5 +100,6 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         layer.set_codebooks(codebooks, codebook_stride)
     if layer.pools[(FMT_VQ8, 0)] is not None:
         layer.set_codebooks8(codebooks8)
-    torch.cuda.synchronize(layer.device)
+    if layer.device.type == "cuda":
+        torch.cuda.synchronize(layer.device)
     return layer

@@ -449,6 +449,47 @@ def test_nvfp4r_layer_host_checks():
                               N) == moeq.MOE_EINVAL
 
 
+def test_nested_layer_host_side():
+    """A nested layer (NVFP4 and two-level NVFP4 resident) built in host
+    memory: the NVFP4 pools are the two-level records (same buffers and
+    strides in the descriptor), the base planes are the plain NVFP4 records,
+    set_residual rewrites only the residual halves, and set_tiers moves
+    experts between the tags."""
+    from bit_quantized_moe_route_amd.layers import build_layer
+    E, H, I = 4, 256, 64
+    rs = np.random.default_rng(31)
+    W = {(e, p): (rs.standard_normal((I, H) if p < 2 else (H, I)) * 0.02).astype(np.float32)
+         for e in range(E) for p in range(3)}
+    tm = np.array([1, 5, 1, 5], np.uint8)
+    lay = build_layer(E, H, I, tm, nvfp4_weights=lambda e, p: W[(e, p)], device="cpu",
+                      workers=2, resident_formats={moeq.FMT_NVFP4, moeq.FMT_NVFP4R})
+    assert lay.alias == {moeq.FMT_NVFP4: moeq.FMT_NVFP4R}
+    for which in (0, 1):
+        assert lay.pools[(1, which)] is lay.pools[(5, which)]
+        assert lay.stride[(1, which)] == lay.stride[(5, which)]
+    d = lay.c()
+    assert d.nvfp4_w13 == d.nvfp4r_w13 and d.nvfp4_w2 == d.nvfp4r_w2
+    assert d.nvfp4_w13_stride == d.nvfp4r_w13_stride and d.nvfp4r_shift == moeq.NVFP4R_SHIFT
+    n13 = moeq.record_bytes(moeq.FMT_NVFP4, 0, H, I)
+    n2 = moeq.record_bytes(moeq.FMT_NVFP4, 1, H, I)
+    s13, s2 = lay.stride[(5, 0)], lay.stride[(5, 1)]
+    p13, p2 = lay.pools[(5, 0)].numpy(), lay.pools[(5, 1)].numpy()
+    for e in range(E):
+        b13, b2 = moeq.pack_nvfp4_expert(*[moeq.quantize_nvfp4(W[(e, p)]) for p in range(3)], H, I)
+        assert np.array_equal(p13[e * s13: e * s13 + n13], b13)
+        assert np.array_equal(p2[e * s2: e * s2 + n2], b2)
+    before = p13.copy(), p2.copy()
+    lay.set_residual(2, np.full(n13, 7, np.uint8), np.full(n2, 9, np.uint8))
+    changed13 = np.flatnonzero(before[0] != p13)
+    changed2 = np.flatnonzero(before[1] != p2)
+    assert changed13.min() >= 2 * s13 + n13 and changed13.max() < 2 * s13 + 2 * n13
+    assert changed2.min() >= 2 * s2 + n2 and changed2.max() < 2 * s2 + 2 * n2
+    lay.set_tiers(np.array([5, 5, 1, 1], np.uint8))
+    assert list(lay.rec_host >> 24) == [5, 5, 1, 1]
+    assert list(lay.rec_host & 0xFFFFFF) == [0, 1, 2, 3]
+    assert lay.counts[1] == 2 and lay.counts[5] == 2
+
+
 def test_layer_forward_host_checks():
     """moe_layer_forward: the step-by-step calls' checks, before any launch."""
     L = moeq.lib()
