@@ -1,0 +1,84 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU contract, the rule that
+committed HBM-traffic counters count only while the roofline kernel's
+sources are the ones they were taken on, and the arithmetic of the committed
+counter summary."""
+
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+TRAFFIC = "traffic_gateup_nvfp4_decode_T32.json"
+
+
+def run_bench(args, env_extra=None):
+    env = dict(os.environ)
+    env.update(env_extra or {})
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args,
+                          capture_output=True, text=True, env=env, timeout=120)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = run_bench(["--gpus", "2"])
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""          # no JSON line for a configuration not measured
+
+
+def test_bench_refuses_a_multi_rank_launch():
+    r = run_bench(["--gpus", "1"], {"WORLD_SIZE": "2"})
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_traffic_counts_only_on_the_sources_it_was_taken_on(monkeypatch):
+    with open(os.path.join(ROOT, "profiles", TRAFFIC)) as f:
+        d = json.load(f)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: d["source_hash"])
+    assert bench.read_traffic(TRAFFIC) == d["bytes_per_launch"]
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.read_traffic(TRAFFIC) is None
+    assert bench.read_traffic("no_such_summary.json") is None
+
+
+def test_source_hash_follows_each_roofline_source(tmp_path, monkeypatch):
+    csrc = tmp_path / "bit_quantized_moe_route_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for name in bench.ROOFLINE_SOURCES:
+        (csrc / name).write_text(f"// {name}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    assert h0 == bench.kernel_source_hash() and len(h0) == 16
+    seen = {h0}
+    for name in bench.ROOFLINE_SOURCES:
+        (csrc / name).write_text(f"// {name} changed\n")
+        h = bench.kernel_source_hash()
+        assert h not in seen, name
+        seen.add(h)
+
+
+def test_committed_traffic_summary_arithmetic():
+    """bytes per launch = mean FETCH_SIZE x (copy bytes / the copy's FETCH_SIZE)
+    + mean WRITE_SIZE x (copy bytes / the copy's WRITE_SIZE), counters in KiB."""
+    with open(os.path.join(ROOT, "profiles", TRAFFIC)) as f:
+        d = json.load(f)
+    cp = d["copy_reference"]
+    fs = cp["bytes"] / (cp["fetch_kib_raw"] * 1024)
+    ws = cp["bytes"] / (cp["write_kib_raw"] * 1024)
+    assert np.isclose(fs, cp["fetch_scale"], rtol=1e-12)
+    assert np.isclose(ws, cp["write_scale"], rtol=1e-12)
+    fetch = np.mean(d["fetch_kib_per_dispatch_raw"]) * 1024 * fs
+    write = np.mean(d["write_kib_per_dispatch_raw"]) * 1024 * ws
+    assert np.isclose(fetch, d["fetch_bytes_per_launch"], rtol=1e-9)
+    assert np.isclose(write, d["write_bytes_per_launch"], rtol=1e-9)
+    assert np.isclose(fetch + write, d["bytes_per_launch"], rtol=1e-9)
+    # the kernel reads its packed weights about once: within 10% above them
+    ratio = d["bytes_per_launch"] / d["algorithmic_bytes_per_launch_same_run"]
+    assert 1.0 <= ratio < 1.1
