@@ -49,6 +49,20 @@ def log(*a):
 ROOFLINE_SOURCES = ("dev_common.h", "ffn_decode.hip", "internal.h")
 
 
+# decode batches (T below this) take the weight-streaming kernels, larger ones
+# the grouped GEMM
+PREFILL_MIN_TOKENS = 128
+
+
+def gateup_kernel_name(T, k, n_experts):
+    """The NVFP4 gate/up decode kernel the library launches for a batch of T
+    tokens: its inputs are split over 4 / 2 / 1 waves when at most 16 / 64 /
+    more experts can be active (min(T k, experts of the format))."""
+    slots = min(T * k, n_experts)
+    ks = 4 if slots <= 16 else 2 if slots <= 64 else 1
+    return f"k_ffn<NvFmt, 1, {ks}, 2, 0, 4, false, false, false, false>"
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_moe_route_amd", "csrc")
@@ -358,6 +372,10 @@ def main():
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
+    if not 1 <= args.T < PREFILL_MIN_TOKENS:
+        print(f"--T is the decode batch of the headline: 1 <= T < {PREFILL_MIN_TOKENS} "
+              "(prefill sizes are the 'prefill' extra line)", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
@@ -565,7 +583,7 @@ def main():
         "packed_GBps": head["packed_GBps"],
         "hbm_read_probe_GBps": read_gbs,
         "roofline": {"bound": "hbm",
-                     "kernel": "k_ffn<NvFmt, 1, 1, 2, 0, 4, false, false, false, false> (NVFP4 gate/up + SwiGLU)",
+                     "kernel": gateup_kernel_name(args.T, wl.k, wl.E) + " (NVFP4 gate/up + SwiGLU)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": head["gateup_bytes_per_launch"],

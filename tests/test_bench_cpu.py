@@ -82,3 +82,32 @@ def test_committed_traffic_summary_arithmetic():
     # the kernel reads its packed weights about once: within 10% above them
     ratio = d["bytes_per_launch"] / d["algorithmic_bytes_per_launch_same_run"]
     assert 1.0 <= ratio < 1.1
+
+
+def test_bench_refuses_a_prefill_sized_headline():
+    r = run_bench(["--T", str(bench.PREFILL_MIN_TOKENS)])
+    assert r.returncode == 2 and "decode batch" in r.stderr
+    assert run_bench(["--T", "0"]).returncode == 2
+
+
+def test_roofline_kernel_name_follows_the_input_split():
+    """The gate/up decode kernel splits its inputs over 4 / 2 / 1 waves for
+    at most 16 / 64 / more possibly active experts (min(T k, E))."""
+    name = bench.gateup_kernel_name
+    assert name(1, 8, 256) == "k_ffn<NvFmt, 1, 4, 2, 0, 4, false, false, false, false>"
+    assert name(2, 8, 256) == name(1, 8, 256)                 # 16 slots
+    assert name(3, 8, 256) == "k_ffn<NvFmt, 1, 2, 2, 0, 4, false, false, false, false>"
+    assert name(8, 8, 256) == name(3, 8, 256)                 # 64 slots
+    assert name(9, 8, 256) == "k_ffn<NvFmt, 1, 1, 2, 0, 4, false, false, false, false>"
+    assert name(32, 8, 256) == name(9, 8, 256)
+    assert name(32, 8, 40) == name(3, 8, 256)                 # a 40-expert layer
+
+
+def test_committed_decode_traces_name_the_roofline_kernel():
+    """Each committed decode kernel trace lists the gate/up instantiation
+    that the bench names for its batch size."""
+    for T in (1, 8, 32):
+        p = os.path.join(ROOT, "profiles", f"decode_T{T}_nvfp4_kernel_trace.md")
+        with open(p) as f:
+            text = f.read()
+        assert f"`{bench.gateup_kernel_name(T, 8, 256)}`" in text, T
