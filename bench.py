@@ -119,7 +119,7 @@ class Runner:
         self.out = torch.empty((T, H), dtype=f32, device=dev)
         self.ws = moeq.gateup_workspace(layer, T, k)
         self.pws = moeq.permute_workspace(T, k, E, dev)
-        self.lws = moeq.layer_workspace(layer, T, k)
+        self.lws = moeq.layer_workspace(layer, T, k, shared=shared)
         self.shared = shared
         if shared is not None:
             self.y_sh = torch.empty((T, H), dtype=f32, device=dev)
@@ -130,18 +130,15 @@ class Runner:
     def step(self, r, timed):
         """One layer forward on batch r.  Untimed (warm-up and the graph
         replays that give the headline figures): the one-call layer,
-        moe_layer_forward (fused for decode batches of <= 16 assignments).
+        moe_layer_forward, or moe_layer_forward_shared with a shared expert
+        (fused for decode batches of <= 16 assignments).
         Timed eager steps: the step-by-step calls, with HIP events around the
         gate/up call (the kernel-level figures)."""
         moeq = self.moeq
         lg, x = self.batches[r % len(self.batches)]
         if not timed:
-            y_sh = None
-            if self.shared is not None:
-                moeq.shared_ffn(self.shared, x, self.y_sh, self.sws)
-                y_sh = self.y_sh
-            moeq.layer_forward(self.layer, x, lg, self.k, y_shared=y_sh, out=self.out,
-                               ids=self.ids, w=self.w, ws=self.lws)
+            moeq.layer_forward(self.layer, x, lg, self.k, out=self.out, ids=self.ids, w=self.w,
+                               ws=self.lws, shared=self.shared)
             return
         moeq.route_permute(lg, self.k, self.wl.E, (self.ids, self.w) + self.perm, self.pws)
         counts, offsets, perm_src, inv_perm = self.perm

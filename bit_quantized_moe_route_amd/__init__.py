@@ -103,6 +103,11 @@ _PROTOS = {
     "moe_layer_forward_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64, _I32]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _I64, _I32, _P, _P,
                                          _P, _P, _P, _SZ, _P]),
+    "moe_layer_forward_shared_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC),
+                                                       ctypes.POINTER(_QLayerC), _I64, _I32]),
+    "moe_layer_forward_shared": (ctypes.c_int, [ctypes.POINTER(_QLayerC),
+                                                ctypes.POINTER(_QLayerC), _P, _P, _I64, _I32,
+                                                _P, _P, _P, _P, _SZ, _P]),
     "moe_quantize_nvfp4": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "moe_quantize_nvfp4_residual": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P]),
     "moe_pack_nvfp4r_expert": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
@@ -747,23 +752,33 @@ def side_stream(device):
     return _side_streams[key]
 
 
-def layer_workspace(layer, T, k):
+def layer_workspace(layer, T, k, shared=None):
+    """Workspace of layer_forward (with `shared`: of its shared-expert form)."""
     torch = _torch()
-    n = lib().moe_layer_forward_workspace_bytes(ctypes.byref(layer.c()), T, k)
+    if shared is None:
+        n = lib().moe_layer_forward_workspace_bytes(ctypes.byref(layer.c()), T, k)
+    else:
+        n = lib().moe_layer_forward_shared_workspace_bytes(ctypes.byref(layer.c()),
+                                                           ctypes.byref(shared.c()), T, k)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=layer.device)
 
 
-def layer_forward(layer, x, logits, k, y_shared=None, out=None, ids=None, w=None, ws=None):
+def layer_forward(layer, x, logits, k, y_shared=None, out=None, ids=None, w=None, ws=None,
+                  shared=None):
     """The whole routed layer in one C call (moe_layer_forward): returns
     (topk_ids [T, k] int32, topk_w [T, k] fp32, out [T, H] fp32), with
     y_shared (fp32 [T, H], a shared expert's output) added after the routed
     sum when given.  Decode batches (T*k <= 16, k <= 8) of single-format,
-    unrotated layers run fused in two launches."""
+    unrotated layers run fused in two launches.  With `shared` (a one-expert
+    layer) instead of y_shared, the shared expert runs in the same C call
+    (moe_layer_forward_shared; `ws` from layer_workspace(..., shared=))."""
     torch = _torch()
     _need_cuda(x, logits)
     T = x.shape[0]
     if tuple(logits.shape) != (T, layer.E) or logits.dtype != torch.float32:
         raise ValueError("logits must be fp32 [T, E]")
+    if shared is not None and y_shared is not None:
+        raise ValueError("give the shared layer or its output y_shared, not both")
     if y_shared is not None:
         _need_cuda(y_shared)
         if tuple(y_shared.shape) != (T, layer.H) or y_shared.dtype != torch.float32:
@@ -775,6 +790,15 @@ def layer_forward(layer, x, logits, k, y_shared=None, out=None, ids=None, w=None
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     if w is None:
         w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if shared is not None:
+        if ws is None:
+            ws = layer_workspace(layer, T, k, shared=shared)
+        _check(lib().moe_layer_forward_shared(ctypes.byref(layer.c()), ctypes.byref(shared.c()),
+                                              _dptr(x), _dptr(logits), T, k, _dptr(ids),
+                                              _dptr(w), _dptr(out), _dptr(ws), ws.numel(),
+                                              _stream(dev)),
+               "moe_layer_forward_shared")
+        return ids, w, out
     if ws is None:
         ws = layer_workspace(layer, T, k)
     _check(lib().moe_layer_forward(ctypes.byref(layer.c()), _dptr(x), _dptr(logits), T, k,

@@ -500,6 +500,68 @@ int moe_layer_forward(const moe_qlayer* layer, const uint16_t* x_bf16, const flo
     return launch_combine(y_perm, inv_perm, topk_w, y_shared, T, k, layer->H, out, stream);
 }
 
+// moe_layer_forward_shared: the routed layer's workspace | the shared
+// expert's (moe_shared_ffn) | y_shared [T, H] fp32 (the unfused order).
+size_t moe_layer_forward_shared_workspace_bytes(const moe_qlayer* layer,
+                                                const moe_qlayer* shared, int64_t T, int32_t k) {
+    if (!layer || !shared || T < 0 || k < 1 || layer->E < 1 || layer->H <= 0 ||
+        layer->I <= 0 || shared->H <= 0 || shared->I <= 0)
+        return 0;
+    return align_up(layer_ws(layer, T, k).total) + shared_ws(shared, T) +
+           align_up((size_t)T * layer->H * 4);
+}
+
+int moe_layer_forward_shared(const moe_qlayer* layer, const moe_qlayer* shared,
+                             const uint16_t* x_bf16, const float* logits, int64_t T, int32_t k,
+                             int32_t* topk_ids, float* topk_w, float* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    LayerInfo li, ls;
+    int st = check_layer("moe_layer_forward_shared", layer, li);
+    if (st) return st;
+    st = check_layer("moe_layer_forward_shared (shared layer)", shared, ls);
+    if (st) return st;
+    if (shared->E != 1)
+        return fail(MOE_EINVAL, "moe_layer_forward_shared: the shared layer must have E == 1");
+    if (shared->rot_signs)
+        return fail(MOE_EUNSUPPORTED,
+                    "moe_layer_forward_shared: a rotated shared layer is not supported");
+    if (shared->H != layer->H)
+        return fail(MOE_EINVAL, "moe_layer_forward_shared: the shared layer's H differs");
+    st = check_route_sizes("moe_layer_forward_shared", T, layer->E, k);
+    if (st) return st;
+    if (layer->H % 4) return fail(MOE_EINVAL, "moe_layer_forward_shared: H % 4 != 0");
+    if (T == 0) return MOE_OK;
+    if (!x_bf16 || !logits || !topk_ids || !topk_w || !out)
+        return fail(MOE_EINVAL, "moe_layer_forward_shared: null pointer");
+    const size_t lw = layer_ws(layer, T, k).total;
+    const size_t sw = shared_ws(shared, T);
+    const size_t need = align_up(lw) + sw + align_up((size_t)T * layer->H * 4);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_EWORKSPACE, "moe_layer_forward_shared: workspace needs " +
+                                        std::to_string(need) + " bytes");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+        return fail(MOE_EINVAL, "moe_layer_forward_shared: workspace must be 256-byte aligned");
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    uint8_t* wsh = w + align_up(lw);
+    if (layer_small_ok(li, T, k) && ls.count[MOE_FMT_BF16] == 1) {
+        int fmt = MOE_FMT_NVFP4;
+        while (!li.count[fmt]) ++fmt;
+        // the shared workspace as moe_shared_ffn lays it out: x16 | h16 | partials
+        uint16_t* sh_h16 = reinterpret_cast<uint16_t*>(wsh + align_up((size_t)T * shared->H * 2));
+        float* sh_part = reinterpret_cast<float*>(wsh + align_up((size_t)T * shared->H * 2) +
+                                                  align_up((size_t)T * shared->I * 2));
+        return launch_layer_small_shared(li.view, fmt, ls.view, x_bf16, logits, T, k, topk_ids,
+                                         topk_w, reinterpret_cast<uint16_t*>(w), sh_h16, sh_part,
+                                         out, stream);
+    }
+    float* y_sh = reinterpret_cast<float*>(wsh + sw);
+    st = moe_shared_ffn(shared, x_bf16, T, y_sh, wsh, sw, stream);
+    if (st) return st;
+    return moe_layer_forward(layer, x_bf16, logits, T, k, y_sh, topk_ids, topk_w, out, w, lw,
+                             stream);
+}
+
 int moe_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
     g_last_error.clear();
     if (!buf || !sink) return fail(MOE_EINVAL, "moe_probe_read: null pointer");

@@ -491,11 +491,16 @@ constexpr int kMinWaves = MOEQ_MIN_WAVES;
 // expert of rank j is its one "row", and h goes to row a (token order, no
 // permutation); one workgroup per token writes the token's ids and weights.
 // Single-format layers only (the record index of expert e is e).
-template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID, bool PART = false,
-          bool ROT = false, bool ROUTE = false>
-__global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
+// ADDOUT (down of a shared expert): y is added to A.out (the routed sum
+// already there) instead of being stored to A.y_perm.
+// The body is a device function of the workgroup's grid coordinates bid, so
+// that one launch can run it beside another kernel's workgroups.
+template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID, bool PART, bool ROT,
+          bool ROUTE, bool ADDOUT = false>
+__device__ __forceinline__ void ffn_body(const DecodeArgs& A, const uint3 bid) {
     static_assert(!ROT || (PART && PHASE == 0 && !ID), "rotated gate/up writes raw products");
     static_assert(!ROUTE || (PHASE == 0 && !ID && !PART && !ROT), "routed gate/up only");
+    static_assert(!ADDOUT || (PHASE == 1 && ID), "the down pass of a shared expert");
     constexpr bool XBF = PHASE == 0 && !ROT;        // B operand is bf16
     constexpr int NM = PHASE == 0 ? 2 * RPW : RPW;   // weight tiles per input tile
     constexpr int SETS = WV / KS;                    // row sets per workgroup
@@ -503,7 +508,7 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
     const int wave = threadIdx.x >> 6;
     ActiveExpert ae;
     if constexpr (ROUTE) {
-        const int a = blockIdx.y;
+        const int a = bid.y;
         const int t = a / A.k, j = a % A.k;
         float top_v[MOE_MAX_K];
         int top_i[MOE_MAX_K];
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
 #pragma unroll
         for (int jj = 1; jj < MOE_MAX_K; ++jj)
             if (jj == j) e = top_i[jj];
-        if (j == 0 && blockIdx.x == 0 && wave == 0 && lane == 0) {
+        if (j == 0 && bid.x == 0 && wave == 0 && lane == 0) {
             float w[MOE_MAX_K];
             topk_weights(top_v, A.k, w);
 #pragma unroll
@@ -524,11 +529,11 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
         }
         ae = ActiveExpert{e, a, 1, e};
     } else {
-        ae = ID ? ActiveExpert{blockIdx.y == 0 ? 0 : -1, 0, A.rows, 0}
-                : find_active_expert(A.offsets, A.rec, A.E, A.fmt, blockIdx.y, lane);
+        ae = ID ? ActiveExpert{bid.y == 0 ? 0 : -1, 0, A.rows, 0}
+                : find_active_expert(A.offsets, A.rec, A.E, A.fmt, bid.y, lane);
     }
     if (ae.e < 0) return;
-    const int c0 = blockIdx.z * 16 * NTT;
+    const int c0 = bid.z * 16 * NTT;
     if (c0 >= ae.me) return;
     const int ntt = min(NTT, (ae.me - c0 + 15) / 16);
     // VQ8: the codebooks of this kernel's projections into LDS (dynamic LDS:
@@ -546,8 +551,8 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
         __syncthreads();
     }
     const int kloc = wave % KS;                      // part of the workgroup's inputs
-    const int split = PART ? (int)blockIdx.x % A.nsplit : 0;
-    const int set = (PART ? (int)blockIdx.x / A.nsplit : (int)blockIdx.x) * SETS + wave / KS;
+    const int split = PART ? (int)bid.x % A.nsplit : 0;
+    const int set = (PART ? (int)bid.x / A.nsplit : (int)bid.x) * SETS + wave / KS;
     const int kpart = split * KS + kloc;             // first input tile of this wave
     const int kstride = PART ? KS * A.nsplit : KS;   // ... and the stride between its tiles
     const int K = PHASE == 0 ? A.H : A.I;
@@ -696,7 +701,16 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
                     f32x4 y = acc[q][tt];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) y[i] *= sd[i];
-                    *reinterpret_cast<f32x4*>(A.y_perm + (int64_t)(ae.r0 + c) * A.H + n0) = y;
+                    if constexpr (ADDOUT) {
+                        // the combine's last addition: out = routed sum + y
+                        float* op = A.out + (int64_t)(ae.r0 + c) * A.H + n0;
+                        const f32x4 o = *reinterpret_cast<const f32x4*>(op);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) y[i] = __fadd_rn(o[i], y[i]);
+                        *reinterpret_cast<f32x4*>(op) = y;
+                    } else {
+                        *reinterpret_cast<f32x4*>(A.y_perm + (int64_t)(ae.r0 + c) * A.H + n0) = y;
+                    }
                 }
             }
         }
@@ -704,11 +718,18 @@ __global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
 }
 
 
+template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID, bool PART = false,
+          bool ROT = false, bool ROUTE = false>
+__global__ __launch_bounds__(64 * WV, kMinWaves) void k_ffn(DecodeArgs A) {
+    ffn_body<F, NTT, KS, RPW, PHASE, WV, ID, PART, ROT, ROUTE>(
+        A, uint3{blockIdx.x, blockIdx.y, blockIdx.z});
+}
+
 // h[c, n..n+3] = silu(g) * u with g, u the sums over the nsplit partials in
 // ascending split order (one thread per 4 channels of a row).
-__global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ part, int nsplit,
-                                                      int rows, int I, _Float16* __restrict__ h16) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void swiglu_parts_body(const float* __restrict__ part, int nsplit,
+                                                  int rows, int I, _Float16* __restrict__ h16,
+                                                  const int64_t i) {
     const int nq = I / 4;
     if (i >= (int64_t)rows * nq) return;
     const int c = (int)(i / nq);
@@ -723,6 +744,11 @@ __global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ 
 #pragma unroll
     for (int q = 0; q < 4; ++q) h[q] = (_Float16)silu_mul(g[q], u[q]);
     *reinterpret_cast<f16x4*>(h16 + (int64_t)c * I + n) = h;
+}
+
+__global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ part, int nsplit,
+                                                      int rows, int I, _Float16* __restrict__ h16) {
+    swiglu_parts_body(part, nsplit, rows, I, h16, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 // Down projection and gated combine of the small-batch fused layer, for one
@@ -743,15 +769,15 @@ __global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ 
 constexpr int kDcKS = 4;     // waves splitting the input dimension of a slot group
 constexpr int kDcMaxK = 8;   // k of the fused path
 template <class F, int NSL, int NG>
-__global__ __launch_bounds__(64 * kDcKS * NG, kMinWaves) void k_down_combine(DecodeArgs A) {
+__device__ __forceinline__ void down_combine_body(const DecodeArgs& A, const uint3 bid) {
     constexpr int KS = kDcKS, NM = NSL, WV = KS * NG;
     static_assert(NSL * NG <= 16, "slots are B columns");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int kloc = wave % KS;
     const int sg = wave / KS;
-    const int t = blockIdx.y;
-    const int g = blockIdx.x;
+    const int t = bid.y;
+    const int g = bid.x;
     extern __shared__ _Float16 lds_cb[];
     if constexpr (F::kVq8) {
         constexpr int CHUNKS = F::CODES * MOE_VQ8_NCODE;
@@ -844,6 +870,11 @@ __global__ __launch_bounds__(64 * kDcKS * NG, kMinWaves) void k_down_combine(Dec
     *reinterpret_cast<f32x4*>(A.out + n) = o;
 }
 
+template <class F, int NSL, int NG>
+__global__ __launch_bounds__(64 * kDcKS * NG, kMinWaves) void k_down_combine(DecodeArgs A) {
+    down_combine_body<F, NSL, NG>(A, uint3{blockIdx.x, blockIdx.y, 0u});
+}
+
 template <class F>
 constexpr size_t codebook_lds_bytes(int phase) {
     if constexpr (F::kVq8)
@@ -915,6 +946,19 @@ int launch_fmt(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_
 #ifndef MOEQ_SH_PART
 #define MOEQ_SH_PART 1      // split the gate/up inputs over workgroups too
 #endif
+// Workgroups over the row-pair groups of a shared expert's gate/up pass
+// (nblk) and the number of workgroups splitting its inputs (nsplit).
+template <class F>
+void shared_gateup_split(const DecodeArgs& a, int& nblk, int& nsplit) {
+    constexpr int KS = MOEQ_SH_KS13, RPW = MOEQ_SH_RPW13, WV = MOEQ_SH_WV13, SETS = WV / KS;
+    const int nsets = (a.I / 16 + RPW - 1) / RPW;
+    nblk = (nsets + SETS - 1) / SETS;
+    const int nkb = (a.H + F::TK - 1) / F::TK;
+    nsplit = (kSharedTargetBlocks + nblk - 1) / nblk;
+    nsplit = nsplit < kSharedMaxSplit ? nsplit : kSharedMaxSplit;
+    nsplit = nsplit <= nkb / KS ? nsplit : (nkb / KS > 1 ? nkb / KS : 1);
+}
+
 template <class F, int NTT>
 int launch_shared_ntt(DecodeArgs a, int phase, hipStream_t s) {
     const int chunks = (a.rows + 16 * NTT - 1) / (16 * NTT);
@@ -923,10 +967,8 @@ int launch_shared_ntt(DecodeArgs a, int phase, hipStream_t s) {
         const int nsets = (a.I / 16 + RPW - 1) / RPW;
         const int nblk = (nsets + SETS - 1) / SETS;
         if constexpr (MOEQ_SH_PART) {
-            const int nkb = (a.H + F::TK - 1) / F::TK;
-            int nsplit = (kSharedTargetBlocks + nblk - 1) / nblk;
-            nsplit = nsplit < kSharedMaxSplit ? nsplit : kSharedMaxSplit;
-            nsplit = nsplit <= nkb / KS ? nsplit : (nkb / KS > 1 ? nkb / KS : 1);
+            int nblk_p = 0, nsplit = 1;
+            shared_gateup_split<F>(a, nblk_p, nsplit);
             a.nsplit = nsplit;
             dim3 grid((unsigned)(nblk * nsplit), 1u, (unsigned)chunks);
             k_ffn<F, NTT, KS, RPW, 0, WV, true, true>
@@ -1029,6 +1071,96 @@ int launch_small_fmt(const DecodeArgs& a, int64_t T, hipStream_t s) {
     return MOE_OK;
 }
 
+// The fused decode layer with a BF16 shared expert, in three launches:
+//   1. k_gateup_routed_shared: workgroups [0, nr) run the routed gate/up
+//      (ranking each token's experts itself) over grid gr, the rest the shared
+//      expert's gate/up partial sums over grid gs -- the same work as the two
+//      separate kernels, so one stream of weight bytes fills the chip;
+//   2. k_down_combine_swiglu: workgroups [0, nd) run the routed down + combine
+//      over grid gd (no shared term yet), the rest sum the shared partials and
+//      apply SwiGLU (one thread per 4 channels);
+//   3. k_shared_down_add: the shared expert's down pass, each output element
+//      added to the routed sum in out -- the combine's last addition.
+// Every value is computed by the same code, in the same order, as in the
+// separate kernels, so the output has the same bits.
+// (Shared experts: "GLM-5.3-EXL3-TR3-3.42bpw", What is quantized.)
+template <class F>
+__global__ __launch_bounds__(256, kMinWaves) void k_gateup_routed_shared(DecodeArgs R,
+                                                                          DecodeArgs S, int nr,
+                                                                          uint3 gr, uint3 gs) {
+    static_assert(64 * MOEQ_SH_WV13 == 256, "both halves run 256-thread workgroups");
+    unsigned b = blockIdx.x;
+    if (b < (unsigned)nr) {
+        ffn_body<F, 1, 4, kRpwGateup, 0, 4, false, false, false, true>(
+            R, uint3{b % gr.x, (b / gr.x) % gr.y, b / (gr.x * gr.y)});
+    } else {
+        b -= (unsigned)nr;
+        ffn_body<Bf16Fmt, 1, MOEQ_SH_KS13, MOEQ_SH_RPW13, 0, MOEQ_SH_WV13, true, true, false,
+                 false>(S, uint3{b % gs.x, (b / gs.x) % gs.y, b / (gs.x * gs.y)});
+    }
+}
+
+template <class F, int NSL, int NG>
+__global__ __launch_bounds__(64 * kDcKS * NG, kMinWaves) void k_down_combine_swiglu(
+    DecodeArgs R, int nd, unsigned gdx, const float* __restrict__ part, int nsplit, int rows,
+    int I, _Float16* __restrict__ h16) {
+    const unsigned b = blockIdx.x;
+    if (b < (unsigned)nd)
+        down_combine_body<F, NSL, NG>(R, uint3{b % gdx, b / gdx, 0u});
+    else
+        swiglu_parts_body(part, nsplit, rows, I, h16,
+                          (int64_t)(b - (unsigned)nd) * (64 * kDcKS * NG) + threadIdx.x);
+}
+
+__global__ __launch_bounds__(64 * MOEQ_SH_WV2, kMinWaves) void k_shared_down_add(DecodeArgs S) {
+    ffn_body<Bf16Fmt, 1, MOEQ_SH_KS2, MOEQ_SH_RPW2, 1, MOEQ_SH_WV2, true, false, false, false,
+             true>(S, uint3{blockIdx.x, blockIdx.y, blockIdx.z});
+}
+
+template <class F>
+int launch_small_shared_fmt(const DecodeArgs& a, DecodeArgs sa, int64_t T, hipStream_t s) {
+    // 1. routed gate/up (as launch_small_fmt) + shared gate/up partials (as
+    // launch_shared_ntt with NTT = 1: at most 16 tokens)
+    const int nsets = (a.I / 16 + kRpwGateup - 1) / kRpwGateup;
+    const uint3 gr{(unsigned)nsets, (unsigned)(T * a.k), 1u};
+    int nblk = 0, nsplit = 1;
+    shared_gateup_split<Bf16Fmt>(sa, nblk, nsplit);
+    sa.nsplit = nsplit;
+    const int chunks = (sa.rows + 15) / 16;
+    const uint3 gs{(unsigned)(nblk * nsplit), 1u, (unsigned)chunks};
+    const int nr = (int)(gr.x * gr.y);
+    const int ns = (int)(gs.x * gs.z);
+    k_gateup_routed_shared<F><<<(unsigned)(nr + ns), 256, codebook_lds_bytes<F>(0), s>>>(
+        a, sa, nr, gr, gs);
+    MOEQ_CHECK_LAUNCH();
+    // 2. routed down + combine (as launch_small_fmt) + the shared SwiGLU
+    const unsigned gdx = (unsigned)(a.H / 16);
+    const int nd = (int)(gdx * T);
+    const int64_t nsw = (int64_t)sa.rows * (sa.I / 4);
+    constexpr bool kWide = std::is_same<F, NvFmt>::value || F::kVq8;
+    if (a.k <= 4) {
+        const int nb = nd + (int)((nsw + 64 * kDcKS - 1) / (64 * kDcKS));
+        k_down_combine_swiglu<F, 4, 1><<<(unsigned)nb, 64 * kDcKS, codebook_lds_bytes<F>(1), s>>>(
+            a, nd, gdx, sa.part, nsplit, sa.rows, sa.I, sa.h16);
+    } else if constexpr (kWide) {
+        const int nb = nd + (int)((nsw + 64 * kDcKS - 1) / (64 * kDcKS));
+        k_down_combine_swiglu<F, 8, 1><<<(unsigned)nb, 64 * kDcKS, codebook_lds_bytes<F>(1), s>>>(
+            a, nd, gdx, sa.part, nsplit, sa.rows, sa.I, sa.h16);
+    } else {
+        const int nb = nd + (int)((nsw + 128 * kDcKS - 1) / (128 * kDcKS));
+        k_down_combine_swiglu<F, 4, 2><<<(unsigned)nb, 128 * kDcKS, codebook_lds_bytes<F>(1), s>>>(
+            a, nd, gdx, sa.part, nsplit, sa.rows, sa.I, sa.h16);
+    }
+    MOEQ_CHECK_LAUNCH();
+    // 3. shared down, added to out (as launch_shared_ntt's down pass, NTT = 1)
+    constexpr int SETS2 = MOEQ_SH_WV2 / MOEQ_SH_KS2;
+    const int nsets2 = (sa.H / 16 + MOEQ_SH_RPW2 - 1) / MOEQ_SH_RPW2;
+    dim3 g3((unsigned)((nsets2 + SETS2 - 1) / SETS2), 1u, (unsigned)chunks);
+    k_shared_down_add<<<g3, 64 * MOEQ_SH_WV2, 0, s>>>(sa);
+    MOEQ_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
 }  // namespace
 
 int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, const float* logits,
@@ -1051,6 +1183,31 @@ int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, cons
         return launch_small_fmt<Vq8Fmt<2>>(a, T, s);
     }
     return launch_small_fmt<VqFmt>(a, T, s);
+}
+
+int launch_layer_small_shared(const LayerView& L, int fmt, const LayerView& SL,
+                              const uint16_t* x_bf16, const float* logits, int64_t T, int32_t k,
+                              int32_t* topk_ids, float* topk_w, uint16_t* h16, uint16_t* sh_h16,
+                              float* sh_part, float* out, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (T == 0) return MOE_OK;
+    DecodeArgs a = decode_args(L, fmt, x_bf16, nullptr, nullptr, T, k, h16, nullptr);
+    a.logits = logits;
+    a.topk_ids = topk_ids;
+    a.topk_w = topk_w;
+    a.out = out;
+    DecodeArgs sa = decode_args(SL, MOE_FMT_BF16, x_bf16, nullptr, nullptr, T, 1, sh_h16, nullptr);
+    sa.part = sh_part;
+    sa.out = out;
+    if (fmt == MOE_FMT_NVFP4) return launch_small_shared_fmt<NvFmt>(a, sa, T, s);
+    if (fmt == MOE_FMT_NVFP4R) return launch_small_shared_fmt<Nv2Fmt>(a, sa, T, s);
+    if (fmt == MOE_FMT_BF16) return launch_small_shared_fmt<Bf16Fmt>(a, sa, T, s);
+    if (fmt == MOE_FMT_VQ8) {
+        if (L.vq8_m == 1) return launch_small_shared_fmt<Vq8Fmt<1>>(a, sa, T, s);
+        if (L.vq8_m == 3) return launch_small_shared_fmt<Vq8Fmt<3>>(a, sa, T, s);
+        return launch_small_shared_fmt<Vq8Fmt<2>>(a, sa, T, s);
+    }
+    return launch_small_shared_fmt<VqFmt>(a, sa, T, s);
 }
 
 int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_bf16,

@@ -155,6 +155,13 @@ constexpr int64_t kSmallFusedAssign = MOEQ_SMALL_ASSIGN;
 int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, const float* logits,
                        int64_t T, int32_t k, int32_t* topk_ids, float* topk_w, uint16_t* h16,
                        const float* y_shared, float* out, void* stream);
+// The same with a BF16 shared expert SL (E == 1, same H): out = routed sum +
+// the shared FFN; sh_h16 [T, SL.I] fp16 and sh_part (shared_part_bytes) are
+// its workspace.
+int launch_layer_small_shared(const LayerView& L, int fmt, const LayerView& SL,
+                              const uint16_t* x_bf16, const float* logits, int64_t T, int32_t k,
+                              int32_t* topk_ids, float* topk_w, uint16_t* h16, uint16_t* sh_h16,
+                              float* sh_part, float* out, void* stream);
 int launch_dequant(const LayerView& L, int fmt, int32_t rec_index, int32_t proj,
                    float* out, void* stream);
 int launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, void* stream);

@@ -424,6 +424,36 @@ int moe_layer_forward(const moe_qlayer* layer, const uint16_t* x_bf16, const flo
                       float* topk_w, float* out, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * moe_layer_forward_shared -- moe_shared_ffn followed by moe_layer_forward
+ * with its output as y_shared, in one call: out = (the routed layer's gated
+ * sum) + the shared expert's FFN of every token.
+ * (Shared experts beside the routed ones: "GLM-5.3-EXL3-TR3-3.42bpw", What
+ * is quantized.)
+ *
+ *   layer, x_bf16, logits, k, topk_ids, topk_w, out  as for moe_layer_forward.
+ *   shared     a one-expert layer (E == 1, unrotated) with the routed layer's
+ *              H, as for moe_shared_ffn.
+ *   workspace  [device] >= moe_layer_forward_shared_workspace_bytes(layer,
+ *              shared, T, k) bytes, 256-byte aligned; contents on return
+ *              unspecified.
+ *
+ * When moe_layer_forward would take its fused path and the shared expert is
+ * BF16, the layer runs in three launches: the routed and the shared gate/up
+ * passes in one, the routed down + combine beside the shared SwiGLU in the
+ * next, then the shared down pass, which adds each of its outputs to the
+ * routed sum (the combine's last addition).  The results are the bits of
+ * moe_shared_ffn + moe_layer_forward on the same inputs.  Otherwise it runs
+ * those two calls.  Errors as for them (checked before any launch), and
+ * MOE_EINVAL if the shared layer's H differs from the routed layer's.
+ */
+size_t moe_layer_forward_shared_workspace_bytes(const moe_qlayer* layer,
+                                                const moe_qlayer* shared, int64_t T, int32_t k);
+int moe_layer_forward_shared(const moe_qlayer* layer, const moe_qlayer* shared,
+                             const uint16_t* x_bf16, const float* logits, int64_t T, int32_t k,
+                             int32_t* topk_ids, float* topk_w, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------- host-side packers */
 
 /*

@@ -581,3 +581,40 @@ def test_rotated_layer_host_checks():
     one.rot_signs = 0x2000
     assert L.moe_shared_ffn(ctypes.byref(one), fake, 4, fake, fake, 1 << 24,
                             N) == moeq.MOE_EUNSUPPORTED
+
+
+def test_layer_forward_shared_host_checks():
+    """moe_layer_forward_shared rejects on the host, before any launch: a
+    shared layer with E != 1 or another H, a short workspace; T = 0 is a no-op."""
+    import ctypes
+    L = moeq.lib()
+    E, H, I = 8, 256, 128
+    fmt = (ctypes.c_uint8 * E)(*([1] * E))
+    rec = ctypes.c_void_p(16)            # never dereferenced on the host
+    lay = moeq._QLayerC()
+    lay.E, lay.H, lay.I = E, H, I
+    lay.fmt_host = ctypes.cast(fmt, ctypes.c_void_p)
+    lay.rec_dev = rec
+    lay.nvfp4_w13 = lay.nvfp4_w2 = ctypes.c_void_p(256)
+    lay.nvfp4_w13_stride = L.moe_record_bytes(1, 0, H, I)
+    lay.nvfp4_w2_stride = L.moe_record_bytes(1, 1, H, I)
+    sfmt = (ctypes.c_uint8 * 2)(4, 4)   # two tags, so that E = 2 below reads valid memory
+    sh = moeq._QLayerC()
+    sh.E, sh.H, sh.I = 1, H, I
+    sh.fmt_host = ctypes.cast(sfmt, ctypes.c_void_p)
+    sh.rec_dev = rec
+    sh.bf16_w13 = sh.bf16_w2 = ctypes.c_void_p(256)
+    sh.bf16_w13_stride = L.moe_record_bytes(4, 0, H, I)
+    sh.bf16_w2_stride = L.moe_record_bytes(4, 1, H, I)
+    p = ctypes.c_void_p(256)
+    need = L.moe_layer_forward_shared_workspace_bytes(ctypes.byref(lay), ctypes.byref(sh), 2, 2)
+    assert need >= L.moe_layer_forward_workspace_bytes(ctypes.byref(lay), 2, 2) + 2 * H * 4
+    call = lambda s, T, ws_bytes: L.moe_layer_forward_shared(
+        ctypes.byref(lay), ctypes.byref(s), p, p, T, 2, p, p, p, p, ws_bytes, None)
+    assert call(sh, 0, 0) == moeq.MOE_OK
+    assert call(sh, 2, need - 1) == moeq.MOE_EWORKSPACE
+    sh.H = 512
+    assert call(sh, 2, need) == moeq.MOE_EINVAL
+    sh.H = H
+    sh.E = 2
+    assert call(sh, 2, need) == moeq.MOE_EINVAL

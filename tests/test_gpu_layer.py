@@ -183,3 +183,108 @@ def test_layer_forward_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(ids, want[0]) and torch.equal(w, want[1]), rep
         assert torch.equal(out, want[2]), rep
+
+
+# moe_layer_forward_shared: fused three-launch form for decode batches with a
+# BF16 shared expert; every other case runs moe_shared_ffn + moe_layer_forward
+SHARED_CASES = {
+    # fused: one and two tokens of top-8 (8 slots per wave), top-4 over
+    # ragged H / I (4 slots per wave), small-codebook VQ routed experts
+    # (codebooks in LDS beside the shared pass), BF16 routed experts at k = 6
+    # (two slot groups per down workgroup: 512-thread SwiGLU blocks)
+    "sf_nv_t1": (synth.small_workload("lfs_nv", E=32, k=8, H=384, I=256, T=2, cfg=196,
+                                      shared=True), 1),
+    "sf_nv_t2": (synth.small_workload("lfs_nv", E=32, k=8, H=384, I=256, T=2, cfg=196,
+                                      shared=True), 2),
+    "sf_nv_k4": (synth.small_workload("lfs_k4", E=16, k=4, H=272, I=80, T=4, cfg=197,
+                                      shared=True), 4),
+    "sf_vq8": (synth.small_workload("lfs_vq8", E=12, k=3, H=512, I=144, T=5, fmt="vq8",
+                                    cfg=198, vq8_m=2, shared=True), 5),
+    "sf_bf16_k6": (synth.small_workload("lfs_bf16", E=16, k=6, H=272, I=80, T=2, fmt="bf16",
+                                        cfg=199, shared=True), 2),
+    # not fused: 18 assignments; a rotated routed layer
+    "sf_t9": (synth.small_workload("lfs_t9", E=8, k=2, H=256, I=128, T=9, cfg=179,
+                                   shared=True), 9),
+    "sf_rot": (synth.small_workload("lfs_rot", E=16, k=4, H=384, I=256, T=1, cfg=178, rot=True,
+                                    shared=True), 1),
+}
+
+
+def two_calls(lay, sh, x, lgd, k):
+    y_sh = moeq.shared_ffn(sh, x)
+    return moeq.layer_forward(lay, x, lgd, k, y_shared=y_sh)
+
+
+@pytest.mark.parametrize("name", list(SHARED_CASES))
+def test_layer_forward_shared_parity(name):
+    wl, T = SHARED_CASES[name]
+    say("layer forward with shared layer", name, T)
+    lay = layer_for(wl)
+    sh = build_shared_layer(wl, DEV)
+    x_bits, lg, x, lgd = inputs(wl, T)
+    ids, w, out = moeq.layer_forward(lay, x, lgd, wl.k, shared=sh)
+    ref_out, ref_ids, _, _ = oracle_out(wl, x_bits, lg, shared=shared_weights(wl))
+    assert np.array_equal(to_np(ids), ref_ids)
+    assert_rows_close(to_np(out), ref_out, name + " out")
+    ids2, w2, out2 = two_calls(lay, sh, x, lgd, wl.k)
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+    assert torch.equal(out, out2), name
+
+
+def test_layer_forward_shared_other_format_falls_back():
+    """A shared expert in NVFP4 takes the two calls (same bits)."""
+    from bit_quantized_moe_route_amd.layers import build_layer
+    wl, T = SHARED_CASES["sf_nv_t1"]
+    say("layer forward with an NVFP4 shared layer")
+    lay = layer_for(wl)
+    sh = build_layer(1, wl.H, wl.I, np.array([moeq.FMT_NVFP4], np.uint8),
+                     nvfp4_weights=lambda e, p: (synth.shared_weights_bf16(wl, p).astype(
+                         np.uint32) << 16).view(np.float32), device=DEV, workers=1)
+    _, _, x, lgd = inputs(wl, T)
+    a = moeq.layer_forward(lay, x, lgd, wl.k, shared=sh)
+    b = two_calls(lay, sh, x, lgd, wl.k)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_layer_forward_shared_graph_replays():
+    """The three-launch form captured in a HIP graph: every replay (new inputs
+    copied into the captured buffers, eager work between replays) equals the
+    eager call on the same inputs."""
+    wl, T = SHARED_CASES["sf_nv_t2"]
+    say("layer forward with shared layer, graph")
+    lay = layer_for(wl)
+    sh = build_shared_layer(wl, DEV)
+    _, _, x0, lg0 = inputs(wl, T, rep=0)
+    x = x0.clone()
+    lg = lg0.clone()
+    ws = moeq.layer_workspace(lay, T, wl.k, shared=sh)
+    ids = torch.empty((T, wl.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, wl.k), dtype=torch.float32, device=DEV)
+    out = torch.empty((T, wl.H), dtype=torch.float32, device=DEV)
+    moeq.layer_forward(lay, x, lg, wl.k, out=out, ids=ids, w=w, ws=ws, shared=sh)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moeq.layer_forward(lay, x, lg, wl.k, out=out, ids=ids, w=w, ws=ws, shared=sh)
+    for rep in (1, 2, 1, 3):
+        _, _, xr, lgr = inputs(wl, T, rep=rep)
+        want = moeq.layer_forward(lay, xr, lgr, wl.k, shared=sh)
+        torch.cuda.synchronize()
+        x.copy_(xr)
+        lg.copy_(lgr)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ids, want[0]) and torch.equal(w, want[1]), rep
+        assert torch.equal(out, want[2]), rep
+
+
+def test_layer_forward_shared_t_zero():
+    wl, _ = SHARED_CASES["sf_nv_t1"]
+    say("layer forward with shared layer, T = 0")
+    lay = layer_for(wl)
+    sh = build_shared_layer(wl, DEV)
+    x = torch.empty((0, wl.H), dtype=torch.int16, device=DEV)
+    lg = torch.empty((0, wl.E), dtype=torch.float32, device=DEV)
+    ids, w, out = moeq.layer_forward(lay, x, lg, wl.k, shared=sh)
+    assert out.shape == (0, wl.H) and ids.shape == (0, wl.k)
