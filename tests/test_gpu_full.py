@@ -298,6 +298,37 @@ def shared_layer(wl):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [1, 2])
+def test_layer_forward_shared_full(T):
+    """The whole decode layer with its BF16 shared expert in one call
+    (moe_layer_forward_shared: three launches at these sizes), as the
+    benchmark times it: the bits of moe_shared_ffn + moe_layer_forward on the
+    same batch, routing against the oracle, and the shared output of token 0
+    against the oracle's shared FFN (out minus the fixed-order routed sum)."""
+    from tests.oracle_runs import shared_weights
+    wl = synth.DECODE_SHARED
+    say("layer_forward_shared full", T)
+    lay = layer("decode")
+    sh = shared_layer(wl)
+    x_bits = synth.activations(wl, T, rep=5)
+    lg = synth.logits(wl, T, rep=5)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(DEV)
+    lgd = torch.from_numpy(lg).to(DEV)
+    ids, w, out = moeq.layer_forward(lay, x, lgd, wl.k, shared=sh)
+    y_sh = moeq.shared_ffn(sh, x)
+    ids2, w2, out2 = moeq.layer_forward(lay, x, lgd, wl.k, y_shared=y_sh)
+    routed = moeq.layer_forward(lay, x, lgd, wl.k)[2]
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w, w2) and torch.equal(out, out2)
+    ref_ids, _ = oracle.route_topk(lg, wl.k)
+    assert np.array_equal(to_np(ids), ref_ids)
+    # out - routed sum is y_shared rounded once more: compare y_shared itself
+    ref = oracle.expert_ffn(x_bits[:1], *shared_weights(wl))
+    assert_rows_close(to_np(y_sh)[:1], ref, "shared FFN of token 0")
+    assert torch.equal(out, routed + y_sh)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,T", [("decode_shared", 1), ("decode_shared", 32),
                                     ("prefill_shared", 4096)])
 def test_shared_expert_full(name, T):
