@@ -17,6 +17,9 @@
  *   moe_combine_shared  y_perm, inv_perm, topk_w,
  *                       y_shared                   -> out [T, H]
  *
+ * (moe_layer_forward_shared runs the routed layer and its shared expert in
+ * one call).
+ *
  * Passages these calls follow (titles and sections of the source pages):
  *   - 256 routed experts per MoE layer, 8 active per token:
  *     "GLM-5-NVFP4-MTP", Model Description.
