@@ -149,10 +149,14 @@ size_t ffn_ws(const moe_qlayer* L, int64_t T, int32_t k) {
     return gateup_ws(L, T, k) + align_up((size_t)T * k * L->I * 2);
 }
 
-// moe_shared_ffn: x16 | h16 | the gate/up partial sums of the decode path.
+// moe_shared_ffn: x16 | h16 | the gate/up partial sums of the decode path
+// (sized for the split that path takes; none where the grouped GEMM runs).
+// The format is the one expert's tag (an unreadable or unknown tag sizes for
+// the largest split; the call itself then fails its layer checks).
 size_t shared_ws(const moe_qlayer* L, int64_t T) {
+    const int fmt = L->fmt_host ? L->fmt_host[0] : 0;
     return align_up((size_t)T * L->H * 2) + align_up((size_t)T * L->I * 2) +
-           align_up(shared_part_bytes(T, L->I));
+           align_up(shared_part_bytes(fmt, T, L->H, L->I));
 }
 
 // moe_layer_forward: the small-batch fused path needs only h [T*k, I] fp16;

@@ -947,16 +947,21 @@ int launch_fmt(const DecodeArgs& a, int slots, int chunks, int phase, hipStream_
 #define MOEQ_SH_PART 1      // split the gate/up inputs over workgroups too
 #endif
 // Workgroups over the row-pair groups of a shared expert's gate/up pass
-// (nblk) and the number of workgroups splitting its inputs (nsplit).
-template <class F>
-void shared_gateup_split(const DecodeArgs& a, int& nblk, int& nsplit) {
+// (nblk) and the number of workgroups splitting its inputs (nsplit), for
+// input tiles of tk inputs.
+void shared_split(int H, int I, int tk, int& nblk, int& nsplit) {
     constexpr int KS = MOEQ_SH_KS13, RPW = MOEQ_SH_RPW13, WV = MOEQ_SH_WV13, SETS = WV / KS;
-    const int nsets = (a.I / 16 + RPW - 1) / RPW;
+    const int nsets = (I / 16 + RPW - 1) / RPW;
     nblk = (nsets + SETS - 1) / SETS;
-    const int nkb = (a.H + F::TK - 1) / F::TK;
+    const int nkb = (H + tk - 1) / tk;
     nsplit = (kSharedTargetBlocks + nblk - 1) / nblk;
     nsplit = nsplit < kSharedMaxSplit ? nsplit : kSharedMaxSplit;
     nsplit = nsplit <= nkb / KS ? nsplit : (nkb / KS > 1 ? nkb / KS : 1);
+}
+
+template <class F>
+void shared_gateup_split(const DecodeArgs& a, int& nblk, int& nsplit) {
+    shared_split(a.H, a.I, F::TK, nblk, nsplit);
 }
 
 template <class F, int NTT>
@@ -1005,8 +1010,9 @@ int launch_shared_fmt(const DecodeArgs& a, int phase, hipStream_t s) {
 
 template <class F>
 int launch_ntt(const DecodeArgs& a, int64_t T, int slots, int phase, hipStream_t s) {
-    // an expert has at most T rows (the k experts of a token are distinct)
-    // tokens of an expert go 16 at a time to the z dimension of the grid
+    // an expert has at most T rows (the k experts of a token are distinct:
+    // a documented precondition of the ABI); tokens of an expert go 16 at a
+    // time to the z dimension of the grid
     const int chunks = (int)((T + 15) / 16);
     return launch_fmt<F, 1>(a, slots, chunks, phase, s);
 }
@@ -1233,6 +1239,18 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
 }  // namespace moeq
 
 namespace moeq {
+
+size_t shared_part_bytes(int fmt, int64_t T, int32_t H, int32_t I) {
+    if (T <= 0 || H <= 0 || I <= 0) return 0;
+    if (T >= kPrefillMinTokens && prefill_fmt(fmt, true)) return 0;   // the grouped GEMM
+    if (!MOEQ_SH_PART) return 0;
+    const bool known = fmt >= MOE_FMT_NVFP4 && fmt <= MOE_FMT_MAX;
+    // input tile of the format (an unknown tag: the smaller tile, the larger split)
+    const int tk = known && (fmt == MOE_FMT_VQ || fmt == MOE_FMT_VQ8) ? kVqTileK : kNvTileK;
+    int nblk = 0, nsplit = 1;
+    shared_split(H, I, tk, nblk, nsplit);
+    return (size_t)nsplit * (size_t)T * 2 * (size_t)I * 4;
+}
 
 int launch_shared_decode(const LayerView& L, int fmt, const uint16_t* x_bf16, int64_t T,
                          uint16_t* h16, float* part, float* y, int phase, void* stream) {

@@ -119,9 +119,10 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
 #endif
 constexpr int kSharedMaxSplit = 16;                  // workgroups splitting the gate/up inputs
 constexpr int kSharedTargetBlocks = MOEQ_SH_TARGET;  // gate/up workgroups aimed for
-inline size_t shared_part_bytes(int64_t T, int32_t I) {
-    return (size_t)kSharedMaxSplit * (size_t)T * 2 * (size_t)I * 4;
-}
+// Bytes of the fp32 partial sums the decode path of a one-expert layer of
+// format fmt writes for T tokens: nsplit x T x 2I x 4 with the split that
+// launch_shared_decode takes; 0 where the grouped GEMM runs instead.
+size_t shared_part_bytes(int fmt, int64_t T, int32_t H, int32_t I);
 int launch_shared_decode(const LayerView& L, int fmt, const uint16_t* x_bf16, int64_t T,
                          uint16_t* h16, float* part, float* y, int phase, void* stream);
 // Experts at T >= kPrefillMinTokens use the grouped-GEMM kernels, every

@@ -252,6 +252,22 @@ size_t moe_record_bytes_vq8(int which, int32_t H, int32_t I, int32_t m) {
     return (size_t)vq8_rec_bytes(which, H, I, m);
 }
 
+// E4M3FN has no infinities; S.1111.111 is its only NaN (0x7F, 0xFF).
+static bool e4m3_is_nan(uint8_t b) { return (b & 0x7F) == 0x7F; }
+// fp16 exponent field all ones: an infinity or a NaN.
+static bool f16_not_finite(uint16_t b) { return (b & 0x7C00) == 0x7C00; }
+
+static bool any_e4m3_nan(const uint8_t* s, int64_t n) {
+    for (int64_t i = 0; i < n; ++i)
+        if (e4m3_is_nan(s[i])) return true;
+    return false;
+}
+static bool any_f16_not_finite(const uint16_t* s, int64_t n) {
+    for (int64_t i = 0; i < n; ++i)
+        if (f16_not_finite(s[i])) return true;
+    return false;
+}
+
 int moe_pack_nvfp4_expert(const uint8_t* gc, const uint8_t* gs, const uint8_t* uc,
                           const uint8_t* us, const uint8_t* dc, const uint8_t* ds, int32_t H,
                           int32_t I, uint8_t* w13, uint8_t* w2) {
@@ -259,6 +275,9 @@ int moe_pack_nvfp4_expert(const uint8_t* gc, const uint8_t* gs, const uint8_t* u
         return fail(MOE_EINVAL, "moe_pack_nvfp4_expert: null pointer");
     if (H <= 0 || I <= 0 || H % 16 || I % 16)
         return fail(MOE_EUNSUPPORTED, "moe_pack_nvfp4_expert: H and I must be positive multiples of 16");
+    const int64_t ns = (int64_t)I * (H / 16);   // scale bytes per gate/up/down matrix
+    if (any_e4m3_nan(gs, ns) || any_e4m3_nan(us, ns) || any_e4m3_nan(ds, ns))
+        return fail(MOE_EINVAL, "moe_pack_nvfp4_expert: a block scale is the E4M3 NaN byte");
     std::memset(w13, 0, (size_t)nv_rec_bytes(0, H, I));
     std::memset(w2, 0, (size_t)nv_rec_bytes(1, H, I));
     nv_tiles(gc, gs, I, H, 2, 0, w13);
@@ -286,6 +305,8 @@ int moe_pack_vq_expert(const uint16_t* gc, const uint16_t* gs, const uint16_t* u
         return fail(MOE_EINVAL, "moe_pack_vq_expert: null pointer");
     if (H <= 0 || I <= 0 || H % 16 || I % 16)
         return fail(MOE_EUNSUPPORTED, "moe_pack_vq_expert: H and I must be positive multiples of 16");
+    if (any_f16_not_finite(gs, I) || any_f16_not_finite(us, I) || any_f16_not_finite(ds, H))
+        return fail(MOE_EINVAL, "moe_pack_vq_expert: a per-row scale is not finite");
     std::memset(w13, 0, (size_t)vq_rec_bytes(0, H, I));
     std::memset(w2, 0, (size_t)vq_rec_bytes(1, H, I));
     vq_tiles(gc, I, H, 2, 0, w13);
@@ -307,6 +328,8 @@ int moe_pack_vq8_expert(const uint8_t* gc, const uint16_t* gs, const uint8_t* uc
         return fail(MOE_EUNSUPPORTED, "moe_pack_vq8_expert: H and I must be positive multiples of 16");
     if (m < 1 || m > MOE_VQ8_MAX_M)
         return fail(MOE_EUNSUPPORTED, "moe_pack_vq8_expert: m must be 1, 2 or 3");
+    if (any_f16_not_finite(gs, I) || any_f16_not_finite(us, I) || any_f16_not_finite(ds, H))
+        return fail(MOE_EINVAL, "moe_pack_vq8_expert: a per-row scale is not finite");
     std::memset(w13, 0, (size_t)vq8_rec_bytes(0, H, I, m));
     std::memset(w2, 0, (size_t)vq8_rec_bytes(1, H, I, m));
     vq8_tiles(gc, I, H, m, 2, 0, w13);

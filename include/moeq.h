@@ -63,11 +63,14 @@
  *   - T == 0 is valid for every device call; moe_permute then writes
  *     counts = 0 and offsets = 0, the other calls launch nothing.
  *   - Device-side preconditions that cannot be checked without reading device
- *     memory (logits not NaN; topk_ids in [0, E); perm_src/offsets produced by
+ *     memory (logits not NaN; topk_ids in [0, E) and the k ids of a token
+ *     distinct, as moe_route_topk writes them; perm_src/offsets produced by
  *     moe_permute for the same topk_ids; the per-expert record table agreeing
  *     with the host tier map) are the caller's; violating them gives
  *     unspecified results but no out-of-bounds access beyond the buffers'
- *     stated sizes for ids in range.
+ *     stated sizes for ids in range.  (With a token naming one expert twice,
+ *     that expert can hold more than T rows; the decode-size FFN kernels,
+ *     T < 128, compute the first T of them only.)
  */
 #ifndef MOEQ_H
 #define MOEQ_H
@@ -246,7 +249,14 @@ size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E);
 
 /*
  * moe_permute -- group the T*k assignments by expert (a stable counting sort).
- *   Assignment a = t*k + j goes to expert e_a = topk_ids[a].
+ *   (The pages' serving stacks run the routed experts through grouped MoE
+ *   runners, which gather each expert's tokens into one contiguous group
+ *   before its expert GEMMs: "GLM-5.3-Flash-TR3-8bpw (K8)", Serving --
+ *   live-qualified turnkey profile (a Triton MoE runner behind an all-to-all);
+ *   "GLM-5-NVFP4-MTP", How to Run (a CUTLASS MoE runner backend).)
+ *   Assignment a = t*k + j goes to expert e_a = topk_ids[a].  moe_permute
+ *   itself takes any ids in [0, E); the FFN calls that use its output need a
+ *   token's k ids distinct (see Conventions).
  *   counts   [device] int32 [E] out: number of assignments per expert.
  *   offsets  [device] int32 [E+1] out: exclusive prefix sum of counts,
  *            offsets[E] = T*k.
@@ -297,7 +307,8 @@ size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k);
  *
  *   x        [device] bf16 [T, H] as uint16 bits, token order.
  *   perm_src [device] int32 [T*k], offsets [device] int32 [E+1]: from
- *            moe_permute.
+ *            moe_permute, for ids with a token's k experts distinct (so no
+ *            expert holds more than T rows).
  *   y_perm   [device] fp32 [T*k, H] out.
  *   ws       [device] >= moe_ffn_workspace_bytes() bytes, 256-byte aligned.
  *
@@ -503,8 +514,16 @@ size_t moe_record_bytes_vq8(int which, int32_t H, int32_t I, int32_t m);
 /*
  * moe_pack_nvfp4_expert -- [host] lay the canonical NVFP4 bytes of one
  * expert out as its two device records (gate/up and down).
+ *   ("GLM-5-NVFP4-MTP", Model Description: 4-bit E2M1 codes with an E4M3
+ *   scale per 16 elements; "GLM-5.3 Vision NestQuant 1.75-4 bit", Contents:
+ *   one record per expert, addressed by expert id at a fixed stride.)
  *   gate/up codes [I, H/2], scales [I, H/16]; down codes [H, I/2],
- *   scales [H, I/16]; w13_rec / w2_rec [host] out, moe_record_bytes() each.
+ *   scales [H, I/16] ([host], canonical layout as moe_quantize_nvfp4 writes
+ *   it); w13_rec / w2_rec [host] out, moe_record_bytes() each (the caller
+ *   uploads them).  MOE_EINVAL on a null pointer or a scale byte that is the
+ *   E4M3 NaN (0x7F or 0xFF: E4M3FN has no infinities); MOE_EUNSUPPORTED if
+ *   H or I is not a positive multiple of 16.  Nothing else is checked: every
+ *   other code and scale byte is a finite value.
  */
 int moe_pack_nvfp4_expert(const uint8_t* gate_codes, const uint8_t* gate_scales,
                           const uint8_t* up_codes, const uint8_t* up_scales,
@@ -517,7 +536,8 @@ int moe_pack_nvfp4_expert(const uint8_t* gate_codes, const uint8_t* gate_scales,
  * the residual plane's (from res_parts).  base_parts / res_parts: the six
  * arrays moe_pack_nvfp4_expert takes, in its order (gate codes, gate scales,
  * up codes, up scales, down codes, down scales).  w13_rec / w2_rec [host]
- * out, moe_record_bytes(MOE_FMT_NVFP4R, ...) each.
+ * out, moe_record_bytes(MOE_FMT_NVFP4R, ...) each.  Errors as
+ * moe_pack_nvfp4_expert (an E4M3 NaN scale byte in either plane: MOE_EINVAL).
  */
 int moe_pack_nvfp4r_expert(const uint8_t* const base_parts[6], const uint8_t* const res_parts[6],
                            int32_t H, int32_t I, uint8_t* w13_rec, uint8_t* w2_rec);
@@ -527,6 +547,8 @@ int moe_pack_nvfp4r_expert(const uint8_t* const base_parts[6], const uint8_t* co
  *   codes uint16 [n, kin/8] (group g covers inputs 8g..8g+7), scales fp16
  *   bits [n], for gate/up (n = I, kin = H) and down (n = H, kin = I).
  *   ("GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw", What it is.)
+ *   MOE_EINVAL on a null pointer or a scale that is not finite (fp16 inf or
+ *   NaN); MOE_EUNSUPPORTED if H or I is not a positive multiple of 16.
  */
 int moe_pack_vq_expert(const uint16_t* gate_codes, const uint16_t* gate_scales,
                        const uint16_t* up_codes, const uint16_t* up_scales,
@@ -538,8 +560,11 @@ int moe_pack_vq_expert(const uint16_t* gate_codes, const uint16_t* gate_scales,
  * records.  codes uint8 [n, kin/8, m] (code j of group g indexes codebook
  * j; group g covers inputs 8g..8g+7), scales fp16 bits [n], for gate/up
  * (n = I, kin = H) and down (n = H, kin = I); m = 1, 2 or 3.
- *   ("GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw", What it is: 1/2/3-bit
- *   modules with per-group codes and shared codebooks.)
+ *   ("GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw", What it is: modules of 1, 2
+ *   and 3 bits per weight, each indexing codebooks shared by the experts.)
+ *   MOE_EINVAL on a null pointer or a scale that is not finite;
+ *   MOE_EUNSUPPORTED for H or I not a positive multiple of 16 or m outside
+ *   1..3.
  */
 int moe_pack_vq8_expert(const uint8_t* gate_codes, const uint16_t* gate_scales,
                         const uint8_t* up_codes, const uint16_t* up_scales,
@@ -597,7 +622,13 @@ int moe_record_table_resident(const uint8_t* fmt_host, int32_t E, int32_t* rec);
 /*
  * moe_dequant_q -- decode projection `proj` (MOE_PROJ_*) of expert `expert`
  * to fp32 out [n, kin] ([device]; gate/up: [I, H], down: [H, I]) with the
- * same device decode routines the FFN kernels use.  NVFP4 and VQ values are
+ * same device decode routines the FFN kernels use.
+ *   (The weight values the formats define: an E2M1 code times its E4M3 block
+ *   scale, "GLM-5-NVFP4-MTP", Model Description; a codebook row times the
+ *   row's scale, "GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw", What it is.)
+ *   A test hook: it lets the stored bytes be compared with the oracle's
+ *   decode without running an FFN.  Errors as moe_expert_ffn_q's layer checks,
+ *   MOE_EINVAL for an expert outside [0, E), a bad proj or a NULL out.  NVFP4 and VQ values are
  * exact; a MOE_FMT_VQ8 value with m >= 2 is fp32(fp32(C_0 + .. + C_{m-1}) * S) (fp32
  * sums; the FFN kernels multiply each codebook row exactly instead); a
  * MOE_FMT_BF16 value is the stored weight as the kernels' fp16 operand; a

@@ -31,7 +31,8 @@ Parity status per function (what pins each one is in tests/test_oracle_*.py):
   e2m1_decode, e4m3_decode, e4m3_encode, nvfp4_quantize, nvfp4_dequant,
   vq_dequant, vq8_dequant, route_topk, permute, expert_ffn, combine,
   combine_shared, forward, hadamard, rotate, unrotate, rotate_weights,
-  unrotate_weights, nvfp4_residual_quantize, nvfp4r_dequant
+  unrotate_weights, nvfp4_residual_quantize, nvfp4r_dequant,
+  bf16_bits_to_f64, f16_bits_to_f64
   -- all pinned.  vq8_dequant's arithmetic is pinned; its code shape (M
   8-bit codes per 8-weight group into M 256-entry codebooks whose rows are
   summed) is a reading the pages do not fix: parity unpinned for the shape.

@@ -19,13 +19,14 @@ per-group codes into a shared codebook) is read as: groups of 8 consecutive
 input weights, one uint16 code per group indexing a 65536 x 8 fp16 codebook,
 and one fp16 scale per output channel: W[o, 8g+j] = S[o] * C[code[o, g], j].
 
-The small-codebook VQ modules (the same page: 1-, 2- and 3-bit modules,
-"per-group codes + shared codebook") are read as groups of 8 input weights
-with M = 1 or 2 uint8 codes each, code m indexing a 256 x 8 fp16 codebook
-C_m shared by the layer's experts, the rows summed (additive codebooks, as
-in AQLM): W[o, 8g+j] = S[o] * sum_m C_m[code[o, g, m], j].  M = 1 is 1 bit
-per weight, M = 2 is 2 bits per weight.  The pages do not give these code
-shapes; they are this reading's.
+The small-codebook VQ modules (the same page and section: the build mixes
+modules of 1, 2 and 3 bits per weight, each coded as per-group indices into a
+codebook that the experts share) are read as groups of 8 input weights with
+M = 1, 2 or 3 uint8 codes each, code m indexing a 256 x 8 fp16 codebook C_m
+shared by the layer's experts, the rows summed (additive codebooks, as in
+AQLM): W[o, 8g+j] = S[o] * sum_m C_m[code[o, g, m], j].  M codes per group
+are M bits per weight.  The pages do not give these code shapes; they are
+this reading's.
 """
 
 import numpy as np

@@ -174,13 +174,19 @@ def test_nvfp4_record_layout(H, I):
     assert np.all(w13[~used] == 0)
 
 
+def _finite_f16_bits(rs, n):
+    """n random fp16 bit patterns of finite values (any sign, exponent field
+    below all-ones)."""
+    return (rs.integers(0, 0x7C00, n) | (rs.integers(0, 2, n) << 15)).astype(np.uint16)
+
+
 def test_vq_record_layout():
     H, I = 272, 48
     rs = np.random.default_rng(0)
     parts = []
     for n, kin in [(I, H), (I, H), (H, I)]:
         parts.append((rs.integers(0, 65536, (n, kin // 8), dtype=np.uint16),
-                      rs.integers(0, 65536, n, dtype=np.uint16)))
+                      _finite_f16_bits(rs, n)))
     w13, w2 = moeq.pack_vq_expert(parts[0], parts[1], parts[2], H, I)
     for (codes, scales), rec, rg_step, rg_off, nrg in [(parts[0], w13, 2, 0, 2 * I // 16),
                                                        (parts[1], w13, 2, 1, 2 * I // 16),
@@ -211,7 +217,7 @@ def test_vq8_record_layout(m):
     parts = []
     for n, kin in [(I, H), (I, H), (H, I)]:
         parts.append((rs.integers(0, 256, (n, kin // 8, m), dtype=np.uint8),
-                      rs.integers(0, 65536, n, dtype=np.uint16)))
+                      _finite_f16_bits(rs, n)))
     w13, w2 = moeq.pack_vq8_expert(parts[0], parts[1], parts[2], H, I, m)
     assert w13.size == moeq.record_bytes(moeq.FMT_VQ8, 0, H, I, m) and w13.size % 256 == 0
     tb = 512 * m
@@ -618,3 +624,107 @@ def test_layer_forward_shared_host_checks():
     sh.H = H
     sh.E = 2
     assert call(sh, 2, need) == moeq.MOE_EINVAL
+
+
+# ------------------------------------------------- packer input validation
+
+def _nv_mats(H, I, seed):
+    rs = np.random.default_rng(seed)
+    return [moeq.quantize_nvfp4((rs.standard_normal(shape) * 0.02).astype(np.float32))
+            for shape in [(I, H), (I, H), (H, I)]]
+
+
+@pytest.mark.parametrize("bad", [0x7F, 0xFF])
+def test_pack_nvfp4_rejects_e4m3_nan_scales(bad):
+    H, I = 256, 128
+    mats = _nv_mats(H, I, 5)
+    for which in range(3):
+        m = [(c, sc.copy()) for c, sc in mats]
+        m[which][1][3, 1] = bad
+        with pytest.raises(moeq.MoeError) as ei:
+            moeq.pack_nvfp4_expert(m[0], m[1], m[2], H, I)
+        assert ei.value.status == moeq.MOE_EINVAL
+        assert b"NaN" in moeq.lib().moe_last_error()
+        # the same byte in either plane of a two-level expert
+        with pytest.raises(moeq.MoeError) as ei:
+            moeq.pack_nvfp4r_expert(mats, m, H, I)
+        assert ei.value.status == moeq.MOE_EINVAL
+        with pytest.raises(moeq.MoeError) as ei:
+            moeq.pack_nvfp4r_expert(m, mats, H, I)
+        assert ei.value.status == moeq.MOE_EINVAL
+    # the largest finite bytes (+-448) and negative scales are values, not errors
+    m = [(c, sc.copy()) for c, sc in mats]
+    m[0][1][0, 0], m[1][1][0, 0], m[2][1][0, 0] = 0x7E, 0xFE, 0x88
+    moeq.pack_nvfp4_expert(m[0], m[1], m[2], H, I)
+
+
+@pytest.mark.parametrize("bad", [0x7C00, 0xFC00, 0x7E00, 0xFFFF])
+def test_pack_vq_rejects_nonfinite_scales(bad):
+    H, I = 256, 128
+    rs = np.random.default_rng(6)
+    parts = [(rs.integers(0, 65536, (n, kin // 8), dtype=np.uint16), _finite_f16_bits(rs, n))
+             for n, kin in [(I, H), (I, H), (H, I)]]
+    parts8 = [(rs.integers(0, 256, (n, kin // 8, 2), dtype=np.uint8), _finite_f16_bits(rs, n))
+              for n, kin in [(I, H), (I, H), (H, I)]]
+    for which in range(3):
+        p = [(c, sc.copy()) for c, sc in parts]
+        p[which][1][7] = bad
+        with pytest.raises(moeq.MoeError) as ei:
+            moeq.pack_vq_expert(p[0], p[1], p[2], H, I)
+        assert ei.value.status == moeq.MOE_EINVAL
+        p8 = [(c, sc.copy()) for c, sc in parts8]
+        p8[which][1][7] = bad
+        with pytest.raises(moeq.MoeError) as ei:
+            moeq.pack_vq8_expert(p8[0], p8[1], p8[2], H, I, 2)
+        assert ei.value.status == moeq.MOE_EINVAL
+    # the largest finite magnitude is accepted
+    p = [(c, sc.copy()) for c, sc in parts]
+    p[0][1][0], p[2][1][1] = 0x7BFF, 0xFBFF
+    moeq.pack_vq_expert(p[0], p[1], p[2], H, I)
+
+
+# ------------------------------------------------- workspace sizes
+
+def _bf16_shared_layer(H, I):
+    d = _fake_layer(np.full(1, moeq.FMT_BF16, np.uint8), H=H, I=I)
+    d.bf16_w13 = d.bf16_w2 = 0x100000
+    d.bf16_w13_stride = d.bf16_w2_stride = 1 << 30
+    return d
+
+
+def _al(n):
+    return (n + 255) // 256 * 256
+
+
+def test_shared_workspace_is_sized_for_the_path_that_runs():
+    """The shared expert's decode path (T < 128) splits its gate/up inputs over
+    nsplit workgroups and keeps nsplit x T x 2I fp32 partial sums; the
+    grouped GEMM (T >= 128, NVFP4 or BF16) keeps none."""
+    L = moeq.lib()
+    H, I = 6144, 2048
+    d = _bf16_shared_layer(H, I)
+    # T = 4096 and 16384: x as fp16 and h only (no partial sums)
+    for T in (4096, 16384):
+        need = L.moe_shared_ffn_workspace_bytes(ctypes.byref(d), T)
+        assert need == _al(T * H * 2) + _al(T * I * 2), T
+    assert L.moe_shared_ffn_workspace_bytes(ctypes.byref(d), 4096) < 80 << 20
+    # decode: I/16 = 128 row-pair groups per input split; 512 workgroups aimed
+    # for -> 4 splits (and 48 input tiles of 128 allow up to 12)
+    for T in (1, 8, 127):
+        need = L.moe_shared_ffn_workspace_bytes(ctypes.byref(d), T)
+        assert need == _al(T * H * 2) + _al(T * I * 2) + _al(4 * T * 2 * I * 4), T
+    # a VQ shared expert keeps the decode path at every T (256-input tiles)
+    dv = _fake_layer(np.full(1, moeq.FMT_VQ, np.uint8), H=H, I=I)
+    need = L.moe_shared_ffn_workspace_bytes(ctypes.byref(dv), 4096)
+    assert need == _al(4096 * H * 2) + _al(4096 * I * 2) + _al(4 * 4096 * 2 * I * 4)
+    # a small layer: the split is capped by the input tiles (H = 256: 2 tiles
+    # of 128 for 4 waves -> one split)
+    ds = _bf16_shared_layer(256, 128)
+    assert L.moe_shared_ffn_workspace_bytes(ctypes.byref(ds), 4) == (
+        _al(4 * 256 * 2) + _al(4 * 128 * 2) + _al(1 * 4 * 2 * 128 * 4))
+    # the one-call layer with a shared expert reserves the same shared part
+    routed = _fake_layer(np.full(256, moeq.FMT_NVFP4, np.uint8), H=H, I=I)
+    T, k = 4096, 8
+    lw = L.moe_layer_forward_workspace_bytes(ctypes.byref(routed), T, k)
+    tot = L.moe_layer_forward_shared_workspace_bytes(ctypes.byref(routed), ctypes.byref(d), T, k)
+    assert tot == _al(lw) + _al(T * H * 2) + _al(T * I * 2) + _al(T * H * 4)

@@ -1,6 +1,7 @@
 """Pins of the oracle's format code (E2M1, E4M3, NVFP4 encoder, VQ decode)
 against facts fixed outside the oracle: published value tables, a library
-cast, hand-worked blocks, brute force and closed forms.  CPU only."""
+cast, hand-worked blocks, brute force and closed forms; the 16-bit float
+widening of activations, codebooks and scales.  CPU only."""
 
 import math
 import os
@@ -22,6 +23,65 @@ def _read_table(path):
                 continue
             rows.append(line.split())
     return rows
+
+
+# ------------------------------------------------- 16-bit activations
+#
+# The oracle widens every bf16 activation (and fp16 codebook entry / scale)
+# with bf16_bits_to_f64 / f16_bits_to_f64.  Both are pinned over all 65,536
+# bit patterns against (a) torch's own bfloat16 / float16 types and (b) the
+# IEEE field decode written out here: sign, biased exponent, fraction, with
+# exponent field 0 subnormal and the all-ones field infinity (fraction 0) or
+# NaN.  bf16 = 1 + 8 + 7 bits, bias 127 (the top half of a binary32); fp16 =
+# 1 + 5 + 10 bits, bias 15.
+
+
+def _ieee_fields_decode(bits, ebits, fbits):
+    bits = np.asarray(bits, dtype=np.int64)
+    bias = (1 << (ebits - 1)) - 1
+    s = (bits >> (ebits + fbits)) & 1
+    e = (bits >> fbits) & ((1 << ebits) - 1)
+    f = bits & ((1 << fbits) - 1)
+    emax = (1 << ebits) - 1
+    mag = np.where(e == 0, np.ldexp(f.astype(np.float64), 1 - bias - fbits),
+                   np.ldexp((f + (1 << fbits)).astype(np.float64), e - bias - fbits))
+    mag = np.where((e == emax) & (f == 0), np.inf, mag)
+    mag = np.where((e == emax) & (f != 0), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def _same_f64(got, want):
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_bf16_widening_all_patterns_vs_torch_and_fields():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_bits_to_f64(bits)
+    ref_t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    _same_f64(got, ref_t)
+    _same_f64(got, _ieee_fields_decode(bits, 8, 7))
+    # named points: 1.0, -2.0, the smallest subnormal, the largest finite, +-inf
+    named = {0x3F80: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -133,
+             0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127, 0x7F80: np.inf, 0xFF80: -np.inf}
+    for b, v in named.items():
+        assert oracle.bf16_bits_to_f64(np.uint16(b)) == v, hex(b)
+    assert np.signbit(oracle.bf16_bits_to_f64(np.uint16(0x8000)))
+
+
+def test_f16_widening_all_patterns_vs_torch_and_fields():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.f16_bits_to_f64(bits)
+    ref_t = torch.from_numpy(bits.view(np.int16)).view(torch.float16).double().numpy()
+    _same_f64(got, ref_t)
+    _same_f64(got, _ieee_fields_decode(bits, 5, 10))
+    named = {0x3C00: 1.0, 0x7BFF: 65504.0, 0x0001: 2.0 ** -24, 0x0400: 2.0 ** -14,
+             0xFC00: -np.inf}
+    for b, v in named.items():
+        assert oracle.f16_bits_to_f64(np.uint16(b)) == v, hex(b)
 
 
 # ---------------------------------------------------------------- E2M1
