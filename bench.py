@@ -2,7 +2,7 @@
 """Benchmark of the routed-expert MoE forward (route -> permute -> expert
 FFN over low-bit weights -> combine) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--detail-out PATH]
 
 Headline workload: the GLM-5-class decode layer -- 256 experts, top-8,
 hidden 6144, expert intermediate 2048, NVFP4 weights quantized from
@@ -11,20 +11,27 @@ logits.  A step is one whole forward over one batch; the batches rotate over
 a pool of seeded inputs resident in HBM (so consecutive steps route to
 different experts and the weights stream from HBM, not from the caches).
 
-Prints ONE JSON line on stdout (progress goes to stderr):
-  value          tokens/s of the whole path
-  roofline       the NVFP4 gate/up kernel: packed gate/up bytes of the
-                 experts it touches per launch / its mean launch time
-                 (HIP events on the launch stream), against 8 TB/s HBM
-  cpu_baseline   the fp64 oracle on a bounded sample (three tokens), one core
-  extra          the same path on the other workloads (decode T = 1 and 8,
-                 prefill T = 4096 with Zipf(1.1) routing, 2-bit VQ T = 8,
-                 small-codebook VQ at 1 and 2 bits per weight T = 8,
-                 mixed NVFP4/VQ T = 8 and 32, the same mixed layer with
-                 its hot experts switched to the NVFP4 tier at run time,
-                 the decode and prefill layers with a BF16 shared expert, and
-                 the decode layer stored rotated (online Hadamard-128
-                 rotations around every matrix))
+Prints ONE compact JSON line on stdout (progress goes to stderr):
+  value            tokens/s of the whole path (graph replays)
+  roofline         the dominant kernel, the NVFP4 gate/up decode kernel:
+                   packed gate/up bytes of the experts it touches per launch
+                   / its mean launch time (HIP events on the launch stream),
+                   against 8 TB/s HBM
+  roofline_ffn     the expert FFN of the headline step: all packed bytes of
+                   the touched experts / the time of its FFN kernels (gate/up
+                   + down), against 8 TB/s
+  roofline_prefill the grouped GEMM of the prefill workload (T = 4096,
+                   Zipf(1.1) routing): 6 H I T k flop / the time of its
+                   gate/up + down kernels, against 2.5 PFLOP/s fp16 MFMA
+  cpu_baseline     the fp64 oracle on a bounded sample of the headline batch,
+                   a process pool over experts on the host's cores
+  extra            per workload: T, tokens/s, ms per step, the bound, and
+                   the fraction of that roofline reached by its FFN kernels
+                   (decode T = 1 and 8, prefill, 2-bit VQ, small-codebook VQ,
+                   mixed NVFP4/VQ, the mixed layer with its hot experts on the
+                   NVFP4 tier, nested two-level NVFP4, a BF16 shared expert,
+                   rotated layers)
+--detail-out writes every figure of every workload to a JSON file.
 """
 
 import argparse
@@ -125,7 +132,41 @@ class Runner:
             self.y_sh = torch.empty((T, H), dtype=f32, device=dev)
             self.sws = moeq.shared_workspace(shared, T)
         self.ev = []
+        self.ev_dn = []
         self.ev_sh = []
+        self.ev_layer = []
+
+    def _timed_call(self, fn, args):
+        """fn(*args) between two HIP events on the current stream (the stream
+        the library launches on); returns the event pair."""
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = fn(*args)
+        e1.record()
+        self.moeq._check(rc, fn.__name__)
+        return e0, e1
+
+    def layer_step(self, r):
+        """moe_layer_forward (moe_layer_forward_shared) on batch r with HIP
+        events around the pre-marshalled C call: the whole layer as the
+        library runs it (for decode batches of <= 16 assignments, the fused
+        launches: routing inside gate/up, the combine inside down)."""
+        import ctypes
+        moeq = self.moeq
+        L = moeq.lib()
+        lg, x = self.batches[r % len(self.batches)]
+        st = moeq._stream(x.device)
+        if self.shared is None:
+            args = (ctypes.byref(self.layer.c()), moeq._dptr(x), moeq._dptr(lg), self.T, self.k,
+                    None, moeq._dptr(self.ids), moeq._dptr(self.w), moeq._dptr(self.out),
+                    moeq._dptr(self.lws), self.lws.numel(), st)
+            self.ev_layer.append(self._timed_call(L.moe_layer_forward, args))
+        else:
+            args = (ctypes.byref(self.layer.c()), ctypes.byref(self.shared.c()), moeq._dptr(x),
+                    moeq._dptr(lg), self.T, self.k, moeq._dptr(self.ids), moeq._dptr(self.w),
+                    moeq._dptr(self.out), moeq._dptr(self.lws), self.lws.numel(), st)
+            self.ev_layer.append(self._timed_call(L.moe_layer_forward_shared, args))
 
     def step(self, r, timed):
         """One layer forward on batch r.  Untimed (warm-up and the graph
@@ -133,7 +174,7 @@ class Runner:
         moe_layer_forward, or moe_layer_forward_shared with a shared expert
         (fused for decode batches of <= 16 assignments).
         Timed eager steps: the step-by-step calls, with HIP events around the
-        gate/up call (the kernel-level figures)."""
+        gate/up and the down call (the kernel-level figures)."""
         moeq = self.moeq
         lg, x = self.batches[r % len(self.batches)]
         if not timed:
@@ -146,17 +187,16 @@ class Runner:
         # the events bracket the kernel rather than Python's overhead
         import ctypes
         L = moeq.lib()
+        st = moeq._stream(x.device)
         args = (ctypes.byref(self.layer.c()), moeq._dptr(x), moeq._dptr(perm_src),
                 moeq._dptr(offsets), self.T, self.k, moeq._dptr(self.h), moeq._dptr(self.ws),
-                self.ws.numel(), moeq._stream(x.device))
-        e0 = self.torch.cuda.Event(enable_timing=True)
-        e1 = self.torch.cuda.Event(enable_timing=True)
-        e0.record()
-        rc = L.moe_expert_gateup_q(*args)
-        e1.record()
-        moeq._check(rc, "moe_expert_gateup_q")
+                self.ws.numel(), st)
+        e0, e1 = self._timed_call(L.moe_expert_gateup_q, args)
         self.ev.append((r, e0, e1))
-        moeq.expert_down_q(self.layer, self.h, offsets, self.k, self.y)
+        args = (ctypes.byref(self.layer.c()), moeq._dptr(self.h), moeq._dptr(offsets), self.T,
+                self.k, moeq._dptr(self.y), st)
+        e0, e1 = self._timed_call(L.moe_expert_down_q, args)
+        self.ev_dn.append((r, e0, e1))
         if self.shared is None:
             moeq.combine(self.y, inv_perm, self.w, self.out)
             return
@@ -169,19 +209,35 @@ class Runner:
         moeq.combine_shared(self.y, inv_perm, self.w, self.y_sh, self.out)
 
     def run(self, steps, warmup):
+        """Eager steps: the step-by-step calls with HIP events around the
+        gate/up and the down call.  Returns (seconds, gate/up ms per launch,
+        down ms per launch)."""
         torch = self.torch
         for i in range(warmup):
             self.step(i, False)
         torch.cuda.synchronize()
-        self.ev = []
-        self.ev_sh = []
+        self.ev, self.ev_dn, self.ev_sh = [], [], []
         t0 = time.perf_counter()
         for i in range(steps):
             self.step(warmup + i, True)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         gu_ms = [e0.elapsed_time(e1) for _, e0, e1 in self.ev]
-        return dt, gu_ms
+        dn_ms = [e0.elapsed_time(e1) for _, e0, e1 in self.ev_dn]
+        return dt, gu_ms, dn_ms
+
+    def run_layer(self, steps, warmup):
+        """Eager one-call layer steps with HIP events around each call; the
+        ms of each call."""
+        torch = self.torch
+        for i in range(warmup):
+            self.layer_step(i)
+        torch.cuda.synchronize()
+        self.ev_layer = []
+        for i in range(steps):
+            self.layer_step(warmup + i)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in self.ev_layer]
 
     def run_graph(self, steps, warmup):
         """The same steps replayed from HIP graphs, as a decode loop would run
@@ -219,10 +275,12 @@ class Runner:
 
     def bytes_of(self, r, which):
         """Algorithmic packed-weight bytes of batch r: 'all' (codes + scales
-        of every touched expert, VQ codebooks once) or 'gateup'."""
+        of every touched expert, VQ codebooks once, and the shared expert's
+        weights), 'routed' (the same without the shared expert) or
+        'gateup'."""
         experts = self.touched[r % len(self.touched)]
-        if which == "all":
-            sh = self.shared.packed_bytes([0]) if self.shared is not None else 0
+        if which in ("all", "routed"):
+            sh = self.shared.packed_bytes([0]) if self.shared is not None and which == "all" else 0
             return self.layer.packed_bytes(experts) + sh
         H, I = self.wl.H, self.wl.I
         tot = 0
@@ -237,22 +295,42 @@ class Runner:
         return tot
 
 
+def fused_path(layer, T, k):
+    """Whether moe_layer_forward takes its fused decode path for this batch
+    (a single-format, unrotated layer of at most 256 experts, k <= 8 and at
+    most 16 assignments): then the whole layer is two launches (three with a
+    BF16 shared expert)."""
+    return (len(set(int(f) for f in layer.fmt_host)) == 1 and layer.rot_signs is None
+            and layer.E <= 256 and k <= 8 and T * k <= 16)
+
+
 def measure(layer, wl, T, steps, warmup, dev, reps=16, shared=None):
-    """Eager launches (per-launch HIP events around the gate/up call), then
-    the same steps replayed from HIP graphs; the headline figures are the
-    graph replay's, the kernel-level ones the eager run's.  A shared expert
-    runs after the routed experts on the same stream (its HIP events bracket
-    its three launches)."""
+    """Eager launches (HIP events around the gate/up and the down call, and
+    around the one-call layer), then the same steps replayed from HIP graphs;
+    the headline figures are the graph replay's, the kernel-level ones the
+    eager runs'.  A shared expert runs after the routed experts on the same
+    stream (its HIP events bracket its launches).
+
+    The FFN roofline of a workload is taken over the kernels of the path its
+    steps run: for a fused decode batch the one-call layer's launches (the
+    routing and the combine run inside them), otherwise the gate/up and down
+    kernels (+ the shared expert's); decode batches against 8 TB/s on all
+    packed bytes the step reads, prefill batches against 2.5 PFLOP/s on
+    6 H I flop per assignment."""
+    import numpy as np
     rn = Runner(layer, wl, T, reps, dev, shared)
-    dte, gu_ms = rn.run(steps, warmup)
+    dte, gu_ms, dn_ms = rn.run(steps, warmup)
+    lay_warm = 2
+    lay_ms = rn.run_layer(steps, lay_warm)
     dt, group = rn.run_graph(steps, warmup)
-    idx = list(range(steps))                    # batches of the timed graph replays
-    idx_e = [warmup + i for i in range(steps)]  # batches of the timed eager steps
+    idx = list(range(steps))                          # batches of the graph replays
+    idx_e = [warmup + i for i in range(steps)]        # batches of the eager steps
+    idx_l = [lay_warm + i for i in range(steps)]      # batches of the one-call layer steps
     all_bytes = sum(rn.bytes_of(r, "all") for r in idx)
     gu_bytes = sum(rn.bytes_of(r, "gateup") for r in idx_e)
     gu_s = sum(gu_ms) / 1e3
-    import numpy as np
     q = np.percentile(rn.replay_step_ms, [10, 50, 90])
+    fused = fused_path(layer, T, wl.k)
     res = {
         "T": T,
         "tokens_per_s": T * steps / dt,
@@ -265,8 +343,11 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16, shared=None):
         "packed_frac_hbm": all_bytes / dt / 1e9 / HBM_PEAK_GBS,
         "experts_touched_mean": sum(len(rn.touched[r % reps]) for r in idx) / steps,
         "gateup_ms_mean": sum(gu_ms) / len(gu_ms),
+        "down_ms_mean": sum(dn_ms) / len(dn_ms),
         "gateup_GBps": gu_bytes / gu_s / 1e9,
         "gateup_bytes_per_launch": gu_bytes / steps,
+        "layer_call_ms_mean": sum(lay_ms) / len(lay_ms),
+        "path": "fused" if fused else "steps",
     }
     if shared is not None:
         sh_ms = [e0.elapsed_time(e1) for _, e0, e1 in rn.ev_sh]
@@ -274,55 +355,96 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16, shared=None):
         res["shared_ms_mean"] = sum(sh_ms) / len(sh_ms)
         res["shared_GBps"] = sh_bytes / (res["shared_ms_mean"] / 1e3) / 1e9
         res["shared_bytes"] = sh_bytes
-    if T >= 1024:
-        flops = 6.0 * wl.H * wl.I * T * (wl.k + (1 if shared is not None else 0))
-        res["TFLOPs"] = flops / (dt / steps) / 1e12
-        res["frac_mfma"] = res["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+    # the FFN kernels of the path the steps run
+    if fused:
+        ffn_ms = res["layer_call_ms_mean"]
+        ffn_bytes = sum(rn.bytes_of(r, "all") for r in idx_l) / steps
+    else:
+        ffn_ms = res["gateup_ms_mean"] + res["down_ms_mean"] + res.get("shared_ms_mean", 0.0)
+        ffn_bytes = sum(rn.bytes_of(r, "all") for r in idx_e) / steps
+    res["ffn_ms"] = ffn_ms
+    res["ffn_bytes_per_step"] = ffn_bytes
+    res["ffn_GBps"] = ffn_bytes / (ffn_ms / 1e3) / 1e9
+    if T >= PREFILL_MIN_TOKENS:
+        flops = 6.0 * wl.H * wl.I * T * wl.k
         if shared is not None:
-            res["shared_TFLOPs"] = 6.0 * wl.H * wl.I * T / (res["shared_ms_mean"] / 1e3) / 1e12
+            flops += 6.0 * shared.H * shared.I * T
+        res["flops_per_step"] = flops
+        res["TFLOPs"] = flops / (dt / steps) / 1e12
+        res["ffn_TFLOPs"] = flops / (ffn_ms / 1e3) / 1e12
+        res["bound"] = "mfma"
+        res["ffn_frac"] = res["ffn_TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+        if shared is not None:
+            res["shared_TFLOPs"] = 6.0 * shared.H * shared.I * T / (res["shared_ms_mean"] / 1e3) / 1e12
+    else:
+        res["bound"] = "hbm"
+        res["ffn_frac"] = res["ffn_GBps"] / HBM_PEAK_GBS
     return res
+
+
+def compact(res):
+    """The figures of one workload kept in the stdout line."""
+    if "error" in res:
+        return {"error": res["error"][:200]}
+    return {"T": res["T"], "tok_s": round(res["tokens_per_s"], 1),
+            "ms": round(res["ms_per_step"], 4), "bound": res["bound"],
+            "frac": round(res["ffn_frac"], 4), "path": res["path"]}
 
 
 # --------------------------------------------------------------------------
 
-CPU_SAMPLE_TOKENS = 3
+CPU_SAMPLE_TOKENS = 8
+CPU_MAX_WORKERS = 16
 
 
-def cpu_baseline(wl, T):
-    """The fp64 oracle on the first CPU_SAMPLE_TOKENS tokens of the batch, on
-    one core (BLAS threads pinned to 1).  The oracle's own encoder prepares
-    the canonical NVFP4 bytes of those tokens' experts in a process pool
-    outside the timed region; the timed region is oracle.forward: route,
-    decode of the touched experts from canonical bytes, FFN and combine."""
+def cpu_baseline(wl, T, ntok=CPU_SAMPLE_TOKENS):
+    """The fp64 oracle on the first ntok tokens of the headline batch, its
+    per-expert loop spread over a process pool on the host's cores (one BLAS
+    thread per process).
+
+    Untimed: the oracle's own encoder writes each touched expert's canonical
+    NVFP4 bytes (codes and scales of gate, up and down) to a scratch folder,
+    in the same pool.  Timed: routing (oracle.route_topk); then per touched
+    expert, in the pool, its canonical bytes read back, decoded to fp64
+    (oracle.nvfp4_dequant) and the FFN of its tokens (oracle.expert_ffn);
+    then the combine (oracle.combine).  That is oracle.forward with its loop
+    over experts run in parallel; the effective GB/s is the touched experts'
+    packed bytes over the timed seconds."""
     import multiprocessing as mp
+    import shutil
+    import tempfile
     from concurrent.futures import ProcessPoolExecutor
 
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     import oracle
     import synth
 
-    nt = CPU_SAMPLE_TOKENS
-    lg = synth.logits(wl, T, rep=0)[:nt]
-    x = synth.activations(wl, T, rep=0)[:nt]
-    ids, _ = oracle.route_topk(lg, wl.k)
-    experts = sorted(int(e) for e in np.unique(ids))
-    jobs = [(e, p) for e in experts for p in range(3)]
+    lg = synth.logits(wl, T, rep=0)[:ntok]
+    x = synth.activations(wl, T, rep=0)[:ntok]
+    ids0, _ = oracle.route_topk(lg, wl.k)
+    experts = sorted(int(e) for e in np.unique(ids0))
     ncpu = len(os.sched_getaffinity(0))
-    with ProcessPoolExecutor(max(1, min(16, ncpu)), mp_context=mp.get_context("spawn")) as ex:
-        enc = list(ex.map(_oracle_encode, [(wl.name, e, p) for e, p in jobs]))
-    canon = {}
-    for (e, p), cs in zip(jobs, enc):
-        canon.setdefault(e, [None, None, None])[p] = cs
-
-    def weights(e):
-        return tuple(oracle.nvfp4_dequant(*canon[e][p]) for p in range(3))
-
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        oracle.forward(x, lg, wl.k, weights)
-        dt = time.perf_counter() - t0
+    workers = max(1, min(CPU_MAX_WORKERS, ncpu, len(experts)))
+    scratch = tempfile.mkdtemp(prefix="moe_oracle_")
+    try:
+        with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"),
+                                 initializer=_one_blas_thread) as ex:
+            list(ex.map(_oracle_encode, [(wl.name, e, scratch) for e in experts]))
+            t0 = time.perf_counter()
+            ids, w = oracle.route_topk(lg, wl.k)
+            jobs = []
+            for e in experts:
+                tt, jj = np.nonzero(ids == e)
+                jobs.append((e, scratch, x[tt]))
+            y = np.zeros((ntok, wl.k, wl.H), dtype=np.float64)
+            for (e, _, _), ye in zip(jobs, ex.map(_oracle_expert, jobs)):
+                tt, jj = np.nonzero(ids == e)
+                y[tt, jj] = ye
+            oracle.combine(y, w)
+            dt = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(scratch, ignore_errors=True)
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -332,20 +454,49 @@ def cpu_baseline(wl, T):
                     break
     except OSError:
         pass
-    return {"value": nt / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{nt} tokens of the decode T={T} batch ({len(experts)} experts): "
-                       f"oracle.forward (fp64 route, NVFP4 decode from canonical bytes, FFN, "
-                       f"combine) on one core of '{cpu_model}' ({ncpu} host cores visible); "
-                       f"{dt:.1f} s"),
+    nbytes = len(experts) * 3 * (wl.H * wl.I // 2 + wl.H * wl.I // 16)
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "GBps": nbytes / dt / 1e9,
+            "sample": (f"the first {ntok} tokens of the decode T={T} batch ({len(experts)} "
+                       f"experts, {nbytes / 1e9:.2f} GB packed): the fp64 oracle (route, NVFP4 "
+                       f"decode from canonical bytes, FFN, combine) with its experts over "
+                       f"{workers} processes of one thread on '{cpu_model}' ({ncpu} cores "
+                       f"visible); {dt:.1f} s"),
             "seconds": dt}
 
 
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
 def _oracle_encode(args):
+    """The oracle's canonical NVFP4 bytes of one expert, saved to the scratch
+    folder (untimed preparation of the oracle's input)."""
+    import numpy as np
+
     import oracle
     import synth
-    name, e, p = args
+    name, e, scratch = args
     wl = synth.WORKLOADS[name]
-    return oracle.nvfp4_quantize(synth.nvfp4_source_weights(wl, e, p))
+    for p in range(3):
+        c, s = oracle.nvfp4_quantize(synth.nvfp4_source_weights(wl, e, p))
+        np.save(os.path.join(scratch, f"e{e}_p{p}_codes.npy"), c)
+        np.save(os.path.join(scratch, f"e{e}_p{p}_scales.npy"), s)
+    return e
+
+
+def _oracle_expert(args):
+    """Timed: decode one expert from its canonical bytes and run the oracle
+    FFN on its tokens."""
+    import numpy as np
+
+    import oracle
+    e, scratch, xe = args
+    W = [oracle.nvfp4_dequant(np.load(os.path.join(scratch, f"e{e}_p{p}_codes.npy")),
+                              np.load(os.path.join(scratch, f"e{e}_p{p}_scales.npy")))
+         for p in range(3)]
+    return oracle.expert_ffn(xe, *W)
 
 
 # --------------------------------------------------------------------------
@@ -364,6 +515,10 @@ def main():
                             "rotprefill",
                     help="comma list of other workloads to measure ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=CPU_SAMPLE_TOKENS,
+                    help="tokens of the headline batch the oracle baseline runs on")
+    ap.add_argument("--detail-out", default=None,
+                    help="write every figure of every workload to this JSON file")
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -553,13 +708,26 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"timing the oracle on a {CPU_SAMPLE_TOKENS}-token sample ...")
-        cpu = cpu_baseline(wl, args.T)
+        log(f"timing the oracle on a {args.cpu_tokens}-token sample ...")
+        cpu = cpu_baseline(wl, args.T, args.cpu_tokens)
         cpu.pop("seconds", None)
         log("  ", json.dumps(cpu))
 
     achieved = head["gateup_GBps"]
     traffic = read_traffic(f"traffic_gateup_nvfp4_decode_T{args.T}.json")
+    roof_ffn = {"bound": "hbm",
+                "kernels": ("moe_layer_forward's fused launches" if head["path"] == "fused"
+                            else "NVFP4 gate/up + down"),
+                "achieved": head["ffn_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": head["ffn_frac"], "bytes_per_step": head["ffn_bytes_per_step"],
+                "ms": head["ffn_ms"]}
+    roof_pf = None
+    pf = extra.get("prefill", {})
+    if "ffn_TFLOPs" in pf:
+        roof_pf = {"bound": "mfma", "kernels": "k_prefill<PfNv, 0> + k_prefill<PfNv, 1>",
+                   "achieved": pf["ffn_TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,
+                   "unit": "TFLOP/s", "frac": pf["ffn_frac"], "ms": pf["ffn_ms"],
+                   "flop_per_step": pf["flops_per_step"], "T": pf["T"]}
     line = {
         "metric": "routed-expert tokens/s + packed-weight HBM GB/s (decode M=1..32, prefill 4K)",
         "value": head["tokens_per_s"],
@@ -585,9 +753,14 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": head["gateup_bytes_per_launch"],
                      "launch_ms_mean": head["gateup_ms_mean"]},
+        "roofline_ffn": roof_ffn,
+        "roofline_prefill": roof_pf,
         "cpu_baseline": cpu,
-        "extra": extra,
+        "extra": {name: compact(r) for name, r in extra.items()},
     }
+    if args.detail_out:
+        with open(args.detail_out, "w") as f:
+            json.dump({"headline": head, "extra": extra, "line": line}, f, indent=1)
     print(json.dumps(line), flush=True)
 
 

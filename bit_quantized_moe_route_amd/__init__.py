@@ -521,6 +521,7 @@ class QLayer:
         over those experts must read."""
         tot = 0
         vq = vq8 = False
+        vq_books = 0                    # per-record VQ codebooks touched
         for e in set(int(x) for x in experts):
             if self.fmt_host[e] in (FMT_NVFP4, FMT_NVFP4R):
                 planes = 2 if self.fmt_host[e] == FMT_NVFP4R else 1
@@ -532,9 +533,11 @@ class QLayer:
                 tot += 3 * (self.H * self.I // 8) * self.vq8_m + (2 * self.I + self.H) * 2
             else:
                 vq = True
+                vq_books += 1
                 tot += 3 * (self.H * self.I // 8) * 2 + (2 * self.I + self.H) * 2
-        if vq and self.codebook_stride == 0:
-            tot += 3 * VQ_NCODE * 8 * 2
+        if vq:
+            # one shared codebook per projection, or each touched record's own
+            tot += 3 * VQ_NCODE * 8 * 2 * (1 if self.codebook_stride == 0 else vq_books)
         if vq8:
             tot += 3 * self.vq8_m * VQ8_NCODE * 8 * 2
         return tot

@@ -44,6 +44,7 @@ KIND_VQ8_CODES = 9
 KIND_VQ8_CODEBOOK = 10
 KIND_SHARED = 11
 KIND_ROT_SIGNS = 12
+KIND_VQ_CODEBOOK_EXPERT = 13
 
 # sides of a rotated expert that carry their own random signs
 ROT_IN13, ROT_OUT_GATE, ROT_OUT_UP, ROT_IN2, ROT_OUT2 = 0, 1, 2, 3, 4
@@ -290,6 +291,14 @@ def vq_codebook(wl, proj, ncode=65536):
     """One fp16 codebook [ncode, 8] per projection type, shared by all the
     layer's experts; entries ~ N(0, 0.02); uint16 bits."""
     c = rng(wl.vq_cfg, KIND_VQ_CODEBOOK, 0, proj).standard_normal(
+        (ncode, 8), dtype=np.float32) * np.float32(0.02)
+    return f32_to_f16_bits(c)
+
+
+def vq_codebook_expert(wl, expert, proj, ncode=65536):
+    """An fp16 codebook [ncode, 8] of one expert's projection (the per-expert
+    codebook variant); entries ~ N(0, 0.02); uint16 bits."""
+    c = rng(wl.vq_cfg, KIND_VQ_CODEBOOK_EXPERT, expert, proj).standard_normal(
         (ncode, 8), dtype=np.float32) * np.float32(0.02)
     return f32_to_f16_bits(c)
 

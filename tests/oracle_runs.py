@@ -69,9 +69,16 @@ def pool_map(jobs, workers=None):
     from concurrent.futures import ProcessPoolExecutor
 
     if workers is None:
-        workers = max(1, min(len(jobs), 8, len(os.sched_getaffinity(0))))
+        workers = 8
+    workers = max(1, min(len(jobs), workers, len(os.sched_getaffinity(0))))
     if workers == 1 or len(jobs) == 1:
         return [expert_rows(j) for j in jobs]
     ctx = mp.get_context("spawn")
-    with ProcessPoolExecutor(workers, mp_context=ctx) as ex:
+    with ProcessPoolExecutor(workers, mp_context=ctx, initializer=_one_blas_thread) as ex:
         return list(ex.map(expert_rows, jobs))
+
+
+def _one_blas_thread():
+    """Pool workers each take one core: BLAS limited to one thread."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)

@@ -111,3 +111,36 @@ def test_committed_decode_traces_name_the_roofline_kernel():
         with open(p) as f:
             text = f.read()
         assert f"`{bench.gateup_kernel_name(T, 8, 256)}`" in text, T
+
+
+def test_compact_workload_entry_is_small_and_complete():
+    """Each workload keeps T, tokens/s, ms per step, the bound, the roofline
+    fraction and the path in the stdout line: all 23 workloads together stay
+    far below the 6 KB the line may take beside the headline fields."""
+    res = {"T": 32, "tokens_per_s": 54884.123456, "ms_per_step": 0.5830123, "bound": "hbm",
+           "ffn_frac": 0.7012345, "path": "steps", "gateup_ms_mean": 0.41, "extra": "x" * 500}
+    c = bench.compact(res)
+    assert set(c) == {"T", "tok_s", "ms", "bound", "frac", "path"}
+    assert c["frac"] == 0.7012 and c["tok_s"] == 54884.1
+    assert len(json.dumps({f"workload{i:02d}": c for i in range(23)})) < 3000
+    assert bench.compact({"error": "RuntimeError(" + "y" * 1000 + ")"})["error"].startswith("Runtime")
+    assert len(json.dumps(bench.compact({"error": "z" * 5000}))) < 300
+
+
+class _FakeLayer:
+    def __init__(self, fmts, E=256, rot=None):
+        self.fmt_host = np.array(fmts, np.uint8)
+        self.E = E
+        self.rot_signs = rot
+
+
+def test_fused_path_rule_matches_the_library():
+    """moe_layer_forward fuses single-format, unrotated layers of at most 256
+    experts for k <= 8 and T k <= 16 assignments."""
+    one = _FakeLayer([1] * 256)
+    assert bench.fused_path(one, 1, 8) and bench.fused_path(one, 2, 8)
+    assert not bench.fused_path(one, 3, 8)
+    assert bench.fused_path(one, 16, 1) and not bench.fused_path(one, 4, 9)
+    assert not bench.fused_path(_FakeLayer([1] * 255 + [2]), 1, 8)
+    assert not bench.fused_path(_FakeLayer([1] * 512, E=512), 1, 8)
+    assert not bench.fused_path(_FakeLayer([1] * 256, rot=object()), 1, 8)

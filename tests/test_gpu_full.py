@@ -6,12 +6,15 @@ NVFP4/VQ layer at T = 8 and 32, and the decode layer held nested (two-level NVFP
 experts) at T = 8.
 
 Routing and permutation are compared in full (bit-exact).  Expert outputs
-are compared row by row against the oracle on sampled experts (the oracle
-decodes one expert's 37.7M weights in fp64 in ~10 s), all rows of each
-sampled expert; for T = 1 every expert of the token is computed so the
-combined output row is compared too.  For the other batches the combine is
-checked through a property that holds at any size: out[t] equals the
-fp64 weighted sum of the kernel's own y_perm rows in ascending j."""
+are compared row by row against the oracle, all rows of each expert checked:
+at T = 8 (NVFP4 decode, 2-bit VQ, mixed NVFP4/VQ) every expert the batch
+touches, so each output row is compared too; at other sizes sampled experts
+(the oracle encodes and decodes one NVFP4 expert's 37.7M weights in fp64 in
+~15 s), and for T = 1 every expert of the token with its combined row.  For
+the sampled batches the combine is checked through a property that holds at
+any size: out[t] equals the fp64 weighted sum of the kernel's own y_perm
+rows in ascending j.  The oracle's experts run in a process pool on the
+host's cores."""
 
 import numpy as np
 import pytest
@@ -60,8 +63,8 @@ def check_routing(wl, lg, r):
     return ids, w, offsets, perm_src
 
 
-def check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, fmt_host):
-    """All rows of each sampled expert: GPU y_perm vs the oracle FFN."""
+def check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, fmt_host, workers=None):
+    """All rows of each given expert: GPU y_perm vs the oracle FFN."""
     y_perm = to_np(r["y_perm"])
     jobs, spans = [], []
     for e in experts:
@@ -69,7 +72,7 @@ def check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, fmt_host):
         toks = perm_src[a:b] // wl.k
         jobs.append((wl.name, int(e), x_bits[toks], int(fmt_host[e])))
         spans.append((a, b))
-    refs = pool_map(jobs)
+    refs = pool_map(jobs, workers=workers)
     worst = 0.0
     for (a, b), ref, e in zip(spans, refs, experts):
         worst = max(worst, assert_rows_close(y_perm[a:b], ref, f"{wl.name} expert {e}"))
@@ -85,6 +88,30 @@ def check_combine_property(wl, r):
     for j in range(wl.k):
         ref += w[:, j, None] * y[inv.reshape(T, wl.k)[:, j]]
     assert_rows_close(to_np(r["out"]), ref, "combine property", tol=1e-5)
+
+
+def check_every_expert(wl, x_bits, lg, r, ids, w, offsets, perm_src, fmt_host):
+    """Every expert the batch touches: all its y_perm rows against the
+    oracle FFN, then every output row against the oracle's combine of the
+    oracle's rows."""
+    act = [int(e) for e in np.nonzero(np.diff(offsets) > 0)[0]]
+    say(f"{wl.name}: all {len(act)} touched experts against the oracle")
+    jobs = []
+    for e in act:
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        jobs.append((wl.name, e, x_bits[perm_src[a:b] // wl.k], int(fmt_host[e])))
+    refs = pool_map(jobs, workers=16)
+    y_perm = to_np(r["y_perm"])
+    T = ids.shape[0]
+    y = np.zeros((T, wl.k, wl.H))
+    worst = 0.0
+    for e, ref in zip(act, refs):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        worst = max(worst, assert_rows_close(y_perm[a:b], ref, f"{wl.name} expert {e}"))
+        for i, src in enumerate(perm_src[a:b]):
+            y[src // wl.k, src % wl.k] = ref[i]
+    assert_rows_close(to_np(r["out"]), oracle.combine(y, w), f"{wl.name} out rows")
+    return worst
 
 
 def pick(offsets, fmt_host=None, fmt=None, n=2, seed=0):
@@ -150,14 +177,25 @@ def test_decode_T2_layer_forward_full():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("T", [8, 32])
-def test_decode_full_sampled(T):
+def test_decode_T8_every_expert():
+    """Decode T = 8: every touched expert's rows and every output row."""
     wl = synth.DECODE
+    say("decode full T=8, every expert")
+    lay = layer("decode")
+    x_bits, lg, r = run_forward(wl, lay, 8)
+    ids, w, offsets, perm_src = check_routing(wl, lg, r)
+    check_every_expert(wl, x_bits, lg, r, ids, w, offsets, perm_src, synth.tier_map(wl))
+
+
+@pytest.mark.timeout(900)
+def test_decode_T32_full_sampled():
+    wl = synth.DECODE
+    T = 32
     say("decode full", T)
     lay = layer("decode")
     x_bits, lg, r = run_forward(wl, lay, T)
     ids, w, offsets, perm_src = check_routing(wl, lg, r)
-    experts = pick(offsets, n=2, seed=T)
+    experts = pick(offsets, n=4, seed=T)
     check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
     check_combine_property(wl, r)
 
@@ -207,15 +245,15 @@ def test_prefill_full_sampled():
 # ------------------------------------------------------------------ VQ and mixed
 
 @pytest.mark.timeout(900)
-def test_vq_full_sampled():
+def test_vq_T8_every_expert():
+    """2-bit VQ at T = 8: every touched expert's rows and every output row."""
     wl = synth.VQ
-    say("vq full T=8")
+    say("vq full T=8, every expert")
     lay = layer("vq")
     x_bits, lg, r = run_forward(wl, lay, 8)
     ids, w, offsets, perm_src = check_routing(wl, lg, r)
-    experts = pick(offsets, n=4, seed=2)
-    check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
-    check_combine_property(wl, r)
+    check_every_expert(wl, x_bits, lg, r, ids, w, offsets, perm_src, synth.tier_map(wl))
+    experts = pick(offsets, n=2, seed=2)
     for e in experts[:2]:
         W = expert_weights(wl, e)
         for p in range(3):
@@ -245,17 +283,22 @@ def test_vq8_full_sampled(name):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("T", [8, 32])
-def test_mixed_full_sampled(T):
+def test_mixed_full(T):
+    """The mixed NVFP4/VQ layer: at T = 8 every touched expert and every
+    output row, at T = 32 sampled experts of each format."""
     wl = synth.MIXED
     say("mixed full", T)
     lay = layer("mixed")
     fmt_host = synth.tier_map(wl)
     x_bits, lg, r = run_forward(wl, lay, T)
     ids, w, offsets, perm_src = check_routing(wl, lg, r)
-    experts = (pick(offsets, fmt_host, synth.FMT_NVFP4, n=2, seed=T)
-               + pick(offsets, fmt_host, synth.FMT_VQ, n=2, seed=T + 1))
-    check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, fmt_host)
-    check_combine_property(wl, r)
+    if T == 8:
+        check_every_expert(wl, x_bits, lg, r, ids, w, offsets, perm_src, fmt_host)
+    else:
+        experts = (pick(offsets, fmt_host, synth.FMT_NVFP4, n=2, seed=T)
+                   + pick(offsets, fmt_host, synth.FMT_VQ, n=2, seed=T + 1))
+        check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, fmt_host)
+        check_combine_property(wl, r)
     # the hot set takes about 60% of the assignments
     hot = synth.hot_experts(wl)
     share = np.isin(ids, hot).mean()
