@@ -43,6 +43,7 @@ REC_COMPACT, REC_RESIDENT = 0, 1
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 VQ_NCODE = 65536
 VQ8_NCODE = 256
+STATIC_WS_BYTES = 32 << 20   # MOE_STATIC_WS_BYTES: moe_layer_forward_static's per-GPU array
 
 
 class MoeError(RuntimeError):
@@ -103,6 +104,8 @@ _PROTOS = {
     "moe_layer_forward_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC), _I64, _I32]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _I64, _I32, _P, _P,
                                          _P, _P, _P, _SZ, _P]),
+    "moe_layer_forward_static": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _P, _P, _I64, _I32,
+                                                _P, _P, _P, _P, _P]),
     "moe_layer_forward_shared_workspace_bytes": (_SZ, [ctypes.POINTER(_QLayerC),
                                                        ctypes.POINTER(_QLayerC), _I64, _I32]),
     "moe_layer_forward_shared": (ctypes.c_int, [ctypes.POINTER(_QLayerC),
@@ -808,6 +811,34 @@ def layer_forward(layer, x, logits, k, y_shared=None, out=None, ids=None, w=None
                                    _dptr(y_shared), _dptr(ids),
                                    _dptr(w), _dptr(out), _dptr(ws), ws.numel(), _stream(dev)),
            "moe_layer_forward")
+    return ids, w, out
+
+
+def layer_forward_static(layer, x, logits, k, y_shared=None, out=None, ids=None, w=None):
+    """moe_layer_forward_static: the whole routed layer in one C call with the
+    library's own per-GPU workspace (no workspace argument; the call
+    allocates nothing).  Pass preallocated out / ids / w to keep this
+    function from allocating them.  Returns (topk_ids, topk_w, out)."""
+    torch = _torch()
+    _need_cuda(x, logits)
+    T = x.shape[0]
+    if tuple(logits.shape) != (T, layer.E) or logits.dtype != torch.float32:
+        raise ValueError("logits must be fp32 [T, E]")
+    if y_shared is not None:
+        _need_cuda(y_shared)
+        if tuple(y_shared.shape) != (T, layer.H) or y_shared.dtype != torch.float32:
+            raise ValueError("y_shared must be fp32 [T, H]")
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, layer.H), dtype=torch.float32, device=dev)
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(lib().moe_layer_forward_static(ctypes.byref(layer.c()), _dptr(x), _dptr(logits), T, k,
+                                          _dptr(y_shared), _dptr(ids), _dptr(w), _dptr(out),
+                                          _stream(dev)),
+           "moe_layer_forward_static")
     return ids, w, out
 
 

@@ -439,6 +439,34 @@ int moe_layer_forward(const moe_qlayer* layer, const uint16_t* x_bf16, const flo
                       void* stream);
 
 /*
+ * moe_layer_forward_static -- moe_layer_forward without a workspace argument:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that must not allocate, harnesses that forbid it).
+ * Its workspace is a device array inside the library, MOE_STATIC_WS_BYTES
+ * bytes per GPU, which each GPU the library runs on holds until the process
+ * ends.  The caller still passes the inputs and outputs, as for
+ * moe_layer_forward (same arguments without workspace / workspace_bytes, same
+ * kernels, the same results bit for bit).
+ *   - The call allocates nothing.  Its first call on a device looks up that
+ *     device's array address (hipGetSymbolAddress) and keeps it: make that
+ *     first call outside graph capture.
+ *   - The array of the current device is used; `stream` must belong to it.
+ *   - MOE_EWORKSPACE (nothing launched) if the batch needs more than
+ *     MOE_STATIC_WS_BYTES, i.e. moe_layer_forward_workspace_bytes(layer, T, k)
+ *     > MOE_STATIC_WS_BYTES (at H 6144, I 2048, E 256, k 8: batches of up to
+ *     T = 138 tokens fit).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (two streams, two threads) race and give unspecified
+ *     results; calls ordered on one stream are safe.  The array keeps the
+ *     last call's contents; nothing in it needs to start at zero (each call
+ *     writes every byte it reads before reading it).
+ */
+#define MOE_STATIC_WS_BYTES (32u << 20)
+int moe_layer_forward_static(const moe_qlayer* layer, const uint16_t* x_bf16, const float* logits,
+                             int64_t T, int32_t k, const float* y_shared, int32_t* topk_ids,
+                             float* topk_w, float* out, void* stream);
+
+/*
  * moe_layer_forward_shared -- moe_shared_ffn followed by moe_layer_forward
  * with its output as y_shared, in one call: out = (the routed layer's gated
  * sum) + the shared expert's FFN of every token.
