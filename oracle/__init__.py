@@ -32,10 +32,12 @@ Parity status per function (what pins each one is in tests/test_oracle_*.py):
   vq_dequant, vq8_dequant, route_topk, permute, expert_ffn, combine,
   combine_shared, forward, hadamard, rotate, unrotate, rotate_weights,
   unrotate_weights, nvfp4_residual_quantize, nvfp4r_dequant,
-  bf16_bits_to_f64, f16_bits_to_f64
+  bf16_bits_to_f64, f16_bits_to_f64, vq8_rate_dequant
   -- all pinned.  vq8_dequant's arithmetic is pinned; its code shape (M
   8-bit codes per 8-weight group into M 256-entry codebooks whose rows are
-  summed) is a reading the pages do not fix: parity unpinned for the shape.
+  summed) is a reading the pages do not fix: parity unpinned for the shape;
+  so is vq8_rate_dequant's reading that an expert at rate m uses the first
+  m of the layer's shared codebooks.
 """
 
 from .formats import (  # noqa: F401
@@ -50,6 +52,7 @@ from .formats import (  # noqa: F401
     nvfp4r_dequant,
     vq_dequant,
     vq8_dequant,
+    vq8_rate_dequant,
     bf16_bits_to_f64,
     f16_bits_to_f64,
 )

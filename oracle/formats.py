@@ -283,3 +283,26 @@ def vq8_dequant(codes, scales_f16, codebooks_f16):
             raise ValueError("codebook must be [256, 8]")
         acc += C[codes[:, :, m].astype(np.int64)]
     return (S[:, None, None] * acc).reshape(n, g * 8)
+
+
+def vq8_rate_dequant(codes, scales_f16, layer_codebooks_f16):
+    """An expert of rate m in a layer of small-codebook VQ experts at mixed
+    rates: W[o, 8g + j] = S[o] * sum_{i<m} C_i[code[o, g, i], j], with m =
+    codes.shape[2] (1, 2 or 3 codes per group, m bits per weight) and C_i the
+    i-th of the layer's codebooks for this projection.
+
+    (GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw, "What it is": one layer's modules
+    run at 1, 2 and 3 bits, chosen per module by a loss-aware allocation,
+    each indexing shared codebooks.)  Reading: the layer keeps up to three
+    256 x 8 codebooks per projection, shared by every expert of the layer,
+    and an expert at rate m uses the first m of them; rates are per expert
+    (all three projections of an expert at one rate).
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    if codes.ndim != 3 or not 1 <= codes.shape[2] <= 3:
+        raise ValueError("codes must be [n, kin/8, m] with m = 1, 2 or 3")
+    m = codes.shape[2]
+    if len(layer_codebooks_f16) < m:
+        raise ValueError("the layer holds fewer codebooks than the expert's rate")
+    return vq8_dequant(codes, scales_f16, list(layer_codebooks_f16)[:m])
+

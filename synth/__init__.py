@@ -56,6 +56,13 @@ FMT_VQ = 2
 FMT_VQ8 = 3
 FMT_BF16 = 4
 FMT_NVFP4R = 5      # nested two-level NVFP4 (base plane + residual plane)
+FMT_VQ8_M1 = 6      # small-codebook VQ at an explicit rate: 1, 2 or 3 codes
+FMT_VQ8_M2 = 7      # (bits per weight) per 8-weight group
+FMT_VQ8_M3 = 8
+# the share of each VQ rate among a layer's experts: the module counts of the
+# 1-, 2- and 3-bit modules of "GLM-5.2 mixed-bit VQ (AQLM) ~1.90 bpw", What it
+# is (every module is one projection of one expert; here one rate per expert)
+VQ8_RATE_COUNTS = (29456, 12441, 15703)
 NVFP4R_SHIFT = 8    # residual-plane exponent of the nested layers
 
 
@@ -95,8 +102,9 @@ class Workload:
     I: int
     T: tuple
     fmt: str            # "nvfp4", "vq", "vq8", "bf16", "mixed" (NVFP4 + VQ), "mixed3"
-                        # (+ VQ8), "nv_bf16" (NVFP4 + BF16) or "nested" (NVFP4 base
-                        # tier, some experts lifted to two-level NVFP4)
+                        # (+ VQ8), "nv_bf16" (NVFP4 + BF16), "nested" (NVFP4 base
+                        # tier, some experts lifted to two-level NVFP4) or "vqmix"
+                        # (small-codebook VQ experts at 1, 2 and 3 bits per weight)
     logits: str         # "normal", "uniform", "zipf" or "hot"
     weight_cfg: int = 1     # seed slot of the NVFP4 weights
     vq_cfg: int = 3         # seed slot of the VQ codes/codebooks/scales
@@ -124,6 +132,11 @@ VQ2X8 = Workload("vq2x8", 6, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=
 # the 3-bit module: three uint8 codes per group into three 256-entry codebooks
 VQ3X8 = Workload("vq3x8", 8, 256, 8, 6144, 2048, (8,), "vq8", "uniform", vq_cfg=8, vq8_m=3)
 
+# small-codebook VQ experts at mixed rates (1, 2 and 3 bits per weight, in the
+# proportions of the page's module counts), three shared codebooks per
+# projection, T = 8
+VQMIX = Workload("vqmix", 10, 256, 8, 6144, 2048, (8,), "vqmix", "uniform", vq_cfg=10, vq8_m=3)
+
 # the NVFP4 decode and prefill layers with a BF16 shared expert of the same
 # intermediate size (the routed experts, routing and tokens are those of
 # DECODE / PREFILL: same seed slots)
@@ -142,7 +155,7 @@ PREFILL_SHARED = Workload("prefill_shared", 2, 256, 8, 6144, 2048, (4096,), "nvf
                           zipf_s=1.1, shared=True)
 
 WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED, VQ1, VQ2X8, VQ3X8, DECODE_SHARED,
-                                 PREFILL_SHARED, DECODE_ROT, NESTED)}
+                                 PREFILL_SHARED, DECODE_ROT, NESTED, VQMIX)}
 
 
 def small_workload(name, E, k, H, I, T, fmt="nvfp4", logits="normal", cfg=100,
@@ -311,23 +324,34 @@ def shared_weights_bf16(wl, proj):
     return f32_to_bf16_bits(z * np.float32(0.02))
 
 
+def vq8_rate(wl, expert):
+    """Codes per 8-weight group of a small-codebook VQ expert: its explicit
+    rate in a mixed-rate layer, else the layer's vq8_m."""
+    if wl.fmt == "vqmix":
+        return int(tier_map(wl)[expert]) - FMT_VQ8_M1 + 1
+    return wl.vq8_m
+
+
 def vq8_codes(wl, expert, proj):
     """Uniform uint8 codes [n, kin/8, M] of one projection of one expert
-    (small-codebook VQ, M = wl.vq8_m codes per 8-weight group)."""
+    (small-codebook VQ, M = the expert's codes per 8-weight group)."""
     n, kin = proj_shape(wl, proj)
     return rng(wl.vq_cfg, KIND_VQ8_CODES, expert, proj).integers(
-        0, 256, size=(n, kin // 8, wl.vq8_m), dtype=np.uint8)
+        0, 256, size=(n, kin // 8, vq8_rate(wl, expert)), dtype=np.uint8)
 
 
 def vq8_codebooks(wl, proj):
-    """The M fp16 codebooks [256, 8] of one projection type, shared by all the
-    layer's experts; entries ~ N(0, 0.02 / sqrt(M)) so that a summed row has
-    the spread of the 2-bit codebook's; uint16 bits."""
+    """The fp16 codebooks [256, 8] of one projection type, shared by all the
+    layer's experts: M = wl.vq8_m of them (an expert at rate m reads the first
+    m); entries ~ N(0, 0.02 / sqrt(M)) so that a summed row has the spread of
+    the 2-bit codebook's (N(0, 0.02 / sqrt(2)) in a mixed-rate layer, the
+    middle rate's); uint16 bits."""
     M = wl.vq8_m
+    sd = 0.02 / np.sqrt(2 if wl.fmt == "vqmix" else M)
     out = []
     for m in range(M):
         c = rng(wl.vq_cfg, KIND_VQ8_CODEBOOK, m, proj).standard_normal(
-            (256, 8), dtype=np.float32) * np.float32(0.02 / np.sqrt(M))
+            (256, 8), dtype=np.float32) * np.float32(sd)
         out.append(f32_to_f16_bits(c))
     return out
 
@@ -360,6 +384,19 @@ def tier_map(wl):
         return np.full(wl.E, FMT_VQ, dtype=np.uint8)
     if wl.fmt == "vq8":
         return np.full(wl.E, FMT_VQ8, dtype=np.uint8)
+    if wl.fmt == "vqmix":
+        # rates 1, 2, 3 over a seeded permutation of the experts, in the
+        # proportions of the page's module counts (largest remainders)
+        share = np.array(VQ8_RATE_COUNTS, np.float64) / sum(VQ8_RATE_COUNTS)
+        n = np.floor(share * wl.E).astype(np.int64)
+        rem = share * wl.E - n
+        n[np.argsort(-rem, kind="stable")[: wl.E - int(n.sum())]] += 1
+        perm = rng(wl.cfg, KIND_TIER).permutation(wl.E)
+        tm = np.empty(wl.E, dtype=np.uint8)
+        tm[perm[: n[0]]] = FMT_VQ8_M1
+        tm[perm[n[0]: n[0] + n[1]]] = FMT_VQ8_M2
+        tm[perm[n[0] + n[1]:]] = FMT_VQ8_M3
+        return tm
     if wl.fmt == "nested":
         # the hot experts (or n_nvfp4 seeded ones) on the two-level tier
         tm = np.full(wl.E, FMT_NVFP4, dtype=np.uint8)

@@ -31,6 +31,10 @@ def expert_weights(wl, e, fmt=None):
         elif fmt == synth.FMT_VQ8:
             mats.append(oracle.vq8_dequant(synth.vq8_codes(wl, e, p), synth.vq_scales(wl, e, p),
                                            synth.vq8_codebooks(wl, p)))
+        elif fmt in (synth.FMT_VQ8_M1, synth.FMT_VQ8_M2, synth.FMT_VQ8_M3):
+            mats.append(oracle.vq8_rate_dequant(synth.vq8_codes(wl, e, p),
+                                                synth.vq_scales(wl, e, p),
+                                                synth.vq8_codebooks(wl, p)))
         else:
             mats.append(oracle.vq_dequant(synth.vq_codes(wl, e, p), synth.vq_scales(wl, e, p),
                                           synth.vq_codebook(wl, p)))

@@ -493,3 +493,69 @@ def test_vq8_three_codebooks_recover_all_codes():
     parts = [oracle.vq8_dequant(codes[:, :, j:j + 1], one, [cb][:1])
              for j, cb in enumerate([cb0, cb1, _f16(cb2)])]
     assert np.array_equal(W.reshape(5, 48), parts[0] + parts[1] + parts[2])
+
+
+# ------------------------------------------- small-codebook VQ at mixed rates
+
+def _rate_books(rs, scale=0.01):
+    return [_f16(rs.standard_normal((256, 8)) * scale) for _ in range(3)]
+
+
+def test_vq8_rate_uses_the_first_m_codebooks_only():
+    """An expert at rate m reads codebooks 0..m-1 of the layer: changing the
+    others leaves its weights unchanged, changing one it reads does not."""
+    rs = np.random.default_rng(21)
+    books = _rate_books(rs)
+    other = _rate_books(rs)
+    sc = _f16(rs.uniform(0.5, 1.5, 6))
+    for m in (1, 2, 3):
+        codes = rs.integers(0, 256, size=(6, 5, m), dtype=np.uint8)
+        W = oracle.vq8_rate_dequant(codes, sc, books)
+        swapped = books[:m] + other[m:]
+        assert np.array_equal(W, oracle.vq8_rate_dequant(codes, sc, swapped)), m
+        changed = list(books)
+        changed[m - 1] = other[m - 1]
+        assert not np.array_equal(W, oracle.vq8_rate_dequant(codes, sc, changed)), m
+
+
+def test_vq8_rates_nest():
+    """A rate-(m+1) expert is the rate-m expert of its first m codes plus the
+    one-code lookup of its last code in codebook m (exact for these ranges)."""
+    rs = np.random.default_rng(22)
+    books = _rate_books(rs)
+    one = _f16(np.ones(4))
+    codes = rs.integers(0, 256, size=(4, 7, 3), dtype=np.uint8)
+    for m in (1, 2):
+        hi = oracle.vq8_rate_dequant(codes[:, :, :m + 1], one, books)
+        lo = oracle.vq8_rate_dequant(codes[:, :, :m], one, books)
+        last = oracle.vq8_dequant(codes[:, :, m:m + 1], one, [books[m]])
+        assert np.array_equal(hi, lo + last), m
+
+
+def test_vq8_rate_identity_codebooks_recover_codes():
+    """Codebooks C_0[c] = 1024 (c % 16), C_1[c] = 32 (c % 16), C_2[c] = c % 16
+    (every sum exact in fp16): each rate gives back all of its codes from the
+    summed row, and a rate-1 expert is the plain lookup."""
+    c = np.arange(256, dtype=np.float64) % 16
+    books = [_f16(np.repeat((f * c)[:, None], 8, axis=1)) for f in (1024.0, 32.0, 1.0)]
+    rs = np.random.default_rng(23)
+    for m in (1, 2, 3):
+        codes = rs.integers(0, 16, size=(5, 6, m), dtype=np.uint8)
+        W = oracle.vq8_rate_dequant(codes, _f16(np.ones(5)), books).reshape(5, 6, 8)
+        v = W[:, :, 0].astype(np.int64)
+        for i, f in enumerate((1024, 32, 1)[:m]):
+            assert np.array_equal((v // f) % 32 if f > 1 else v % 32, codes[:, :, i]), (m, i)
+    cb = books[0]
+    codes = rs.integers(0, 256, size=(3, 4, 1), dtype=np.uint8)
+    sc = _f16([2.0, 0.5, 1.0])
+    assert np.array_equal(oracle.vq8_rate_dequant(codes, sc, books),
+                          oracle.vq_dequant(codes[:, :, 0].astype(np.uint16), sc, cb))
+
+
+def test_vq8_rate_rejects_bad_rates():
+    books = [_f16(np.zeros((256, 8)))] * 2
+    with pytest.raises(ValueError):
+        oracle.vq8_rate_dequant(np.zeros((2, 3, 3), np.uint8), _f16(np.ones(2)), books)
+    with pytest.raises(ValueError):
+        oracle.vq8_rate_dequant(np.zeros((2, 3, 4), np.uint8), _f16(np.ones(2)), books * 2)
+
