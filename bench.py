@@ -288,8 +288,9 @@ class Runner:
             if self.layer.fmt_host[e] in (self.moeq.FMT_NVFP4, self.moeq.FMT_NVFP4R):
                 planes = 2 if self.layer.fmt_host[e] == self.moeq.FMT_NVFP4R else 1
                 tot += planes * 2 * (H * I // 2 + H * I // 16)
-            elif self.layer.fmt_host[e] == self.moeq.FMT_VQ8:
-                tot += 2 * (H * I // 8) * self.layer.vq8_m + 2 * I * 2
+            elif self.moeq.vq8_rate(int(self.layer.fmt_host[e]), self.layer.vq8_m):
+                m = self.moeq.vq8_rate(int(self.layer.fmt_host[e]), self.layer.vq8_m)
+                tot += 2 * (H * I // 8) * m + 2 * I * 2
             else:
                 tot += 2 * (H * I // 8) * 2 + 2 * I * 2
         return tot
@@ -509,6 +510,7 @@ def main():
     ap.add_argument("--T", type=int, default=32, help="decode batch of the headline")
     ap.add_argument("--extra",
                     default="decode1,decode8,prefill,vq,vqprefill,vq1,vq2x8,vq3x8,vq2x8prefill,"
+                            "vqmix,vqmixprefill,"
                             "mixed8,mixed32,mixedhot8,"
                             "mixedhot32,nested8,nested32,shared1,shared8,shared32,prefillshared,"
                             "rot1,rot8,rot32,"
@@ -642,7 +644,8 @@ def main():
                     extra[name] = measure(layers["vq"], wp, 4096, 3, 1, dev, reps=4)
                 else:
                     extra[name] = measure(layers["vq"], wq, 8, 30, 5, dev)
-            elif name in ("vq1", "vq2x8", "vq3x8", "vq1prefill", "vq2x8prefill", "vq3x8prefill"):
+            elif name in ("vq1", "vq2x8", "vq3x8", "vq1prefill", "vq2x8prefill", "vq3x8prefill",
+                          "vqmix", "vqmixprefill"):
                 w8 = synth.WORKLOADS[name.replace("prefill", "")]
                 log(f"building the small-codebook VQ layer {name} ...")
                 lay8 = build_layer(
@@ -652,7 +655,7 @@ def main():
                     device=dev, workers=16)
                 if name.endswith("prefill"):
                     # the same layer at T = 4096 with the prefill routing
-                    wp = synth.Workload(name, 2, w8.E, w8.k, w8.H, w8.I, (4096,), "vq8", "zipf",
+                    wp = synth.Workload(name, 2, w8.E, w8.k, w8.H, w8.I, (4096,), w8.fmt, "zipf",
                                         zipf_s=1.1, vq_cfg=w8.vq_cfg, vq8_m=w8.vq8_m)
                     extra[name] = measure(lay8, wp, 4096, 3, 1, dev, reps=4)
                 else:

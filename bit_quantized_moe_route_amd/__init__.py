@@ -38,7 +38,19 @@ FMT_VQ = 2
 FMT_VQ8 = 3
 FMT_BF16 = 4
 FMT_NVFP4R = 5      # nested two-level NVFP4: base plane + residual plane
-FORMATS = (FMT_NVFP4, FMT_VQ, FMT_VQ8, FMT_BF16, FMT_NVFP4R)
+FMT_VQ8_M1, FMT_VQ8_M2, FMT_VQ8_M3 = 6, 7, 8   # small-codebook VQ at 1 / 2 / 3 bits
+FMT_VQ8_RATES = (FMT_VQ8_M1, FMT_VQ8_M2, FMT_VQ8_M3)
+FORMATS = (FMT_NVFP4, FMT_VQ, FMT_VQ8, FMT_BF16, FMT_NVFP4R) + FMT_VQ8_RATES
+
+
+def vq8_rate(fmt, vq8_m):
+    """Codes per 8-weight group of a small-codebook VQ format (vq8_m for
+    FMT_VQ8), 0 for other formats."""
+    if fmt == FMT_VQ8:
+        return vq8_m
+    if fmt in FMT_VQ8_RATES:
+        return fmt - FMT_VQ8_M1 + 1
+    return 0
 REC_COMPACT, REC_RESIDENT = 0, 1
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 VQ_NCODE = 65536
@@ -74,6 +86,8 @@ class _QLayerC(ctypes.Structure):
         ("nvfp4r_w13", ctypes.c_void_p), ("nvfp4r_w13_stride", ctypes.c_int64),
         ("nvfp4r_w2", ctypes.c_void_p), ("nvfp4r_w2_stride", ctypes.c_int64),
         ("nvfp4r_shift", ctypes.c_int32), ("reserved2", ctypes.c_int32),
+        ("vq8r_w13", ctypes.c_void_p * 3), ("vq8r_w13_stride", ctypes.c_int64 * 3),
+        ("vq8r_w2", ctypes.c_void_p * 3), ("vq8r_w2_stride", ctypes.c_int64 * 3),
     ]
 
 
@@ -375,6 +389,9 @@ class QLayer:
         self.counts = counts
         if sizes[FMT_VQ8] and vq8_m not in (1, 2, 3):
             raise ValueError("a layer with small-codebook VQ experts needs vq8_m = 1, 2 or 3")
+        # the layer's small codebooks per projection: as many as its largest rate
+        self.vq8_ncb = max([vq8_m if sizes[FMT_VQ8] else 0]
+                           + [vq8_rate(f, 0) for f in FMT_VQ8_RATES if sizes[f]])
         self.vq8_m = int(vq8_m)
         self.nvfp4r_shift = int(nvfp4r_shift)
         self.rec_host = rec
@@ -462,15 +479,17 @@ class QLayer:
         self._c = None
 
     def set_codebooks8(self, cbs):
-        """Small-codebook VQ: for gate, up and down, a list of vq8_m uint16
-        arrays [256, 8] (fp16 bits), codebook 0 first."""
+        """Small-codebook VQ: for gate, up and down, a list of uint16 arrays
+        [256, 8] (fp16 bits), codebook 0 first: as many as the layer's largest
+        rate (vq8_m, or the largest explicit rate); an expert at rate m reads
+        the first m."""
         torch = _torch()
         out = []
         for books in cbs:
-            if len(books) != self.vq8_m:
-                raise ValueError("vq8_m codebooks per projection")
+            if len(books) != self.vq8_ncb:
+                raise ValueError(f"{self.vq8_ncb} codebooks per projection (the largest rate)")
             a = np.ascontiguousarray(np.concatenate([np.asarray(b, dtype=np.uint16) for b in books]))
-            if a.shape != (self.vq8_m * VQ8_NCODE, 8):
+            if a.shape != (self.vq8_ncb * VQ8_NCODE, 8):
                 raise ValueError("codebooks must be [256, 8] each")
             out.append(torch.from_numpy(a.view(np.int16)).to(self.device))
         self.codebooks8 = out
@@ -507,6 +526,12 @@ class QLayer:
                 setattr(d, n2, p2.data_ptr() if p2 is not None else None)
                 setattr(d, n13 + "_stride", self.stride[(fmt, 0)])
                 setattr(d, n2 + "_stride", self.stride[(fmt, 1)])
+            for i, fmt in enumerate(FMT_VQ8_RATES):
+                p13, p2 = self.pools[(fmt, 0)], self.pools[(fmt, 1)]
+                d.vq8r_w13[i] = p13.data_ptr() if p13 is not None else None
+                d.vq8r_w2[i] = p2.data_ptr() if p2 is not None else None
+                d.vq8r_w13_stride[i] = self.stride[(fmt, 0)]
+                d.vq8r_w2_stride[i] = self.stride[(fmt, 1)]
             for p in range(3):
                 cb = self.codebooks[p]
                 d.vq_codebook[p] = cb.data_ptr() if cb is not None else None
@@ -531,9 +556,10 @@ class QLayer:
                 tot += planes * 3 * (self.H * self.I // 2 + self.H * self.I // 16)
             elif self.fmt_host[e] == FMT_BF16:
                 tot += 3 * self.H * self.I * 2
-            elif self.fmt_host[e] == FMT_VQ8:
+            elif self.fmt_host[e] == FMT_VQ8 or self.fmt_host[e] in FMT_VQ8_RATES:
                 vq8 = True
-                tot += 3 * (self.H * self.I // 8) * self.vq8_m + (2 * self.I + self.H) * 2
+                m = vq8_rate(int(self.fmt_host[e]), self.vq8_m)
+                tot += 3 * (self.H * self.I // 8) * m + (2 * self.I + self.H) * 2
             else:
                 vq = True
                 vq_books += 1
@@ -542,7 +568,7 @@ class QLayer:
             # one shared codebook per projection, or each touched record's own
             tot += 3 * VQ_NCODE * 8 * 2 * (1 if self.codebook_stride == 0 else vq_books)
         if vq8:
-            tot += 3 * self.vq8_m * VQ8_NCODE * 8 * 2
+            tot += 3 * self.vq8_ncb * VQ8_NCODE * 8 * 2
         return tot
 
 

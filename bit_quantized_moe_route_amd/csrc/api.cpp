@@ -81,6 +81,13 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     v.pool2[MOE_FMT_BF16] = static_cast<const uint8_t*>(L->bf16_w2);
     v.stride13[MOE_FMT_BF16] = L->bf16_w13_stride;
     v.stride2[MOE_FMT_BF16] = L->bf16_w2_stride;
+    for (int m = 1; m <= MOE_VQ8_MAX_M; ++m) {
+        const int f = MOE_FMT_VQ8_M1 + m - 1;
+        v.pool13[f] = static_cast<const uint8_t*>(L->vq8r_w13[m - 1]);
+        v.pool2[f] = static_cast<const uint8_t*>(L->vq8r_w2[m - 1]);
+        v.stride13[f] = L->vq8r_w13_stride[m - 1];
+        v.stride2[f] = L->vq8r_w2_stride[m - 1];
+    }
     v.pool13[MOE_FMT_NVFP4R] = static_cast<const uint8_t*>(L->nvfp4r_w13);
     v.pool2[MOE_FMT_NVFP4R] = static_cast<const uint8_t*>(L->nvfp4r_w2);
     v.stride13[MOE_FMT_NVFP4R] = L->nvfp4r_w13_stride;
@@ -105,19 +112,21 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
         return fail(MOE_EUNSUPPORTED, f + ": vq8_m must be 1, 2 or 3");
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!out.count[fmt]) continue;
-        const char* name = fmt == MOE_FMT_NVFP4  ? "NVFP4"
-                           : fmt == MOE_FMT_VQ   ? "VQ"
-                           : fmt == MOE_FMT_VQ8  ? "VQ8"
-                           : fmt == MOE_FMT_BF16 ? "BF16"
-                                                 : "NVFP4R";
+        const char* name = fmt == MOE_FMT_NVFP4     ? "NVFP4"
+                           : fmt == MOE_FMT_VQ      ? "VQ"
+                           : fmt == MOE_FMT_VQ8     ? "VQ8"
+                           : fmt == MOE_FMT_BF16    ? "BF16"
+                           : fmt == MOE_FMT_NVFP4R  ? "NVFP4R"
+                           : fmt == MOE_FMT_VQ8_M1  ? "VQ8 (1 bit)"
+                           : fmt == MOE_FMT_VQ8_M2  ? "VQ8 (2 bits)"
+                                                    : "VQ8 (3 bits)";
         if (!v.pool13[fmt] || !v.pool2[fmt])
             return fail(MOE_EINVAL, f + ": " + name + " experts present but their pool is NULL");
-        const int64_t b13 = fmt == MOE_FMT_VQ8
-                                ? (int64_t)moe_record_bytes_vq8(0, L->H, L->I, L->vq8_m)
-                                : (int64_t)moe_record_bytes(fmt, 0, L->H, L->I);
-        const int64_t b2 = fmt == MOE_FMT_VQ8
-                               ? (int64_t)moe_record_bytes_vq8(1, L->H, L->I, L->vq8_m)
-                               : (int64_t)moe_record_bytes(fmt, 1, L->H, L->I);
+        const int rate = is_vq8(fmt) ? vq8_rate(fmt, L->vq8_m) : 0;
+        const int64_t b13 = is_vq8(fmt) ? (int64_t)moe_record_bytes_vq8(0, L->H, L->I, rate)
+                                        : (int64_t)moe_record_bytes(fmt, 0, L->H, L->I);
+        const int64_t b2 = is_vq8(fmt) ? (int64_t)moe_record_bytes_vq8(1, L->H, L->I, rate)
+                                       : (int64_t)moe_record_bytes(fmt, 1, L->H, L->I);
         if (v.stride13[fmt] < b13 || v.stride2[fmt] < b2 || v.stride13[fmt] % 256 ||
             v.stride2[fmt] % 256)
             return fail(MOE_EINVAL, f + ": " + name +
@@ -130,7 +139,9 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
         if (v.cb_stride < 0 || (v.cb_stride && v.cb_stride < (int64_t)MOE_VQ_NCODE * 16))
             return fail(MOE_EINVAL, f + ": bad vq_codebook_stride");
     }
-    if (out.count[MOE_FMT_VQ8])
+    int n_vq8 = 0;
+    for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) n_vq8 += is_vq8(fmt) ? out.count[fmt] : 0;
+    if (n_vq8)
         for (int p = 0; p < 3; ++p)
             if (!v.cb8[p]) return fail(MOE_EINVAL, f + ": VQ8 experts present but a codebook is NULL");
     return MOE_OK;

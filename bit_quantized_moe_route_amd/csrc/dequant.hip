@@ -153,16 +153,17 @@ int launch_dequant(const LayerView& L, int fmt, int32_t ridx, int32_t proj, floa
     } else if (fmt == MOE_FMT_BF16) {
         dim3 grid((unsigned)(n / 16), (unsigned)bf16_tiles_k(kin));
         k_dequant_bf16<<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, out);
-    } else if (fmt == MOE_FMT_VQ8) {
+    } else if (is_vq8(fmt)) {
+        const int m = vq8_rate(fmt, L.vq8_m);
         const int64_t nkb = vq_tiles_k(kin);
         const int groups = down ? L.H / 16 : 2 * (L.I / 16);
-        const int64_t tb = (int64_t)kVq8TileBytesPerCode * L.vq8_m;
+        const int64_t tb = (int64_t)kVq8TileBytesPerCode * m;
         const _Float16* sc = reinterpret_cast<const _Float16*>(rec + (int64_t)groups * nkb * tb);
         if (proj == MOE_PROJ_UP) sc += L.I;
         dim3 grid((unsigned)(n / 16), (unsigned)nkb);
-        if (L.vq8_m == 1)
+        if (m == 1)
             k_dequant_vq8<1><<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, L.cb8[proj], sc, out);
-        else if (L.vq8_m == 3)
+        else if (m == 3)
             k_dequant_vq8<3><<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, L.cb8[proj], sc, out);
         else
             k_dequant_vq8<2><<<grid, 64, 0, s>>>(rec, rg_step, rg_off, n, kin, L.cb8[proj], sc, out);

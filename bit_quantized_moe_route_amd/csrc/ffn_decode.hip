@@ -40,9 +40,12 @@ struct NvFmt {
     static constexpr int TB = kNvTileBytes;   // bytes per tile
     static constexpr int STEPS = 4;           // MFMA K-steps per tile
     static constexpr int KSPAN = 32;          // inputs per lane per tile
+    // The two scale bytes are held as the 16-bit value the load returns: a
+    // 32-bit field makes the compiler zero-extend it right after the load,
+    // inside the conditional prefetch, which waits for the prefetch to land.
     struct Frag {
         u32x4 codes;
-        uint32_t scales;
+        uint16_t scales;
     };
     __device__ __forceinline__ static void load(Frag& fr, const uint8_t* tile, int lane) {
         fr.codes = load_stream16(tile + lane * 16);
@@ -168,22 +171,23 @@ __device__ __forceinline__ f16x8 act_f16(u32x4 v) {
         return __builtin_bit_cast(f16x8, v);
 }
 
-// B operand fragments of one tile for the first `ntt` of NTT token tiles:
-// lane L holds token (L & 15) + 16 tt, inputs k0 + 8 s .. +7 with
-// k0 = kb*TK + (L>>4)*KSPAN.
+// B operand fragments of one tile for the NTT token tiles: lane L holds
+// token (L & 15) + 16 tt, inputs k0 + 8 s .. +7 with k0 = kb*TK + (L>>4)*KSPAN.
+// Every lane loads, always from a valid address, so that no load sits on a
+// branch (a load on a branch makes the compiler wait for all loads in flight
+// before the next use, which defeats the prefetch): rows past the expert's
+// rows come in as a valid row of it (xrow holds one; their output columns are
+// never stored) and inputs past K as inputs K-8..K-1 of the row (the weights
+// of those inputs are zero codes, so their products are zero).
 template <class F, int NTT>
-__device__ __forceinline__ void load_b(const uint16_t* const xrow[NTT], int ntt, int k0, int K,
+__device__ __forceinline__ void load_b(const uint16_t* const xrow[NTT], int k0, int K,
                                        u32x4 b[NTT][F::STEPS]) {
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-        if (tt >= ntt) break;
 #pragma unroll
         for (int s = 0; s < F::STEPS; ++s) {
-            const int kk = k0 + 8 * s;
-            if (xrow[tt] != nullptr && kk < K)
-                b[tt][s] = *reinterpret_cast<const u32x4*>(xrow[tt] + kk);
-            else
-                b[tt][s] = u32x4{0u, 0u, 0u, 0u};
+            const int kk = min(k0 + 8 * s, K - 8);
+            b[tt][s] = *reinterpret_cast<const u32x4*>(xrow[tt] + kk);
         }
     }
 }
@@ -237,10 +241,13 @@ __device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
     const int nkb = tiles_k<F>(K);
     const int ksub = (lane >> 4) * F::KSPAN;
     const int niter = kpart < nkb ? (nkb - kpart + KS - 1) / KS : 0;   // tiles of this wave
+    if (niter == 0) return;
     typename F::Frag wr[D + 1][NM];
     u32x4 br[D + 1][NTT][F::STEPS];
+    // the loads of tile i; past the last tile the last one is loaded again
+    // (from the caches; never used), so that the prefetch is not on a branch
     auto issue = [&](int i, typename F::Frag (&w)[NM], u32x4 (&b)[NTT][F::STEPS]) {
-        const int kb = kpart + i * KS;
+        const int kb = kpart + min(i, niter - 1) * KS;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             if constexpr (F::PLANES == 2)
@@ -248,17 +255,19 @@ __device__ __forceinline__ void stream_tiles(const uint8_t* const tbase[NM],
             else
                 F::load(w[m], tbase[m] + (int64_t)kb * F::TB, lane);
         }
-        load_b<F, NTT>(xrow, ntt, kb * F::TK + ksub, K, b);
+        load_b<F, NTT>(xrow, kb * F::TK + ksub, K, b);
     };
 #pragma unroll
-    for (int u = 0; u < D; ++u)
-        if (u < niter) issue(u, wr[u], br[u]);
-    for (int it = 0; it < niter; it += D + 1) {
+    for (int u = 0; u < D; ++u) issue(u, wr[u], br[u]);
+    // the trip count rounded up to the unroll: every pass issues its loads,
+    // only the decode and the products are skipped past the last tile
+    const int nround = (niter + D) / (D + 1) * (D + 1);
+    for (int it = 0; it < nround; it += D + 1) {
 #pragma unroll
         for (int u = 0; u <= D; ++u) {
             const int i = it + u;
-            if (i >= niter) break;
-            if (i + D < niter) issue(i + D, wr[(u + D) % (D + 1)], br[(u + D) % (D + 1)]);
+            issue(i + D, wr[(u + D) % (D + 1)], br[(u + D) % (D + 1)]);
+            if (i >= niter) continue;
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 if constexpr (F::PLANES == 2) {
@@ -412,15 +421,33 @@ __device__ __forceinline__ void stream_tiles_vq8(const uint8_t* const tbase[NM],
                 for (int q = 0; q < 4; ++q) c[m][q] = v[q];
             }
         }
-        load_b<F, NTT>(xrow, ntt, kb * F::TK + ksub, K, b);
+        load_b<F, NTT>(xrow, kb * F::TK + ksub, K, b);
     };
-    if (niter > 0) issue(0, cw[0], br[0]);
-    for (int it = 0; it < niter; it += 2) {
+    if (niter == 0) return;
+    issue(0, cw[0], br[0]);
+    // the trip count rounded up to the unroll; past the last tile the last
+    // one is loaded again (never used): no load on a branch
+    const int nround = (niter + 1) / 2 * 2;
+    for (int it = 0; it < nround; it += 2) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int i = it + u;
-            if (i >= niter) break;
-            if (i + 1 < niter) issue(i + 1, cw[u ^ 1], br[u ^ 1]);
+            issue(min(i + 1, niter - 1), cw[u ^ 1], br[u ^ 1]);
+            if (i >= niter) continue;
+            {
+                // the tile holding the end of K: its groups past K carry zero
+                // codes, which still select a codebook row, so their
+                // activations are zeroed here (after the wait, not at the load)
+                const int kb = kpart + i * KS;
+                if (kb * F::TK + F::TK > K) {
+                    const int k0 = kb * F::TK + ksub;
+#pragma unroll
+                    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                        for (int s = 0; s < F::STEPS; ++s)
+                            if (k0 + 8 * s >= K) br[u][tt][s] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -573,12 +600,15 @@ __device__ __forceinline__ void ffn_body(const DecodeArgs& A, const uint3 bid) {
                            : A.cb_down + (int64_t)ae.ridx * A.cb_stride;
     }
 
+    // B rows of the lanes' tokens; a lane past the expert's rows takes row c0
+    // (its output column is never stored)
     const uint16_t* xrow[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-        const int c = c0 + (lane & 15) + 16 * tt;
-        if (c >= ae.me)
-            xrow[tt] = nullptr;
+        const int c0l = c0 + (lane & 15) + 16 * tt;
+        const int c = c0l < ae.me ? c0l : c0;
+        if (F::kVq && !F::kVq8 && c0l >= ae.me)
+            xrow[tt] = nullptr;     // 16-bit VQ: stream_tiles_vq substitutes its safe row
         else if (PHASE == 0)
             xrow[tt] = A.xbf + (int64_t)(ROT     ? ae.r0 + c
                                          : ROUTE ? ae.r0 / A.k
@@ -806,10 +836,18 @@ __device__ __forceinline__ void down_combine_body(const DecodeArgs& A, const uin
         cb[m] = A.cb_down + (int64_t)e * A.cb_stride;
     }
     const int col = lane & 15;                     // B column = slot j0 + col
+    // columns past the live slots read the last live slot's h row (those
+    // columns are never part of the sum)
     const uint16_t* xrow[1];
-    xrow[0] = col < nsl ? reinterpret_cast<const uint16_t*>(A.h16) +
-                              ((int64_t)t * A.k + j0 + col) * A.I
-                        : nullptr;
+    if constexpr (F::kVq && !F::kVq8) {
+        // 16-bit VQ: stream_tiles_vq substitutes its safe row for NULL
+        xrow[0] = col < nsl ? reinterpret_cast<const uint16_t*>(A.h16) +
+                                  ((int64_t)t * A.k + j0 + col) * A.I
+                            : nullptr;
+    } else {
+        const int cs = col < nsl ? col : nsl - 1;
+        xrow[0] = reinterpret_cast<const uint16_t*>(A.h16) + ((int64_t)t * A.k + j0 + cs) * A.I;
+    }
     f32x4 acc[NM][1];
 #pragma unroll
     for (int m = 0; m < NM; ++m) acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1183,9 +1221,10 @@ int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, cons
     if (fmt == MOE_FMT_NVFP4) return launch_small_fmt<NvFmt>(a, T, s);
     if (fmt == MOE_FMT_NVFP4R) return launch_small_fmt<Nv2Fmt>(a, T, s);
     if (fmt == MOE_FMT_BF16) return launch_small_fmt<Bf16Fmt>(a, T, s);
-    if (fmt == MOE_FMT_VQ8) {
-        if (L.vq8_m == 1) return launch_small_fmt<Vq8Fmt<1>>(a, T, s);
-        if (L.vq8_m == 3) return launch_small_fmt<Vq8Fmt<3>>(a, T, s);
+    if (is_vq8(fmt)) {
+        const int m = vq8_rate(fmt, L.vq8_m);
+        if (m == 1) return launch_small_fmt<Vq8Fmt<1>>(a, T, s);
+        if (m == 3) return launch_small_fmt<Vq8Fmt<3>>(a, T, s);
         return launch_small_fmt<Vq8Fmt<2>>(a, T, s);
     }
     return launch_small_fmt<VqFmt>(a, T, s);
@@ -1208,9 +1247,10 @@ int launch_layer_small_shared(const LayerView& L, int fmt, const LayerView& SL,
     if (fmt == MOE_FMT_NVFP4) return launch_small_shared_fmt<NvFmt>(a, sa, T, s);
     if (fmt == MOE_FMT_NVFP4R) return launch_small_shared_fmt<Nv2Fmt>(a, sa, T, s);
     if (fmt == MOE_FMT_BF16) return launch_small_shared_fmt<Bf16Fmt>(a, sa, T, s);
-    if (fmt == MOE_FMT_VQ8) {
-        if (L.vq8_m == 1) return launch_small_shared_fmt<Vq8Fmt<1>>(a, sa, T, s);
-        if (L.vq8_m == 3) return launch_small_shared_fmt<Vq8Fmt<3>>(a, sa, T, s);
+    if (is_vq8(fmt)) {
+        const int m = vq8_rate(fmt, L.vq8_m);
+        if (m == 1) return launch_small_shared_fmt<Vq8Fmt<1>>(a, sa, T, s);
+        if (m == 3) return launch_small_shared_fmt<Vq8Fmt<3>>(a, sa, T, s);
         return launch_small_shared_fmt<Vq8Fmt<2>>(a, sa, T, s);
     }
     return launch_small_shared_fmt<VqFmt>(a, sa, T, s);
@@ -1228,9 +1268,10 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
     if (fmt == MOE_FMT_NVFP4) return launch_ntt<NvFmt>(a, T, slots, phase, s);
     if (fmt == MOE_FMT_NVFP4R) return launch_ntt<Nv2Fmt>(a, T, slots, phase, s);
     if (fmt == MOE_FMT_BF16) return launch_ntt<Bf16Fmt>(a, T, slots, phase, s);
-    if (fmt == MOE_FMT_VQ8) {
-        if (L.vq8_m == 1) return launch_ntt<Vq8Fmt<1>>(a, T, slots, phase, s);
-        if (L.vq8_m == 3) return launch_ntt<Vq8Fmt<3>>(a, T, slots, phase, s);
+    if (is_vq8(fmt)) {
+        const int m = vq8_rate(fmt, L.vq8_m);
+        if (m == 1) return launch_ntt<Vq8Fmt<1>>(a, T, slots, phase, s);
+        if (m == 3) return launch_ntt<Vq8Fmt<3>>(a, T, slots, phase, s);
         return launch_ntt<Vq8Fmt<2>>(a, T, slots, phase, s);
     }
     return launch_ntt<VqFmt>(a, T, slots, phase, s);
@@ -1246,7 +1287,7 @@ size_t shared_part_bytes(int fmt, int64_t T, int32_t H, int32_t I) {
     if (!MOEQ_SH_PART) return 0;
     const bool known = fmt >= MOE_FMT_NVFP4 && fmt <= MOE_FMT_MAX;
     // input tile of the format (an unknown tag: the smaller tile, the larger split)
-    const int tk = known && (fmt == MOE_FMT_VQ || fmt == MOE_FMT_VQ8) ? kVqTileK : kNvTileK;
+    const int tk = known && (fmt == MOE_FMT_VQ || is_vq8(fmt)) ? kVqTileK : kNvTileK;
     int nblk = 0, nsplit = 1;
     shared_split(H, I, tk, nblk, nsplit);
     return (size_t)nsplit * (size_t)T * 2 * (size_t)I * 4;
@@ -1261,9 +1302,10 @@ int launch_shared_decode(const LayerView& L, int fmt, const uint16_t* x_bf16, in
     if (fmt == MOE_FMT_NVFP4) return launch_shared_fmt<NvFmt>(a, phase, s);
     if (fmt == MOE_FMT_NVFP4R) return launch_shared_fmt<Nv2Fmt>(a, phase, s);
     if (fmt == MOE_FMT_BF16) return launch_shared_fmt<Bf16Fmt>(a, phase, s);
-    if (fmt == MOE_FMT_VQ8) {
-        if (L.vq8_m == 1) return launch_shared_fmt<Vq8Fmt<1>>(a, phase, s);
-        if (L.vq8_m == 3) return launch_shared_fmt<Vq8Fmt<3>>(a, phase, s);
+    if (is_vq8(fmt)) {
+        const int m = vq8_rate(fmt, L.vq8_m);
+        if (m == 1) return launch_shared_fmt<Vq8Fmt<1>>(a, phase, s);
+        if (m == 3) return launch_shared_fmt<Vq8Fmt<3>>(a, phase, s);
         return launch_shared_fmt<Vq8Fmt<2>>(a, phase, s);
     }
     return launch_shared_fmt<VqFmt>(a, phase, s);

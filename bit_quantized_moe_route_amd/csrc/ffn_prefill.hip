@@ -195,7 +195,7 @@ __device__ __forceinline__ WorkItem locate_item(const int32_t* __restrict__ offs
 // (L >> 5) * 64 .. +64 = two 16-byte code chunks and their 4 scales.
 struct AFrag {
     u32x4 c0, c1;
-    uint32_t s0, s1;
+    uint16_t s0, s1;
 };
 
 __device__ __forceinline__ void load_a(AFrag& f, const uint8_t* grp_base, int64_t gstride,
@@ -232,8 +232,11 @@ __device__ __forceinline__ f16x8 a_step(const AFrag& f, int s) {
 // A operand j of K-step s (inputs 64h + 8s .. +7 of the step); kScales: fp16
 // per-row scales follow the record's code tiles; cb_lds(phase): bytes of
 // codebooks the workgroup keeps in LDS; ctx: the lane's codebook base.
+#ifndef MOEQ_PF_NV_BM
+#define MOEQ_PF_NV_BM 64
+#endif
 struct PfNv {
-    static constexpr int BM = 64;
+    static constexpr int BM = MOEQ_PF_NV_BM;
     static constexpr int NA = 2;
     static constexpr int NSUB = 1;
     static constexpr bool kScales = false;
@@ -755,9 +758,14 @@ int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x
         case MOE_FMT_VQ:
             return launch_pf<PfVq, false>(a, tk, act, phase, s);
         case MOE_FMT_VQ8:
-            if (L.vq8_m == 1) return launch_pf<PfVq8<1>, false>(a, tk, act, phase, s);
-            if (L.vq8_m == 3) return launch_pf<PfVq8<3>, false>(a, tk, act, phase, s);
+        case MOE_FMT_VQ8_M1:
+        case MOE_FMT_VQ8_M2:
+        case MOE_FMT_VQ8_M3: {
+            const int m = vq8_rate(fmt, L.vq8_m);
+            if (m == 1) return launch_pf<PfVq8<1>, false>(a, tk, act, phase, s);
+            if (m == 3) return launch_pf<PfVq8<3>, false>(a, tk, act, phase, s);
             return launch_pf<PfVq8<2>, false>(a, tk, act, phase, s);
+        }
         case MOE_FMT_NVFP4R:
             return id ? launch_pf<PfNv2, true>(a, tk, act, phase, s)
                       : launch_pf<PfNv2, false>(a, tk, act, phase, s);

@@ -73,6 +73,14 @@ inline int64_t bf16_matrix_bytes(int32_t n, int32_t kin) {
 
 // Launchers (device code lives in the .hip files) ----------------------------
 constexpr int kNumFmt = MOE_FMT_MAX + 1;   // format tags 1 .. MOE_FMT_MAX
+// Small-codebook VQ at the layer's rate (MOE_FMT_VQ8) or an explicit one.
+inline bool is_vq8(int fmt) {
+    return fmt == MOE_FMT_VQ8 || (fmt >= MOE_FMT_VQ8_M1 && fmt <= MOE_FMT_VQ8_M3);
+}
+// Codes per 8-weight group of a small-codebook VQ format.
+inline int vq8_rate(int fmt, int layer_vq8_m) {
+    return fmt == MOE_FMT_VQ8 ? layer_vq8_m : fmt - MOE_FMT_VQ8_M1 + 1;
+}
 struct LayerView {
     int32_t E, H, I;
     int32_t vq8_m;

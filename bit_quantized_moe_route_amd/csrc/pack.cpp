@@ -243,6 +243,8 @@ size_t moe_record_bytes(int fmt, int which, int32_t H, int32_t I) {
         if (H % 16 || I % 16) return 0;
         return (size_t)bf16_rec_bytes(which, H, I);
     }
+    if (fmt >= MOE_FMT_VQ8_M1 && fmt <= MOE_FMT_VQ8_M3)
+        return moe_record_bytes_vq8(which, H, I, fmt - MOE_FMT_VQ8_M1 + 1);
     return 0;
 }
 

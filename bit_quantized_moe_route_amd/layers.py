@@ -11,7 +11,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from . import (FMT_BF16, FMT_NVFP4, FMT_NVFP4R, FMT_VQ, FMT_VQ8, PROJ_DOWN, PROJ_GATE, PROJ_UP,
+from . import (FMT_BF16, FMT_NVFP4, FMT_NVFP4R, FMT_VQ, FMT_VQ8, FMT_VQ8_RATES, PROJ_DOWN,
+               PROJ_GATE, PROJ_UP, vq8_rate,
                QLayer, pack_bf16_expert, pack_nvfp4_expert, pack_nvfp4r_expert, pack_vq8_expert,
                pack_vq_expert, quantize_nvfp4, quantize_nvfp4_residual)
 
@@ -30,9 +31,10 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         of a VQ expert.
     codebooks: three uint16 arrays (fp16 bits) [65536 * n_books, 8] for gate,
         up, down.
-    vq8_codes(e, proj) -> (codes uint8 [n, kin/8, vq8_m], scales fp16 bits [n])
-        of a small-codebook VQ expert; codebooks8: for gate, up, down a list of
-        vq8_m uint16 arrays [256, 8].
+    vq8_codes(e, proj) -> (codes uint8 [n, kin/8, m], scales fp16 bits [n])
+        of a small-codebook VQ expert (m = vq8_m for FMT_VQ8, the tag's rate
+        for FMT_VQ8_M1..3); codebooks8: for gate, up, down a list of uint16
+        arrays [256, 8], as many as the layer's largest rate.
     bf16_weights(e, proj) -> bf16 bits uint16 [n, kin] of a BF16 expert (a
         routed BF16-tier expert, or the one expert of a shared-expert layer).
     resident_formats: None, or the formats every expert is packed in (slot e of
@@ -80,9 +82,9 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         elif fmt == FMT_BF16:
             parts = [bf16_weights(e, p) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
             w13, w2 = pack_bf16_expert(parts[0], parts[1], parts[2], H, I)
-        elif fmt == FMT_VQ8:
+        elif fmt == FMT_VQ8 or fmt in FMT_VQ8_RATES:
             parts = [vq8_codes(e, p) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
-            w13, w2 = pack_vq8_expert(parts[0], parts[1], parts[2], H, I, vq8_m)
+            w13, w2 = pack_vq8_expert(parts[0], parts[1], parts[2], H, I, vq8_rate(fmt, vq8_m))
         else:
             parts = [vq_codes(e, p) for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)]
             w13, w2 = pack_vq_expert(parts[0], parts[1], parts[2], H, I)
@@ -98,7 +100,7 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         layer.set_rot_signs(np.stack([pack_rot_signs(*rot_signs(e), H, I) for e in range(E)]))
     if layer.pools[(FMT_VQ, 0)] is not None:
         layer.set_codebooks(codebooks, codebook_stride)
-    if layer.pools[(FMT_VQ8, 0)] is not None:
+    if any(layer.pools[(f, 0)] is not None for f in (FMT_VQ8,) + FMT_VQ8_RATES):
         layer.set_codebooks8(codebooks8)
     if layer.device.type == "cuda":
         torch.cuda.synchronize(layer.device)

@@ -101,7 +101,10 @@ extern "C" {
 #define MOE_FMT_NVFP4R 5      /* nested two-level NVFP4: an NVFP4 base plane
                                  plus an NVFP4 residual plane on top of it
                                  (weights = base + residual) */
-#define MOE_FMT_MAX   5       /* largest format tag */
+#define MOE_FMT_VQ8_M1 6      /* MOE_FMT_VQ8 at an explicit rate: 1, 2 or 3 */
+#define MOE_FMT_VQ8_M2 7      /* uint8 codes per group (bits per weight), */
+#define MOE_FMT_VQ8_M3 8      /* whatever the layer's vq8_m; one pool each */
+#define MOE_FMT_MAX   8       /* largest format tag */
 
 #define MOE_PROJ_GATE 0
 #define MOE_PROJ_UP   1
@@ -139,8 +142,17 @@ extern "C" {
  *   vq8_m           codes per group of the MOE_FMT_VQ8 experts (1, 2 or 3);
  *                   any value if the layer has none.
  *   vq8_w13 / vq8_w2   pool bases of the MOE_FMT_VQ8 records;
- *   vq8_codebook[p] fp16 [vq8_m][256][8]: the small codebooks of projection
- *                   p, shared by every MOE_FMT_VQ8 expert of the layer.
+ *   vq8_codebook[p] fp16 [n][256][8]: the small codebooks of projection p,
+ *                   shared by every small-codebook VQ expert of the layer; an
+ *                   expert at rate m (MOE_FMT_VQ8: vq8_m; MOE_FMT_VQ8_Mm: m)
+ *                   reads codebooks 0 .. m-1, so n must be at least the
+ *                   largest rate in the layer.
+ *   vq8r_w13[m-1] / vq8r_w2[m-1]  pool bases of the MOE_FMT_VQ8_Mm records
+ *                   (moe_record_bytes_vq8(.., m) each), m = 1, 2, 3: a
+ *                   layer's small-codebook VQ experts at mixed rates, the
+ *                   rate chosen per expert ("GLM-5.2 mixed-bit VQ (AQLM)
+ *                   ~1.90 bpw", What it is: one layer's modules at 1, 2 and
+ *                   3 bits, chosen per module).
  *   bf16_w13 / bf16_w2 pool bases of the MOE_FMT_BF16 records.
  *   nvfp4r_w13 / nvfp4r_w2  pool bases of the MOE_FMT_NVFP4R records: each
  *                   record is an NVFP4 record (the base plane) followed by
@@ -210,6 +222,8 @@ typedef struct moe_qlayer {
     const void* nvfp4r_w2;  int64_t nvfp4r_w2_stride;
     int32_t nvfp4r_shift;
     int32_t reserved2;
+    const void* vq8r_w13[3]; int64_t vq8r_w13_stride[3];
+    const void* vq8r_w2[3];  int64_t vq8r_w2_stride[3];
 } moe_qlayer;
 
 #define MOE_REC_COMPACT   0
@@ -529,8 +543,9 @@ int moe_quantize_nvfp4_residual(const float* w, int32_t n, int32_t kin, int32_t 
 /*
  * Bytes of one expert record in the device tile layout.
  *   fmt = MOE_FMT_NVFP4 / MOE_FMT_VQ / MOE_FMT_BF16 / MOE_FMT_NVFP4R (twice
- *   the NVFP4 record: base plane, then residual plane) (MOE_FMT_VQ8: use
- *   moe_record_bytes_vq8); which = 0 for the gate/up record
+ *   the NVFP4 record: base plane, then residual plane) / MOE_FMT_VQ8_Mm
+ *   (= moe_record_bytes_vq8(which, H, I, m)) (MOE_FMT_VQ8: use
+ *   moe_record_bytes_vq8 with the layer's vq8_m); which = 0 for the gate/up record
  *   (both projections, rows interleaved by 16), 1 for the down record.
  * Returns 0 for an unsupported format or shape.
  */

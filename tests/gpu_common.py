@@ -44,7 +44,8 @@ def build_small_layer(wl, device="cuda", resident_formats=None):
         resident_formats = {synth.FMT_NVFP4, synth.FMT_NVFP4R}
     used = set(np.unique(fmt_host).tolist()) | set(resident_formats or ())
     cbs = [synth.vq_codebook(wl, p) for p in range(3)] if synth.FMT_VQ in used else None
-    cbs8 = [synth.vq8_codebooks(wl, p) for p in range(3)] if synth.FMT_VQ8 in used else None
+    vq8_tags = {synth.FMT_VQ8, synth.FMT_VQ8_M1, synth.FMT_VQ8_M2, synth.FMT_VQ8_M3}
+    cbs8 = [synth.vq8_codebooks(wl, p) for p in range(3)] if used & vq8_tags else None
     return build_layer(
         wl.E, wl.H, wl.I, fmt_host,
         nvfp4_weights=lambda e, p: synth.nvfp4_source_weights(wl, e, p),

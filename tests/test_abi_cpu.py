@@ -295,14 +295,14 @@ def test_record_table_resident():
     rec = moeq.record_table_resident(tm)
     assert np.array_equal(rec >> 24, tm) and np.array_equal(rec & 0xFFFFFF, np.arange(6))
     with pytest.raises(moeq.MoeError) as ei:
-        moeq.record_table_resident(np.array([1, 6], np.uint8))
+        moeq.record_table_resident(np.array([1, 9], np.uint8))
     assert ei.value.status == moeq.MOE_EUNSUPPORTED
 
 
 def test_record_table():
     tm = synth.tier_map(synth.MIXED)
     rec, counts = moeq.record_table(tm)
-    assert counts == {1: 108, 2: 148, 3: 0, 4: 0, 5: 0}
+    assert counts == {1: 108, 2: 148, 3: 0, 4: 0, 5: 0, 6: 0, 7: 0, 8: 0}
     for fmt in (1, 2):
         sel = np.nonzero(tm == fmt)[0]
         assert np.all(rec[sel] >> 24 == fmt)
@@ -316,13 +316,17 @@ def test_record_table():
         assert np.all(rec[sel] >> 24 == fmt)
         assert np.array_equal(rec[sel] & 0xFFFFFF, np.arange(sel.size))
     rec, counts = moeq.record_table(np.array([4, 1, 4], np.uint8))
-    assert counts == {1: 1, 2: 0, 3: 0, 4: 2, 5: 0}
+    assert counts == {1: 1, 2: 0, 3: 0, 4: 2, 5: 0, 6: 0, 7: 0, 8: 0}
     assert list(rec) == [4 << 24, 1 << 24, (4 << 24) | 1]
+    # small-codebook VQ experts at explicit rates: one pool (index space) each
+    rec, counts = moeq.record_table(np.array([7, 6, 8, 7, 6, 1], np.uint8))
+    assert counts[6] == 2 and counts[7] == 2 and counts[8] == 1 and counts[1] == 1
+    assert list(rec) == [7 << 24, 6 << 24, 8 << 24, (7 << 24) | 1, (6 << 24) | 1, 1 << 24]
     rec, counts = moeq.record_table(np.array([5, 1, 5, 5], np.uint8))
     assert counts[5] == 3 and counts[1] == 1
     assert list(rec) == [5 << 24, 1 << 24, (5 << 24) | 1, (5 << 24) | 2]
     bad = tm.copy()
-    bad[7] = 6
+    bad[7] = 9
     with pytest.raises(moeq.MoeError) as ei:
         moeq.record_table(bad)
     assert ei.value.status == moeq.MOE_EUNSUPPORTED
@@ -393,7 +397,7 @@ def test_ffn_fails_closed_on_unknown_format():
     L = moeq.lib()
     fake = ctypes.c_void_p(0x1000)
     tm = np.full(8, moeq.FMT_NVFP4, np.uint8)
-    tm[3] = 7
+    tm[3] = 9
     d = _fake_layer(tm)
     st = L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, 1 << 20,
                             ctypes.c_void_p(0))

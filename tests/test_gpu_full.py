@@ -260,6 +260,27 @@ def test_vq_T8_every_expert():
             assert np.array_equal(to_np(moeq.dequant_q(lay, e, p)).astype(np.float64), W[p]), (e, p)
 
 
+@pytest.mark.timeout(900)
+def test_vqmix_T8_every_expert():
+    """Small-codebook VQ experts at mixed rates (131 / 55 / 70 experts at 1 /
+    2 / 3 bits per weight) at the full layer size, T = 8: every touched
+    expert's rows and every output row; the dequant hook on one expert of
+    each rate."""
+    wl = synth.VQMIX
+    say("vqmix full T=8, every expert")
+    lay = layer("vqmix")
+    tm = synth.tier_map(wl)
+    x_bits, lg, r = run_forward(wl, lay, 8)
+    ids, w, offsets, perm_src = check_routing(wl, lg, r)
+    check_every_expert(wl, x_bits, lg, r, ids, w, offsets, perm_src, tm)
+    for tag in (synth.FMT_VQ8_M1, synth.FMT_VQ8_M2, synth.FMT_VQ8_M3):
+        e = int(np.flatnonzero(tm == tag)[0])
+        W = expert_weights(wl, e)
+        for p in range(3):
+            got = to_np(moeq.dequant_q(lay, e, p)).astype(np.float64)
+            assert np.all(np.abs(got - W[p]) <= 2.0 ** -22 * np.abs(W[p])), (e, p)
+
+
 @pytest.mark.parametrize("name", ["vq1", "vq2x8", "vq3x8"])
 def test_vq8_full_sampled(name):
     """Small-codebook VQ (1 and 2 bits per weight) at the full layer size, T = 8."""

@@ -88,6 +88,14 @@ SMALL = {
                                        cfg=129),
     "rot_vq8_prefill": synth.small_workload("rot_vq8_prefill", E=8, k=2, H=256, I=128, T=200,
                                             fmt="vq8", cfg=176, vq8_m=2, rot=True),
+    # small-codebook VQ experts at mixed rates (1, 2 and 3 bits per weight in
+    # one layer, three shared codebooks per projection): decode with ragged
+    # shapes, the grouped GEMM under Zipf routing
+    "vqmix_ragged": synth.small_workload("vqmix_ragged", E=12, k=3, H=208, I=48, T=21,
+                                         fmt="vqmix", cfg=130, vq8_m=3),
+    "vqmix_prefill": synth.small_workload("vqmix_prefill", E=12, k=3, H=272, I=80, T=260,
+                                          fmt="vqmix", logits="zipf", zipf_s=1.1, cfg=131,
+                                          vq8_m=3),
 }
 
 _layers = {}
@@ -117,19 +125,26 @@ def test_dequant_bit_exact(name):
             assert np.array_equal(got, W[p]), (name, e, p)
 
 
-@pytest.mark.parametrize("name", ["vq8_1", "vq8_2_ragged", "mixed3", "vq8_3_ragged"])
+@pytest.mark.parametrize("name", ["vq8_1", "vq8_2_ragged", "mixed3", "vq8_3_ragged",
+                                  "vqmix_ragged"])
 def test_dequant_vq8(name):
-    """Small-codebook VQ decode: exact with one code per group; with two, the
-    hook's fp32(fp32(C_0 + C_1) * S) is within 2 roundings of the exact value."""
+    """Small-codebook VQ decode: exact with one code per group; with two or
+    three, the hook's fp32(fp32(C_0 + ..) * S) is within 2 roundings of the
+    exact value.  Mixed-rate layers: every expert at its own rate, reading
+    the first m of the layer's codebooks."""
     wl = SMALL[name]
     say("dequant vq8", name)
     layer = layer_for(name)
     tm = synth.tier_map(wl)
-    for e in np.flatnonzero(tm == synth.FMT_VQ8):
+    vq8_tags = (synth.FMT_VQ8, synth.FMT_VQ8_M1, synth.FMT_VQ8_M2, synth.FMT_VQ8_M3)
+    if wl.fmt == "vqmix":
+        assert set(np.unique(tm).tolist()) == {synth.FMT_VQ8_M1, synth.FMT_VQ8_M2,
+                                               synth.FMT_VQ8_M3}
+    for e in np.flatnonzero(np.isin(tm, vq8_tags)):
         W = expert_weights(wl, int(e))
         for p in range(3):
             got = to_np(moeq.dequant_q(layer, int(e), p)).astype(np.float64)
-            if wl.vq8_m == 1:
+            if synth.vq8_rate(wl, int(e)) == 1:
                 assert np.array_equal(got, W[p]), (name, e, p)
             else:
                 assert np.all(np.abs(got - W[p]) <= 2.0 ** -22 * np.abs(W[p])), (name, e, p)
