@@ -198,6 +198,21 @@ LayerWs layer_ws(const moe_qlayer* L, int64_t T, int32_t k) {
     return w;
 }
 
+// The two formats of a layer holding exactly NVFP4 and one VQ form, for the
+// one-launch decode path (false for other layers).
+bool decode_pair(const LayerInfo& li, int64_t T, int32_t k, int& f1, int& f2) {
+    int nf = 0;
+    f1 = f2 = 0;
+    for (int f = MOE_FMT_NVFP4; f < kNumFmt; ++f) {
+        if (!li.count[f]) continue;
+        ++nf;
+        if (f == MOE_FMT_NVFP4) f1 = f;
+        else f2 = f;
+    }
+    return nf == 2 && f1 && f2 &&
+           ffn_decode_pair_ok(li.view, f1, li.count[f1], f2, li.count[f2], T, k);
+}
+
 // Gate/up + SwiGLU of every format present.  perm_src == offsets == NULL is
 // the identity map of a one-expert layer (k = 1; part: the decode path's
 // partial sums).  x16 [T, H] is workspace for the fp16 copy of x that the
@@ -231,6 +246,10 @@ int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_
         const int st = launch_x_to_f16(x_bf16, T * li.view.H, x16, stream);
         if (st) return st;
     }
+    int f1, f2;
+    if (!prefill && offsets && decode_pair(li, T, k, f1, f2))
+        return launch_ffn_decode_pair(li.view, f1, li.count[f1], f2, li.count[f2], x_bf16, perm_src,
+                                      offsets, T, k, h_f16, nullptr, 0, stream);
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!li.count[fmt]) continue;
         const int st =
@@ -250,6 +269,11 @@ int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_
 int run_down(const LayerInfo& li, const uint16_t* h_f16, const int32_t* offsets, int64_t T,
              int32_t k, float* y_perm, void* stream) {
     const bool prefill = T >= kPrefillMinTokens;
+    int f1, f2;
+    if (!prefill && offsets && !li.view.rot && decode_pair(li, T, k, f1, f2))
+        return launch_ffn_decode_pair(li.view, f1, li.count[f1], f2, li.count[f2], nullptr,
+                                      nullptr, offsets, T, k, const_cast<uint16_t*>(h_f16),
+                                      y_perm, 1, stream);
     for (int fmt = MOE_FMT_NVFP4; fmt < kNumFmt; ++fmt) {
         if (!li.count[fmt]) continue;
         uint16_t* h = const_cast<uint16_t*>(h_f16);

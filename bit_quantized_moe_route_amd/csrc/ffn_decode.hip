@@ -1205,7 +1205,87 @@ int launch_small_shared_fmt(const DecodeArgs& a, DecodeArgs sa, int64_t T, hipSt
     return MOE_OK;
 }
 
+// Two formats of a mixed layer in one launch (decode batches): workgroups
+// [0, n2) run the second format's grid g2, the rest the first format's grid
+// g1, each with the body of its own kernel (so the same bits).  The second
+// format is a VQ form, whose gather-bound workgroups go first; the NVFP4
+// weight stream then runs beside them instead of after them.
+// ("GLM-5.3-EXL3-TR3-3.42bpw", What is quantized: layers that mix two
+// per-expert tiers.)
+template <class F1, class F2, int KS, int PHASE>
+__global__ __launch_bounds__(256, kMinWaves) void k_ffn_pair(DecodeArgs A1, DecodeArgs A2,
+                                                             int n2, uint3 g1, uint3 g2) {
+    constexpr int RPW = PHASE == 0 ? kRpwGateup : kRpwDown;
+    unsigned b = blockIdx.x;
+    if (b < (unsigned)n2) {
+        ffn_body<F2, 1, KS, RPW, PHASE, 4, false, false, false, false>(
+            A2, uint3{b % g2.x, (b / g2.x) % g2.y, b / (g2.x * g2.y)});
+    } else {
+        b -= (unsigned)n2;
+        ffn_body<F1, 1, KS, RPW, PHASE, 4, false, false, false, false>(
+            A1, uint3{b % g1.x, (b / g1.x) % g1.y, b / (g1.x * g1.y)});
+    }
+}
+
+// The input split launch_fmt picks for this many active-expert slots.
+int decode_ks(int slots) { return slots <= 16 ? 4 : slots <= 64 ? 2 : 1; }
+
+template <class F2, int KS>
+int launch_pair_ks(const DecodeArgs& a1, int slots1, const DecodeArgs& a2, int slots2, int chunks,
+                   int phase, hipStream_t s) {
+    constexpr int SETS = 4 / KS;
+    const int nrg = phase == 0 ? a1.I / 16 : a1.H / 16;
+    const int rpw = phase == 0 ? kRpwGateup : kRpwDown;
+    const int nsets = (nrg + rpw - 1) / rpw;
+    const unsigned gx = (unsigned)((nsets + SETS - 1) / SETS);
+    const uint3 g1{gx, (unsigned)slots1, (unsigned)chunks};
+    const uint3 g2{gx, (unsigned)slots2, (unsigned)chunks};
+    const int n2 = (int)(g2.x * g2.y * g2.z);
+    const unsigned nb = (unsigned)n2 + g1.x * g1.y * g1.z;
+    if (phase == 0)
+        k_ffn_pair<NvFmt, F2, KS, 0><<<nb, 256, codebook_lds_bytes<F2>(0), s>>>(a1, a2, n2, g1, g2);
+    else
+        k_ffn_pair<NvFmt, F2, KS, 1><<<nb, 256, codebook_lds_bytes<F2>(1), s>>>(a1, a2, n2, g1, g2);
+    MOEQ_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+template <class F2>
+int launch_pair_fmt(const DecodeArgs& a1, int slots1, const DecodeArgs& a2, int slots2,
+                    int chunks, int phase, hipStream_t s) {
+    switch (decode_ks(slots1)) {
+        case 4: return launch_pair_ks<F2, 4>(a1, slots1, a2, slots2, chunks, phase, s);
+        case 2: return launch_pair_ks<F2, 2>(a1, slots1, a2, slots2, chunks, phase, s);
+        default: return launch_pair_ks<F2, 1>(a1, slots1, a2, slots2, chunks, phase, s);
+    }
+}
+
 }  // namespace
+
+bool ffn_decode_pair_ok(const LayerView& L, int fmt1, int n1, int fmt2, int n2, int64_t T,
+                        int32_t k) {
+    if (fmt1 != MOE_FMT_NVFP4 || !(fmt2 == MOE_FMT_VQ || is_vq8(fmt2)) || L.rot) return false;
+    const int64_t tk = T * k;
+    const int s1 = (int)(tk < n1 ? tk : n1), s2 = (int)(tk < n2 ? tk : n2);
+    return s1 > 0 && s2 > 0 && decode_ks(s1) == decode_ks(s2);
+}
+
+int launch_ffn_decode_pair(const LayerView& L, int fmt1, int n1, int fmt2, int n2,
+                           const uint16_t* x_bf16, const int32_t* perm_src,
+                           const int32_t* offsets, int64_t T, int32_t k, uint16_t* h16,
+                           float* y_perm, int phase, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const DecodeArgs a1 = decode_args(L, fmt1, x_bf16, perm_src, offsets, T, k, h16, y_perm);
+    const DecodeArgs a2 = decode_args(L, fmt2, x_bf16, perm_src, offsets, T, k, h16, y_perm);
+    const int64_t tk = T * k;
+    const int s1 = (int)(tk < n1 ? tk : n1), s2 = (int)(tk < n2 ? tk : n2);
+    const int chunks = (int)((T + 15) / 16);
+    if (fmt2 == MOE_FMT_VQ) return launch_pair_fmt<VqFmt>(a1, s1, a2, s2, chunks, phase, s);
+    const int m = vq8_rate(fmt2, L.vq8_m);
+    if (m == 1) return launch_pair_fmt<Vq8Fmt<1>>(a1, s1, a2, s2, chunks, phase, s);
+    if (m == 3) return launch_pair_fmt<Vq8Fmt<3>>(a1, s1, a2, s2, chunks, phase, s);
+    return launch_pair_fmt<Vq8Fmt<2>>(a1, s1, a2, s2, chunks, phase, s);
+}
 
 int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, const float* logits,
                        int64_t T, int32_t k, int32_t* topk_ids, float* topk_w, uint16_t* h16,

@@ -119,6 +119,15 @@ int launch_ffn_decode(const LayerView& L, int fmt, int n_fmt, const uint16_t* x_
                       const int32_t* perm_src, const int32_t* offsets, int64_t T,
                       int32_t k, uint16_t* h16, float* y_perm, int phase,
                       void* stream, float* gu = nullptr);
+// A mixed layer of NVFP4 and one VQ form (decode batches): both formats'
+// gate/up (phase 0) or down (phase 1) work in one launch, when both pick the
+// same input split (ffn_decode_pair_ok); the same bits as the two launches.
+bool ffn_decode_pair_ok(const LayerView& L, int fmt1, int n1, int fmt2, int n2, int64_t T,
+                        int32_t k);
+int launch_ffn_decode_pair(const LayerView& L, int fmt1, int n1, int fmt2, int n2,
+                           const uint16_t* x_bf16, const int32_t* perm_src,
+                           const int32_t* offsets, int64_t T, int32_t k, uint16_t* h16,
+                           float* y_perm, int phase, void* stream);
 // The one expert of a shared-expert layer through the identity map (rows
 // 0 .. T-1 are tokens 0 .. T-1): phase 0 writes fp32 partial g | u to part
 // (shared_part_bytes) and then h, phase 1 writes y [T, H].
