@@ -47,6 +47,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
+# device clock cycles, per timed step, of the spin kernel queued ahead of the
+# eager timed steps (about 0.4 ms at 2.4 GHz: longer than the host takes to
+# issue one step), so that the host has issued every step before the device
+# starts the first
+HEAD_START_CYCLES_PER_STEP = 1_000_000
+
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
@@ -208,32 +214,50 @@ class Runner:
         self.ev_sh.append((r, e0, e1))
         moeq.combine_shared(self.y, inv_perm, self.w, self.y_sh, self.out)
 
+    def _head_start(self, steps):
+        """A spin kernel ahead of `steps` eager steps, then an event: the host
+        issues every step (and its events) while the device spins, so the
+        steps then run back to back as in a loop that keeps the device busy,
+        and each event pair brackets its kernels rather than the host's time
+        to issue them.  Returns the event after the spin."""
+        self.torch.cuda._sleep(HEAD_START_CYCLES_PER_STEP * steps)
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def _end_event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
     def run(self, steps, warmup):
         """Eager steps: the step-by-step calls with HIP events around the
-        gate/up and the down call.  Returns (seconds, gate/up ms per launch,
-        down ms per launch)."""
+        gate/up and the down call, issued ahead of the device (a spin kernel
+        first).  Returns (device ms per step from the first step's start to
+        the last one's end, gate/up ms per launch, down ms per launch)."""
         torch = self.torch
         for i in range(warmup):
             self.step(i, False)
         torch.cuda.synchronize()
         self.ev, self.ev_dn, self.ev_sh = [], [], []
-        t0 = time.perf_counter()
+        e_start = self._head_start(steps)
         for i in range(steps):
             self.step(warmup + i, True)
+        e_end = self._end_event()
         torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
         gu_ms = [e0.elapsed_time(e1) for _, e0, e1 in self.ev]
         dn_ms = [e0.elapsed_time(e1) for _, e0, e1 in self.ev_dn]
-        return dt, gu_ms, dn_ms
+        return e_start.elapsed_time(e_end) / steps, gu_ms, dn_ms
 
     def run_layer(self, steps, warmup):
-        """Eager one-call layer steps with HIP events around each call; the
-        ms of each call."""
+        """Eager one-call layer steps with HIP events around each call, issued
+        ahead of the device (a spin kernel first); the ms of each call."""
         torch = self.torch
         for i in range(warmup):
             self.layer_step(i)
         torch.cuda.synchronize()
         self.ev_layer = []
+        self._head_start(steps)
         for i in range(steps):
             self.layer_step(warmup + i)
         torch.cuda.synchronize()
@@ -320,7 +344,7 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16, shared=None):
     6 H I flop per assignment."""
     import numpy as np
     rn = Runner(layer, wl, T, reps, dev, shared)
-    dte, gu_ms, dn_ms = rn.run(steps, warmup)
+    ms_eager, gu_ms, dn_ms = rn.run(steps, warmup)
     lay_warm = 2
     lay_ms = rn.run_layer(steps, lay_warm)
     dt, group = rn.run_graph(steps, warmup)
@@ -337,8 +361,8 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16, shared=None):
         "tokens_per_s": T * steps / dt,
         "ms_per_step": dt / steps * 1e3,
         "step_ms_p10_p50_p90": [float(v) for v in q],
-        "tokens_per_s_eager": T * steps / dte,
-        "ms_per_step_eager": dte / steps * 1e3,
+        "tokens_per_s_eager": T / (ms_eager / 1e3),
+        "ms_per_step_eager": ms_eager,
         "steps_per_graph": group,
         "packed_GBps": all_bytes / dt / 1e9,
         "packed_frac_hbm": all_bytes / dt / 1e9 / HBM_PEAK_GBS,

@@ -71,6 +71,13 @@
  *     stated sizes for ids in range.  (With a token naming one expert twice,
  *     that expert can hold more than T rows; the decode-size FFN kernels,
  *     T < 128, compute the first T of them only.)
+ *   - Operand range: the expert FFNs multiply on the matrix cores' fp16
+ *     operands, so each activation x and each SwiGLU output h must lie in
+ *     fp16's finite range, |v| <= 65504 (every bf16 value up to 65280 is
+ *     exact there; below 2^-14 a value is rounded to fp16's subnormal grid,
+ *     error < 2^-25).  A token with a value beyond the range gets a
+ *     non-finite output row; the other tokens' rows are unaffected, since no
+ *     product mixes two tokens.
  */
 #ifndef MOEQ_H
 #define MOEQ_H
