@@ -1104,7 +1104,11 @@ int launch_small_fmt(const DecodeArgs& a, int64_t T, hipStream_t s) {
         <<<g1, 256, codebook_lds_bytes<F>(0), s>>>(a);
     MOEQ_CHECK_LAUNCH();
     dim3 g2((unsigned)(a.H / 16), (unsigned)T, 1u);
-    constexpr bool kWide = std::is_same<F, NvFmt>::value || F::kVq8;   // 8 slots per wave
+    // 8 slots per wave for small-codebook VQ (one LDS codebook copy serves
+    // them all); NVFP4 takes two slot groups of 4 waves each (128 VGPRs: two
+    // 8-wave workgroups per CU, so a token's 384 workgroups all fit at once;
+    // 4% faster at one token than 8 slots per wave in 4-wave workgroups)
+    constexpr bool kWide = F::kVq8;
     if (a.k <= 4)
         k_down_combine<F, 4, 1><<<g2, 64 * kDcKS, codebook_lds_bytes<F>(1), s>>>(a);
     else if constexpr (kWide)
@@ -1181,7 +1185,7 @@ int launch_small_shared_fmt(const DecodeArgs& a, DecodeArgs sa, int64_t T, hipSt
     const unsigned gdx = (unsigned)(a.H / 16);
     const int nd = (int)(gdx * T);
     const int64_t nsw = (int64_t)sa.rows * (sa.I / 4);
-    constexpr bool kWide = std::is_same<F, NvFmt>::value || F::kVq8;
+    constexpr bool kWide = F::kVq8;   // as launch_small_fmt
     if (a.k <= 4) {
         const int nb = nd + (int)((nsw + 64 * kDcKS - 1) / (64 * kDcKS));
         k_down_combine_swiglu<F, 4, 1><<<(unsigned)nb, 64 * kDcKS, codebook_lds_bytes<F>(1), s>>>(

@@ -33,6 +33,8 @@ CASES = {
     # k = 6: two slot groups, the second with two live slots; ragged H
     # (17 row groups) and I (one partial tile)
     "nv_k6": (synth.small_workload("lf_nv_k6", E=16, k=6, H=272, I=80, T=2, cfg=181), 2),
+    # k = 5: the second slot group of the down + combine has one live slot
+    "nv_k5": (synth.small_workload("lf_nv_k5", E=12, k=5, H=256, I=96, T=3, cfg=210), 3),
     # k = 8 over 32 experts, one token and two tokens
     "nv_k8_t1": (synth.small_workload("lf_nv_k8", E=32, k=8, H=384, I=256, T=1, cfg=182), 1),
     "nv_k8_t2": (synth.small_workload("lf_nv_k8", E=32, k=8, H=384, I=256, T=2, cfg=182), 2),
