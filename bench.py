@@ -220,7 +220,11 @@ class Runner:
         steps then run back to back as in a loop that keeps the device busy,
         and each event pair brackets its kernels rather than the host's time
         to issue them.  Returns the event after the spin."""
-        self.torch.cuda._sleep(HEAD_START_CYCLES_PER_STEP * steps)
+        spin = getattr(self.torch.cuda, "_sleep", None)
+        if spin is not None:
+            spin(HEAD_START_CYCLES_PER_STEP * steps)
+        else:
+            log("no spin kernel in this torch: the eager events include the host's issue time")
         e = self.torch.cuda.Event(enable_timing=True)
         e.record()
         return e
