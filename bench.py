@@ -53,6 +53,11 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # starts the first
 HEAD_START_CYCLES_PER_STEP = 1_000_000
 
+# untimed steps queued between the spin kernel and the eager timed steps: after
+# an idle gap the weight-streaming kernels slow down over the first ~7 steps of
+# load (by up to ~40%) and take ~25 steps to settle
+SETTLE_STEPS = 32
+
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
@@ -237,16 +242,22 @@ class Runner:
     def run(self, steps, warmup):
         """Eager steps: the step-by-step calls with HIP events around the
         gate/up and the down call, issued ahead of the device (a spin kernel
-        first).  Returns (device ms per step from the first step's start to
-        the last one's end, gate/up ms per launch, down ms per launch)."""
+        first, then SETTLE_STEPS untimed steps in the same queue, so the timed
+        ones run on a chip whose clocks have settled under the load).  The
+        timed steps take batches warmup + SETTLE_STEPS + i.  Returns (device
+        ms per step from the first timed step's start to the last one's end,
+        gate/up ms per launch, down ms per launch)."""
         torch = self.torch
         for i in range(warmup):
             self.step(i, False)
         torch.cuda.synchronize()
         self.ev, self.ev_dn, self.ev_sh = [], [], []
-        e_start = self._head_start(steps)
+        self._head_start(steps + SETTLE_STEPS)
+        for i in range(SETTLE_STEPS):
+            self.step(warmup + i, False)
+        e_start = self._end_event()
         for i in range(steps):
-            self.step(warmup + i, True)
+            self.step(warmup + SETTLE_STEPS + i, True)
         e_end = self._end_event()
         torch.cuda.synchronize()
         gu_ms = [e0.elapsed_time(e1) for _, e0, e1 in self.ev]
@@ -255,15 +266,19 @@ class Runner:
 
     def run_layer(self, steps, warmup):
         """Eager one-call layer steps with HIP events around each call, issued
-        ahead of the device (a spin kernel first); the ms of each call."""
+        ahead of the device (a spin kernel first, then SETTLE_STEPS untimed
+        calls, as in run); the timed calls take batches warmup +
+        SETTLE_STEPS + i; the ms of each timed call."""
         torch = self.torch
         for i in range(warmup):
             self.layer_step(i)
         torch.cuda.synchronize()
-        self.ev_layer = []
-        self._head_start(steps)
-        for i in range(steps):
+        self._head_start(steps + SETTLE_STEPS)
+        for i in range(SETTLE_STEPS):
             self.layer_step(warmup + i)
+        self.ev_layer = []
+        for i in range(steps):
+            self.layer_step(warmup + SETTLE_STEPS + i)
         torch.cuda.synchronize()
         return [e0.elapsed_time(e1) for e0, e1 in self.ev_layer]
 
@@ -272,7 +287,9 @@ class Runner:
         them: each graph holds `group` consecutive steps (each on its own input
         batch; group = the largest divisor of `steps` up to 16), so the host's
         per-graph launch cost is paid once per group.  The graphs together
-        cover the batch pool a whole number of times.  Returns (seconds, group)."""
+        cover the batch pool a whole number of times.  The timed replays follow
+        warm-up replays of at least the warm-up steps and SETTLE_STEPS steps.
+        Returns (seconds, group)."""
         import math
         torch = self.torch
         nb = len(self.batches)
@@ -285,7 +302,11 @@ class Runner:
                 for u in range(group):
                     self.step(gi * group + u, False)
             graphs.append(g)
-        for i in range(max(1, (warmup + group - 1) // group)):
+        # warm-up: the W warm-up steps, and at least SETTLE_STEPS steps (after
+        # the idle gap of the captures the kernels take ~25 steps of load to
+        # settle; the timed replays are meant to see a decode loop's steady
+        # state)
+        for i in range(max((warmup + group - 1) // group, (SETTLE_STEPS + group - 1) // group)):
             graphs[i % ng].replay()
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps // group + 1)]
@@ -353,8 +374,8 @@ def measure(layer, wl, T, steps, warmup, dev, reps=16, shared=None):
     lay_ms = rn.run_layer(steps, lay_warm)
     dt, group = rn.run_graph(steps, warmup)
     idx = list(range(steps))                          # batches of the graph replays
-    idx_e = [warmup + i for i in range(steps)]        # batches of the eager steps
-    idx_l = [lay_warm + i for i in range(steps)]      # batches of the one-call layer steps
+    idx_e = [warmup + SETTLE_STEPS + i for i in range(steps)]     # batches of the eager steps
+    idx_l = [lay_warm + SETTLE_STEPS + i for i in range(steps)]   # ... of the one-call layer steps
     all_bytes = sum(rn.bytes_of(r, "all") for r in idx)
     gu_bytes = sum(rn.bytes_of(r, "gateup") for r in idx_e)
     gu_s = sum(gu_ms) / 1e3
