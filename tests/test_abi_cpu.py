@@ -9,6 +9,8 @@ import subprocess
 
 import numpy as np
 import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 import bit_quantized_moe_route_amd as moeq
 import oracle
@@ -112,6 +114,42 @@ def test_quantize_nvfp4_crafted_matches_oracle(golden_dir):
     for name, v, sb, cb in _handworked(golden_dir):
         c, s = moeq.quantize_nvfp4(v[None, :])
         assert s[0, 0] == sb and list(c[0]) == cb, name
+
+
+_E2M1_POINTS = [0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0, 7.0]
+
+
+def _e4m3_value(byte):
+    e, m = (byte >> 3) & 15, byte & 7
+    return (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+
+
+@settings(max_examples=400, deadline=None)
+@given(data=st.data())
+def test_quantize_nvfp4_adversarial_blocks_match_oracle(data):
+    """Random blocks built on the encoder's decision points: a block scale
+    from any finite positive E4M3 byte (subnormals included), elements at the
+    E2M1 values and at the midpoints between them times that scale, each
+    possibly nudged by one float32 ulp either way, with random signs and
+    zeros: the library's encoder (C) and the oracle's (brute-force nearest
+    value, numpy) give the same code and scale bytes."""
+    rows = data.draw(st.integers(1, 4))
+    blocks = []
+    for _ in range(rows * 2):
+        S = _e4m3_value(data.draw(st.integers(1, 126)))
+        pts = data.draw(st.lists(st.sampled_from(_E2M1_POINTS), min_size=16, max_size=16))
+        sign = data.draw(st.lists(st.booleans(), min_size=16, max_size=16))
+        nudge = data.draw(st.lists(st.sampled_from([-1, 0, 0, 1]), min_size=16, max_size=16))
+        v = np.array([(-p if sg else p) * S for p, sg in zip(pts, sign)], dtype=np.float32)
+        for i, d in enumerate(nudge):
+            if d:
+                v[i] = np.nextafter(v[i], np.float32(np.inf if d > 0 else -np.inf), dtype=np.float32)
+        blocks.append(v)
+    w = np.stack(blocks).reshape(rows, 32)
+    c, s = moeq.quantize_nvfp4(w)
+    oc, os_ = oracle.nvfp4_quantize(w)
+    assert np.array_equal(c, oc)
+    assert np.array_equal(s, os_)
 
 
 def test_quantize_nvfp4_rejects_nonfinite():
