@@ -18,7 +18,8 @@ DEV = "cuda"
 @pytest.mark.parametrize("T,E,k", [(1, 256, 8), (32, 256, 8), (512, 256, 8), (700, 64, 8),
                                    (5, 1024, 16), (3, 4, 1), (4096, 256, 8), (300, 1024, 16),
                                    (8, 256, 8), (4, 1024, 16), (64, 16, 1), (9, 64, 7),
-                                   (0, 8, 2)])
+                                   (0, 8, 2), (65, 16, 1), (64, 256, 8), (65, 256, 8),
+                                   (32, 1024, 16), (33, 1024, 16), (21, 600, 3)])
 def test_route_permute_equals_separate_calls(T, E, k):
     say("route_permute", T, E, k)
     g = np.random.default_rng(T + E)
