@@ -443,7 +443,7 @@ def compact(res):
 
 # --------------------------------------------------------------------------
 
-CPU_SAMPLE_TOKENS = 8
+CPU_SAMPLE_TOKENS = 16
 CPU_MAX_WORKERS = 16
 
 
