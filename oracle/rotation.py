@@ -6,7 +6,7 @@ TEST INFRASTRUCTURE ONLY -- see oracle/__init__.py.
 Hadamard-128 transform on both sides of each weight matrix.  Read here as the
 orthonormal block-diagonal rotation
 
-    R = blockdiag(H_128 / sqrt(128), ...) @ diag(s),   s in {+1, -1}^N,
+    R = blockdiag(H_b / sqrt(b), ...) @ diag(s),   s in {+1, -1}^N,   b = 128,
 
 on each side of a matrix: the stored (then quantized) matrix is
 W_rot = R_out W R_in^T, so that W = R_out^T W_rot R_in and the layer computes
@@ -19,6 +19,14 @@ weights R_out^T Q(W_rot) R_in (Q = the stored format's decode); the oracle
 takes that definition: it un-rotates the decoded matrix and evaluates the
 ordinary expert FFN.  (Reading: gate and up share their input-side rotation,
 because they share their input; every other side has its own signs.)
+
+The same Method names a wider variant for the down projection of some layers:
+its input side takes random signs and one Hadamard-512 per tensor-parallel
+shard of the intermediate dimension, with a flat (uniform) input-channel
+scale.  Read here as the same rotation with block b = 512 on that one side
+(R_in = blockdiag(H_512 / sqrt(512)) diag(s)); the scale is the rotation's own
+normalisation, no per-channel factor.  Every side therefore takes its own
+block: `rotate_weights` / `unrotate_weights` accept block_out and block_in.
 """
 
 import numpy as np
@@ -62,14 +70,15 @@ def unrotate(v, signs, block=BLOCK):
     return w.reshape(v.shape) * np.asarray(signs, dtype=np.float64)
 
 
-def rotate_weights(w, s_out, s_in, block=BLOCK):
-    """W_rot = R_out W R_in^T for W [n_out, n_in]."""
-    a = rotate(np.asarray(w, dtype=np.float64), s_in, block)      # rows: W R_in^T
-    return rotate(a.T, s_out, block).T                               # columns: R_out (.)
+def rotate_weights(w, s_out, s_in, block_out=BLOCK, block_in=BLOCK):
+    """W_rot = R_out W R_in^T for W [n_out, n_in], R_out of block block_out and
+    R_in of block block_in."""
+    a = rotate(np.asarray(w, dtype=np.float64), s_in, block_in)     # rows: W R_in^T
+    return rotate(a.T, s_out, block_out).T                           # columns: R_out (.)
 
 
-def unrotate_weights(w_rot, s_out, s_in, block=BLOCK):
+def unrotate_weights(w_rot, s_out, s_in, block_out=BLOCK, block_in=BLOCK):
     """R_out^T W_rot R_in for W_rot [n_out, n_in]: the effective weights of a
-    rotated matrix."""
-    a = unrotate(np.asarray(w_rot, dtype=np.float64), s_in, block)  # rows: W_rot R_in
-    return unrotate(a.T, s_out, block).T                             # columns: R_out^T (.)
+    rotated matrix (blocks as in rotate_weights)."""
+    a = unrotate(np.asarray(w_rot, dtype=np.float64), s_in, block_in)   # rows: W_rot R_in
+    return unrotate(a.T, s_out, block_out).T                             # columns: R_out^T (.)

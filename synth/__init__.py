@@ -115,6 +115,8 @@ class Workload:
     vq8_m: int = 0          # codes per 8-weight group of the small-codebook VQ
     shared: bool = False    # the layer has a BF16 shared expert
     rot: bool = False       # expert weights stored rotated (signs + Hadamard-128)
+    rot_in2: int = 128      # Hadamard block of the down projection's input side
+                            # of a rotated layer: 128, or 512 (the wide variant)
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
 
@@ -144,6 +146,11 @@ VQMIX = Workload("vqmix", 10, 256, 8, 6144, 2048, (8,), "vqmix", "uniform", vq_c
 # source weights) are taken to be in the rotated domain, W_rot ~ N(0, 0.02)
 DECODE_ROT = Workload("decode_rot", 7, 256, 8, 6144, 2048, (1, 8, 32), "nvfp4", "uniform",
                       weight_cfg=1, rot=True)
+# the same with the wide down-input rotation (signs + one Hadamard-512 per
+# 512 intermediate channels on the down projection's input side); same seed
+# slot: same stored matrices and signs
+DECODE_ROT512 = Workload("decode_rot512", 7, 256, 8, 6144, 2048, (1, 8, 32), "nvfp4", "uniform",
+                         weight_cfg=1, rot=True, rot_in2=512)
 DECODE_SHARED = Workload("decode_shared", 1, 256, 8, 6144, 2048, (1, 8, 32), "nvfp4", "uniform",
                          shared=True)
 # the decode layer's NVFP4 experts (same source weights) held nested: every
@@ -155,16 +162,16 @@ PREFILL_SHARED = Workload("prefill_shared", 2, 256, 8, 6144, 2048, (4096,), "nvf
                           zipf_s=1.1, shared=True)
 
 WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL, VQ, MIXED, VQ1, VQ2X8, VQ3X8, DECODE_SHARED,
-                                 PREFILL_SHARED, DECODE_ROT, NESTED, VQMIX)}
+                                 PREFILL_SHARED, DECODE_ROT, DECODE_ROT512, NESTED, VQMIX)}
 
 
 def small_workload(name, E, k, H, I, T, fmt="nvfp4", logits="normal", cfg=100,
                    n_nvfp4=0, n_hot=0, hot_share=0.0, zipf_s=0.0, vq8_m=0, shared=False,
-                   rot=False):
+                   rot=False, rot_in2=128):
     """A property-test workload with its own seed slot."""
     return Workload(name, cfg, E, k, H, I, (T,), fmt, logits, weight_cfg=cfg,
                     vq_cfg=cfg, n_nvfp4=n_nvfp4, n_hot=n_hot, hot_share=hot_share,
-                    zipf_s=zipf_s, vq8_m=vq8_m, shared=shared, rot=rot)
+                    zipf_s=zipf_s, vq8_m=vq8_m, shared=shared, rot=rot, rot_in2=rot_in2)
 
 
 # --------------------------------------------------------------------------

@@ -43,7 +43,8 @@ def expert_weights(wl, e, fmt=None):
         s = {side: synth.rot_signs(wl, e, side) for side in range(5)}
         mats = [oracle.unrotate_weights(mats[0], s[synth.ROT_OUT_GATE], s[synth.ROT_IN13]),
                 oracle.unrotate_weights(mats[1], s[synth.ROT_OUT_UP], s[synth.ROT_IN13]),
-                oracle.unrotate_weights(mats[2], s[synth.ROT_OUT2], s[synth.ROT_IN2])]
+                oracle.unrotate_weights(mats[2], s[synth.ROT_OUT2], s[synth.ROT_IN2],
+                                        block_in=wl.rot_in2)]
     return tuple(mats)
 
 
