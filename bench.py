@@ -563,7 +563,7 @@ def main():
                             "mixed8,mixed32,mixedhot8,"
                             "mixedhot32,nested8,nested32,shared1,shared8,shared32,prefillshared,"
                             "rot1,rot8,rot32,"
-                            "rotprefill",
+                            "rotprefill,rotw32,rotwprefill",
                     help="comma list of other workloads to measure ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=CPU_SAMPLE_TOKENS,
@@ -659,17 +659,21 @@ def main():
             elif name.startswith("rot"):
                 # the same NVFP4 codes read as the rotated matrices of a rotated
                 # layer: the decode layer with each expert's signs attached
-                wr = synth.DECODE_ROT
+                # ("rotw": the wide 512-block rotation of the down input)
+                wide = name.startswith("rotw")
+                wr = synth.DECODE_ROT512 if wide else synth.DECODE_ROT
                 nv_layer.set_rot_signs(np.stack([
                     moeq.pack_rot_signs(*[synth.rot_signs(wr, e, sd) for sd in range(5)],
-                                        wr.H, wr.I) for e in range(wr.E)]))
+                                        wr.H, wr.I) for e in range(wr.E)]), in2_block=wr.rot_in2)
                 try:
-                    if name == "rotprefill":
-                        wpr = synth.Workload("prefill_rot", 2, 256, 8, 6144, 2048, (4096,),
-                                             "nvfp4", "zipf", zipf_s=1.1, rot=True)
+                    if name.endswith("prefill"):
+                        wpr = synth.Workload(wr.name.replace("decode", "prefill"), 2, 256, 8,
+                                             6144, 2048, (4096,), "nvfp4", "zipf", zipf_s=1.1,
+                                             rot=True, rot_in2=wr.rot_in2)
                         extra[name] = measure(nv_layer, wpr, 4096, 5, 2, dev, reps=4)
                     else:
-                        extra[name] = measure(nv_layer, wr, int(name[len("rot"):]), 30, 5, dev)
+                        T = int(name[len("rotw" if wide else "rot"):])
+                        extra[name] = measure(nv_layer, wr, T, 30, 5, dev)
                 finally:
                     nv_layer.set_rot_signs(None)
             elif name.startswith("decode"):

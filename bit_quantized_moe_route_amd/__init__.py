@@ -81,7 +81,7 @@ class _QLayerC(ctypes.Structure):
         ("vq8_codebook", ctypes.c_void_p * 3),
         ("bf16_w13", ctypes.c_void_p), ("bf16_w13_stride", ctypes.c_int64),
         ("bf16_w2", ctypes.c_void_p), ("bf16_w2_stride", ctypes.c_int64),
-        ("record_mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("record_mode", ctypes.c_int32), ("rot_in2_block", ctypes.c_int32),
         ("rot_signs", ctypes.c_void_p),
         ("nvfp4r_w13", ctypes.c_void_p), ("nvfp4r_w13_stride", ctypes.c_int64),
         ("nvfp4r_w2", ctypes.c_void_p), ("nvfp4r_w2_stride", ctypes.c_int64),
@@ -137,6 +137,7 @@ _PROTOS = {
     "moe_rot_sign_bytes": (_SZ, [_I32, _I32]),
     "moe_pack_rot_signs": (ctypes.c_int, [_P] * 5 + [_I32, _I32, _P]),
     "moe_rotate_matrix": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P]),
+    "moe_rotate_matrix_blocks": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I32, _I32, _P]),
     "moe_record_table": (ctypes.c_int, [_P, _I32, _P, _P]),
     "moe_record_table_resident": (ctypes.c_int, [_P, _I32, _P]),
     "moe_dequant_q": (ctypes.c_int, [ctypes.POINTER(_QLayerC), _I32, _I32, _P, _P]),
@@ -299,15 +300,17 @@ def pack_rot_signs(s_in13, s_out_gate, s_out_up, s_in2, s_out2, H, I):
     return out
 
 
-def rotate_matrix(w, s_out, s_in):
+def rotate_matrix(w, s_out, s_in, block_out=128, block_in=128):
     """W_rot = R_out W R_in^T (fp32 in and out, fp64 inside), R = signs then
-    Hadamard-128 / sqrt(128) per block: the offline step of a rotated format."""
+    Hadamard-b / sqrt(b) per block of b (128, or 512 for the input side of a
+    wide-variant down matrix): the offline step of a rotated format."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     so = np.ascontiguousarray(s_out, dtype=np.int8)
     si = np.ascontiguousarray(s_in, dtype=np.int8)
     out = np.empty_like(w)
-    _check(lib().moe_rotate_matrix(_np_ptr(w), w.shape[0], w.shape[1], _np_ptr(so), _np_ptr(si),
-                                   _np_ptr(out)), "moe_rotate_matrix")
+    _check(lib().moe_rotate_matrix_blocks(_np_ptr(w), w.shape[0], w.shape[1], _np_ptr(so),
+                                          _np_ptr(si), block_out, block_in, _np_ptr(out)),
+           "moe_rotate_matrix_blocks")
     return out
 
 
@@ -419,6 +422,7 @@ class QLayer:
         self.codebook_stride = 0
         self.codebooks8 = [None, None, None]
         self.rot_signs = None
+        self.rot_in2_block = 128
         self._c = None
 
     def record_index(self, e):
@@ -495,10 +499,13 @@ class QLayer:
         self.codebooks8 = out
         self._c = None
 
-    def set_rot_signs(self, signs):
+    def set_rot_signs(self, signs, in2_block=128):
         """Rotated storage: signs uint8 [E, rot_sign_bytes(H, I)] (one row per
-        expert from pack_rot_signs); None: the stored matrices are the weights."""
+        expert from pack_rot_signs); None: the stored matrices are the weights.
+        in2_block: the Hadamard block of the down projection's input side (128,
+        or 512 for the wide variant)."""
         torch = _torch()
+        self.rot_in2_block = in2_block
         if signs is None:
             self.rot_signs = None
         else:
@@ -540,6 +547,7 @@ class QLayer:
                 cb = self.codebooks8[p]
                 d.vq8_codebook[p] = cb.data_ptr() if cb is not None else None
             d.rot_signs = self.rot_signs.data_ptr() if self.rot_signs is not None else None
+            d.rot_in2_block = self.rot_in2_block
             self._c = d
         return self._c
 

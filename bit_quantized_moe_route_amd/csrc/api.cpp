@@ -103,6 +103,15 @@ int check_layer(const char* fn, const moe_qlayer* L, LayerInfo& out) {
     v.rot_stride = (int64_t)(2 * (int64_t)L->H + 3 * (int64_t)L->I) / 8;
     if (v.rot && (L->H % MOE_ROT_BLOCK || L->I % MOE_ROT_BLOCK))
         return fail(MOE_EUNSUPPORTED, f + ": a rotated layer needs H and I multiples of 128");
+    v.rot_in2 = MOE_ROT_BLOCK;
+    if (v.rot && L->rot_in2_block != 0 && L->rot_in2_block != MOE_ROT_BLOCK) {
+        if (L->rot_in2_block != MOE_ROT_BLOCK_WIDE)
+            return fail(MOE_EUNSUPPORTED, f + ": rot_in2_block must be 0, 128 or 512");
+        if (L->I % MOE_ROT_BLOCK_WIDE)
+            return fail(MOE_EUNSUPPORTED,
+                        f + ": the 512-block down-input rotation needs I a multiple of 512");
+        v.rot_in2 = MOE_ROT_BLOCK_WIDE;
+    }
     if (out.count[MOE_FMT_NVFP4R]) {
         if (L->nvfp4r_shift < 0 || L->nvfp4r_shift > 14)
             return fail(MOE_EUNSUPPORTED, f + ": nvfp4r_shift must be in [0, 14]");

@@ -96,6 +96,7 @@ struct LayerView {
     float res_scale;            // ... and its decode factor 2^-nvfp4r_shift
     const uint8_t* rot;         // rotation sign bits per expert (NULL: not rotated)
     int64_t rot_stride;         // bytes per expert: (2H + 3I) / 8
+    int32_t rot_in2;            // Hadamard block of the down input: 128 or 512
 };
 
 int launch_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,

@@ -395,44 +395,56 @@ int moe_pack_rot_signs(const int8_t* s_in13, const int8_t* s_og, const int8_t* s
     return MOE_OK;
 }
 
-// v <- R v for one vector: signs, then per 128-block the Hadamard butterflies
-// and 1/sqrt(128) (fp64).
-static void rotate_vec(double* v, int32_t n, const int8_t* s) {
-    const double norm = 1.0 / std::sqrt((double)MOE_ROT_BLOCK);
+// v <- R v for one vector: signs, then per block of b entries the Hadamard
+// butterflies and 1/sqrt(b) (fp64).
+static void rotate_vec(double* v, int32_t n, const int8_t* s, int32_t b) {
+    const double norm = 1.0 / std::sqrt((double)b);
     for (int32_t i = 0; i < n; ++i) v[i] *= s[i];
-    for (int32_t b0 = 0; b0 < n; b0 += MOE_ROT_BLOCK) {
+    for (int32_t b0 = 0; b0 < n; b0 += b) {
         double* w = v + b0;
-        for (int len = 1; len < MOE_ROT_BLOCK; len <<= 1)
-            for (int i = 0; i < MOE_ROT_BLOCK; i += 2 * len)
+        for (int len = 1; len < b; len <<= 1)
+            for (int i = 0; i < b; i += 2 * len)
                 for (int j = i; j < i + len; ++j) {
                     const double a = w[j], c = w[j + len];
                     w[j] = a + c;
                     w[j + len] = a - c;
                 }
-        for (int i = 0; i < MOE_ROT_BLOCK; ++i) w[i] *= norm;
+        for (int i = 0; i < b; ++i) w[i] *= norm;
     }
 }
 
-int moe_rotate_matrix(const float* w, int32_t n_out, int32_t n_in, const int8_t* s_out,
-                      const int8_t* s_in, float* out) {
+static bool rot_block_ok(int32_t b) { return b == MOE_ROT_BLOCK || b == MOE_ROT_BLOCK_WIDE; }
+
+int moe_rotate_matrix_blocks(const float* w, int32_t n_out, int32_t n_in, const int8_t* s_out,
+                             const int8_t* s_in, int32_t block_out, int32_t block_in,
+                             float* out) {
     if (!w || !s_out || !s_in || !out) return fail(MOE_EINVAL, "moe_rotate_matrix: null pointer");
-    if (n_out <= 0 || n_in <= 0 || n_out % MOE_ROT_BLOCK || n_in % MOE_ROT_BLOCK)
-        return fail(MOE_EINVAL, "moe_rotate_matrix: sizes must be positive multiples of 128");
+    if (!rot_block_ok(block_out) || !rot_block_ok(block_in))
+        return fail(MOE_EINVAL, "moe_rotate_matrix: a block must be 128 or 512");
+    if (n_out <= 0 || n_in <= 0 || n_out % block_out || n_in % block_in)
+        return fail(MOE_EINVAL, "moe_rotate_matrix: sizes must be positive multiples of the blocks");
     for (int32_t i = 0; i < n_in; ++i)
         if (s_in[i] != 1 && s_in[i] != -1) return fail(MOE_EINVAL, "moe_rotate_matrix: bad sign");
     for (int32_t i = 0; i < n_out; ++i)
         if (s_out[i] != 1 && s_out[i] != -1) return fail(MOE_EINVAL, "moe_rotate_matrix: bad sign");
     std::vector<double> m((size_t)n_out * n_in);
     for (size_t i = 0; i < m.size(); ++i) m[i] = w[i];
-    for (int32_t o = 0; o < n_out; ++o) rotate_vec(&m[(size_t)o * n_in], n_in, s_in);  // W R_in^T
+    for (int32_t o = 0; o < n_out; ++o)                                               // W R_in^T
+        rotate_vec(&m[(size_t)o * n_in], n_in, s_in, block_in);
     std::vector<double> col(n_out);
     for (int32_t c = 0; c < n_in; ++c) {                                               // R_out (.)
         for (int32_t o = 0; o < n_out; ++o) col[o] = m[(size_t)o * n_in + c];
-        rotate_vec(col.data(), n_out, s_out);
+        rotate_vec(col.data(), n_out, s_out, block_out);
         for (int32_t o = 0; o < n_out; ++o) m[(size_t)o * n_in + c] = col[o];
     }
     for (size_t i = 0; i < m.size(); ++i) out[i] = (float)m[i];
     return MOE_OK;
+}
+
+int moe_rotate_matrix(const float* w, int32_t n_out, int32_t n_in, const int8_t* s_out,
+                      const int8_t* s_in, float* out) {
+    return moe_rotate_matrix_blocks(w, n_out, n_in, s_out, s_in, MOE_ROT_BLOCK, MOE_ROT_BLOCK,
+                                    out);
 }
 
 int moe_record_table(const uint8_t* fmt_host, int32_t E, int32_t* rec, int32_t* n_by_fmt) {

@@ -12,8 +12,13 @@
 //                              h = silu(g) * u,
 //                              h'[r] = H (s_in2[e] * h) / 16               -> fp16
 //   k_rot<2> (down output):    y[r]  = s_o2[e] * H y'[r] / 8               (in place)
+//   k_rot<3> (middle, wide):   as k_rot<1> with h'[r] = H_512 (s_in2[e] * h) / 32
 //
-// for every permuted row r of expert e and token t = perm_src[r] / k.  A
+// for every permuted row r of expert e and token t = perm_src[r] / k.
+// k_rot<3> serves the same Method's wide variant of the down projection's
+// input side (random signs and one Hadamard-512 per 512 intermediate
+// channels): the factors 1/sqrt(512) and 1/sqrt(128) of that matrix fold into
+// 1/32 and 1/8 (32 * 8 = 256), so the down output step stays k_rot<2>.  A
 // workgroup of 4 waves owns 4 spw 256-element spans of a row (all of it for
 // many rows, 4 spans for few, so that a decode step still has enough
 // workgroups); wave w takes spans w, w + 4, ...: lane L holds elements
@@ -22,6 +27,10 @@
 // contiguous 16-byte-per-lane load or store, and a block's seven butterfly
 // stages are two in-lane stages and five lane exchanges inside a half-wave.
 // The next span's loads are issued before the current span is transformed.
+// k_rot<3>'s unit is a 512-block, two adjacent spans in one wave (lane L
+// holds elements 4L .. 4L+3 of each): Sylvester's H_512 = H_4 (x) H_128 adds
+// two stages to the spans' 128-point transforms, one across the half-waves
+// (element bit 7) and one between the two spans in-lane (bit 8).
 // A row of an odd number of 128-blocks ends with a half span: its upper
 // half-wave neither loads nor stores (its butterflies never mix with the
 // lower half's).
@@ -90,13 +99,14 @@ struct RotArgs {
     int64_t sign_stride;
     const uint16_t* x;      // MODE 0: bf16 tokens [T, H]
     _Float16* xrot;         // MODE 0: out [rows, H]
-    const float* gu;        // MODE 1: g' | u' [rows, 2I]
-    _Float16* h16;          // MODE 1: out h' [rows, I]
+    const float* gu;        // MODE 1, 3: g' | u' [rows, 2I]
+    _Float16* h16;          // MODE 1, 3: out h' [rows, I]
     float* y;               // MODE 2: [rows, H] in place
     int E, H, I, k, rows;
     int nspan;              // 256-element spans per row, the last maybe half
+                            // (MODE 3: 512-blocks)
     int half_tail;          // the row ends with a half span
-    int spw;                // spans per wave
+    int spw;                // spans (MODE 3: 512-blocks) per wave
     int nwg;                // workgroups per row
 };
 
@@ -158,6 +168,56 @@ __global__ __launch_bounds__(256) void k_rot(RotArgs A) {
             g = gn;
             u = un;
         }
+    } else if constexpr (MODE == 3) {
+        // unit p = spans 2p and 2p + 1 (I is a multiple of 512: no tail)
+        const float* gp = A.gu + (int64_t)r * (2 * A.I) + o;
+        _Float16* dst = A.h16 + (int64_t)r * A.I + o;
+        const uint8_t* s_og = sg + A.H / 8;
+        const uint8_t* s_ou = s_og + A.I / 8;
+        const uint8_t* s_i2 = s_ou + A.I / 8;
+        const bool hi = lane >= 32;
+        f32x4 g[2], u[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            g[j] = *reinterpret_cast<const f32x4*>(gp + 256 * (2 * s0 + j));
+            u[j] = *reinterpret_cast<const f32x4*>(gp + A.I + 256 * (2 * s0 + j));
+        }
+        for (int p = s0; p < send; p += 4) {
+            f32x4 gn[2] = {g[0], g[1]}, un[2] = {u[0], u[1]};
+            if (p + 4 < send) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    gn[j] = *reinterpret_cast<const f32x4*>(gp + 256 * (2 * (p + 4) + j));
+                    un[j] = *reinterpret_cast<const f32x4*>(gp + A.I + 256 * (2 * (p + 4) + j));
+                }
+            }
+            f32x4 h[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int s = 2 * p + j;
+                fwht128(g[j], lane);
+                fwht128(u[j], lane);
+                const f32x4 gj = g[j] * signs4(s_og, s, lane, true) * 0.125f;
+                const f32x4 uj = u[j] * signs4(s_ou, s, lane, true) * 0.125f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) h[j][q] = silu_mul_r(gj[q], uj[q]);
+                h[j] = h[j] * signs4(s_i2, s, lane, true);
+                fwht128(h[j], lane);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {   // element bit 7: the other half-wave
+                    const float t = __shfl_xor(h[j][q], 32);
+                    h[j][q] = hi ? t - h[j][q] : h[j][q] + t;
+                }
+            }
+            // element bit 8: the two spans
+            *reinterpret_cast<f16x4*>(dst + 256 * (2 * p)) = to_f16x4(h[0] + h[1], 0.03125f);
+            *reinterpret_cast<f16x4*>(dst + 256 * (2 * p + 1)) = to_f16x4(h[0] - h[1], 0.03125f);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                g[j] = gn[j];
+                u[j] = un[j];
+            }
+        }
     } else {
         float* yp = A.y + (int64_t)r * A.H + o;
         const uint8_t* s_o2 = sg + A.H / 8 + 3 * (A.I / 8);
@@ -181,8 +241,11 @@ constexpr int kRotWholeRowMin = 1024;   // rows from which a workgroup takes a w
 
 template <int MODE>
 int launch_rot(RotArgs a, int n, hipStream_t s) {
-    a.nspan = (n + 255) / 256;
-    a.half_tail = n % 256 != 0;
+    // units of a row: 256-element spans (the last maybe half), or 512-blocks
+    // for the wide middle step (n a multiple of 512)
+    const int unit = MODE == 3 ? 512 : 256;
+    a.nspan = (n + unit - 1) / unit;
+    a.half_tail = n % unit != 0;
     // whole rows per workgroup once there are enough rows to fill the chip
     a.spw = a.rows >= kRotWholeRowMin ? (a.nspan + 3) / 4 : 1;
     a.nwg = (a.nspan + 4 * a.spw - 1) / (4 * a.spw);
@@ -221,6 +284,10 @@ int launch_rot_mid(const LayerView& L, const float* gu, const int32_t* offsets, 
     RotArgs a = rot_args(L, offsets, rows);
     a.gu = gu;
     a.h16 = reinterpret_cast<_Float16*>(h16);
+    if (L.rot_in2 == MOE_ROT_BLOCK_WIDE) {
+        if (L.I % MOE_ROT_BLOCK_WIDE) return fail(MOE_EUNSUPPORTED, "rotation: I % 512 != 0");
+        return launch_rot<3>(a, L.I, reinterpret_cast<hipStream_t>(stream));
+    }
     return launch_rot<1>(a, L.I, reinterpret_cast<hipStream_t>(stream));
 }
 

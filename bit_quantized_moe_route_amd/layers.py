@@ -20,7 +20,7 @@ from . import (FMT_BF16, FMT_NVFP4, FMT_NVFP4R, FMT_VQ, FMT_VQ8, FMT_VQ8_RATES, 
 def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=None,
                 codebook_stride=0, vq8_codes=None, codebooks8=None, vq8_m=0, bf16_weights=None,
                 device="cuda", workers=8, resident_formats=None, rot_signs=None,
-                nvfp4r_shift=None):
+                nvfp4r_shift=None, rot_in2_block=128):
     """Build a QLayer.
 
     nvfp4_weights(e, proj) -> fp32 [n, kin] source weights of an NVFP4 expert
@@ -48,6 +48,8 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         s_out2 [H]) int8 +-1: the layer's matrices are stored rotated (the
         providers above return the rotated matrices) and these are each
         expert's signs.
+    rot_in2_block: the Hadamard block of the down projection's input side of
+        a rotated layer (128, or 512 for the wide variant).
     """
     import torch
 
@@ -97,7 +99,8 @@ def build_layer(E, H, I, fmt_host, nvfp4_weights=None, vq_codes=None, codebooks=
         layer.pools[key].copy_(torch.from_numpy(arr))
     if rot_signs is not None:
         from . import pack_rot_signs
-        layer.set_rot_signs(np.stack([pack_rot_signs(*rot_signs(e), H, I) for e in range(E)]))
+        layer.set_rot_signs(np.stack([pack_rot_signs(*rot_signs(e), H, I) for e in range(E)]),
+                            in2_block=rot_in2_block)
     if layer.pools[(FMT_VQ, 0)] is not None:
         layer.set_codebooks(codebooks, codebook_stride)
     if any(layer.pools[(f, 0)] is not None for f in (FMT_VQ8,) + FMT_VQ8_RATES):

@@ -38,8 +38,9 @@
  *   - a fixed expert-combine order (the order changes the bits):
  *     "GLM-5.3-Flash-TR3-8bpw (K8)", Fidelity / Excess over control.
  *   - stored matrices rotated by random signs and a Hadamard-128 transform
- *     on both sides, the activations rotated online:
- *     "GLM-5.3 Vision NestQuant 1.75-4 bit", Method.
+ *     on both sides, the activations rotated online, with the wide variant
+ *     of the down projection's input side (one Hadamard-512 per 512
+ *     intermediate channels): "GLM-5.3 Vision NestQuant 1.75-4 bit", Method.
  *   - a nested two-level format, a base plus a residual plane that lifts an
  *     expert to the higher tier at serving time with the base bytes
  *     unchanged: "GLM-5.3 Vision NestQuant 1.75-4 bit", introduction.
@@ -124,6 +125,7 @@ extern "C" {
 #define MOE_VQ8_NCODE 256     /* entries of each small codebook (uint8 codes) */
 #define MOE_VQ8_MAX_M 3       /* small codebooks per group */
 #define MOE_ROT_BLOCK 128     /* Hadamard block of rotated layers */
+#define MOE_ROT_BLOCK_WIDE 512 /* the down-input block of the wide variant */
 
 /*
  * A packed expert layer.  Host struct; the pointers inside are [device]
@@ -190,6 +192,16 @@ extern "C" {
  *                   input (shared by gate and up), the gate output, the up
  *                   output, the down input and the down output.  Needs H and
  *                   I multiples of 128.
+ *   rot_in2_block   the Hadamard block of the down projection's input side
+ *                   of a rotated layer: 0 or MOE_ROT_BLOCK (128, like every
+ *                   other side), or MOE_ROT_BLOCK_WIDE (512: R_in2 =
+ *                   blockdiag(H_512/sqrt(512)) diag(s), the page's variant
+ *                   for the down projections of some layers -- random signs
+ *                   and one Hadamard-512 per tensor-parallel shard of the
+ *                   intermediate dimension, with a flat input-channel scale,
+ *                   "GLM-5.3 Vision NestQuant 1.75-4 bit", Method; needs I a
+ *                   multiple of 512).  Any other value: MOE_EUNSUPPORTED.
+ *                   Ignored when rot_signs is NULL.
  *   record_mode     MOE_REC_COMPACT: index(e) = e's rank among the experts of
  *                   its format (rec from moe_record_table);
  *                   MOE_REC_RESIDENT: every pool that is used holds a record for
@@ -223,7 +235,7 @@ typedef struct moe_qlayer {
     const void* bf16_w13;   int64_t bf16_w13_stride;
     const void* bf16_w2;    int64_t bf16_w2_stride;
     int32_t record_mode;
-    int32_t reserved;
+    int32_t rot_in2_block;
     const uint8_t* rot_signs;
     const void* nvfp4r_w13; int64_t nvfp4r_w13_stride;
     const void* nvfp4r_w2;  int64_t nvfp4r_w2_stride;
@@ -344,8 +356,10 @@ size_t moe_ffn_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k);
  *   its expert's input signs (x' = H_128 (s x) / 16, fp16), the stored
  *   matrices multiply x', the gate and up products are rotated back
  *   (g = s H_128 g' / 8) before SwiGLU, h is rotated for the down product
- *   (h' = H_128 (s h) / 16) and its output rotated back (y = s H_128 y' / 8);
- *   the powers of two make the rotations' 1/sqrt(128) factors exact.
+ *   (h' = H_128 (s h) / 16; with rot_in2_block 512, h' = H_512 (s h) / 32)
+ *   and its output rotated back (y = s H_128 y' / 8); the powers of two make
+ *   the rotations' 1/sqrt(128) and 1/sqrt(512) factors exact (16 * 8 = 128,
+ *   32 * 8 = 256 = sqrt(128 * 512)).
  *   Requirements: H and I multiples of 16 (of 128 for a rotated layer);
  *   every format tag in layer->fmt_host must be one of MOE_FMT_*, else
  *   MOE_EUNSUPPORTED; every pool that a tag refers to must be non-NULL.
@@ -362,8 +376,8 @@ int moe_expert_ffn_q(const moe_qlayer* layer, const uint16_t* x_bf16,
  *
  * moe_expert_gateup_q -- h[i] = silu(W_gate[e] x_t) * (W_up[e] x_t) for every
  *   permuted row i (e, t as above), written as fp16 to
- *   h_f16 [device] [T*k, I] (for a rotated layer: h' = H_128 (s h) / 16, the
- *   down product's input).  ws [device] >= moe_gateup_workspace_bytes(),
+ *   h_f16 [device] [T*k, I] (for a rotated layer: h' = H_128 (s h) / 16, or
+ *   H_512 (s h) / 32 with rot_in2_block 512, the down product's input).  ws [device] >= moe_gateup_workspace_bytes(),
  *   256-byte aligned (holds the fp16 copy of x, or the rotated rows).
  * moe_expert_down_q -- y_perm[i] = W_down[e] h[i] (fp32 [T*k, H]) from
  *   h_f16 [device] [T*k, I] and offsets [device] [E+1].
@@ -659,6 +673,17 @@ int moe_pack_rot_signs(const int8_t* s_in13, const int8_t* s_out_gate, const int
  */
 int moe_rotate_matrix(const float* w, int32_t n_out, int32_t n_in, const int8_t* s_out,
                       const int8_t* s_in, float* out);
+
+/*
+ * moe_rotate_matrix_blocks -- [host] the same with a Hadamard block per side:
+ * R_out = blockdiag(H_bo/sqrt(bo)) diag(s_out), R_in likewise with bi; bo and
+ * bi each MOE_ROT_BLOCK or MOE_ROT_BLOCK_WIDE, n_out a multiple of bo and n_in
+ * of bi ("GLM-5.3 Vision NestQuant 1.75-4 bit", Method: the down matrix of a
+ * wide-variant layer takes bo = 128, bi = 512).  MOE_EINVAL otherwise.
+ */
+int moe_rotate_matrix_blocks(const float* w, int32_t n_out, int32_t n_in, const int8_t* s_out,
+                             const int8_t* s_in, int32_t block_out, int32_t block_in,
+                             float* out);
 
 /*
  * moe_record_table_resident -- [host] rec [E] = (fmt << 24) | e for a layer

@@ -57,7 +57,7 @@ def build_small_layer(wl, device="cuda", resident_formats=None):
         device=device, workers=16, resident_formats=resident_formats,
         nvfp4r_shift=synth.NVFP4R_SHIFT,
         rot_signs=(lambda e: tuple(synth.rot_signs(wl, e, side) for side in range(5)))
-        if wl.rot else None)
+        if wl.rot else None, rot_in2_block=wl.rot_in2)
 
 
 def build_shared_layer(wl, device="cuda"):

@@ -588,22 +588,31 @@ def test_rot_sign_bytes_and_packing():
     assert ei.value.status == moeq.MOE_EINVAL
 
 
-def test_rotate_matrix_matches_oracle():
+@pytest.mark.parametrize("n_out,n_in,bo,bi", [(256, 384, 128, 128), (256, 1024, 128, 512),
+                                               (512, 256, 512, 128)])
+def test_rotate_matrix_matches_oracle(n_out, n_in, bo, bi):
     """The library's offline rotation (fp64 butterflies, one rounding to fp32)
     against the oracle's (fp64 block products): equal to within one fp32
-    rounding, and the inverse rotation gives the matrix back."""
-    rs = np.random.default_rng(9)
-    n_out, n_in = 256, 384
+    rounding, and the inverse rotation gives the matrix back; also with the
+    wide 512-block on one side."""
+    rs = np.random.default_rng(9 + n_in)
     w = (rs.standard_normal((n_out, n_in)) * 0.02).astype(np.float32)
     so = np.where(rs.random(n_out) < 0.5, -1, 1).astype(np.int8)
     si = np.where(rs.random(n_in) < 0.5, -1, 1).astype(np.int8)
-    got = moeq.rotate_matrix(w, so, si)
-    want = oracle.rotate_weights(w.astype(np.float64), so, si)
+    got = moeq.rotate_matrix(w, so, si, block_out=bo, block_in=bi)
+    want = oracle.rotate_weights(w.astype(np.float64), so, si, block_out=bo, block_in=bi)
     assert np.all(np.abs(got - want) <= 2.0 ** -24 * np.abs(want) + 1e-45)
-    back = oracle.unrotate_weights(got.astype(np.float64), so, si)
+    back = oracle.unrotate_weights(got.astype(np.float64), so, si, block_out=bo, block_in=bi)
     assert np.allclose(back, w, rtol=0, atol=1e-8)
+    if bo == bi == 128:
+        assert np.array_equal(moeq.rotate_matrix(w, so, si), got)
     with pytest.raises(moeq.MoeError):
         moeq.rotate_matrix(w[:, :200], so, si[:200])
+    with pytest.raises(moeq.MoeError):                       # blocks are 128 or 512
+        moeq.rotate_matrix(w, so, si, block_in=256)
+    with pytest.raises(moeq.MoeError):                       # 384 is no multiple of 512
+        moeq.rotate_matrix(np.zeros((128, 384), np.float32), so[:128],
+                           np.ones(384, np.int8), block_in=512)
 
 
 def test_rotated_layer_host_checks():
@@ -625,6 +634,19 @@ def test_rotated_layer_host_checks():
     assert rot > plain
     assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, rot - 1,
                               N) == moeq.MOE_EWORKSPACE
+    # the down-input block: 0 / 128 / 512, and 512 needs I a multiple of 512
+    for blk in (256, 64, -1, 1024):
+        d = _fake_layer(tm)
+        d.rot_signs = 0x2000
+        d.rot_in2_block = blk
+        assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, rot,
+                                  N) == moeq.MOE_EUNSUPPORTED
+    d = _fake_layer(tm)                       # I = 128
+    d.rot_signs = 0x2000
+    d.rot_in2_block = 512
+    assert L.moe_expert_ffn_q(ctypes.byref(d), fake, fake, fake, 4, 2, fake, fake, rot,
+                              N) == moeq.MOE_EUNSUPPORTED
+    assert b"512" in L.moe_last_error()
     one = _fake_layer(np.full(1, moeq.FMT_NVFP4, np.uint8))
     one.rot_signs = 0x2000
     assert L.moe_shared_ffn(ctypes.byref(one), fake, 4, fake, fake, 1 << 24,

@@ -430,15 +430,23 @@ def test_shared_expert_full(name, T):
 # ------------------------------------------------------------------ rotated storage
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("T", [1, 32])
-def test_rotated_full_sampled(T):
+@pytest.mark.parametrize("name,T", [("decode_rot", 1), ("decode_rot", 32), ("decode_rot512", 1),
+                                    ("decode_rot512", 32)])
+def test_rotated_full_sampled(name, T):
     """The decode layer stored rotated (signs + Hadamard-128 on both sides of
-    every matrix, the NVFP4 codes those of the rotated matrices): sampled
-    experts' rows against the oracle's R_out^T Q(W_rot) R_in, the combine
-    through its property."""
-    wl = synth.DECODE_ROT
-    say("rotated full", T)
+    every matrix, the NVFP4 codes those of the rotated matrices; or the wide
+    512-block on the down projection's input side): sampled experts' rows
+    against the oracle's R_out^T Q(W_rot) R_in, the combine through its
+    property.  Both workloads store the same matrices and signs, so the wide
+    one reuses the layer with its down-input block switched."""
+    import copy
+    wl = synth.WORKLOADS[name]
+    say("rotated full", name, T)
     lay = layer("decode_rot")
+    if wl.rot_in2 != lay.rot_in2_block:
+        lay = copy.copy(lay)
+        lay.rot_in2_block = wl.rot_in2
+        lay._c = None
     x_bits, lg, r = run_forward(wl, lay, T)
     ids, w, offsets, perm_src = check_routing(wl, lg, r)
     experts = pick(offsets, n=2, seed=T + 40)

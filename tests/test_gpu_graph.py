@@ -122,11 +122,14 @@ def test_graph_with_shared_expert_on_side_stream(T):
         torch.cuda.synchronize()
 
 
-def test_graph_rotated_layer():
+@pytest.mark.parametrize("in2_block,I", [(128, 128), (512, 512)])
+def test_graph_rotated_layer(in2_block, I):
     """A rotated layer's forward (three rotation launches around the GEMMs)
-    captured in a graph: replays equal the eager result bit for bit."""
-    wl = synth.small_workload("graph_rot", E=16, k=4, H=256, I=128, T=24, cfg=113, rot=True)
-    say("graph rotated")
+    captured in a graph: replays equal the eager result bit for bit (also with
+    the wide down-input rotation)."""
+    wl = synth.small_workload("graph_rot", E=16, k=4, H=256, I=I, T=24, cfg=113, rot=True,
+                              rot_in2=in2_block)
+    say("graph rotated", in2_block)
     layer = build_small_layer(wl, DEV)
     T = wl.T[0]
     lg = torch.from_numpy(synth.logits(wl, T)).to(DEV)

@@ -74,6 +74,22 @@ SMALL = {
     "rot_bf16_prefill": synth.small_workload("rot_bf16_prefill", E=6, k=2, H=256, I=128,
                                              T=200, fmt="nv_bf16", cfg=174, n_nvfp4=3,
                                              rot=True),
+    # the wide down-input rotation (signs + one Hadamard-512 per 512
+    # intermediate channels): decode, the grouped GEMM with two 512-blocks
+    # (two of a workgroup's four waves idle), rows enough for whole-row
+    # workgroups with a wave taking two blocks (I = 2560: five blocks), and a
+    # mixed-format layer
+    "rot512_nv": synth.small_workload("rot512_nv", E=16, k=4, H=384, I=512, T=37, cfg=211,
+                                      rot=True, rot_in2=512),
+    "rot512_prefill": synth.small_workload("rot512_prefill", E=8, k=2, H=256, I=1024, T=300,
+                                           logits="zipf", zipf_s=1.1, cfg=212, rot=True,
+                                           rot_in2=512),
+    "rot512_rows": synth.small_workload("rot512_rows", E=4, k=2, H=256, I=2560, T=600, cfg=213,
+                                        rot=True, rot_in2=512),
+    "rot512_mixed3": synth.small_workload("rot512_mixed3", E=24, k=6, H=384, I=512, T=70,
+                                          fmt="mixed3", logits="hot", cfg=214, n_nvfp4=8,
+                                          n_hot=4, hot_share=0.6, vq8_m=2, rot=True,
+                                          rot_in2=512),
     # VQ codes in the grouped GEMM: small codebooks in LDS (1-3 codes per
     # group) and 16-bit codes from L2, inputs not a multiple of the 256-input
     # tile (zero codes past K still select a row: masked), a rotated layer
@@ -501,25 +517,27 @@ def test_rotated_dequant_is_the_stored_matrix():
             assert np.array_equal(to_np(moeq.dequant_q(layer, e, p)).astype(np.float64), W[p])
 
 
-def test_rotation_changes_nothing_for_unrotated_weights():
+@pytest.mark.parametrize("in2_block,I,T", [(128, 128, 12), (512, 512, 12), (512, 1024, 160)])
+def test_rotation_changes_nothing_for_unrotated_weights(in2_block, I, T):
     """Storing R_out W R_in^T (the library's offline rotation, in fp32) and
     running the rotated layer gives the plain layer's output within the
-    tolerance: the online rotations undo the stored ones."""
+    tolerance: the online rotations undo the stored ones (also with the wide
+    512-block on the down projection's input side, decode and grouped GEMM)."""
     from bit_quantized_moe_route_amd.layers import build_layer
-    wl = synth.small_workload("rot_id", E=8, k=2, H=256, I=128, T=12, fmt="bf16", cfg=175)
-    say("rotation round trip")
-    T = wl.T[0]
+    wl = synth.small_workload("rot_id", E=8, k=2, H=256, I=I, T=T, fmt="bf16", cfg=175)
+    say("rotation round trip", in2_block, I, T)
     signs = {e: tuple(synth.rot_signs(wl, e, side) for side in range(5)) for e in range(wl.E)}
     sides = {0: (1, 0), 1: (2, 0), 2: (4, 3)}            # proj -> (out side, in side)
 
     def rotated(e, p):
         w = oracle.bf16_bits_to_f64(synth.bf16_weights(wl, e, p)).astype(np.float32)
         so, si = sides[p]
-        return synth.f32_to_bf16_bits(moeq.rotate_matrix(w, signs[e][so], signs[e][si]))
+        return synth.f32_to_bf16_bits(moeq.rotate_matrix(
+            w, signs[e][so], signs[e][si], block_in=in2_block if p == 2 else 128))
 
     plain = build_small_layer(wl, DEV)
     rot = build_layer(wl.E, wl.H, wl.I, synth.tier_map(wl), bf16_weights=rotated, device=DEV,
-                      workers=4, rot_signs=lambda e: signs[e])
+                      workers=4, rot_signs=lambda e: signs[e], rot_in2_block=in2_block)
     x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(DEV)
     lg = torch.from_numpy(synth.logits(wl, T)).to(DEV)
     a = moeq.forward(plain, x, lg, wl.k)["out"]
