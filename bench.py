@@ -347,10 +347,11 @@ class Runner:
 
 def fused_path(layer, T, k):
     """Whether moe_layer_forward takes its fused decode path for this batch
-    (a single-format, unrotated layer of at most 256 experts, k <= 8 and at
-    most 16 assignments): then the whole layer is two launches (three with a
-    BF16 shared expert)."""
-    return (len(set(int(f) for f in layer.fmt_host)) == 1 and layer.rot_signs is None
+    (a single-format layer of at most 256 experts, k <= 8 and at most 16
+    assignments; a rotated one with H <= 12288): then the whole layer is two
+    launches (three with a BF16 shared expert, four for a rotated layer)."""
+    return (len(set(int(f) for f in layer.fmt_host)) == 1
+            and (layer.rot_signs is None or layer.H <= 12288)
             and layer.E <= 256 and k <= 8 and T * k <= 16)
 
 

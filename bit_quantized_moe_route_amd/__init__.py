@@ -808,8 +808,9 @@ def layer_forward(layer, x, logits, k, y_shared=None, out=None, ids=None, w=None
     """The whole routed layer in one C call (moe_layer_forward): returns
     (topk_ids [T, k] int32, topk_w [T, k] fp32, out [T, H] fp32), with
     y_shared (fp32 [T, H], a shared expert's output) added after the routed
-    sum when given.  Decode batches (T*k <= 16, k <= 8) of single-format,
-    unrotated layers run fused in two launches.  With `shared` (a one-expert
+    sum when given.  Decode batches (T*k <= 16, k <= 8) of single-format
+    layers run fused in two launches (four for a rotated layer).  With
+    `shared` (a one-expert
     layer) instead of y_shared, the shared expert runs in the same C call
     (moe_layer_forward_shared; `ws` from layer_workspace(..., shared=))."""
     torch = _torch()

@@ -179,14 +179,15 @@ size_t shared_ws(const moe_qlayer* L, int64_t T) {
            align_up(shared_part_bytes(fmt, T, L->H, L->I));
 }
 
-// moe_layer_forward: the small-batch fused path needs only h [T*k, I] fp16;
-// the step-by-step path counts | offsets | perm_src | inv_perm | the permute
-// workspace | the expert-FFN workspace | y_perm [T*k, H] fp32.
+// moe_layer_forward: the small-batch fused path needs only h [T*k, I] fp16
+// (a rotated layer also the raw products and y', small_rot_ws_bytes); the
+// step-by-step path counts | offsets | perm_src | inv_perm | the permute
+// workspace | the expert-FFN workspace | y_perm [T*k, H] fp32, which is more.
 bool layer_small_ok(const LayerInfo& li, int64_t T, int32_t k) {
     int nfmt = 0;
     for (int f = MOE_FMT_NVFP4; f < kNumFmt; ++f) nfmt += li.count[f] > 0;
-    return nfmt == 1 && !li.view.rot && li.view.E <= 256 && k <= 8 &&
-           T * k <= kSmallFusedAssign;
+    return nfmt == 1 && li.view.E <= 256 && k <= 8 && T * k <= kSmallFusedAssign &&
+           (!li.view.rot || li.view.H <= kSmallRotMaxH);
 }
 
 struct LayerWs {
@@ -275,8 +276,10 @@ int run_gateup(const LayerInfo& li, const uint16_t* x_bf16, const int32_t* perm_
 }
 
 // Down projection of every format present (offsets == NULL: identity map).
+// rot_back = false leaves a rotated layer's outputs in the rotated domain
+// (launch_combine_rot rotates them back).
 int run_down(const LayerInfo& li, const uint16_t* h_f16, const int32_t* offsets, int64_t T,
-             int32_t k, float* y_perm, void* stream) {
+             int32_t k, float* y_perm, void* stream, bool rot_back = true) {
     const bool prefill = T >= kPrefillMinTokens;
     int f1, f2;
     if (!prefill && offsets && !li.view.rot && decode_pair(li, T, k, f1, f2))
@@ -296,7 +299,7 @@ int run_down(const LayerInfo& li, const uint16_t* h_f16, const int32_t* offsets,
                                              stream);
         if (st) return st;
     }
-    if (li.view.rot) return launch_rot_out(li.view, y_perm, offsets, T * k, stream);
+    if (li.view.rot && rot_back) return launch_rot_out(li.view, y_perm, offsets, T * k, stream);
     return MOE_OK;
 }
 
@@ -542,6 +545,19 @@ int moe_layer_forward(const moe_qlayer* layer, const uint16_t* x_bf16, const flo
     st = moe_route_permute(logits, T, layer->E, k, topk_ids, topk_w, counts, offsets, perm_src,
                            inv_perm, w + lw.pws, lw.ffn - lw.pws, stream);
     if (st) return st;
+    if (li.view.rot) {
+        // rotated: the down outputs stay rotated and the combine rotates each
+        // slot back (one pass over y instead of two)
+        const size_t xbytes = gateup_ws(layer, T, k);
+        uint16_t* h16 = reinterpret_cast<uint16_t*>(w + lw.ffn + xbytes);
+        st = run_gateup(li, x_bf16, perm_src, offsets, T, k, h16,
+                        reinterpret_cast<uint16_t*>(w + lw.ffn), nullptr, stream);
+        if (st) return st;
+        st = run_down(li, h16, offsets, T, k, y_perm, stream, false);
+        if (st) return st;
+        return launch_combine_rot(li.view, y_perm, inv_perm, topk_ids, topk_w, y_shared, T, k,
+                                  out, stream);
+    }
     st = moe_expert_ffn_q(layer, x_bf16, perm_src, offsets, T, k, y_perm, w + lw.ffn,
                           lw.y_perm - lw.ffn, stream);
     if (st) return st;
@@ -592,7 +608,7 @@ int moe_layer_forward_shared(const moe_qlayer* layer, const moe_qlayer* shared,
         return fail(MOE_EINVAL, "moe_layer_forward_shared: workspace must be 256-byte aligned");
     uint8_t* w = static_cast<uint8_t*>(ws);
     uint8_t* wsh = w + align_up(lw);
-    if (layer_small_ok(li, T, k) && ls.count[MOE_FMT_BF16] == 1) {
+    if (layer_small_ok(li, T, k) && !li.view.rot && ls.count[MOE_FMT_BF16] == 1) {
         int fmt = MOE_FMT_NVFP4;
         while (!li.count[fmt]) ++fmt;
         // the shared workspace as moe_shared_ffn lays it out: x16 | h16 | partials

@@ -23,6 +23,7 @@
 //     2^-14 <= |x| <= 65504) or from the fp16 activations h (down).
 #include <type_traits>
 
+#include "rot_dev.h"
 #include "topk_dev.h"
 
 namespace moeq {
@@ -220,6 +221,8 @@ struct DecodeArgs {
     float* topk_w;
     const float* y_shared; // NULL or fp32 [T, H], added after the routed sum
     float* out;            // fp32 [T, H]
+    const uint8_t* rot;    // rotated layers: sign bits per expert (rot_stride bytes each)
+    int64_t rot_stride;
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -522,11 +525,21 @@ constexpr int kMinWaves = MOEQ_MIN_WAVES;
 // already there) instead of being stored to A.y_perm.
 // The body is a device function of the workgroup's grid coordinates bid, so
 // that one launch can run it beside another kernel's workgroups.
+// Dynamic LDS of the small-codebook VQ kernels: the codebooks of the
+// projections a pass reads (gate and up, or down).
+template <class F>
+constexpr size_t codebook_lds_bytes(int phase) {
+    if constexpr (F::kVq8)
+        return (size_t)(phase == 0 ? 2 : 1) * F::CODES * MOE_VQ8_NCODE * 16;
+    else
+        return 0;
+}
+
 template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID, bool PART, bool ROT,
           bool ROUTE, bool ADDOUT = false>
 __device__ __forceinline__ void ffn_body(const DecodeArgs& A, const uint3 bid) {
     static_assert(!ROT || (PART && PHASE == 0 && !ID), "rotated gate/up writes raw products");
-    static_assert(!ROUTE || (PHASE == 0 && !ID && !PART && !ROT), "routed gate/up only");
+    static_assert(!ROUTE || (PHASE == 0 && !ID && PART == ROT), "routed gate/up only");
     static_assert(!ADDOUT || (PHASE == 1 && ID), "the down pass of a shared expert");
     constexpr bool XBF = PHASE == 0 && !ROT;        // B operand is bf16
     constexpr int NM = PHASE == 0 ? 2 * RPW : RPW;   // weight tiles per input tile
@@ -577,6 +590,44 @@ __device__ __forceinline__ void ffn_body(const DecodeArgs& A, const uint3 bid) {
         }
         __syncthreads();
     }
+    if constexpr (ROUTE && ROT) {
+        // the rotated row of this assignment, x' = H (s_in13[e] * x_t) / 16 in
+        // fp16, into LDS after the codebooks: the separate rotation pass's
+        // arithmetic (the same bits), 256-element spans per wave, lane L
+        // holding elements 4L .. 4L+3 (the upper half-wave idle in a half span)
+        // The loads of up to 8 spans per wave are issued before the first is
+        // transformed (from clamped addresses: a lane outside the row reads
+        // the lower half-wave's elements, which it never stores).
+        constexpr int UB = 8;
+        _Float16* xs = lds_cb + codebook_lds_bytes<F>(0) / 2;
+        const uint16_t* xt = A.xbf + (int64_t)(ae.r0 / A.k) * A.H + 4 * lane;
+        const uint8_t* s_in = A.rot + (int64_t)ae.e * A.rot_stride;
+        const int nspan = (A.H + 255) / 256;
+        const bool half = A.H % 256 != 0;
+        for (int sp0 = wave; sp0 < nspan; sp0 += WV * UB) {
+            uint2 raw[UB];
+            uint32_t sb[UB];
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const int sp = min(sp0 + WV * u, nspan - 1);
+                const bool in = !half || sp + 1 < nspan || lane < 32;
+                raw[u] = *reinterpret_cast<const uint2*>(xt + 256 * sp - (in ? 0 : 128));
+                sb[u] = *sign_byte(s_in, sp, in ? lane : lane - 32);
+            }
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const int sp = sp0 + WV * u;
+                if (sp >= nspan) break;
+                const bool in = !half || sp + 1 < nspan || lane < 32;
+                f32x4 v = bf16x4_to_f32(raw[u]) *
+                          signs_of(in ? sb[u] >> (4 * (lane & 1)) : 0u);
+                fwht128(v, lane);
+                if (in)
+                    *reinterpret_cast<f16x4*>(xs + 256 * sp + 4 * lane) = to_f16x4(v, 0.0625f);
+            }
+        }
+        __syncthreads();
+    }
     const int kloc = wave % KS;                      // part of the workgroup's inputs
     const int split = PART ? (int)bid.x % A.nsplit : 0;
     const int set = (PART ? (int)bid.x / A.nsplit : (int)bid.x) * SETS + wave / KS;
@@ -607,7 +658,9 @@ __device__ __forceinline__ void ffn_body(const DecodeArgs& A, const uint3 bid) {
     for (int tt = 0; tt < NTT; ++tt) {
         const int c0l = c0 + (lane & 15) + 16 * tt;
         const int c = c0l < ae.me ? c0l : c0;
-        if (F::kVq && !F::kVq8 && c0l >= ae.me)
+        if (ROUTE && ROT)   // the assignment's rotated row in LDS (every column)
+            xrow[tt] = reinterpret_cast<const uint16_t*>(lds_cb + codebook_lds_bytes<F>(0) / 2);
+        else if (F::kVq && !F::kVq8 && c0l >= ae.me)
             xrow[tt] = nullptr;     // 16-bit VQ: stream_tiles_vq substitutes its safe row
         else if (PHASE == 0)
             xrow[tt] = A.xbf + (int64_t)(ROT     ? ae.r0 + c
@@ -633,7 +686,8 @@ __device__ __forceinline__ void ffn_body(const DecodeArgs& A, const uint3 bid) {
         } else if constexpr (F::kVq && MOEQ_VQ_GATHER_AHEAD) {
             // row c0 of the expert exists: a safe row for lanes past its rows
             const uint16_t* xsafe =
-                PHASE == 0
+                ROUTE && ROT ? xrow[0]
+                : PHASE == 0
                     ? A.xbf + (int64_t)(ROT     ? ae.r0 + c0
                                         : ROUTE ? ae.r0 / A.k
                                         : ID    ? c0
@@ -798,7 +852,9 @@ __global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ 
 // (BF16 and 16-bit VQ, whose A fragments take more registers: NG groups).
 constexpr int kDcKS = 4;     // waves splitting the input dimension of a slot group
 constexpr int kDcMaxK = 8;   // k of the fused path
-template <class F, int NSL, int NG>
+// SLOTS: each slot's output rows y'[t*k + j] go to y_perm (a rotated layer:
+// the combine rotates them back per slot) instead of the weighted sum.
+template <class F, int NSL, int NG, bool SLOTS = false>
 __device__ __forceinline__ void down_combine_body(const DecodeArgs& A, const uint3 bid) {
     constexpr int KS = kDcKS, NM = NSL, WV = KS * NG;
     static_assert(NSL * NG <= 16, "slots are B columns");
@@ -889,8 +945,15 @@ __device__ __forceinline__ void down_combine_body(const DecodeArgs& A, const uin
 #pragma unroll
             for (int i = 0; i < 4; ++i) y[i] *= (float)sp[n0 + i];
         }
-        ys[sg][lane] = y;
+        if constexpr (SLOTS) {
+            if (col < nsl)
+                *reinterpret_cast<f32x4*>(A.y_perm + ((int64_t)t * A.k + j0 + col) * A.H +
+                                          16 * g + (lane >> 4) * 4) = y;
+        } else {
+            ys[sg][lane] = y;
+        }
     }
+    if constexpr (SLOTS) return;
     __syncthreads();
     if (wave != 0) return;
     // lane 16q + c of ys[sg] holds rows 4q .. 4q+3 of the group for slot NSL sg + c
@@ -908,17 +971,9 @@ __device__ __forceinline__ void down_combine_body(const DecodeArgs& A, const uin
     *reinterpret_cast<f32x4*>(A.out + n) = o;
 }
 
-template <class F, int NSL, int NG>
+template <class F, int NSL, int NG, bool SLOTS = false>
 __global__ __launch_bounds__(64 * kDcKS * NG, kMinWaves) void k_down_combine(DecodeArgs A) {
-    down_combine_body<F, NSL, NG>(A, uint3{blockIdx.x, blockIdx.y, 0u});
-}
-
-template <class F>
-constexpr size_t codebook_lds_bytes(int phase) {
-    if constexpr (F::kVq8)
-        return (size_t)(phase == 0 ? 2 : 1) * F::CODES * MOE_VQ8_NCODE * 16;
-    else
-        return 0;
+    down_combine_body<F, NSL, NG, SLOTS>(A, uint3{blockIdx.x, blockIdx.y, 0u});
 }
 
 template <class F, int NTT, int KS, int WV>
@@ -1090,6 +1145,8 @@ DecodeArgs decode_args(const LayerView& L, int fmt, const uint16_t* x_bf16,
     a.topk_w = nullptr;
     a.y_shared = nullptr;
     a.out = nullptr;
+    a.rot = L.rot;
+    a.rot_stride = L.rot_stride;
     return a;
 }
 
@@ -1117,6 +1174,41 @@ int launch_small_fmt(const DecodeArgs& a, int64_t T, hipStream_t s) {
         k_down_combine<F, 4, 2><<<g2, 128 * kDcKS, codebook_lds_bytes<F>(1), s>>>(a);
     MOEQ_CHECK_LAUNCH();
     return MOE_OK;
+}
+
+// The same for a rotated layer, in four launches: the routed gate/up with
+// each workgroup rotating its assignment's x row into LDS and writing the raw
+// products g' | u' (token order, no permutation); the middle rotation (g, u
+// back, SwiGLU, h' for the down pass) with each row's expert from topk_ids;
+// the down pass writing every slot's y' row; the combine rotating each slot
+// back.  Every value is computed as on the step-by-step path (same input
+// split, same products, same rotation arithmetic), so the output has the same
+// bits.  gu [T*k, 2I] fp32, h16 [T*k, I] fp16 and y_perm [T*k, H] fp32 are
+// workspace.
+template <class F>
+int launch_small_rot_fmt(const LayerView& L, DecodeArgs a, int64_t T, float* gu, float* y_perm,
+                         hipStream_t s) {
+    a.part = gu;
+    a.nsplit = 1;
+    a.y_perm = y_perm;
+    const int nsets = (a.I / 16 + kRpwGateup - 1) / kRpwGateup;
+    dim3 g1((unsigned)nsets, (unsigned)(T * a.k), 1u);
+    k_ffn<F, 1, 4, kRpwGateup, 0, 4, false, true, true, true>
+        <<<g1, 256, codebook_lds_bytes<F>(0) + (size_t)a.H * 2, s>>>(a);
+    MOEQ_CHECK_LAUNCH();
+    int st = launch_rot_mid(L, gu, nullptr, T * a.k, reinterpret_cast<uint16_t*>(a.h16), s,
+                            a.topk_ids);
+    if (st) return st;
+    dim3 g2((unsigned)(a.H / 16), (unsigned)T, 1u);
+    if (a.k <= 4)
+        k_down_combine<F, 4, 1, true><<<g2, 64 * kDcKS, codebook_lds_bytes<F>(1), s>>>(a);
+    else if constexpr (F::kVq8)
+        k_down_combine<F, 8, 1, true><<<g2, 64 * kDcKS, codebook_lds_bytes<F>(1), s>>>(a);
+    else
+        k_down_combine<F, 4, 2, true><<<g2, 128 * kDcKS, codebook_lds_bytes<F>(1), s>>>(a);
+    MOEQ_CHECK_LAUNCH();
+    return launch_combine_rot(L, y_perm, nullptr, a.topk_ids, a.topk_w, a.y_shared, T, a.k,
+                              a.out, s);
 }
 
 // The fused decode layer with a BF16 shared expert, in three launches:
@@ -1302,6 +1394,22 @@ int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, cons
     a.y_shared = y_shared;
     a.out = out;
     if (T == 0) return MOE_OK;
+    if (L.rot) {
+        // workspace after h16 [T*k, I]: g' | u' [T*k, 2I], then y' [T*k, H]
+        const int64_t tk = T * k;
+        float* gu = reinterpret_cast<float*>(h16 + round_up(tk * L.I, 128));
+        float* yp = gu + round_up(tk * 2 * L.I, 64);
+        if (fmt == MOE_FMT_NVFP4) return launch_small_rot_fmt<NvFmt>(L, a, T, gu, yp, s);
+        if (fmt == MOE_FMT_NVFP4R) return launch_small_rot_fmt<Nv2Fmt>(L, a, T, gu, yp, s);
+        if (fmt == MOE_FMT_BF16) return launch_small_rot_fmt<Bf16Fmt>(L, a, T, gu, yp, s);
+        if (is_vq8(fmt)) {
+            const int m = vq8_rate(fmt, L.vq8_m);
+            if (m == 1) return launch_small_rot_fmt<Vq8Fmt<1>>(L, a, T, gu, yp, s);
+            if (m == 3) return launch_small_rot_fmt<Vq8Fmt<3>>(L, a, T, gu, yp, s);
+            return launch_small_rot_fmt<Vq8Fmt<2>>(L, a, T, gu, yp, s);
+        }
+        return launch_small_rot_fmt<VqFmt>(L, a, T, gu, yp, s);
+    }
     if (fmt == MOE_FMT_NVFP4) return launch_small_fmt<NvFmt>(a, T, s);
     if (fmt == MOE_FMT_NVFP4R) return launch_small_fmt<Nv2Fmt>(a, T, s);
     if (fmt == MOE_FMT_BF16) return launch_small_fmt<Bf16Fmt>(a, T, s);

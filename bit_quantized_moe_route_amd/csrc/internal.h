@@ -112,6 +112,13 @@ int launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, i
 int launch_combine(const float* y_perm, const int32_t* inv_perm, const float* w,
                    const float* y_shared, int64_t T, int32_t k, int32_t H, float* out,
                    void* stream);
+// A rotated layer: the down outputs y' (not yet rotated back) rotated back
+// per slot with its expert's down-output signs and combined as launch_combine
+// does, the same bits as launch_rot_out followed by launch_combine
+// (inv_perm NULL: slot (t, j) is row t*k + j).
+int launch_combine_rot(const LayerView& L, const float* y_perm, const int32_t* inv_perm,
+                       const int32_t* ids, const float* w, const float* y_shared, int64_t T,
+                       int32_t k, float* out, void* stream);
 int launch_x_to_f16(const uint16_t* x, int64_t n, uint16_t* x16, void* stream);
 // gu != NULL (gate/up of a rotated layer): x is the fp16 rotated rows
 // [T*k, H] in permuted order, and the raw fp32 products g | u go to
@@ -159,18 +166,27 @@ int launch_ffn_prefill(const LayerView& L, int fmt, int n_fmt, const uint16_t* x
 // place (fp32 [rows, H]).
 int launch_rot_in(const LayerView& L, const uint16_t* x_bf16, const int32_t* perm_src,
                   const int32_t* offsets, int64_t T, int32_t k, uint16_t* xrot, void* stream);
+// row_ids != NULL: rows in assignment order, row r of expert row_ids[r]
+// (offsets unused).
 int launch_rot_mid(const LayerView& L, const float* gu, const int32_t* offsets, int64_t rows,
-                   uint16_t* h16, void* stream);
+                   uint16_t* h16, void* stream, const int32_t* row_ids = nullptr);
 int launch_rot_out(const LayerView& L, float* y, const int32_t* offsets, int64_t rows,
                    void* stream);
-// The small-batch fused layer (single-format, unrotated layers, E <= 256,
-// k <= 8, T*k <= kSmallFusedAssign): gate/up with the routing inside
-// (topk_ids / topk_w written, h16 [T*k, I] in token order), then down +
-// gated combine (+ y_shared) into out [T, H].
+// The small-batch fused layer (single-format layers, E <= 256, k <= 8,
+// T*k <= kSmallFusedAssign): gate/up with the routing inside (topk_ids /
+// topk_w written, h16 [T*k, I] in token order), then down + gated combine
+// (+ y_shared) into out [T, H].  A rotated layer (H <= kSmallRotMaxH) takes
+// four launches and after h16 (rounded up to 256 bytes) the raw products
+// [T*k, 2I] fp32 and then y' [T*k, H] fp32 (small_rot_ws_bytes in all).
 #ifndef MOEQ_SMALL_ASSIGN
 #define MOEQ_SMALL_ASSIGN 16
 #endif
 constexpr int64_t kSmallFusedAssign = MOEQ_SMALL_ASSIGN;
+constexpr int32_t kSmallRotMaxH = 12288;   // the rotated row in LDS: 2H bytes
+inline size_t small_rot_ws_bytes(int64_t T, int32_t k, int32_t H, int32_t I) {
+    const int64_t tk = T * k;
+    return (size_t)(round_up(tk * I, 128) * 2 + round_up(tk * 2 * I, 64) * 4 + tk * H * 4);
+}
 int launch_layer_small(const LayerView& L, int fmt, const uint16_t* x_bf16, const float* logits,
                        int64_t T, int32_t k, int32_t* topk_ids, float* topk_w, uint16_t* h16,
                        const float* y_shared, float* out, void* stream);

@@ -1,0 +1,58 @@
+// Device helpers of the online rotations, shared by the rotation kernels and
+// the rotated layer's combine (the same butterflies in the same order, so
+// both give the same bits).
+#pragma once
+
+#include "dev_common.h"
+
+namespace moeq {
+namespace {
+
+// Unnormalised Walsh-Hadamard transform of each half-wave's 128 values
+// (Sylvester order: out[i] = sum_j (-1)^popcount(i & j) in[j]), lane L
+// holding elements 4 (L & 31) + q.
+__device__ __forceinline__ void fwht128(f32x4& v, int lane) {
+    float a = v[0] + v[1], b = v[0] - v[1], c = v[2] + v[3], d = v[2] - v[3];
+    v = f32x4{a + c, b + d, a - c, b - d};
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+        const bool hi = (lane >> s) & 1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float p = __shfl_xor(v[q], 1 << s);
+            v[q] = hi ? p - v[q] : v[q] + p;
+        }
+    }
+}
+
+// +1 / -1 of 4 elements from their sign bits (bit set = -1).
+__device__ __forceinline__ f32x4 signs_of(uint32_t bits) {
+    return f32x4{bits & 1 ? -1.f : 1.f, bits & 2 ? -1.f : 1.f, bits & 4 ? -1.f : 1.f,
+                 bits & 8 ? -1.f : 1.f};
+}
+
+// The byte of a section holding the sign bits of the lane's 4 elements of
+// span s (its nibble: lane & 1).
+__device__ __forceinline__ const uint8_t* sign_byte(const uint8_t* sec, int s, int lane) {
+    return sec + 32 * s + (lane >> 1);
+}
+
+// Signs of the lane's 4 elements of span s of a section (bit set = -1);
+// +1 for a lane outside the row.
+__device__ __forceinline__ f32x4 signs4(const uint8_t* sec, int s, int lane, bool in) {
+    const uint32_t bits = in ? *sign_byte(sec, s, lane) >> (4 * (lane & 1)) : 0u;
+    return signs_of(bits);
+}
+
+__device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 v) {
+    return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
+
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 v, float sc) {
+    return f16x4{(_Float16)(v[0] * sc), (_Float16)(v[1] * sc), (_Float16)(v[2] * sc),
+                 (_Float16)(v[3] * sc)};
+}
+
+}  // namespace
+}  // namespace moeq

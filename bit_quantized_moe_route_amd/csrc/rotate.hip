@@ -34,28 +34,11 @@
 // A row of an odd number of 128-blocks ends with a half span: its upper
 // half-wave neither loads nor stores (its butterflies never mix with the
 // lower half's).
-#include "dev_common.h"
+#include "rot_dev.h"
 
 namespace moeq {
 
 namespace {
-
-// Unnormalised Walsh-Hadamard transform of each half-wave's 128 values
-// (Sylvester order: out[i] = sum_j (-1)^popcount(i & j) in[j]), lane L
-// holding elements 4 (L & 31) + q.
-__device__ __forceinline__ void fwht128(f32x4& v, int lane) {
-    float a = v[0] + v[1], b = v[0] - v[1], c = v[2] + v[3], d = v[2] - v[3];
-    v = f32x4{a + c, b + d, a - c, b - d};
-#pragma unroll
-    for (int s = 0; s < 5; ++s) {
-        const bool hi = (lane >> s) & 1;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float p = __shfl_xor(v[q], 1 << s);
-            v[q] = hi ? p - v[q] : v[q] + p;
-        }
-    }
-}
 
 // The expert whose permuted rows hold row r: the number of experts whose
 // segment ends at or before r (offsets[E] = rows > r).  One round of loads.
@@ -70,30 +53,13 @@ __device__ __forceinline__ int row_expert(const int32_t* __restrict__ offsets, i
     return n;
 }
 
-// Signs of the lane's 4 elements of span s of a section (bit set = -1);
-// +1 for a lane outside the row.
-__device__ __forceinline__ f32x4 signs4(const uint8_t* sec, int s, int lane, bool in) {
-    const uint32_t bits = in ? sec[32 * s + (lane >> 1)] >> (4 * (lane & 1)) : 0u;
-    return f32x4{bits & 1 ? -1.f : 1.f, bits & 2 ? -1.f : 1.f, bits & 4 ? -1.f : 1.f,
-                 bits & 8 ? -1.f : 1.f};
-}
-
 __device__ __forceinline__ float silu_mul_r(float g, float u) {
     return g * u / (1.0f + expf(-g));
 }
 
-__device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 v) {
-    return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
-}
-
-__device__ __forceinline__ f16x4 to_f16x4(f32x4 v, float sc) {
-    return f16x4{(_Float16)(v[0] * sc), (_Float16)(v[1] * sc), (_Float16)(v[2] * sc),
-                 (_Float16)(v[3] * sc)};
-}
-
 struct RotArgs {
     const int32_t* offsets;
+    const int32_t* row_ids;   // MODE 1, 3: row r is of expert row_ids[r] (NULL: from offsets)
     const int32_t* perm_src;
     const uint8_t* signs;   // per expert: s_in13 | s_og | s_ou | s_in2 | s_o2
     int64_t sign_stride;
@@ -118,7 +84,7 @@ __global__ __launch_bounds__(256) void k_rot(RotArgs A) {
     const int s0 = (blockIdx.x % A.nwg) * 4 * A.spw + wave;   // first span of the wave
     const int send = min(A.nspan, s0 - wave + 4 * A.spw);     // end of the workgroup's spans
     if (s0 >= send) return;
-    const int e = row_expert(A.offsets, A.E, r, lane);
+    const int e = A.row_ids ? A.row_ids[r] : row_expert(A.offsets, A.E, r, lane);
     const uint8_t* sg = A.signs + (int64_t)e * A.sign_stride;
     const int o = 4 * lane;                                   // lane's offset in a span
     // does the lane's part of span s lie inside the row?
@@ -280,8 +246,9 @@ int launch_rot_in(const LayerView& L, const uint16_t* x_bf16, const int32_t* per
 }
 
 int launch_rot_mid(const LayerView& L, const float* gu, const int32_t* offsets, int64_t rows,
-                   uint16_t* h16, void* stream) {
+                   uint16_t* h16, void* stream, const int32_t* row_ids) {
     RotArgs a = rot_args(L, offsets, rows);
+    a.row_ids = row_ids;
     a.gu = gu;
     a.h16 = reinterpret_cast<_Float16*>(h16);
     if (L.rot_in2 == MOE_ROT_BLOCK_WIDE) {

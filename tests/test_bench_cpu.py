@@ -128,19 +128,24 @@ def test_compact_workload_entry_is_small_and_complete():
 
 
 class _FakeLayer:
-    def __init__(self, fmts, E=256, rot=None):
+    def __init__(self, fmts, E=256, rot=None, H=6144):
         self.fmt_host = np.array(fmts, np.uint8)
         self.E = E
+        self.H = H
         self.rot_signs = rot
 
 
 def test_fused_path_rule_matches_the_library():
-    """moe_layer_forward fuses single-format, unrotated layers of at most 256
-    experts for k <= 8 and T k <= 16 assignments."""
+    """moe_layer_forward fuses single-format layers of at most 256 experts for
+    k <= 8 and T k <= 16 assignments (rotated ones up to H = 12288, their
+    rotated row held in LDS)."""
     one = _FakeLayer([1] * 256)
     assert bench.fused_path(one, 1, 8) and bench.fused_path(one, 2, 8)
     assert not bench.fused_path(one, 3, 8)
     assert bench.fused_path(one, 16, 1) and not bench.fused_path(one, 4, 9)
     assert not bench.fused_path(_FakeLayer([1] * 255 + [2]), 1, 8)
     assert not bench.fused_path(_FakeLayer([1] * 512, E=512), 1, 8)
-    assert not bench.fused_path(_FakeLayer([1] * 256, rot=object()), 1, 8)
+    assert bench.fused_path(_FakeLayer([1] * 256, rot=object()), 1, 8)
+    assert bench.fused_path(_FakeLayer([1] * 256, rot=object(), H=12288), 2, 8)
+    assert not bench.fused_path(_FakeLayer([1] * 256, rot=object(), H=12416), 1, 8)
+    assert not bench.fused_path(_FakeLayer([1] * 256, rot=object()), 3, 8)

@@ -122,6 +122,34 @@ def test_graph_with_shared_expert_on_side_stream(T):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("T,in2_block,I", [(2, 128, 128), (2, 512, 512)])
+def test_graph_rotated_fused_layer(T, in2_block, I):
+    """A rotated layer's fused small-batch forward (moe_layer_forward: four
+    launches) captured in a graph: replays equal the eager call bit for bit,
+    with the program's own calls on other inputs between the replays."""
+    wl = synth.small_workload("graph_rot_fused", E=16, k=4, H=384, I=I, T=T, cfg=114, rot=True,
+                              rot_in2=in2_block)
+    say("graph rotated fused", in2_block)
+    layer = build_small_layer(wl, DEV)
+    lg = torch.from_numpy(synth.logits(wl, T)).to(DEV)
+    x = torch.from_numpy(synth.activations(wl, T).view(np.int16)).to(DEV)
+    ws = moeq.layer_workspace(layer, T, wl.k)
+    ids, w, out = moeq.layer_forward(layer, x, lg, wl.k, ws=ws)
+    eager = out.clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _, _, cap = moeq.layer_forward(layer, x, lg, wl.k, ids=ids, w=w, ws=ws)
+    other = torch.from_numpy(synth.logits(wl, T, rep=2)).to(DEV)
+    for i in range(3):
+        cap.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cap, eager), f"replay {i}"
+        moeq.layer_forward(layer, x, other, wl.k, ws=ws)
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("in2_block,I", [(128, 128), (512, 512)])
 def test_graph_rotated_layer(in2_block, I):
     """A rotated layer's forward (three rotation launches around the GEMMs)

@@ -1,13 +1,14 @@
 """GPU parity of the one-call layer forward (moe_layer_forward).
 
-Decode batches (T*k <= 16, k <= 8) of single-format, unrotated layers run the
-fused path (routing inside the gate/up kernel, the gated combine inside the
-down kernel, no permutation).  Its outputs are checked against the oracle
+Decode batches (T*k <= 16, k <= 8) of single-format layers run the fused path
+(routing inside the gate/up kernel, the gated combine inside the down kernel,
+no permutation; a rotated layer rotates x into LDS inside the gate/up kernel
+and its down outputs back inside the combine).  Its outputs are checked against the oracle
 (routing bit-exact, rows within the FFN tolerance) and against the
 step-by-step calls on the same inputs, which they must equal bit for bit:
 both take each expert's products, partial sums and the combine in the same
-order.  Batches outside the fused path (more assignments, mixed formats,
-rotated layers) go through the step-by-step calls and must equal them too."""
+order.  Batches outside the fused path (more assignments, mixed formats) go
+through the step-by-step calls and must equal them too."""
 
 import numpy as np
 import pytest
@@ -51,7 +52,31 @@ CASES = {
     "tiny_t9": (synth.TINY, 9),
     "mixed": (synth.small_workload("lf_mixed", E=24, k=6, H=384, I=96, T=2, fmt="mixed",
                                    logits="hot", cfg=188, n_nvfp4=9, n_hot=4, hot_share=0.6), 2),
+    # rotated layers: small batches fused (the rotated x row in LDS, the
+    # rotations between the passes, the down outputs rotated back inside the
+    # combine): rows ending in half a 256-span, two slot groups of 4 (k = 8),
+    # small-codebook and 16-bit VQ, BF16, the wide down-input rotation
     "rot": (synth.small_workload("lf_rot", E=16, k=4, H=384, I=256, T=1, cfg=189, rot=True), 1),
+    "rot_k8_t2": (synth.small_workload("lf_rot_k8", E=32, k=8, H=256, I=128, T=2, cfg=219,
+                                       rot=True), 2),
+    "rot_vq8": (synth.small_workload("lf_rot_vq8", E=8, k=2, H=512, I=128, T=3, fmt="vq8",
+                                     cfg=220, vq8_m=2, rot=True), 3),
+    "rot_vq": (synth.small_workload("lf_rot_vq", E=8, k=2, H=256, I=128, T=4, fmt="vq",
+                                    cfg=221, rot=True), 4),
+    "rot_bf16": (synth.small_workload("lf_rot_bf16", E=8, k=3, H=384, I=128, T=2, fmt="bf16",
+                                      cfg=222, rot=True), 2),
+    # ... and outside the fused path the combine rotates the down outputs back:
+    # many decode tokens with a half 256-span at the end of the rows, the
+    # grouped-GEMM path, the wide down-input rotation (also fused: 9
+    # assignments), and k = 16
+    "rot_t40": (synth.small_workload("lf_rot_t40", E=16, k=4, H=384, I=256, T=40, cfg=215,
+                                     rot=True), 40),
+    "rot_prefill": (synth.small_workload("lf_rot_pf", E=8, k=2, H=256, I=256, T=160,
+                                         logits="zipf", zipf_s=1.1, cfg=216, rot=True), 160),
+    "rot512": (synth.small_workload("lf_rot512", E=12, k=3, H=384, I=512, T=3, cfg=217,
+                                    rot=True, rot_in2=512), 3),
+    "rot_k16": (synth.small_workload("lf_rot_k16", E=32, k=16, H=128, I=128, T=5, cfg=218,
+                                     rot=True), 5),
     # the edges of the fused path: exactly 16 assignments (fused) and 17
     # (not), k = 9 > 8 at one token (not), 257 experts (not: more than 256)
     "edge_16": (synth.small_workload("lf_edge16", E=24, k=4, H=256, I=128, T=4, cfg=192), 4),
