@@ -54,5 +54,10 @@ __device__ __forceinline__ f16x4 to_f16x4(f32x4 v, float sc) {
                  (_Float16)(v[3] * sc)};
 }
 
+// silu(g) * u of the middle rotation step.
+__device__ __forceinline__ float silu_mul_r(float g, float u) {
+    return g * u / (1.0f + expf(-g));
+}
+
 }  // namespace
 }  // namespace moeq

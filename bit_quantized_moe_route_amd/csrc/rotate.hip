@@ -53,10 +53,6 @@ __device__ __forceinline__ int row_expert(const int32_t* __restrict__ offsets, i
     return n;
 }
 
-__device__ __forceinline__ float silu_mul_r(float g, float u) {
-    return g * u / (1.0f + expf(-g));
-}
-
 struct RotArgs {
     const int32_t* offsets;
     const int32_t* row_ids;   // MODE 1, 3: row r is of expert row_ids[r] (NULL: from offsets)

@@ -104,6 +104,11 @@ SMALL = {
                                        cfg=129),
     "rot_vq8_prefill": synth.small_workload("rot_vq8_prefill", E=8, k=2, H=256, I=128, T=200,
                                             fmt="vq8", cfg=176, vq8_m=2, rot=True),
+    # rotated 16-bit VQ in the grouped GEMM (128-token items: the middle
+    # rotation's epilogue takes four 32-token tiles), two 128-channel blocks
+    "rot_vq_prefill": synth.small_workload("rot_vq_prefill", E=8, k=2, H=256, I=256, T=200,
+                                           fmt="vq", logits="zipf", zipf_s=1.1, cfg=223,
+                                           rot=True),
     # small-codebook VQ experts at mixed rates (1, 2 and 3 bits per weight in
     # one layer, three shared codebooks per projection): decode with ragged
     # shapes, the grouped GEMM under Zipf routing
