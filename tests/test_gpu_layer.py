@@ -65,6 +65,13 @@ CASES = {
                                     cfg=221, rot=True), 4),
     "rot_bf16": (synth.small_workload("lf_rot_bf16", E=8, k=3, H=384, I=128, T=2, fmt="bf16",
                                       cfg=222, rot=True), 2),
+    # the fused rotated path holds the rotated x row in LDS up to H = 12288
+    # (with 3-code small codebooks, 64 KB of LDS in all); one block more runs
+    # the step-by-step calls
+    "rot_h12288": (synth.small_workload("lf_rot_h12288", E=4, k=2, H=12288, I=128, T=1,
+                                        fmt="vq8", cfg=224, vq8_m=3, rot=True), 1),
+    "rot_h12416": (synth.small_workload("lf_rot_h12416", E=4, k=2, H=12416, I=128, T=1,
+                                        cfg=225, rot=True), 1),
     # ... and outside the fused path the combine rotates the down outputs back:
     # many decode tokens with a half 256-span at the end of the rows, the
     # grouped-GEMM path, the wide down-input rotation (also fused: 9
