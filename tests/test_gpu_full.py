@@ -455,6 +455,36 @@ def test_rotated_full_sampled(name, T):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["decode_rot", "decode_rot512"])
+def test_rotated_prefill_full_sampled(name):
+    """The rotated decode layer (and its wide down-input form) at T = 4096
+    with the prefill routing: x rotated per assignment, the grouped GEMM's raw
+    products, the middle rotation, and the combine rotating the down outputs
+    back.  Sampled experts' rows against the oracle (the busiest, a random one
+    and the least busy), the combine through its property."""
+    import copy
+    import dataclasses
+    base = synth.WORKLOADS[name]
+    # the prefill batch's seed slot and routing; the layer's weights and
+    # signs (looked up by name for the oracle) are unchanged
+    wl = dataclasses.replace(base, cfg=2, T=(4096,), logits="zipf", zipf_s=1.1)
+    say("rotated prefill full", name)
+    lay = layer("decode_rot")
+    if base.rot_in2 != lay.rot_in2_block:
+        lay = copy.copy(lay)
+        lay.rot_in2_block = base.rot_in2
+        lay._c = None
+    x_bits, lg, r = run_forward(wl, lay, 4096)
+    ids, w, offsets, perm_src = check_routing(wl, lg, r)
+    counts = np.diff(offsets)
+    experts = pick(offsets, n=2, seed=7)
+    act = np.nonzero(counts > 0)[0]
+    experts.append(int(act[np.argmin(counts[act])]))
+    check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
+    check_combine_property(wl, r)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["vq2x8", "vq"])
 def test_vq_prefill_full_sampled(name):
     """VQ layers (2 x 8-bit codes with LDS codebooks; 16-bit codes from L2) at
