@@ -459,13 +459,18 @@ int moe_combine_shared(const float* y_perm, const int32_t* inv_perm, const float
  *   workspace  [device] >= moe_layer_forward_workspace_bytes(layer, T, k)
  *              bytes, 256-byte aligned; contents on return unspecified.
  *
- * Small batches of single-format, unrotated layers (T*k <= 16, k <= 8,
- * E <= 256: decode) take a fused path of two launches and no permutation:
- * the gate/up kernel ranks the token's experts from the logits itself, the
- * down kernel forms the gated sum in ascending j.  Its results are the bits
- * of the step-by-step calls on the same inputs (each expert's rows, partial
- * sums and the combine are taken in the same order).  Other batches run the
- * step-by-step calls.  Errors as for those calls (checked before any launch).
+ * Small batches of single-format layers (T*k <= 16, k <= 8, E <= 256:
+ * decode) take a fused path of two launches and no permutation: the gate/up
+ * kernel ranks the token's experts from the logits itself, the down kernel
+ * forms the gated sum in ascending j.  A rotated layer (H <= 12288) takes
+ * four: the gate/up kernel also rotates the token's row for its expert, then
+ * the middle rotation, the down pass per slot, and the combine rotating each
+ * slot's output back.  Its results are the bits of the step-by-step calls on
+ * the same inputs (each expert's rows, partial sums, rotations and the
+ * combine are taken in the same order).  Other batches run the step-by-step
+ * calls (a rotated layer's combine rotating the down outputs back, with the
+ * same bits as moe_expert_down_q's rotation followed by moe_combine).
+ * Errors as for those calls (checked before any launch).
  */
 size_t moe_layer_forward_workspace_bytes(const moe_qlayer* layer, int64_t T, int32_t k);
 int moe_layer_forward(const moe_qlayer* layer, const uint16_t* x_bf16, const float* logits,
