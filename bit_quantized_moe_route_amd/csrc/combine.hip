@@ -31,24 +31,12 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_per
     const int64_t t = blockIdx.x / nbh;
     const int h = ((blockIdx.x % nbh) * 256 + threadIdx.x) * 4;
     if (h >= H) return;
-    // slots in groups of 8, every load of a group issued before its first
-    // addition (clamped slots past k are loaded and not added)
-    constexpr int UB = 8;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < k; j0 += UB) {
-        f32x4 ys[UB];
-        float wj[UB];
-#pragma unroll
-        for (int u = 0; u < UB; ++u) {
-            const int64_t a = t * k + min(j0 + u, k - 1);
-            ys[u] = *reinterpret_cast<const f32x4*>(y_perm + (int64_t)inv_perm[a] * H + h);
-            wj[u] = w[a];
-        }
-#pragma unroll
-        for (int u = 0; u < UB; ++u) {
-            if (j0 + u >= k) break;
-            acc = acc + wj[u] * ys[u];
-        }
+    for (int j = 0; j < k; ++j) {
+        const int64_t row = inv_perm[t * k + j];
+        const float wj = w[t * k + j];
+        f32x4 y = *reinterpret_cast<const f32x4*>(y_perm + row * H + h);
+        acc = acc + wj * y;
     }
     if constexpr (SHARED) acc = acc + *reinterpret_cast<const f32x4*>(y_shared + t * H + h);
     *reinterpret_cast<f32x4*>(out + t * H + h) = acc;
