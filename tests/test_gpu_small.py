@@ -74,6 +74,13 @@ SMALL = {
     "rot_bf16_prefill": synth.small_workload("rot_bf16_prefill", E=6, k=2, H=256, I=128,
                                              T=200, fmt="nv_bf16", cfg=174, n_nvfp4=3,
                                              rot=True),
+    # the library's largest layer shape in experts and slots (E = 1024, k = 16):
+    # many active experts in the decode kernels' expert lookup and in the
+    # grouped GEMM's work list
+    "max_e_decode": synth.small_workload("max_e_decode", E=1024, k=16, H=128, I=64, T=20,
+                                         cfg=226),
+    "max_e_prefill": synth.small_workload("max_e_prefill", E=1024, k=16, H=128, I=64, T=200,
+                                          logits="zipf", zipf_s=1.1, cfg=227),
     # the wide down-input rotation (signs + one Hadamard-512 per 512
     # intermediate channels): decode, the grouped GEMM with two 512-blocks
     # (two of a workgroup's four waves idle), rows enough for whole-row
