@@ -74,6 +74,16 @@ SMALL = {
     "rot_bf16_prefill": synth.small_workload("rot_bf16_prefill", E=6, k=2, H=256, I=128,
                                              T=200, fmt="nv_bf16", cfg=174, n_nvfp4=3,
                                              rot=True),
+    # the decode / grouped-GEMM boundary (T = 127 decode kernels, with hot
+    # experts past 16 tokens in several 16-token chunks; T = 128 the grouped
+    # GEMM), the same weights
+    "edge_t127": synth.small_workload("edge_t127", E=16, k=4, H=256, I=128, T=127,
+                                      logits="zipf", zipf_s=1.1, cfg=228),
+    "edge_t128": synth.small_workload("edge_t128", E=16, k=4, H=256, I=128, T=128,
+                                      logits="zipf", zipf_s=1.1, cfg=228),
+    "edge_t127_mixed3": synth.small_workload("edge_t127_mixed3", E=24, k=6, H=256, I=128,
+                                             T=127, fmt="mixed3", logits="hot", cfg=229,
+                                             n_nvfp4=8, n_hot=4, hot_share=0.6, vq8_m=2),
     # the library's largest layer shape in experts and slots (E = 1024, k = 16):
     # many active experts in the decode kernels' expert lookup and in the
     # grouped GEMM's work list
