@@ -36,6 +36,7 @@ Prints ONE compact JSON line on stdout (progress goes to stderr):
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -81,12 +82,21 @@ def gateup_kernel_name(T, k, n_experts):
     return f"k_ffn<NvFmt, 1, {ks}, 2, 0, 4, false, false, false, false>"
 
 
+def _code_only(text):
+    """C++ source without its comments and with whitespace runs collapsed, so
+    that an edit of comments alone leaves the hash (and a traffic summary taken
+    on that code) valid."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_moe_route_amd", "csrc")
     for f in ROOFLINE_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

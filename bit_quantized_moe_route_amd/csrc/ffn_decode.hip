@@ -501,6 +501,16 @@ constexpr int kPrefetchRoute = MOEQ_ROUTE_PREFETCH;
 #endif
 constexpr int kMinWaves = MOEQ_MIN_WAVES;
 
+// Dynamic LDS of the small-codebook VQ kernels: the codebooks of the
+// projections a pass reads (gate and up, or down).
+template <class F>
+constexpr size_t codebook_lds_bytes(int phase) {
+    if constexpr (F::kVq8)
+        return (size_t)(phase == 0 ? 2 : 1) * F::CODES * MOE_VQ8_NCODE * 16;
+    else
+        return 0;
+}
+
 // One kernel for both halves.  PHASE 0 (gate/up + SwiGLU): a wave owns RPW
 // row-pair groups (RPW gate tiles and RPW up tiles per input tile); PHASE 1
 // (down): a wave owns RPW row groups of W_down.  KS waves split the input
@@ -520,21 +530,14 @@ constexpr int kMinWaves = MOEQ_MIN_WAVES;
 // a = t*k + j; each wave takes token t's top-k from the logits itself, the
 // expert of rank j is its one "row", and h goes to row a (token order, no
 // permutation); one workgroup per token writes the token's ids and weights.
-// Single-format layers only (the record index of expert e is e).
+// Single-format layers only (the record index of expert e is e).  ROUTE with
+// ROT (and PART): the workgroup first rotates its assignment's x row into
+// LDS (after the codebooks), the B operand is read from there, and the raw
+// products go to A.part row a.
 // ADDOUT (down of a shared expert): y is added to A.out (the routed sum
 // already there) instead of being stored to A.y_perm.
 // The body is a device function of the workgroup's grid coordinates bid, so
 // that one launch can run it beside another kernel's workgroups.
-// Dynamic LDS of the small-codebook VQ kernels: the codebooks of the
-// projections a pass reads (gate and up, or down).
-template <class F>
-constexpr size_t codebook_lds_bytes(int phase) {
-    if constexpr (F::kVq8)
-        return (size_t)(phase == 0 ? 2 : 1) * F::CODES * MOE_VQ8_NCODE * 16;
-    else
-        return 0;
-}
-
 template <class F, int NTT, int KS, int RPW, int PHASE, int WV, bool ID, bool PART, bool ROT,
           bool ROUTE, bool ADDOUT = false>
 __device__ __forceinline__ void ffn_body(const DecodeArgs& A, const uint3 bid) {

@@ -52,13 +52,13 @@ def test_source_hash_follows_each_roofline_source(tmp_path, monkeypatch):
     csrc = tmp_path / "bit_quantized_moe_route_amd" / "csrc"
     csrc.mkdir(parents=True)
     for name in bench.ROOFLINE_SOURCES:
-        (csrc / name).write_text(f"// {name}\n")
+        (csrc / name).write_text("constexpr int v = 0;\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     h0 = bench.kernel_source_hash()
     assert h0 == bench.kernel_source_hash() and len(h0) == 16
     seen = {h0}
     for name in bench.ROOFLINE_SOURCES:
-        (csrc / name).write_text(f"// {name} changed\n")
+        (csrc / name).write_text("constexpr int v = 1;\n")
         h = bench.kernel_source_hash()
         assert h not in seen, name
         seen.add(h)
@@ -149,3 +149,13 @@ def test_fused_path_rule_matches_the_library():
     assert bench.fused_path(_FakeLayer([1] * 256, rot=object(), H=12288), 2, 8)
     assert not bench.fused_path(_FakeLayer([1] * 256, rot=object(), H=12416), 1, 8)
     assert not bench.fused_path(_FakeLayer([1] * 256, rot=object()), 3, 8)
+
+
+def test_kernel_source_hash_ignores_comments_only():
+    """The traffic summary stays valid across comment edits of the roofline
+    kernel's sources, and not across code edits."""
+    a = "int f(int x) {\n    return x + 1;   // one\n}\n/* block\n comment */\n"
+    b = "// header\nint f(int x) {\n  return x + 1;\n}\n"
+    c = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
