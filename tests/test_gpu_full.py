@@ -90,6 +90,17 @@ def check_combine_property(wl, r):
     assert_rows_close(to_np(r["out"]), ref, "combine property", tol=1e-5)
 
 
+def check_layer_forward_bits(wl, lay, x_bits, lg, r):
+    """The one-call layer (fused for small batches; for a rotated layer the
+    combine rotating the down outputs back) gives the step-by-step calls'
+    bits."""
+    ids, w, out = moeq.layer_forward(lay, torch.from_numpy(x_bits.view(np.int16)).to(DEV),
+                                     torch.from_numpy(lg).to(DEV), wl.k)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, r["topk_ids"]) and torch.equal(w, r["topk_w"])
+    assert torch.equal(out, r["out"])
+
+
 def check_every_expert(wl, x_bits, lg, r, ids, w, offsets, perm_src, fmt_host):
     """Every expert the batch touches: all its y_perm rows against the
     oracle FFN, then every output row against the oracle's combine of the
@@ -452,6 +463,7 @@ def test_rotated_full_sampled(name, T):
     experts = pick(offsets, n=2, seed=T + 40)
     check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
     check_combine_property(wl, r)
+    check_layer_forward_bits(wl, lay, x_bits, lg, r)
 
 
 @pytest.mark.timeout(900)
@@ -482,6 +494,7 @@ def test_rotated_prefill_full_sampled(name):
     experts.append(int(act[np.argmin(counts[act])]))
     check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
     check_combine_property(wl, r)
+    check_layer_forward_bits(wl, lay, x_bits, lg, r)
 
 
 @pytest.mark.timeout(900)
