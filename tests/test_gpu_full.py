@@ -196,6 +196,7 @@ def test_decode_T8_every_expert():
     x_bits, lg, r = run_forward(wl, lay, 8)
     ids, w, offsets, perm_src = check_routing(wl, lg, r)
     check_every_expert(wl, x_bits, lg, r, ids, w, offsets, perm_src, synth.tier_map(wl))
+    check_layer_forward_bits(wl, lay, x_bits, lg, r)
 
 
 @pytest.mark.timeout(900)
@@ -209,6 +210,7 @@ def test_decode_T32_full_sampled():
     experts = pick(offsets, n=4, seed=T)
     check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
     check_combine_property(wl, r)
+    check_layer_forward_bits(wl, lay, x_bits, lg, r)
 
 
 @pytest.mark.timeout(900)
@@ -251,6 +253,7 @@ def test_prefill_full_sampled():
     experts.append(int(act[np.argmin(counts[act])]))
     check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, synth.tier_map(wl))
     check_combine_property(wl, r)
+    check_layer_forward_bits(wl, lay, x_bits, lg, r)
 
 
 # ------------------------------------------------------------------ VQ and mixed
@@ -331,6 +334,7 @@ def test_mixed_full(T):
                    + pick(offsets, fmt_host, synth.FMT_VQ, n=2, seed=T + 1))
         check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, fmt_host)
         check_combine_property(wl, r)
+    check_layer_forward_bits(wl, lay, x_bits, lg, r)
     # the hot set takes about 60% of the assignments
     hot = synth.hot_experts(wl)
     share = np.isin(ids, hot).mean()
@@ -357,6 +361,7 @@ def test_nested_full_sampled():
                + pick(offsets, fmt_host, synth.FMT_NVFP4, n=1, seed=T + 1))
     check_experts(wl, x_bits, r, ids, offsets, perm_src, experts, fmt_host)
     check_combine_property(wl, r)
+    check_layer_forward_bits(wl, lay, x_bits, lg, r)
 
 
 # ------------------------------------------------------------------ shared expert
